@@ -1,0 +1,374 @@
+"""fp64 CPU oracle for the Fourier-neural-operator spectral convolution.
+
+TEST INFRASTRUCTURE ONLY.  This module is the checker, not the product: only
+the test suite, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import it.  It shares no code with the HIP library (no
+kernels, tables, constants or helpers) and never imports the package that
+wraps the library.
+
+Sources (the three web pages this method is described on):
+
+* P1 -- "TurboFNO: FFT-GEMM-iFFT full-chain fused GPU operator" (gsyq.cn):
+  section 1 (FFT -> frequency-domain GEMM -> iFFT chain), section 2.2 (only the
+  low-frequency block of the spectrum is multiplied by the weights, the rest is
+  zero; complex product (a+bi)(c+di) = (ac-bd) + (ad+bc)i), sections 3.1/4.4
+  (orthonormal normalisation, scale 1/sqrt(M*N) on each transform).
+* P2 -- "FFT for operator optimisation" (lpnh.cn): section 1.2 (convolution
+  theorem), sections 2.1/2.2 (real-to-complex half spectrum of length N/2+1 on
+  the last axis, complex-to-real inverse), section 6.4 (dump intermediate
+  spectra from a Python reference and compare them point by point).
+
+What is computed (all in float64 / complex128; fp32 / complex64 inputs are
+upcast exactly):
+
+1. forward, ortho:  X[b,i,kx,ky] = (HW)^-1/2 sum_h sum_w x[b,i,h,w]
+                                    exp(-2 pi i (kx h / H + ky w / W))
+2. truncate:  Xh[b,i,0,r,ky] = X[b,i,r,ky],  Xh[b,i,1,r,ky] = X[b,i,H-mx+r,ky]
+              for r < mx, ky < my
+3. mix:  Yh[b,o,s,r,ky] = sum_i Xh[b,i,s,r,ky] * W[s,r,ky,i,o]   (no conjugate)
+4. zero-fill + complex-to-real inverse, ortho:
+     out[b,o,h,w] = (HW)^-1/2 sum_kx sum_{ky<=W/2} c_ky
+                      Re( Y[b,o,kx,ky] exp(+2 pi i (kx h / H + ky w / W)) )
+   with c_0 = c_{W/2} = 1 and c_ky = 2 otherwise (the standard C2R rule: the
+   imaginary parts of the DC and Nyquist columns do not contribute).
+5. 1D: the same with H = 1, one weight block W[modes, Cin, Cout].
+
+Two independent ways of computing the transforms are provided:
+
+* ``transform="dft"`` (default): the sums above written out as products with
+  explicit DFT matrices whose phases come from the exact integer reduction
+  (j*k) mod N.  This is the definition itself.
+* ``transform="fft"``: full transforms by a textbook recursive radix-2
+  decimation-in-time Cooley-Tukey FFT, then truncation; the inverse builds the
+  Hermitian-extended row spectrum and transforms it.
+
+``spectral_conv2d_loops`` is a pure-Python loop twin of the whole operator for
+tiny sizes (brute force, no library transforms at all).
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+__all__ = [
+    "dft_brute",
+    "fft_radix2",
+    "dft_matrix",
+    "kept_kx",
+    "c2r_weights",
+    "forward_truncated_2d",
+    "mix_2d",
+    "inverse_from_truncated_2d",
+    "spectral_conv2d_ref",
+    "forward_truncated_1d",
+    "mix_1d",
+    "inverse_from_truncated_1d",
+    "spectral_conv1d_ref",
+    "spectral_conv2d_loops",
+    "spectral_conv1d_loops",
+]
+
+
+# --------------------------------------------------------------------------
+# 1D transforms
+# --------------------------------------------------------------------------
+
+def _phase(m: np.ndarray, n: int, sign: int) -> np.ndarray:
+    """exp(sign * 2 pi i * m / n) for integer m already reduced mod n."""
+    ang = (2.0 * math.pi / n) * m.astype(np.float64)
+    return np.cos(ang) + (1j * sign) * np.sin(ang)
+
+
+def dft_matrix(n: int, rows: np.ndarray, cols: np.ndarray, sign: int) -> np.ndarray:
+    """M[a, b] = exp(sign * 2 pi i * (rows[a] * cols[b] mod n) / n).
+
+    The product of the two integer indices is reduced modulo n in integer
+    arithmetic before it becomes an angle, so the phase is exact up to one
+    rounding of cos/sin in float64.
+    """
+    rows = np.asarray(rows, dtype=np.int64)
+    cols = np.asarray(cols, dtype=np.int64)
+    m = np.mod(np.outer(rows, cols), n)
+    return _phase(m, n, sign)
+
+
+def dft_brute(a: np.ndarray, axis: int = -1, sign: int = -1) -> np.ndarray:
+    """Unnormalised O(N^2) DFT along ``axis``: A[k] = sum_n a[n] exp(sign 2 pi i n k / N)."""
+    a = np.asarray(a, dtype=np.complex128)
+    n = a.shape[axis]
+    idx = np.arange(n)
+    f = dft_matrix(n, idx, idx, sign)          # f[n, k]
+    moved = np.moveaxis(a, axis, -1)
+    out = moved @ f
+    return np.moveaxis(out, -1, axis)
+
+
+def fft_radix2(a: np.ndarray, axis: int = -1, sign: int = -1) -> np.ndarray:
+    """Unnormalised recursive radix-2 decimation-in-time FFT along ``axis``.
+
+    Textbook Cooley-Tukey: split into even and odd samples, transform each
+    half, combine with the twiddles exp(sign 2 pi i k / N), k < N/2.
+    N must be a power of two.
+    """
+    a = np.asarray(a, dtype=np.complex128)
+    n = a.shape[axis]
+    if n & (n - 1):
+        raise ValueError(f"fft_radix2 needs a power-of-two length, got {n}")
+    moved = np.moveaxis(a, axis, -1)
+
+    def rec(v: np.ndarray) -> np.ndarray:
+        m = v.shape[-1]
+        if m == 1:
+            return v.copy()
+        even = rec(v[..., 0::2])
+        odd = rec(v[..., 1::2])
+        tw = _phase(np.arange(m // 2), m, sign) * odd
+        return np.concatenate([even + tw, even - tw], axis=-1)
+
+    return np.moveaxis(rec(moved), -1, axis)
+
+
+def _transform(a: np.ndarray, axis: int, sign: int, transform: str) -> np.ndarray:
+    if transform == "dft":
+        return dft_brute(a, axis, sign)
+    if transform == "fft":
+        return fft_radix2(a, axis, sign)
+    raise ValueError(f"unknown transform {transform!r}")
+
+
+# --------------------------------------------------------------------------
+# Mode bookkeeping
+# --------------------------------------------------------------------------
+
+def kept_kx(h: int, mx: int) -> np.ndarray:
+    """Frequencies along H kept by the truncation, in weight-block order.
+
+    Block 0 holds kx = r and block 1 holds kx = H - mx + r, r < mx.
+    """
+    r = np.arange(mx)
+    return np.concatenate([r, h - mx + r])
+
+
+def c2r_weights(w: int, my: int) -> np.ndarray:
+    """c_ky of the complex-to-real inverse: 1 at ky = 0 and ky = W/2, 2 elsewhere."""
+    ky = np.arange(my)
+    c = np.full(my, 2.0)
+    c[ky == 0] = 1.0
+    c[2 * ky == w] = 1.0
+    return c
+
+
+def _check_2d(h: int, w: int, mx: int, my: int) -> None:
+    if mx < 1 or 2 * mx > h:
+        raise ValueError(f"need 1 <= mx and 2*mx <= H (mx={mx}, H={h})")
+    if my < 1 or my > w // 2 + 1:
+        raise ValueError(f"need 1 <= my <= W/2+1 (my={my}, W={w})")
+
+
+# --------------------------------------------------------------------------
+# 2D operator, stage by stage
+# --------------------------------------------------------------------------
+
+def forward_truncated_2d(x: np.ndarray, mx: int, my: int, transform: str = "dft") -> np.ndarray:
+    """Steps 1-2: ortho forward transform of real x[B,C,H,W], truncated to Xh[B,C,2,mx,my]."""
+    x = np.asarray(x, dtype=np.float64)
+    b, c, h, w = x.shape
+    _check_2d(h, w, mx, my)
+    scale = 1.0 / math.sqrt(h * w)
+    kx = kept_kx(h, mx)
+    if transform == "dft":
+        fw = dft_matrix(w, np.arange(w), np.arange(my), -1)        # [W, my]
+        fh = dft_matrix(h, kx, np.arange(h), -1)                   # [2mx, H]
+        rows = x @ fw                                               # [B,C,H,my]
+        full = np.einsum("qh,bchk->bcqk", fh, rows)                # [B,C,2mx,my]
+    else:
+        rows = _transform(x.astype(np.complex128), 3, -1, transform)[..., :my]
+        cols = _transform(rows, 2, -1, transform)                  # [B,C,H,my]
+        full = cols[:, :, kx, :]
+    return (full * scale).reshape(b, c, 2, mx, my)
+
+
+def mix_2d(xh: np.ndarray, weight: np.ndarray) -> np.ndarray:
+    """Step 3: Yh[b,o,s,r,k] = sum_i Xh[b,i,s,r,k] W[s,r,k,i,o] (plain complex product)."""
+    xh = np.asarray(xh, dtype=np.complex128)
+    weight = np.asarray(weight, dtype=np.complex128)
+    return np.einsum("bisrk,srkio->bosrk", xh, weight)
+
+
+def inverse_from_truncated_2d(yh: np.ndarray, h: int, w: int, transform: str = "dft") -> np.ndarray:
+    """Step 4: zero-fill Yh[B,C,2,mx,my] into the half spectrum and apply the ortho C2R inverse."""
+    yh = np.asarray(yh, dtype=np.complex128)
+    b, c, _, mx, my = yh.shape
+    _check_2d(h, w, mx, my)
+    scale = 1.0 / math.sqrt(h * w)
+    kx = kept_kx(h, mx)
+    yq = yh.reshape(b, c, 2 * mx, my)
+    if transform == "dft":
+        gh = dft_matrix(h, np.arange(h), kx, +1)                   # [H, 2mx]
+        gw = dft_matrix(w, np.arange(my), np.arange(w), +1)        # [my, W]
+        gw = gw * c2r_weights(w, my)[:, None]
+        cols = np.einsum("hq,bcqk->bchk", gh, yq)                  # [B,C,H,my]
+        out = (cols @ gw).real
+        return out * scale
+    # full half spectrum, zero outside the kept modes
+    half = np.zeros((b, c, h, w // 2 + 1), dtype=np.complex128)
+    half[:, :, kx, :my] = yq
+    cols = _transform(half, 2, +1, transform)                      # inverse along H
+    # Hermitian extension of every row, imaginary parts of DC / Nyquist dropped
+    z = np.zeros((b, c, h, w), dtype=np.complex128)
+    z[..., 1:w // 2] = cols[..., 1:w // 2]
+    z[..., 0] = cols[..., 0].real
+    z[..., w // 2] = cols[..., w // 2].real
+    z[..., w // 2 + 1:] = np.conj(cols[..., 1:w // 2][..., ::-1])
+    out = _transform(z, 3, +1, transform).real
+    return out * scale
+
+
+def spectral_conv2d_ref(x, weight, mx: int, my: int, transform: str = "dft",
+                        return_stages: bool = False):
+    """Whole 2D operator: x[B,Cin,H,W] real, weight[2,mx,my,Cin,Cout] complex -> out[B,Cout,H,W]."""
+    x = np.asarray(x)
+    weight = np.asarray(weight)
+    _, cin, h, w = x.shape
+    if weight.shape[:3] != (2, mx, my) or weight.shape[3] != cin:
+        raise ValueError(f"weight shape {weight.shape} does not match (2,{mx},{my},{cin},Cout)")
+    xh = forward_truncated_2d(x, mx, my, transform)
+    yh = mix_2d(xh, weight)
+    out = inverse_from_truncated_2d(yh, h, w, transform)
+    if return_stages:
+        return out, xh, yh
+    return out
+
+
+# --------------------------------------------------------------------------
+# 1D operator (global token mixing along a sequence)
+# --------------------------------------------------------------------------
+
+def forward_truncated_1d(x: np.ndarray, modes: int, transform: str = "dft") -> np.ndarray:
+    """Ortho forward transform of real x[B,C,N], bins ky < modes -> Xh[B,C,modes]."""
+    x = np.asarray(x, dtype=np.float64)
+    n = x.shape[-1]
+    if modes < 1 or modes > n // 2 + 1:
+        raise ValueError(f"need 1 <= modes <= N/2+1 (modes={modes}, N={n})")
+    scale = 1.0 / math.sqrt(n)
+    if transform == "dft":
+        full = x @ dft_matrix(n, np.arange(n), np.arange(modes), -1)
+    else:
+        full = _transform(x.astype(np.complex128), -1, -1, transform)[..., :modes]
+    return full * scale
+
+
+def mix_1d(xh: np.ndarray, weight: np.ndarray) -> np.ndarray:
+    """Yh[b,o,k] = sum_i Xh[b,i,k] W[k,i,o]."""
+    return np.einsum("bik,kio->bok", np.asarray(xh, np.complex128), np.asarray(weight, np.complex128))
+
+
+def inverse_from_truncated_1d(yh: np.ndarray, n: int, transform: str = "dft") -> np.ndarray:
+    """Zero-fill Yh[B,C,modes] and apply the ortho C2R inverse of length n."""
+    yh = np.asarray(yh, dtype=np.complex128)
+    modes = yh.shape[-1]
+    scale = 1.0 / math.sqrt(n)
+    if transform == "dft":
+        g = dft_matrix(n, np.arange(modes), np.arange(n), +1) * c2r_weights(n, modes)[:, None]
+        return (yh @ g).real * scale
+    z = np.zeros(yh.shape[:-1] + (n,), dtype=np.complex128)
+    half = np.zeros(yh.shape[:-1] + (n // 2 + 1,), dtype=np.complex128)
+    half[..., :modes] = yh
+    z[..., 1:n // 2] = half[..., 1:n // 2]
+    z[..., 0] = half[..., 0].real
+    z[..., n // 2] = half[..., n // 2].real
+    z[..., n // 2 + 1:] = np.conj(half[..., 1:n // 2][..., ::-1])
+    return _transform(z, -1, +1, transform).real * scale
+
+
+def spectral_conv1d_ref(x, weight, modes: int, transform: str = "dft", return_stages: bool = False):
+    """Whole 1D operator: x[B,Cin,N] real, weight[modes,Cin,Cout] complex -> out[B,Cout,N]."""
+    x = np.asarray(x)
+    weight = np.asarray(weight)
+    if weight.shape[0] != modes or weight.shape[1] != x.shape[1]:
+        raise ValueError(f"weight shape {weight.shape} does not match ({modes},{x.shape[1]},Cout)")
+    xh = forward_truncated_1d(x, modes, transform)
+    yh = mix_1d(xh, weight)
+    out = inverse_from_truncated_1d(yh, x.shape[-1], transform)
+    if return_stages:
+        return out, xh, yh
+    return out
+
+
+# --------------------------------------------------------------------------
+# Pure-Python loop twins (tiny sizes only)
+# --------------------------------------------------------------------------
+
+def spectral_conv2d_loops(x, weight, mx: int, my: int):
+    """The whole 2D operator as explicit loops over every index (tiny inputs only).
+
+    Each output sample is the sum over the kept modes of c_ky * Re(Y e^{+i phase})
+    with Y the mixed spectrum; each spectrum entry is the double sum over the grid.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    weight = np.asarray(weight, dtype=np.complex128)
+    b_n, cin, h, w = x.shape
+    cout = weight.shape[-1]
+    _check_2d(h, w, mx, my)
+    scale = 1.0 / math.sqrt(h * w)
+
+    def e(sign, num, den):
+        num %= den
+        ang = 2.0 * math.pi * num / den
+        return complex(math.cos(ang), sign * math.sin(ang))
+
+    out = np.zeros((b_n, cout, h, w))
+    for b in range(b_n):
+        xh = {}
+        for i in range(cin):
+            for s in range(2):
+                for r in range(mx):
+                    kx = r if s == 0 else h - mx + r
+                    for ky in range(my):
+                        acc = 0j
+                        for hh in range(h):
+                            for ww in range(w):
+                                acc += x[b, i, hh, ww] * e(-1, kx * hh, h) * e(-1, ky * ww, w)
+                        xh[i, s, r, ky] = acc * scale
+        for o in range(cout):
+            for s in range(2):
+                for r in range(mx):
+                    kx = r if s == 0 else h - mx + r
+                    for ky in range(my):
+                        y = 0j
+                        for i in range(cin):
+                            y += xh[i, s, r, ky] * weight[s, r, ky, i, o]
+                        c = 1.0 if (ky == 0 or 2 * ky == w) else 2.0
+                        for hh in range(h):
+                            for ww in range(w):
+                                out[b, o, hh, ww] += c * (y * e(+1, kx * hh, h) * e(+1, ky * ww, w)).real
+    return out * scale
+
+
+def spectral_conv1d_loops(x, weight, modes: int):
+    """The whole 1D operator as explicit loops (tiny inputs only)."""
+    x = np.asarray(x, dtype=np.float64)
+    weight = np.asarray(weight, dtype=np.complex128)
+    b_n, cin, n = x.shape
+    cout = weight.shape[-1]
+    scale = 1.0 / math.sqrt(n)
+    out = np.zeros((b_n, cout, n))
+    for b in range(b_n):
+        xh = np.zeros((cin, modes), dtype=np.complex128)
+        for i in range(cin):
+            for k in range(modes):
+                acc = 0j
+                for t in range(n):
+                    ang = 2.0 * math.pi * ((k * t) % n) / n
+                    acc += x[b, i, t] * complex(math.cos(ang), -math.sin(ang))
+                xh[i, k] = acc * scale
+        for o in range(cout):
+            for k in range(modes):
+                y = sum(xh[i, k] * weight[k, i, o] for i in range(cin))
+                c = 1.0 if (k == 0 or 2 * k == n) else 2.0
+                for t in range(n):
+                    ang = 2.0 * math.pi * ((k * t) % n) / n
+                    out[b, o, t] += c * (y * complex(math.cos(ang), math.sin(ang))).real
+    return out * scale

@@ -1,0 +1,493 @@
+"""Pins for the fp64 oracle (CPU only).
+
+The oracle is trusted only because of these checks, each of which fixes the
+answer from outside the oracle: closed forms of the transforms, Parseval,
+identity / projector properties, the convolution theorem against a directly
+computed circular convolution, a library FFT (numpy.fft) as an independent
+witness, and brute-force loops on tiny inputs.  ``test_planted_mistakes``
+plants plausible bugs into the oracle (a flipped sign, a conjugated weight,
+a wrong block-1 index, a wrong C2R weight, transposed channels) and checks
+that some pin catches each one.
+"""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import spectral as S
+
+TRANSFORMS = ["dft", "fft"]
+
+
+def rel(a, b):
+    a = np.asarray(a)
+    b = np.asarray(b)
+    den = np.linalg.norm(b.ravel())
+    return np.linalg.norm((a - b).ravel()) / (den if den > 0 else 1.0)
+
+
+def rand_c(rng, shape):
+    return rng.standard_normal(shape) + 1j * rng.standard_normal(shape)
+
+
+# --------------------------------------------------------------------------
+# 1D transforms
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("n", [1, 2, 4, 8, 16, 64])
+@pytest.mark.parametrize("sign", [-1, +1])
+def test_dft_brute_vs_radix2(n, sign):
+    rng = np.random.default_rng(n)
+    a = rand_c(rng, (3, n))
+    assert rel(S.fft_radix2(a, -1, sign), S.dft_brute(a, -1, sign)) < 1e-13
+
+
+def test_dft_brute_vs_radix2_2d_8x8():
+    rng = np.random.default_rng(7)
+    a = rand_c(rng, (2, 8, 8))
+    brute = S.dft_brute(S.dft_brute(a, 1, -1), 2, -1)
+    fast = S.fft_radix2(S.fft_radix2(a, 2, -1), 1, -1)
+    assert rel(fast, brute) < 1e-13
+
+
+@pytest.mark.parametrize("n", [1, 4, 16, 32])
+@pytest.mark.parametrize("fn", [S.dft_brute, S.fft_radix2])
+def test_dft_impulse_constant_exponential(n, fn):
+    delta = np.zeros(n)
+    delta[0] = 1.0
+    np.testing.assert_allclose(fn(delta), np.ones(n), atol=1e-13)
+    np.testing.assert_allclose(fn(np.ones(n)), n * delta, atol=1e-12)
+    # a single complex exponential e^{+2 pi i q t / n} lands in bin q with weight n
+    q = 3 % n
+    t = np.arange(n)
+    e = np.exp(2j * np.pi * q * t / n)
+    expect = np.zeros(n, dtype=complex)
+    expect[q] = n
+    np.testing.assert_allclose(fn(e), expect, atol=1e-11)
+
+
+@pytest.mark.parametrize("n", [2, 8, 32, 128])
+def test_transforms_vs_numpy_fft(n):
+    rng = np.random.default_rng(n + 1)
+    a = rand_c(rng, (4, n))
+    ref = np.fft.fft(a, axis=-1)
+    assert rel(S.dft_brute(a), ref) < 1e-13
+    assert rel(S.fft_radix2(a), ref) < 1e-13
+    assert rel(S.fft_radix2(a, sign=+1), np.fft.ifft(a, axis=-1) * n) < 1e-13
+
+
+def test_radix2_rejects_non_power_of_two():
+    with pytest.raises(ValueError):
+        S.fft_radix2(np.ones(6))
+
+
+# --------------------------------------------------------------------------
+# Forward transform + ortho scale
+# --------------------------------------------------------------------------
+
+def full_modes_xh_to_half(xh, h):
+    """Map the full-modes truncated spectrum [.., 2, H/2, W/2+1] back to [.., H, W/2+1]."""
+    mx = xh.shape[-2]
+    assert 2 * mx == h
+    return np.concatenate([xh[..., 0, :, :], xh[..., 1, :, :]], axis=-2)
+
+
+@pytest.mark.parametrize("transform", TRANSFORMS)
+@pytest.mark.parametrize("h,w", [(8, 8), (16, 8), (4, 16)])
+def test_forward_parseval(transform, h, w):
+    rng = np.random.default_rng(h * 100 + w)
+    x = rng.uniform(-1, 1, (2, 3, h, w))
+    xh = S.forward_truncated_2d(x, h // 2, w // 2 + 1, transform)
+    half = full_modes_xh_to_half(xh, h)
+    c = np.full(w // 2 + 1, 2.0)
+    c[0] = 1.0
+    c[w // 2] = 1.0
+    energy_x = np.sum(x ** 2, axis=(-2, -1))
+    energy_k = np.sum(c * np.abs(half) ** 2, axis=(-2, -1))
+    np.testing.assert_allclose(energy_k, energy_x, rtol=1e-13)
+
+
+@pytest.mark.parametrize("transform", TRANSFORMS)
+@pytest.mark.parametrize("h,w,a,b", [(8, 8, 1, 2), (16, 8, 5, 3), (8, 16, 7, 1)])
+def test_forward_single_cosine(transform, h, w, a, b):
+    hh, ww = np.meshgrid(np.arange(h), np.arange(w), indexing="ij")
+    x = np.cos(2 * np.pi * (a * hh / h + b * ww / w))[None, None]
+    half = full_modes_xh_to_half(S.forward_truncated_2d(x, h // 2, w // 2 + 1, transform), h)[0, 0]
+    expect = np.zeros_like(half)
+    expect[a, b] = math.sqrt(h * w) / 2
+    np.testing.assert_allclose(half, expect, atol=1e-12)
+
+
+@pytest.mark.parametrize("transform", TRANSFORMS)
+def test_forward_constant(transform):
+    h, w = 16, 8
+    x = np.ones((1, 1, h, w))
+    half = full_modes_xh_to_half(S.forward_truncated_2d(x, h // 2, w // 2 + 1, transform), h)[0, 0]
+    expect = np.zeros_like(half)
+    expect[0, 0] = math.sqrt(h * w)
+    np.testing.assert_allclose(half, expect, atol=1e-12)
+
+
+@pytest.mark.parametrize("transform", TRANSFORMS)
+def test_forward_1d_closed_forms(transform):
+    n = 32
+    t = np.arange(n)
+    x = np.cos(2 * np.pi * 5 * t / n)[None, None]
+    xh = S.forward_truncated_1d(x, n // 2 + 1, transform)[0, 0]
+    expect = np.zeros(n // 2 + 1, dtype=complex)
+    expect[5] = math.sqrt(n) / 2
+    np.testing.assert_allclose(xh, expect, atol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# Truncation, kx mapping, mix and C2R closed forms
+# --------------------------------------------------------------------------
+
+def single_mode_weight(mx, my, s, r, ky, c):
+    w = np.zeros((2, mx, my, 1, 1), dtype=complex)
+    w[s, r, ky, 0, 0] = c
+    return w
+
+
+def inband_error(h, w, mx, my, a, b, c, transform="dft"):
+    """|out - (Re c cos th - Im c sin th)| for x = cos th, th = 2 pi (a h/H + b w/W)."""
+    hh, ww = np.meshgrid(np.arange(h), np.arange(w), indexing="ij")
+    th = 2 * np.pi * (a * hh / h + b * ww / w)
+    x = np.cos(th)[None, None]
+    if a < mx:
+        s, r = 0, a
+    else:
+        s, r = 1, a - (h - mx)
+    wt = single_mode_weight(mx, my, s, r, b, c)
+    out = S.spectral_conv2d_ref(x, wt, mx, my, transform)[0, 0]
+    expect = c.real * np.cos(th) - c.imag * np.sin(th)
+    return np.max(np.abs(out - expect))
+
+
+@pytest.mark.parametrize("transform", TRANSFORMS)
+@pytest.mark.parametrize("h,w,mx,my,a,b", [
+    (16, 16, 4, 5, 3, 2),    # block 0, a = mx - 1
+    (16, 16, 4, 5, 12, 2),   # block 1, r = 0 (kx = H - mx)
+    (16, 16, 4, 5, 15, 4),   # block 1, r = mx - 1, ky = my - 1
+    (32, 8, 3, 4, 1, 3),     # non-square
+])
+def test_inband_single_mode(transform, h, w, mx, my, a, b):
+    assert inband_error(h, w, mx, my, a, b, 0.7 - 0.4j, transform) < 1e-12
+
+
+def outband_max(h, w, mx, my, a, b, transform="dft"):
+    hh, ww = np.meshgrid(np.arange(h), np.arange(w), indexing="ij")
+    x = np.cos(2 * np.pi * (a * hh / h + b * ww / w))[None, None]
+    wt = np.ones((2, mx, my, 1, 1), dtype=complex) * (0.3 + 0.9j)
+    return np.max(np.abs(S.spectral_conv2d_ref(x, wt, mx, my, transform)))
+
+
+@pytest.mark.parametrize("transform", TRANSFORMS)
+@pytest.mark.parametrize("a,b", [(4, 2), (11, 2), (2, 5)])
+def test_out_of_band_is_zero(transform, a, b):
+    # H=W=16, mx=4, my=5: a=mx and a=H-mx-1 are dropped along H; b=my is dropped along W.
+    assert outband_max(16, 16, 4, 5, a, b, transform) < 1e-12
+
+
+@pytest.mark.parametrize("transform", TRANSFORMS)
+def test_two_corner_ky0(transform):
+    h, w, mx, my, a = 16, 8, 5, 3, 2
+    th = 2 * np.pi * a * np.arange(h) / h
+    x = np.repeat(np.cos(th)[:, None], w, axis=1)[None, None]
+    c1, c2 = 0.8 + 0.3j, -0.2 + 0.6j
+    wt = np.zeros((2, mx, my, 1, 1), dtype=complex)
+    wt[0, a, 0, 0, 0] = c1           # kx = a
+    wt[1, mx - a, 0, 0, 0] = c2      # kx = H - mx + (mx - a) = H - a
+    out = S.spectral_conv2d_ref(x, wt, mx, my, transform)[0, 0]
+    expect = (c1 * np.exp(1j * th) + c2 * np.exp(-1j * th)).real / 2
+    np.testing.assert_allclose(out, np.repeat(expect[:, None], w, axis=1), atol=1e-12)
+
+
+@pytest.mark.parametrize("transform", TRANSFORMS)
+def test_dc_and_nyquist_imaginary_dropped(transform):
+    h, w = 8, 8
+    mx, my = 2, w // 2 + 1
+    x = np.ones((1, 1, h, w))
+    wt = single_mode_weight(mx, my, 0, 0, 0, 1j)
+    assert np.max(np.abs(S.spectral_conv2d_ref(x, wt, mx, my, transform))) < 1e-12
+    wt = single_mode_weight(mx, my, 0, 0, 0, 1.0)
+    np.testing.assert_allclose(S.spectral_conv2d_ref(x, wt, mx, my, transform), x, atol=1e-12)
+    # Nyquist column: x = (-1)^w sits entirely in ky = W/2 with weight c_{W/2} = 1
+    alt = np.tile((-1.0) ** np.arange(w), (h, 1))[None, None]
+    wt = single_mode_weight(mx, my, 0, 0, w // 2, 1j)
+    assert np.max(np.abs(S.spectral_conv2d_ref(alt, wt, mx, my, transform))) < 1e-12
+    wt = single_mode_weight(mx, my, 0, 0, w // 2, 1.0)
+    np.testing.assert_allclose(S.spectral_conv2d_ref(alt, wt, mx, my, transform), alt, atol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# Whole-operator invariants
+# --------------------------------------------------------------------------
+
+def identity_weight(mx, my, c):
+    return np.broadcast_to(np.eye(c), (2, mx, my, c, c)).astype(complex)
+
+
+@pytest.mark.parametrize("transform", TRANSFORMS)
+@pytest.mark.parametrize("h,w", [(8, 8), (16, 8), (4, 32), (2, 2)])
+def test_identity_full_modes(transform, h, w):
+    rng = np.random.default_rng(h + w)
+    x = rng.uniform(-1, 1, (2, 3, h, w))
+    out = S.spectral_conv2d_ref(x, identity_weight(h // 2, w // 2 + 1, 3), h // 2, w // 2 + 1, transform)
+    np.testing.assert_allclose(out, x, atol=1e-13)
+
+
+@pytest.mark.parametrize("transform", TRANSFORMS)
+@pytest.mark.parametrize("n", [2, 8, 64])
+def test_identity_full_modes_1d(transform, n):
+    rng = np.random.default_rng(n)
+    x = rng.standard_normal((3, 2, n))
+    wt = np.broadcast_to(np.eye(2), (n // 2 + 1, 2, 2)).astype(complex)
+    np.testing.assert_allclose(S.spectral_conv1d_ref(x, wt, n // 2 + 1, transform), x, atol=1e-12)
+
+
+@pytest.mark.parametrize("transform", TRANSFORMS)
+def test_projector_idempotent(transform):
+    rng = np.random.default_rng(3)
+    h, w, mx, my = 16, 16, 3, 4
+    x = rng.uniform(-1, 1, (2, 2, h, w))
+    wt = identity_weight(mx, my, 2).copy()
+    # kx = H - mx at ky = 0 has no conjugate partner in the kept set (kx = mx is
+    # dropped), so C2R keeps only half of it and the map is not idempotent there;
+    # with that one mode switched off the operator is an orthogonal projector.
+    wt[1, 0, 0] = 0.0
+    once = S.spectral_conv2d_ref(x, wt, mx, my, transform)
+    twice = S.spectral_conv2d_ref(once, wt, mx, my, transform)
+    np.testing.assert_allclose(twice, once, atol=1e-13)
+    assert rel(once, x) > 0.1      # it really projects
+
+
+def circular_conv2d_direct(x, k):
+    """out[b,o] = sum_i x[b,i] (*) k[i,o], circular, by explicit shifted sums."""
+    b_n, cin, h, w = x.shape
+    cout = k.shape[1]
+    out = np.zeros((b_n, cout, h, w))
+    for b in range(b_n):
+        for o in range(cout):
+            for i in range(cin):
+                for hp in range(h):
+                    for wp in range(w):
+                        out[b, o] += x[b, i, hp, wp] * np.roll(k[i, o], (hp, wp), axis=(0, 1))
+    return out
+
+
+@pytest.mark.parametrize("transform", TRANSFORMS)
+@pytest.mark.parametrize("h,w", [(8, 8), (16, 8)])
+def test_convolution_theorem_full_modes(transform, h, w):
+    rng = np.random.default_rng(11)
+    b_n, cin, cout = 2, 2, 3
+    x = rng.uniform(-1, 1, (b_n, cin, h, w))
+    k = rng.standard_normal((cin, cout, h, w))
+    mx, my = h // 2, w // 2 + 1
+    spec = np.fft.rfft2(k, axes=(-2, -1))                       # [Cin,Cout,H,W/2+1]
+    kx = np.concatenate([np.arange(mx), h - mx + np.arange(mx)])
+    wt = np.transpose(spec[:, :, kx, :my], (2, 3, 0, 1)).reshape(2, mx, my, cin, cout)
+    out = S.spectral_conv2d_ref(x, wt, mx, my, transform)
+    np.testing.assert_allclose(out, circular_conv2d_direct(x, k), atol=1e-11)
+
+
+@pytest.mark.parametrize("transform", TRANSFORMS)
+def test_convolution_theorem_bandlimited_partial_modes(transform):
+    rng = np.random.default_rng(12)
+    h, w, mx, my = 16, 8, 3, 3
+    b_n, cin, cout = 2, 2, 3
+    x = rng.uniform(-1, 1, (b_n, cin, h, w))
+    spec = np.zeros((cin, cout, h, w // 2 + 1), dtype=complex)
+    kx = np.concatenate([np.arange(mx), h - mx + np.arange(mx)])
+    for q in kx:
+        spec[:, :, q, :my] = rand_c(rng, (cin, cout, my))
+    # Hermitian consistency of the ky = 0 column over the kept kx set
+    spec[:, :, 0, 0] = spec[:, :, 0, 0].real
+    for r in range(1, mx):
+        spec[:, :, h - r, 0] = np.conj(spec[:, :, r, 0])
+    spec[:, :, h - mx, 0] = 0.0           # its partner kx = mx is not kept
+    k = np.fft.irfft2(spec, s=(h, w), axes=(-2, -1))
+    np.testing.assert_allclose(np.fft.rfft2(k, axes=(-2, -1)), spec, atol=1e-12)
+    wt = np.transpose(spec[:, :, kx, :my], (2, 3, 0, 1)).reshape(2, mx, my, cin, cout)
+    out = S.spectral_conv2d_ref(x, wt, mx, my, transform)
+    np.testing.assert_allclose(out, circular_conv2d_direct(x, k), atol=1e-11)
+
+
+@pytest.mark.parametrize("transform", TRANSFORMS)
+def test_convolution_theorem_1d(transform):
+    rng = np.random.default_rng(13)
+    n, b_n, cin, cout = 16, 3, 2, 3
+    x = rng.standard_normal((b_n, cin, n))
+    k = rng.standard_normal((cin, cout, n))
+    spec = np.fft.rfft(k, axis=-1)                                 # [Cin,Cout,N/2+1]
+    wt = np.transpose(spec, (2, 0, 1))
+    out = S.spectral_conv1d_ref(x, wt, n // 2 + 1, transform)
+    direct = np.zeros((b_n, cout, n))
+    for b in range(b_n):
+        for o in range(cout):
+            for i in range(cin):
+                for t in range(n):
+                    direct[b, o] += x[b, i, t] * np.roll(k[i, o], t)
+    np.testing.assert_allclose(out, direct, atol=1e-11)
+
+
+@pytest.mark.parametrize("transform", TRANSFORMS)
+def test_linearity(transform):
+    rng = np.random.default_rng(5)
+    h, w, mx, my = 16, 8, 3, 4
+    x1 = rng.uniform(-1, 1, (2, 3, h, w))
+    x2 = rng.uniform(-1, 1, (2, 3, h, w))
+    w1 = rand_c(rng, (2, mx, my, 3, 2))
+    w2 = rand_c(rng, (2, mx, my, 3, 2))
+    f = lambda x, wt: S.spectral_conv2d_ref(x, wt, mx, my, transform)
+    np.testing.assert_allclose(f(0.3 * x1 - 1.7 * x2, w1), 0.3 * f(x1, w1) - 1.7 * f(x2, w1), atol=1e-12)
+    np.testing.assert_allclose(f(x1, 0.3 * w1 + 2.0 * w2), 0.3 * f(x1, w1) + 2.0 * f(x1, w2), atol=1e-12)
+
+
+def test_mode_tagging():
+    rng = np.random.default_rng(6)
+    h, w, mx, my = 8, 8, 2, 3
+    x = rng.uniform(-1, 1, (1, 2, h, w))
+    wt = rand_c(rng, (2, mx, my, 2, 2))
+    full = S.spectral_conv2d_ref(x, wt, mx, my)
+    acc = np.zeros_like(full)
+    for s in range(2):
+        for r in range(mx):
+            for ky in range(my):
+                tag = np.zeros_like(wt)
+                tag[s, r, ky] = wt[s, r, ky]
+                part = S.spectral_conv2d_ref(x, tag, mx, my)
+                assert np.max(np.abs(part)) > 0
+                acc += part
+    np.testing.assert_allclose(acc, full, atol=1e-13)
+
+
+def test_channel_permutation():
+    rng = np.random.default_rng(8)
+    h, w, mx, my, c = 8, 16, 2, 5, 4
+    x = rng.uniform(-1, 1, (2, c, h, w))
+    sigma = [2, 0, 3, 1]
+    wt = np.zeros((2, mx, my, c, c), dtype=complex)
+    for o in range(c):
+        wt[..., sigma[o], o] = 1.0
+    out = S.spectral_conv2d_ref(x, wt, mx, my)
+    one = np.ones((2, mx, my, 1, 1), dtype=complex)
+    for o in range(c):
+        proj = S.spectral_conv2d_ref(x[:, sigma[o]:sigma[o] + 1], one, mx, my)[:, 0]
+        np.testing.assert_allclose(out[:, o], proj, atol=1e-13)
+
+
+# --------------------------------------------------------------------------
+# The two transform paths and the loop twins
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("h,w,mx,my", [(32, 32, 8, 8), (16, 64, 5, 33), (64, 8, 32, 2)])
+def test_dft_and_fft_paths_agree(h, w, mx, my):
+    rng = np.random.default_rng(9)
+    x = rng.uniform(-1, 1, (2, 3, h, w)).astype(np.float32)
+    wt = (rand_c(rng, (2, mx, my, 3, 2)) / 6).astype(np.complex64)
+    a, xa, ya = S.spectral_conv2d_ref(x, wt, mx, my, "dft", return_stages=True)
+    b, xb, yb = S.spectral_conv2d_ref(x, wt, mx, my, "fft", return_stages=True)
+    assert rel(xa, xb) < 1e-13
+    assert rel(ya, yb) < 1e-13
+    assert rel(a, b) < 1e-13
+
+
+def test_1d_dft_and_fft_paths_agree():
+    rng = np.random.default_rng(10)
+    x = rng.standard_normal((3, 4, 256))
+    wt = rand_c(rng, (20, 4, 5))
+    assert rel(S.spectral_conv1d_ref(x, wt, 20, "dft"), S.spectral_conv1d_ref(x, wt, 20, "fft")) < 1e-13
+
+
+@pytest.mark.parametrize("h,w,mx,my", [(4, 4, 1, 2), (8, 4, 2, 3), (4, 8, 2, 5)])
+def test_loops_twin_2d(h, w, mx, my):
+    rng = np.random.default_rng(h * w)
+    x = rng.uniform(-1, 1, (2, 2, h, w))
+    wt = rand_c(rng, (2, mx, my, 2, 3))
+    np.testing.assert_allclose(S.spectral_conv2d_ref(x, wt, mx, my),
+                               S.spectral_conv2d_loops(x, wt, mx, my), atol=1e-12)
+
+
+def test_loops_twin_1d():
+    rng = np.random.default_rng(1)
+    x = rng.standard_normal((2, 3, 16))
+    wt = rand_c(rng, (9, 3, 2))
+    np.testing.assert_allclose(S.spectral_conv1d_ref(x, wt, 9), S.spectral_conv1d_loops(x, wt, 9), atol=1e-12)
+
+
+def test_shape_checks():
+    x = np.zeros((1, 1, 8, 8))
+    with pytest.raises(ValueError):
+        S.spectral_conv2d_ref(x, np.zeros((2, 5, 2, 1, 1)), 5, 2)     # 2*mx > H
+    with pytest.raises(ValueError):
+        S.spectral_conv2d_ref(x, np.zeros((2, 2, 6, 1, 1)), 2, 6)     # my > W/2+1
+
+
+# --------------------------------------------------------------------------
+# Planted mistakes: each one must be caught by at least one pin above
+# --------------------------------------------------------------------------
+
+def _pins_pass():
+    """Run a compact set of pins against the (possibly mutated) oracle."""
+    checks = []
+    checks.append(inband_error(16, 16, 4, 5, 3, 2, 0.7 - 0.4j) < 1e-12)
+    checks.append(inband_error(16, 16, 4, 5, 12, 2, 0.7 - 0.4j) < 1e-12)
+    rng = np.random.default_rng(0)
+    x = rng.uniform(-1, 1, (1, 2, 8, 8))
+    out = S.spectral_conv2d_ref(x, identity_weight(4, 5, 2), 4, 5)
+    checks.append(np.max(np.abs(out - x)) < 1e-12)
+    xo = np.ones((1, 1, 8, 8))
+    checks.append(np.max(np.abs(S.spectral_conv2d_ref(xo, single_mode_weight(2, 5, 0, 0, 0, 1j), 2, 5))) < 1e-12)
+    # convolution theorem with a non-symmetric channel coupling
+    h = w = 8
+    x = rng.uniform(-1, 1, (1, 3, h, w))
+    k = rng.standard_normal((3, 3, h, w))
+    spec = np.fft.rfft2(k, axes=(-2, -1))
+    kx = np.concatenate([np.arange(4), 4 + np.arange(4)])
+    wt = np.transpose(spec[:, :, kx, :5], (2, 3, 0, 1)).reshape(2, 4, 5, 3, 3)
+    checks.append(np.max(np.abs(S.spectral_conv2d_ref(x, wt, 4, 5) - circular_conv2d_direct(x, k))) < 1e-10)
+    return all(checks)
+
+
+def test_pins_pass_on_clean_oracle():
+    assert _pins_pass()
+
+
+def test_planted_mistakes(monkeypatch):
+    import contextlib
+
+    mutations = []
+
+    def flip_forward_sign(n, rows, cols, sign, _orig=S.dft_matrix):
+        return _orig(n, rows, cols, -sign)
+    mutations.append(("dft_matrix", flip_forward_sign))
+
+    def conj_mix(xh, weight, _orig=S.mix_2d):
+        return _orig(xh, np.conj(weight))
+    mutations.append(("mix_2d", conj_mix))
+
+    def transposed_mix(xh, weight):
+        return np.einsum("bisrk,srkoi->bosrk", np.asarray(xh, complex), np.asarray(weight, complex))
+    mutations.append(("mix_2d", transposed_mix))
+
+    def shifted_block1(h, mx, _orig=S.kept_kx):
+        k = _orig(h, mx).copy()
+        k[mx:] = (k[mx:] + 1) % h
+        return k
+    mutations.append(("kept_kx", shifted_block1))
+
+    def all_twos(w, my):
+        return np.full(my, 2.0)
+    mutations.append(("c2r_weights", all_twos))
+
+    for name, fn in mutations:
+        with monkeypatch.context() as m:
+            m.setattr(S, name, fn)
+            try:
+                caught = not _pins_pass()
+            except Exception:
+                caught = True
+        assert caught, f"planted mistake in {name} ({fn.__name__}) was not caught"
