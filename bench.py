@@ -1,0 +1,258 @@
+#!/usr/bin/env python3
+"""Benchmark of libfno's spectral convolution on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c3] [--variant fused|unfused]
+
+One step = one full spectral-convolution call (forward pruned FFT, per-mode
+channel mix, inverse pruned FFT) over one batch of synthetic inputs already
+resident in device memory.  Default workload: the 128x128 grid shaped like the
+TurboFNO blog's PDE step (B=32, Cin=Cout=64, modes 32x32).  Buffer sets
+(x, out) rotate so repeated calls cannot be served from the 256 MiB
+last-level cache when one set is larger than it.
+
+Prints ONE JSON line.  `value` is compulsory bytes (x + W + out) per second
+in GB/s; the line also carries calls/s, the fraction of the 8 TB/s HBM peak,
+a `roofline` entry for the longest-running kernel (its algorithmic bytes per
+launch over its average launch time, timed with HIP events recorded by the
+library around each kernel inside the timed region) and a `cpu_baseline`
+entry: the fp64 CPU oracle timed on this host on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from fft_spectral_convolution_amd.inputs import CONFIGS, make_inputs  # noqa: E402
+
+
+# Algorithmic bytes each kernel must move per launch (read once + write once),
+# by kernel name; see the design doc for the per-unit figures.
+def kernel_bytes(name: str, cfg) -> int:
+    c8 = 8
+    if cfg.kind == "1d":
+        n_in = cfg.B * cfg.Cin * cfg.W * 4
+        n_out = cfg.B * cfg.Cout * cfg.W * 4
+        xh = cfg.B * cfg.Cin * cfg.my * c8
+        yh = cfg.B * cfg.Cout * cfg.my * c8
+        wb = cfg.my * cfg.Cin * cfg.Cout * c8
+        r_in = r_out = 0
+    else:
+        m = 2 * cfg.mx * cfg.my
+        n_in = cfg.B * cfg.Cin * cfg.H * cfg.W * 4
+        n_out = cfg.B * cfg.Cout * cfg.H * cfg.W * 4
+        xh = cfg.B * cfg.Cin * m * c8
+        yh = cfg.B * cfg.Cout * m * c8
+        wb = m * cfg.Cin * cfg.Cout * c8
+        r_in = cfg.B * cfg.Cin * cfg.H * cfg.my * c8
+        r_out = cfg.B * cfg.Cout * cfg.H * cfg.my * c8
+    table = {
+        "rows_fwd": n_in + (r_in if cfg.kind == "2d" else xh),
+        "cols_fwd": r_in + xh,
+        "mix_valu": xh + wb + yh,
+        "mix_mfma": xh + wb + yh,
+        "cols_inv": yh + r_out,
+        "rows_inv": (r_out if cfg.kind == "2d" else yh) + n_out,
+        "fwd2d": n_in + xh,
+        "inv2d": yh + n_out,
+        "fused2d": n_in + wb + n_out,
+        "fused1d": n_in + wb + n_out,
+    }
+    return table[name]
+
+
+def load_traffic(kernel: str, workload: str):
+    """Measured HBM bytes per launch from committed rocprofv3 counter runs, if
+    they were taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+        entry = rec.get(workload, {}).get(kernel)
+        if not entry:
+            return None
+        import hashlib
+        h = hashlib.sha256()
+        for src in sorted(entry["sources"]):
+            with open(os.path.join(ROOT, src), "rb") as f:
+                h.update(f.read())
+        if h.hexdigest() != entry["sources_sha256"]:
+            return None
+        return int(entry["bytes_per_launch"])
+    except Exception:
+        return None
+
+
+def cpu_baseline(cfg, x, w, budget_s: float = 12.0):
+    """Time the fp64 oracle (as it stands) on this host on a bounded sample."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([d.get("num_threads", 1) for d in threadpool_info()] + [1])
+    except Exception:
+        threads = 1
+    # one batch item first, to size the sample
+    def call(nb):
+        if cfg.kind == "1d":
+            return oracle.spectral_conv1d_ref(x[:nb], w, cfg.my)
+        return oracle.spectral_conv2d_ref(x[:nb], w, cfg.mx, cfg.my)
+
+    t0 = time.perf_counter()
+    call(1)
+    t1 = time.perf_counter() - t0
+    nb = int(max(1, min(cfg.B, budget_s / max(t1, 1e-3))))
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        call(nb)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s * 0.5 or reps >= 3:
+            break
+    per_item = el / (reps * nb)
+    call_time = per_item * cfg.B
+    return {
+        "value": round(cfg.compulsory_bytes / call_time / 1e9, 6),
+        "unit": "GB/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"{reps} oracle call(s) on {nb} of {cfg.B} batch items of the same workload "
+                   f"({el:.1f} s total); scaled to the full batch: {call_time:.3f} s per layer call"),
+        "calls_per_s": round(1.0 / call_time, 6),
+        "os_cpu_count": os.cpu_count(),
+        "affinity_cpus": len(os.sched_getaffinity(0)),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="c3", choices=sorted(CONFIGS))
+    ap.add_argument("--variant", default="fused", choices=["fused", "unfused"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the batch would shard across GPUs with W replicated; not built).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import fft_spectral_convolution_amd as fno
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cfg = CONFIGS[args.workload]
+    x_np, w_np = make_inputs(cfg, 0)
+
+    # enough (x, out) sets that the rotation exceeds the 256 MiB last-level cache
+    set_bytes = 4 * (np.prod(cfg.x_shape) + np.prod(cfg.out_shape))
+    nsets = int(max(1, min(4, -(-3 * 256 * 2**20 // set_bytes))))
+    xs = [torch.from_numpy(x_np).to(dev)]
+    for _ in range(nsets - 1):
+        xs.append(xs[0].clone())
+    outs = [torch.empty(cfg.out_shape, dtype=torch.float32, device=dev) for _ in range(nsets)]
+    w = torch.from_numpy(w_np).to(dev)
+
+    if cfg.kind == "1d":
+        fn = fno.fno_spectral_conv1d if args.variant == "fused" else fno.fno_spectral_conv1d_unfused
+        step = lambda i: fn(xs[i % nsets], w, cfg.my, out=outs[i % nsets])
+    else:
+        fn = fno.fno_spectral_conv2d if args.variant == "fused" else fno.fno_spectral_conv2d_unfused
+        step = lambda i: fn(xs[i % nsets], w, cfg.mx, cfg.my, out=outs[i % nsets])
+
+    stream = torch.cuda.current_stream(dev)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    kernels = fno.fno_last_kernels()
+    nk = len(kernels)
+    # events recorded by the library around each kernel of every timed step
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nk + 1)] for _ in range(args.steps)]
+    for row in evs:                      # torch creates the HIP event on first record
+        for e in row:
+            e.record(stream)
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record(stream)
+    for i in range(args.steps):
+        fno.fno_set_timing_events(evs[i])
+        step(i)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    fno.fno_set_timing_events(None)
+
+    ms_per_step = start.elapsed_time(stop) / args.steps
+    per_kernel_ms = [float(np.mean([evs[i][k].elapsed_time(evs[i][k + 1]) for i in range(args.steps)]))
+                     for k in range(nk)]
+    dom = int(np.argmax(per_kernel_ms))
+    dom_name = kernels[dom]
+    dom_bytes = kernel_bytes(dom_name, cfg)
+    achieved = dom_bytes / (per_kernel_ms[dom] * 1e-3) / 1e9
+    traffic = load_traffic(dom_name, cfg.name)
+
+    gbs = cfg.compulsory_bytes / (ms_per_step * 1e-3) / 1e9
+    line = {
+        "metric": "spectral-conv GB/s (HBM % of peak) and layer calls/s vs fp64 CPU oracle",
+        "value": round(gbs, 3),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{cfg.name}: {cfg.describe()}",
+            "variant": args.variant,
+            "x_dist": cfg.dist,
+            "compulsory_bytes": cfg.compulsory_bytes,
+            "buffer_sets": nsets,
+        },
+        "calls_per_s": round(1e3 / ms_per_step, 3),
+        "hbm_pct": round(100.0 * gbs / HBM_PEAK_GBS, 3),
+        "wall_s_timed": round(wall, 4),
+        "kernels": {k: round(t * 1e3, 3) for k, t in zip(kernels, per_kernel_ms)},
+        "kernels_unit": "us per launch (HIP events)",
+        "roofline": {
+            "kernel": dom_name,
+            "bound": "hbm",
+            "achieved": round(achieved, 3),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 5),
+            "traffic": traffic,
+            "algorithmic_bytes": dom_bytes,
+            "avg_launch_us": round(per_kernel_ms[dom] * 1e3, 3),
+        },
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(cfg, x_np, w_np, args.cpu_budget)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

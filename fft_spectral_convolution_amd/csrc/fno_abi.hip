@@ -1,0 +1,509 @@
+// C ABI of libfno: argument validation, per-device state (twiddle table and
+// internal workspace), and the choice of schedule for each call.
+//
+// Validation follows the statement of the problem in the TurboFNO blog
+// (section 3.3: contiguous input, power-of-two last dimension) and the
+// truncation rule of section 2.2 (kx in [0,mx) u [H-mx,H), ky < my, so
+// 2*mx <= H and my <= W/2+1 keep the two kx corners disjoint and inside the
+// half spectrum).  Everything is checked before anything is enqueued.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <mutex>
+#include <vector>
+
+#include "../../include/fno.h"
+#include "fno_device.hpp"
+#include "fno_internal.hpp"
+
+namespace fno {
+namespace {
+
+constexpr int kVersion = 100;   // 0.1.0
+
+thread_local int g_last_hip_error = 0;
+
+struct DeviceState {
+    bool init = false;
+    float2* twiddle = nullptr;     // kNMax entries exp(-2 pi i m / kNMax)
+    void* ws = nullptr;            // internal grow-only workspace
+    size_t ws_bytes = 0;
+};
+
+std::mutex g_mutex;
+std::vector<DeviceState> g_devices;
+
+// Optional per-kernel event recording (fno_set_timing_events).
+constexpr int kMaxKernels = 16;
+struct Recorder {
+    void** events = nullptr;
+    int n_events = 0;
+    int k = 0;
+    const char* names[kMaxKernels] = {};
+    int count = 0;
+    const char* last_names[kMaxKernels] = {};
+    int last_count = 0;
+};
+thread_local Recorder g_rec;
+
+void rec_begin() {
+    g_rec.k = 0;
+    g_rec.count = 0;
+}
+
+// Call right before launching a kernel on stream s.
+void rec_kernel(const char* name, hipStream_t s) {
+    if (g_rec.events && g_rec.k < g_rec.n_events)
+        (void)hipEventRecord(static_cast<hipEvent_t>(g_rec.events[g_rec.k]), s);
+    if (g_rec.count < kMaxKernels) g_rec.names[g_rec.count++] = name;
+    ++g_rec.k;
+}
+
+// Call after the last kernel of a successful call.
+int rec_end(hipStream_t s, int rc) {
+    if (rc != 0) return rc;
+    if (g_rec.events && g_rec.k < g_rec.n_events)
+        (void)hipEventRecord(static_cast<hipEvent_t>(g_rec.events[g_rec.k]), s);
+    for (int i = 0; i < g_rec.count; ++i) g_rec.last_names[i] = g_rec.names[i];
+    g_rec.last_count = g_rec.count;
+    return rc;
+}
+
+int hip_fail(hipError_t e) {
+    g_last_hip_error = (int)e;
+    return FNO_ERR_HIP;
+}
+
+bool is_pow2(int v) { return v > 0 && (v & (v - 1)) == 0; }
+
+int ilog2(int v) {
+    int l = 0;
+    while ((1 << l) < v) ++l;
+    return l;
+}
+
+bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+
+bool overlap(const void* a, size_t abytes, const void* b, size_t bbytes) {
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+    return a0 < b0 + bbytes && b0 < a0 + abytes;
+}
+
+// Per-device twiddle table, built in double precision with the exact integer
+// angle index m and rounded once to float.
+int device_state(DeviceState** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e);
+    std::lock_guard<std::mutex> lock(g_mutex);
+    if ((int)g_devices.size() <= dev) g_devices.resize(dev + 1);
+    DeviceState& st = g_devices[dev];
+    if (!st.init) {
+        std::vector<float2> host(kNMax);
+        for (int m = 0; m < kNMax; ++m) {
+            const double ang = 2.0 * M_PI * (double)m / (double)kNMax;
+            host[m] = make_float2((float)std::cos(ang), (float)(-std::sin(ang)));
+        }
+        void* d = nullptr;
+        e = hipMalloc(&d, sizeof(float2) * kNMax);
+        if (e != hipSuccess) return e == hipErrorOutOfMemory ? FNO_ERR_NOMEM : hip_fail(e);
+        e = hipMemcpy(d, host.data(), sizeof(float2) * kNMax, hipMemcpyHostToDevice);
+        if (e != hipSuccess) {
+            (void)hipFree(d);
+            return hip_fail(e);
+        }
+        st.twiddle = static_cast<float2*>(d);
+        st.init = true;
+    }
+    *out = &st;
+    return FNO_OK;
+}
+
+// Grow the internal workspace of the current device to at least `bytes`.
+int internal_workspace(DeviceState* st, size_t bytes, void** ws) {
+    std::lock_guard<std::mutex> lock(g_mutex);
+    if (bytes == 0) {
+        *ws = nullptr;
+        return FNO_OK;
+    }
+    if (st->ws_bytes < bytes) {
+        if (st->ws) {
+            // in-flight work may still read the old buffer
+            hipError_t e = hipDeviceSynchronize();
+            if (e != hipSuccess) return hip_fail(e);
+            (void)hipFree(st->ws);
+            st->ws = nullptr;
+            st->ws_bytes = 0;
+        }
+        void* d = nullptr;
+        hipError_t e = hipMalloc(&d, bytes);
+        if (e != hipSuccess) {
+            (void)hipGetLastError();
+            return e == hipErrorOutOfMemory ? FNO_ERR_NOMEM : hip_fail(e);
+        }
+        st->ws = d;
+        st->ws_bytes = bytes;
+    }
+    *ws = st->ws;
+    return FNO_OK;
+}
+
+size_t align_up(size_t v) { return (v + 255) & ~size_t(255); }
+
+// ---------------------------------------------------------------------------
+// validation
+// ---------------------------------------------------------------------------
+
+int check_dims_2d(int B, int C, int H, int W, int mx, int my) {
+    if (B < 1 || C < 1) return FNO_ERR_SHAPE;
+    if (!is_pow2(H) || !is_pow2(W) || H < 2 || W < 2 || H > kNMax || W > kNMax) return FNO_ERR_SHAPE;
+    if (mx < 1 || 2 * mx > H || my < 1 || my > W / 2 + 1) return FNO_ERR_MODES;
+    return FNO_OK;
+}
+
+int check_dims_1d(int B, int C, int N, int modes) {
+    if (B < 1 || C < 1) return FNO_ERR_SHAPE;
+    if (!is_pow2(N) || N < 2 || N > kNMax) return FNO_ERR_SHAPE;
+    if (modes < 1 || modes > N / 2 + 1) return FNO_ERR_MODES;
+    return FNO_OK;
+}
+
+int check_conv(const float* x, const void* w, const float* out, size_t xbytes, size_t wbytes, size_t obytes) {
+    if (!x || !w || !out) return FNO_ERR_NULL;
+    if (misaligned(x) || misaligned(w) || misaligned(out)) return FNO_ERR_ALIGN;
+    if (overlap(x, xbytes, out, obytes) || overlap(w, wbytes, out, obytes)) return FNO_ERR_ALIAS;
+    return FNO_OK;
+}
+
+Shape2d make2d(int B, int Cin, int Cout, int H, int W, int mx, int my) {
+    Shape2d s;
+    s.B = B; s.Cin = Cin; s.Cout = Cout; s.H = H; s.W = W; s.mx = mx; s.my = my;
+    s.log2H = ilog2(H); s.log2W = ilog2(W);
+    return s;
+}
+
+// ---------------------------------------------------------------------------
+// schedules
+// ---------------------------------------------------------------------------
+
+// Unfused: rows_fwd -> cols_fwd -> mix -> cols_inv -> rows_inv, the spectra in
+// workspace.  Layout: [R or R' (shared)] [xh] [yh].
+size_t unfused_ws_2d(const Shape2d& s) {
+    const size_t rmax = (size_t)s.B * (size_t)(s.Cin > s.Cout ? s.Cin : s.Cout) * s.H * s.my * sizeof(float2);
+    const size_t m = (size_t)2 * s.mx * s.my;
+    return align_up(rmax) + align_up((size_t)s.B * s.Cin * m * sizeof(float2)) +
+           align_up((size_t)s.B * s.Cout * m * sizeof(float2));
+}
+
+int run_forward2d(const Shape2d& s, int64_t C, const float* x, float2* xh, float2* r, const float2* tw,
+                  hipStream_t st) {
+    const float scale = (float)(1.0 / std::sqrt((double)s.H * (double)s.W));
+    rec_kernel("rows_fwd", st);
+    hipError_t e = launch_rows_fwd(x, r, s.B * C * s.H, s.log2W, s.my, s.my, 1.0f, tw, st);
+    if (e != hipSuccess) return hip_fail(e);
+    rec_kernel("cols_fwd", st);
+    e = launch_cols_fwd(r, xh, s.B * C, s.log2H, s.mx, s.my, scale, tw, st);
+    if (e != hipSuccess) return hip_fail(e);
+    return FNO_OK;
+}
+
+int run_inverse2d(const Shape2d& s, int64_t C, const float2* yh, float* out, float2* r, const float2* tw,
+                  hipStream_t st) {
+    const float scale = (float)(1.0 / std::sqrt((double)s.H * (double)s.W));
+    rec_kernel("cols_inv", st);
+    hipError_t e = launch_cols_inv(yh, r, s.B * C, s.log2H, s.mx, s.my, tw, st);
+    if (e != hipSuccess) return hip_fail(e);
+    rec_kernel("rows_inv", st);
+    e = launch_rows_inv(r, out, s.B * C * s.H, s.log2W, s.my, s.my, scale, tw, st);
+    if (e != hipSuccess) return hip_fail(e);
+    return FNO_OK;
+}
+
+int run_unfused_2d(const Shape2d& s, const float* x, const float2* w, float* out, void* ws, const float2* tw,
+                   hipStream_t st) {
+    const size_t m = (size_t)2 * s.mx * s.my;
+    const size_t rmax = (size_t)s.B * (size_t)(s.Cin > s.Cout ? s.Cin : s.Cout) * s.H * s.my * sizeof(float2);
+    char* p = static_cast<char*>(ws);
+    float2* r = reinterpret_cast<float2*>(p);
+    p += align_up(rmax);
+    float2* xh = reinterpret_cast<float2*>(p);
+    p += align_up((size_t)s.B * s.Cin * m * sizeof(float2));
+    float2* yh = reinterpret_cast<float2*>(p);
+    int rc = run_forward2d(s, s.Cin, x, xh, r, tw, st);
+    if (rc) return rc;
+    rec_kernel("mix_valu", st);
+    hipError_t e = launch_mix_valu(xh, w, yh, s.B, s.Cin, s.Cout, (int64_t)m, st);
+    if (e != hipSuccess) return hip_fail(e);
+    return run_inverse2d(s, s.Cout, yh, out, r, tw, st);
+}
+
+size_t unfused_ws_1d(int64_t B, int64_t Cin, int64_t Cout, int modes) {
+    return align_up((size_t)B * Cin * modes * sizeof(float2)) + align_up((size_t)B * Cout * modes * sizeof(float2));
+}
+
+int run_unfused_1d(int64_t B, int64_t Cin, int64_t Cout, int N, int modes, const float* x, const float2* w,
+                   float* out, void* ws, const float2* tw, hipStream_t st) {
+    const float scale = (float)(1.0 / std::sqrt((double)N));
+    char* p = static_cast<char*>(ws);
+    float2* xh = reinterpret_cast<float2*>(p);
+    p += align_up((size_t)B * Cin * modes * sizeof(float2));
+    float2* yh = reinterpret_cast<float2*>(p);
+    const int l2 = ilog2(N);
+    rec_kernel("rows_fwd", st);
+    hipError_t e = launch_rows_fwd(x, xh, B * Cin, l2, modes, modes, scale, tw, st);
+    if (e != hipSuccess) return hip_fail(e);
+    rec_kernel("mix_valu", st);
+    e = launch_mix_valu(xh, w, yh, B, Cin, Cout, modes, st);
+    if (e != hipSuccess) return hip_fail(e);
+    rec_kernel("rows_inv", st);
+    e = launch_rows_inv(yh, out, B * Cout, l2, modes, modes, scale, tw, st);
+    if (e != hipSuccess) return hip_fail(e);
+    return FNO_OK;
+}
+
+// Fastest schedule for the shape.  Every shape currently runs the staged
+// kernels; the workspace size follows the chosen schedule.
+size_t best_ws_2d(const Shape2d& s) { return unfused_ws_2d(s); }
+
+int run_best_2d(const Shape2d& s, const float* x, const float2* w, float* out, void* ws, const float2* tw,
+                hipStream_t st) {
+    return run_unfused_2d(s, x, w, out, ws, tw, st);
+}
+
+int conv2d_common(const float* x, const void* w, float* out, int B, int Cin, int Cout, int H, int W, int mx,
+                  int my, void* user_ws, size_t user_ws_bytes, bool use_user_ws, bool unfused, void* stream) {
+    int rc = check_dims_2d(B, Cin, H, W, mx, my);
+    if (rc) return rc;
+    if (Cout < 1) return FNO_ERR_SHAPE;
+    const size_t xbytes = (size_t)B * Cin * H * W * sizeof(float);
+    const size_t obytes = (size_t)B * Cout * H * W * sizeof(float);
+    const size_t wbytes = (size_t)2 * mx * my * Cin * Cout * sizeof(float2);
+    rc = check_conv(x, w, out, xbytes, wbytes, obytes);
+    if (rc) return rc;
+    const Shape2d s = make2d(B, Cin, Cout, H, W, mx, my);
+    const size_t need = unfused ? unfused_ws_2d(s) : best_ws_2d(s);
+    void* ws = user_ws;
+    if (use_user_ws) {
+        if (user_ws_bytes < need || (need > 0 && !user_ws)) return FNO_ERR_WORKSPACE;
+        if (need > 0 && (reinterpret_cast<uintptr_t>(user_ws) & 255u)) return FNO_ERR_ALIGN;
+    }
+    DeviceState* st = nullptr;
+    rc = device_state(&st);
+    if (rc) return rc;
+    if (!use_user_ws) {
+        rc = internal_workspace(st, need, &ws);
+        if (rc) return rc;
+    }
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    const float2* wc = static_cast<const float2*>(w);
+    rec_begin();
+    if (unfused) return rec_end(hs, run_unfused_2d(s, x, wc, out, ws, st->twiddle, hs));
+    return rec_end(hs, run_best_2d(s, x, wc, out, ws, st->twiddle, hs));
+}
+
+int conv1d_common(const float* x, const void* w, float* out, int B, int Cin, int Cout, int N, int modes,
+                  void* user_ws, size_t user_ws_bytes, bool use_user_ws, bool unfused, void* stream) {
+    (void)unfused;
+    int rc = check_dims_1d(B, Cin, N, modes);
+    if (rc) return rc;
+    if (Cout < 1) return FNO_ERR_SHAPE;
+    const size_t xbytes = (size_t)B * Cin * N * sizeof(float);
+    const size_t obytes = (size_t)B * Cout * N * sizeof(float);
+    const size_t wbytes = (size_t)modes * Cin * Cout * sizeof(float2);
+    rc = check_conv(x, w, out, xbytes, wbytes, obytes);
+    if (rc) return rc;
+    const size_t need = unfused_ws_1d(B, Cin, Cout, modes);
+    void* ws = user_ws;
+    if (use_user_ws) {
+        if (user_ws_bytes < need || !user_ws) return FNO_ERR_WORKSPACE;
+        if (reinterpret_cast<uintptr_t>(user_ws) & 255u) return FNO_ERR_ALIGN;
+    }
+    DeviceState* st = nullptr;
+    rc = device_state(&st);
+    if (rc) return rc;
+    if (!use_user_ws) {
+        rc = internal_workspace(st, need, &ws);
+        if (rc) return rc;
+    }
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    rec_begin();
+    return rec_end(hs, run_unfused_1d(B, Cin, Cout, N, modes, x, static_cast<const float2*>(w), out, ws,
+                                      st->twiddle, hs));
+}
+
+}  // namespace
+}  // namespace fno
+
+using namespace fno;
+
+extern "C" {
+
+int fno_version(void) { return kVersion; }
+
+const char* fno_status_string(int status) {
+    switch (status) {
+        case FNO_OK: return "ok";
+        case FNO_ERR_NULL: return "a required pointer is NULL";
+        case FNO_ERR_SHAPE: return "a size is out of range or not a power of two";
+        case FNO_ERR_MODES: return "mode counts out of range (need 1<=mx, 2*mx<=H, 1<=my<=W/2+1)";
+        case FNO_ERR_ALIAS: return "output overlaps an input";
+        case FNO_ERR_ALIGN: return "a pointer is not suitably aligned";
+        case FNO_ERR_NOMEM: return "device workspace allocation failed";
+        case FNO_ERR_HIP: return "a HIP runtime call or kernel launch failed";
+        case FNO_ERR_WORKSPACE: return "caller workspace missing or too small";
+        default: return "unknown status";
+    }
+}
+
+int fno_last_hip_error(void) { return g_last_hip_error; }
+
+int fno_set_timing_events(void** events, int n_events) {
+    g_rec.events = (events && n_events > 0) ? events : nullptr;
+    g_rec.n_events = g_rec.events ? n_events : 0;
+    return FNO_OK;
+}
+
+int fno_last_kernel_count(void) { return g_rec.last_count; }
+
+const char* fno_last_kernel_name(int k) {
+    return (k >= 0 && k < g_rec.last_count) ? g_rec.last_names[k] : "";
+}
+
+int fno_spectral_conv2d(const float* x, const void* w, float* out, int B, int Cin, int Cout, int H, int W, int mx,
+                        int my, void* stream) {
+    return conv2d_common(x, w, out, B, Cin, Cout, H, W, mx, my, nullptr, 0, false, false, stream);
+}
+
+int fno_spectral_conv2d_unfused(const float* x, const void* w, float* out, int B, int Cin, int Cout, int H, int W,
+                                int mx, int my, void* stream) {
+    return conv2d_common(x, w, out, B, Cin, Cout, H, W, mx, my, nullptr, 0, false, true, stream);
+}
+
+int fno_spectral_conv2d_ws(const float* x, const void* w, float* out, int B, int Cin, int Cout, int H, int W,
+                           int mx, int my, void* workspace, size_t ws_bytes, void* stream) {
+    return conv2d_common(x, w, out, B, Cin, Cout, H, W, mx, my, workspace, ws_bytes, true, false, stream);
+}
+
+int fno_spectral_conv1d(const float* x, const void* w, float* out, int B, int Cin, int Cout, int N, int modes,
+                        void* stream) {
+    return conv1d_common(x, w, out, B, Cin, Cout, N, modes, nullptr, 0, false, false, stream);
+}
+
+int fno_spectral_conv1d_unfused(const float* x, const void* w, float* out, int B, int Cin, int Cout, int N,
+                                int modes, void* stream) {
+    return conv1d_common(x, w, out, B, Cin, Cout, N, modes, nullptr, 0, false, true, stream);
+}
+
+int fno_spectral_conv1d_ws(const float* x, const void* w, float* out, int B, int Cin, int Cout, int N, int modes,
+                           void* workspace, size_t ws_bytes, void* stream) {
+    return conv1d_common(x, w, out, B, Cin, Cout, N, modes, workspace, ws_bytes, true, false, stream);
+}
+
+size_t fno_workspace_size_2d(int B, int Cin, int Cout, int H, int W, int mx, int my) {
+    if (check_dims_2d(B, Cin, H, W, mx, my) || Cout < 1) return 0;
+    return best_ws_2d(make2d(B, Cin, Cout, H, W, mx, my));
+}
+
+size_t fno_workspace_size_1d(int B, int Cin, int Cout, int N, int modes) {
+    if (check_dims_1d(B, Cin, N, modes) || Cout < 1) return 0;
+    return unfused_ws_1d(B, Cin, Cout, modes);
+}
+
+int fno_forward2d(const float* x, void* xh, int B, int C, int H, int W, int mx, int my, void* stream) {
+    int rc = check_dims_2d(B, C, H, W, mx, my);
+    if (rc) return rc;
+    if (!x || !xh) return FNO_ERR_NULL;
+    if (misaligned(x) || misaligned(xh)) return FNO_ERR_ALIGN;
+    const size_t xbytes = (size_t)B * C * H * W * sizeof(float);
+    const size_t hbytes = (size_t)B * C * 2 * mx * my * sizeof(float2);
+    if (overlap(x, xbytes, xh, hbytes)) return FNO_ERR_ALIAS;
+    const Shape2d s = make2d(B, C, C, H, W, mx, my);
+    DeviceState* st = nullptr;
+    rc = device_state(&st);
+    if (rc) return rc;
+    void* ws = nullptr;
+    rc = internal_workspace(st, (size_t)B * C * H * my * sizeof(float2), &ws);
+    if (rc) return rc;
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    rec_begin();
+    return rec_end(hs, run_forward2d(s, C, x, static_cast<float2*>(xh), static_cast<float2*>(ws), st->twiddle, hs));
+}
+
+int fno_inverse2d(const void* yh, float* out, int B, int C, int H, int W, int mx, int my, void* stream) {
+    int rc = check_dims_2d(B, C, H, W, mx, my);
+    if (rc) return rc;
+    if (!yh || !out) return FNO_ERR_NULL;
+    if (misaligned(yh) || misaligned(out)) return FNO_ERR_ALIGN;
+    const size_t obytes = (size_t)B * C * H * W * sizeof(float);
+    const size_t hbytes = (size_t)B * C * 2 * mx * my * sizeof(float2);
+    if (overlap(out, obytes, yh, hbytes)) return FNO_ERR_ALIAS;
+    const Shape2d s = make2d(B, C, C, H, W, mx, my);
+    DeviceState* st = nullptr;
+    rc = device_state(&st);
+    if (rc) return rc;
+    void* ws = nullptr;
+    rc = internal_workspace(st, (size_t)B * C * H * my * sizeof(float2), &ws);
+    if (rc) return rc;
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    rec_begin();
+    return rec_end(hs, run_inverse2d(s, C, static_cast<const float2*>(yh), out, static_cast<float2*>(ws),
+                                     st->twiddle, hs));
+}
+
+int fno_mix(const void* xh, const void* w, void* yh, int B, int Cin, int Cout, int M, void* stream) {
+    if (B < 1 || Cin < 1 || Cout < 1 || M < 1) return FNO_ERR_SHAPE;
+    if (!xh || !w || !yh) return FNO_ERR_NULL;
+    if (misaligned(xh) || misaligned(w) || misaligned(yh)) return FNO_ERR_ALIGN;
+    const size_t ybytes = (size_t)B * Cout * M * sizeof(float2);
+    if (overlap(xh, (size_t)B * Cin * M * sizeof(float2), yh, ybytes) ||
+        overlap(w, (size_t)M * Cin * Cout * sizeof(float2), yh, ybytes))
+        return FNO_ERR_ALIAS;
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    rec_begin();
+    rec_kernel("mix_valu", hs);
+    hipError_t e = launch_mix_valu(static_cast<const float2*>(xh), static_cast<const float2*>(w),
+                                   static_cast<float2*>(yh), B, Cin, Cout, M, hs);
+    return rec_end(hs, e == hipSuccess ? FNO_OK : hip_fail(e));
+}
+
+int fno_forward1d(const float* x, void* xh, int B, int C, int N, int modes, void* stream) {
+    int rc = check_dims_1d(B, C, N, modes);
+    if (rc) return rc;
+    if (!x || !xh) return FNO_ERR_NULL;
+    if (misaligned(x) || misaligned(xh)) return FNO_ERR_ALIGN;
+    if (overlap(x, (size_t)B * C * N * sizeof(float), xh, (size_t)B * C * modes * sizeof(float2)))
+        return FNO_ERR_ALIAS;
+    DeviceState* st = nullptr;
+    rc = device_state(&st);
+    if (rc) return rc;
+    const float scale = (float)(1.0 / std::sqrt((double)N));
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    rec_begin();
+    rec_kernel("rows_fwd", hs);
+    hipError_t e = launch_rows_fwd(x, static_cast<float2*>(xh), (int64_t)B * C, ilog2(N), modes, modes, scale,
+                                   st->twiddle, hs);
+    return rec_end(hs, e == hipSuccess ? FNO_OK : hip_fail(e));
+}
+
+int fno_inverse1d(const void* yh, float* out, int B, int C, int N, int modes, void* stream) {
+    int rc = check_dims_1d(B, C, N, modes);
+    if (rc) return rc;
+    if (!yh || !out) return FNO_ERR_NULL;
+    if (misaligned(yh) || misaligned(out)) return FNO_ERR_ALIGN;
+    if (overlap(out, (size_t)B * C * N * sizeof(float), yh, (size_t)B * C * modes * sizeof(float2)))
+        return FNO_ERR_ALIAS;
+    DeviceState* st = nullptr;
+    rc = device_state(&st);
+    if (rc) return rc;
+    const float scale = (float)(1.0 / std::sqrt((double)N));
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    rec_begin();
+    rec_kernel("rows_inv", hs);
+    hipError_t e = launch_rows_inv(static_cast<const float2*>(yh), out, (int64_t)B * C, ilog2(N), modes, modes,
+                                   scale, st->twiddle, hs);
+    return rec_end(hs, e == hipSuccess ? FNO_OK : hip_fail(e));
+}
+
+}  // extern "C"

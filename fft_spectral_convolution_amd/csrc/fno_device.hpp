@@ -1,0 +1,171 @@
+// Device-side building blocks of libfno: complex arithmetic, small in-register
+// DFTs and a Stockham FFT over rows held in LDS.
+//
+// Conventions: complex64 values are float2 (x = re, y = im).  SIGN = -1 is the
+// forward transform exp(-2 pi i n k / N), SIGN = +1 the unnormalised inverse
+// (TurboFNO blog, sections 2.1-2.2: row and column 1D transforms make the 2D
+// transform; FFT blog, section 2.2: R2C / C2R with the N/2+1 half spectrum).
+//
+// Twiddles W_N^m = exp(-2 pi i m / N) for the Stockham passes come from one
+// table of length kNMax that the host fills once per device in double
+// precision (angle 2 pi m / kNMax with exact integer m) and rounds to float.
+// The small radix-2/4/8/16 butterflies use the exact constants cos(pi/4),
+// cos(pi/8), sin(pi/8) written out to float precision.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+namespace fno {
+
+constexpr int kLog2NMax = 12;            // longest transform: 4096 points
+constexpr int kNMax = 1 << kLog2NMax;    // twiddle table length
+constexpr int kLdsElems = 4096;          // complex elements per LDS ping-pong buffer
+
+constexpr float kSqrtHalf = 0.70710678118654752440f;  // cos(pi/4)
+constexpr float kCosPi8 = 0.92387953251128675613f;    // cos(pi/8)
+constexpr float kSinPi8 = 0.38268343236508977173f;    // sin(pi/8)
+
+__host__ __device__ constexpr float cos16(int e) {
+    // cos(2 pi e / 16)
+    switch (e & 15) {
+        case 0: return 1.0f;
+        case 1: return kCosPi8;
+        case 2: return kSqrtHalf;
+        case 3: return kSinPi8;
+        case 4: return 0.0f;
+        case 5: return -kSinPi8;
+        case 6: return -kSqrtHalf;
+        case 7: return -kCosPi8;
+        case 8: return -1.0f;
+        case 9: return -kCosPi8;
+        case 10: return -kSqrtHalf;
+        case 11: return -kSinPi8;
+        case 12: return 0.0f;
+        case 13: return kSinPi8;
+        case 14: return kSqrtHalf;
+        default: return kCosPi8;
+    }
+}
+
+__host__ __device__ constexpr float sin16(int e) { return cos16(e - 4); }  // sin x = cos(x - pi/2)
+
+__device__ __forceinline__ float2 cadd(float2 a, float2 b) { return make_float2(a.x + b.x, a.y + b.y); }
+__device__ __forceinline__ float2 csub(float2 a, float2 b) { return make_float2(a.x - b.x, a.y - b.y); }
+__device__ __forceinline__ float2 cscale(float2 a, float s) { return make_float2(a.x * s, a.y * s); }
+__device__ __forceinline__ float2 cmul(float2 a, float2 b) {
+    // (a+bi)(c+di) = (ac-bd) + (ad+bc)i   (TurboFNO blog, section 2.2)
+    return make_float2(a.x * b.x - a.y * b.y, a.x * b.y + a.y * b.x);
+}
+__device__ __forceinline__ float2 cfma(float2 acc, float2 a, float2 b) {
+    acc.x = fmaf(a.x, b.x, acc.x);
+    acc.x = fmaf(-a.y, b.y, acc.x);
+    acc.y = fmaf(a.x, b.y, acc.y);
+    acc.y = fmaf(a.y, b.x, acc.y);
+    return acc;
+}
+
+// v * (SIGN * i)
+template <int SIGN>
+__device__ __forceinline__ float2 mul_i(float2 v) {
+    return SIGN < 0 ? make_float2(v.y, -v.x) : make_float2(-v.y, v.x);
+}
+
+// v * exp(SIGN * 2 pi i * e / 16), e a compile-time constant after unrolling.
+template <int SIGN>
+__device__ __forceinline__ float2 w16mul(float2 v, int e) {
+    e &= 15;
+    if (e == 0) return v;
+    if (e == 4) return mul_i<SIGN>(v);
+    if (e == 8) return make_float2(-v.x, -v.y);
+    if (e == 12) return mul_i<-SIGN>(v);
+    const float c = cos16(e);
+    const float s = SIGN * sin16(e);
+    return make_float2(v.x * c - v.y * s, v.x * s + v.y * c);
+}
+
+// In-register DFT of size R <= 16, natural order in and out:
+// v[k] <- sum_r v[r] exp(SIGN 2 pi i r k / R).  Radix-2 decimation in time.
+template <int R, int SIGN>
+__device__ __forceinline__ void dft(float2 (&v)[R]) {
+    static_assert(R >= 1 && R <= 16 && (R & (R - 1)) == 0, "radix must be a power of two <= 16");
+    if constexpr (R == 2) {
+        const float2 a = v[0], b = v[1];
+        v[0] = cadd(a, b);
+        v[1] = csub(a, b);
+    } else if constexpr (R > 2) {
+        constexpr int HALF = R / 2;
+        float2 e[HALF], o[HALF];
+#pragma unroll
+        for (int i = 0; i < HALF; ++i) {
+            e[i] = v[2 * i];
+            o[i] = v[2 * i + 1];
+        }
+        dft<HALF, SIGN>(e);
+        dft<HALF, SIGN>(o);
+#pragma unroll
+        for (int k = 0; k < HALF; ++k) {
+            const float2 t = w16mul<SIGN>(o[k], k * (16 / R));
+            v[k] = cadd(e[k], t);
+            v[k + HALF] = csub(e[k], t);
+        }
+    }
+}
+
+// Twiddle exp(SIGN 2 pi i m / kNMax) from the host-built table of exp(-2 pi i m / kNMax).
+template <int SIGN>
+__device__ __forceinline__ float2 table_twiddle(const float2* __restrict__ tw, int m) {
+    float2 t = tw[m];
+    if (SIGN > 0) t.y = -t.y;
+    return t;
+}
+
+// One radix-R Stockham pass (decimation in time, autosort) of an N-point
+// transform whose sub-transforms of length NS are already done.  Butterfly j
+// reads src[j + r N/R], twiddles by W_{NS R}^{r (j mod NS)}, runs a radix-R
+// DFT and writes dst[(j - j mod NS) R + j mod NS + r NS].
+template <int N, int NS, int R, int SIGN>
+__device__ __forceinline__ void stockham_pass(const float2* src, float2* dst, int j,
+                                              const float2* __restrict__ tw) {
+    constexpr int STRIDE = N / R;
+    constexpr int TW_STEP = kNMax / (NS * R);
+    float2 v[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) v[r] = src[j + r * STRIDE];
+    const int k = j & (NS - 1);
+    if constexpr (NS > 1) {
+#pragma unroll
+        for (int r = 1; r < R; ++r) v[r] = cmul(v[r], table_twiddle<SIGN>(tw, r * k * TW_STEP));
+    }
+    dft<R, SIGN>(v);
+    const int base = (j - k) * R + k;
+#pragma unroll
+    for (int r = 0; r < R; ++r) dst[base + r * NS] = v[r];
+}
+
+// Full N = 2^LOG2N point transform of `nrows` rows (row stride `ld`) held in
+// LDS buffer `a`, ping-ponging through `b`.  All threads of the block must
+// call it.  Returns the buffer that holds the result (natural order).
+template <int LOG2N, int SIGN, int DONE = 0>
+__device__ __forceinline__ float2* fft_rows_lds(float2* a, float2* b, int nrows, int ld,
+                                                const float2* __restrict__ tw, int tid, int nthr) {
+    if constexpr (DONE >= LOG2N) {
+        return a;
+    } else {
+        constexpr int REM = LOG2N - DONE;
+        constexpr int RB = REM >= 4 ? 4 : REM;
+        constexpr int R = 1 << RB;
+        constexpr int N = 1 << LOG2N;
+        constexpr int NS = 1 << DONE;
+        constexpr int J = N / R;
+        const int total = nrows * J;
+        for (int idx = tid; idx < total; idx += nthr) {
+            const int row = idx / J;
+            const int j = idx & (J - 1);
+            stockham_pass<N, NS, R, SIGN>(a + row * ld, b + row * ld, j, tw);
+        }
+        __syncthreads();
+        return fft_rows_lds<LOG2N, SIGN, DONE + RB>(b, a, nrows, ld, tw, tid, nthr);
+    }
+}
+
+}  // namespace fno

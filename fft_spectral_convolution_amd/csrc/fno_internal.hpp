@@ -1,0 +1,42 @@
+// Host-side internal interface between the C ABI (fno_abi.hip) and the kernel
+// launchers.  Not part of the public API.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+namespace fno {
+
+struct Shape2d {
+    int64_t B, Cin, Cout;
+    int H, W, mx, my;
+    int log2H, log2W;
+};
+
+struct Shape1d {
+    int64_t B, Cin, Cout;
+    int N, modes, log2N;
+};
+
+// ---- generic stage launchers (fno_generic.hip) -------------------------------
+// All return hipSuccess or the launch error.  `tw` is the device twiddle table.
+
+// Rows of length W (real) -> bins ky < my, row-major [nrows][y_ld], times scale.
+hipError_t launch_rows_fwd(const float* x, float2* y, int64_t nrows, int log2W, int my, int y_ld,
+                           float scale, const float2* tw, hipStream_t s);
+// R[nimg][H][my] -> xh[nimg][2][mx][my] (kept kx only), times scale.
+hipError_t launch_cols_fwd(const float2* r, float2* xh, int64_t nimg, int log2H, int mx, int my,
+                           float scale, const float2* tw, hipStream_t s);
+// Per-mode channel mix, VALU: yh[b][o][m] = sum_i xh[b][i][m] w[m][i][o].
+hipError_t launch_mix_valu(const float2* xh, const float2* w, float2* yh, int64_t B, int64_t Cin,
+                           int64_t Cout, int64_t M, hipStream_t s);
+// yh[nimg][2][mx][my] -> zero-filled column inverse -> R'[nimg][H][my].
+hipError_t launch_cols_inv(const float2* yh, float2* r, int64_t nimg, int log2H, int mx, int my,
+                           const float2* tw, hipStream_t s);
+// R'[nrows][y_ld] (bins ky < my) -> C2R rows of length W, times scale.
+hipError_t launch_rows_inv(const float2* y, float* out, int64_t nrows, int log2W, int my, int y_ld,
+                           float scale, const float2* tw, hipStream_t s);
+
+}  // namespace fno

@@ -1,0 +1,160 @@
+/*
+ * libfno -- Fourier-neural-operator spectral convolution on MI355X (gfx950).
+ *
+ * C ABI.  Every pointer argument named x, w, out, xh, yh or workspace is
+ * DEVICE memory on the current HIP device, owned by the caller; the library
+ * never frees caller memory.  `stream` is a hipStream_t passed as void*
+ * (NULL = the null stream).  All calls only enqueue work on `stream` and
+ * return without synchronising; a kernel fault shows up at the caller's next
+ * synchronisation.
+ *
+ * Argument checks run on the host before anything is enqueued: when a check
+ * fails the call returns a negative status and nothing runs.
+ *
+ * The operation (sources: the TurboFNO blog "FFT-GEMM-iFFT full-chain fused
+ * GPU operator", sections 1, 2.2, 3.1, 3.3 and 4.4; the "FFT for operator
+ * optimisation" blog, sections 1.2, 2.1 and 2.2):
+ *
+ *   forward, ortho:  X[b,i,kx,ky] = (HW)^-1/2 sum_{h,w} x[b,i,h,w] e^{-2 pi i (kx h/H + ky w/W)}
+ *                    for ky in [0, W/2] (real-to-complex half spectrum)
+ *   truncate:        kx in [0,mx) u [H-mx,H) and ky in [0,my).  Weight block 0
+ *                    holds kx = r, block 1 holds kx = H-mx+r, r < mx.
+ *   mix:             Y[b,o,s,r,ky] = sum_i X[b,i,s,r,ky] * w[s,r,ky,i,o]
+ *                    (plain complex product, no conjugate)
+ *   inverse, ortho:  zero-fill every other mode, complex inverse along H,
+ *                    complex-to-real inverse along W (the imaginary parts of
+ *                    the ky = 0 and ky = W/2 bins do not contribute), scaled
+ *                    by (HW)^-1/2.
+ *
+ * Layouts (row-major, contiguous, last index fastest):
+ *   x    float32   [B][Cin][H][W]         (1D: [B][Cin][N])
+ *   w    complex64 [2][mx][my][Cin][Cout] (1D: [modes][Cin][Cout])
+ *   out  float32   [B][Cout][H][W]        (1D: [B][Cout][N])
+ *   complex64 = interleaved (re, im) float32 pairs, as torch.complex64.
+ *
+ * Limits: 1 <= B, Cin, Cout; H and W powers of two with 2 <= H, W <= 4096
+ * (1D: 2 <= N <= 4096); 1 <= mx, 2*mx <= H; 1 <= my <= W/2+1
+ * (1D: 1 <= modes <= N/2+1).  x, w, out must be 16-byte aligned and x must
+ * not overlap out.  `out` is fully overwritten.
+ */
+#ifndef LIBFNO_FNO_H
+#define LIBFNO_FNO_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum fno_status {
+    FNO_OK = 0,
+    FNO_ERR_NULL = -1,       /* a required pointer is NULL */
+    FNO_ERR_SHAPE = -2,      /* a size is out of range or not a power of two */
+    FNO_ERR_MODES = -3,      /* mx / my / modes out of range */
+    FNO_ERR_ALIAS = -4,      /* x and out overlap */
+    FNO_ERR_ALIGN = -5,      /* a pointer is not 16-byte aligned */
+    FNO_ERR_NOMEM = -6,      /* the internal workspace could not be allocated */
+    FNO_ERR_HIP = -7,        /* a HIP runtime call or kernel launch failed */
+    FNO_ERR_WORKSPACE = -8   /* caller workspace missing or smaller than required */
+};
+
+/* Library version as major*10000 + minor*100 + patch. */
+int fno_version(void);
+
+/* Human-readable text for a status code (static storage, never NULL). */
+const char* fno_status_string(int status);
+
+/* The hipError_t of the last FNO_ERR_HIP on the calling thread (0 if none). */
+int fno_last_hip_error(void);
+
+/*
+ * 2D spectral convolution (TurboFNO blog, sections 1 and 2.2; FFT blog
+ * sections 2.1-2.2).  Picks the fastest implemented schedule for the shape.
+ * Uses an internal per-device workspace (grow-only, allocated on first use and
+ * kept until process exit); calls that share a device and overlap in time on
+ * different streams must use fno_spectral_conv2d_ws instead.
+ */
+int fno_spectral_conv2d(const float* x, const void* w, float* out,
+                        int B, int Cin, int Cout, int H, int W, int mx, int my,
+                        void* stream);
+
+/*
+ * 1D spectral convolution along a sequence of length N (FFT blog, section 3.2:
+ * FFT token mixing; the weight has one block because a length-N axis has no
+ * second frequency axis to truncate).  Scale N^-1/2 on each transform.
+ */
+int fno_spectral_conv1d(const float* x, const void* w, float* out,
+                        int B, int Cin, int Cout, int N, int modes, void* stream);
+
+/*
+ * Unfused schedules of the same hand-written stages, kept for ablation
+ * (TurboFNO blog, sections 1 and 2.1: FFT, GEMM and iFFT as separate passes
+ * with the spectra round-tripping through device memory).  Same arguments and
+ * results as the calls above.
+ */
+int fno_spectral_conv2d_unfused(const float* x, const void* w, float* out,
+                                int B, int Cin, int Cout, int H, int W, int mx, int my,
+                                void* stream);
+int fno_spectral_conv1d_unfused(const float* x, const void* w, float* out,
+                                int B, int Cin, int Cout, int N, int modes, void* stream);
+
+/*
+ * Bytes of caller workspace the _ws calls need for this shape (0 when the
+ * fastest schedule needs none).  Never fails; returns 0 for invalid shapes.
+ */
+size_t fno_workspace_size_2d(int B, int Cin, int Cout, int H, int W, int mx, int my);
+size_t fno_workspace_size_1d(int B, int Cin, int Cout, int N, int modes);
+
+/*
+ * As fno_spectral_conv2d / _1d, but all scratch lives in `workspace`
+ * (device memory, at least fno_workspace_size_* bytes, 256-byte aligned,
+ * caller-owned).  Returns FNO_ERR_WORKSPACE if it is too small or NULL while
+ * a non-zero size is needed.  No allocation happens inside these calls.
+ */
+int fno_spectral_conv2d_ws(const float* x, const void* w, float* out,
+                           int B, int Cin, int Cout, int H, int W, int mx, int my,
+                           void* workspace, size_t ws_bytes, void* stream);
+int fno_spectral_conv1d_ws(const float* x, const void* w, float* out,
+                           int B, int Cin, int Cout, int N, int modes,
+                           void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * Stage calls, for stage-by-stage comparison of the intermediate spectra
+ * (FFT blog, section 6.4).  The truncated spectra use the weight's mode
+ * order: xh complex64 [B][C][2][mx][my] (1D: [B][C][modes]).
+ *
+ *   fno_forward2d:  x[B][C][H][W] -> xh, ortho scale included.
+ *   fno_mix:        xh[B][Cin][M], w[M][Cin][Cout] -> yh[B][Cout][M], M modes.
+ *   fno_inverse2d:  yh[B][C][2][mx][my] -> out[B][C][H][W], ortho scale included.
+ *   fno_forward1d / fno_inverse1d: the same for sequences.
+ * fno_forward2d / fno_inverse2d use the internal workspace (see above).
+ */
+int fno_forward2d(const float* x, void* xh, int B, int C, int H, int W, int mx, int my,
+                  void* stream);
+int fno_mix(const void* xh, const void* w, void* yh, int B, int Cin, int Cout, int M,
+            void* stream);
+int fno_inverse2d(const void* yh, float* out, int B, int C, int H, int W, int mx, int my,
+                  void* stream);
+int fno_forward1d(const float* x, void* xh, int B, int C, int N, int modes, void* stream);
+int fno_inverse1d(const void* yh, float* out, int B, int C, int N, int modes, void* stream);
+
+/*
+ * Per-kernel timing for benchmarks and profilers.  While `events` is non-NULL,
+ * every convolution or stage call made on the calling thread records
+ * events[k] (a hipEvent_t, created by the caller) on its stream right before
+ * its k-th kernel and events[n] right after its last kernel, where n is the
+ * number of kernels the call launched (events beyond n_events-1 are not
+ * recorded; the call still runs).  Pass NULL to stop.  Returns FNO_OK.
+ * fno_last_kernel_count / fno_last_kernel_name report, for the calling
+ * thread's last successful call, how many kernels it launched and their
+ * names (static storage; "" for an index out of range).
+ */
+int fno_set_timing_events(void** events, int n_events);
+int fno_last_kernel_count(void);
+const char* fno_last_kernel_name(int k);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBFNO_FNO_H */

@@ -130,6 +130,22 @@ def fft_radix2(a: np.ndarray, axis: int = -1, sign: int = -1) -> np.ndarray:
     return np.moveaxis(rec(moved), -1, axis)
 
 
+def _real_times_complex(x: np.ndarray, m: np.ndarray) -> np.ndarray:
+    """x @ m for real x[..., K] and complex m[K, J], as two real matrix products."""
+    flat = np.ascontiguousarray(x, dtype=np.float64).reshape(-1, x.shape[-1])
+    re = flat @ np.ascontiguousarray(m.real)
+    im = flat @ np.ascontiguousarray(m.imag)
+    return (re + 1j * im).reshape(x.shape[:-1] + (m.shape[1],))
+
+
+def _real_part_of_product(a: np.ndarray, m: np.ndarray) -> np.ndarray:
+    """Re(a @ m) for complex a[..., K] and complex m[K, J]."""
+    flat = np.ascontiguousarray(a).reshape(-1, a.shape[-1])
+    out = np.ascontiguousarray(flat.real) @ np.ascontiguousarray(m.real)
+    out -= np.ascontiguousarray(flat.imag) @ np.ascontiguousarray(m.imag)
+    return out.reshape(a.shape[:-1] + (m.shape[1],))
+
+
 def _transform(a: np.ndarray, axis: int, sign: int, transform: str) -> np.ndarray:
     if transform == "dft":
         return dft_brute(a, axis, sign)
@@ -181,8 +197,8 @@ def forward_truncated_2d(x: np.ndarray, mx: int, my: int, transform: str = "dft"
     if transform == "dft":
         fw = dft_matrix(w, np.arange(w), np.arange(my), -1)        # [W, my]
         fh = dft_matrix(h, kx, np.arange(h), -1)                   # [2mx, H]
-        rows = x @ fw                                               # [B,C,H,my]
-        full = np.einsum("qh,bchk->bcqk", fh, rows)                # [B,C,2mx,my]
+        rows = _real_times_complex(x, fw)                          # [B,C,H,my]
+        full = fh @ rows                                           # [B,C,2mx,my]
     else:
         rows = _transform(x.astype(np.complex128), 3, -1, transform)[..., :my]
         cols = _transform(rows, 2, -1, transform)                  # [B,C,H,my]
@@ -209,8 +225,8 @@ def inverse_from_truncated_2d(yh: np.ndarray, h: int, w: int, transform: str = "
         gh = dft_matrix(h, np.arange(h), kx, +1)                   # [H, 2mx]
         gw = dft_matrix(w, np.arange(my), np.arange(w), +1)        # [my, W]
         gw = gw * c2r_weights(w, my)[:, None]
-        cols = np.einsum("hq,bcqk->bchk", gh, yq)                  # [B,C,H,my]
-        out = (cols @ gw).real
+        cols = gh @ yq                                             # [B,C,H,my]
+        out = _real_part_of_product(cols, gw)                      # Re(cols @ gw)
         return out * scale
     # full half spectrum, zero outside the kept modes
     half = np.zeros((b, c, h, w // 2 + 1), dtype=np.complex128)
@@ -254,7 +270,7 @@ def forward_truncated_1d(x: np.ndarray, modes: int, transform: str = "dft") -> n
         raise ValueError(f"need 1 <= modes <= N/2+1 (modes={modes}, N={n})")
     scale = 1.0 / math.sqrt(n)
     if transform == "dft":
-        full = x @ dft_matrix(n, np.arange(n), np.arange(modes), -1)
+        full = _real_times_complex(x, dft_matrix(n, np.arange(n), np.arange(modes), -1))
     else:
         full = _transform(x.astype(np.complex128), -1, -1, transform)[..., :modes]
     return full * scale
@@ -272,7 +288,7 @@ def inverse_from_truncated_1d(yh: np.ndarray, n: int, transform: str = "dft") ->
     scale = 1.0 / math.sqrt(n)
     if transform == "dft":
         g = dft_matrix(n, np.arange(modes), np.arange(n), +1) * c2r_weights(n, modes)[:, None]
-        return (yh @ g).real * scale
+        return _real_part_of_product(yh, g) * scale
     z = np.zeros(yh.shape[:-1] + (n,), dtype=np.complex128)
     half = np.zeros(yh.shape[:-1] + (n // 2 + 1,), dtype=np.complex128)
     half[..., :modes] = yh

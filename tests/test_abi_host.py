@@ -1,0 +1,137 @@
+"""Host-side checks of the C ABI (no GPU needed).
+
+The library must load, export every function include/fno.h declares, and
+reject bad arguments on the host before touching the device.  Pointers in
+the rejection tests are fake addresses: validation fails before any of them
+is dereferenced or handed to HIP.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import fft_spectral_convolution_amd as fno
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fno.h")
+
+OK, NULL, SHAPE, MODES, ALIAS, ALIGN, NOMEM, HIP, WORKSPACE = 0, -1, -2, -3, -4, -5, -6, -7, -8
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"\b(fno_[a-z0-9_]+)\s*\(", text)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(fno.library_path()):
+        pytest.skip("libfno.so not built (run __graft_entry__.build())")
+    return fno.lib()
+
+
+def test_header_and_binding_agree():
+    assert declared_functions() == sorted(fno.EXPORTED_SYMBOLS)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), f"{name} declared in include/fno.h but not exported"
+
+
+def test_version_and_status_strings(lib):
+    assert fno.fno_version() >= 100
+    for code in (OK, NULL, SHAPE, MODES, ALIAS, ALIGN, NOMEM, HIP, WORKSPACE):
+        assert fno.fno_status_string(code)
+    assert fno.fno_status_string(12345) == "unknown status"
+
+
+A = 0x10000000          # fake, 256-byte aligned device addresses
+B = 0x20000000
+C = 0x30000000
+
+
+def conv2d(lib, x, w, out, *dims):
+    return lib.fno_spectral_conv2d(x, w, out, *dims, None)
+
+
+@pytest.mark.parametrize("dims,code", [
+    ((1, 1, 1, 8, 8, 2, 2), OK),          # valid: reaches the NULL check below only if a pointer is NULL
+    ((0, 1, 1, 8, 8, 2, 2), SHAPE),
+    ((1, 0, 1, 8, 8, 2, 2), SHAPE),
+    ((1, 1, 0, 8, 8, 2, 2), SHAPE),
+    ((1, 1, 1, 12, 8, 2, 2), SHAPE),     # H not a power of two
+    ((1, 1, 1, 8, 6, 2, 2), SHAPE),      # W not a power of two
+    ((1, 1, 1, 1, 8, 1, 2), SHAPE),      # H < 2
+    ((1, 1, 1, 8192, 8, 2, 2), SHAPE),   # longer than the supported 4096
+    ((1, 1, 1, 8, 8, 0, 2), MODES),
+    ((1, 1, 1, 8, 8, 5, 2), MODES),      # 2*mx > H
+    ((1, 1, 1, 8, 8, 2, 0), MODES),
+    ((1, 1, 1, 8, 8, 2, 6), MODES),      # my > W/2+1
+])
+def test_conv2d_shape_checks(lib, dims, code):
+    if code == OK:
+        assert conv2d(lib, None, B, C, *dims) == NULL
+    else:
+        assert conv2d(lib, A, B, C, *dims) == code
+
+
+def test_conv2d_pointer_checks(lib):
+    dims = (2, 3, 4, 16, 16, 4, 4)
+    assert conv2d(lib, None, B, C, *dims) == NULL
+    assert conv2d(lib, A, None, C, *dims) == NULL
+    assert conv2d(lib, A, B, None, *dims) == NULL
+    assert conv2d(lib, A + 4, B, C, *dims) == ALIGN
+    assert conv2d(lib, A, B + 8, C, *dims) == ALIGN
+    xbytes = 2 * 3 * 16 * 16 * 4
+    assert conv2d(lib, A, B, A + xbytes - 16, *dims) == ALIAS      # out starts inside x
+    assert conv2d(lib, A + 64, B, A, *dims) == ALIAS                # x starts inside out
+    assert conv2d(lib, A, B, B, *dims) == ALIAS                     # out on top of the weights
+
+
+def test_conv1d_checks(lib):
+    f = lib.fno_spectral_conv1d
+    assert f(A, B, C, 1, 1, 1, 12, 2, None) == SHAPE
+    assert f(A, B, C, 1, 1, 1, 16, 0, None) == MODES
+    assert f(A, B, C, 1, 1, 1, 16, 10, None) == MODES
+    assert f(None, B, C, 1, 1, 1, 16, 9, None) == NULL
+    assert f(A, B, A, 1, 1, 1, 16, 9, None) == ALIAS
+
+
+def test_ws_variant_checks(lib):
+    dims = (2, 3, 4, 16, 16, 4, 4)
+    need = fno.fno_workspace_size_2d(*dims)
+    assert need > 0
+    assert lib.fno_spectral_conv2d_ws(A, B, C, *dims, None, need, None) == WORKSPACE
+    assert lib.fno_spectral_conv2d_ws(A, B, C, *dims, 0x40000000, need - 1, None) == WORKSPACE
+    assert lib.fno_spectral_conv2d_ws(A, B, C, *dims, 0x40000010, need, None) == ALIGN
+    assert fno.fno_workspace_size_2d(1, 1, 1, 12, 8, 2, 2) == 0
+    assert fno.fno_workspace_size_1d(1, 1, 1, 16, 10) == 0
+
+
+def test_stage_call_checks(lib):
+    assert lib.fno_forward2d(None, B, 1, 1, 8, 8, 2, 2, None) == NULL
+    assert lib.fno_forward2d(A, B, 1, 1, 8, 8, 5, 2, None) == MODES
+    assert lib.fno_inverse2d(A, B + 4, 1, 1, 8, 8, 2, 2, None) == ALIGN
+    assert lib.fno_mix(A, B, C, 0, 1, 1, 1, None) == SHAPE
+    assert lib.fno_mix(A, B, A, 1, 1, 1, 4, None) == ALIAS
+    assert lib.fno_forward1d(A, B, 1, 1, 6, 2, None) == SHAPE
+    assert lib.fno_inverse1d(A, B, 1, 1, 8, 6, None) == MODES
+
+
+def test_binding_requires_gpu_tensors():
+    torch = pytest.importorskip("torch")
+    x = torch.zeros((1, 1, 8, 8))
+    w = torch.zeros((2, 2, 2, 1, 1), dtype=torch.complex64)
+    with pytest.raises(ValueError):
+        fno.fno_spectral_conv2d(x, w, 2, 2)
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setenv("LIBFNO_PATH", str(tmp_path / "nope.so"))
+    monkeypatch.setattr(fno, "_lib", None)
+    with pytest.raises(ImportError):
+        fno.lib()
