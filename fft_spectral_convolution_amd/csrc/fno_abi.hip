@@ -188,17 +188,29 @@ Shape2d make2d(int B, int Cin, int Cout, int H, int W, int mx, int my) {
 // schedules
 // ---------------------------------------------------------------------------
 
-// Unfused: rows_fwd -> cols_fwd -> mix -> cols_inv -> rows_inv, the spectra in
-// workspace.  Layout: [R or R' (shared)] [xh] [yh].
-size_t unfused_ws_2d(const Shape2d& s) {
-    const size_t rmax = (size_t)s.B * (size_t)(s.Cin > s.Cout ? s.Cin : s.Cout) * s.H * s.my * sizeof(float2);
-    const size_t m = (size_t)2 * s.mx * s.my;
-    return align_up(rmax) + align_up((size_t)s.B * s.Cin * m * sizeof(float2)) +
-           align_up((size_t)s.B * s.Cout * m * sizeof(float2));
+// The channel mix: MFMA when the per-mode GEMM is big enough to fill a
+// 32-row x 64-column tile reasonably, VALU otherwise.
+bool use_mfma_mix(int64_t B, int64_t Cin, int64_t Cout) { return B >= 8 && Cin >= 8 && Cout >= 16; }
+
+int run_mix(const float2* xh, const SpecLayout& lx, const float2* w, float2* yh, const SpecLayout& ly, int64_t B,
+            int64_t Cin, int64_t Cout, int64_t M, hipStream_t st) {
+    hipError_t e;
+    if (use_mfma_mix(B, Cin, Cout)) {
+        rec_kernel("mix_mfma", st);
+        e = launch_mix_mfma(xh, lx, w, yh, ly, B, Cin, Cout, M, st);
+    } else {
+        rec_kernel("mix_valu", st);
+        e = launch_mix_valu(xh, lx, w, yh, ly, B, Cin, Cout, M, st);
+    }
+    return e == hipSuccess ? FNO_OK : hip_fail(e);
 }
 
-int run_forward2d(const Shape2d& s, int64_t C, const float* x, float2* xh, float2* r, const float2* tw,
-                  hipStream_t st) {
+bool small_path(const Shape2d& s) { return small2d_supported(s.log2H, s.log2W, s.my); }
+
+// Staged (unfused) transforms: rows and columns as separate kernels, the row
+// spectrum R (or R') in workspace; spectra in the canonical layout.
+int run_forward2d_staged(const Shape2d& s, int64_t C, const float* x, float2* xh, float2* r, const float2* tw,
+                         hipStream_t st) {
     const float scale = (float)(1.0 / std::sqrt((double)s.H * (double)s.W));
     rec_kernel("rows_fwd", st);
     hipError_t e = launch_rows_fwd(x, r, s.B * C * s.H, s.log2W, s.my, s.my, 1.0f, tw, st);
@@ -209,8 +221,8 @@ int run_forward2d(const Shape2d& s, int64_t C, const float* x, float2* xh, float
     return FNO_OK;
 }
 
-int run_inverse2d(const Shape2d& s, int64_t C, const float2* yh, float* out, float2* r, const float2* tw,
-                  hipStream_t st) {
+int run_inverse2d_staged(const Shape2d& s, int64_t C, const float2* yh, float* out, float2* r, const float2* tw,
+                         hipStream_t st) {
     const float scale = (float)(1.0 / std::sqrt((double)s.H * (double)s.W));
     rec_kernel("cols_inv", st);
     hipError_t e = launch_cols_inv(yh, r, s.B * C, s.log2H, s.mx, s.my, tw, st);
@@ -221,9 +233,35 @@ int run_inverse2d(const Shape2d& s, int64_t C, const float2* yh, float* out, flo
     return FNO_OK;
 }
 
+// Fused per-image transforms (grids up to 128 x 128), any spectrum layout.
+int run_forward2d_small(const Shape2d& s, int64_t C, const float* x, float2* xh, const SpecLayout& lay,
+                        const float2* tw, hipStream_t st) {
+    const float scale = (float)(1.0 / std::sqrt((double)s.H * (double)s.W));
+    rec_kernel("fwd2d", st);
+    hipError_t e = launch_fwd2d_small(x, xh, lay, s.B * C, s.log2H, s.log2W, s.mx, s.my, scale, tw, st);
+    return e == hipSuccess ? FNO_OK : hip_fail(e);
+}
+
+int run_inverse2d_small(const Shape2d& s, int64_t C, const float2* yh, float* out, const SpecLayout& lay,
+                        const float2* tw, hipStream_t st) {
+    const float scale = (float)(1.0 / std::sqrt((double)s.H * (double)s.W));
+    rec_kernel("inv2d", st);
+    hipError_t e = launch_inv2d_small(yh, out, lay, s.B * C, s.log2H, s.log2W, s.mx, s.my, scale, tw, st);
+    return e == hipSuccess ? FNO_OK : hip_fail(e);
+}
+
+// Unfused: rows_fwd -> cols_fwd -> mix -> cols_inv -> rows_inv, every
+// intermediate spectrum in workspace.  Layout: [R or R' (shared)] [xh] [yh].
+size_t unfused_ws_2d(const Shape2d& s) {
+    const size_t rmax = (size_t)s.B * (size_t)(s.Cin > s.Cout ? s.Cin : s.Cout) * s.H * s.my * sizeof(float2);
+    const size_t m = (size_t)2 * s.mx * s.my;
+    return align_up(rmax) + align_up((size_t)s.B * s.Cin * m * sizeof(float2)) +
+           align_up((size_t)s.B * s.Cout * m * sizeof(float2));
+}
+
 int run_unfused_2d(const Shape2d& s, const float* x, const float2* w, float* out, void* ws, const float2* tw,
                    hipStream_t st) {
-    const size_t m = (size_t)2 * s.mx * s.my;
+    const int64_t m = (int64_t)2 * s.mx * s.my;
     const size_t rmax = (size_t)s.B * (size_t)(s.Cin > s.Cout ? s.Cin : s.Cout) * s.H * s.my * sizeof(float2);
     char* p = static_cast<char*>(ws);
     float2* r = reinterpret_cast<float2*>(p);
@@ -231,12 +269,34 @@ int run_unfused_2d(const Shape2d& s, const float* x, const float2* w, float* out
     float2* xh = reinterpret_cast<float2*>(p);
     p += align_up((size_t)s.B * s.Cin * m * sizeof(float2));
     float2* yh = reinterpret_cast<float2*>(p);
-    int rc = run_forward2d(s, s.Cin, x, xh, r, tw, st);
+    int rc = run_forward2d_staged(s, s.Cin, x, xh, r, tw, st);
     if (rc) return rc;
-    rec_kernel("mix_valu", st);
-    hipError_t e = launch_mix_valu(xh, w, yh, s.B, s.Cin, s.Cout, (int64_t)m, st);
-    if (e != hipSuccess) return hip_fail(e);
-    return run_inverse2d(s, s.Cout, yh, out, r, tw, st);
+    rc = run_mix(xh, canonical_layout(s.Cin, m), w, yh, canonical_layout(s.Cout, m), s.B, s.Cin, s.Cout, m, st);
+    if (rc) return rc;
+    return run_inverse2d_staged(s, s.Cout, yh, out, r, tw, st);
+}
+
+// Fused (grids up to 128 x 128): fwd2d -> mix -> inv2d, the truncated spectra
+// in the tiled layout (64-byte runs of 8 modes).
+size_t fused_small_ws_2d(const Shape2d& s) {
+    const int64_t m = (int64_t)2 * s.mx * s.my;
+    return align_up((size_t)layout_elems(tiled_layout(s.Cin, m), s.B) * sizeof(float2)) +
+           align_up((size_t)layout_elems(tiled_layout(s.Cout, m), s.B) * sizeof(float2));
+}
+
+int run_fused_small_2d(const Shape2d& s, const float* x, const float2* w, float* out, void* ws, const float2* tw,
+                       hipStream_t st) {
+    const int64_t m = (int64_t)2 * s.mx * s.my;
+    const SpecLayout lx = tiled_layout(s.Cin, m);
+    const SpecLayout ly = tiled_layout(s.Cout, m);
+    float2* xh = static_cast<float2*>(ws);
+    float2* yh = reinterpret_cast<float2*>(static_cast<char*>(ws) +
+                                           align_up((size_t)layout_elems(lx, s.B) * sizeof(float2)));
+    int rc = run_forward2d_small(s, s.Cin, x, xh, lx, tw, st);
+    if (rc) return rc;
+    rc = run_mix(xh, lx, w, yh, ly, s.B, s.Cin, s.Cout, m, st);
+    if (rc) return rc;
+    return run_inverse2d_small(s, s.Cout, yh, out, ly, tw, st);
 }
 
 size_t unfused_ws_1d(int64_t B, int64_t Cin, int64_t Cout, int modes) {
@@ -254,21 +314,20 @@ int run_unfused_1d(int64_t B, int64_t Cin, int64_t Cout, int N, int modes, const
     rec_kernel("rows_fwd", st);
     hipError_t e = launch_rows_fwd(x, xh, B * Cin, l2, modes, modes, scale, tw, st);
     if (e != hipSuccess) return hip_fail(e);
-    rec_kernel("mix_valu", st);
-    e = launch_mix_valu(xh, w, yh, B, Cin, Cout, modes, st);
-    if (e != hipSuccess) return hip_fail(e);
+    int rc = run_mix(xh, canonical_layout(Cin, modes), w, yh, canonical_layout(Cout, modes), B, Cin, Cout, modes, st);
+    if (rc) return rc;
     rec_kernel("rows_inv", st);
     e = launch_rows_inv(yh, out, B * Cout, l2, modes, modes, scale, tw, st);
     if (e != hipSuccess) return hip_fail(e);
     return FNO_OK;
 }
 
-// Fastest schedule for the shape.  Every shape currently runs the staged
-// kernels; the workspace size follows the chosen schedule.
-size_t best_ws_2d(const Shape2d& s) { return unfused_ws_2d(s); }
+// Fastest schedule for the shape; the workspace size follows the schedule.
+size_t best_ws_2d(const Shape2d& s) { return small_path(s) ? fused_small_ws_2d(s) : unfused_ws_2d(s); }
 
 int run_best_2d(const Shape2d& s, const float* x, const float2* w, float* out, void* ws, const float2* tw,
                 hipStream_t st) {
+    if (small_path(s)) return run_fused_small_2d(s, x, w, out, ws, tw, st);
     return run_unfused_2d(s, x, w, out, ws, tw, st);
 }
 
@@ -423,12 +482,17 @@ int fno_forward2d(const float* x, void* xh, int B, int C, int H, int W, int mx, 
     DeviceState* st = nullptr;
     rc = device_state(&st);
     if (rc) return rc;
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    float2* out = static_cast<float2*>(xh);
+    if (small_path(s)) {
+        rec_begin();
+        return rec_end(hs, run_forward2d_small(s, C, x, out, canonical_layout(C, 2 * mx * my), st->twiddle, hs));
+    }
     void* ws = nullptr;
     rc = internal_workspace(st, (size_t)B * C * H * my * sizeof(float2), &ws);
     if (rc) return rc;
-    hipStream_t hs = static_cast<hipStream_t>(stream);
     rec_begin();
-    return rec_end(hs, run_forward2d(s, C, x, static_cast<float2*>(xh), static_cast<float2*>(ws), st->twiddle, hs));
+    return rec_end(hs, run_forward2d_staged(s, C, x, out, static_cast<float2*>(ws), st->twiddle, hs));
 }
 
 int fno_inverse2d(const void* yh, float* out, int B, int C, int H, int W, int mx, int my, void* stream) {
@@ -443,13 +507,17 @@ int fno_inverse2d(const void* yh, float* out, int B, int C, int H, int W, int mx
     DeviceState* st = nullptr;
     rc = device_state(&st);
     if (rc) return rc;
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    const float2* in = static_cast<const float2*>(yh);
+    if (small_path(s)) {
+        rec_begin();
+        return rec_end(hs, run_inverse2d_small(s, C, in, out, canonical_layout(C, 2 * mx * my), st->twiddle, hs));
+    }
     void* ws = nullptr;
     rc = internal_workspace(st, (size_t)B * C * H * my * sizeof(float2), &ws);
     if (rc) return rc;
-    hipStream_t hs = static_cast<hipStream_t>(stream);
     rec_begin();
-    return rec_end(hs, run_inverse2d(s, C, static_cast<const float2*>(yh), out, static_cast<float2*>(ws),
-                                     st->twiddle, hs));
+    return rec_end(hs, run_inverse2d_staged(s, C, in, out, static_cast<float2*>(ws), st->twiddle, hs));
 }
 
 int fno_mix(const void* xh, const void* w, void* yh, int B, int Cin, int Cout, int M, void* stream) {
@@ -462,10 +530,8 @@ int fno_mix(const void* xh, const void* w, void* yh, int B, int Cin, int Cout, i
         return FNO_ERR_ALIAS;
     hipStream_t hs = static_cast<hipStream_t>(stream);
     rec_begin();
-    rec_kernel("mix_valu", hs);
-    hipError_t e = launch_mix_valu(static_cast<const float2*>(xh), static_cast<const float2*>(w),
-                                   static_cast<float2*>(yh), B, Cin, Cout, M, hs);
-    return rec_end(hs, e == hipSuccess ? FNO_OK : hip_fail(e));
+    return rec_end(hs, run_mix(static_cast<const float2*>(xh), canonical_layout(Cin, M), static_cast<const float2*>(w),
+                               static_cast<float2*>(yh), canonical_layout(Cout, M), B, Cin, Cout, M, hs));
 }
 
 int fno_forward1d(const float* x, void* xh, int B, int C, int N, int modes, void* stream) {

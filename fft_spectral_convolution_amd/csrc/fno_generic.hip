@@ -168,10 +168,17 @@ __global__ __launch_bounds__(kThreads) void k_rows_inv(const float2* __restrict_
 
 constexpr int kMixBT = 8;   // batch rows per thread
 
-__global__ __launch_bounds__(kThreads) void k_mix_valu(const float2* __restrict__ xh, const float2* __restrict__ w,
-                                                      float2* __restrict__ yh, int64_t B, int64_t Cin,
-                                                      int64_t Cout, int64_t M, int ot_log2, int64_t n_ot,
-                                                      int64_t n_mt) {
+struct MixAddr {
+    int64_t sb, sc, st;
+    __device__ __forceinline__ int64_t at(int64_t b, int64_t c, int64_t m) const {
+        return b * sb + c * sc + (m >> 3) * st + (m & 7);
+    }
+};
+
+__global__ __launch_bounds__(kThreads) void k_mix_valu(const float2* __restrict__ xh, MixAddr ax,
+                                                      const float2* __restrict__ w, float2* __restrict__ yh,
+                                                      MixAddr ay, int64_t B, int64_t Cin, int64_t Cout, int64_t M,
+                                                      int ot_log2, int64_t n_ot, int64_t n_mt) {
     const int tid = threadIdx.x;
     const int64_t bid = blockIdx.x;
     const int64_t bx = bid % n_ot;
@@ -188,12 +195,12 @@ __global__ __launch_bounds__(kThreads) void k_mix_valu(const float2* __restrict_
         const float2 wv = w[(m * Cin + i) * Cout + o];
 #pragma unroll
         for (int t = 0; t < kMixBT; ++t) {
-            if (b0 + t < B) acc[t] = cfma(acc[t], xh[((b0 + t) * Cin + i) * M + m], wv);
+            if (b0 + t < B) acc[t] = cfma(acc[t], xh[ax.at(b0 + t, i, m)], wv);
         }
     }
 #pragma unroll
     for (int t = 0; t < kMixBT; ++t) {
-        if (b0 + t < B) yh[((b0 + t) * Cout + o) * M + m] = acc[t];
+        if (b0 + t < B) yh[ay.at(b0 + t, o, m)] = acc[t];
     }
 }
 
@@ -269,8 +276,8 @@ hipError_t launch_cols_inv(const float2* yh, float2* r, int64_t nimg, int log2H,
     return hipGetLastError();
 }
 
-hipError_t launch_mix_valu(const float2* xh, const float2* w, float2* yh, int64_t B, int64_t Cin, int64_t Cout,
-                           int64_t M, hipStream_t s) {
+hipError_t launch_mix_valu(const float2* xh, const SpecLayout& lx, const float2* w, float2* yh,
+                           const SpecLayout& ly, int64_t B, int64_t Cin, int64_t Cout, int64_t M, hipStream_t s) {
     int ot_log2 = 0;
     while ((1 << ot_log2) < Cout && ot_log2 < 6) ++ot_log2;
     const int64_t ot = 1 << ot_log2;
@@ -279,7 +286,10 @@ hipError_t launch_mix_valu(const float2* xh, const float2* w, float2* yh, int64_
     const int64_t n_mt = (M + mt - 1) / mt;
     const int64_t n_bt = (B + kMixBT - 1) / kMixBT;
     const dim3 grid((unsigned)(n_ot * n_mt * n_bt));
-    hipLaunchKernelGGL(k_mix_valu, grid, dim3(kThreads), 0, s, xh, w, yh, B, Cin, Cout, M, ot_log2, n_ot, n_mt);
+    const MixAddr ax{lx.sb, lx.sc, lx.st};
+    const MixAddr ay{ly.sb, ly.sc, ly.st};
+    hipLaunchKernelGGL(k_mix_valu, grid, dim3(kThreads), 0, s, xh, ax, w, yh, ay, B, Cin, Cout, M, ot_log2, n_ot,
+                       n_mt);
     return hipGetLastError();
 }
 

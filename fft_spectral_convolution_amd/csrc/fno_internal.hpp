@@ -20,6 +20,35 @@ struct Shape1d {
     int N, modes, log2N;
 };
 
+// Address of truncated-spectrum entry (b, c, m), in complex elements:
+//   b * sb + c * sc + (m / 8) * st + (m % 8)
+// Canonical [B][C][M]: sb = C*M, sc = M, st = 8.
+// Tiled [B][ceil(M/8)][C][8] (8 modes of one (b, c) form a 64-byte chunk).
+struct SpecLayout {
+    int64_t sb, sc, st;
+    int C;
+};
+
+inline SpecLayout canonical_layout(int64_t C, int64_t M) { return SpecLayout{C * M, M, 8, (int)C}; }
+inline SpecLayout tiled_layout(int64_t C, int64_t M) {
+    const int64_t nt = (M + 7) / 8;
+    return SpecLayout{nt * C * 8, 8, C * 8, (int)C};
+}
+// Complex elements a spectrum of B batch items spans in either layout.
+inline int64_t layout_elems(const SpecLayout& l, int64_t B) { return B * l.sb; }
+
+// ---- fused small-grid transforms (fno_small2d.hip), H, W in [8, 128] --------
+bool small2d_supported(int log2H, int log2W, int my);
+hipError_t launch_fwd2d_small(const float* x, float2* xh, const SpecLayout& lay, int64_t nimg, int log2H, int log2W,
+                              int mx, int my, float scale, const float2* tw, hipStream_t s);
+hipError_t launch_inv2d_small(const float2* yh, float* out, const SpecLayout& lay, int64_t nimg, int log2H,
+                              int log2W, int mx, int my, float scale, const float2* tw, hipStream_t s);
+
+// ---- channel mix on MFMA (fno_mix.hip) --------------------------------------
+// yh(b, o, m) = sum_i xh(b, i, m) * w[m][i][o], spectra addressed by layouts.
+hipError_t launch_mix_mfma(const float2* xh, const SpecLayout& lx, const float2* w, float2* yh,
+                           const SpecLayout& ly, int64_t B, int64_t Cin, int64_t Cout, int64_t M, hipStream_t s);
+
 // ---- generic stage launchers (fno_generic.hip) -------------------------------
 // All return hipSuccess or the launch error.  `tw` is the device twiddle table.
 
@@ -29,9 +58,9 @@ hipError_t launch_rows_fwd(const float* x, float2* y, int64_t nrows, int log2W, 
 // R[nimg][H][my] -> xh[nimg][2][mx][my] (kept kx only), times scale.
 hipError_t launch_cols_fwd(const float2* r, float2* xh, int64_t nimg, int log2H, int mx, int my,
                            float scale, const float2* tw, hipStream_t s);
-// Per-mode channel mix, VALU: yh[b][o][m] = sum_i xh[b][i][m] w[m][i][o].
-hipError_t launch_mix_valu(const float2* xh, const float2* w, float2* yh, int64_t B, int64_t Cin,
-                           int64_t Cout, int64_t M, hipStream_t s);
+// Per-mode channel mix, VALU: yh(b, o, m) = sum_i xh(b, i, m) w[m][i][o].
+hipError_t launch_mix_valu(const float2* xh, const SpecLayout& lx, const float2* w, float2* yh,
+                           const SpecLayout& ly, int64_t B, int64_t Cin, int64_t Cout, int64_t M, hipStream_t s);
 // yh[nimg][2][mx][my] -> zero-filled column inverse -> R'[nimg][H][my].
 hipError_t launch_cols_inv(const float2* yh, float2* r, int64_t nimg, int log2H, int mx, int my,
                            const float2* tw, hipStream_t s);
