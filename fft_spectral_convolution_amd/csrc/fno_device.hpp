@@ -111,6 +111,19 @@ __device__ __forceinline__ void dft(float2 (&v)[R]) {
     }
 }
 
+// Workgroup barrier that orders LDS accesses only: global loads issued before
+// it stay in flight (a plain __syncthreads would wait for them too), which
+// lets a kernel prefetch the next item's inputs across its LDS phases.
+// The scheduling barriers keep the compiler from moving arithmetic of the
+// next phase above it (which would keep two phases' registers live at once).
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+    __builtin_amdgcn_sched_barrier(0);
+}
+
 // Twiddle exp(SIGN 2 pi i m / kNMax) from the host-built table of exp(-2 pi i m / kNMax).
 template <int SIGN>
 __device__ __forceinline__ float2 table_twiddle(const float2* __restrict__ tw, int m) {

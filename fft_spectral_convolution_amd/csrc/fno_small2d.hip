@@ -1,11 +1,11 @@
 // Fused per-image forward and inverse transforms for grids with H, W <= 128.
 //
-// Forward (one workgroup per image): the real rows are transformed two at a
-// time as one complex row z = x[p] + i x[p + H/2]; only the bins a truncated
-// row spectrum needs (ky < my and their mirrors W - ky) are kept in LDS.
-// The column pass then rebuilds each row's half spectrum on the fly
-// (A = (Z[k] + conj Z[-k]) / 2, B = (Z[k] - conj Z[-k]) / 2i), transforms the
-// my columns along H and writes only kx in [0,mx) u [H-mx,H), scaled.
+// Forward (per image): the real rows are transformed two at a time as one
+// complex row z = x[p] + i x[p + H/2]; only the bins a truncated row spectrum
+// needs (ky < my and their mirrors W - ky) are kept in LDS.  The column pass
+// rebuilds each row's half spectrum on the fly (A = (Z[k] + conj Z[-k]) / 2,
+// B = (Z[k] - conj Z[-k]) / 2i), transforms the my columns along H and writes
+// only kx in [0,mx) u [H-mx,H), scaled.
 // Inverse: the mirror image -- zero-filled columns are inverted straight from
 // the truncated spectrum into LDS, then pairs of rows are turned back into
 // real rows by one complex inverse transform of Ya + i Yb (Hermitian
@@ -17,7 +17,17 @@
 // Each length-N transform is split N = R1 * R2: a thread holds R1 points
 // (n = t + R2 m), does an R1-point DFT in registers, multiplies by
 // W_N^{t k1} and hands the R1 results through LDS to the R2 threads that do
-// the R2-point DFTs across t, giving X[k1 + R1 k2].
+// the R2-point DFTs across t, giving X[k1 + R1 k2].  Rows add one radix-2
+// level on top (even and odd samples per thread, see SmallPlan).
+//
+// Scheduling: a persistent grid of a few workgroups per CU walks the images;
+// as soon as a workgroup has moved the current image's global inputs from
+// registers into LDS it issues the loads of its next image, which land while
+// it finishes the current one (its barriers order LDS only, so those loads
+// are not waited for early).  Images are handed
+// out so that the workgroups the hardware places on one XCD at the same time
+// work on neighbouring channels, whose spectra share 128-byte lines in the
+// tiled layout below.
 //
 // Spectra outside the kernels use a mode-addressed layout:
 //   addr(b, c, m) = b * sb + c * sc + (m / 8) * st + (m % 8)   [complex elements]
@@ -32,8 +42,10 @@ namespace fno {
 namespace {
 
 constexpr int kSmallThreads = 256;
+constexpr int kSmallBlocksPerCU = 2;
 
 template <int N> struct Split;
+template <> struct Split<4>   { static constexpr int R1 = 2,  R2 = 2; };
 template <> struct Split<8>   { static constexpr int R1 = 4,  R2 = 2; };
 template <> struct Split<16>  { static constexpr int R1 = 4,  R2 = 4; };
 template <> struct Split<32>  { static constexpr int R1 = 8,  R2 = 4; };
@@ -45,255 +57,400 @@ __device__ __forceinline__ float2 conjf2(float2 a) { return make_float2(a.x, -a.
 struct ModeAddr {
     int64_t sb, sc, st;
     int C;
-    __device__ __forceinline__ int64_t at(int64_t img, int m) const {
-        const int64_t b = img / C;
-        const int64_t c = img - b * C;
-        return b * sb + c * sc + (int64_t)(m >> 3) * st + (m & 7);
+    // address of mode m of image img = b * C + c, relative to the image base
+    // (image counts stay below 2^31 on this path: every image has >= 64 points)
+    __device__ __forceinline__ int64_t base(int64_t img) const {
+        const uint32_t i32 = (uint32_t)img;
+        const uint32_t b = i32 / (uint32_t)C;
+        const uint32_t c = i32 - b * (uint32_t)C;
+        return (int64_t)b * sb + (int64_t)c * sc;
     }
+    __device__ __forceinline__ int64_t off(int m) const { return (int64_t)(m >> 3) * st + (m & 7); }
 };
 
+// Logical work index -> image.  Indices L and L + 8 (same XCD under
+// round-robin workgroup dispatch, same step of the persistent loop when the
+// grid is a multiple of 16) get images 2j and 2j + 1.
+__device__ __forceinline__ int64_t paired_image(int64_t L, int64_t nimg) {
+    const int64_t g = L >> 4;
+    if ((g + 1) * 16 > nimg) return L;
+    const int r = (int)(L & 15);
+    return g * 16 + 2 * (r & 7) + (r >> 3);
+}
+
+// Rows: a complex row of length W is split as n = q + 2 (t + T m) with
+// q in {0,1} held in one thread (so every lane moves float2 pairs), t < T
+// across the T lanes of the row and m < M in registers (W / 2 = T * M).  The
+// even / odd halves (q) get a W/2-point transform each (in-register DFT over
+// m, twiddle, LDS hand-over, DFT over t), and one radix-2 step with
+// W_W^k joins them.  Columns: n = t + R2 m with R1 = M points per thread.
 template <int LOG2H, int LOG2W>
 struct SmallPlan {
     static constexpr int H = 1 << LOG2H;
     static constexpr int W = 1 << LOG2W;
     static constexpr int P = H / 2;                 // complex rows (real row pairs)
-    static constexpr int R1W = Split<W>::R1, R2W = Split<W>::R2;
+    static constexpr int MW = Split<W / 2>::R1;     // points per thread and half (q)
+    static constexpr int TW = Split<W / 2>::R2;     // lanes per row
     static constexpr int R1H = Split<H>::R1, R2H = Split<H>::R2;
-    static constexpr int XSW = R1W + 1;             // padded per-thread slot (rows)
-    static constexpr int XSH = R1H + 1;             // padded per-thread slot (cols)
-    static constexpr int ROWS_IT = kSmallThreads / R2W;
+    // LDS exchange: each row (column) group owns T slots of an odd number of
+    // complex values.  In the row phase the lanes of a wave are (group, slot)
+    // with the slot fastest, so the group stride is made congruent to T
+    // modulo 16 double-words; in the column phase the group (column) index is
+    // fastest, so that stride is made odd.  Either way the 8-byte accesses of
+    // a wave spread over all banks.
+    static constexpr int XSW = 2 * MW + 1;
+    static constexpr int XSH = R1H + 1;
+    static constexpr int GSR = TW * XSW + ((TW - (TW * XSW) % 16) + 16) % 16;
+    static constexpr int GSC = R2H * XSH + ((R2H * XSH) % 2 == 0 ? 1 : 0);
+    static constexpr int ROWS_IT = kSmallThreads / TW;
     static constexpr int COLS_IT = kSmallThreads / R2H;
-    static constexpr int XBUF = (ROWS_IT * R2W * XSW > COLS_IT * R2H * XSH) ? ROWS_IT * R2W * XSW
-                                                                              : COLS_IT * R2H * XSH;
-    static_assert(R1W >= R2W && R1W % R2W == 0, "row split");
+    static constexpr int ITERS_R = (P + ROWS_IT - 1) / ROWS_IT;
+    static constexpr int XBUF = (ROWS_IT * GSR > COLS_IT * GSC) ? ROWS_IT * GSR : COLS_IT * GSC;
+    static_assert(MW >= TW && MW % TW == 0, "row split");
     static_assert(R1H >= R2H && R1H % R2H == 0 && R1H >= 2, "column split");
-    // LDS: twiddles for W and H, two spectrum planes of H/2 x my (forward) or
-    // one plane of H x my (inverse), and the exchange buffer.
-    static size_t lds_bytes(int my) { return sizeof(float2) * ((size_t)W + H + (size_t)H * my + XBUF); }
+    // Row stride of the spectrum planes: >= my and congruent to T modulo 16,
+    // so the rows written by one wave land on different banks.
+    static __host__ __device__ int plane_stride(int my) { return my + ((TW - my % 16) + 16) % 16; }
+    // LDS: twiddles for W and H, two spectrum planes of H/2 rows (forward) or
+    // one plane of H rows (inverse), and the exchange buffer.
+    static size_t lds_bytes(int my) {
+        return sizeof(float2) * ((size_t)W + H + (size_t)H * plane_stride(my) + XBUF);
+    }
 };
 
 template <int LOG2H, int LOG2W>
-__global__ __launch_bounds__(kSmallThreads) void k_fwd2d_small(const float* __restrict__ x, float2* __restrict__ xh,
-                                                              ModeAddr ma, int mx, int my, float scale,
-                                                              const float2* __restrict__ tw) {
+__global__ __launch_bounds__(kSmallThreads, kSmallBlocksPerCU) void k_fwd2d_small(
+    const float* __restrict__ x, float2* __restrict__ xh, ModeAddr ma, int64_t nimg, int mx_arg, int my_arg,
+    float scale, const float2* __restrict__ tw) {
     using S = SmallPlan<LOG2H, LOG2W>;
     constexpr int H = S::H, W = S::W, P = S::P;
-    constexpr int R1W = S::R1W, R2W = S::R2W, R1H = S::R1H, R2H = S::R2H;
+    constexpr int MW = S::MW, TW = S::TW, R1H = S::R1H, R2H = S::R2H;
+    constexpr int IT = S::ITERS_R;
     extern __shared__ float2 smem[];
     float2* twW = smem;
     float2* twH = twW + W;
-    float2* zlo = twH + H;              // [P][my]: Z_p[k], k < my
-    float2* zhi = zlo + P * my;         // [P][my]: Z_p[(W - k) mod W]
-    float2* xbuf = zhi + P * my;
+    // zlo = [P][ms]: Z_p[k], k < my; zhi = [P][ms]: Z_p[(W - k) mod W]
+    float2* zplanes = twH + H;
+    float2* xbuf = zplanes + 2 * P * S::plane_stride(my_arg);
 
     const int tid = threadIdx.x;
-    const int64_t img = blockIdx.x;
     for (int j = tid; j < W; j += kSmallThreads) twW[j] = tw[j * (kNMax / W)];
     for (int j = tid; j < H; j += kSmallThreads) twH[j] = tw[j * (kNMax / H)];
-    __syncthreads();
+    lds_barrier();
 
-    const float* xi = x + img * (int64_t)(H * W);
+    const int pl = tid / TW;             // row-pass role
+    const int t = tid % TW;
+    const int tc = tid / S::COLS_IT;     // column-pass role
+    const int cl = tid % S::COLS_IT;
+    float2* xbr = xbuf + pl * S::GSR;
+    float2* xbc = xbuf + cl * S::GSC;
 
-    // ---- rows: complex row p = x[p] + i x[p + P] --------------------------
-    {
-        const int pl = tid / R2W;
-        const int t = tid % R2W;
-        float2* xb = xbuf + pl * (R2W * S::XSW);
-        for (int p0 = 0; p0 < P; p0 += S::ROWS_IT) {
-            const int p = p0 + pl;
+    // row batch `it` of an image: rows a = p and b = p + P, float2 pairs at
+    // 2 (t + T m).  Rows past P (small grids) load row 0 and are not used.
+    auto load = [&](int64_t img, float2 (&ba)[IT][MW], float2 (&bb)[IT][MW]) {
+        const float* xi = x + img * (int64_t)(H * W);
+#pragma unroll
+        for (int it = 0; it < IT; ++it) {
+            const int p = it * S::ROWS_IT + pl;
+            const int pp = p < P ? p : 0;
+            const float2* ra = reinterpret_cast<const float2*>(xi + pp * W) + t;
+            const float2* rb = reinterpret_cast<const float2*>(xi + (pp + P) * W) + t;
+#pragma unroll
+            for (int m = 0; m < MW; ++m) {
+                ba[it][m] = ra[TW * m];
+                bb[it][m] = rb[TW * m];
+            }
+        }
+    };
+
+    const int64_t G = gridDim.x;
+    int64_t L = blockIdx.x;
+    float2 ba[IT][MW], bb[IT][MW];
+    load(paired_image(L, nimg), ba, bb);
+    while (true) {
+        const int64_t img = paired_image(L, nimg);
+        const int64_t Ln = L + G;
+        // Opaque per-image copies of the mode counts: everything derived from
+        // them (predicates, LDS and output offsets) is recomputed per image
+        // instead of being hoisted out of the loop into ~100 live registers.
+        int my = my_arg, mx = mx_arg;
+        asm volatile("" : "+s"(my), "+s"(mx));
+        const int ms = S::plane_stride(my);
+        float2* zlo = zplanes;
+        float2* zhi = zplanes + P * ms;
+        // ---- rows: complex row p = x[p] + i x[p + P] ----------------------
+#pragma unroll
+        for (int it = 0; it < IT; ++it) {
+            const int p = it * S::ROWS_IT + pl;
             const bool active = p < P;
             if (active) {
-                const float* ra = xi + p * W;
-                const float* rb = ra + P * W;
-                float2 v[R1W];
+                float2 c0[MW], c1[MW];         // even (q = 0) and odd (q = 1) samples
 #pragma unroll
-                for (int m = 0; m < R1W; ++m) v[m] = make_float2(ra[t + R2W * m], rb[t + R2W * m]);
-                dft<R1W, -1>(v);
+                for (int m = 0; m < MW; ++m) {
+                    c0[m] = make_float2(ba[it][m].x, bb[it][m].x);
+                    c1[m] = make_float2(ba[it][m].y, bb[it][m].y);
+                }
+                dft<MW, -1>(c0);
+                dft<MW, -1>(c1);
 #pragma unroll
-                for (int k1 = 1; k1 < R1W; ++k1) v[k1] = cmul(v[k1], twW[(t * k1) & (W - 1)]);
+                for (int k1 = 1; k1 < MW; ++k1) {
+                    const float2 w = twW[(2 * t * k1) & (W - 1)];   // W_{W/2}^{t k1}
+                    c0[k1] = cmul(c0[k1], w);
+                    c1[k1] = cmul(c1[k1], w);
+                }
 #pragma unroll
-                for (int k1 = 0; k1 < R1W; ++k1) xb[t * S::XSW + k1] = v[k1];
+                for (int k1 = 0; k1 < MW; ++k1) {
+                    xbr[t * S::XSW + k1] = c0[k1];
+                    xbr[t * S::XSW + MW + k1] = c1[k1];
+                }
             }
-            __syncthreads();
+            lds_barrier();
             if (active) {
-                const int p = p0 + pl;
 #pragma unroll
-                for (int j = 0; j < R1W / R2W; ++j) {
-                    const int k1 = t + R2W * j;
-                    float2 u[R2W];
+                for (int jj = 0; jj < MW / TW; ++jj) {
+                    const int k1 = t + TW * jj;
+                    float2 u0[TW], u1[TW];
 #pragma unroll
-                    for (int tt = 0; tt < R2W; ++tt) u[tt] = xb[tt * S::XSW + k1];
-                    dft<R2W, -1>(u);
+                    for (int tt = 0; tt < TW; ++tt) {
+                        u0[tt] = xbr[tt * S::XSW + k1];
+                        u1[tt] = xbr[tt * S::XSW + MW + k1];
+                    }
+                    dft<TW, -1>(u0);
+                    dft<TW, -1>(u1);
 #pragma unroll
-                    for (int k2 = 0; k2 < R2W; ++k2) {
-                        const int k = k1 + R1W * k2;
-                        if (k < my) zlo[p * my + k] = u[k2];
-                        const int km = (W - k) & (W - 1);
-                        if (km < my) zhi[p * my + km] = u[k2];
+                    for (int k2 = 0; k2 < TW; ++k2) {
+                        const int kh = k1 + MW * k2;                    // < W/2
+                        const float2 y1 = cmul(u1[k2], twW[kh]);
+                        const float2 lo = cadd(u0[k2], y1);             // Z[kh]
+                        const float2 hi = csub(u0[k2], y1);             // Z[kh + W/2]
+                        if (kh < my) zlo[p * ms + kh] = lo;
+                        const int kml = (W - kh) & (W - 1);
+                        if (kml < my) zhi[p * ms + kml] = lo;
+                        const int khh = kh + W / 2;
+                        if (khh < my) zlo[p * ms + khh] = hi;
+                        const int kmh = W / 2 - kh;                     // (W - khh) mod W
+                        if (kmh < my) zhi[p * ms + kmh] = hi;
                     }
                 }
             }
-            __syncthreads();
+            lds_barrier();
         }
-    }
 
-    // ---- columns ky < my along H, kept kx only ------------------------------
-    {
-        const int t = tid / S::COLS_IT;
-        const int cl = tid % S::COLS_IT;
-        float2* xb = xbuf + cl * (R2H * S::XSH);
-        for (int c0 = 0; c0 < my; c0 += S::COLS_IT) {
-            const int ky = c0 + cl;
+        // the register buffer is free once every row batch has gone through
+        // LDS: start fetching the next image, it lands during the column pass
+        // (the empty asm keeps the compiler from hoisting these loads into
+        // the row pass, where the current image's registers are still live)
+        asm volatile("" ::: "memory");
+        if (Ln < nimg) load(paired_image(Ln, nimg), ba, bb);
+
+        // ---- columns ky < my along H, kept kx only (one batch: my <= COLS_IT)
+        const int64_t obase = ma.base(img);
+        {
+            const int ky = cl;
             const bool active = ky < my;
             if (active) {
                 float2 v[R1H];
 #pragma unroll
                 for (int m = 0; m < R1H / 2; ++m) {
-                    const int p = t + R2H * m;
-                    const float2 zl = zlo[p * my + ky];
-                    const float2 zm = zhi[p * my + ky];
+                    const int p = tc + R2H * m;
+                    const float2 zl = zlo[p * ms + ky];
+                    const float2 zm = zhi[p * ms + ky];
                     v[m] = make_float2(0.5f * (zl.x + zm.x), 0.5f * (zl.y - zm.y));
                     v[m + R1H / 2] = make_float2(0.5f * (zl.y + zm.y), -0.5f * (zl.x - zm.x));
                 }
                 dft<R1H, -1>(v);
 #pragma unroll
-                for (int k1 = 1; k1 < R1H; ++k1) v[k1] = cmul(v[k1], twH[(t * k1) & (H - 1)]);
+                for (int k1 = 1; k1 < R1H; ++k1) v[k1] = cmul(v[k1], twH[(tc * k1) & (H - 1)]);
 #pragma unroll
-                for (int k1 = 0; k1 < R1H; ++k1) xb[t * S::XSH + k1] = v[k1];
+                for (int k1 = 0; k1 < R1H; ++k1) xbc[tc * S::XSH + k1] = v[k1];
             }
-            __syncthreads();
+            lds_barrier();
             if (active) {
 #pragma unroll
                 for (int j = 0; j < R1H / R2H; ++j) {
-                    const int k1 = t + R2H * j;
+                    const int k1 = tc + R2H * j;
                     float2 u[R2H];
 #pragma unroll
-                    for (int tt = 0; tt < R2H; ++tt) u[tt] = xb[tt * S::XSH + k1];
+                    for (int tt = 0; tt < R2H; ++tt) u[tt] = xbc[tt * S::XSH + k1];
                     dft<R2H, -1>(u);
 #pragma unroll
                     for (int k2 = 0; k2 < R2H; ++k2) {
                         const int kx = k1 + R1H * k2;
                         const int q = kx < mx ? kx : (kx >= H - mx ? kx - H + 2 * mx : -1);
-                        if (q >= 0) xh[ma.at(img, q * my + ky)] = cscale(u[k2], scale);
+                        if (q >= 0) xh[obase + ma.off(q * my + ky)] = cscale(u[k2], scale);
                     }
                 }
             }
-            __syncthreads();
+            lds_barrier();
         }
+        L = Ln;
+        if (L >= nimg) break;
     }
 }
 
 template <int LOG2H, int LOG2W>
-__global__ __launch_bounds__(kSmallThreads) void k_inv2d_small(const float2* __restrict__ yh, float* __restrict__ out,
-                                                              ModeAddr ma, int mx, int my, float scale,
-                                                              const float2* __restrict__ tw) {
+__global__ __launch_bounds__(kSmallThreads, kSmallBlocksPerCU) void k_inv2d_small(
+    const float2* __restrict__ yh, float* __restrict__ out, ModeAddr ma, int64_t nimg, int mx_arg, int my_arg,
+    float scale, const float2* __restrict__ tw) {
     using S = SmallPlan<LOG2H, LOG2W>;
     constexpr int H = S::H, W = S::W, P = S::P;
-    constexpr int R1W = S::R1W, R2W = S::R2W, R1H = S::R1H, R2H = S::R2H;
+    constexpr int MW = S::MW, TW = S::TW, R1H = S::R1H, R2H = S::R2H;
+    constexpr int KJ = R1H / R2H;
     extern __shared__ float2 smem[];
     float2* twW = smem;
     float2* twH = twW + W;
-    float2* rp = twH + H;               // [H][my]: column-inverted spectrum R'[h][ky]
-    float2* xbuf = rp + H * my;
+    float2* rp = twH + H;               // [H][ms]: column-inverted spectrum R'[h][ky]
+    float2* xbuf = rp + H * S::plane_stride(my_arg);
 
     const int tid = threadIdx.x;
-    const int64_t img = blockIdx.x;
     for (int j = tid; j < W; j += kSmallThreads) twW[j] = tw[j * (kNMax / W)];
     for (int j = tid; j < H; j += kSmallThreads) twH[j] = tw[j * (kNMax / H)];
-    __syncthreads();
+    lds_barrier();
 
-    // ---- columns: R'[h][ky] = sum_{kept kx} Y[kx][ky] W_H^{+h kx} -------------
-    {
-        const int t = tid / S::COLS_IT;
-        const int cl = tid % S::COLS_IT;
-        float2* xb = xbuf + cl * (R2H * S::XSH);
-        for (int c0 = 0; c0 < my; c0 += S::COLS_IT) {
-            const int ky = c0 + cl;
+    const int pl = tid / TW;
+    const int t = tid % TW;
+    const int tc = tid / S::COLS_IT;
+    const int cl = tid % S::COLS_IT;
+    const int kyc = cl < my_arg ? cl : 0;    // column this thread gathers (dummy 0 when idle)
+    float2* xbr = xbuf + pl * S::GSR;
+    float2* xbc = xbuf + cl * S::GSC;
+
+    // Inputs of this thread's column batch: Y[kx][ky] at kx = k1 + R1H k2.
+    // Loads are unconditional (dropped kx read mode 0) so the prefetch never
+    // forces an early wait; dropped values are zeroed where they are used.
+    auto gather = [&](int64_t img, float2 (&u)[KJ][R2H]) {
+        int my = my_arg, mx = mx_arg;
+        asm volatile("" : "+s"(my), "+s"(mx));
+        const int64_t ibase = ma.base(img);
+#pragma unroll
+        for (int j = 0; j < KJ; ++j) {
+            const int k1 = tc + R2H * j;
+#pragma unroll
+            for (int k2 = 0; k2 < R2H; ++k2) {
+                const int kx = k1 + R1H * k2;
+                const int q = kx < mx ? kx : (kx >= H - mx ? kx - H + 2 * mx : -1);
+                const int mode = q >= 0 ? q * my + kyc : 0;
+                u[j][k2] = yh[ibase + ma.off(mode)];
+            }
+        }
+    };
+
+    const int64_t G = gridDim.x;
+    int64_t L = blockIdx.x;
+    float2 pre[KJ][R2H];
+    gather(paired_image(L, nimg), pre);
+    while (true) {
+        const int64_t img = paired_image(L, nimg);
+        const int64_t Ln = L + G;
+        // opaque per-image copies of the mode counts (see the forward kernel)
+        int my = my_arg, mx = mx_arg;
+        asm volatile("" : "+s"(my), "+s"(mx));
+        const int ms = S::plane_stride(my);
+        // ---- columns: R'[h][ky] = sum_{kept kx} Y[kx][ky] W_H^{+h kx} -------
+        // (one batch: my <= COLS_IT on this path)
+        {
+            const int ky = cl;
             const bool active = ky < my;
             if (active) {
 #pragma unroll
-                for (int j = 0; j < R1H / R2H; ++j) {
-                    const int k1 = t + R2H * j;
+                for (int j = 0; j < KJ; ++j) {
+                    const int k1 = tc + R2H * j;
                     float2 u[R2H];
 #pragma unroll
                     for (int k2 = 0; k2 < R2H; ++k2) {
                         const int kx = k1 + R1H * k2;
-                        const int q = kx < mx ? kx : (kx >= H - mx ? kx - H + 2 * mx : -1);
-                        u[k2] = q >= 0 ? yh[ma.at(img, q * my + ky)] : make_float2(0.0f, 0.0f);
+                        const bool kept = kx < mx || kx >= H - mx;
+                        u[k2] = kept ? pre[j][k2] : make_float2(0.0f, 0.0f);
                     }
                     dft<R2H, +1>(u);
 #pragma unroll
                     for (int tt = 1; tt < R2H; ++tt) u[tt] = cmul(u[tt], conjf2(twH[(tt * k1) & (H - 1)]));
 #pragma unroll
-                    for (int tt = 0; tt < R2H; ++tt) xb[tt * S::XSH + k1] = u[tt];
+                    for (int tt = 0; tt < R2H; ++tt) xbc[tt * S::XSH + k1] = u[tt];
                 }
             }
-            __syncthreads();
+            // the prefetch registers are free: fetch the next image's columns
+            asm volatile("" ::: "memory");
+            if (Ln < nimg) gather(paired_image(Ln, nimg), pre);
+            lds_barrier();
             if (active) {
                 float2 v[R1H];
 #pragma unroll
-                for (int k1 = 0; k1 < R1H; ++k1) v[k1] = xb[t * S::XSH + k1];
+                for (int k1 = 0; k1 < R1H; ++k1) v[k1] = xbc[tc * S::XSH + k1];
                 dft<R1H, +1>(v);
 #pragma unroll
-                for (int m = 0; m < R1H; ++m) rp[(t + R2H * m) * my + ky] = v[m];
+                for (int m = 0; m < R1H; ++m) rp[(tc + R2H * m) * ms + ky] = v[m];
             }
-            __syncthreads();
+            lds_barrier();
         }
-    }
 
-    // ---- rows: two real rows per complex inverse transform -----------------
-    {
-        const int pl = tid / R2W;
-        const int t = tid % R2W;
-        float2* xb = xbuf + pl * (R2W * S::XSW);
+        // ---- rows: two real rows per complex inverse transform -------------
+        // Z = Ya_herm + i Yb_herm (imaginary parts of DC / Nyquist dropped);
+        // even / odd outputs q: S_q[k] = (Z[k] +- Z[k + W/2]) W_W^{+q k}.
         float* oi = out + img * (int64_t)(H * W);
-        for (int p0 = 0; p0 < P; p0 += S::ROWS_IT) {
-            const int p = p0 + pl;
+#pragma unroll
+        for (int it = 0; it < S::ITERS_R; ++it) {
+            const int p = it * S::ROWS_IT + pl;
             const bool active = p < P;
             if (active) {
-                const float2* ya_row = rp + p * my;
-                const float2* yb_row = rp + (p + P) * my;
-#pragma unroll
-                for (int j = 0; j < R1W / R2W; ++j) {
-                    const int k1 = t + R2W * j;
-                    float2 u[R2W];
-#pragma unroll
-                    for (int k2 = 0; k2 < R2W; ++k2) {
-                        const int k = k1 + R1W * k2;
-                        const int kk = k <= W / 2 ? k : W - k;
-                        float2 z = make_float2(0.0f, 0.0f);
-                        if (kk < my) {
-                            const float2 ya = ya_row[kk];
-                            const float2 yb = yb_row[kk];
-                            if (kk == 0 || 2 * kk == W) z = make_float2(ya.x, yb.x);
-                            else if (k == kk) z = make_float2(ya.x - yb.y, ya.y + yb.x);
-                            else z = make_float2(ya.x + yb.y, yb.x - ya.y);
-                        }
-                        u[k2] = z;
+                const float2* ya_row = rp + p * ms;
+                const float2* yb_row = rp + (p + P) * ms;
+                auto zin = [&](int k) {
+                    const int kk = k <= W / 2 ? k : W - k;
+                    float2 z = make_float2(0.0f, 0.0f);
+                    if (kk < my) {
+                        const float2 ya = ya_row[kk];
+                        const float2 yb = yb_row[kk];
+                        if (kk == 0 || 2 * kk == W) z = make_float2(ya.x, yb.x);
+                        else if (k == kk) z = make_float2(ya.x - yb.y, ya.y + yb.x);
+                        else z = make_float2(ya.x + yb.y, yb.x - ya.y);
                     }
-                    dft<R2W, +1>(u);
+                    return z;
+                };
 #pragma unroll
-                    for (int tt = 1; tt < R2W; ++tt) u[tt] = cmul(u[tt], conjf2(twW[(tt * k1) & (W - 1)]));
+                for (int jj = 0; jj < MW / TW; ++jj) {
+                    const int k1 = t + TW * jj;
+                    float2 u0[TW], u1[TW];
 #pragma unroll
-                    for (int tt = 0; tt < R2W; ++tt) xb[tt * S::XSW + k1] = u[tt];
+                    for (int k2 = 0; k2 < TW; ++k2) {
+                        const int kh = k1 + MW * k2;                    // < W/2
+                        const float2 zl = zin(kh);
+                        const float2 zh = zin(kh + W / 2);
+                        u0[k2] = cadd(zl, zh);
+                        u1[k2] = cmul(csub(zl, zh), conjf2(twW[kh]));
+                    }
+                    dft<TW, +1>(u0);
+                    dft<TW, +1>(u1);
+#pragma unroll
+                    for (int tt = 0; tt < TW; ++tt) {
+                        const float2 w = conjf2(twW[(2 * tt * k1) & (W - 1)]);   // W_{W/2}^{+tt k1}
+                        xbr[tt * S::XSW + k1] = cmul(u0[tt], w);
+                        xbr[tt * S::XSW + MW + k1] = cmul(u1[tt], w);
+                    }
                 }
             }
-            __syncthreads();
+            lds_barrier();
             if (active) {
-                float2 v[R1W];
+                float2 v0[MW], v1[MW];
 #pragma unroll
-                for (int k1 = 0; k1 < R1W; ++k1) v[k1] = xb[t * S::XSW + k1];
-                dft<R1W, +1>(v);
-                float* oa = oi + p * W;
-                float* ob = oa + P * W;
+                for (int k1 = 0; k1 < MW; ++k1) {
+                    v0[k1] = xbr[t * S::XSW + k1];
+                    v1[k1] = xbr[t * S::XSW + MW + k1];
+                }
+                dft<MW, +1>(v0);
+                dft<MW, +1>(v1);
+                float2* oa = reinterpret_cast<float2*>(oi + p * W) + t;
+                float2* ob = reinterpret_cast<float2*>(oi + (p + P) * W) + t;
 #pragma unroll
-                for (int m = 0; m < R1W; ++m) {
-                    oa[t + R2W * m] = v[m].x * scale;
-                    ob[t + R2W * m] = v[m].y * scale;
+                for (int m = 0; m < MW; ++m) {
+                    oa[TW * m] = make_float2(v0[m].x * scale, v1[m].x * scale);
+                    ob[TW * m] = make_float2(v0[m].y * scale, v1[m].y * scale);
                 }
             }
-            __syncthreads();
+            lds_barrier();
         }
+        L = Ln;
+        if (L >= nimg) break;
     }
 }
 
@@ -313,23 +470,43 @@ ModeAddr make_addr(const SpecLayout& l) {
     return a;
 }
 
+// Persistent grid: a multiple of 16 workgroups (see paired_image), at most
+// kSmallBlocksPerCU per CU, never more than there are images.
+unsigned persistent_grid(int64_t nimg) {
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) == hipSuccess) {
+        int v = 0;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) cus = v;
+    }
+    int64_t g = (int64_t)cus * kSmallBlocksPerCU;
+    g = (g / 16) * 16;
+    if (g < 16) g = 16;
+    if (g > nimg) g = nimg;
+    return (unsigned)g;
+}
+
 }  // namespace
 
 bool small2d_supported(int log2H, int log2W, int my) {
     if (log2H < 3 || log2H > 7 || log2W < 3 || log2W > 7) return false;
-    const size_t need = sizeof(float2) * ((size_t)(1 << log2W) + (1 << log2H) + (size_t)(1 << log2H) * my + 256 * 17);
+    // the my kept columns must fit one column batch of the workgroup
+    const int r2h = log2H == 3 ? 2 : log2H <= 5 ? 4 : 8;
+    if (my > kSmallThreads / r2h) return false;
+    const size_t need = sizeof(float2) * ((size_t)(1 << log2W) + (1 << log2H) + (size_t)(1 << log2H) * (my + 16) +
+                                          256 * 18);
     return need <= 150 * 1024;
 }
 
 hipError_t launch_fwd2d_small(const float* x, float2* xh, const SpecLayout& lay, int64_t nimg, int log2H, int log2W,
                               int mx, int my, float scale, const float2* tw, hipStream_t s) {
     const ModeAddr ma = make_addr(lay);
+    const dim3 grid(persistent_grid(nimg));
     switch (log2H * 16 + log2W) {
 #define CASE(LH, LW)                                                                                          \
     case LH * 16 + LW: {                                                                                      \
         const size_t lds = SmallPlan<LH, LW>::lds_bytes(my);                                                  \
-        hipLaunchKernelGGL((k_fwd2d_small<LH, LW>), dim3((unsigned)nimg), dim3(kSmallThreads), lds, s, x, xh, \
-                           ma, mx, my, scale, tw);                                                            \
+        hipLaunchKernelGGL((k_fwd2d_small<LH, LW>), grid, dim3(kSmallThreads), lds, s, x, xh, ma, nimg, mx, my, \
+                           scale, tw);                                                                        \
         break;                                                                                                \
     }
         FNO_SMALL_CASES(CASE)
@@ -342,12 +519,13 @@ hipError_t launch_fwd2d_small(const float* x, float2* xh, const SpecLayout& lay,
 hipError_t launch_inv2d_small(const float2* yh, float* out, const SpecLayout& lay, int64_t nimg, int log2H, int log2W,
                               int mx, int my, float scale, const float2* tw, hipStream_t s) {
     const ModeAddr ma = make_addr(lay);
+    const dim3 grid(persistent_grid(nimg));
     switch (log2H * 16 + log2W) {
 #define CASE(LH, LW)                                                                                            \
     case LH * 16 + LW: {                                                                                        \
         const size_t lds = SmallPlan<LH, LW>::lds_bytes(my);                                                    \
-        hipLaunchKernelGGL((k_inv2d_small<LH, LW>), dim3((unsigned)nimg), dim3(kSmallThreads), lds, s, yh, out, \
-                           ma, mx, my, scale, tw);                                                              \
+        hipLaunchKernelGGL((k_inv2d_small<LH, LW>), grid, dim3(kSmallThreads), lds, s, yh, out, ma, nimg, mx, my, \
+                           scale, tw);                                                                          \
         break;                                                                                                  \
     }
         FNO_SMALL_CASES(CASE)
