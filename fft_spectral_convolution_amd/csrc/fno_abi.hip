@@ -195,7 +195,7 @@ bool use_mfma_mix(int64_t B, int64_t Cin, int64_t Cout) { return B >= 8 && Cin >
 int run_mix(const float2* xh, const SpecLayout& lx, const float2* w, float2* yh, const SpecLayout& ly, int64_t B,
             int64_t Cin, int64_t Cout, int64_t M, hipStream_t st) {
     hipError_t e;
-    if (use_mfma_mix(B, Cin, Cout)) {
+    if (use_mfma_mix(B, Cin, Cout) && mix_mfma_supported(Cout, w)) {
         rec_kernel("mix_mfma", st);
         e = launch_mix_mfma(xh, lx, w, yh, ly, B, Cin, Cout, M, st);
     } else {

@@ -46,6 +46,8 @@ hipError_t launch_inv2d_small(const float2* yh, float* out, const SpecLayout& la
 
 // ---- channel mix on MFMA (fno_mix.hip) --------------------------------------
 // yh(b, o, m) = sum_i xh(b, i, m) * w[m][i][o], spectra addressed by layouts.
+// Needs an even Cout and a 16-byte aligned w (float4 weight pairs).
+bool mix_mfma_supported(int64_t Cout, const void* w);
 hipError_t launch_mix_mfma(const float2* xh, const SpecLayout& lx, const float2* w, float2* yh,
                            const SpecLayout& ly, int64_t B, int64_t Cin, int64_t Cout, int64_t M, hipStream_t s);
 

@@ -151,6 +151,9 @@ EDGE_2D = [
     (1, 2, 2, 4096, 4, 3, 2),       # longest columns
     (1, 2, 1, 4, 4096, 2, 100),     # longest rows
     (9, 1, 1, 128, 128, 64, 65),    # odd batch, full modes
+    (9, 12, 18, 16, 16, 3, 5),      # matrix-core mix: ragged batch, channels and modes (30 modes)
+    (40, 16, 34, 32, 32, 4, 4),     # matrix-core mix: two batch tiles, ragged output tile
+    (33, 64, 66, 64, 64, 8, 8),     # matrix-core mix: 64+2 output channels, 33 batch rows
 ]
 
 
