@@ -238,7 +238,9 @@ int run_forward2d_small(const Shape2d& s, int64_t C, const float* x, float2* xh,
                         const float2* tw, hipStream_t st) {
     const float scale = (float)(1.0 / std::sqrt((double)s.H * (double)s.W));
     rec_kernel("fwd2d", st);
-    hipError_t e = launch_fwd2d_small(x, xh, lay, s.B * C, s.log2H, s.log2W, s.mx, s.my, scale, tw, st);
+    hipError_t e = rowreg2d_supported(s.log2H, s.log2W, s.mx, s.my, lay)
+                       ? launch_fwd2d_rowreg(x, xh, lay, s.B * C, s.log2H, s.log2W, s.mx, s.my, tw, st)
+                       : launch_fwd2d_small(x, xh, lay, s.B * C, s.log2H, s.log2W, s.mx, s.my, scale, tw, st);
     return e == hipSuccess ? FNO_OK : hip_fail(e);
 }
 

@@ -15,6 +15,9 @@
 
 #include <hip/hip_runtime.h>
 
+#include <cstdint>
+#include <type_traits>
+
 namespace fno {
 
 constexpr int kLog2NMax = 12;            // longest transform: 4096 points
@@ -48,6 +51,49 @@ __host__ __device__ constexpr float cos16(int e) {
 }
 
 __host__ __device__ constexpr float sin16(int e) { return cos16(e - 4); }  // sin x = cos(x - pi/2)
+
+// Compile-time cos / sin of 2 pi e / N for the register-resident transforms:
+// argument reduction to [0, pi/4] by octant symmetries, then Taylor series in
+// double (terms to x^29; |x| <= pi/4 so the remainder is far below double
+// rounding), rounded once to float.
+constexpr double kPi = 3.14159265358979323846264338327950288;
+
+constexpr double taylor_cos(double x) {
+    double term = 1.0, sum = 1.0;
+    for (int k = 1; k <= 15; ++k) {
+        term *= -x * x / ((2.0 * k - 1.0) * (2.0 * k));
+        sum += term;
+    }
+    return sum;
+}
+constexpr double taylor_sin(double x) {
+    double term = x, sum = x;
+    for (int k = 1; k <= 15; ++k) {
+        term *= -x * x / ((2.0 * k) * (2.0 * k + 1.0));
+        sum += term;
+    }
+    return sum;
+}
+// cos(2 pi e / n) and sin(2 pi e / n) for integer e, n a multiple of 8
+constexpr double exact_cos(int e, int n) {
+    e = ((e % n) + n) % n;
+    const int oct = n / 8;                    // e in octant e / oct
+    const int o = e / oct;
+    const int r = e % oct;
+    const double a = 2.0 * kPi * r / n;       // in [0, pi/4)
+    const double b = 2.0 * kPi * (oct - r) / n;
+    switch (o) {
+        case 0: return taylor_cos(a);
+        case 1: return taylor_sin(b);
+        case 2: return -taylor_sin(a);
+        case 3: return -taylor_cos(b);
+        case 4: return -taylor_cos(a);
+        case 5: return -taylor_sin(b);
+        case 6: return taylor_sin(a);
+        default: return taylor_cos(b);
+    }
+}
+constexpr double exact_sin(int e, int n) { return exact_cos(e - n / 4, n); }
 
 __device__ __forceinline__ float2 cadd(float2 a, float2 b) { return make_float2(a.x + b.x, a.y + b.y); }
 __device__ __forceinline__ float2 csub(float2 a, float2 b) { return make_float2(a.x - b.x, a.y - b.y); }
@@ -83,16 +129,50 @@ __device__ __forceinline__ float2 w16mul(float2 v, int e) {
     return make_float2(v.x * c - v.y * s, v.x * s + v.y * c);
 }
 
-// In-register DFT of size R <= 16, natural order in and out:
+// v * exp(SIGN * 2 pi i * E / N), N a power of two >= 8.  E is a template
+// argument so the constants are folded at compile time.
+template <int SIGN, int N, int E>
+__device__ __forceinline__ float2 wmul(float2 v) {
+    constexpr int e = E & (N - 1);
+    if constexpr (e == 0) {
+        return v;
+    } else if constexpr (4 * e == N) {
+        return mul_i<SIGN>(v);
+    } else if constexpr (2 * e == N) {
+        return make_float2(-v.x, -v.y);
+    } else if constexpr (4 * e == 3 * N) {
+        return mul_i<-SIGN>(v);
+    } else if constexpr (8 * e == N || 8 * e == 3 * N || 8 * e == 5 * N || 8 * e == 7 * N) {
+        // |cos| = |sin| = cos(pi/4): two adds and two multiplies
+        constexpr float sc = exact_cos(e, N) < 0 ? -1.0f : 1.0f;
+        constexpr float ss = SIGN * exact_sin(e, N) < 0 ? -1.0f : 1.0f;
+        return make_float2((v.x * sc - v.y * ss) * kSqrtHalf, (v.x * ss + v.y * sc) * kSqrtHalf);
+    } else {
+        constexpr float c = (float)exact_cos(e, N);
+        constexpr float s = (float)(SIGN * exact_sin(e, N));
+        return make_float2(v.x * c - v.y * s, v.x * s + v.y * c);
+    }
+}
+
+// Calls f(std::integral_constant<int, I>) for I = B, ..., E-1 in order.
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (B < E) {
+        [[clang::always_inline]] f(std::integral_constant<int, B>{});
+        static_for<B + 1, E>(f);
+    }
+}
+
+// In-register DFT of size R <= 64, natural order in and out:
 // v[k] <- sum_r v[r] exp(SIGN 2 pi i r k / R).  Radix-2 decimation in time.
 template <int R, int SIGN>
 __device__ __forceinline__ void dft(float2 (&v)[R]) {
-    static_assert(R >= 1 && R <= 16 && (R & (R - 1)) == 0, "radix must be a power of two <= 16");
+    static_assert(R >= 1 && R <= 64 && (R & (R - 1)) == 0, "radix must be a power of two <= 64");
     if constexpr (R == 2) {
         const float2 a = v[0], b = v[1];
         v[0] = cadd(a, b);
         v[1] = csub(a, b);
-    } else if constexpr (R > 2) {
+    } else if constexpr (R > 2 && R <= 16) {
         constexpr int HALF = R / 2;
         float2 e[HALF], o[HALF];
 #pragma unroll
@@ -108,6 +188,20 @@ __device__ __forceinline__ void dft(float2 (&v)[R]) {
             v[k] = cadd(e[k], t);
             v[k + HALF] = csub(e[k], t);
         }
+    } else if constexpr (R > 16) {
+        constexpr int HALF = R / 2;
+        float2 e[HALF], o[HALF];
+        static_for<0, HALF>([&](auto i) {
+            e[i] = v[2 * i];
+            o[i] = v[2 * i + 1];
+        });
+        dft<HALF, SIGN>(e);
+        dft<HALF, SIGN>(o);
+        static_for<0, HALF>([&](auto k) {
+            const float2 t = wmul<SIGN, R, k>(o[k]);
+            v[k] = cadd(e[k], t);
+            v[k + HALF] = csub(e[k], t);
+        });
     }
 }
 
@@ -122,6 +216,49 @@ __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
     __builtin_amdgcn_sched_barrier(0);
+}
+
+// Orders LDS accesses between the lanes of one wave (LDS operations of a wave
+// complete in issue order; this only stops the compiler from moving them).
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+}
+
+// Raw buffer resource over `bytes` bytes at `base` (gfx9 word 3: 32-bit
+// data format, no swizzle, no stride).  The hardware range-checks every
+// access: a load at a byte offset >= bytes returns zero and such a store is
+// dropped, so an offset of kBufferSkip turns a store off without a branch.
+constexpr uint32_t kBufferSkip = 0x80000000u;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+typedef unsigned int u32x2_t __attribute__((__vector_size__(2 * sizeof(unsigned int))));
+typedef unsigned int u32x4_t __attribute__((__vector_size__(4 * sizeof(unsigned int))));
+
+__device__ __forceinline__ float4 buffer_load_f4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0);
+    return make_float4(__uint_as_float(v[0]), __uint_as_float(v[1]), __uint_as_float(v[2]), __uint_as_float(v[3]));
+}
+
+__device__ __forceinline__ void buffer_store_f2(float2 a, __amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    u32x2_t v;
+    v[0] = __float_as_uint(a.x);
+    v[1] = __float_as_uint(a.y);
+    __builtin_amdgcn_raw_buffer_store_b64(v, r, (int)voff, (int)soff, 0);
+}
+
+// Logical work index -> image.  Indices L and L + 8 (same XCD under
+// round-robin workgroup dispatch, same step of the persistent loop when the
+// grid is a multiple of 16) get images 2j and 2j + 1.
+__device__ __forceinline__ int64_t paired_image(int64_t L, int64_t nimg) {
+    const int64_t g = L >> 4;
+    if ((g + 1) * 16 > nimg) return L;
+    const int r = (int)(L & 15);
+    return g * 16 + 2 * (r & 7) + (r >> 3);
 }
 
 // Twiddle exp(SIGN 2 pi i m / kNMax) from the host-built table of exp(-2 pi i m / kNMax).

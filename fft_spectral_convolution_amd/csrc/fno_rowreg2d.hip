@@ -1,0 +1,293 @@
+// Forward transform with register-resident rows, for 64x64 .. 128x128 grids.
+//
+// Row pass: one thread per real row.  The row is taken as W/2 complex
+// samples z[n] = x[2n] + i x[2n+1] and the whole W/2-point DFT runs in the
+// thread's registers, with no exchange and no barrier.  The real row's half
+// spectrum follows from the even / odd split (FFT blog, section 2.2: R2C
+// keeps the N/2+1 half spectrum):
+//   a = Z[k] + conj Z[W/2-k],  b = Z[k] - conj Z[W/2-k],
+//   X[k] = a / 2 + W_W^k (-i / 2) b,   k < my,
+// with the ortho factor (HW)^-1/2 folded into those constants.
+// Column pass (TurboFNO blog, sections 2.1-2.2: the second 1D transform of
+// the 2D one, only the kept kx written): the X plane sits in LDS; batches of
+// KB columns are split H = R1 * R2 (R1 points per thread: an R1-point DFT
+// in registers, the twiddle W_H^{t k1}, a hand-over through LDS, R2-point
+// DFTs across threads) and only kx in [0,mx) u [H-mx,H) are stored.
+//
+// Data movement: the rows arrive through coalesced loads (8 lanes per
+// 128-byte run) and a wave-private LDS transpose hands each lane its own row.
+// The transpose stage, the X plane and the hand-over buffers share one LDS
+// region (about 35 KiB at 128 x 128), so four workgroups of two waves fit on
+// a CU: two waves per SIMD, one doing VALU work while the other waits on LDS
+// or HBM.  The grid is persistent (as many workgroups as fit), each walking
+// images in XCD-paired order; the output goes through buffer stores whose
+// hardware range check drops the outputs of dropped modes.
+#include <cstdint>
+
+#include "fno_device.hpp"
+#include "fno_internal.hpp"
+
+namespace fno {
+namespace {
+
+template <int N> struct ColSplit;
+template <> struct ColSplit<64>  { static constexpr int R1 = 8,  R2 = 8; };
+template <> struct ColSplit<128> { static constexpr int R1 = 16, R2 = 8; };
+
+// Base of image img = b * C + c in a mode-addressed spectrum (complex elements).
+struct ImageBase {
+    int64_t sb, sc;
+    int C;
+    __device__ __forceinline__ int64_t operator()(int64_t img) const {
+        const uint32_t i32 = (uint32_t)img;
+        const uint32_t b = i32 / (uint32_t)C;
+        const uint32_t c = i32 - b * (uint32_t)C;
+        return (int64_t)b * sb + (int64_t)c * sc;
+    }
+};
+
+// 2^(-e/2)
+constexpr double inv_sqrt_pow2(int e) {
+    double v = 1.0;
+    for (int i = 0; i < e / 2; ++i) v *= 0.5;
+    return (e & 1) ? v * 0.70710678118654752440 : v;
+}
+
+template <int LOG2H, int LOG2W, int MYMAX>
+struct RowPlan {
+    static constexpr int H = 1 << LOG2H;
+    static constexpr int W = 1 << LOG2W;
+    static constexpr int NZ = W / 2;                // complex samples per row
+    static constexpr int NT = H;                    // threads: one per row
+    static constexpr int F4 = W / 4;                // float4 per row
+    static constexpr int NCK = F4 / 8;              // 128-byte runs per row
+    static constexpr int R1 = ColSplit<H>::R1;
+    static constexpr int R2 = ColSplit<H>::R2;
+    static constexpr int NJ = R1 / R2;              // second-stage DFTs per thread
+    static constexpr int KB = NT / R2;              // columns per batch
+    static constexpr int NB = MYMAX / KB;           // batches
+    static constexpr int PS = MYMAX + 1;            // plane row stride (odd)
+    static constexpr int XS = R1 + 1;               // hand-over slot stride (odd)
+    static constexpr int GS = (R2 * XS) | 1;        // hand-over column stride (odd)
+    static constexpr int SS = 36;                   // transpose stage row stride (floats)
+    static constexpr int PLANE = H * PS;            // complex elements
+    static constexpr int XBUF = KB * GS;
+    static constexpr int XBUFS = NB * XBUF;         // one hand-over buffer per batch
+    static constexpr int STAGE = NT * SS / 2;
+    static constexpr int XREG = XBUFS > STAGE ? XBUFS : STAGE;
+    // the stage, the plane and the hand-over buffers share one region,
+    // behind a table of the column twiddles W_H^j
+    static constexpr int REGION = H + (PLANE > XREG ? PLANE : XREG);
+    static_assert(MYMAX % KB == 0 && MYMAX <= NZ, "column batches");
+    static_assert(R1 % R2 == 0, "column split");
+    static size_t lds_bytes() { return sizeof(float2) * (size_t)REGION; }
+};
+
+// Bin K of the scaled half spectrum of a real row of length W from its packed
+// transform Z (NZ = W/2 points), s = 2^(-LOG2HW/2):
+//   s X[K] = (s/2) a + c b,   c = (s/2) (-i) W_W^K = (s/2) (-sin, -cos)(2 pi K / W).
+template <int W, int K, int NZ, int LOG2HW>
+__device__ __forceinline__ float2 half_bin_scaled(const float2 (&z)[NZ]) {
+    constexpr double hs = 0.5 * inv_sqrt_pow2(LOG2HW);
+    constexpr float h = (float)hs;
+    const float2 zk = z[K % NZ];
+    const float2 zm = z[(NZ - K % NZ) % NZ];
+    const float ax = zk.x + zm.x, ay = zk.y - zm.y;
+    const float bx = zk.x - zm.x, by = zk.y + zm.y;
+    constexpr double sn = exact_sin(K, W), cs = exact_cos(K, W);
+    float tx, ty;
+    if constexpr (sn == 0.0) {          // c = (0, -h cos)
+        constexpr float ci = (float)(-hs * cs);
+        tx = -by * ci;
+        ty = bx * ci;
+    } else if constexpr (cs == 0.0) {   // c = (-h sin, 0)
+        constexpr float cr = (float)(-hs * sn);
+        tx = bx * cr;
+        ty = by * cr;
+    } else {
+        constexpr float cr = (float)(-hs * sn), ci = (float)(-hs * cs);
+        tx = fmaf(bx, cr, -by * ci);
+        ty = fmaf(bx, ci, by * cr);
+    }
+    return make_float2(fmaf(h, ax, tx), fmaf(h, ay, ty));
+}
+
+template <int LOG2H, int LOG2W, int MYMAX>
+__global__ __launch_bounds__(1 << LOG2H) __attribute__((amdgpu_waves_per_eu(2))) void k_fwd2d_rows(const float* __restrict__ x, float2* __restrict__ xh,
+                                                           ImageBase ib, int st, int64_t nimg, int mx, int my,
+                                                           const float2* __restrict__ tw) {
+    using S = RowPlan<LOG2H, LOG2W, MYMAX>;
+    constexpr int H = S::H, W = S::W, NZ = S::NZ, F4 = S::F4, R1 = S::R1, R2 = S::R2, KB = S::KB, NB = S::NB,
+                  NJ = S::NJ;
+    extern __shared__ float2 smem[];
+    float2* const twH = smem;                   // W_H^j, j < H
+    float2* const plane = smem + H;             // [H][PS]: scaled X of every row
+    float2* const xreg = smem + H;              // transpose stage / hand-over buffers (same region)
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int t = tid / KB;                     // column pass: slot t of column cl
+    const int cl = tid % KB;
+    twH[tid] = tw[tid * (kNMax / H)];           // NT == H: one entry per thread
+
+    // Per-thread constants for the stores: q * my for every output (k1 = t +
+    // R2 jj, k2) of the last column stage, where q is the row of kx = k1 +
+    // R1 k2 in the truncated spectrum (-1: kx is not kept).
+    int qm[NJ][R2];
+#pragma unroll
+    for (int jj = 0; jj < NJ; ++jj)
+#pragma unroll
+        for (int k2 = 0; k2 < R2; ++k2) {
+            const int kx = t + R2 * jj + R1 * k2;
+            const int q = kx < mx ? kx : (kx >= H - mx ? kx - (H - 2 * mx) : -1);
+            qm[jj][k2] = q < 0 ? -1 : q * my;
+        }
+    const uint32_t out_bytes = (uint32_t)((((2 * mx * my) - 1) >> 3) * st + 8) * 8u;
+    const uint32_t st8 = (uint32_t)(st - 8);
+
+    // Coalesced row loads: load i = (run c, group ii) of lane l reads float4
+    // 8c + (l & 7) of row 8 ii + (l >> 3) of the wave's 64 rows.
+    uint32_t loff[8];
+#pragma unroll
+    for (int ii = 0; ii < 8; ++ii) loff[ii] = (uint32_t)(((tid & ~63) + 8 * ii + (lane >> 3)) * F4 + (lane & 7)) * 16u;
+    float2 ld[2 * F4];
+    auto issue = [&](int64_t img) __attribute__((always_inline)) {
+        const __amdgpu_buffer_rsrc_t r = make_rsrc(x + img * (int64_t)(H * W), (uint32_t)(H * W * 4));
+        static_for<0, F4>([&](auto i) {
+            constexpr int c = i / 8, ii = i % 8;
+            const float4 v = buffer_load_f4(r, loff[ii] + 128 * c, 0);
+            ld[2 * i] = make_float2(v.x, v.y);
+            ld[2 * i + 1] = make_float2(v.z, v.w);
+        });
+    };
+
+    const int64_t G = gridDim.x;
+    int64_t L = blockIdx.x;
+    for (; L < nimg; L += G) {
+        const int64_t img = paired_image(L, nimg);
+        issue(img);
+        lds_barrier();                          // the previous image is out of the shared region
+
+        // ---- hand the loaded rows over: lane l gets row l of its wave ------
+        float2 z[NZ];
+        {
+            float* stage = reinterpret_cast<float*>(xreg) + (tid >> 6) * 64 * S::SS;
+            static_for<0, S::NCK>([&](auto c) {
+                static_for<0, 8>([&](auto ii) {
+                    constexpr int i = c * 8 + ii;
+                    *reinterpret_cast<float4*>(stage + (8 * ii + (lane >> 3)) * S::SS + 4 * (lane & 7)) =
+                        make_float4(ld[2 * i].x, ld[2 * i].y, ld[2 * i + 1].x, ld[2 * i + 1].y);
+                });
+                wave_lds_sync();
+                static_for<0, 8>([&](auto q) {
+                    const float4 v = *reinterpret_cast<const float4*>(stage + lane * S::SS + 4 * q);
+                    z[2 * (8 * c + q)] = make_float2(v.x, v.y);
+                    z[2 * (8 * c + q) + 1] = make_float2(v.z, v.w);
+                });
+                wave_lds_sync();
+            });
+        }
+        lds_barrier();                          // every wave is out of the stage before the plane is written
+
+        // ---- row tid: packed W/2-point DFT, scaled half spectrum -> plane --
+        dft<NZ, -1>(z);
+        static_for<0, MYMAX>([&](auto k) {
+            plane[tid * S::PS + k] = half_bin_scaled<W, k, NZ, LOG2H + LOG2W>(z);
+        });
+        lds_barrier();
+
+        // ---- columns: every batch's first stage, one hand-over, last stage -
+        float2 v[NB][R1];
+        static_for<0, NB>([&](auto bt) {
+#pragma unroll
+            for (int m = 0; m < R1; ++m) v[bt][m] = plane[(t + R2 * m) * S::PS + bt * KB + cl];
+        });
+        lds_barrier();                          // the plane is read before the hand-over overwrites it
+        static_for<0, NB>([&](auto bt) {
+            dft<R1, -1>(v[bt]);
+#pragma unroll
+            for (int k1 = 1; k1 < R1; ++k1) v[bt][k1] = cmul(v[bt][k1], twH[(t * k1) & (H - 1)]);
+            float2* const xb = xreg + bt * S::XBUF + cl * S::GS + t * S::XS;
+#pragma unroll
+            for (int k1 = 0; k1 < R1; ++k1) xb[k1] = v[bt][k1];
+        });
+        lds_barrier();
+        const __amdgpu_buffer_rsrc_t ro = make_rsrc(xh + ib(img), out_bytes);
+        static_for<0, NB>([&](auto bt) {
+            const float2* const xb = xreg + bt * S::XBUF + cl * S::GS;
+            const int ky = bt * KB + cl;
+            const bool kyok = ky < my;
+#pragma unroll
+            for (int jj = 0; jj < NJ; ++jj) {
+                const int k1 = t + R2 * jj;
+                float2 u[R2];
+#pragma unroll
+                for (int tt = 0; tt < R2; ++tt) u[tt] = xb[tt * S::XS + k1];
+                dft<R2, -1>(u);
+#pragma unroll
+                for (int k2 = 0; k2 < R2; ++k2) {
+                    // mode m = q my + ky at (m >> 3) st + (m & 7) = m + (m >> 3)(st - 8)
+                    const int q = qm[jj][k2];
+                    const uint32_t m = (uint32_t)(q + ky);
+                    const uint32_t off = (q < 0 || !kyok) ? kBufferSkip : (m + (m >> 3) * st8) * 8u;
+                    buffer_store_f2(u[k2], ro, off, 0);
+                }
+            }
+        });
+    }
+}
+
+template <int LH, int LW, int MYM>
+hipError_t launch_one(const float* x, float2* xh, const ImageBase& ib, int st, int64_t nimg, int mx, int my,
+                      const float2* tw, hipStream_t s) {
+    using P = RowPlan<LH, LW, MYM>;
+    static int per_cu = 0;                      // resident workgroups per CU for this instance
+    static int cus = 0;
+    if (per_cu == 0) {
+        int dev = 0, v = 0, n = 0;
+        if (hipGetDevice(&dev) != hipSuccess) return hipErrorInvalidDevice;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+        const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_fwd2d_rows<LH, LW, MYM>, P::NT,
+                                                                          P::lds_bytes());
+        if (e != hipSuccess) return e;
+        cus = v;
+        per_cu = n > 0 ? n : 1;
+    }
+    int64_t g = (int64_t)cus * per_cu;
+    g = g >= 16 ? (g / 16) * 16 : g;            // whole groups of 16 for the XCD pairing
+    if (g > nimg) g = nimg;
+    hipLaunchKernelGGL((k_fwd2d_rows<LH, LW, MYM>), dim3((unsigned)g), dim3(P::NT), P::lds_bytes(), s, x, xh, ib,
+                       st, nimg, mx, my, tw);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+bool rowreg2d_supported(int log2H, int log2W, int mx, int my, const SpecLayout& lay) {
+    // byte offsets inside one image's spectrum stay below kBufferSkip
+    const int64_t tiles = ((int64_t)2 * mx * my + 7) / 8;
+    return (log2H == 6 || log2H == 7) && (log2W == 6 || log2W == 7) && my <= 32 && lay.st >= 8 &&
+           (tiles * lay.st + 8) * 8 < (int64_t)kBufferSkip;
+}
+
+hipError_t launch_fwd2d_rowreg(const float* x, float2* xh, const SpecLayout& lay, int64_t nimg, int log2H,
+                               int log2W, int mx, int my, const float2* tw, hipStream_t s) {
+    if (!rowreg2d_supported(log2H, log2W, mx, my, lay) || nimg >= INT32_MAX) return hipErrorInvalidValue;
+    ImageBase ib;
+    ib.sb = lay.sb;
+    ib.sc = lay.sc;
+    ib.C = lay.C;
+    const int st = (int)lay.st;
+#define FNO_ROWREG(LH, LW)                                                                             \
+    if (log2H == LH && log2W == LW)                                                                    \
+        return my <= 16 ? launch_one<LH, LW, 16>(x, xh, ib, st, nimg, mx, my, tw, s)                  \
+                        : launch_one<LH, LW, 32>(x, xh, ib, st, nimg, mx, my, tw, s);
+    FNO_ROWREG(7, 7)
+    FNO_ROWREG(6, 6)
+    FNO_ROWREG(7, 6)
+    FNO_ROWREG(6, 7)
+#undef FNO_ROWREG
+    return hipErrorInvalidValue;
+}
+
+}  // namespace fno

@@ -68,16 +68,6 @@ struct ModeAddr {
     __device__ __forceinline__ int64_t off(int m) const { return (int64_t)(m >> 3) * st + (m & 7); }
 };
 
-// Logical work index -> image.  Indices L and L + 8 (same XCD under
-// round-robin workgroup dispatch, same step of the persistent loop when the
-// grid is a multiple of 16) get images 2j and 2j + 1.
-__device__ __forceinline__ int64_t paired_image(int64_t L, int64_t nimg) {
-    const int64_t g = L >> 4;
-    if ((g + 1) * 16 > nimg) return L;
-    const int r = (int)(L & 15);
-    return g * 16 + 2 * (r & 7) + (r >> 3);
-}
-
 // Rows: a complex row of length W is split as n = q + 2 (t + T m) with
 // q in {0,1} held in one thread (so every lane moves float2 pairs), t < T
 // across the T lanes of the row and m < M in registers (W / 2 = T * M).  The

@@ -154,6 +154,10 @@ EDGE_2D = [
     (9, 12, 18, 16, 16, 3, 5),      # matrix-core mix: ragged batch, channels and modes (30 modes)
     (40, 16, 34, 32, 32, 4, 4),     # matrix-core mix: two batch tiles, ragged output tile
     (33, 64, 66, 64, 64, 8, 8),     # matrix-core mix: 64+2 output channels, 33 batch rows
+    (3, 2, 5, 128, 128, 7, 13),     # one-row-per-thread forward: ragged column batch
+    (2, 3, 4, 64, 64, 32, 32),      # one-row-per-thread forward: every kx kept, two column batches
+    (2, 2, 2, 128, 64, 5, 17),      # one-row-per-thread forward: tall, my just past one batch
+    (2, 2, 2, 64, 128, 9, 3),       # one-row-per-thread forward: wide rows, few columns
 ]
 
 
