@@ -248,7 +248,9 @@ int run_inverse2d_small(const Shape2d& s, int64_t C, const float2* yh, float* ou
                         const float2* tw, hipStream_t st) {
     const float scale = (float)(1.0 / std::sqrt((double)s.H * (double)s.W));
     rec_kernel("inv2d", st);
-    hipError_t e = launch_inv2d_small(yh, out, lay, s.B * C, s.log2H, s.log2W, s.mx, s.my, scale, tw, st);
+    hipError_t e = rowreg2d_supported(s.log2H, s.log2W, s.mx, s.my, lay)
+                       ? launch_inv2d_rowreg(yh, out, lay, s.B * C, s.log2H, s.log2W, s.mx, s.my, tw, st)
+                       : launch_inv2d_small(yh, out, lay, s.B * C, s.log2H, s.log2W, s.mx, s.my, scale, tw, st);
     return e == hipSuccess ? FNO_OK : hip_fail(e);
 }
 

@@ -244,6 +244,20 @@ __device__ __forceinline__ float4 buffer_load_f4(__amdgpu_buffer_rsrc_t r, uint3
     return make_float4(__uint_as_float(v[0]), __uint_as_float(v[1]), __uint_as_float(v[2]), __uint_as_float(v[3]));
 }
 
+__device__ __forceinline__ float2 buffer_load_f2(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, (int)soff, 0);
+    return make_float2(__uint_as_float(v[0]), __uint_as_float(v[1]));
+}
+
+__device__ __forceinline__ void buffer_store_f4(float4 a, __amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    u32x4_t v;
+    v[0] = __float_as_uint(a.x);
+    v[1] = __float_as_uint(a.y);
+    v[2] = __float_as_uint(a.z);
+    v[3] = __float_as_uint(a.w);
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)voff, (int)soff, 0);
+}
+
 __device__ __forceinline__ void buffer_store_f2(float2 a, __amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
     u32x2_t v;
     v[0] = __float_as_uint(a.x);

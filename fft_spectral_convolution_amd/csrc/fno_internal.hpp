@@ -44,11 +44,14 @@ hipError_t launch_fwd2d_small(const float* x, float2* xh, const SpecLayout& lay,
 hipError_t launch_inv2d_small(const float2* yh, float* out, const SpecLayout& lay, int64_t nimg, int log2H,
                               int log2W, int mx, int my, float scale, const float2* tw, hipStream_t s);
 
-// ---- forward transform with one real row per thread (fno_rowreg2d.hip) -----
+// ---- 2D transforms with one real row per thread (fno_rowreg2d.hip) ---------
 // H, W in {64, 128}, my <= 32; same output as launch_fwd2d_small (scaled by
 // (HW)^-1/2).  Persistent grid sized from the kernel's occupancy.
 bool rowreg2d_supported(int log2H, int log2W, int mx, int my, const SpecLayout& lay);
 hipError_t launch_fwd2d_rowreg(const float* x, float2* xh, const SpecLayout& lay, int64_t nimg, int log2H,
+                               int log2W, int mx, int my, const float2* tw, hipStream_t s);
+// and its inverse: truncated spectrum -> real image, same shapes and scale
+hipError_t launch_inv2d_rowreg(const float2* yh, float* out, const SpecLayout& lay, int64_t nimg, int log2H,
                                int log2W, int mx, int my, const float2* tw, hipStream_t s);
 
 // ---- channel mix on MFMA (fno_mix.hip) --------------------------------------

@@ -237,28 +237,214 @@ __global__ __launch_bounds__(1 << LOG2H) __attribute__((amdgpu_waves_per_eu(2)))
     }
 }
 
-template <int LH, int LW, int MYM>
-hipError_t launch_one(const float* x, float2* xh, const ImageBase& ib, int st, int64_t nimg, int mx, int my,
-                      const float2* tw, hipStream_t s) {
-    using P = RowPlan<LH, LW, MYM>;
-    static int per_cu = 0;                      // resident workgroups per CU for this instance
-    static int cus = 0;
-    if (per_cu == 0) {
-        int dev = 0, v = 0, n = 0;
-        if (hipGetDevice(&dev) != hipSuccess) return hipErrorInvalidDevice;
-        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
-        const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_fwd2d_rows<LH, LW, MYM>, P::NT,
-                                                                          P::lds_bytes());
-        if (e != hipSuccess) return e;
-        cus = v;
-        per_cu = n > 0 ? n : 1;
+// Bin k of the packed inverse row spectrum, for the C2R of a real row of
+// length W whose half spectrum X is zero from MYMAX on (FFT blog, section
+// 2.2: C2R from the N/2+1 half spectrum, imaginary part of the DC bin
+// ignored).  With x[2n] + i x[2n+1] = IDFT_{W/2}(Z)[n]:
+//   Z[k] = s (X[k] + conj X[W/2-k]) + c (X[k] - conj X[W/2-k]),
+//   c = s i W_W^{-k} = s (-sin, cos)(2 pi k / W),   s = 2^(-LOG2HW/2).
+template <int W, int K, int MYMAX, int LOG2HW>
+__device__ __forceinline__ float2 packed_c2r_bin(const float2 (&X)[MYMAX]) {
+    constexpr int NZ = W / 2;
+    constexpr double s = inv_sqrt_pow2(LOG2HW);
+    constexpr double sn = exact_sin(K, W), cs = exact_cos(K, W);
+    constexpr bool has_k = K < MYMAX;
+    constexpr bool has_m = K > 0 && NZ - K < MYMAX;
+    if constexpr (K == 0) {
+        // X[0] real, X[W/2] = 0: Z[0] = s Re X[0] (1 + i)
+        const float v = (float)s * X[0].x;
+        return make_float2(v, v);
+    } else if constexpr (has_k && has_m) {
+        const float2 xk = X[K], xm = X[has_m ? NZ - K : 0];
+        const float ax = xk.x + xm.x, ay = xk.y - xm.y;
+        const float bx = xk.x - xm.x, by = xk.y + xm.y;
+        constexpr float cr = (float)(-s * sn), ci = (float)(s * cs), sf = (float)s;
+        return make_float2(fmaf(sf, ax, fmaf(bx, cr, -by * ci)), fmaf(sf, ay, fmaf(bx, ci, by * cr)));
+    } else if constexpr (has_k) {
+        // Z = (s + c) X[k]
+        constexpr float pr = (float)(s - s * sn), pi = (float)(s * cs);
+        const float2 xk = X[has_k ? K : 0];
+        return make_float2(fmaf(xk.x, pr, -xk.y * pi), fmaf(xk.x, pi, xk.y * pr));
+    } else if constexpr (has_m) {
+        // Z = (s - c) conj X[W/2-k]
+        constexpr float pr = (float)(s + s * sn), pi = (float)(-s * cs);
+        const float2 xm = X[has_m ? NZ - K : 0];
+        return make_float2(fmaf(xm.x, pr, xm.y * pi), fmaf(xm.x, pi, -xm.y * pr));
+    } else {
+        return make_float2(0.0f, 0.0f);
     }
-    int64_t g = (int64_t)cus * per_cu;
-    g = g >= 16 ? (g / 16) * 16 : g;            // whole groups of 16 for the XCD pairing
+}
+
+// Inverse of k_fwd2d_rows: truncated spectrum (kept kx only, ky < my, the
+// rest zero) -> real image, scaled by (HW)^-1/2.  Column pass first
+// (kx = k1 + R1 k2 -> h = t + R2 m: R2-point inverse DFTs over k2 read straight
+// from the spectrum, the hand-over, the twiddle conj W_H^{t k1}, R1-point
+// inverse DFTs over k1), its rows in the LDS plane; then one thread per row
+// builds the packed spectrum Z, runs the W/2-point inverse DFT in registers
+// and hands its row out through the stage to coalesced buffer stores.
+template <int LOG2H, int LOG2W, int MYMAX>
+__global__ __launch_bounds__(1 << LOG2H) __attribute__((amdgpu_waves_per_eu(2))) void k_inv2d_rows(
+    const float2* __restrict__ yh, float* __restrict__ out, ImageBase ib, int st, int64_t nimg, int mx, int my,
+    const float2* __restrict__ tw) {
+    using S = RowPlan<LOG2H, LOG2W, MYMAX>;
+    constexpr int H = S::H, W = S::W, NZ = S::NZ, F4 = S::F4, R1 = S::R1, R2 = S::R2, KB = S::KB, NB = S::NB,
+                  NJ = S::NJ;
+    extern __shared__ float2 smem[];
+    float2* const twH = smem;                   // W_H^j, j < H
+    float2* const plane = smem + H;             // [H][PS]: column-inverted spectrum, one row per thread
+    float2* const xreg = smem + H;              // hand-over buffers / output stage (same region)
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int t = tid / KB;                     // column pass: slot t of column cl
+    const int cl = tid % KB;
+    twH[tid] = tw[tid * (kNMax / H)];           // NT == H: one entry per thread
+
+    // q * my for every input (k1 = t + R2 jj, k2) of the first column stage
+    // (q: row of kx = k1 + R1 k2 in the truncated spectrum, -1: not kept)
+    int qm[NJ][R2];
+#pragma unroll
+    for (int jj = 0; jj < NJ; ++jj)
+#pragma unroll
+        for (int k2 = 0; k2 < R2; ++k2) {
+            const int kx = t + R2 * jj + R1 * k2;
+            const int q = kx < mx ? kx : (kx >= H - mx ? kx - (H - 2 * mx) : -1);
+            qm[jj][k2] = q < 0 ? -1 : q * my;
+        }
+    const uint32_t in_bytes = (uint32_t)((((2 * mx * my) - 1) >> 3) * st + 8) * 8u;
+    const uint32_t st8 = (uint32_t)(st - 8);
+    // coalesced output: store (run c, group ii) of lane l writes float4
+    // 8c + (l & 7) of row 8 ii + (l >> 3) of the wave's 64 rows
+    uint32_t soffs[8];
+#pragma unroll
+    for (int ii = 0; ii < 8; ++ii)
+        soffs[ii] = (uint32_t)(((tid & ~63) + 8 * ii + (lane >> 3)) * F4 + (lane & 7)) * 16u;
+
+    const int64_t G = gridDim.x;
+    for (int64_t L = blockIdx.x; L < nimg; L += G) {
+        const int64_t img = paired_image(L, nimg);
+        lds_barrier();                          // the previous image is out of the shared region
+
+        // ---- columns, first stage: R2-point inverse DFTs over k2 ----------
+        // Dropped modes read as zero through the buffer range check.
+        const __amdgpu_buffer_rsrc_t ri = make_rsrc(yh + ib(img), in_bytes);
+        float2 g[NB][NJ][R2];
+        static_for<0, NB>([&](auto bt) {
+            const int ky = bt * KB + cl;
+            const bool kyok = ky < my;
+#pragma unroll
+            for (int jj = 0; jj < NJ; ++jj)
+#pragma unroll
+                for (int k2 = 0; k2 < R2; ++k2) {
+                    const int q = qm[jj][k2];
+                    const uint32_t m = (uint32_t)(q + ky);
+                    const uint32_t off = (q < 0 || !kyok) ? kBufferSkip : (m + (m >> 3) * st8) * 8u;
+                    g[bt][jj][k2] = buffer_load_f2(ri, off, 0);
+                }
+        });
+        static_for<0, NB>([&](auto bt) {
+            float2* const xb = xreg + bt * S::XBUF + cl * S::GS;
+#pragma unroll
+            for (int jj = 0; jj < NJ; ++jj) {
+                dft<R2, 1>(g[bt][jj]);
+#pragma unroll
+                for (int tt = 0; tt < R2; ++tt) xb[tt * S::XS + t + R2 * jj] = g[bt][jj][tt];
+            }
+        });
+        lds_barrier();
+
+        // ---- columns, second stage: twiddle, R1-point inverse DFTs over k1 -
+        float2 v[NB][R1];
+        static_for<0, NB>([&](auto bt) {
+            const float2* const xb = xreg + bt * S::XBUF + cl * S::GS + t * S::XS;
+#pragma unroll
+            for (int k1 = 0; k1 < R1; ++k1) v[bt][k1] = xb[k1];
+        });
+        lds_barrier();                          // the hand-over is read before the plane overwrites it
+        static_for<0, NB>([&](auto bt) {
+#pragma unroll
+            for (int k1 = 1; k1 < R1; ++k1) {
+                const float2 w = twH[(t * k1) & (H - 1)];
+                v[bt][k1] = cmul(v[bt][k1], make_float2(w.x, -w.y));
+            }
+            dft<R1, 1>(v[bt]);
+#pragma unroll
+            for (int m = 0; m < R1; ++m) plane[(t + R2 * m) * S::PS + bt * KB + cl] = v[bt][m];
+        });
+        lds_barrier();
+
+        // ---- row tid: packed C2R in registers ------------------------------
+        float2 z[NZ];
+        {
+            float2 X[MYMAX];
+#pragma unroll
+            for (int k = 0; k < MYMAX; ++k) X[k] = plane[tid * S::PS + k];
+            static_for<0, NZ>([&](auto k) { z[k] = packed_c2r_bin<W, k, MYMAX, LOG2H + LOG2W>(X); });
+        }
+        dft<NZ, 1>(z);
+        lds_barrier();                          // every row is out of the plane before the stage is written
+
+        // ---- hand the row out: coalesced stores through the stage ---------
+        {
+            const __amdgpu_buffer_rsrc_t ro = make_rsrc(out + img * (int64_t)(H * W), (uint32_t)(H * W * 4));
+            float* stage = reinterpret_cast<float*>(xreg) + (tid >> 6) * 64 * S::SS;
+            static_for<0, S::NCK>([&](auto c) {
+                static_for<0, 8>([&](auto q) {
+                    *reinterpret_cast<float4*>(stage + lane * S::SS + 4 * q) =
+                        make_float4(z[2 * (8 * c + q)].x, z[2 * (8 * c + q)].y, z[2 * (8 * c + q) + 1].x,
+                                    z[2 * (8 * c + q) + 1].y);
+                });
+                wave_lds_sync();
+                static_for<0, 8>([&](auto ii) {
+                    const float4 o =
+                        *reinterpret_cast<const float4*>(stage + (8 * ii + (lane >> 3)) * S::SS + 4 * (lane & 7));
+                    buffer_store_f4(o, ro, soffs[ii] + 128 * c, 0);
+                });
+                wave_lds_sync();
+            });
+        }
+    }
+}
+
+// Launches kernel k on a persistent grid: as many workgroups as fit on the
+// device (from the occupancy of k with `lds` bytes), in whole groups of 16
+// for the XCD pairing, never more than there are images.
+template <typename K, typename... A>
+hipError_t launch_persistent(K k, int nt, size_t lds, int64_t nimg, hipStream_t s, A... args) {
+    int dev = 0, cus = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return hipErrorInvalidDevice;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+    const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, nt, lds);
+    if (e != hipSuccess) return e;
+    int64_t g = (int64_t)cus * (per_cu > 0 ? per_cu : 1);
+    g = g >= 16 ? (g / 16) * 16 : g;
     if (g > nimg) g = nimg;
-    hipLaunchKernelGGL((k_fwd2d_rows<LH, LW, MYM>), dim3((unsigned)g), dim3(P::NT), P::lds_bytes(), s, x, xh, ib,
-                       st, nimg, mx, my, tw);
+    hipLaunchKernelGGL(k, dim3((unsigned)g), dim3(nt), lds, s, args...);
     return hipGetLastError();
+}
+
+template <int LH, int LW, int MYM>
+hipError_t launch_fwd_one(const float* x, float2* xh, const ImageBase& ib, int st, int64_t nimg, int mx, int my,
+                          const float2* tw, hipStream_t s) {
+    using P = RowPlan<LH, LW, MYM>;
+    return launch_persistent(k_fwd2d_rows<LH, LW, MYM>, P::NT, P::lds_bytes(), nimg, s, x, xh, ib, st, nimg, mx, my,
+                             tw);
+}
+
+template <int LH, int LW, int MYM>
+hipError_t launch_inv_one(const float2* yh, float* out, const ImageBase& ib, int st, int64_t nimg, int mx, int my,
+                          const float2* tw, hipStream_t s) {
+    using P = RowPlan<LH, LW, MYM>;
+    return launch_persistent(k_inv2d_rows<LH, LW, MYM>, P::NT, P::lds_bytes(), nimg, s, yh, out, ib, st, nimg, mx,
+                             my, tw);
+}
+
+ImageBase image_base(const SpecLayout& lay) {
+    ImageBase ib;
+    ib.sb = lay.sb;
+    ib.sc = lay.sc;
+    ib.C = lay.C;
+    return ib;
 }
 
 }  // namespace
@@ -270,24 +456,28 @@ bool rowreg2d_supported(int log2H, int log2W, int mx, int my, const SpecLayout& 
            (tiles * lay.st + 8) * 8 < (int64_t)kBufferSkip;
 }
 
+#define FNO_ROWREG_DISPATCH(FN, ...)                                                                   \
+    if (log2H == 7 && log2W == 7) return my <= 16 ? FN<7, 7, 16>(__VA_ARGS__) : FN<7, 7, 32>(__VA_ARGS__); \
+    if (log2H == 6 && log2W == 6) return my <= 16 ? FN<6, 6, 16>(__VA_ARGS__) : FN<6, 6, 32>(__VA_ARGS__); \
+    if (log2H == 7 && log2W == 6) return my <= 16 ? FN<7, 6, 16>(__VA_ARGS__) : FN<7, 6, 32>(__VA_ARGS__); \
+    if (log2H == 6 && log2W == 7) return my <= 16 ? FN<6, 7, 16>(__VA_ARGS__) : FN<6, 7, 32>(__VA_ARGS__); \
+    return hipErrorInvalidValue;
+
 hipError_t launch_fwd2d_rowreg(const float* x, float2* xh, const SpecLayout& lay, int64_t nimg, int log2H,
                                int log2W, int mx, int my, const float2* tw, hipStream_t s) {
     if (!rowreg2d_supported(log2H, log2W, mx, my, lay) || nimg >= INT32_MAX) return hipErrorInvalidValue;
-    ImageBase ib;
-    ib.sb = lay.sb;
-    ib.sc = lay.sc;
-    ib.C = lay.C;
+    const ImageBase ib = image_base(lay);
     const int st = (int)lay.st;
-#define FNO_ROWREG(LH, LW)                                                                             \
-    if (log2H == LH && log2W == LW)                                                                    \
-        return my <= 16 ? launch_one<LH, LW, 16>(x, xh, ib, st, nimg, mx, my, tw, s)                  \
-                        : launch_one<LH, LW, 32>(x, xh, ib, st, nimg, mx, my, tw, s);
-    FNO_ROWREG(7, 7)
-    FNO_ROWREG(6, 6)
-    FNO_ROWREG(7, 6)
-    FNO_ROWREG(6, 7)
-#undef FNO_ROWREG
-    return hipErrorInvalidValue;
+    FNO_ROWREG_DISPATCH(launch_fwd_one, x, xh, ib, st, nimg, mx, my, tw, s)
 }
+
+hipError_t launch_inv2d_rowreg(const float2* yh, float* out, const SpecLayout& lay, int64_t nimg, int log2H,
+                               int log2W, int mx, int my, const float2* tw, hipStream_t s) {
+    if (!rowreg2d_supported(log2H, log2W, mx, my, lay) || nimg >= INT32_MAX) return hipErrorInvalidValue;
+    const ImageBase ib = image_base(lay);
+    const int st = (int)lay.st;
+    FNO_ROWREG_DISPATCH(launch_inv_one, yh, out, ib, st, nimg, mx, my, tw, s)
+}
+#undef FNO_ROWREG_DISPATCH
 
 }  // namespace fno
