@@ -331,9 +331,10 @@ def fno_mix(xh, w, yh=None):
 
 
 def fno_set_timing_events(events):
-    """Record the given torch.cuda.Event list around each kernel of later calls
-    on this thread (see include/fno.h); pass None to stop.  The list must stay
-    alive while recording is on."""
+    """Launch kernel k of later calls on this thread with events[2k] and
+    events[2k+1] (torch.cuda.Event, already recorded once so that the HIP
+    event exists) as its start and stop events (see include/fno.h); pass None
+    to stop.  The list must stay alive while recording is on."""
     global _timing_keepalive
     if events is None:
         _timing_keepalive = None

@@ -35,7 +35,8 @@ struct DeviceState {
 std::mutex g_mutex;
 std::vector<DeviceState> g_devices;
 
-// Optional per-kernel event recording (fno_set_timing_events).
+// Optional per-kernel timing (fno_set_timing_events): kernel k of a call
+// launches with events[2k], events[2k + 1] as its start and stop events.
 constexpr int kMaxKernels = 16;
 struct Recorder {
     void** events = nullptr;
@@ -47,25 +48,28 @@ struct Recorder {
     int last_count = 0;
 };
 thread_local Recorder g_rec;
+thread_local LaunchEvents g_pending;
 
 void rec_begin() {
     g_rec.k = 0;
     g_rec.count = 0;
+    g_pending = LaunchEvents{};
 }
 
-// Call right before launching a kernel on stream s.
-void rec_kernel(const char* name, hipStream_t s) {
-    if (g_rec.events && g_rec.k < g_rec.n_events)
-        (void)hipEventRecord(static_cast<hipEvent_t>(g_rec.events[g_rec.k]), s);
+// Call right before launching a kernel: hands the launch its event pair.
+void rec_kernel(const char* name, hipStream_t) {
+    if (g_rec.events && 2 * g_rec.k + 1 < g_rec.n_events) {
+        g_pending.start = static_cast<hipEvent_t>(g_rec.events[2 * g_rec.k]);
+        g_pending.stop = static_cast<hipEvent_t>(g_rec.events[2 * g_rec.k + 1]);
+    }
     if (g_rec.count < kMaxKernels) g_rec.names[g_rec.count++] = name;
     ++g_rec.k;
 }
 
-// Call after the last kernel of a successful call.
-int rec_end(hipStream_t s, int rc) {
+// Call after the last kernel of a call.
+int rec_end(hipStream_t, int rc) {
+    g_pending = LaunchEvents{};
     if (rc != 0) return rc;
-    if (g_rec.events && g_rec.k < g_rec.n_events)
-        (void)hipEventRecord(static_cast<hipEvent_t>(g_rec.events[g_rec.k]), s);
     for (int i = 0; i < g_rec.count; ++i) g_rec.last_names[i] = g_rec.names[i];
     g_rec.last_count = g_rec.count;
     return rc;
@@ -195,7 +199,7 @@ bool use_mfma_mix(int64_t B, int64_t Cin, int64_t Cout) { return B >= 8 && Cin >
 int run_mix(const float2* xh, const SpecLayout& lx, const float2* w, float2* yh, const SpecLayout& ly, int64_t B,
             int64_t Cin, int64_t Cout, int64_t M, hipStream_t st) {
     hipError_t e;
-    if (use_mfma_mix(B, Cin, Cout) && mix_mfma_supported(Cout, w)) {
+    if (use_mfma_mix(B, Cin, Cout) && mix_mfma_supported(Cin, Cout, w)) {
         rec_kernel("mix_mfma", st);
         e = launch_mix_mfma(xh, lx, w, yh, ly, B, Cin, Cout, M, st);
     } else {
@@ -397,6 +401,12 @@ int conv1d_common(const float* x, const void* w, float* out, int B, int Cin, int
 }
 
 }  // namespace
+
+LaunchEvents take_launch_events() {
+    const LaunchEvents e = g_pending;
+    g_pending = LaunchEvents{};
+    return e;
+}
 }  // namespace fno
 
 using namespace fno;

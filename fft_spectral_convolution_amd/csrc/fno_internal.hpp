@@ -2,6 +2,7 @@
 // launchers.  Not part of the public API.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <cstddef>
@@ -28,6 +29,23 @@ struct SpecLayout {
     int64_t sb, sc, st;
     int C;
 };
+
+// Events the next kernel launch carries (set by the per-kernel timing
+// recorder of the C ABI, both null otherwise).  Taking them clears them.
+struct LaunchEvents {
+    hipEvent_t start = nullptr, stop = nullptr;
+};
+LaunchEvents take_launch_events();
+
+// Every kernel is launched through here: with per-kernel timing on, the
+// launch itself carries the events, which then take the kernel's own start
+// and end timestamps (no marker packets between dependent kernels).
+template <typename K, typename... Args>
+hipError_t launch_kernel(K kernel, dim3 grid, dim3 block, size_t lds, hipStream_t s, Args... args) {
+    const LaunchEvents ev = take_launch_events();
+    hipExtLaunchKernelGGL(kernel, grid, block, (std::uint32_t)lds, s, ev.start, ev.stop, 0u, args...);
+    return hipGetLastError();
+}
 
 inline SpecLayout canonical_layout(int64_t C, int64_t M) { return SpecLayout{C * M, M, 8, (int)C}; }
 inline SpecLayout tiled_layout(int64_t C, int64_t M) {
@@ -56,8 +74,8 @@ hipError_t launch_inv2d_rowreg(const float2* yh, float* out, const SpecLayout& l
 
 // ---- channel mix on MFMA (fno_mix.hip) --------------------------------------
 // yh(b, o, m) = sum_i xh(b, i, m) * w[m][i][o], spectra addressed by layouts.
-// Needs an even Cout and a 16-byte aligned w (float4 weight pairs).
-bool mix_mfma_supported(int64_t Cout, const void* w);
+// Needs an even Cout, a 16-byte aligned w (float4 weight pairs) and Cin <= 128.
+bool mix_mfma_supported(int64_t Cin, int64_t Cout, const void* w);
 hipError_t launch_mix_mfma(const float2* xh, const SpecLayout& lx, const float2* w, float2* yh,
                            const SpecLayout& ly, int64_t B, int64_t Cin, int64_t Cout, int64_t M, hipStream_t s);
 

@@ -1,26 +1,28 @@
 // Per-mode channel mix on the fp32 matrix cores (v_mfma_f32_16x16x4_f32).
 //
 // For every kept mode m the mix is a complex GEMM (TurboFNO blog, section 2.2:
-// the frequency-domain GEMM is a per-mode complex multiply-accumulate,
-// (a+bi)(c+di) = (ac-bd) + (ad+bc)i):
-//   Y_m[b][o] = sum_i X_m[b][i] * W_m[i][o]
-// done as four real products, Yr += Xr Wr - Xi Wi and Yi += Xr Wi + Xi Wr,
+// the frequency-domain GEMM is a per-mode complex multiply-accumulate):
+//   Y_m[b][o] = sum_i X_m[b][i] * W_m[i][o].
+// It runs as three real GEMMs (the 3M form of the complex product):
+//   P1 = Xr Wr,  P2 = Xi Wi,  P3 = (Xr + Xi)(Wr + Wi),
+//   Yr = P1 - P2,  Yi = P3 - P1 - P2,
 // all accumulated in fp32.
 //
-// Workgroup = 8 waves = one tile of 8 consecutive modes x 32 batch rows x 64
-// output channels; wave w owns mode m0 + w, i.e. a 32 x 64 complex result =
-// 2 x 4 blocks of 16 x 16, each with a real and an imaginary accumulator.
-// The input channels are consumed in chunks of 8 (two MFMA k-steps of 4):
+// Tile = 8 consecutive modes x 32 batch rows x 32 output channels, one
+// workgroup of 8 waves; wave w owns mode m0 + w, a 32 x 32 result = 2 x 2
+// blocks of 16 x 16 with three accumulators each.  Input channels are
+// consumed in chunks of 8 (two MFMA k-steps of 4):
 //  * the X chunk of all 8 modes ([32 b][8 i][8 m], one 64-byte run per
 //    (b, i)) is staged in LDS as [i][m][b] and shared by the 8 waves;
 //  * each wave streams its own W_m rows from global memory straight into the
-//    B operand, as float4 pairs (o, o + 1): column block (h, parity) holds
-//    o = 32 h + 2 c + parity, c < 16.
-// Both are fetched two chunks ahead of their use, with unconditional
-// (clamped) loads so the compiler can count outstanding loads exactly.
-// Results go back through LDS so that every store instruction of a wave
-// writes 1 KiB of consecutive output.  Rows, channels and modes past the ends
-// are masked.
+//    B operand, as float4 pairs (o, o + 1): column block p holds
+//    o = 2 c + p, c < 16.
+// The grid is persistent and every workgroup walks a contiguous range of
+// tiles as one flat sequence of chunks: X and W are fetched two chunks ahead across tile
+// boundaries (unconditional, clamped loads, so the compiler can count
+// outstanding loads exactly), and a tile's results leave through LDS in
+// 32-byte runs while the next tile's first chunks are already in flight.
+// Rows, channels and modes past the ends are masked.
 #include "fno_device.hpp"
 #include "fno_internal.hpp"
 
@@ -33,7 +35,7 @@ constexpr int kMixWaves = 8;           // = modes per tile
 constexpr int kMixThreads = 64 * kMixWaves;
 constexpr int kMixKC = 8;              // input channels per chunk
 constexpr int kMixBRows = 32;          // batch rows per tile (2 MFMA row blocks)
-constexpr int kMixOCols = 64;          // output channels per tile (4 MFMA column blocks)
+constexpr int kMixOCols = 32;          // output channels per tile (2 MFMA column blocks)
 
 struct Addr {
     int64_t sb, sc, st;
@@ -42,63 +44,58 @@ struct Addr {
     }
 };
 
+struct TileGrid {
+    int n_mt, n_bt, n_ot, n_tiles;
+};
+
+struct Tile {
+    int m0, b0, o0;
+};
+
 __device__ __forceinline__ floatx4 mfma16(float a, float b, floatx4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
+// tile t -> (mode tile, batch tile, output tile), output tile fastest
+__device__ __forceinline__ Tile tile_of(const TileGrid& tg, int t) {
+    const int ot = t % tg.n_ot;
+    const int r = t / tg.n_ot;
+    return Tile{(r % tg.n_mt) * 8, (r / tg.n_mt) * kMixBRows, ot * kMixOCols};
+}
+
 // VEC: every (b, c) run of 8 modes is 16-byte aligned and complete (tiled
 // layout), so X is read and Y written as float4; otherwise element-wise.
-// NCH > 0: exactly NCH chunks of input channels (unrolled); 0: runtime count.
+// NCH: chunks of input channels per tile (even; chunks past Cin are zero).
 template <int NCH, bool VEC>
 __global__ __launch_bounds__(kMixThreads) void k_mix_mfma(const float2* __restrict__ xh, Addr ax,
                                                           const float2* __restrict__ w, float2* __restrict__ yh,
-                                                          Addr ay, int B, int Cin, int Cout, int M, int n_mt,
-                                                          int n_bt) {
+                                                          Addr ay, int B, int Cin, int Cout, int M, TileGrid tg) {
+    static_assert(NCH % 2 == 0, "chunks alternate between two register sets");
     constexpr int kAS = kMixBRows + 1;                     // [i][m][b] row stride
     constexpr int kYS = kMixOCols + 1;                     // [b8][m][o] row stride
     constexpr int kAChunk = kMixKC * 8 * kAS;
     __shared__ float2 a_lds[2 * kAChunk];                  // 2 x 16.5 KiB
-    __shared__ float2 y_lds[8 * 8 * kYS];                  // 32.5 KiB
+    __shared__ float2 y_lds[8 * 8 * kYS];                  // 16.5 KiB
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int mt = blockIdx.x % n_mt;
-    const int bt = (blockIdx.x / n_mt) % n_bt;
-    const int ot = blockIdx.x / (n_mt * n_bt);
-    const int m0 = mt * 8;
-    const int b0 = bt * kMixBRows;
-    const int o0 = ot * kMixOCols;
-    const int m = m0 + wave;                 // this wave's mode
     const int l16 = lane & 15;               // MFMA row (A) / column (B, C)
     const int lk = lane >> 4;                // MFMA k index within a step (0..3)
-    const int nch = NCH > 0 ? NCH : (Cin + kMixKC - 1) / kMixKC;
-    const int last = nch - 1;
-
     // staging role: thread -> (b, i, half of the 8 modes) of a chunk
     const int sbl = tid >> 4;
     const int sil = (tid >> 1) & 7;
     const int shalf = tid & 1;
-    const int sb_c = (b0 + sbl < B) ? b0 + sbl : B - 1;
-    const int mw_c = m < M ? m : M - 1;
-
-    floatx4 cr[2][4], ci[2][4];
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-        for (int cb = 0; cb < 4; ++cb) {
-            cr[rb][cb] = floatx4{0.f, 0.f, 0.f, 0.f};
-            ci[rb][cb] = floatx4{0.f, 0.f, 0.f, 0.f};
-        }
 
     // X[b0 + sbl][chunk * 8 + sil][m0 + 4 * shalf + q], q < 4.  Clamped
     // indices only feed results that are never stored, except channels past
     // Cin, which are zeroed when the chunk is written to LDS.
-    auto load_a = [&](int chunk, float2 (&av)[4]) {
+    auto load_a = [&](const Tile& tl, int chunk, float2 (&av)[4]) __attribute__((always_inline)) {
         const int i = chunk * kMixKC + sil;
         const int ic = i < Cin ? i : Cin - 1;
+        const int b = tl.b0 + sbl < B ? tl.b0 + sbl : B - 1;
         if constexpr (VEC) {
-            const float4* src = reinterpret_cast<const float4*>(xh + ax.at(sb_c, ic, m0 + shalf * 4));
+            const float4* src = reinterpret_cast<const float4*>(xh + ax.at(b, ic, tl.m0 + shalf * 4));
             const float4 v0 = src[0], v1 = src[1];
             av[0] = make_float2(v0.x, v0.y);
             av[1] = make_float2(v0.z, v0.w);
@@ -107,35 +104,36 @@ __global__ __launch_bounds__(kMixThreads) void k_mix_mfma(const float2* __restri
         } else {
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const int mm = m0 + shalf * 4 + q;
-                av[q] = xh[ax.at(sb_c, ic, mm < M ? mm : M - 1)];
+                const int mm = tl.m0 + shalf * 4 + q;
+                av[q] = xh[ax.at(b, ic, mm < M ? mm : M - 1)];
             }
         }
     };
-    auto store_a = [&](int chunk, const float2 (&av)[4], float2* buf) {
+    auto store_a = [&](int chunk, const float2 (&av)[4], float2* buf) __attribute__((always_inline)) {
         const bool iok = chunk * kMixKC + sil < Cin;
 #pragma unroll
         for (int q = 0; q < 4; ++q)
             buf[(sil * 8 + shalf * 4 + q) * kAS + sbl] = iok ? av[q] : make_float2(0.0f, 0.0f);
     };
-    // W pairs for k-step s (channels chunk*8 + 4s + lk), column half h:
-    // wv[s][h] = (W[i][o], W[i][o + 1]), o = o0 + 32 h + 2 l16 (Cout is even
-    // on this path; columns past Cout are clamped and never stored).
-    auto load_w = [&](int chunk, float4 (&wv)[2][2]) {
+    // W pairs for k-step s (channels chunk*8 + 4s + lk): wv[s] = (W[i][o],
+    // W[i][o + 1]), o = o0 + 2 l16 (Cout is even on this path; columns past
+    // Cout are clamped and never stored).
+    auto load_w = [&](const Tile& tl, int chunk, float2 (&wv)[4]) __attribute__((always_inline)) {
+        const int mw = tl.m0 + wave < M ? tl.m0 + wave : M - 1;
+        int o = tl.o0 + 2 * l16;
+        o = o < Cout ? o : Cout - 2;
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
             const int i = chunk * kMixKC + 4 * s + lk;
             const int ic = i < Cin ? i : Cin - 1;
-            const float2* row = w + ((int64_t)mw_c * Cin + ic) * Cout;
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                int o = o0 + 32 * h + 2 * l16;
-                o = o < Cout ? o : Cout - 2;
-                wv[s][h] = *reinterpret_cast<const float4*>(row + o);
-            }
+            const float4 v = *reinterpret_cast<const float4*>(w + ((int64_t)mw * Cin + ic) * Cout + o);
+            wv[2 * s] = make_float2(v.x, v.y);
+            wv[2 * s + 1] = make_float2(v.z, v.w);
         }
     };
-    auto mfma_chunk = [&](const float2* buf, const float4 (&wv)[2][2]) {
+
+    floatx4 p1[2][2], p2[2][2], p3[2][2];
+    auto mfma_chunk = [&](const float2* buf, const float2 (&wv)[4]) __attribute__((always_inline)) {
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
             float2 a[2];
@@ -143,150 +141,170 @@ __global__ __launch_bounds__(kMixThreads) void k_mix_mfma(const float2* __restri
             for (int rb = 0; rb < 2; ++rb) a[rb] = buf[((4 * s + lk) * 8 + wave) * kAS + 16 * rb + l16];
 #pragma unroll
             for (int rb = 0; rb < 2; ++rb) {
+                const float as = a[rb].x + a[rb].y;
 #pragma unroll
-                for (int cb = 0; cb < 4; ++cb) {
-                    const float4 q = wv[s][cb >> 1];
-                    const float wr = (cb & 1) ? q.z : q.x;
-                    const float wi = (cb & 1) ? q.w : q.y;
-                    cr[rb][cb] = mfma16(a[rb].x, wr, cr[rb][cb]);
-                    ci[rb][cb] = mfma16(a[rb].x, wi, ci[rb][cb]);
-                }
-            }
-#pragma unroll
-            for (int rb = 0; rb < 2; ++rb) {
-#pragma unroll
-                for (int cb = 0; cb < 4; ++cb) {
-                    const float4 q = wv[s][cb >> 1];
-                    const float wr = (cb & 1) ? q.z : q.x;
-                    const float wi = (cb & 1) ? q.w : q.y;
-                    cr[rb][cb] = mfma16(-a[rb].y, wi, cr[rb][cb]);
-                    ci[rb][cb] = mfma16(a[rb].y, wr, ci[rb][cb]);
+                for (int cb = 0; cb < 2; ++cb) {
+                    const float2 wc = wv[2 * s + cb];
+                    p1[rb][cb] = mfma16(a[rb].x, wc.x, p1[rb][cb]);
+                    p2[rb][cb] = mfma16(a[rb].y, wc.y, p2[rb][cb]);
+                    p3[rb][cb] = mfma16(as, wc.x + wc.y, p3[rb][cb]);
                 }
             }
         }
     };
 
-    // Two register sets alternate, each refilled two chunks ahead right after
-    // use; the LDS barriers leave those loads in flight.  LDS buffer k & 1 is
-    // rewritten only after every wave passed the barrier of chunk k - 1, i.e.
-    // after all reads of chunk k - 2.
-    float2 aA[4], aB[4];
-    float4 wA[2][2], wB[2][2];
-    load_a(0, aA);
-    load_w(0, wA);
-    load_a(min(1, last), aB);
-    load_w(min(1, last), wB);
-#pragma unroll
-    for (int k = 0; k < nch; k += 2) {
-        store_a(k, aA, a_lds);
-        load_a(min(k + 2, last), aA);
-        lds_barrier();
-        mfma_chunk(a_lds, wA);
-        load_w(min(k + 2, last), wA);
-        if (k + 1 >= nch) break;
-        store_a(k + 1, aB, a_lds + kAChunk);
-        load_a(min(k + 3, last), aB);
-        lds_barrier();
-        mfma_chunk(a_lds + kAChunk, wB);
-        load_w(min(k + 3, last), wB);
-    }
-
     // C layout of a 16x16 block: lane holds column l16 and, in register r,
-    // row 4 * lk + r.  Row block rb adds 16; column block cb = 2 h + parity
-    // holds o = 32 h + 2 l16 + parity.  Four rounds of 8 batch rows: round rr
-    // holds row block rr / 2 and the lanes with lk / 2 == rr % 2.
+    // row 4 * lk + r.  Row block rb adds 16; column block cb holds
+    // o = 2 l16 + cb.  Four rounds of 8 batch rows: round rr holds row block
+    // rr / 2 and the lanes with lk / 2 == rr % 2.
+    auto epilogue = [&](const Tile& tl) __attribute__((always_inline)) {
+        // thread -> (b, o, half of the modes) of a round: consecutive threads
+        // write consecutive 32-byte runs
+        const int bl_s = tid >> 6;
+        const int ol_s = (tid >> 1) & 31;
+        const int qh = tid & 1;
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-        const int rb = rr >> 1;
-        if ((lk >> 1) == (rr & 1)) {
+        for (int rr = 0; rr < 4; ++rr) {
+            const int rb = rr >> 1;
+            if ((lk >> 1) == (rr & 1)) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int bl = 4 * (lk & 1) + r;    // row within the round
+                for (int r = 0; r < 4; ++r) {
+                    const int bl = 4 * (lk & 1) + r;    // row within the round
 #pragma unroll
-                for (int cb = 0; cb < 4; ++cb) {
-                    const int ol = 32 * (cb >> 1) + 2 * l16 + (cb & 1);
-                    y_lds[(bl * 8 + wave) * kYS + ol] = make_float2(cr[rb][cb][r], ci[rb][cb][r]);
+                    for (int cb = 0; cb < 2; ++cb) {
+                        const float pr = p1[rb][cb][r], pi = p2[rb][cb][r];
+                        y_lds[(bl * 8 + wave) * kYS + 2 * l16 + cb] = make_float2(pr - pi, p3[rb][cb][r] - pr - pi);
+                    }
                 }
             }
-        }
-        lds_barrier();
-        if constexpr (VEC) {
-            // thread -> (b, o, half of the modes): consecutive threads write
-            // consecutive 32-byte runs, 2 KiB per wave and instruction pair
+            lds_barrier();
+            const int b = tl.b0 + rr * 8 + bl_s;
+            const int o = tl.o0 + ol_s;
+            if (b < B && o < Cout) {
+                float2 v[4];
 #pragma unroll
-            for (int hh = 0; hh < 2; ++hh) {
-                const int e = tid + kMixThreads * hh;   // 1024 items = 8 b x 64 o x 2 mode halves
-                const int bl = e >> 7;
-                const int ol = (e >> 1) & 63;
-                const int qh = e & 1;
-                const int b = b0 + rr * 8 + bl;
-                const int o = o0 + ol;
-                if (b < B && o < Cout) {
-                    float2 v[4];
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) v[q] = y_lds[(bl * 8 + 4 * qh + q) * kYS + ol];
-                    float4* dst = reinterpret_cast<float4*>(yh + ay.at(b, o, m0 + 4 * qh));
+                for (int q = 0; q < 4; ++q) v[q] = y_lds[(bl_s * 8 + 4 * qh + q) * kYS + ol_s];
+                if constexpr (VEC) {
+                    float4* dst = reinterpret_cast<float4*>(yh + ay.at(b, o, tl.m0 + 4 * qh));
                     dst[0] = make_float4(v[0].x, v[0].y, v[1].x, v[1].y);
                     dst[1] = make_float4(v[2].x, v[2].y, v[3].x, v[3].y);
-                }
-            }
-        } else {
-            const int bl = tid >> 6;
-            const int ol = tid & 63;
-            const int b = b0 + rr * 8 + bl;
-            const int o = o0 + ol;
-            if (b < B && o < Cout) {
+                } else {
 #pragma unroll
-                for (int q = 0; q < 8; ++q) {
-                    const int mm = m0 + q;
-                    if (mm < M) yh[ay.at(b, o, mm)] = y_lds[(bl * 8 + q) * kYS + ol];
+                    for (int q = 0; q < 4; ++q) {
+                        const int mm = tl.m0 + 4 * qh + q;
+                        if (mm < M) yh[ay.at(b, o, mm)] = v[q];
+                    }
                 }
             }
+            lds_barrier();
         }
-        lds_barrier();
+    };
+
+    // Flat chunk sequence over this workgroup's tiles.  Register sets A and B
+    // alternate, each refilled two chunks ahead right after use (past the
+    // last tile the last chunk is reloaded).  LDS buffer k & 1 is rewritten
+    // only after every wave passed the barrier of chunk k - 1, i.e. after all
+    // reads of chunk k - 2.
+    // workgroup j walks the contiguous tile range [t_begin, t_end), so both
+    // output tiles of a mode tile run back to back (the second reads X from L2)
+    const int G = gridDim.x;
+    const int t_begin = (int)((int64_t)tg.n_tiles * blockIdx.x / G);
+    const int t_end = (int)((int64_t)tg.n_tiles * (blockIdx.x + 1) / G);
+    int t = t_begin;
+    Tile cur = tile_of(tg, t);
+    Tile nxt = tile_of(tg, t + 1 < t_end ? t + 1 : t);
+    float2 aA[4], aB[4];
+    float2 wA[4], wB[4];
+    load_a(cur, 0, aA);
+    load_w(cur, 0, wA);
+    load_a(cur, 1, aB);
+    load_w(cur, 1, wB);
+    for (; t < t_end; ++t) {
+        const bool more = t + 1 < t_end;
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+            for (int cb = 0; cb < 2; ++cb) {
+                p1[rb][cb] = floatx4{0.f, 0.f, 0.f, 0.f};
+                p2[rb][cb] = floatx4{0.f, 0.f, 0.f, 0.f};
+                p3[rb][cb] = floatx4{0.f, 0.f, 0.f, 0.f};
+            }
+#pragma unroll
+        for (int k = 0; k < NCH; k += 2) {
+            // chunks k + 2 and k + 3: this tile's, or the next tile's first two
+            const bool here = k + 2 < NCH;
+            const Tile& t2 = here ? cur : (more ? nxt : cur);
+            const int c2 = here ? k + 2 : (more ? 0 : NCH - 1);
+            const int c3 = here ? k + 3 : (more ? 1 : NCH - 1);
+            store_a(k, aA, a_lds);
+            load_a(t2, c2, aA);
+            lds_barrier();
+            mfma_chunk(a_lds, wA);
+            load_w(t2, c2, wA);
+            store_a(k + 1, aB, a_lds + kAChunk);
+            load_a(t2, c3, aB);
+            lds_barrier();
+            mfma_chunk(a_lds + kAChunk, wB);
+            load_w(t2, c3, wB);
+        }
+        epilogue(cur);
+        cur = nxt;
+        nxt = tile_of(tg, t + 2 < t_end ? t + 2 : (more ? t + 1 : t));
     }
 }
 
 template <bool VEC>
 void launch_mix_variant(dim3 grid, hipStream_t s, const float2* xh, Addr ax, const float2* w, float2* yh, Addr ay,
-                        int B, int Cin, int Cout, int M, int n_mt, int n_bt) {
-    const int nch = (Cin + kMixKC - 1) / kMixKC;
+                        int B, int Cin, int Cout, int M, TileGrid tg, int nch) {
     switch (nch) {
-#define CASE(N)                                                                                                   \
-    case N:                                                                                                       \
-        hipLaunchKernelGGL((k_mix_mfma<N, VEC>), grid, dim3(kMixThreads), 0, s, xh, ax, w, yh, ay, B, Cin, Cout, \
-                           M, n_mt, n_bt);                                                                        \
+#define CASE(N)                                                                                              \
+    case N:                                                                                                  \
+        launch_kernel((k_mix_mfma<N, VEC>), grid, dim3(kMixThreads), 0, s, xh, ax, w, yh, ay, B, Cin, \
+                           Cout, M, tg);                                                                     \
         break;
-        CASE(1) CASE(2) CASE(3) CASE(4) CASE(5) CASE(6) CASE(7) CASE(8)
-        CASE(9) CASE(10) CASE(11) CASE(12) CASE(13) CASE(14) CASE(15) CASE(16)
+        CASE(2) CASE(4) CASE(6) CASE(8) CASE(10) CASE(12) CASE(14) CASE(16)
 #undef CASE
         default:
-            hipLaunchKernelGGL((k_mix_mfma<0, VEC>), grid, dim3(kMixThreads), 0, s, xh, ax, w, yh, ay, B, Cin, Cout,
-                               M, n_mt, n_bt);
+            break;
     }
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// Chunks of 8 input channels, rounded up to an even count.
+int64_t mix_chunks(int64_t Cin) { return ((Cin + kMixKC - 1) / kMixKC + 1) / 2 * 2; }
+
 }  // namespace
 
-bool mix_mfma_supported(int64_t Cout, const void* w) { return Cout % 2 == 0 && aligned16(w); }
+bool mix_mfma_supported(int64_t Cin, int64_t Cout, const void* w) {
+    return Cout % 2 == 0 && aligned16(w) && mix_chunks(Cin) <= 16;
+}
 
 hipError_t launch_mix_mfma(const float2* xh, const SpecLayout& lx, const float2* w, float2* yh, const SpecLayout& ly,
                            int64_t B, int64_t Cin, int64_t Cout, int64_t M, hipStream_t s) {
-    if (!mix_mfma_supported(Cout, w)) return hipErrorInvalidValue;
-    const int n_mt = (int)((M + 7) / 8);
-    const int n_bt = (int)((B + kMixBRows - 1) / kMixBRows);
-    const int n_ot = (int)((Cout + kMixOCols - 1) / kMixOCols);
+    if (!mix_mfma_supported(Cin, Cout, w)) return hipErrorInvalidValue;
+    TileGrid tg;
+    tg.n_mt = (int)((M + 7) / 8);
+    tg.n_bt = (int)((B + kMixBRows - 1) / kMixBRows);
+    tg.n_ot = (int)((Cout + kMixOCols - 1) / kMixOCols);
+    const int64_t n_tiles = (int64_t)tg.n_mt * tg.n_bt * tg.n_ot;
+    if (n_tiles >= INT32_MAX / 2) return hipErrorInvalidValue;
+    tg.n_tiles = (int)n_tiles;
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return hipErrorInvalidDevice;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+    // one workgroup (8 waves: two per SIMD) per CU, each walking its tiles
+    const int64_t g = n_tiles < cus ? n_tiles : cus;
     const Addr ax{lx.sb, lx.sc, lx.st};
     const Addr ay{ly.sb, ly.sc, ly.st};
-    const dim3 grid((unsigned)((int64_t)n_mt * n_bt * n_ot));
+    const dim3 grid((unsigned)g);
     // float4 access needs every 8-mode run whole and 16-byte aligned: the
     // tiled layout (runs of exactly 8 in a 256-byte aligned workspace) has it.
     const bool vec = lx.sc == 8 && ly.sc == 8 && lx.st % 2 == 0 && ly.st % 2 == 0 && lx.sb % 2 == 0 &&
                      ly.sb % 2 == 0 && M % 8 == 0 && aligned16(xh) && aligned16(yh);
-    if (vec) launch_mix_variant<true>(grid, s, xh, ax, w, yh, ay, (int)B, (int)Cin, (int)Cout, (int)M, n_mt, n_bt);
-    else launch_mix_variant<false>(grid, s, xh, ax, w, yh, ay, (int)B, (int)Cin, (int)Cout, (int)M, n_mt, n_bt);
+    const int nch = (int)mix_chunks(Cin);
+    if (vec) launch_mix_variant<true>(grid, s, xh, ax, w, yh, ay, (int)B, (int)Cin, (int)Cout, (int)M, tg, nch);
+    else launch_mix_variant<false>(grid, s, xh, ax, w, yh, ay, (int)B, (int)Cin, (int)Cout, (int)M, tg, nch);
     return hipGetLastError();
 }
 

@@ -495,7 +495,7 @@ hipError_t launch_fwd2d_small(const float* x, float2* xh, const SpecLayout& lay,
 #define CASE(LH, LW)                                                                                          \
     case LH * 16 + LW: {                                                                                      \
         const size_t lds = SmallPlan<LH, LW>::lds_bytes(my);                                                  \
-        hipLaunchKernelGGL((k_fwd2d_small<LH, LW>), grid, dim3(kSmallThreads), lds, s, x, xh, ma, nimg, mx, my, \
+        launch_kernel((k_fwd2d_small<LH, LW>), grid, dim3(kSmallThreads), lds, s, x, xh, ma, nimg, mx, my, \
                            scale, tw);                                                                        \
         break;                                                                                                \
     }
@@ -514,7 +514,7 @@ hipError_t launch_inv2d_small(const float2* yh, float* out, const SpecLayout& la
 #define CASE(LH, LW)                                                                                            \
     case LH * 16 + LW: {                                                                                        \
         const size_t lds = SmallPlan<LH, LW>::lds_bytes(my);                                                    \
-        hipLaunchKernelGGL((k_inv2d_small<LH, LW>), grid, dim3(kSmallThreads), lds, s, yh, out, ma, nimg, mx, my, \
+        launch_kernel((k_inv2d_small<LH, LW>), grid, dim3(kSmallThreads), lds, s, yh, out, ma, nimg, mx, my, \
                            scale, tw);                                                                          \
         break;                                                                                                  \
     }

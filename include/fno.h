@@ -140,14 +140,14 @@ int fno_inverse1d(const void* yh, float* out, int B, int C, int N, int modes, vo
 
 /*
  * Per-kernel timing for benchmarks and profilers.  While `events` is non-NULL,
- * every convolution or stage call made on the calling thread records
- * events[k] (a hipEvent_t, created by the caller) on its stream right before
- * its k-th kernel and events[n] right after its last kernel, where n is the
- * number of kernels the call launched (events beyond n_events-1 are not
- * recorded; the call still runs).  Pass NULL to stop.  Returns FNO_OK.
- * fno_last_kernel_count / fno_last_kernel_name report, for the calling
- * thread's last successful call, how many kernels it launched and their
- * names (static storage; "" for an index out of range).
+ * every convolution or stage call made on the calling thread launches its
+ * k-th kernel with events[2k] and events[2k+1] (hipEvent_t, created by the
+ * caller) as the launch's start and stop events, so they hold that kernel's
+ * own start and end timestamps; no extra work is queued between kernels.
+ * Kernels whose pair lies beyond n_events-1 launch without events.  Pass NULL
+ * to stop.  Returns FNO_OK.  fno_last_kernel_count / fno_last_kernel_name
+ * report, for the calling thread's last successful call, how many kernels it
+ * launched and their names (static storage; "" for an index out of range).
  */
 int fno_set_timing_events(void** events, int n_events);
 int fno_last_kernel_count(void);
