@@ -213,6 +213,7 @@ int rows_per_block(int log2n) { return (1 << log2n) >= kLdsElems ? 1 : kLdsElems
 
 hipError_t launch_rows_fwd(const float* x, float2* y, int64_t nrows, int log2W, int my, int y_ld, float scale,
                            const float2* tw, hipStream_t s) {
+    if (rows_pruned_supported(log2W, my)) return launch_rows_fwd_pruned(x, y, nrows, log2W, my, y_ld, scale, tw, s);
     const int64_t npairs = (nrows + 1) / 2;
     const int p = rows_per_block(log2W);
     const dim3 grid((unsigned)((npairs + p - 1) / p));
@@ -228,6 +229,7 @@ hipError_t launch_rows_fwd(const float* x, float2* y, int64_t nrows, int log2W, 
 
 hipError_t launch_rows_inv(const float2* y, float* out, int64_t nrows, int log2W, int my, int y_ld, float scale,
                            const float2* tw, hipStream_t s) {
+    if (rows_pruned_supported(log2W, my)) return launch_rows_inv_pruned(y, out, nrows, log2W, my, y_ld, scale, tw, s);
     const int64_t npairs = (nrows + 1) / 2;
     const int p = rows_per_block(log2W);
     const dim3 grid((unsigned)((npairs + p - 1) / p));

@@ -79,6 +79,16 @@ bool mix_mfma_supported(int64_t Cin, int64_t Cout, const void* w);
 hipError_t launch_mix_mfma(const float2* xh, const SpecLayout& lx, const float2* w, float2* yh,
                            const SpecLayout& ly, int64_t B, int64_t Cin, int64_t Cout, int64_t M, hipStream_t s);
 
+// ---- pruned long-row transforms (fno_rows_pruned.hip) ------------------------
+// Rows of W = 2^log2W real points, W in [512, 4096], bins ky < my <= 64:
+// same contract as launch_rows_fwd / launch_rows_inv below, which use them
+// whenever rows_pruned_supported holds.
+bool rows_pruned_supported(int log2W, int my);
+hipError_t launch_rows_fwd_pruned(const float* x, float2* y, int64_t nrows, int log2W, int my, int y_ld, float scale,
+                                  const float2* tw, hipStream_t s);
+hipError_t launch_rows_inv_pruned(const float2* y, float* out, int64_t nrows, int log2W, int my, int y_ld,
+                                  float scale, const float2* tw, hipStream_t s);
+
 // ---- generic stage launchers (fno_generic.hip) -------------------------------
 // All return hipSuccess or the launch error.  `tw` is the device twiddle table.
 

@@ -1,0 +1,243 @@
+// Pruned transforms of long real rows (N = 64 Q points, Q in {8, 16, 32, 64})
+// when only the bins k < my <= 64 are kept: the forward R2C that computes
+// just those bins, and the C2R that rebuilds a row from them (FFT blog,
+// section 2.2: R2C / C2R on the N/2+1 half spectrum; TurboFNO blog, section
+// 2.1: only the kept modes are ever needed, so the rest is never computed).
+//
+// One wave per row, lane n1 < 64 holding the samples n = n1 + 64 n2, n2 < Q:
+// every load / store instruction of the wave touches 256 consecutive bytes.
+// With n = n1 + 64 n2 and W = exp(-2 pi i / N):
+//   X[k] = sum_n1 W^{n1 k} Y_n1[k mod Q],   Y_n1 = DFT_Q of lane n1's samples.
+// Forward: each lane runs its Q-point real DFT in registers (packed as a
+// Q/2-point complex one), twiddles the kept bins by W^{n1 k} and the 64 lanes'
+// contributions are summed through a per-wave LDS stage, 16 bins at a time.
+// Inverse: lane n1 forms V[r] = sum_{k = r mod Q} c_k X[k] W^{-n1 k}
+// (c_0 = 1 with the DC imaginary part dropped, c_k = 2 otherwise: the
+// Hermitian extension of the half spectrum); the real part of its inverse
+// DFT over r is exactly the lane's Q output samples, computed as the C2R of
+// the Hermitian part H[r] = (V[r] + conj V[-r]) / 2, packed as a Q/2-point
+// complex inverse DFT in registers.
+//
+// The twiddle W^{n1 k} is A[k & 7] * B[k >> 3] with A[j] = W^{n1 j} and
+// B[j] = W^{8 n1 j} read from the host-built table, so every twiddle is one
+// product of two correctly rounded values.  The waves of a workgroup share no
+// data; the grid is persistent, each wave walking rows.
+#include "fno_device.hpp"
+#include "fno_internal.hpp"
+
+namespace fno {
+namespace {
+
+constexpr int kPrunedThreads = 256;     // 4 independent waves
+constexpr int kPrunedWaves = kPrunedThreads / 64;
+constexpr int kStageStride = 68;        // reduction stage row stride (complex)
+
+// index of (bin kk, lane n1) in a wave's reduction stage
+__device__ __forceinline__ int stage_at(int kk, int n1) { return kk * kStageStride + n1 + (n1 >> 4); }
+
+__device__ __forceinline__ float dpp_xor1(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float dpp_xor2(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
+}
+
+__device__ __forceinline__ float2 conj2(float2 a) { return make_float2(a.x, -a.y); }
+
+// Makes the twiddle factors opaque once per row, so that their 64 products
+// are formed per row instead of being hoisted out of the row loop into 128
+// live registers.
+__device__ __forceinline__ void opaque_twiddles(float2 (&A)[8], float2 (&B)[8]) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) asm volatile("" : "+v"(A[j].x), "+v"(A[j].y), "+v"(B[j].x), "+v"(B[j].y));
+}
+
+// Bin K (K <= Q/2) of the DFT of a real length-Q sequence s from its packed
+// transform Z = DFT_{Q/2}(s[2m] + i s[2m+1]):
+//   Y[K] = (Z[K] + conj Z[-K]) / 2 + W_Q^K (Z[K] - conj Z[-K]) / 2i.
+template <int Q, int K>
+__device__ __forceinline__ float2 real_bin(const float2 (&z)[Q / 2]) {
+    constexpr int NZ = Q / 2;
+    const float2 zk = z[K % NZ];
+    const float2 zm = z[(NZ - K % NZ) % NZ];
+    const float2 e = make_float2(0.5f * (zk.x + zm.x), 0.5f * (zk.y - zm.y));
+    const float2 o = make_float2(0.5f * (zk.y + zm.y), -0.5f * (zk.x - zm.x));
+    return cadd(e, wmul<-1, Q, K>(o));
+}
+
+// Packed C2R bin K (K < Q/2) from a Hermitian half spectrum H[0..Q/2]:
+//   s[2m] + i s[2m+1] = IDFT_{Q/2}(Zp)[m],
+//   Zp[K] = (H[K] + conj H[Q/2-K]) + i W_Q^{-K} (H[K] - conj H[Q/2-K]).
+template <int Q, int K>
+__device__ __forceinline__ float2 packed_bin(const float2 (&H)[Q / 2 + 1]) {
+    constexpr int NZ = Q / 2;
+    const float2 hk = H[K], hm = H[NZ - K];
+    const float2 a = make_float2(hk.x + hm.x, hk.y - hm.y);
+    const float2 b = make_float2(hk.x - hm.x, hk.y + hm.y);
+    // i W_Q^{-K} b = W_Q^{-K} (i b)
+    return cadd(a, wmul<1, Q, K>(make_float2(-b.y, b.x)));
+}
+
+template <int Q>
+__global__ __launch_bounds__(kPrunedThreads) __attribute__((amdgpu_waves_per_eu(2))) void k_rows_fwd_pruned(const float* __restrict__ x,
+                                                                    float2* __restrict__ y, int64_t nrows, int my,
+                                                                    int y_ld, float scale,
+                                                                    const float2* __restrict__ tw) {
+    constexpr int N = 64 * Q;
+    constexpr int NZ = Q / 2;
+    __shared__ float2 stage_all[kPrunedWaves][16 * kStageStride];
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    float2* const stage = stage_all[wave];
+
+    float2 A[8], Bt[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        A[j] = tw[(lane * j * (kNMax / N)) & (kNMax - 1)];
+        Bt[j] = tw[(lane * 8 * j * (kNMax / N)) & (kNMax - 1)];
+    }
+    const int kk_r = lane >> 2;              // reduction role: bin kk_r of a chunk,
+    const int q_r = lane & 3;                // summing lanes 16 q_r .. 16 q_r + 15
+
+    const int64_t nwaves = (int64_t)gridDim.x * kPrunedWaves;
+    for (int64_t row = (int64_t)blockIdx.x * kPrunedWaves + wave; row < nrows; row += nwaves) {
+        opaque_twiddles(A, Bt);
+        const float* src = x + row * N + lane;
+        float2 z[NZ];
+#pragma unroll
+        for (int m = 0; m < NZ; ++m) z[m] = make_float2(src[64 * (2 * m)], src[64 * (2 * m + 1)]);
+        dft<NZ, -1>(z);
+        float2 Y[NZ + 1];
+        static_for<0, NZ + 1>([&](auto k) { Y[k] = real_bin<Q, k>(z); });
+
+        float2* const dst = y + row * (int64_t)y_ld;
+        static_for<0, 4>([&](auto ch) {
+            if (16 * ch < my) {                 // uniform: whole chunks of 16 bins
+                static_for<0, 16>([&](auto kk) {
+                    constexpr int k = 16 * ch + kk;
+                    constexpr int r = k % Q;
+                    const float2 yk = (r <= NZ) ? Y[r <= NZ ? r : 0] : conj2(Y[r <= NZ ? 0 : Q - r]);
+                    stage[stage_at(kk, lane)] = cmul(cmul(A[k & 7], Bt[k >> 3]), yk);
+                });
+                wave_lds_sync();
+                float2 acc = make_float2(0.0f, 0.0f);
+#pragma unroll
+                for (int t = 0; t < 16; ++t) acc = cadd(acc, stage[stage_at(kk_r, 16 * q_r + t)]);
+                acc.x += dpp_xor1(acc.x);
+                acc.y += dpp_xor1(acc.y);
+                acc.x += dpp_xor2(acc.x);
+                acc.y += dpp_xor2(acc.y);
+                const int k = 16 * ch + kk_r;
+                if (q_r == 0 && k < my) dst[k] = cscale(acc, scale);
+                wave_lds_sync();
+            }
+        });
+    }
+}
+
+template <int Q>
+__global__ __launch_bounds__(kPrunedThreads) __attribute__((amdgpu_waves_per_eu(2))) void k_rows_inv_pruned(const float2* __restrict__ y,
+                                                                    float* __restrict__ out, int64_t nrows, int my,
+                                                                    int y_ld, float scale,
+                                                                    const float2* __restrict__ tw) {
+    constexpr int N = 64 * Q;
+    constexpr int NZ = Q / 2;
+    __shared__ float2 xrow_all[kPrunedWaves][64];
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    float2* const xrow = xrow_all[wave];
+
+    float2 A[8], Bt[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        A[j] = tw[(lane * j * (kNMax / N)) & (kNMax - 1)];
+        Bt[j] = tw[(lane * 8 * j * (kNMax / N)) & (kNMax - 1)];
+    }
+
+    const int64_t nwaves = (int64_t)gridDim.x * kPrunedWaves;
+    for (int64_t row = (int64_t)blockIdx.x * kPrunedWaves + wave; row < nrows; row += nwaves) {
+        opaque_twiddles(A, Bt);
+        // the row's kept bins, zero past my, DC imaginary part dropped
+        {
+            float2 v = lane < my ? y[row * (int64_t)y_ld + lane] : make_float2(0.0f, 0.0f);
+            if (lane == 0) v.y = 0.0f;
+            xrow[lane] = v;
+        }
+        wave_lds_sync();
+        // V[r] = sum_{k = r mod Q} c_k X[k] conj(W^{n1 k}), c_0 = 1, c_k = 2
+        float2 V[Q];
+#pragma unroll
+        for (int r = 0; r < Q; ++r) V[r] = make_float2(0.0f, 0.0f);
+        static_for<0, 4>([&](auto ch) {
+            if (16 * ch < my) {
+                static_for<0, 16>([&](auto kk) {
+                    constexpr int k = 16 * ch + kk;
+                    const float2 w = cmul(A[k & 7], Bt[k >> 3]);
+                    const float2 u = cmul(xrow[k], make_float2(w.x, -w.y));
+                    constexpr float c = k == 0 ? 1.0f : 2.0f;
+                    V[k % Q] = make_float2(fmaf(c, u.x, V[k % Q].x), fmaf(c, u.y, V[k % Q].y));
+                });
+            }
+        });
+        wave_lds_sync();                        // the row buffer is read before the next row overwrites it
+        // Hermitian part H[r] = (V[r] + conj V[-r]) / 2, r <= Q/2, scaled
+        float2 H[NZ + 1];
+        static_for<0, NZ + 1>([&](auto r) {
+            const float2 a = V[r];
+            const float2 b = V[(Q - r) % Q];
+            const float h = 0.5f * scale;
+            H[r] = make_float2(h * (a.x + b.x), h * (a.y - b.y));
+        });
+        float2 z[NZ];
+        static_for<0, NZ>([&](auto k) { z[k] = packed_bin<Q, k>(H); });
+        dft<NZ, 1>(z);
+        float* const dst = out + row * N + lane;
+#pragma unroll
+        for (int m = 0; m < NZ; ++m) {
+            dst[64 * (2 * m)] = z[m].x;
+            dst[64 * (2 * m + 1)] = z[m].y;
+        }
+    }
+}
+
+template <typename K, typename TI, typename TO>
+hipError_t launch_rows(K kernel, int64_t nrows, hipStream_t s, const TI* in, TO* out, int my, int y_ld, float scale,
+                       const float2* tw) {
+    int dev = 0, cus = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return hipErrorInvalidDevice;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+    const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kPrunedThreads, 0);
+    if (e != hipSuccess) return e;
+    int64_t g = (int64_t)cus * (per_cu > 0 ? per_cu : 1);
+    const int64_t need = (nrows + kPrunedWaves - 1) / kPrunedWaves;
+    if (g > need) g = need;
+    return launch_kernel(kernel, dim3((unsigned)g), dim3(kPrunedThreads), 0, s, in, out, nrows, my, y_ld, scale, tw);
+}
+
+}  // namespace
+
+bool rows_pruned_supported(int log2W, int my) { return log2W >= 9 && log2W <= 12 && my >= 1 && my <= 64; }
+
+hipError_t launch_rows_fwd_pruned(const float* x, float2* y, int64_t nrows, int log2W, int my, int y_ld, float scale,
+                                  const float2* tw, hipStream_t s) {
+    if (!rows_pruned_supported(log2W, my) || nrows <= 0) return hipErrorInvalidValue;
+    switch (log2W) {
+        case 9: return launch_rows(k_rows_fwd_pruned<8>, nrows, s, x, y, my, y_ld, scale, tw);
+        case 10: return launch_rows(k_rows_fwd_pruned<16>, nrows, s, x, y, my, y_ld, scale, tw);
+        case 11: return launch_rows(k_rows_fwd_pruned<32>, nrows, s, x, y, my, y_ld, scale, tw);
+        default: return launch_rows(k_rows_fwd_pruned<64>, nrows, s, x, y, my, y_ld, scale, tw);
+    }
+}
+
+hipError_t launch_rows_inv_pruned(const float2* y, float* out, int64_t nrows, int log2W, int my, int y_ld,
+                                  float scale, const float2* tw, hipStream_t s) {
+    if (!rows_pruned_supported(log2W, my) || nrows <= 0) return hipErrorInvalidValue;
+    switch (log2W) {
+        case 9: return launch_rows(k_rows_inv_pruned<8>, nrows, s, y, out, my, y_ld, scale, tw);
+        case 10: return launch_rows(k_rows_inv_pruned<16>, nrows, s, y, out, my, y_ld, scale, tw);
+        case 11: return launch_rows(k_rows_inv_pruned<32>, nrows, s, y, out, my, y_ld, scale, tw);
+        default: return launch_rows(k_rows_inv_pruned<64>, nrows, s, y, out, my, y_ld, scale, tw);
+    }
+}
+
+}  // namespace fno

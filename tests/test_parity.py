@@ -158,6 +158,8 @@ EDGE_2D = [
     (2, 3, 4, 64, 64, 32, 32),      # one-row-per-thread forward: every kx kept, two column batches
     (2, 2, 2, 128, 64, 5, 17),      # one-row-per-thread forward: tall, my just past one batch
     (2, 2, 2, 64, 128, 9, 3),       # one-row-per-thread forward: wide rows, few columns
+    (1, 2, 3, 16, 1024, 5, 50),     # pruned long rows (1024 points), ragged last bin chunk
+    (1, 1, 2, 8, 4096, 2, 64),      # pruned long rows at the longest length, every chunk
 ]
 
 
@@ -179,6 +181,10 @@ EDGE_1D = [
     (7, 3, 5, 64, 17),              # odd rows B*Cin = 21
     (2, 4, 70, 4096, 2049),         # longest sequence, every bin kept
     (33, 2, 3, 256, 1),             # DC only
+    (5, 3, 2, 512, 64),             # pruned rows, 8 samples per lane, bins wrap mod 8
+    (3, 2, 3, 1024, 1),             # pruned rows, DC only
+    (4, 3, 5, 2048, 37),            # pruned rows, partial last chunk of 16 bins
+    (9, 2, 2, 4096, 17),            # pruned rows, odd row count
 ]
 
 
