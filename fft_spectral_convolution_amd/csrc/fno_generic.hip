@@ -219,12 +219,11 @@ hipError_t launch_rows_fwd(const float* x, float2* y, int64_t nrows, int log2W, 
     const dim3 grid((unsigned)((npairs + p - 1) / p));
     switch (log2W) {
 #define CASE(L) \
-    case L: launch_kernel(k_rows_fwd<L>, grid, dim3(kThreads), 0, s, x, y, nrows, my, y_ld, scale, tw); break;
+    case L: return launch_kernel(k_rows_fwd<L>, grid, dim3(kThreads), 0, s, x, y, nrows, my, y_ld, scale, tw);
         FNO_LOG2_CASES(CASE)
 #undef CASE
         default: return hipErrorInvalidValue;
     }
-    return hipGetLastError();
 }
 
 hipError_t launch_rows_inv(const float2* y, float* out, int64_t nrows, int log2W, int my, int y_ld, float scale,
@@ -235,12 +234,11 @@ hipError_t launch_rows_inv(const float2* y, float* out, int64_t nrows, int log2W
     const dim3 grid((unsigned)((npairs + p - 1) / p));
     switch (log2W) {
 #define CASE(L) \
-    case L: launch_kernel(k_rows_inv<L>, grid, dim3(kThreads), 0, s, y, out, nrows, my, y_ld, scale, tw); break;
+    case L: return launch_kernel(k_rows_inv<L>, grid, dim3(kThreads), 0, s, y, out, nrows, my, y_ld, scale, tw);
         FNO_LOG2_CASES(CASE)
 #undef CASE
         default: return hipErrorInvalidValue;
     }
-    return hipGetLastError();
 }
 
 static int cols_per_block(int log2H, int my) {
@@ -255,12 +253,11 @@ hipError_t launch_cols_fwd(const float2* r, float2* xh, int64_t nimg, int log2H,
     const dim3 grid((unsigned)(nkb * nimg));
     switch (log2H) {
 #define CASE(L) \
-    case L: launch_kernel(k_cols_fwd<L>, grid, dim3(kThreads), 0, s, r, xh, mx, my, kb, nkb, scale, tw); break;
+    case L: return launch_kernel(k_cols_fwd<L>, grid, dim3(kThreads), 0, s, r, xh, mx, my, kb, nkb, scale, tw);
         FNO_LOG2_CASES(CASE)
 #undef CASE
         default: return hipErrorInvalidValue;
     }
-    return hipGetLastError();
 }
 
 hipError_t launch_cols_inv(const float2* yh, float2* r, int64_t nimg, int log2H, int mx, int my,
@@ -270,12 +267,11 @@ hipError_t launch_cols_inv(const float2* yh, float2* r, int64_t nimg, int log2H,
     const dim3 grid((unsigned)(nkb * nimg));
     switch (log2H) {
 #define CASE(L) \
-    case L: launch_kernel(k_cols_inv<L>, grid, dim3(kThreads), 0, s, yh, r, mx, my, kb, nkb, tw); break;
+    case L: return launch_kernel(k_cols_inv<L>, grid, dim3(kThreads), 0, s, yh, r, mx, my, kb, nkb, tw);
         FNO_LOG2_CASES(CASE)
 #undef CASE
         default: return hipErrorInvalidValue;
     }
-    return hipGetLastError();
 }
 
 hipError_t launch_mix_valu(const float2* xh, const SpecLayout& lx, const float2* w, float2* yh,
@@ -290,9 +286,8 @@ hipError_t launch_mix_valu(const float2* xh, const SpecLayout& lx, const float2*
     const dim3 grid((unsigned)(n_ot * n_mt * n_bt));
     const MixAddr ax{lx.sb, lx.sc, lx.st};
     const MixAddr ay{ly.sb, ly.sc, ly.st};
-    launch_kernel(k_mix_valu, grid, dim3(kThreads), 0, s, xh, ax, w, yh, ay, B, Cin, Cout, M, ot_log2, n_ot,
-                       n_mt);
-    return hipGetLastError();
+    return launch_kernel(k_mix_valu, grid, dim3(kThreads), 0, s, xh, ax, w, yh, ay, B, Cin, Cout, M, ot_log2, n_ot,
+                         n_mt);
 }
 
 }  // namespace fno

@@ -18,8 +18,8 @@
 //    B operand, as float4 pairs (o, o + 1): column block p holds
 //    o = 2 c + p, c < 16.
 // The grid is persistent and every workgroup walks a contiguous range of
-// tiles as one flat sequence of chunks: X and W are fetched two chunks ahead across tile
-// boundaries (unconditional, clamped loads, so the compiler can count
+// tiles as one flat sequence of chunks: X and W are fetched two chunks ahead
+// across tile boundaries (unconditional, clamped loads, so the compiler can count
 // outstanding loads exactly), and a tile's results leave through LDS in
 // 32-byte runs while the next tile's first chunks are already in flight.
 // Rows, channels and modes past the ends are masked.
@@ -254,18 +254,17 @@ __global__ __launch_bounds__(kMixThreads) void k_mix_mfma(const float2* __restri
 }
 
 template <bool VEC>
-void launch_mix_variant(dim3 grid, hipStream_t s, const float2* xh, Addr ax, const float2* w, float2* yh, Addr ay,
+hipError_t launch_mix_variant(dim3 grid, hipStream_t s, const float2* xh, Addr ax, const float2* w, float2* yh, Addr ay,
                         int B, int Cin, int Cout, int M, TileGrid tg, int nch) {
     switch (nch) {
 #define CASE(N)                                                                                              \
     case N:                                                                                                  \
-        launch_kernel((k_mix_mfma<N, VEC>), grid, dim3(kMixThreads), 0, s, xh, ax, w, yh, ay, B, Cin, \
-                           Cout, M, tg);                                                                     \
-        break;
+        return launch_kernel((k_mix_mfma<N, VEC>), grid, dim3(kMixThreads), 0, s, xh, ax, w, yh, ay, B, Cin, \
+                           Cout, M, tg);
         CASE(2) CASE(4) CASE(6) CASE(8) CASE(10) CASE(12) CASE(14) CASE(16)
 #undef CASE
         default:
-            break;
+            return hipErrorInvalidValue;
     }
 }
 
@@ -303,9 +302,8 @@ hipError_t launch_mix_mfma(const float2* xh, const SpecLayout& lx, const float2*
     const bool vec = lx.sc == 8 && ly.sc == 8 && lx.st % 2 == 0 && ly.st % 2 == 0 && lx.sb % 2 == 0 &&
                      ly.sb % 2 == 0 && M % 8 == 0 && aligned16(xh) && aligned16(yh);
     const int nch = (int)mix_chunks(Cin);
-    if (vec) launch_mix_variant<true>(grid, s, xh, ax, w, yh, ay, (int)B, (int)Cin, (int)Cout, (int)M, tg, nch);
-    else launch_mix_variant<false>(grid, s, xh, ax, w, yh, ay, (int)B, (int)Cin, (int)Cout, (int)M, tg, nch);
-    return hipGetLastError();
+    if (vec) return launch_mix_variant<true>(grid, s, xh, ax, w, yh, ay, (int)B, (int)Cin, (int)Cout, (int)M, tg, nch);
+    return launch_mix_variant<false>(grid, s, xh, ax, w, yh, ay, (int)B, (int)Cin, (int)Cout, (int)M, tg, nch);
 }
 
 }  // namespace fno

@@ -419,8 +419,7 @@ hipError_t launch_persistent(K k, int nt, size_t lds, int64_t nimg, hipStream_t 
     int64_t g = (int64_t)cus * (per_cu > 0 ? per_cu : 1);
     g = g >= 16 ? (g / 16) * 16 : g;
     if (g > nimg) g = nimg;
-    launch_kernel(k, dim3((unsigned)g), dim3(nt), lds, s, args...);
-    return hipGetLastError();
+    return launch_kernel(k, dim3((unsigned)g), dim3(nt), lds, s, args...);
 }
 
 template <int LH, int LW, int MYM>

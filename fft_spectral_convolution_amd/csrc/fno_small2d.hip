@@ -495,15 +495,13 @@ hipError_t launch_fwd2d_small(const float* x, float2* xh, const SpecLayout& lay,
 #define CASE(LH, LW)                                                                                          \
     case LH * 16 + LW: {                                                                                      \
         const size_t lds = SmallPlan<LH, LW>::lds_bytes(my);                                                  \
-        launch_kernel((k_fwd2d_small<LH, LW>), grid, dim3(kSmallThreads), lds, s, x, xh, ma, nimg, mx, my, \
+        return launch_kernel((k_fwd2d_small<LH, LW>), grid, dim3(kSmallThreads), lds, s, x, xh, ma, nimg, mx, my, \
                            scale, tw);                                                                        \
-        break;                                                                                                \
     }
         FNO_SMALL_CASES(CASE)
 #undef CASE
         default: return hipErrorInvalidValue;
     }
-    return hipGetLastError();
 }
 
 hipError_t launch_inv2d_small(const float2* yh, float* out, const SpecLayout& lay, int64_t nimg, int log2H, int log2W,
@@ -514,15 +512,13 @@ hipError_t launch_inv2d_small(const float2* yh, float* out, const SpecLayout& la
 #define CASE(LH, LW)                                                                                            \
     case LH * 16 + LW: {                                                                                        \
         const size_t lds = SmallPlan<LH, LW>::lds_bytes(my);                                                    \
-        launch_kernel((k_inv2d_small<LH, LW>), grid, dim3(kSmallThreads), lds, s, yh, out, ma, nimg, mx, my, \
+        return launch_kernel((k_inv2d_small<LH, LW>), grid, dim3(kSmallThreads), lds, s, yh, out, ma, nimg, mx, my, \
                            scale, tw);                                                                          \
-        break;                                                                                                  \
     }
         FNO_SMALL_CASES(CASE)
 #undef CASE
         default: return hipErrorInvalidValue;
     }
-    return hipGetLastError();
 }
 
 }  // namespace fno
