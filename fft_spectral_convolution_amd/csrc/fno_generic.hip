@@ -248,6 +248,7 @@ static int cols_per_block(int log2H, int my) {
 
 hipError_t launch_cols_fwd(const float2* r, float2* xh, int64_t nimg, int log2H, int mx, int my, float scale,
                            const float2* tw, hipStream_t s) {
+    if (cols_pruned_supported(log2H, mx, my)) return launch_cols_fwd_pruned(r, xh, nimg, log2H, mx, my, scale, tw, s);
     const int kb = cols_per_block(log2H, my);
     const int nkb = (my + kb - 1) / kb;
     const dim3 grid((unsigned)(nkb * nimg));
@@ -262,6 +263,7 @@ hipError_t launch_cols_fwd(const float2* r, float2* xh, int64_t nimg, int log2H,
 
 hipError_t launch_cols_inv(const float2* yh, float2* r, int64_t nimg, int log2H, int mx, int my,
                            const float2* tw, hipStream_t s) {
+    if (cols_pruned_supported(log2H, mx, my)) return launch_cols_inv_pruned(yh, r, nimg, log2H, mx, my, tw, s);
     const int kb = cols_per_block(log2H, my);
     const int nkb = (my + kb - 1) / kb;
     const dim3 grid((unsigned)(nkb * nimg));

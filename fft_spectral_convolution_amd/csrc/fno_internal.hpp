@@ -89,6 +89,16 @@ hipError_t launch_rows_fwd_pruned(const float* x, float2* y, int64_t nrows, int 
 hipError_t launch_rows_inv_pruned(const float2* y, float* out, int64_t nrows, int log2W, int my, int y_ld,
                                   float scale, const float2* tw, hipStream_t s);
 
+// ---- pruned column transforms (fno_cols_pruned.hip) --------------------------
+// H in [512, 2048], 2 mx <= 128 and a multiple of H / 64, my <= 64: same
+// contract as launch_cols_fwd / launch_cols_inv below, which use them
+// whenever cols_pruned_supported holds.
+bool cols_pruned_supported(int log2H, int mx, int my);
+hipError_t launch_cols_fwd_pruned(const float2* r, float2* xh, int64_t nimg, int log2H, int mx, int my, float scale,
+                                  const float2* tw, hipStream_t s);
+hipError_t launch_cols_inv_pruned(const float2* yh, float2* r, int64_t nimg, int log2H, int mx, int my,
+                                  const float2* tw, hipStream_t s);
+
 // ---- generic stage launchers (fno_generic.hip) -------------------------------
 // All return hipSuccess or the launch error.  `tw` is the device twiddle table.
 

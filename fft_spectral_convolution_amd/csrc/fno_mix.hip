@@ -71,11 +71,16 @@ __global__ __launch_bounds__(kMixThreads) void k_mix_mfma(const float2* __restri
                                                           const float2* __restrict__ w, float2* __restrict__ yh,
                                                           Addr ay, int B, int Cin, int Cout, int M, TileGrid tg) {
     static_assert(NCH % 2 == 0, "chunks alternate between two register sets");
-    constexpr int kAS = kMixBRows + 1;                     // [i][m][b] row stride
-    constexpr int kYS = kMixOCols + 1;                     // [b8][m][o] row stride
-    constexpr int kAChunk = kMixKC * 8 * kAS;
-    __shared__ float2 a_lds[2 * kAChunk];                  // 2 x 16.5 KiB
-    __shared__ float2 y_lds[8 * 8 * kYS];                  // 16.5 KiB
+    // X chunk in LDS: (i, m, b) at i * kAI + m * kAM + (b ^ 2 (i >> 1)).  The
+    // strides and the swizzle make both the staging writes (lanes over
+    // mode halves, channels and two batch rows) and the MFMA operand reads
+    // (lanes over 16 batch rows and two channels) hit 32 different bank pairs.
+    constexpr int kAM = 34;                                // mode stride (complex)
+    constexpr int kAI = 8 * kAM;                           // channel stride: 16 mod 32
+    constexpr int kAChunk = kMixKC * kAI;
+    constexpr int kYS = 36;                                // [b8][m][o] row stride (16-byte rows, 4 mod 8)
+    __shared__ float2 a_lds[2 * kAChunk];                  // 2 x 17 KiB
+    __shared__ __attribute__((aligned(16))) float2 y_lds[8 * 8 * kYS];   // 18 KiB
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -113,7 +118,7 @@ __global__ __launch_bounds__(kMixThreads) void k_mix_mfma(const float2* __restri
         const bool iok = chunk * kMixKC + sil < Cin;
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-            buf[(sil * 8 + shalf * 4 + q) * kAS + sbl] = iok ? av[q] : make_float2(0.0f, 0.0f);
+            buf[sil * kAI + (shalf * 4 + q) * kAM + (sbl ^ (2 * (sil >> 1)))] = iok ? av[q] : make_float2(0.0f, 0.0f);
     };
     // W pairs for k-step s (channels chunk*8 + 4s + lk): wv[s] = (W[i][o],
     // W[i][o + 1]), o = o0 + 2 l16 (Cout is even on this path; columns past
@@ -138,7 +143,10 @@ __global__ __launch_bounds__(kMixThreads) void k_mix_mfma(const float2* __restri
         for (int s = 0; s < 2; ++s) {
             float2 a[2];
 #pragma unroll
-            for (int rb = 0; rb < 2; ++rb) a[rb] = buf[((4 * s + lk) * 8 + wave) * kAS + 16 * rb + l16];
+            for (int rb = 0; rb < 2; ++rb) {
+                const int i = 4 * s + lk;
+                a[rb] = buf[i * kAI + wave * kAM + ((16 * rb + l16) ^ (2 * (i >> 1)))];
+            }
 #pragma unroll
             for (int rb = 0; rb < 2; ++rb) {
                 const float as = a[rb].x + a[rb].y;
@@ -170,11 +178,16 @@ __global__ __launch_bounds__(kMixThreads) void k_mix_mfma(const float2* __restri
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int bl = 4 * (lk & 1) + r;    // row within the round
+                    // columns 2 l16 and 2 l16 + 1 (blocks cb = 0, 1) as one 16-byte write
+                    float y4[4];
 #pragma unroll
                     for (int cb = 0; cb < 2; ++cb) {
                         const float pr = p1[rb][cb][r], pi = p2[rb][cb][r];
-                        y_lds[(bl * 8 + wave) * kYS + 2 * l16 + cb] = make_float2(pr - pi, p3[rb][cb][r] - pr - pi);
+                        y4[2 * cb] = pr - pi;
+                        y4[2 * cb + 1] = p3[rb][cb][r] - pr - pi;
                     }
+                    *reinterpret_cast<float4*>(y_lds + (bl * 8 + wave) * kYS + 2 * l16) =
+                        make_float4(y4[0], y4[1], y4[2], y4[3]);
                 }
             }
             lds_barrier();

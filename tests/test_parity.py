@@ -160,6 +160,10 @@ EDGE_2D = [
     (2, 2, 2, 64, 128, 9, 3),       # one-row-per-thread forward: wide rows, few columns
     (1, 2, 3, 16, 1024, 5, 50),     # pruned long rows (1024 points), ragged last bin chunk
     (1, 1, 2, 8, 4096, 2, 64),      # pruned long rows at the longest length, every chunk
+    (1, 2, 3, 1024, 16, 8, 9),      # pruned columns (1024 rows), ragged column block
+    (2, 2, 2, 512, 32, 4, 7),       # pruned columns (512 rows), few kept rows
+    (1, 1, 2, 1024, 8, 5, 3),       # tall grid whose kept rows do not suit the pruned columns
+    (1, 2, 2, 2048, 128, 64, 60),   # pruned columns at the large-grid row count, 128 kept rows
 ]
 
 
