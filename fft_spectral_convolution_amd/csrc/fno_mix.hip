@@ -8,15 +8,16 @@
 //   Yr = P1 - P2,  Yi = P3 - P1 - P2,
 // all accumulated in fp32.
 //
-// Tile = 8 consecutive modes x 32 batch rows x 32 output channels, one
-// workgroup of 8 waves; wave w owns mode m0 + w, a 32 x 32 result = 2 x 2
-// blocks of 16 x 16 with three accumulators each.  Input channels are
-// consumed in chunks of 8 (two MFMA k-steps of 4):
+// Tile = 8 consecutive modes x 32 batch rows x 16 NCB output channels
+// (NCB = 4 when Cout allows it, so that each X element is fetched once; else
+// 2), one workgroup of 8 waves; wave w owns mode m0 + w, a 32 x 16 NCB result
+// = 2 x NCB blocks of 16 x 16 with three accumulators each.  Input channels
+// are consumed in chunks of 8 (two MFMA k-steps of 4):
 //  * the X chunk of all 8 modes ([32 b][8 i][8 m], one 64-byte run per
 //    (b, i)) is staged in LDS as [i][m][b] and shared by the 8 waves;
 //  * each wave streams its own W_m rows from global memory straight into the
-//    B operand, as float4 pairs (o, o + 1): column block p holds
-//    o = 2 c + p, c < 16.
+//    B operand, as float4 pairs (o, o + 1): column block 2 h + p holds
+//    o = 32 h + 2 c + p, c < 16.
 // The grid is persistent and every workgroup walks a contiguous range of
 // tiles as one flat sequence of chunks: X and W are fetched two chunks ahead
 // across tile boundaries (unconditional, clamped loads, so the compiler can count
@@ -35,7 +36,6 @@ constexpr int kMixWaves = 8;           // = modes per tile
 constexpr int kMixThreads = 64 * kMixWaves;
 constexpr int kMixKC = 8;              // input channels per chunk
 constexpr int kMixBRows = 32;          // batch rows per tile (2 MFMA row blocks)
-constexpr int kMixOCols = 32;          // output channels per tile (2 MFMA column blocks)
 
 struct Addr {
     int64_t sb, sc, st;
@@ -45,7 +45,7 @@ struct Addr {
 };
 
 struct TileGrid {
-    int n_mt, n_bt, n_ot, n_tiles;
+    int n_mt, n_bt, n_ot, n_tiles, o_cols;
 };
 
 struct Tile {
@@ -60,17 +60,20 @@ __device__ __forceinline__ floatx4 mfma16(float a, float b, floatx4 c) {
 __device__ __forceinline__ Tile tile_of(const TileGrid& tg, int t) {
     const int ot = t % tg.n_ot;
     const int r = t / tg.n_ot;
-    return Tile{(r % tg.n_mt) * 8, (r / tg.n_mt) * kMixBRows, ot * kMixOCols};
+    return Tile{(r % tg.n_mt) * 8, (r / tg.n_mt) * kMixBRows, ot * tg.o_cols};
 }
 
 // VEC: every (b, c) run of 8 modes is 16-byte aligned and complete (tiled
 // layout), so X is read and Y written as float4; otherwise element-wise.
 // NCH: chunks of input channels per tile (even; chunks past Cin are zero).
-template <int NCH, bool VEC>
+// NCB: 16-column MFMA blocks per tile (2 or 4; Cout is a multiple of NCB).
+template <int NCH, bool VEC, int NCB>
 __global__ __launch_bounds__(kMixThreads) void k_mix_mfma(const float2* __restrict__ xh, Addr ax,
                                                           const float2* __restrict__ w, float2* __restrict__ yh,
                                                           Addr ay, int B, int Cin, int Cout, int M, TileGrid tg) {
     static_assert(NCH % 2 == 0, "chunks alternate between two register sets");
+    static_assert(NCB == 2 || NCB == 4, "W runs are one or two float4 per lane");
+    constexpr int kO = 16 * NCB;                           // output channels per tile
     // X chunk in LDS: (i, m, b) at i * kAI + m * kAM + (b ^ 2 (i >> 1)).  The
     // strides and the swizzle make both the staging writes (lanes over
     // mode halves, channels and two batch rows) and the MFMA operand reads
@@ -78,9 +81,9 @@ __global__ __launch_bounds__(kMixThreads) void k_mix_mfma(const float2* __restri
     constexpr int kAM = 34;                                // mode stride (complex)
     constexpr int kAI = 8 * kAM;                           // channel stride: 16 mod 32
     constexpr int kAChunk = kMixKC * kAI;
-    constexpr int kYS = 36;                                // [b8][m][o] row stride (16-byte rows, 4 mod 8)
+    constexpr int kYS = kO + 4;                            // [b8][m][o] row stride (16-byte rows, 4 mod 8)
     __shared__ float2 a_lds[2 * kAChunk];                  // 2 x 17 KiB
-    __shared__ __attribute__((aligned(16))) float2 y_lds[8 * 8 * kYS];   // 18 KiB
+    __shared__ __attribute__((aligned(16))) float2 y_lds[8 * 8 * kYS];   // 18 or 34 KiB
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -120,25 +123,28 @@ __global__ __launch_bounds__(kMixThreads) void k_mix_mfma(const float2* __restri
         for (int q = 0; q < 4; ++q)
             buf[sil * kAI + (shalf * 4 + q) * kAM + (sbl ^ (2 * (sil >> 1)))] = iok ? av[q] : make_float2(0.0f, 0.0f);
     };
-    // W pairs for k-step s (channels chunk*8 + 4s + lk): wv[s] = (W[i][o],
-    // W[i][o + 1]), o = o0 + 2 l16 (Cout is even on this path; columns past
-    // Cout are clamped and never stored).
-    auto load_w = [&](const Tile& tl, int chunk, float2 (&wv)[4]) __attribute__((always_inline)) {
+    // W pairs for k-step s (channels chunk*8 + 4s + lk): wv[NCB s + 2 h + p]
+    // = W[i][o_h + p], o_h = o0 + 32 h + 2 l16 (Cout is even on this path;
+    // columns past Cout are clamped and never stored).
+    auto load_w = [&](const Tile& tl, int chunk, float2 (&wv)[2 * NCB]) __attribute__((always_inline)) {
         const int mw = tl.m0 + wave < M ? tl.m0 + wave : M - 1;
-        int o = tl.o0 + 2 * l16;
-        o = o < Cout ? o : Cout - 2;
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
             const int i = chunk * kMixKC + 4 * s + lk;
             const int ic = i < Cin ? i : Cin - 1;
-            const float4 v = *reinterpret_cast<const float4*>(w + ((int64_t)mw * Cin + ic) * Cout + o);
-            wv[2 * s] = make_float2(v.x, v.y);
-            wv[2 * s + 1] = make_float2(v.z, v.w);
+#pragma unroll
+            for (int h = 0; h < NCB / 2; ++h) {
+                int o = tl.o0 + 32 * h + 2 * l16;
+                o = o < Cout ? o : Cout - 2;
+                const float4 v = *reinterpret_cast<const float4*>(w + ((int64_t)mw * Cin + ic) * Cout + o);
+                wv[NCB * s + 2 * h] = make_float2(v.x, v.y);
+                wv[NCB * s + 2 * h + 1] = make_float2(v.z, v.w);
+            }
         }
     };
 
-    floatx4 p1[2][2], p2[2][2], p3[2][2];
-    auto mfma_chunk = [&](const float2* buf, const float2 (&wv)[4]) __attribute__((always_inline)) {
+    floatx4 p1[2][NCB], p2[2][NCB], p3[2][NCB];
+    auto mfma_chunk = [&](const float2* buf, const float2 (&wv)[2 * NCB]) __attribute__((always_inline)) {
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
             float2 a[2];
@@ -151,8 +157,8 @@ __global__ __launch_bounds__(kMixThreads) void k_mix_mfma(const float2* __restri
             for (int rb = 0; rb < 2; ++rb) {
                 const float as = a[rb].x + a[rb].y;
 #pragma unroll
-                for (int cb = 0; cb < 2; ++cb) {
-                    const float2 wc = wv[2 * s + cb];
+                for (int cb = 0; cb < NCB; ++cb) {
+                    const float2 wc = wv[NCB * s + cb];
                     p1[rb][cb] = mfma16(a[rb].x, wc.x, p1[rb][cb]);
                     p2[rb][cb] = mfma16(a[rb].y, wc.y, p2[rb][cb]);
                     p3[rb][cb] = mfma16(as, wc.x + wc.y, p3[rb][cb]);
@@ -162,15 +168,10 @@ __global__ __launch_bounds__(kMixThreads) void k_mix_mfma(const float2* __restri
     };
 
     // C layout of a 16x16 block: lane holds column l16 and, in register r,
-    // row 4 * lk + r.  Row block rb adds 16; column block cb holds
-    // o = 2 l16 + cb.  Four rounds of 8 batch rows: round rr holds row block
+    // row 4 * lk + r.  Row block rb adds 16; column block 2 h + p holds
+    // o = 32 h + 2 l16 + p.  Four rounds of 8 batch rows: round rr holds row block
     // rr / 2 and the lanes with lk / 2 == rr % 2.
     auto epilogue = [&](const Tile& tl) __attribute__((always_inline)) {
-        // thread -> (b, o, half of the modes) of a round: consecutive threads
-        // write consecutive 32-byte runs
-        const int bl_s = tid >> 6;
-        const int ol_s = (tid >> 1) & 31;
-        const int qh = tid & 1;
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
             const int rb = rr >> 1;
@@ -178,34 +179,44 @@ __global__ __launch_bounds__(kMixThreads) void k_mix_mfma(const float2* __restri
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int bl = 4 * (lk & 1) + r;    // row within the round
-                    // columns 2 l16 and 2 l16 + 1 (blocks cb = 0, 1) as one 16-byte write
-                    float y4[4];
+                    // columns 32 h + 2 l16 + p, p < 2, as one 16-byte write per h
+                    float yv[2 * NCB];
 #pragma unroll
-                    for (int cb = 0; cb < 2; ++cb) {
+                    for (int cb = 0; cb < NCB; ++cb) {
                         const float pr = p1[rb][cb][r], pi = p2[rb][cb][r];
-                        y4[2 * cb] = pr - pi;
-                        y4[2 * cb + 1] = p3[rb][cb][r] - pr - pi;
+                        yv[2 * cb] = pr - pi;
+                        yv[2 * cb + 1] = p3[rb][cb][r] - pr - pi;
                     }
-                    *reinterpret_cast<float4*>(y_lds + (bl * 8 + wave) * kYS + 2 * l16) =
-                        make_float4(y4[0], y4[1], y4[2], y4[3]);
+#pragma unroll
+                    for (int h = 0; h < NCB / 2; ++h)
+                        *reinterpret_cast<float4*>(y_lds + (bl * 8 + wave) * kYS + 32 * h + 2 * l16) =
+                            make_float4(yv[4 * h], yv[4 * h + 1], yv[4 * h + 2], yv[4 * h + 3]);
                 }
             }
             lds_barrier();
-            const int b = tl.b0 + rr * 8 + bl_s;
-            const int o = tl.o0 + ol_s;
-            if (b < B && o < Cout) {
-                float2 v[4];
+            // item -> (b, o, half of the modes) of the round: consecutive
+            // items write consecutive 32-byte runs
 #pragma unroll
-                for (int q = 0; q < 4; ++q) v[q] = y_lds[(bl_s * 8 + 4 * qh + q) * kYS + ol_s];
-                if constexpr (VEC) {
-                    float4* dst = reinterpret_cast<float4*>(yh + ay.at(b, o, tl.m0 + 4 * qh));
-                    dst[0] = make_float4(v[0].x, v[0].y, v[1].x, v[1].y);
-                    dst[1] = make_float4(v[2].x, v[2].y, v[3].x, v[3].y);
-                } else {
+            for (int it = tid; it < 8 * kO * 2; it += kMixThreads) {
+                const int bl_s = it / (2 * kO);
+                const int ol_s = (it >> 1) % kO;
+                const int qh = it & 1;
+                const int b = tl.b0 + rr * 8 + bl_s;
+                const int o = tl.o0 + ol_s;
+                if (b < B && o < Cout) {
+                    float2 v[4];
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const int mm = tl.m0 + 4 * qh + q;
-                        if (mm < M) yh[ay.at(b, o, mm)] = v[q];
+                    for (int q = 0; q < 4; ++q) v[q] = y_lds[(bl_s * 8 + 4 * qh + q) * kYS + ol_s];
+                    if constexpr (VEC) {
+                        float4* dst = reinterpret_cast<float4*>(yh + ay.at(b, o, tl.m0 + 4 * qh));
+                        dst[0] = make_float4(v[0].x, v[0].y, v[1].x, v[1].y);
+                        dst[1] = make_float4(v[2].x, v[2].y, v[3].x, v[3].y);
+                    } else {
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            const int mm = tl.m0 + 4 * qh + q;
+                            if (mm < M) yh[ay.at(b, o, mm)] = v[q];
+                        }
                     }
                 }
             }
@@ -218,8 +229,8 @@ __global__ __launch_bounds__(kMixThreads) void k_mix_mfma(const float2* __restri
     // last tile the last chunk is reloaded).  LDS buffer k & 1 is rewritten
     // only after every wave passed the barrier of chunk k - 1, i.e. after all
     // reads of chunk k - 2.
-    // workgroup j walks the contiguous tile range [t_begin, t_end), so both
-    // output tiles of a mode tile run back to back (the second reads X from L2)
+    // workgroup j walks the contiguous tile range [t_begin, t_end), so the
+    // output tiles of a mode tile (when Cout needs several) run back to back
     const int G = gridDim.x;
     const int t_begin = (int)((int64_t)tg.n_tiles * blockIdx.x / G);
     const int t_end = (int)((int64_t)tg.n_tiles * (blockIdx.x + 1) / G);
@@ -227,7 +238,7 @@ __global__ __launch_bounds__(kMixThreads) void k_mix_mfma(const float2* __restri
     Tile cur = tile_of(tg, t);
     Tile nxt = tile_of(tg, t + 1 < t_end ? t + 1 : t);
     float2 aA[4], aB[4];
-    float2 wA[4], wB[4];
+    float2 wA[2 * NCB], wB[2 * NCB];
     load_a(cur, 0, aA);
     load_w(cur, 0, wA);
     load_a(cur, 1, aB);
@@ -237,7 +248,7 @@ __global__ __launch_bounds__(kMixThreads) void k_mix_mfma(const float2* __restri
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-            for (int cb = 0; cb < 2; ++cb) {
+            for (int cb = 0; cb < NCB; ++cb) {
                 p1[rb][cb] = floatx4{0.f, 0.f, 0.f, 0.f};
                 p2[rb][cb] = floatx4{0.f, 0.f, 0.f, 0.f};
                 p3[rb][cb] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -266,13 +277,13 @@ __global__ __launch_bounds__(kMixThreads) void k_mix_mfma(const float2* __restri
     }
 }
 
-template <bool VEC>
+template <bool VEC, int NCB>
 hipError_t launch_mix_variant(dim3 grid, hipStream_t s, const float2* xh, Addr ax, const float2* w, float2* yh, Addr ay,
                         int B, int Cin, int Cout, int M, TileGrid tg, int nch) {
     switch (nch) {
-#define CASE(N)                                                                                              \
-    case N:                                                                                                  \
-        return launch_kernel((k_mix_mfma<N, VEC>), grid, dim3(kMixThreads), 0, s, xh, ax, w, yh, ay, B, Cin, \
+#define CASE(N)                                                                                                   \
+    case N:                                                                                                       \
+        return launch_kernel((k_mix_mfma<N, VEC, NCB>), grid, dim3(kMixThreads), 0, s, xh, ax, w, yh, ay, B, Cin, \
                            Cout, M, tg);
         CASE(2) CASE(4) CASE(6) CASE(8) CASE(10) CASE(12) CASE(14) CASE(16)
 #undef CASE
@@ -298,13 +309,19 @@ hipError_t launch_mix_mfma(const float2* xh, const SpecLayout& lx, const float2*
     TileGrid tg;
     tg.n_mt = (int)((M + 7) / 8);
     tg.n_bt = (int)((B + kMixBRows - 1) / kMixBRows);
-    tg.n_ot = (int)((Cout + kMixOCols - 1) / kMixOCols);
-    const int64_t n_tiles = (int64_t)tg.n_mt * tg.n_bt * tg.n_ot;
-    if (n_tiles >= INT32_MAX / 2) return hipErrorInvalidValue;
-    tg.n_tiles = (int)n_tiles;
     int dev = 0, cus = 0;
     if (hipGetDevice(&dev) != hipSuccess) return hipErrorInvalidDevice;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+    // four column blocks (64 output channels) when Cout needs more than two
+    // and the wider tiles still give every CU one, so that X is fetched once
+    // per mode tile for Cout <= 64; two otherwise
+    const int64_t mb_tiles = (int64_t)tg.n_mt * tg.n_bt;
+    const bool wide = Cout > 32 && mb_tiles * ((Cout + 63) / 64) >= cus;
+    tg.o_cols = wide ? 64 : 32;
+    tg.n_ot = (int)((Cout + tg.o_cols - 1) / tg.o_cols);
+    const int64_t n_tiles = mb_tiles * tg.n_ot;
+    if (n_tiles >= INT32_MAX / 2) return hipErrorInvalidValue;
+    tg.n_tiles = (int)n_tiles;
     // one workgroup (8 waves: two per SIMD) per CU, each walking its tiles
     const int64_t g = n_tiles < cus ? n_tiles : cus;
     const Addr ax{lx.sb, lx.sc, lx.st};
@@ -315,8 +332,11 @@ hipError_t launch_mix_mfma(const float2* xh, const SpecLayout& lx, const float2*
     const bool vec = lx.sc == 8 && ly.sc == 8 && lx.st % 2 == 0 && ly.st % 2 == 0 && lx.sb % 2 == 0 &&
                      ly.sb % 2 == 0 && M % 8 == 0 && aligned16(xh) && aligned16(yh);
     const int nch = (int)mix_chunks(Cin);
-    if (vec) return launch_mix_variant<true>(grid, s, xh, ax, w, yh, ay, (int)B, (int)Cin, (int)Cout, (int)M, tg, nch);
-    return launch_mix_variant<false>(grid, s, xh, ax, w, yh, ay, (int)B, (int)Cin, (int)Cout, (int)M, tg, nch);
+    const int iB = (int)B, iCin = (int)Cin, iCout = (int)Cout, iM = (int)M;
+    if (vec && wide) return launch_mix_variant<true, 4>(grid, s, xh, ax, w, yh, ay, iB, iCin, iCout, iM, tg, nch);
+    if (vec) return launch_mix_variant<true, 2>(grid, s, xh, ax, w, yh, ay, iB, iCin, iCout, iM, tg, nch);
+    if (wide) return launch_mix_variant<false, 4>(grid, s, xh, ax, w, yh, ay, iB, iCin, iCout, iM, tg, nch);
+    return launch_mix_variant<false, 2>(grid, s, xh, ax, w, yh, ay, iB, iCin, iCout, iM, tg, nch);
 }
 
 }  // namespace fno

@@ -9,19 +9,21 @@
 // With n = n1 + 64 n2 and W = exp(-2 pi i / N):
 //   X[k] = sum_n1 W^{n1 k} Y_n1[k mod Q],   Y_n1 = DFT_Q of lane n1's samples.
 // Forward: each lane runs its Q-point real DFT in registers (packed as a
-// Q/2-point complex one), twiddles the kept bins by W^{n1 k} and the 64 lanes'
-// contributions are summed through a per-wave LDS stage, 16 bins at a time.
+// Q/2-point complex one), twiddles the kept bins by W^{n1 k} = A[k mod 8]
+// B[k div 8] (A[j] = W^{n1 j}, B[j] = W^{8 n1 j}: one product of two
+// correctly rounded table values) and the 64 lanes' contributions are summed
+// through a per-wave LDS stage, 16 bins at a time.
 // Inverse: lane n1 forms V[r] = sum_{k = r mod Q} c_k X[k] W^{-n1 k}
 // (c_0 = 1 with the DC imaginary part dropped, c_k = 2 otherwise: the
 // Hermitian extension of the half spectrum); the real part of its inverse
 // DFT over r is exactly the lane's Q output samples, computed as the C2R of
 // the Hermitian part H[r] = (V[r] + conj V[-r]) / 2, packed as a Q/2-point
-// complex inverse DFT in registers.
-//
-// The twiddle W^{n1 k} is A[k & 7] * B[k >> 3] with A[j] = W^{n1 j} and
-// B[j] = W^{8 n1 j} read from the host-built table, so every twiddle is one
-// product of two correctly rounded values.  The waves of a workgroup share no
-// data; the grid is persistent, each wave walking rows.
+// complex inverse DFT in registers.  Its twiddles split as
+// W^{n1 (r + Q j)} = W^{n1 r} W_64^{n1 j}: the residue factors W^{n1 r} sit
+// in registers for Q <= 32 and in a per-workgroup LDS table for Q = 64, so
+// the factor W^{-n1 r} is applied once per residue after the sum over j.
+// The waves of a workgroup share no data; the grid is persistent, each wave
+// walking rows.
 #include "fno_device.hpp"
 #include "fno_internal.hpp"
 
@@ -30,38 +32,95 @@ namespace {
 
 constexpr int kPrunedThreads = 256;     // 4 independent waves
 constexpr int kPrunedWaves = kPrunedThreads / 64;
-constexpr int kStageStride = 68;        // reduction stage row stride (complex)
+constexpr int kStageStride = 68;        // forward reduction stage row stride (complex)
 
-// index of (bin kk, lane n1) in a wave's reduction stage
+// index of (bin kk, lane n1) in a wave's forward reduction stage
 __device__ __forceinline__ int stage_at(int kk, int n1) { return kk * kStageStride + n1 + (n1 >> 4); }
 
-__device__ __forceinline__ float dpp_xor1(float v) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
-}
-__device__ __forceinline__ float dpp_xor2(float v) {
+// Lane exchanges of the forward reduction's last two steps.
+__device__ __forceinline__ float xchg2(float v) {           // DPP quad_perm [2,3,0,1]
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float xchg1(float v) {           // DPP quad_perm [1,0,3,2]
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
 }
 
 __device__ __forceinline__ float2 conj2(float2 a) { return make_float2(a.x, -a.y); }
 
-// Makes the twiddle factors opaque once per row, so that their 64 products
-// are formed per row instead of being hoisted out of the row loop into 128
-// live registers.
-__device__ __forceinline__ void opaque_twiddles(float2 (&A)[8], float2 (&B)[8]) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) asm volatile("" : "+v"(A[j].x), "+v"(A[j].y), "+v"(B[j].x), "+v"(B[j].y));
-}
+// Inverse twiddles of a row of N = 64 Q points, lane n1:
+// W^{n1 k} = res(k mod Q) * W_64^{n1 (k div Q)} (W = exp(-2 pi i / N)).
+template <int Q>
+struct LaneTwiddles {
+    static constexpr int NR = Q <= 32 ? Q : 1;      // residue factors kept in registers
+    static constexpr int NJ = 64 / Q > 1 ? 64 / Q : 1;
+    float2 tr[NR];                                  // W^{n1 r}, r < Q (Q <= 32)
+    float2 pj[NJ];                                  // W_64^{n1 j}, j < 64 / Q
+    const float2* tl;                               // Q = 64: LDS table [r][64 lanes]
 
-// Bin K (K <= Q/2) of the DFT of a real length-Q sequence s from its packed
-// transform Z = DFT_{Q/2}(s[2m] + i s[2m+1]):
-//   Y[K] = (Z[K] + conj Z[-K]) / 2 + W_Q^K (Z[K] - conj Z[-K]) / 2i.
+    __device__ __forceinline__ void init(const float2* __restrict__ tw, int lane, float2* lds_table) {
+        constexpr int N = 64 * Q;
+        if constexpr (Q <= 32) {
+#pragma unroll
+            for (int r = 0; r < Q; ++r) tr[r] = tw[(lane * r * (kNMax / N)) & (kNMax - 1)];
+        } else {
+            // 64 x 64 residue factors, filled by the whole workgroup
+            for (int e = threadIdx.x; e < 64 * 64; e += blockDim.x) {
+                const int r = e >> 6, l = e & 63;
+                lds_table[e] = tw[(l * r * (kNMax / N)) & (kNMax - 1)];
+            }
+            tl = lds_table;
+        }
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) pj[j] = tw[(lane * j * (kNMax / 64)) & (kNMax - 1)];
+        // keep them opaque: formed once here, never re-derived in the row loop
+#pragma unroll
+        for (int r = 0; r < NR; ++r) asm volatile("" : "+v"(tr[r].x), "+v"(tr[r].y));
+    }
+    template <int R>
+    __device__ __forceinline__ float2 res(int lane) const {
+        if constexpr (Q <= 32) return tr[R];
+        else return tl[R * 64 + lane];
+    }
+};
+
+// W^{n1 K} = A[K mod 8] * B[K div 8], A[j] = W^{n1 j}, B[j] = W^{8 n1 j}
+template <int Q>
+struct ABTwiddles {
+    float2 A[8], B[8];
+    __device__ __forceinline__ void init(const float2* __restrict__ tw, int lane) {
+        constexpr int N = 64 * Q;
+        static_assert(Q <= 64, "A.B covers bins below 64");
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            A[j] = tw[(lane * j * (kNMax / N)) & (kNMax - 1)];
+            B[j] = tw[(lane * 8 * j * (kNMax / N)) & (kNMax - 1)];
+        }
+    }
+    // Hides the factors from loop-invariant code motion: called once per row,
+    // it keeps their 64 products per row instead of hoisted into live registers.
+    __device__ __forceinline__ void opaque() {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) asm volatile("" : "+v"(A[j].x), "+v"(A[j].y), "+v"(B[j].x), "+v"(B[j].y));
+    }
+    template <int K>
+    __device__ __forceinline__ float2 full() const {
+        if constexpr (K < 8) return A[K];
+        else if constexpr (K % 8 == 0) return B[K / 8];
+        else return cmul(A[K % 8], B[K / 8]);
+    }
+};
+
+// Twice bin K (K <= Q/2) of the DFT of a real length-Q sequence s, from its
+// packed transform Z = DFT_{Q/2}(s[2m] + i s[2m+1]):
+//   2 Y[K] = (Z[K] + conj Z[-K]) - i W_Q^K (Z[K] - conj Z[-K]).
+// The factor 2 is taken out with the output scale.
 template <int Q, int K>
-__device__ __forceinline__ float2 real_bin(const float2 (&z)[Q / 2]) {
+__device__ __forceinline__ float2 real_bin2(const float2 (&z)[Q / 2]) {
     constexpr int NZ = Q / 2;
     const float2 zk = z[K % NZ];
     const float2 zm = z[(NZ - K % NZ) % NZ];
-    const float2 e = make_float2(0.5f * (zk.x + zm.x), 0.5f * (zk.y - zm.y));
-    const float2 o = make_float2(0.5f * (zk.y + zm.y), -0.5f * (zk.x - zm.x));
+    const float2 e = make_float2(zk.x + zm.x, zk.y - zm.y);
+    const float2 o = make_float2(zk.y + zm.y, zm.x - zk.x);
     return cadd(e, wmul<-1, Q, K>(o));
 }
 
@@ -79,36 +138,31 @@ __device__ __forceinline__ float2 packed_bin(const float2 (&H)[Q / 2 + 1]) {
 }
 
 template <int Q>
-__global__ __launch_bounds__(kPrunedThreads) __attribute__((amdgpu_waves_per_eu(2))) void k_rows_fwd_pruned(const float* __restrict__ x,
-                                                                    float2* __restrict__ y, int64_t nrows, int my,
-                                                                    int y_ld, float scale,
-                                                                    const float2* __restrict__ tw) {
+__global__ __launch_bounds__(kPrunedThreads) __attribute__((amdgpu_waves_per_eu(2))) void k_rows_fwd_pruned(
+    const float* __restrict__ x, float2* __restrict__ y, int64_t nrows, int my, int y_ld, float scale,
+    const float2* __restrict__ tw) {
     constexpr int N = 64 * Q;
     constexpr int NZ = Q / 2;
     __shared__ float2 stage_all[kPrunedWaves][16 * kStageStride];
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     float2* const stage = stage_all[wave];
-
-    float2 A[8], Bt[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        A[j] = tw[(lane * j * (kNMax / N)) & (kNMax - 1)];
-        Bt[j] = tw[(lane * 8 * j * (kNMax / N)) & (kNMax - 1)];
-    }
+    ABTwiddles<Q> tws;
+    tws.init(tw, lane);
     const int kk_r = lane >> 2;              // reduction role: bin kk_r of a chunk,
     const int q_r = lane & 3;                // summing lanes 16 q_r .. 16 q_r + 15
+    const float half_scale = 0.5f * scale;   // the bins below are doubled
 
     const int64_t nwaves = (int64_t)gridDim.x * kPrunedWaves;
     for (int64_t row = (int64_t)blockIdx.x * kPrunedWaves + wave; row < nrows; row += nwaves) {
-        opaque_twiddles(A, Bt);
+        tws.opaque();
         const float* src = x + row * N + lane;
         float2 z[NZ];
 #pragma unroll
         for (int m = 0; m < NZ; ++m) z[m] = make_float2(src[64 * (2 * m)], src[64 * (2 * m + 1)]);
         dft<NZ, -1>(z);
-        float2 Y[NZ + 1];
-        static_for<0, NZ + 1>([&](auto k) { Y[k] = real_bin<Q, k>(z); });
+        float2 Y2[NZ + 1];
+        static_for<0, NZ + 1>([&](auto k) { Y2[k] = real_bin2<Q, k>(z); });
 
         float2* const dst = y + row * (int64_t)y_ld;
         static_for<0, 4>([&](auto ch) {
@@ -116,19 +170,19 @@ __global__ __launch_bounds__(kPrunedThreads) __attribute__((amdgpu_waves_per_eu(
                 static_for<0, 16>([&](auto kk) {
                     constexpr int k = 16 * ch + kk;
                     constexpr int r = k % Q;
-                    const float2 yk = (r <= NZ) ? Y[r <= NZ ? r : 0] : conj2(Y[r <= NZ ? 0 : Q - r]);
-                    stage[stage_at(kk, lane)] = cmul(cmul(A[k & 7], Bt[k >> 3]), yk);
+                    const float2 yk = (r <= NZ) ? Y2[r <= NZ ? r : 0] : conj2(Y2[r <= NZ ? 0 : Q - r]);
+                    stage[stage_at(kk, lane)] = cmul(tws.template full<k>(), yk);
                 });
                 wave_lds_sync();
                 float2 acc = make_float2(0.0f, 0.0f);
 #pragma unroll
                 for (int t = 0; t < 16; ++t) acc = cadd(acc, stage[stage_at(kk_r, 16 * q_r + t)]);
-                acc.x += dpp_xor1(acc.x);
-                acc.y += dpp_xor1(acc.y);
-                acc.x += dpp_xor2(acc.x);
-                acc.y += dpp_xor2(acc.y);
+                acc.x += xchg1(acc.x);
+                acc.y += xchg1(acc.y);
+                acc.x += xchg2(acc.x);
+                acc.y += xchg2(acc.y);
                 const int k = 16 * ch + kk_r;
-                if (q_r == 0 && k < my) dst[k] = cscale(acc, scale);
+                if (q_r == 0 && k < my) dst[k] = cscale(acc, half_scale);
                 wave_lds_sync();
             }
         });
@@ -143,20 +197,16 @@ __global__ __launch_bounds__(kPrunedThreads) __attribute__((amdgpu_waves_per_eu(
     constexpr int N = 64 * Q;
     constexpr int NZ = Q / 2;
     __shared__ float2 xrow_all[kPrunedWaves][64];
+    __shared__ float2 table[Q == 64 ? 64 * 64 : 1];
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     float2* const xrow = xrow_all[wave];
-
-    float2 A[8], Bt[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        A[j] = tw[(lane * j * (kNMax / N)) & (kNMax - 1)];
-        Bt[j] = tw[(lane * 8 * j * (kNMax / N)) & (kNMax - 1)];
-    }
+    LaneTwiddles<Q> tws;
+    tws.init(tw, lane, table);
+    if constexpr (Q == 64) __syncthreads();
 
     const int64_t nwaves = (int64_t)gridDim.x * kPrunedWaves;
     for (int64_t row = (int64_t)blockIdx.x * kPrunedWaves + wave; row < nrows; row += nwaves) {
-        opaque_twiddles(A, Bt);
         // the row's kept bins, zero past my, DC imaginary part dropped
         {
             float2 v = lane < my ? y[row * (int64_t)y_ld + lane] : make_float2(0.0f, 0.0f);
@@ -164,20 +214,22 @@ __global__ __launch_bounds__(kPrunedThreads) __attribute__((amdgpu_waves_per_eu(
             xrow[lane] = v;
         }
         wave_lds_sync();
-        // V[r] = sum_{k = r mod Q} c_k X[k] conj(W^{n1 k}), c_0 = 1, c_k = 2
+        // V[r] = conj(W^{n1 r}) sum_j c_k X[k] conj(W_64^{n1 j}), k = r + Q j,
+        // c_0 = 1, c_k = 2
+        constexpr int NT = Q < 64 ? Q : 64;
         float2 V[Q];
 #pragma unroll
         for (int r = 0; r < Q; ++r) V[r] = make_float2(0.0f, 0.0f);
-        static_for<0, 4>([&](auto ch) {
-            if (16 * ch < my) {
-                static_for<0, 16>([&](auto kk) {
-                    constexpr int k = 16 * ch + kk;
-                    const float2 w = cmul(A[k & 7], Bt[k >> 3]);
-                    const float2 u = cmul(xrow[k], make_float2(w.x, -w.y));
-                    constexpr float c = k == 0 ? 1.0f : 2.0f;
-                    V[k % Q] = make_float2(fmaf(c, u.x, V[k % Q].x), fmaf(c, u.y, V[k % Q].y));
-                });
-            }
+        static_for<0, NT>([&](auto r) {
+            float2 acc = make_float2(0.0f, 0.0f);
+            static_for<0, 64 / NT>([&](auto j) {
+                constexpr int k = r + NT * j;
+                constexpr float c = k == 0 ? 1.0f : 2.0f;
+                float2 u = xrow[k];
+                if constexpr (j > 0) u = cmul(u, conj2(tws.pj[j]));
+                acc = make_float2(fmaf(c, u.x, acc.x), fmaf(c, u.y, acc.y));
+            });
+            V[r] = cmul(acc, conj2(tws.template res<r>(lane)));
         });
         wave_lds_sync();                        // the row buffer is read before the next row overwrites it
         // Hermitian part H[r] = (V[r] + conj V[-r]) / 2, r <= Q/2, scaled
