@@ -166,7 +166,7 @@ __global__ __launch_bounds__(kThreads) void k_rows_inv(const float2* __restrict_
     }
 }
 
-constexpr int kMixBT = 8;   // batch rows per thread
+constexpr int kMixIC = 8;   // input channels per batch of loads
 
 struct MixAddr {
     int64_t sb, sc, st;
@@ -175,6 +175,12 @@ struct MixAddr {
     }
 };
 
+// Thread (m, o) accumulates Y_m[b][o] for BT batch rows.  Input channels go in
+// batches of kMixIC: all W and X loads of a batch are issued (clamped
+// indices, no branches) before any of its products, so each thread keeps
+// about 8 (BT + 1) loads in flight; W, the largest operand when the channel
+// counts are small, is read exactly once.
+template <int BT>
 __global__ __launch_bounds__(kThreads) void k_mix_valu(const float2* __restrict__ xh, MixAddr ax,
                                                       const float2* __restrict__ w, float2* __restrict__ yh,
                                                       MixAddr ay, int64_t B, int64_t Cin, int64_t Cout, int64_t M,
@@ -186,20 +192,34 @@ __global__ __launch_bounds__(kThreads) void k_mix_valu(const float2* __restrict_
     const int64_t bz = bid / (n_ot * n_mt);
     const int64_t o = bx * (1 << ot_log2) + (tid & ((1 << ot_log2) - 1));
     const int64_t m = by * (kThreads >> ot_log2) + (tid >> ot_log2);
-    const int64_t b0 = bz * kMixBT;
+    const int64_t b0 = bz * BT;
     if (o >= Cout || m >= M) return;
-    float2 acc[kMixBT];
+    float2 acc[BT];
 #pragma unroll
-    for (int t = 0; t < kMixBT; ++t) acc[t] = make_float2(0.0f, 0.0f);
-    for (int64_t i = 0; i < Cin; ++i) {
-        const float2 wv = w[(m * Cin + i) * Cout + o];
+    for (int t = 0; t < BT; ++t) acc[t] = make_float2(0.0f, 0.0f);
+    for (int64_t i0 = 0; i0 < Cin; i0 += kMixIC) {
+        float2 wv[kMixIC], xv[BT][kMixIC];
 #pragma unroll
-        for (int t = 0; t < kMixBT; ++t) {
-            if (b0 + t < B) acc[t] = cfma(acc[t], xh[ax.at(b0 + t, i, m)], wv);
+        for (int j = 0; j < kMixIC; ++j) {
+            const int64_t i = i0 + j < Cin ? i0 + j : Cin - 1;
+            wv[j] = w[(m * Cin + i) * Cout + o];
+#pragma unroll
+            for (int t = 0; t < BT; ++t) {
+                const int64_t b = b0 + t < B ? b0 + t : B - 1;
+                xv[t][j] = xh[ax.at(b, i, m)];
+            }
         }
+        // channels past Cin contribute nothing
+#pragma unroll
+        for (int j = 0; j < kMixIC; ++j)
+            if (i0 + j >= Cin) wv[j] = make_float2(0.0f, 0.0f);
+#pragma unroll
+        for (int t = 0; t < BT; ++t)
+#pragma unroll
+            for (int j = 0; j < kMixIC; ++j) acc[t] = cfma(acc[t], xv[t][j], wv[j]);
     }
 #pragma unroll
-    for (int t = 0; t < kMixBT; ++t) {
+    for (int t = 0; t < BT; ++t) {
         if (b0 + t < B) yh[ay.at(b0 + t, o, m)] = acc[t];
     }
 }
@@ -284,12 +304,25 @@ hipError_t launch_mix_valu(const float2* xh, const SpecLayout& lx, const float2*
     const int64_t mt = kThreads >> ot_log2;
     const int64_t n_ot = (Cout + ot - 1) / ot;
     const int64_t n_mt = (M + mt - 1) / mt;
-    const int64_t n_bt = (B + kMixBT - 1) / kMixBT;
-    const dim3 grid((unsigned)(n_ot * n_mt * n_bt));
+    // batch rows per thread: the fewest of 2, 4, 8 that cover B (8 past it)
+    const int bt = B <= 2 ? 2 : (B <= 4 ? 4 : 8);
+    const int64_t n_bt = (B + bt - 1) / bt;
+    const int64_t nb = n_ot * n_mt * n_bt;
+    if (nb >= INT32_MAX) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)nb);
     const MixAddr ax{lx.sb, lx.sc, lx.st};
     const MixAddr ay{ly.sb, ly.sc, ly.st};
-    return launch_kernel(k_mix_valu, grid, dim3(kThreads), 0, s, xh, ax, w, yh, ay, B, Cin, Cout, M, ot_log2, n_ot,
-                         n_mt);
+    switch (bt) {
+        case 2:
+            return launch_kernel(k_mix_valu<2>, grid, dim3(kThreads), 0, s, xh, ax, w, yh, ay, B, Cin, Cout, M, ot_log2,
+                                 n_ot, n_mt);
+        case 4:
+            return launch_kernel(k_mix_valu<4>, grid, dim3(kThreads), 0, s, xh, ax, w, yh, ay, B, Cin, Cout, M, ot_log2,
+                                 n_ot, n_mt);
+        default:
+            return launch_kernel(k_mix_valu<8>, grid, dim3(kThreads), 0, s, xh, ax, w, yh, ay, B, Cin, Cout, M, ot_log2,
+                                 n_ot, n_mt);
+    }
 }
 
 }  // namespace fno

@@ -47,7 +47,7 @@ __device__ __forceinline__ float xchg1(float v) {           // DPP quad_perm [1,
 
 __device__ __forceinline__ float2 conj2(float2 a) { return make_float2(a.x, -a.y); }
 
-// Inverse twiddles of a row of N = 64 Q points, lane n1:
+// Residue-factored twiddles of a row of N = 64 Q points, lane n1:
 // W^{n1 k} = res(k mod Q) * W_64^{n1 (k div Q)} (W = exp(-2 pi i / N)).
 template <int Q>
 struct LaneTwiddles {
@@ -60,6 +60,7 @@ struct LaneTwiddles {
     __device__ __forceinline__ void init(const float2* __restrict__ tw, int lane, float2* lds_table) {
         constexpr int N = 64 * Q;
         if constexpr (Q <= 32) {
+            (void)lds_table;
 #pragma unroll
             for (int r = 0; r < Q; ++r) tr[r] = tw[(lane * r * (kNMax / N)) & (kNMax - 1)];
         } else {
@@ -147,15 +148,25 @@ __global__ __launch_bounds__(kPrunedThreads) __attribute__((amdgpu_waves_per_eu(
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     float2* const stage = stage_all[wave];
-    ABTwiddles<Q> tws;
-    tws.init(tw, lane);
-    const int kk_r = lane >> 2;              // reduction role: bin kk_r of a chunk,
+    // Q <= 32: residue factors W^{n1 r} and W_64^{n1 j} (bin k = r + Q j);
+    // Q = 64: every bin its own residue, twiddles as A.B products
+    using TW = std::conditional_t<(Q <= 32), LaneTwiddles<Q>, ABTwiddles<Q>>;
+    TW tws;
+    if constexpr (Q <= 32) tws.init(tw, lane, nullptr);
+    else tws.init(tw, lane);
+    const int kk_r = lane >> 2;              // reduction role: stage row kk_r of a chunk,
     const int q_r = lane & 3;                // summing lanes 16 q_r .. 16 q_r + 15
     const float half_scale = 0.5f * scale;   // the bins below are doubled
+    // Q <= 32: a chunk holds RPC residues r and, for each, its NJ bins
+    // r + Q j, so that t_r = W^{n1 r} Y[r] is formed once and reused NJ times;
+    // stage row jj RPC + rr holds bin RPC ch + rr + Q jj.
+    constexpr int NJ = Q <= 32 ? 64 / Q : 1;
+    constexpr int RPC = 16 / NJ;
+    const int k_r = Q <= 32 ? (kk_r % RPC) + Q * (kk_r / RPC) : kk_r;   // bin of stage row kk_r, chunk 0
 
     const int64_t nwaves = (int64_t)gridDim.x * kPrunedWaves;
     for (int64_t row = (int64_t)blockIdx.x * kPrunedWaves + wave; row < nrows; row += nwaves) {
-        tws.opaque();
+        if constexpr (Q == 64) tws.opaque();
         const float* src = x + row * N + lane;
         float2 z[NZ];
 #pragma unroll
@@ -163,16 +174,30 @@ __global__ __launch_bounds__(kPrunedThreads) __attribute__((amdgpu_waves_per_eu(
         dft<NZ, -1>(z);
         float2 Y2[NZ + 1];
         static_for<0, NZ + 1>([&](auto k) { Y2[k] = real_bin2<Q, k>(z); });
+        auto ybin = [&](auto r) __attribute__((always_inline)) {    // 2 Y[r], r < Q
+            if constexpr (r <= NZ) return Y2[r <= NZ ? r : 0];
+            else return conj2(Y2[r <= NZ ? 0 : Q - r]);
+        };
 
         float2* const dst = y + row * (int64_t)y_ld;
         static_for<0, 4>([&](auto ch) {
-            if (16 * ch < my) {                 // uniform: whole chunks of 16 bins
-                static_for<0, 16>([&](auto kk) {
-                    constexpr int k = 16 * ch + kk;
-                    constexpr int r = k % Q;
-                    const float2 yk = (r <= NZ) ? Y2[r <= NZ ? r : 0] : conj2(Y2[r <= NZ ? 0 : Q - r]);
-                    stage[stage_at(kk, lane)] = cmul(tws.template full<k>(), yk);
-                });
+            constexpr int k0 = Q <= 32 ? RPC * ch : 16 * ch;      // lowest bin of the chunk
+            if (k0 < my) {                      // uniform: chunks with a kept bin
+                if constexpr (Q <= 32) {
+                    static_for<0, RPC>([&](auto rr) {
+                        constexpr int r = RPC * ch + rr;
+                        const float2 t = cmul(tws.tr[r], ybin(std::integral_constant<int, r>{}));
+                        stage[stage_at(rr, lane)] = t;
+                        static_for<1, NJ>([&](auto jj) {
+                            if (r + Q * jj < my) stage[stage_at(jj * RPC + rr, lane)] = cmul(tws.pj[jj], t);
+                        });
+                    });
+                } else {
+                    static_for<0, 16>([&](auto kk) {
+                        constexpr int k = 16 * ch + kk;
+                        stage[stage_at(kk, lane)] = cmul(tws.template full<k>(), ybin(std::integral_constant<int, k>{}));
+                    });
+                }
                 wave_lds_sync();
                 float2 acc = make_float2(0.0f, 0.0f);
 #pragma unroll
@@ -181,7 +206,7 @@ __global__ __launch_bounds__(kPrunedThreads) __attribute__((amdgpu_waves_per_eu(
                 acc.y += xchg1(acc.y);
                 acc.x += xchg2(acc.x);
                 acc.y += xchg2(acc.y);
-                const int k = 16 * ch + kk_r;
+                const int k = k0 + k_r;
                 if (q_r == 0 && k < my) dst[k] = cscale(acc, half_scale);
                 wave_lds_sync();
             }
