@@ -8,12 +8,13 @@
 //   Yr = P1 - P2,  Yi = P3 - P1 - P2,
 // all accumulated in fp32.
 //
-// Tile = 8 consecutive modes x 32 batch rows x 16 NCB output channels
-// (NCB = 4 when Cout allows it, so that each X element is fetched once; else
-// 2), one workgroup of 8 waves; wave w owns mode m0 + w, a 32 x 16 NCB result
-// = 2 x NCB blocks of 16 x 16 with three accumulators each.  Input channels
+// Tile = 8 consecutive modes x 16 RB batch rows x 16 NCB output channels
+// (NCB = 4 when Cout allows it, so that each X element is fetched once, else
+// 2; RB = 2 unless B is small or the tiles would be too few for the CUs),
+// one workgroup of 8 waves; wave w owns mode m0 + w, a 16 RB x 16 NCB result
+// = RB x NCB blocks of 16 x 16 with three accumulators each.  Input channels
 // are consumed in chunks of 8 (two MFMA k-steps of 4):
-//  * the X chunk of all 8 modes ([32 b][8 i][8 m], one 64-byte run per
+//  * the X chunk of all 8 modes ([16 RB b][8 i][8 m], one 64-byte run per
 //    (b, i)) is staged in LDS as [i][m][b] and shared by the 8 waves;
 //  * each wave streams its own W_m rows from global memory straight into the
 //    B operand, as float4 pairs (o, o + 1): column block 2 h + p holds
@@ -35,7 +36,6 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 constexpr int kMixWaves = 8;           // = modes per tile
 constexpr int kMixThreads = 64 * kMixWaves;
 constexpr int kMixKC = 8;              // input channels per chunk
-constexpr int kMixBRows = 32;          // batch rows per tile (2 MFMA row blocks)
 
 struct Addr {
     int64_t sb, sc, st;
@@ -45,7 +45,7 @@ struct Addr {
 };
 
 struct TileGrid {
-    int n_mt, n_bt, n_ot, n_tiles, o_cols;
+    int n_mt, n_bt, n_ot, n_tiles;
 };
 
 struct Tile {
@@ -56,23 +56,27 @@ __device__ __forceinline__ floatx4 mfma16(float a, float b, floatx4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-// tile t -> (mode tile, batch tile, output tile), output tile fastest
+// tile t -> (mode tile, batch tile, output tile), output tile fastest; KB
+// batch rows and KO output channels per tile
+template <int KB, int KO>
 __device__ __forceinline__ Tile tile_of(const TileGrid& tg, int t) {
     const int ot = t % tg.n_ot;
     const int r = t / tg.n_ot;
-    return Tile{(r % tg.n_mt) * 8, (r / tg.n_mt) * kMixBRows, ot * tg.o_cols};
+    return Tile{(r % tg.n_mt) * 8, (r / tg.n_mt) * KB, ot * KO};
 }
 
 // VEC: every (b, c) run of 8 modes is 16-byte aligned and complete (tiled
 // layout), so X is read and Y written as float4; otherwise element-wise.
 // NCH: chunks of input channels per tile (even; chunks past Cin are zero).
-// NCB: 16-column MFMA blocks per tile (2 or 4; Cout is a multiple of NCB).
-template <int NCH, bool VEC, int NCB>
+// NCB: 16-column MFMA blocks per tile (2 or 4); RB: 16-row blocks (1 or 2).
+template <int NCH, bool VEC, int NCB, int RB>
 __global__ __launch_bounds__(kMixThreads) void k_mix_mfma(const float2* __restrict__ xh, Addr ax,
                                                           const float2* __restrict__ w, float2* __restrict__ yh,
                                                           Addr ay, int B, int Cin, int Cout, int M, TileGrid tg) {
     static_assert(NCH % 2 == 0, "chunks alternate between two register sets");
     static_assert(NCB == 2 || NCB == 4, "W runs are one or two float4 per lane");
+    static_assert(RB == 1 || RB == 2, "one or two 16-row blocks");
+    constexpr int kB = 16 * RB;                            // batch rows per tile
     constexpr int kO = 16 * NCB;                           // output channels per tile
     // X chunk in LDS: (i, m, b) at i * kAI + m * kAM + (b ^ 2 (i >> 1)).  The
     // strides and the swizzle make both the staging writes (lanes over
@@ -90,8 +94,10 @@ __global__ __launch_bounds__(kMixThreads) void k_mix_mfma(const float2* __restri
     const int wave = tid >> 6;
     const int l16 = lane & 15;               // MFMA row (A) / column (B, C)
     const int lk = lane >> 4;                // MFMA k index within a step (0..3)
-    // staging role: thread -> (b, i, half of the 8 modes) of a chunk
+    // staging role: thread -> (b, i, half of the 8 modes) of a chunk (threads
+    // with sbl >= kB stage nothing)
     const int sbl = tid >> 4;
+    const bool stager = RB == 2 || sbl < kB;
     const int sil = (tid >> 1) & 7;
     const int shalf = tid & 1;
 
@@ -101,7 +107,8 @@ __global__ __launch_bounds__(kMixThreads) void k_mix_mfma(const float2* __restri
     auto load_a = [&](const Tile& tl, int chunk, float2 (&av)[4]) __attribute__((always_inline)) {
         const int i = chunk * kMixKC + sil;
         const int ic = i < Cin ? i : Cin - 1;
-        const int b = tl.b0 + sbl < B ? tl.b0 + sbl : B - 1;
+        const int bl = RB == 2 ? sbl : sbl % kB;   // non-stagers repeat a stager's row (same lines)
+        const int b = tl.b0 + bl < B ? tl.b0 + bl : B - 1;
         if constexpr (VEC) {
             const float4* src = reinterpret_cast<const float4*>(xh + ax.at(b, ic, tl.m0 + shalf * 4));
             const float4 v0 = src[0], v1 = src[1];
@@ -118,6 +125,7 @@ __global__ __launch_bounds__(kMixThreads) void k_mix_mfma(const float2* __restri
         }
     };
     auto store_a = [&](int chunk, const float2 (&av)[4], float2* buf) __attribute__((always_inline)) {
+        if (!stager) return;
         const bool iok = chunk * kMixKC + sil < Cin;
 #pragma unroll
         for (int q = 0; q < 4; ++q)
@@ -143,18 +151,18 @@ __global__ __launch_bounds__(kMixThreads) void k_mix_mfma(const float2* __restri
         }
     };
 
-    floatx4 p1[2][NCB], p2[2][NCB], p3[2][NCB];
+    floatx4 p1[RB][NCB], p2[RB][NCB], p3[RB][NCB];
     auto mfma_chunk = [&](const float2* buf, const float2 (&wv)[2 * NCB]) __attribute__((always_inline)) {
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
-            float2 a[2];
+            float2 a[RB];
 #pragma unroll
-            for (int rb = 0; rb < 2; ++rb) {
+            for (int rb = 0; rb < RB; ++rb) {
                 const int i = 4 * s + lk;
                 a[rb] = buf[i * kAI + wave * kAM + ((16 * rb + l16) ^ (2 * (i >> 1)))];
             }
 #pragma unroll
-            for (int rb = 0; rb < 2; ++rb) {
+            for (int rb = 0; rb < RB; ++rb) {
                 const float as = a[rb].x + a[rb].y;
 #pragma unroll
                 for (int cb = 0; cb < NCB; ++cb) {
@@ -173,7 +181,7 @@ __global__ __launch_bounds__(kMixThreads) void k_mix_mfma(const float2* __restri
     // rr / 2 and the lanes with lk / 2 == rr % 2.
     auto epilogue = [&](const Tile& tl) __attribute__((always_inline)) {
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
+        for (int rr = 0; rr < 2 * RB; ++rr) {
             const int rb = rr >> 1;
             if ((lk >> 1) == (rr & 1)) {
 #pragma unroll
@@ -235,8 +243,8 @@ __global__ __launch_bounds__(kMixThreads) void k_mix_mfma(const float2* __restri
     const int t_begin = (int)((int64_t)tg.n_tiles * blockIdx.x / G);
     const int t_end = (int)((int64_t)tg.n_tiles * (blockIdx.x + 1) / G);
     int t = t_begin;
-    Tile cur = tile_of(tg, t);
-    Tile nxt = tile_of(tg, t + 1 < t_end ? t + 1 : t);
+    Tile cur = tile_of<kB, kO>(tg, t);
+    Tile nxt = tile_of<kB, kO>(tg, t + 1 < t_end ? t + 1 : t);
     float2 aA[4], aB[4];
     float2 wA[2 * NCB], wB[2 * NCB];
     load_a(cur, 0, aA);
@@ -246,7 +254,7 @@ __global__ __launch_bounds__(kMixThreads) void k_mix_mfma(const float2* __restri
     for (; t < t_end; ++t) {
         const bool more = t + 1 < t_end;
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
+        for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
             for (int cb = 0; cb < NCB; ++cb) {
                 p1[rb][cb] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -273,23 +281,29 @@ __global__ __launch_bounds__(kMixThreads) void k_mix_mfma(const float2* __restri
         }
         epilogue(cur);
         cur = nxt;
-        nxt = tile_of(tg, t + 2 < t_end ? t + 2 : (more ? t + 1 : t));
+        nxt = tile_of<kB, kO>(tg, t + 2 < t_end ? t + 2 : (more ? t + 1 : t));
     }
 }
 
-template <bool VEC, int NCB>
+template <bool VEC, int NCB, int RB>
 hipError_t launch_mix_variant(dim3 grid, hipStream_t s, const float2* xh, Addr ax, const float2* w, float2* yh, Addr ay,
                         int B, int Cin, int Cout, int M, TileGrid tg, int nch) {
-    switch (nch) {
 #define CASE(N)                                                                                                   \
     case N:                                                                                                       \
-        return launch_kernel((k_mix_mfma<N, VEC, NCB>), grid, dim3(kMixThreads), 0, s, xh, ax, w, yh, ay, B, Cin, \
+        return launch_kernel((k_mix_mfma<N, VEC, NCB, RB>), grid, dim3(kMixThreads), 0, s, xh, ax, w, yh, ay, B, Cin, \
                            Cout, M, tg);
-        CASE(2) CASE(4) CASE(6) CASE(8) CASE(10) CASE(12) CASE(14) CASE(16)
-#undef CASE
-        default:
-            return hipErrorInvalidValue;
+    switch (nch) {
+        CASE(2) CASE(4) CASE(6) CASE(8)
+        default: break;
     }
+    if constexpr (NCB == 2) {               // the 64-column tiles take at most 8 chunks
+        switch (nch) {
+            CASE(10) CASE(12) CASE(14) CASE(16)
+            default: break;
+        }
+    }
+#undef CASE
+    return hipErrorInvalidValue;
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -306,19 +320,29 @@ bool mix_mfma_supported(int64_t Cin, int64_t Cout, const void* w) {
 hipError_t launch_mix_mfma(const float2* xh, const SpecLayout& lx, const float2* w, float2* yh, const SpecLayout& ly,
                            int64_t B, int64_t Cin, int64_t Cout, int64_t M, hipStream_t s) {
     if (!mix_mfma_supported(Cin, Cout, w)) return hipErrorInvalidValue;
-    TileGrid tg;
-    tg.n_mt = (int)((M + 7) / 8);
-    tg.n_bt = (int)((B + kMixBRows - 1) / kMixBRows);
     int dev = 0, cus = 0;
     if (hipGetDevice(&dev) != hipSuccess) return hipErrorInvalidDevice;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
-    // four column blocks (64 output channels) when Cout needs more than two
-    // and the wider tiles still give every CU one, so that X is fetched once
-    // per mode tile for Cout <= 64; two otherwise
+    // float4 access needs every 8-mode run whole and 16-byte aligned: the
+    // tiled layout (runs of exactly 8 in a 256-byte aligned workspace) has it.
+    const bool vec = lx.sc == 8 && ly.sc == 8 && lx.st % 2 == 0 && ly.st % 2 == 0 && lx.sb % 2 == 0 &&
+                     ly.sb % 2 == 0 && M % 8 == 0 && aligned16(xh) && aligned16(yh);
+    const int nch = (int)mix_chunks(Cin);
+    // Tile shape: 32 batch rows unless B fits 16 or 32-row tiles would leave
+    // CUs without one; 64 output channels when Cout needs more than 32 and
+    // the wider tiles still give every CU one (X is then fetched once per
+    // mode tile for Cout <= 64), else 32.  The 64-column tiles hold 96
+    // accumulators per lane: they are used with float4 access and at most 8
+    // channel chunks only, where they fit the registers of two waves per SIMD.
+    TileGrid tg;
+    tg.n_mt = (int)((M + 7) / 8);
+    const bool short_b = B <= 16 || (int64_t)tg.n_mt * ((B + 31) / 32) * ((Cout + 31) / 32) < cus;
+    const int b_rows = short_b ? 16 : 32;
+    tg.n_bt = (int)((B + b_rows - 1) / b_rows);
     const int64_t mb_tiles = (int64_t)tg.n_mt * tg.n_bt;
-    const bool wide = Cout > 32 && mb_tiles * ((Cout + 63) / 64) >= cus;
-    tg.o_cols = wide ? 64 : 32;
-    tg.n_ot = (int)((Cout + tg.o_cols - 1) / tg.o_cols);
+    const bool wide = Cout > 32 && vec && nch <= 8 && mb_tiles * ((Cout + 63) / 64) >= cus;
+    const int o_cols = wide ? 64 : 32;
+    tg.n_ot = (int)((Cout + o_cols - 1) / o_cols);
     const int64_t n_tiles = mb_tiles * tg.n_ot;
     if (n_tiles >= INT32_MAX / 2) return hipErrorInvalidValue;
     tg.n_tiles = (int)n_tiles;
@@ -327,16 +351,13 @@ hipError_t launch_mix_mfma(const float2* xh, const SpecLayout& lx, const float2*
     const Addr ax{lx.sb, lx.sc, lx.st};
     const Addr ay{ly.sb, ly.sc, ly.st};
     const dim3 grid((unsigned)g);
-    // float4 access needs every 8-mode run whole and 16-byte aligned: the
-    // tiled layout (runs of exactly 8 in a 256-byte aligned workspace) has it.
-    const bool vec = lx.sc == 8 && ly.sc == 8 && lx.st % 2 == 0 && ly.st % 2 == 0 && lx.sb % 2 == 0 &&
-                     ly.sb % 2 == 0 && M % 8 == 0 && aligned16(xh) && aligned16(yh);
-    const int nch = (int)mix_chunks(Cin);
     const int iB = (int)B, iCin = (int)Cin, iCout = (int)Cout, iM = (int)M;
-    if (vec && wide) return launch_mix_variant<true, 4>(grid, s, xh, ax, w, yh, ay, iB, iCin, iCout, iM, tg, nch);
-    if (vec) return launch_mix_variant<true, 2>(grid, s, xh, ax, w, yh, ay, iB, iCin, iCout, iM, tg, nch);
-    if (wide) return launch_mix_variant<false, 4>(grid, s, xh, ax, w, yh, ay, iB, iCin, iCout, iM, tg, nch);
-    return launch_mix_variant<false, 2>(grid, s, xh, ax, w, yh, ay, iB, iCin, iCout, iM, tg, nch);
+    if (wide && !short_b) return launch_mix_variant<true, 4, 2>(grid, s, xh, ax, w, yh, ay, iB, iCin, iCout, iM, tg, nch);
+    if (wide) return launch_mix_variant<true, 4, 1>(grid, s, xh, ax, w, yh, ay, iB, iCin, iCout, iM, tg, nch);
+    if (vec && !short_b) return launch_mix_variant<true, 2, 2>(grid, s, xh, ax, w, yh, ay, iB, iCin, iCout, iM, tg, nch);
+    if (vec) return launch_mix_variant<true, 2, 1>(grid, s, xh, ax, w, yh, ay, iB, iCin, iCout, iM, tg, nch);
+    if (!short_b) return launch_mix_variant<false, 2, 2>(grid, s, xh, ax, w, yh, ay, iB, iCin, iCout, iM, tg, nch);
+    return launch_mix_variant<false, 2, 1>(grid, s, xh, ax, w, yh, ay, iB, iCin, iCout, iM, tg, nch);
 }
 
 }  // namespace fno
