@@ -27,15 +27,24 @@ constexpr int kMaxKept = 128;            // 2 mx
 constexpr int kRedStride = 64 * 9;       // reduction buffer: [kk][n1] rows of 9 (8 columns + pad)
 
 // Twiddle table T[q][n1] = W^{n1 k_q} for the kept modes k_q (q < 2 mx).
+// Every thread issues all of its (at most 16) table reads before it writes
+// any entry, so the gathers overlap instead of queueing one by one.
 template <int H>
 __device__ __forceinline__ void fill_twiddles(float2* T, int mx, const float2* __restrict__ tw, int sign) {
-    const int nk = 2 * mx;
-    for (int e = threadIdx.x; e < nk * 64; e += kColThreads) {
+    constexpr int kPer = kMaxKept * 64 / kColThreads;
+    const int ne = 2 * mx * 64;
+    float2 w[kPer];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+        const int e = threadIdx.x + kColThreads * j;
         const int q = e >> 6, n1 = e & 63;
         const int k = q < mx ? q : H - 2 * mx + q;
-        float2 w = tw[((int64_t)n1 * k * (kNMax / H)) & (kNMax - 1)];
-        if (sign > 0) w.y = -w.y;
-        T[e] = w;
+        if (e < ne) w[j] = tw[((int64_t)n1 * k * (kNMax / H)) & (kNMax - 1)];
+    }
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+        const int e = threadIdx.x + kColThreads * j;
+        if (e < ne) T[e] = make_float2(w[j].x, sign > 0 ? -w[j].y : w[j].y);
     }
 }
 
@@ -49,17 +58,22 @@ __global__ __launch_bounds__(kColThreads) void k_cols_fwd_pruned(const float2* _
     const int tid = threadIdx.x;
     const int c = tid & 7;                           // column within the block
     const int n1 = tid >> 3;                         // row phase
-    const int64_t img = blockIdx.x / nkb;
-    const int ky = (blockIdx.x % nkb) * kColC + c;
+    // column blocks 2j and 2j + 1 (the two halves of every 128-byte line of
+    // the row spectrum) go to workgroups on the same XCD at the same time,
+    // so that L2 fetches each line once
+    const int64_t blk = paired_image(blockIdx.x, (int64_t)gridDim.x);
+    const int64_t img = blk / nkb;
+    const int ky = (int)(blk % nkb) * kColC + c;
     const bool cok = ky < my;
     const int kyc = cok ? ky : my - 1;
 
-    fill_twiddles<H>(T, mx, tw, -1);
-    // column samples n1 + 64 n2 -> Q-point DFT in registers
+    // column samples n1 + 64 n2 (issued first, so that the twiddle table is
+    // built while they are in flight) -> Q-point DFT in registers
     const float2* src = r + img * (int64_t)H * my + kyc;
     float2 v[Q];
 #pragma unroll
     for (int n2 = 0; n2 < Q; ++n2) v[n2] = src[(int64_t)(n1 + 64 * n2) * my];
+    fill_twiddles<H>(T, mx, tw, -1);
     dft<Q, -1>(v);
     __syncthreads();                                 // twiddle table complete
 
