@@ -164,6 +164,8 @@ EDGE_2D = [
     (2, 2, 2, 512, 32, 4, 7),       # pruned columns (512 rows), few kept rows
     (1, 1, 2, 1024, 8, 5, 3),       # tall grid whose kept rows do not suit the pruned columns
     (1, 2, 2, 2048, 128, 64, 60),   # pruned columns at the large-grid row count, 128 kept rows
+    (8, 64, 64, 128, 128, 32, 32),  # matrix-core mix: 16-row tiles of 64 output channels
+    (64, 16, 32, 128, 128, 32, 32), # matrix-core mix: 32-row tiles of 32 output channels
 ]
 
 
