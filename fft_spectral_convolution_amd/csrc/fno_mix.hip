@@ -56,13 +56,14 @@ __device__ __forceinline__ floatx4 mfma16(float a, float b, floatx4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-// tile t -> (mode tile, batch tile, output tile), output tile fastest; KB
-// batch rows and KO output channels per tile
+// tile t -> (mode tile, batch tile, output tile): output tile fastest, mode
+// tile slowest, so that neighbouring tiles share X (same batch rows) or W
+// (same modes); KB batch rows and KO output channels per tile
 template <int KB, int KO>
 __device__ __forceinline__ Tile tile_of(const TileGrid& tg, int t) {
     const int ot = t % tg.n_ot;
     const int r = t / tg.n_ot;
-    return Tile{(r % tg.n_mt) * 8, (r / tg.n_mt) * KB, ot * KO};
+    return Tile{(r / tg.n_bt) * 8, (r % tg.n_bt) * KB, ot * KO};
 }
 
 // VEC: every (b, c) run of 8 modes is 16-byte aligned and complete (tiled
@@ -237,11 +238,14 @@ __global__ __launch_bounds__(kMixThreads) void k_mix_mfma(const float2* __restri
     // last tile the last chunk is reloaded).  LDS buffer k & 1 is rewritten
     // only after every wave passed the barrier of chunk k - 1, i.e. after all
     // reads of chunk k - 2.
-    // workgroup j walks the contiguous tile range [t_begin, t_end), so the
-    // output tiles of a mode tile (when Cout needs several) run back to back
+    // Every workgroup walks a contiguous range of the tile sequence.  The
+    // ranges are dealt out so that the workgroups of one XCD (indices equal
+    // mod 8 under round-robin dispatch) hold one contiguous eighth of the
+    // sequence: tiles that share X or W then share that XCD's L2.
     const int G = gridDim.x;
-    const int t_begin = (int)((int64_t)tg.n_tiles * blockIdx.x / G);
-    const int t_end = (int)((int64_t)tg.n_tiles * (blockIdx.x + 1) / G);
+    const int j = G % 8 == 0 ? (int)(blockIdx.x % 8) * (G / 8) + (int)(blockIdx.x / 8) : (int)blockIdx.x;
+    const int t_begin = (int)((int64_t)tg.n_tiles * j / G);
+    const int t_end = (int)((int64_t)tg.n_tiles * (j + 1) / G);
     int t = t_begin;
     Tile cur = tile_of<kB, kO>(tg, t);
     Tile nxt = tile_of<kB, kO>(tg, t + 1 < t_end ? t + 1 : t);
