@@ -19,8 +19,10 @@ launch-carried events lengthen the gaps between kernels.
 Prints ONE JSON line.  `value` is compulsory bytes (x + W + out) per second
 in GB/s; the line also carries calls/s, the fraction of the 8 TB/s HBM peak,
 a `roofline` entry for the longest-running kernel (its algorithmic bytes per
-launch over its average launch time) and a `cpu_baseline`
-entry: the fp64 CPU oracle timed on this host on a bounded sample.
+launch over its average launch time), a `mix` entry for the matrix-core
+channel mix (its flops against the fp32 MFMA peak) when the workload uses
+it, and a `cpu_baseline` entry: the fp64 CPU oracle timed on this host on a
+bounded sample.
 """
 from __future__ import annotations
 
@@ -33,6 +35,7 @@ import time
 import numpy as np
 
 HBM_PEAK_GBS = 8000.0
+MFMA_FP32_PEAK_TFLOPS = 157.3     # dense fp32 matrix-core peak of one MI355X
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
@@ -272,6 +275,25 @@ def main():
             "avg_launch_us": round(per_kernel_ms[dom] * 1e3, 3),
         },
     }
+    if "mix_mfma" in kernels:
+        # the matrix-core stage against the fp32 MFMA peak: executed flops of
+        # the 3M form (three real GEMMs, 2 flops per multiply-add), and the
+        # algorithmic count of 8 flops per complex multiply-add
+        k = kernels.index("mix_mfma")
+        macs = cfg.B * cfg.Cin * cfg.Cout * (cfg.my if cfg.kind == "1d" else 2 * cfg.mx * cfg.my)
+        t = per_kernel_ms[k] * 1e-3
+        line["mix"] = {
+            "kernel": "mix_mfma",
+            "bound": "mfma",
+            "achieved": round(6.0 * macs / t / 1e12, 3),
+            "peak": MFMA_FP32_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(6.0 * macs / t / 1e12 / MFMA_FP32_PEAK_TFLOPS, 5),
+            "flops_executed_3m": 6 * macs,
+            "flops_complex_8": 8 * macs,
+            "hbm_gbs": round(kernel_bytes("mix_mfma", cfg) / t / 1e9, 3),
+            "avg_launch_us": round(per_kernel_ms[k] * 1e3, 3),
+        }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(cfg, x_np, w_np, args.cpu_budget)
     print(json.dumps(line), flush=True)
