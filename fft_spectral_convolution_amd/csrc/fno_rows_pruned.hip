@@ -49,11 +49,14 @@ __device__ __forceinline__ float2 conj2(float2 a) { return make_float2(a.x, -a.y
 
 // Residue-factored twiddles of a row of N = 64 Q points, lane n1:
 // W^{n1 k} = res(k mod Q) * W_64^{n1 (k div Q)} (W = exp(-2 pi i / N)).
-template <int Q>
+// HALF keeps only the residues r <= Q/2 in registers and forms the others as
+// W^{n1 r} = W_64^{n1} conj(W^{n1 (Q - r)}) (W^{n1 Q} = W_64^{n1}): one more
+// complex product each, Q/2 - 1 fewer register pairs.
+template <int Q, bool HALF = false>
 struct LaneTwiddles {
-    static constexpr int NR = Q <= 32 ? Q : 1;      // residue factors kept in registers
+    static constexpr int NR = Q <= 32 ? (HALF ? Q / 2 + 1 : Q) : 1;   // residue factors in registers
     static constexpr int NJ = 64 / Q > 1 ? 64 / Q : 1;
-    float2 tr[NR];                                  // W^{n1 r}, r < Q (Q <= 32)
+    float2 tr[NR];                                  // W^{n1 r}, r < NR (Q <= 32)
     float2 pj[NJ];                                  // W_64^{n1 j}, j < 64 / Q
     const float2* tl;                               // Q = 64: LDS table [r][64 lanes]
 
@@ -62,7 +65,7 @@ struct LaneTwiddles {
         if constexpr (Q <= 32) {
             (void)lds_table;
 #pragma unroll
-            for (int r = 0; r < Q; ++r) tr[r] = tw[(lane * r * (kNMax / N)) & (kNMax - 1)];
+            for (int r = 0; r < NR; ++r) tr[r] = tw[(lane * r * (kNMax / N)) & (kNMax - 1)];
         } else {
             // 64 x 64 residue factors, filled by the whole workgroup
             for (int e = threadIdx.x; e < 64 * 64; e += blockDim.x) {
@@ -77,10 +80,20 @@ struct LaneTwiddles {
 #pragma unroll
         for (int r = 0; r < NR; ++r) asm volatile("" : "+v"(tr[r].x), "+v"(tr[r].y));
     }
+    // Hides the factors from loop-invariant code motion (called once per row),
+    // so that the derived factors are formed per row, not hoisted into
+    // registers.
+    __device__ __forceinline__ void opaque() {
+#pragma unroll
+        for (int r = 0; r < NR; ++r) asm volatile("" : "+v"(tr[r].x), "+v"(tr[r].y));
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) asm volatile("" : "+v"(pj[j].x), "+v"(pj[j].y));
+    }
     template <int R>
     __device__ __forceinline__ float2 res(int lane) const {
-        if constexpr (Q <= 32) return tr[R];
-        else return tl[R * 64 + lane];
+        if constexpr (Q > 32) return tl[R * 64 + lane];
+        else if constexpr (R < NR) return tr[R];
+        else return cmul(pj[1], conj2(tr[R < NR ? 0 : Q - R]));
     }
 };
 
@@ -226,12 +239,13 @@ __global__ __launch_bounds__(kPrunedThreads) __attribute__((amdgpu_waves_per_eu(
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     float2* const xrow = xrow_all[wave];
-    LaneTwiddles<Q> tws;
+    LaneTwiddles<Q, true> tws;
     tws.init(tw, lane, table);
     if constexpr (Q == 64) __syncthreads();
 
     const int64_t nwaves = (int64_t)gridDim.x * kPrunedWaves;
     for (int64_t row = (int64_t)blockIdx.x * kPrunedWaves + wave; row < nrows; row += nwaves) {
+        if constexpr (Q <= 32) tws.opaque();
         // the row's kept bins, zero past my, DC imaginary part dropped
         {
             float2 v = lane < my ? y[row * (int64_t)y_ld + lane] : make_float2(0.0f, 0.0f);
