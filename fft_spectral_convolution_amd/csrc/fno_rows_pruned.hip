@@ -255,30 +255,28 @@ __global__ __launch_bounds__(kPrunedThreads) __attribute__((amdgpu_waves_per_eu(
         wave_lds_sync();
         // V[r] = conj(W^{n1 r}) sum_j c_k X[k] conj(W_64^{n1 j}), k = r + Q j,
         // c_0 = 1, c_k = 2
-        constexpr int NT = Q < 64 ? Q : 64;
-        float2 V[Q];
-#pragma unroll
-        for (int r = 0; r < Q; ++r) V[r] = make_float2(0.0f, 0.0f);
-        static_for<0, NT>([&](auto r) {
+        auto vres = [&](auto r) __attribute__((always_inline)) {
             float2 acc = make_float2(0.0f, 0.0f);
-            static_for<0, 64 / NT>([&](auto j) {
-                constexpr int k = r + NT * j;
+            static_for<0, 64 / Q>([&](auto j) {
+                constexpr int k = r + Q * j;
                 constexpr float c = k == 0 ? 1.0f : 2.0f;
                 float2 u = xrow[k];
                 if constexpr (j > 0) u = cmul(u, conj2(tws.pj[j]));
                 acc = make_float2(fmaf(c, u.x, acc.x), fmaf(c, u.y, acc.y));
             });
-            V[r] = cmul(acc, conj2(tws.template res<r>(lane)));
-        });
-        wave_lds_sync();                        // the row buffer is read before the next row overwrites it
-        // Hermitian part H[r] = (V[r] + conj V[-r]) / 2, r <= Q/2, scaled
+            return cmul(acc, conj2(tws.template res<r>(lane)));
+        };
+        // Hermitian part H[r] = (V[r] + conj V[-r]) / 2, r <= Q/2, scaled,
+        // each pair V[r], V[Q - r] formed where it is used
         float2 H[NZ + 1];
         static_for<0, NZ + 1>([&](auto r) {
-            const float2 a = V[r];
-            const float2 b = V[(Q - r) % Q];
+            constexpr int rm = (Q - r) % Q;
+            const float2 a = vres(r);
+            const float2 b = (rm == r) ? a : vres(std::integral_constant<int, rm>{});
             const float h = 0.5f * scale;
             H[r] = make_float2(h * (a.x + b.x), h * (a.y - b.y));
         });
+        wave_lds_sync();                        // the row buffer is read before the next row overwrites it
         float2 z[NZ];
         static_for<0, NZ>([&](auto k) { z[k] = packed_bin<Q, k>(H); });
         dft<NZ, 1>(z);
