@@ -231,6 +231,8 @@ def main():
     ms_per_step = start.elapsed_time(stop) / args.steps
     per_kernel_ms = [float(np.mean([evs[i][2 * k].elapsed_time(evs[i][2 * k + 1]) for i in range(args.steps)]))
                      for k in range(nk)]
+    # per-step span in pass 2 (first kernel's start to last kernel's stop)
+    spans_us = [evs[i][0].elapsed_time(evs[i][2 * nk - 1]) * 1e3 for i in range(args.steps)]
     dom = int(np.argmax(per_kernel_ms))
     dom_name = kernels[dom]
     dom_bytes = kernel_bytes(dom_name, cfg)
@@ -257,12 +259,17 @@ def main():
             "x_dist": cfg.dist,
             "compulsory_bytes": cfg.compulsory_bytes,
             "buffer_sets": nsets,
+            # every buffer a step touches fits the 256 MiB last-level cache:
+            # the GB/s figure is then not an HBM rate
+            "cache_resident": bool(nsets * set_bytes + w_np.nbytes <= 256 * 2**20),
         },
         "calls_per_s": round(1e3 / ms_per_step, 3),
         "hbm_pct": round(100.0 * gbs / HBM_PEAK_GBS, 3),
         "wall_s_timed": round(wall, 4),
         "kernels": {k: round(t * 1e3, 3) for k, t in zip(kernels, per_kernel_ms)},
         "kernels_unit": "us per launch (start/stop events carried by each launch)",
+        "step_span_us": {"median": round(float(np.median(spans_us)), 3), "min": round(float(np.min(spans_us)), 3),
+                         "note": "first kernel start to last kernel stop of each step, event-carrying pass"},
         "roofline": {
             "kernel": dom_name,
             "bound": "hbm",
