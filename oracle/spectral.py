@@ -32,6 +32,13 @@ upcast exactly):
    with c_0 = c_{W/2} = 1 and c_ky = 2 otherwise (the standard C2R rule: the
    imaginary parts of the DC and Nyquist columns do not contribute).
 5. 1D: the same with H = 1, one weight block W[modes, Cin, Cout].
+6. gradients of a real loss with dL/dout = g (the backward pass):
+     dL/dx = the chain 1-4 applied to g with the conjugate-transposed weight
+             W^H[s,r,ky,o,i] = conj W[s,r,ky,i,o];
+     dL/dRe W + i dL/dIm W [s,r,ky,i,o] = c_ky sum_b conj(Xh[b,i,s,r,ky]) Gh[b,o,s,r,ky],
+   Gh the truncated forward transform of g (derived below
+   ``spectral_conv2d_backward_ref``; pinned by the adjoint identity and the
+   exact change of the loss under weight perturbations).
 
 Two independent ways of computing the transforms are provided:
 
@@ -68,6 +75,8 @@ __all__ = [
     "spectral_conv1d_ref",
     "spectral_conv2d_loops",
     "spectral_conv1d_loops",
+    "spectral_conv2d_backward_ref",
+    "spectral_conv1d_backward_ref",
 ]
 
 
@@ -311,6 +320,62 @@ def spectral_conv1d_ref(x, weight, modes: int, transform: str = "dft", return_st
     if return_stages:
         return out, xh, yh
     return out
+
+
+# --------------------------------------------------------------------------
+# Gradients (the backward pass of the same operator)
+# --------------------------------------------------------------------------
+#
+# For a real loss L with g = dL/dout, write the operator as
+#   out = sum_m c_m Re(Y_m phi_m),  Y_m = sum_i X_m,i W_m,i,o,
+#   X_m = <x, phi_m> = sum_hw x conj(phi_m),  phi_m = (HW)^-1/2 exp(+2 pi i (kx h/H + ky w/W))
+# (m runs over the kept modes, c_m the C2R weight of its ky).  With
+# G_m = <g, phi_m> (the truncated forward transform of g):
+#   dL/dx      = sum_m c_m Re(phi_m sum_o conj(W_m,i,o) G_m,o)
+#              = the same forward -> mix -> inverse chain on g with the
+#                conjugate-transposed weight W^H[m,o,i] = conj(W[m,i,o]);
+#   dL/dRe W + i dL/dIm W = c_m sum_b conj(X_b,m,i) G_b,m,o.
+# Both follow from dL = sum_m c_m Re(dY_m conj(G_m)) (the C2R weights enter
+# the weight gradient only: in dL/dx the inverse applies them again).
+
+def spectral_conv2d_backward_ref(x, weight, grad_out, mx: int, my: int, transform: str = "dft"):
+    """Gradients of sum(grad_out * spectral_conv2d_ref(x, weight)).
+
+    Returns (grad_x[B,Cin,H,W] float64, grad_w[2,mx,my,Cin,Cout] complex128),
+    grad_w = dL/dRe(W) + i dL/dIm(W).
+    """
+    x = np.asarray(x)
+    weight = np.asarray(weight, dtype=np.complex128)
+    g = np.asarray(grad_out)
+    _, cin, h, w = x.shape
+    if weight.shape[:3] != (2, mx, my) or weight.shape[3] != cin or g.shape[1] != weight.shape[4]:
+        raise ValueError(f"weight shape {weight.shape} does not match x {x.shape} / grad_out {g.shape}")
+    xh = forward_truncated_2d(x, mx, my, transform)              # [B,Cin,2,mx,my]
+    gh = forward_truncated_2d(g, mx, my, transform)              # [B,Cout,2,mx,my]
+    zh = np.einsum("bosrk,srkio->bisrk", gh, np.conj(weight))     # G W^H
+    grad_x = inverse_from_truncated_2d(zh, h, w, transform)
+    c = c2r_weights(w, my)                                       # [my]
+    grad_w = np.einsum("bisrk,bosrk->srkio", np.conj(xh), gh) * c[None, None, :, None, None]
+    return grad_x, grad_w
+
+
+def spectral_conv1d_backward_ref(x, weight, grad_out, modes: int, transform: str = "dft"):
+    """Gradients of sum(grad_out * spectral_conv1d_ref(x, weight)).
+
+    Returns (grad_x[B,Cin,N] float64, grad_w[modes,Cin,Cout] complex128).
+    """
+    x = np.asarray(x)
+    weight = np.asarray(weight, dtype=np.complex128)
+    g = np.asarray(grad_out)
+    n = x.shape[-1]
+    if weight.shape[0] != modes or weight.shape[1] != x.shape[1] or g.shape[1] != weight.shape[2]:
+        raise ValueError(f"weight shape {weight.shape} does not match x {x.shape} / grad_out {g.shape}")
+    xh = forward_truncated_1d(x, modes, transform)               # [B,Cin,modes]
+    gh = forward_truncated_1d(g, modes, transform)               # [B,Cout,modes]
+    zh = np.einsum("bok,kio->bik", gh, np.conj(weight))
+    grad_x = inverse_from_truncated_1d(zh, n, transform)
+    grad_w = np.einsum("bik,bok->kio", np.conj(xh), gh) * c2r_weights(n, modes)[:, None, None]
+    return grad_x, grad_w
 
 
 # --------------------------------------------------------------------------

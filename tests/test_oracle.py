@@ -491,3 +491,124 @@ def test_planted_mistakes(monkeypatch):
             except Exception:
                 caught = True
         assert caught, f"planted mistake in {name} ({fn.__name__}) was not caught"
+
+
+# --------------------------------------------------------------------------
+# Gradients: the adjoint identity <A x, g> = <x, A^T g> and the exact change
+# of the (linear-in-W) loss under a weight perturbation
+# --------------------------------------------------------------------------
+
+BWD_2D = [(2, 3, 4, 8, 8, 2, 3), (1, 2, 3, 16, 8, 3, 5), (2, 2, 2, 8, 16, 4, 9), (1, 1, 2, 4, 4, 2, 3)]
+
+
+def _loss_2d(x, w, g, mx, my, transform="dft"):
+    return float(np.sum(g * S.spectral_conv2d_ref(x, w, mx, my, transform)))
+
+
+@pytest.mark.parametrize("transform", TRANSFORMS)
+@pytest.mark.parametrize("shape", BWD_2D)
+def test_backward_adjoint_2d(transform, shape):
+    b, cin, cout, h, w, mx, my = shape
+    rng = np.random.default_rng(31)
+    x = rng.standard_normal((b, cin, h, w))
+    wt = rand_c(rng, (2, mx, my, cin, cout))
+    g = rng.standard_normal((b, cout, h, w))
+    gx, _ = S.spectral_conv2d_backward_ref(x, wt, g, mx, my, transform)
+    lhs = _loss_2d(x, wt, g, mx, my, transform)          # <A x, g>
+    rhs = float(np.sum(x * gx))                           # <x, A^T g>
+    assert abs(lhs - rhs) <= 1e-11 * max(1.0, abs(lhs))
+
+
+@pytest.mark.parametrize("transform", TRANSFORMS)
+@pytest.mark.parametrize("shape", BWD_2D)
+def test_backward_weight_exact_difference_2d(transform, shape):
+    # L is linear in W: L(W + E) - L(W) = Re sum conj(dL/dW) E exactly
+    b, cin, cout, h, w, mx, my = shape
+    rng = np.random.default_rng(32)
+    x = rng.standard_normal((b, cin, h, w))
+    wt = rand_c(rng, (2, mx, my, cin, cout))
+    g = rng.standard_normal((b, cout, h, w))
+    e = rand_c(rng, wt.shape)
+    _, gw = S.spectral_conv2d_backward_ref(x, wt, g, mx, my, transform)
+    diff = _loss_2d(x, wt + e, g, mx, my, transform) - _loss_2d(x, wt, g, mx, my, transform)
+    pred = float(np.real(np.sum(np.conj(gw) * e)))
+    assert abs(diff - pred) <= 1e-10 * max(1.0, abs(diff))
+    # and one coordinate at a time, real and imaginary directions separately
+    for idx in [(0, 0, 0, 0, 0), (1, mx - 1, my - 1, cin - 1, cout - 1), (0, 0, my - 1, 0, cout - 1)]:
+        for unit, part in ((1.0, np.real), (1j, np.imag)):
+            e1 = np.zeros_like(wt)
+            e1[idx] = unit
+            d1 = _loss_2d(x, wt + e1, g, mx, my, transform) - _loss_2d(x, wt, g, mx, my, transform)
+            assert abs(d1 - part(gw[idx])) <= 1e-10 * max(1.0, abs(d1))
+
+
+def test_backward_ones_weight_full_modes_is_identity_adjoint():
+    # full modes, identity weights: the operator is the identity, so its
+    # adjoint returns g itself
+    rng = np.random.default_rng(33)
+    h, w, c = 8, 8, 3
+    mx, my = h // 2, w // 2 + 1
+    wt = np.zeros((2, mx, my, c, c), dtype=np.complex128)
+    for i in range(c):
+        wt[..., i, i] = 1.0
+    g = rng.standard_normal((2, c, h, w))
+    gx, _ = S.spectral_conv2d_backward_ref(rng.standard_normal((2, c, h, w)), wt, g, mx, my)
+    assert rel(gx, g) < 1e-12
+
+
+BWD_1D = [(2, 3, 4, 16, 5), (1, 2, 2, 8, 5), (3, 1, 2, 32, 1)]
+
+
+def _loss_1d(x, w, g, modes, transform="dft"):
+    return float(np.sum(g * S.spectral_conv1d_ref(x, w, modes, transform)))
+
+
+@pytest.mark.parametrize("transform", TRANSFORMS)
+@pytest.mark.parametrize("shape", BWD_1D)
+def test_backward_1d(transform, shape):
+    b, cin, cout, n, modes = shape
+    rng = np.random.default_rng(34)
+    x = rng.standard_normal((b, cin, n))
+    wt = rand_c(rng, (modes, cin, cout))
+    g = rng.standard_normal((b, cout, n))
+    gx, gw = S.spectral_conv1d_backward_ref(x, wt, g, modes, transform)
+    lhs = _loss_1d(x, wt, g, modes, transform)
+    assert abs(lhs - float(np.sum(x * gx))) <= 1e-11 * max(1.0, abs(lhs))
+    e = rand_c(rng, wt.shape)
+    diff = _loss_1d(x, wt + e, g, modes, transform) - lhs
+    assert abs(diff - float(np.real(np.sum(np.conj(gw) * e)))) <= 1e-10 * max(1.0, abs(diff))
+
+
+def test_backward_planted_mistakes():
+    # plausible slips in the gradient formulas, each caught by the pins above
+    b, cin, cout, h, w, mx, my = 2, 3, 4, 8, 8, 2, 5     # my = W/2 + 1: Nyquist column kept
+    rng = np.random.default_rng(35)
+    x = rng.standard_normal((b, cin, h, w))
+    wt = rand_c(rng, (2, mx, my, cin, cout))
+    g = rng.standard_normal((b, cout, h, w))
+    e = rand_c(rng, wt.shape)
+    gx, gw = S.spectral_conv2d_backward_ref(x, wt, g, mx, my)
+    lhs = _loss_2d(x, wt, g, mx, my)
+    diff = _loss_2d(x, wt + e, g, mx, my) - lhs
+
+    def adjoint_ok(gx_try):
+        return abs(lhs - float(np.sum(x * gx_try))) <= 1e-11 * max(1.0, abs(lhs))
+
+    def weight_ok(gw_try):
+        return abs(diff - float(np.real(np.sum(np.conj(gw_try) * e)))) <= 1e-10 * max(1.0, abs(diff))
+
+    assert adjoint_ok(gx) and weight_ok(gw)
+    gh = S.forward_truncated_2d(g, mx, my)
+    xh = S.forward_truncated_2d(x, mx, my)
+    c = S.c2r_weights(w, my)[None, None, :, None, None]
+    # weight not conjugated in the input gradient
+    assert not adjoint_ok(S.inverse_from_truncated_2d(np.einsum("bosrk,srkio->bisrk", gh, wt), h, w))
+    # C2R weights applied to the input gradient as well
+    assert not adjoint_ok(S.inverse_from_truncated_2d(
+        np.einsum("bosrk,srkio->bisrk", gh, np.conj(wt)) * S.c2r_weights(w, my), h, w))
+    # C2R weights missing from the weight gradient
+    assert not weight_ok(np.einsum("bisrk,bosrk->srkio", np.conj(xh), gh))
+    # conjugate on the wrong factor
+    assert not weight_ok(np.einsum("bisrk,bosrk->srkio", xh, np.conj(gh)) * c)
+    # batch not summed (first item only)
+    assert not weight_ok(np.einsum("isrk,osrk->srkio", np.conj(xh[0]), gh[0]) * c)
