@@ -28,6 +28,8 @@ __all__ = [
     "fno_spectral_conv1d_unfused",
     "fno_spectral_conv2d_ws",
     "fno_spectral_conv1d_ws",
+    "fno_spectral_conv2d_backward",
+    "fno_spectral_conv1d_backward",
     "fno_workspace_size_2d",
     "fno_workspace_size_1d",
     "fno_forward2d",
@@ -68,6 +70,8 @@ _SIGNATURES = {
     "fno_inverse2d": (_I, [_P, _P, _I, _I, _I, _I, _I, _I, _P]),
     "fno_forward1d": (_I, [_P, _P, _I, _I, _I, _I, _P]),
     "fno_inverse1d": (_I, [_P, _P, _I, _I, _I, _I, _P]),
+    "fno_spectral_conv2d_backward": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P]),
+    "fno_spectral_conv1d_backward": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P]),
     "fno_set_timing_events": (_I, [ctypes.POINTER(ctypes.c_void_p), _I]),
     "fno_last_kernel_count": (_I, []),
     "fno_last_kernel_name": (ctypes.c_char_p, [_I]),
@@ -253,6 +257,50 @@ def fno_spectral_conv1d_ws(x, w, modes: int, workspace, out=None):
         _check(lib().fno_spectral_conv1d_ws(_ptr(x), _ptr(w), _ptr(out), b, cin, cout, n, modes,
                                             ws_ptr, ws_bytes, _stream_ptr(x.device)), "fno_spectral_conv1d_ws")
     return out
+
+
+def _grad_outputs(x, w, grad_out, need_x, need_w, out_shape):
+    torch = _torch()
+    if not (need_x or need_w):
+        raise ValueError("ask for at least one of the two gradients")
+    _need(grad_out, torch.float32, x.dim(), "grad_out")
+    if tuple(grad_out.shape) != out_shape:
+        raise ValueError(f"grad_out has shape {tuple(grad_out.shape)}, expected {out_shape}")
+    if grad_out.device != x.device:
+        raise ValueError("grad_out must be on the device of x")
+    gx = torch.empty_like(x) if need_x else None
+    gw = torch.empty_like(w) if need_w else None
+    return gx, gw
+
+
+def fno_spectral_conv2d_backward(x, w, grad_out, mx: int, my: int, need_x: bool = True, need_w: bool = True):
+    """Gradients (grad_x[B,Cin,H,W] f32, grad_w[2,mx,my,Cin,Cout] c64) of a real loss
+    through fno_spectral_conv2d, given grad_out = dL/dout; grad_w = dL/dRe w + i dL/dIm w.
+    A gradient not asked for is returned as None."""
+    _, (b, cin, cout, h, wd) = _conv2d_args(x, w, mx, my, grad_out)
+    gx, gw = _grad_outputs(x, w, grad_out, need_x, need_w, (b, cout, h, wd))
+    nullp = ctypes.c_void_p(0)
+    with _on_device(x):
+        _check(lib().fno_spectral_conv2d_backward(_ptr(x), _ptr(w), _ptr(grad_out),
+                                                  _ptr(gx) if gx is not None else nullp,
+                                                  _ptr(gw) if gw is not None else nullp,
+                                                  b, cin, cout, h, wd, mx, my, _stream_ptr(x.device)),
+               "fno_spectral_conv2d_backward")
+    return gx, gw
+
+
+def fno_spectral_conv1d_backward(x, w, grad_out, modes: int, need_x: bool = True, need_w: bool = True):
+    """Gradients (grad_x[B,Cin,N] f32, grad_w[modes,Cin,Cout] c64) through fno_spectral_conv1d."""
+    _, (b, cin, cout, n) = _conv1d_args(x, w, modes, grad_out)
+    gx, gw = _grad_outputs(x, w, grad_out, need_x, need_w, (b, cout, n))
+    nullp = ctypes.c_void_p(0)
+    with _on_device(x):
+        _check(lib().fno_spectral_conv1d_backward(_ptr(x), _ptr(w), _ptr(grad_out),
+                                                  _ptr(gx) if gx is not None else nullp,
+                                                  _ptr(gw) if gw is not None else nullp,
+                                                  b, cin, cout, n, modes, _stream_ptr(x.device)),
+               "fno_spectral_conv1d_backward")
+    return gx, gw
 
 
 def fno_forward2d(x, mx: int, my: int, xh=None):

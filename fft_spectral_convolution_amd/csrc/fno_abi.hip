@@ -400,6 +400,169 @@ int conv1d_common(const float* x, const void* w, float* out, int B, int Cin, int
                                       st->twiddle, hs));
 }
 
+// ---------------------------------------------------------------------------
+// backward pass
+// ---------------------------------------------------------------------------
+
+// Outputs of a backward call must not overlap any input or each other.
+int check_backward(const float* x, const void* w, const float* g, const float* gx, const void* gw, size_t xbytes,
+                   size_t wbytes, size_t gbytes) {
+    if (!x || !w || !g || (!gx && !gw)) return FNO_ERR_NULL;
+    if (misaligned(x) || misaligned(w) || misaligned(g) || (gx && misaligned(gx)) || (gw && misaligned(gw)))
+        return FNO_ERR_ALIGN;
+    if (gx && (overlap(gx, xbytes, x, xbytes) || overlap(gx, xbytes, w, wbytes) || overlap(gx, xbytes, g, gbytes)))
+        return FNO_ERR_ALIAS;
+    if (gw && (overlap(gw, wbytes, x, xbytes) || overlap(gw, wbytes, w, wbytes) || overlap(gw, wbytes, g, gbytes) ||
+               (gx && overlap(gw, wbytes, gx, xbytes))))
+        return FNO_ERR_ALIAS;
+    return FNO_OK;
+}
+
+// Workspace of the backward pass: [R (staged transforms only)] [X] [G] [Z]
+// [W^H], the spectra in the layout of the forward schedule for the shape.
+struct BackwardPlan {
+    bool small;
+    SpecLayout lx, lg;
+    size_t r_bytes, x_bytes, g_bytes, z_bytes, wt_bytes;
+    size_t total() const { return r_bytes + x_bytes + g_bytes + z_bytes + wt_bytes; }
+};
+
+BackwardPlan backward_plan_2d(const Shape2d& s) {
+    BackwardPlan p;
+    const int64_t m = (int64_t)2 * s.mx * s.my;
+    p.small = small_path(s);
+    p.lx = p.small ? tiled_layout(s.Cin, m) : canonical_layout(s.Cin, m);
+    p.lg = p.small ? tiled_layout(s.Cout, m) : canonical_layout(s.Cout, m);
+    p.r_bytes = p.small ? 0
+                        : align_up((size_t)s.B * (size_t)(s.Cin > s.Cout ? s.Cin : s.Cout) * s.H * s.my *
+                                   sizeof(float2));
+    p.x_bytes = align_up((size_t)layout_elems(p.lx, s.B) * sizeof(float2));
+    p.g_bytes = align_up((size_t)layout_elems(p.lg, s.B) * sizeof(float2));
+    p.z_bytes = p.x_bytes;
+    p.wt_bytes = align_up((size_t)m * s.Cin * s.Cout * sizeof(float2));
+    return p;
+}
+
+int run_backward_2d(const Shape2d& s, const float* x, const float2* w, const float* g, float* gx, float2* gw,
+                    void* ws, const float2* tw, hipStream_t st) {
+    const BackwardPlan p = backward_plan_2d(s);
+    const int64_t m = (int64_t)2 * s.mx * s.my;
+    char* q = static_cast<char*>(ws);
+    float2* r = reinterpret_cast<float2*>(q);
+    q += p.r_bytes;
+    float2* xh = reinterpret_cast<float2*>(q);
+    q += p.x_bytes;
+    float2* gh = reinterpret_cast<float2*>(q);
+    q += p.g_bytes;
+    float2* zh = reinterpret_cast<float2*>(q);
+    q += p.z_bytes;
+    float2* wt = reinterpret_cast<float2*>(q);
+    auto forward = [&](int64_t C, const float* in, float2* out_h, const SpecLayout& lay) {
+        return p.small ? run_forward2d_small(s, C, in, out_h, lay, tw, st)
+                       : run_forward2d_staged(s, C, in, out_h, r, tw, st);
+    };
+    int rc = forward(s.Cout, g, gh, p.lg);
+    if (rc) return rc;
+    if (gw) {
+        rc = forward(s.Cin, x, xh, p.lx);
+        if (rc) return rc;
+        rec_kernel("wgrad", st);
+        hipError_t e = launch_weight_grad(xh, p.lx, gh, p.lg, gw, s.B, s.Cin, s.Cout, m, s.my, s.W / 2, st);
+        if (e != hipSuccess) return hip_fail(e);
+    }
+    if (gx) {
+        rec_kernel("wadjoint", st);
+        hipError_t e = launch_weight_adjoint(w, wt, m, s.Cin, s.Cout, st);
+        if (e != hipSuccess) return hip_fail(e);
+        rc = run_mix(gh, p.lg, wt, zh, p.lx, s.B, s.Cout, s.Cin, m, st);
+        if (rc) return rc;
+        rc = p.small ? run_inverse2d_small(s, s.Cin, zh, gx, p.lx, tw, st)
+                     : run_inverse2d_staged(s, s.Cin, zh, gx, r, tw, st);
+        if (rc) return rc;
+    }
+    return FNO_OK;
+}
+
+int backward2d_common(const float* x, const void* w, const float* g, float* gx, void* gw, int B, int Cin, int Cout,
+                      int H, int W, int mx, int my, void* stream) {
+    int rc = check_dims_2d(B, Cin, H, W, mx, my);
+    if (rc) return rc;
+    if (Cout < 1) return FNO_ERR_SHAPE;
+    const size_t xbytes = (size_t)B * Cin * H * W * sizeof(float);
+    const size_t gbytes = (size_t)B * Cout * H * W * sizeof(float);
+    const size_t wbytes = (size_t)2 * mx * my * Cin * Cout * sizeof(float2);
+    rc = check_backward(x, w, g, gx, gw, xbytes, wbytes, gbytes);
+    if (rc) return rc;
+    const Shape2d s = make2d(B, Cin, Cout, H, W, mx, my);
+    DeviceState* st = nullptr;
+    rc = device_state(&st);
+    if (rc) return rc;
+    void* ws = nullptr;
+    rc = internal_workspace(st, backward_plan_2d(s).total(), &ws);
+    if (rc) return rc;
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    rec_begin();
+    return rec_end(hs, run_backward_2d(s, x, static_cast<const float2*>(w), g, gx, static_cast<float2*>(gw), ws,
+                                       st->twiddle, hs));
+}
+
+int backward1d_common(const float* x, const void* w, const float* g, float* gx, void* gw, int B, int Cin, int Cout,
+                      int N, int modes, void* stream) {
+    int rc = check_dims_1d(B, Cin, N, modes);
+    if (rc) return rc;
+    if (Cout < 1) return FNO_ERR_SHAPE;
+    const size_t xbytes = (size_t)B * Cin * N * sizeof(float);
+    const size_t gbytes = (size_t)B * Cout * N * sizeof(float);
+    const size_t wbytes = (size_t)modes * Cin * Cout * sizeof(float2);
+    rc = check_backward(x, w, g, gx, gw, xbytes, wbytes, gbytes);
+    if (rc) return rc;
+    const size_t xb = align_up((size_t)B * Cin * modes * sizeof(float2));
+    const size_t gb = align_up((size_t)B * Cout * modes * sizeof(float2));
+    const size_t wtb = align_up((size_t)modes * Cin * Cout * sizeof(float2));
+    DeviceState* st = nullptr;
+    rc = device_state(&st);
+    if (rc) return rc;
+    void* ws = nullptr;
+    rc = internal_workspace(st, 2 * xb + gb + wtb, &ws);
+    if (rc) return rc;
+    char* q = static_cast<char*>(ws);
+    float2* xh = reinterpret_cast<float2*>(q);
+    float2* zh = reinterpret_cast<float2*>(q + xb);
+    float2* gh = reinterpret_cast<float2*>(q + 2 * xb);
+    float2* wt = reinterpret_cast<float2*>(q + 2 * xb + gb);
+    const SpecLayout lx = canonical_layout(Cin, modes), lg = canonical_layout(Cout, modes);
+    const float scale = (float)(1.0 / std::sqrt((double)N));
+    const int l2 = ilog2(N);
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    const float2* wc = static_cast<const float2*>(w);
+    auto run = [&]() -> int {
+        rec_kernel("rows_fwd", hs);
+        hipError_t e = launch_rows_fwd(g, gh, (int64_t)B * Cout, l2, modes, modes, scale, st->twiddle, hs);
+        if (e != hipSuccess) return hip_fail(e);
+        if (gw) {
+            rec_kernel("rows_fwd", hs);
+            e = launch_rows_fwd(x, xh, (int64_t)B * Cin, l2, modes, modes, scale, st->twiddle, hs);
+            if (e != hipSuccess) return hip_fail(e);
+            rec_kernel("wgrad", hs);
+            e = launch_weight_grad(xh, lx, gh, lg, static_cast<float2*>(gw), B, Cin, Cout, modes, modes, N / 2, hs);
+            if (e != hipSuccess) return hip_fail(e);
+        }
+        if (gx) {
+            rec_kernel("wadjoint", hs);
+            e = launch_weight_adjoint(wc, wt, modes, Cin, Cout, hs);
+            if (e != hipSuccess) return hip_fail(e);
+            const int mrc = run_mix(gh, lg, wt, zh, lx, B, Cout, Cin, modes, hs);
+            if (mrc) return mrc;
+            rec_kernel("rows_inv", hs);
+            e = launch_rows_inv(zh, gx, (int64_t)B * Cin, l2, modes, modes, scale, st->twiddle, hs);
+            if (e != hipSuccess) return hip_fail(e);
+        }
+        return FNO_OK;
+    };
+    rec_begin();
+    return rec_end(hs, run());
+}
+
 }  // namespace
 
 LaunchEvents take_launch_events() {
@@ -565,6 +728,16 @@ int fno_forward1d(const float* x, void* xh, int B, int C, int N, int modes, void
     hipError_t e = launch_rows_fwd(x, static_cast<float2*>(xh), (int64_t)B * C, ilog2(N), modes, modes, scale,
                                    st->twiddle, hs);
     return rec_end(hs, e == hipSuccess ? FNO_OK : hip_fail(e));
+}
+
+int fno_spectral_conv2d_backward(const float* x, const void* w, const float* grad_out, float* grad_x, void* grad_w,
+                                 int B, int Cin, int Cout, int H, int W, int mx, int my, void* stream) {
+    return backward2d_common(x, w, grad_out, grad_x, grad_w, B, Cin, Cout, H, W, mx, my, stream);
+}
+
+int fno_spectral_conv1d_backward(const float* x, const void* w, const float* grad_out, float* grad_x, void* grad_w,
+                                 int B, int Cin, int Cout, int N, int modes, void* stream) {
+    return backward1d_common(x, w, grad_out, grad_x, grad_w, B, Cin, Cout, N, modes, stream);
 }
 
 int fno_inverse1d(const void* yh, float* out, int B, int C, int N, int modes, void* stream) {

@@ -118,4 +118,13 @@ hipError_t launch_cols_inv(const float2* yh, float2* r, int64_t nimg, int log2H,
 hipError_t launch_rows_inv(const float2* y, float* out, int64_t nrows, int log2W, int my, int y_ld,
                            float scale, const float2* tw, hipStream_t s);
 
+// ---- backward pass (fno_backward.hip) ---------------------------------------
+// wt[m][o][i] = conj(w[m][i][o]) for M modes.
+hipError_t launch_weight_adjoint(const float2* w, float2* wt, int64_t M, int64_t Cin, int64_t Cout, hipStream_t s);
+// gw[m][i][o] = c_m sum_b conj(xh(b, i, m)) gh(b, o, m), c_m = 1 when
+// ky = m mod my is 0 or nyq, 2 otherwise (spectra addressed by layouts).
+hipError_t launch_weight_grad(const float2* xh, const SpecLayout& lx, const float2* gh, const SpecLayout& lg,
+                              float2* gw, int64_t B, int64_t Cin, int64_t Cout, int64_t M, int my, int nyq,
+                              hipStream_t s);
+
 }  // namespace fno

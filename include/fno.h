@@ -1,9 +1,9 @@
 /*
  * libfno -- Fourier-neural-operator spectral convolution on MI355X (gfx950).
  *
- * C ABI.  Every pointer argument named x, w, out, xh, yh or workspace is
- * DEVICE memory on the current HIP device, owned by the caller; the library
- * never frees caller memory.  `stream` is a hipStream_t passed as void*
+ * C ABI.  Every pointer argument named x, w, out, xh, yh, grad_out, grad_x,
+ * grad_w or workspace is DEVICE memory on the current HIP device, owned by
+ * the caller; the library never frees caller memory.  `stream` is a hipStream_t passed as void*
  * (NULL = the null stream).  All calls only enqueue work on `stream` and
  * return without synchronising; a kernel fault shows up at the caller's next
  * synchronisation.
@@ -137,6 +137,33 @@ int fno_inverse2d(const void* yh, float* out, int B, int C, int H, int W, int mx
                   void* stream);
 int fno_forward1d(const float* x, void* xh, int B, int C, int N, int modes, void* stream);
 int fno_inverse1d(const void* yh, float* out, int B, int C, int N, int modes, void* stream);
+
+/*
+ * Backward pass: gradients of a real loss L through fno_spectral_conv2d /
+ * _1d, given grad_out = dL/dout (float32, the layout of out):
+ *
+ *   grad_x  float32   [B][Cin][H][W]           dL/dx
+ *           = the forward chain applied to grad_out with the conjugate-
+ *             transposed weight w^H[s,r,ky,o,i] = conj w[s,r,ky,i,o]
+ *   grad_w  complex64 [2][mx][my][Cin][Cout]   dL/dRe(w) + i dL/dIm(w)
+ *           = c_ky sum_b conj(X[b,i,s,r,ky]) G[b,o,s,r,ky]
+ *
+ * X and G are the truncated forward transforms of x and grad_out, c_ky the
+ * complex-to-real weight (1 for ky = 0 and ky = W/2, 2 otherwise) (chain
+ * rule through the TurboFNO blog's section 2.2 product and the FFT blog's
+ * section 2.2 C2R).  1D: the same with one weight block [modes][Cin][Cout].
+ * x, w and grad_out are required; grad_x or grad_w may be NULL to skip that
+ * gradient, not both.  Outputs are fully overwritten and must not overlap
+ * any input or each other.  Uses the internal workspace (see
+ * fno_spectral_conv2d).
+ */
+int fno_spectral_conv2d_backward(const float* x, const void* w, const float* grad_out,
+                                 float* grad_x, void* grad_w,
+                                 int B, int Cin, int Cout, int H, int W, int mx, int my,
+                                 void* stream);
+int fno_spectral_conv1d_backward(const float* x, const void* w, const float* grad_out,
+                                 float* grad_x, void* grad_w,
+                                 int B, int Cin, int Cout, int N, int modes, void* stream);
 
 /*
  * Per-kernel timing for benchmarks and profilers.  While `events` is non-NULL,

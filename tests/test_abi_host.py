@@ -135,3 +135,22 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(fno, "_lib", None)
     with pytest.raises(ImportError):
         fno.lib()
+
+
+def test_backward_checks(lib):
+    f2 = lib.fno_spectral_conv2d_backward
+    dims = (2, 3, 4, 16, 16, 4, 4)
+    D = 0x40000000
+    assert f2(A, B, C, None, None, *dims, None) == NULL          # no gradient asked for
+    assert f2(None, B, C, D, None, *dims, None) == NULL
+    assert f2(A, B, C, D, None, 2, 3, 4, 12, 16, 4, 4, None) == SHAPE
+    assert f2(A, B, C, D, None, 2, 3, 4, 16, 16, 9, 4, None) == MODES
+    assert f2(A, B, C, D + 4, None, *dims, None) == ALIGN
+    assert f2(A, B, C, A, None, *dims, None) == ALIAS              # grad_x on top of x
+    assert f2(A, B, C, None, B, *dims, None) == ALIAS              # grad_w on top of w
+    assert f2(A, B, C, D, D, *dims, None) == ALIAS                 # the two gradients overlap
+    f1 = lib.fno_spectral_conv1d_backward
+    assert f1(A, B, C, D, None, 1, 1, 1, 12, 2, None) == SHAPE
+    assert f1(A, B, C, D, None, 1, 1, 1, 16, 10, None) == MODES
+    assert f1(A, B, C, None, None, 1, 1, 1, 16, 4, None) == NULL
+
