@@ -44,7 +44,14 @@ from fft_spectral_convolution_amd.inputs import CONFIGS, make_inputs  # noqa: E4
 
 # Algorithmic bytes each kernel must move per launch (read once + write once),
 # by kernel name (per-unit figures: x, W, out and the truncated spectra).
-def kernel_bytes(name: str, cfg) -> int:
+def kernel_bytes(name: str, cfg, backward: bool = False) -> int:
+    """Bytes of kernel `name` (a repeat launch carries ":n").  In the backward
+    pass the first transform runs on dL/dout (Cout channels) and the inverse
+    writes dL/dx (Cin channels): both see the channel counts swapped; the
+    second forward transform (":2") runs on x."""
+    if backward and not name.endswith(":2"):
+        import dataclasses
+        cfg = dataclasses.replace(cfg, Cin=cfg.Cout, Cout=cfg.Cin)
     c8 = 8
     if cfg.kind == "1d":
         n_in = cfg.B * cfg.Cin * cfg.W * 4
@@ -73,8 +80,15 @@ def kernel_bytes(name: str, cfg) -> int:
         "inv2d": yh + n_out,
         "fused2d": n_in + wb + n_out,
         "fused1d": n_in + wb + n_out,
+        # backward pass: the weight gradient reads both truncated spectra and
+        # writes a weight-sized gradient; the adjoint transposes the weight
+        "wgrad": xh + yh + wb,
+        "wadjoint": 2 * wb,
+        # sum of the batch splits' partial weight gradients (when the batch
+        # is split): counted as its one compulsory write
+        "wgrad_reduce": wb,
     }
-    return table[name]
+    return table[name.split(":")[0]]
 
 
 def load_traffic(kernel: str, workload: str):
@@ -101,8 +115,9 @@ def load_traffic(kernel: str, workload: str):
         return None
 
 
-def cpu_baseline(cfg, x, w, budget_s: float = 12.0):
-    """Time the fp64 oracle (as it stands) on this host on a bounded sample."""
+def cpu_baseline(cfg, x, w, budget_s: float = 12.0, g=None, compulsory=None):
+    """Time the fp64 oracle (as it stands) on this host on a bounded sample
+    (the backward pass when the output gradient g is given)."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -111,6 +126,10 @@ def cpu_baseline(cfg, x, w, budget_s: float = 12.0):
         threads = 1
     # one batch item first, to size the sample
     def call(nb):
+        if g is not None:
+            if cfg.kind == "1d":
+                return oracle.spectral_conv1d_backward_ref(x[:nb], w, g[:nb], cfg.my)
+            return oracle.spectral_conv2d_backward_ref(x[:nb], w, g[:nb], cfg.mx, cfg.my)
         if cfg.kind == "1d":
             return oracle.spectral_conv1d_ref(x[:nb], w, cfg.my)
         return oracle.spectral_conv2d_ref(x[:nb], w, cfg.mx, cfg.my)
@@ -130,7 +149,7 @@ def cpu_baseline(cfg, x, w, budget_s: float = 12.0):
     per_item = el / (reps * nb)
     call_time = per_item * cfg.B
     return {
-        "value": round(cfg.compulsory_bytes / call_time / 1e9, 6),
+        "value": round((compulsory or cfg.compulsory_bytes) / call_time / 1e9, 6),
         "unit": "GB/s",
         "cores": int(threads),
         "kind": "oracle",
@@ -149,6 +168,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="c3", choices=sorted(CONFIGS))
     ap.add_argument("--variant", default="fused", choices=["fused", "unfused"])
+    ap.add_argument("--pass", dest="which", default="forward", choices=["forward", "backward"],
+                    help="time the operator (default) or its backward pass (both gradients)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -189,7 +210,25 @@ def main():
     outs = [torch.empty(cfg.out_shape, dtype=torch.float32, device=dev) for _ in range(nsets)]
     w = torch.from_numpy(w_np).to(dev)
 
-    if cfg.kind == "1d":
+    compulsory = cfg.compulsory_bytes
+    g_np = None
+    if args.which == "backward":
+        # step: both gradients of a real loss, given a synthetic dL/dout of the
+        # output's shape; compulsory bytes: x, w, dL/dout read, dL/dx, dL/dw written
+        g_np = np.random.default_rng(1).uniform(-1.0, 1.0, size=cfg.out_shape).astype(np.float32)
+        gs = [torch.from_numpy(g_np).to(dev)]
+        for _ in range(nsets - 1):
+            gs.append(gs[0].clone())
+        compulsory = 2 * int(x_np.nbytes) + 2 * int(w_np.nbytes) + int(g_np.nbytes)
+        gxs = [torch.empty_like(xs[0]) for _ in range(nsets)]
+        gw = torch.empty_like(w)
+        if cfg.kind == "1d":
+            step = lambda i: fno.fno_spectral_conv1d_backward(xs[i % nsets], w, gs[i % nsets], cfg.my,
+                                                              grad_x=gxs[i % nsets], grad_w=gw)
+        else:
+            step = lambda i: fno.fno_spectral_conv2d_backward(xs[i % nsets], w, gs[i % nsets], cfg.mx, cfg.my,
+                                                              grad_x=gxs[i % nsets], grad_w=gw)
+    elif cfg.kind == "1d":
         fn = fno.fno_spectral_conv1d if args.variant == "fused" else fno.fno_spectral_conv1d_unfused
         step = lambda i: fn(xs[i % nsets], w, cfg.my, out=outs[i % nsets])
     else:
@@ -201,6 +240,12 @@ def main():
         step(i)
     torch.cuda.synchronize()
     kernels = fno.fno_last_kernels()
+    # a kernel that runs more than once per step gets its launch number
+    seen = {}
+    for j, k in enumerate(kernels):
+        seen[k] = seen.get(k, 0) + 1
+        if seen[k] > 1:
+            kernels[j] = f"{k}:{seen[k]}"
     nk = len(kernels)
     # start / stop events that every kernel of every timed step launches with
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * nk)] for _ in range(args.steps)]
@@ -235,11 +280,16 @@ def main():
     spans_us = [evs[i][0].elapsed_time(evs[i][2 * nk - 1]) * 1e3 for i in range(args.steps)]
     dom = int(np.argmax(per_kernel_ms))
     dom_name = kernels[dom]
-    dom_bytes = kernel_bytes(dom_name, cfg)
+    dom_bytes = kernel_bytes(dom_name, cfg, args.which == "backward")
     achieved = dom_bytes / (per_kernel_ms[dom] * 1e-3) / 1e9
-    traffic = load_traffic(dom_name, cfg.name)
+    traffic = load_traffic(dom_name, cfg.name if args.which == "forward" else cfg.name + "/backward")
 
-    gbs = cfg.compulsory_bytes / (ms_per_step * 1e-3) / 1e9
+    gbs = compulsory / (ms_per_step * 1e-3) / 1e9
+    # bytes of all buffers the timed steps touch (the backward adds dL/dx per
+    # set and dL/dw)
+    touched = nsets * set_bytes + w_np.nbytes
+    if args.which == "backward":
+        touched += nsets * x_np.nbytes + w_np.nbytes
     line = {
         "metric": "spectral-conv GB/s (HBM % of peak) and layer calls/s vs fp64 CPU oracle",
         "value": round(gbs, 3),
@@ -256,12 +306,13 @@ def main():
         "config": {
             "workload": f"{cfg.name}: {cfg.describe()}",
             "variant": args.variant,
+            "pass": args.which,
             "x_dist": cfg.dist,
-            "compulsory_bytes": cfg.compulsory_bytes,
+            "compulsory_bytes": compulsory,
             "buffer_sets": nsets,
             # every buffer a step touches fits the 256 MiB last-level cache:
             # the GB/s figure is then not an HBM rate
-            "cache_resident": bool(nsets * set_bytes + w_np.nbytes <= 256 * 2**20),
+            "cache_resident": bool(touched <= 256 * 2**20),
         },
         "calls_per_s": round(1e3 / ms_per_step, 3),
         "hbm_pct": round(100.0 * gbs / HBM_PEAK_GBS, 3),
@@ -282,7 +333,7 @@ def main():
             "avg_launch_us": round(per_kernel_ms[dom] * 1e3, 3),
         },
     }
-    if "mix_mfma" in kernels:
+    if "mix_mfma" in kernels and args.which == "forward":
         # the matrix-core stage against the fp32 MFMA peak: executed flops of
         # the 3M form (three real GEMMs, 2 flops per multiply-add), and the
         # algorithmic count of 8 flops per complex multiply-add
@@ -302,7 +353,7 @@ def main():
             "avg_launch_us": round(per_kernel_ms[k] * 1e3, 3),
         }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(cfg, x_np, w_np, args.cpu_budget)
+        line["cpu_baseline"] = cpu_baseline(cfg, x_np, w_np, args.cpu_budget, g=g_np, compulsory=compulsory)
     print(json.dumps(line), flush=True)
 
 

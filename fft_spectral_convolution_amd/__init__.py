@@ -259,7 +259,7 @@ def fno_spectral_conv1d_ws(x, w, modes: int, workspace, out=None):
     return out
 
 
-def _grad_outputs(x, w, grad_out, need_x, need_w, out_shape):
+def _grad_outputs(x, w, grad_out, need_x, need_w, out_shape, grad_x, grad_w):
     torch = _torch()
     if not (need_x or need_w):
         raise ValueError("ask for at least one of the two gradients")
@@ -268,17 +268,28 @@ def _grad_outputs(x, w, grad_out, need_x, need_w, out_shape):
         raise ValueError(f"grad_out has shape {tuple(grad_out.shape)}, expected {out_shape}")
     if grad_out.device != x.device:
         raise ValueError("grad_out must be on the device of x")
-    gx = torch.empty_like(x) if need_x else None
-    gw = torch.empty_like(w) if need_w else None
+
+    def target(given, like, name):
+        if given is None:
+            return torch.empty_like(like)
+        _need(given, like.dtype, like.dim(), name)
+        if given.shape != like.shape or given.device != like.device:
+            raise ValueError(f"{name} must match {tuple(like.shape)} on {like.device}")
+        return given
+
+    gx = target(grad_x, x, "grad_x") if need_x else None
+    gw = target(grad_w, w, "grad_w") if need_w else None
     return gx, gw
 
 
-def fno_spectral_conv2d_backward(x, w, grad_out, mx: int, my: int, need_x: bool = True, need_w: bool = True):
+def fno_spectral_conv2d_backward(x, w, grad_out, mx: int, my: int, need_x: bool = True, need_w: bool = True,
+                                 grad_x=None, grad_w=None):
     """Gradients (grad_x[B,Cin,H,W] f32, grad_w[2,mx,my,Cin,Cout] c64) of a real loss
     through fno_spectral_conv2d, given grad_out = dL/dout; grad_w = dL/dRe w + i dL/dIm w.
-    A gradient not asked for is returned as None."""
+    A gradient not asked for is returned as None; grad_x / grad_w, when given,
+    are written in place of new tensors."""
     _, (b, cin, cout, h, wd) = _conv2d_args(x, w, mx, my, grad_out)
-    gx, gw = _grad_outputs(x, w, grad_out, need_x, need_w, (b, cout, h, wd))
+    gx, gw = _grad_outputs(x, w, grad_out, need_x, need_w, (b, cout, h, wd), grad_x, grad_w)
     nullp = ctypes.c_void_p(0)
     with _on_device(x):
         _check(lib().fno_spectral_conv2d_backward(_ptr(x), _ptr(w), _ptr(grad_out),
@@ -289,10 +300,11 @@ def fno_spectral_conv2d_backward(x, w, grad_out, mx: int, my: int, need_x: bool 
     return gx, gw
 
 
-def fno_spectral_conv1d_backward(x, w, grad_out, modes: int, need_x: bool = True, need_w: bool = True):
+def fno_spectral_conv1d_backward(x, w, grad_out, modes: int, need_x: bool = True, need_w: bool = True,
+                                 grad_x=None, grad_w=None):
     """Gradients (grad_x[B,Cin,N] f32, grad_w[modes,Cin,Cout] c64) through fno_spectral_conv1d."""
     _, (b, cin, cout, n) = _conv1d_args(x, w, modes, grad_out)
-    gx, gw = _grad_outputs(x, w, grad_out, need_x, need_w, (b, cout, n))
+    gx, gw = _grad_outputs(x, w, grad_out, need_x, need_w, (b, cout, n), grad_x, grad_w)
     nullp = ctypes.c_void_p(0)
     with _on_device(x):
         _check(lib().fno_spectral_conv1d_backward(_ptr(x), _ptr(w), _ptr(grad_out),

@@ -423,8 +423,8 @@ int check_backward(const float* x, const void* w, const float* g, const float* g
 struct BackwardPlan {
     bool small;
     SpecLayout lx, lg;
-    size_t r_bytes, x_bytes, g_bytes, z_bytes, wt_bytes;
-    size_t total() const { return r_bytes + x_bytes + g_bytes + z_bytes + wt_bytes; }
+    size_t r_bytes, x_bytes, g_bytes, z_bytes, wt_bytes, wg_bytes;
+    size_t total() const { return r_bytes + x_bytes + g_bytes + z_bytes + wt_bytes + wg_bytes; }
 };
 
 BackwardPlan backward_plan_2d(const Shape2d& s) {
@@ -440,6 +440,7 @@ BackwardPlan backward_plan_2d(const Shape2d& s) {
     p.g_bytes = align_up((size_t)layout_elems(p.lg, s.B) * sizeof(float2));
     p.z_bytes = p.x_bytes;
     p.wt_bytes = align_up((size_t)m * s.Cin * s.Cout * sizeof(float2));
+    p.wg_bytes = align_up(weight_grad_workspace(s.B, s.Cin, s.Cout, m));
     return p;
 }
 
@@ -457,6 +458,8 @@ int run_backward_2d(const Shape2d& s, const float* x, const float2* w, const flo
     float2* zh = reinterpret_cast<float2*>(q);
     q += p.z_bytes;
     float2* wt = reinterpret_cast<float2*>(q);
+    q += p.wt_bytes;
+    void* wg_ws = q;
     auto forward = [&](int64_t C, const float* in, float2* out_h, const SpecLayout& lay) {
         return p.small ? run_forward2d_small(s, C, in, out_h, lay, tw, st)
                        : run_forward2d_staged(s, C, in, out_h, r, tw, st);
@@ -467,8 +470,15 @@ int run_backward_2d(const Shape2d& s, const float* x, const float2* w, const flo
         rc = forward(s.Cin, x, xh, p.lx);
         if (rc) return rc;
         rec_kernel("wgrad", st);
-        hipError_t e = launch_weight_grad(xh, p.lx, gh, p.lg, gw, s.B, s.Cin, s.Cout, m, s.my, s.W / 2, st);
+        int splits = 1;
+        hipError_t e = launch_weight_grad(xh, p.lx, gh, p.lg, gw, s.B, s.Cin, s.Cout, m, s.my, s.W / 2, wg_ws,
+                                          p.wg_bytes, &splits, st);
         if (e != hipSuccess) return hip_fail(e);
+        if (splits > 1) {
+            rec_kernel("wgrad_reduce", st);
+            e = launch_weight_grad_reduce(wg_ws, gw, s.Cin, s.Cout, m, splits, s.my, s.W / 2, st);
+            if (e != hipSuccess) return hip_fail(e);
+        }
     }
     if (gx) {
         rec_kernel("wadjoint", st);
@@ -519,17 +529,19 @@ int backward1d_common(const float* x, const void* w, const float* g, float* gx, 
     const size_t xb = align_up((size_t)B * Cin * modes * sizeof(float2));
     const size_t gb = align_up((size_t)B * Cout * modes * sizeof(float2));
     const size_t wtb = align_up((size_t)modes * Cin * Cout * sizeof(float2));
+    const size_t wgb = align_up(weight_grad_workspace(B, Cin, Cout, modes));
     DeviceState* st = nullptr;
     rc = device_state(&st);
     if (rc) return rc;
     void* ws = nullptr;
-    rc = internal_workspace(st, 2 * xb + gb + wtb, &ws);
+    rc = internal_workspace(st, 2 * xb + gb + wtb + wgb, &ws);
     if (rc) return rc;
     char* q = static_cast<char*>(ws);
     float2* xh = reinterpret_cast<float2*>(q);
     float2* zh = reinterpret_cast<float2*>(q + xb);
     float2* gh = reinterpret_cast<float2*>(q + 2 * xb);
     float2* wt = reinterpret_cast<float2*>(q + 2 * xb + gb);
+    void* wg_ws = q + 2 * xb + gb + wtb;
     const SpecLayout lx = canonical_layout(Cin, modes), lg = canonical_layout(Cout, modes);
     const float scale = (float)(1.0 / std::sqrt((double)N));
     const int l2 = ilog2(N);
@@ -544,8 +556,16 @@ int backward1d_common(const float* x, const void* w, const float* g, float* gx, 
             e = launch_rows_fwd(x, xh, (int64_t)B * Cin, l2, modes, modes, scale, st->twiddle, hs);
             if (e != hipSuccess) return hip_fail(e);
             rec_kernel("wgrad", hs);
-            e = launch_weight_grad(xh, lx, gh, lg, static_cast<float2*>(gw), B, Cin, Cout, modes, modes, N / 2, hs);
+            int splits = 1;
+            e = launch_weight_grad(xh, lx, gh, lg, static_cast<float2*>(gw), B, Cin, Cout, modes, modes, N / 2, wg_ws,
+                                   wgb, &splits, hs);
             if (e != hipSuccess) return hip_fail(e);
+            if (splits > 1) {
+                rec_kernel("wgrad_reduce", hs);
+                e = launch_weight_grad_reduce(wg_ws, static_cast<float2*>(gw), Cin, Cout, modes, splits, modes,
+                                              N / 2, hs);
+                if (e != hipSuccess) return hip_fail(e);
+            }
         }
         if (gx) {
             rec_kernel("wadjoint", hs);

@@ -123,8 +123,14 @@ hipError_t launch_rows_inv(const float2* y, float* out, int64_t nrows, int log2W
 hipError_t launch_weight_adjoint(const float2* w, float2* wt, int64_t M, int64_t Cin, int64_t Cout, hipStream_t s);
 // gw[m][i][o] = c_m sum_b conj(xh(b, i, m)) gh(b, o, m), c_m = 1 when
 // ky = m mod my is 0 or nyq, 2 otherwise (spectra addressed by layouts).
+// When the batch is split (*splits > 1 on return) the partial sums are left
+// in ws (weight_grad_workspace bytes) and launch_weight_grad_reduce must
+// follow to write gw.
+size_t weight_grad_workspace(int64_t B, int64_t Cin, int64_t Cout, int64_t M);
 hipError_t launch_weight_grad(const float2* xh, const SpecLayout& lx, const float2* gh, const SpecLayout& lg,
-                              float2* gw, int64_t B, int64_t Cin, int64_t Cout, int64_t M, int my, int nyq,
-                              hipStream_t s);
+                              float2* gw, int64_t B, int64_t Cin, int64_t Cout, int64_t M, int my, int nyq, void* ws,
+                              size_t ws_bytes, int* splits, hipStream_t s);
+hipError_t launch_weight_grad_reduce(const void* ws, float2* gw, int64_t Cin, int64_t Cout, int64_t M, int splits,
+                                     int my, int nyq, hipStream_t s);
 
 }  // namespace fno

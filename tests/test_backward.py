@@ -75,6 +75,7 @@ BACKWARD_2D = [
     (1, 2, 3, 256, 256, 9, 11),     # staged generic transforms
     (1, 2, 3, 16, 1024, 5, 50),     # pruned long rows
     (1, 2, 2, 1024, 16, 8, 9),      # pruned columns
+    (9, 16, 24, 64, 64, 8, 8),      # weight-gradient tiles of 16 x 32 channels
 ]
 
 
@@ -89,6 +90,8 @@ BACKWARD_1D = [
     (3, 2, 5, 16, 9),               # every bin kept (Nyquist bin)
     (5, 3, 2, 512, 64),             # pruned rows
     (2, 16, 32, 4096, 64),          # longest rows, matrix-core mix both ways
+    (37, 20, 40, 256, 13),          # weight gradient: batch split in two, odd chunk counts, modes not a multiple of 8
+    (300, 8, 8, 128, 16),           # weight gradient: 19 uneven batch splits, ragged last chunk
 ]
 
 
