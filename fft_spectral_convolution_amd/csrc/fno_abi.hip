@@ -209,6 +209,24 @@ int run_mix(const float2* xh, const SpecLayout& lx, const float2* w, float2* yh,
     return e == hipSuccess ? FNO_OK : hip_fail(e);
 }
 
+// zh(b, i, m) = sum_o gh(b, o, m) conj(w[m][i][o]) (the adjoint mix of the
+// backward pass, w the forward weight [m][Cz][Cg]): on the matrix cores with
+// the weight read transposed where supported, else through an explicit
+// conjugate transpose into wt and the plain mix.
+int run_mix_adjoint(const float2* gh, const SpecLayout& lg, const float2* w, float2* wt, float2* zh,
+                    const SpecLayout& lz, int64_t B, int64_t Cg, int64_t Cz, int64_t M, hipStream_t st) {
+    hipError_t e;
+    if (use_mfma_mix(B, Cg, Cz) && mix_mfma_adjoint_supported(gh, lg, w, zh, lz, Cg, M)) {
+        rec_kernel("mix_mfma_adj", st);
+        e = launch_mix_mfma(gh, lg, w, zh, lz, B, Cg, Cz, M, st, true);
+        return e == hipSuccess ? FNO_OK : hip_fail(e);
+    }
+    rec_kernel("wadjoint", st);
+    e = launch_weight_adjoint(w, wt, M, Cz, Cg, st);
+    if (e != hipSuccess) return hip_fail(e);
+    return run_mix(gh, lg, wt, zh, lz, B, Cg, Cz, M, st);
+}
+
 bool small_path(const Shape2d& s) { return small2d_supported(s.log2H, s.log2W, s.my); }
 
 // Staged (unfused) transforms: rows and columns as separate kernels, the row
@@ -481,10 +499,7 @@ int run_backward_2d(const Shape2d& s, const float* x, const float2* w, const flo
         }
     }
     if (gx) {
-        rec_kernel("wadjoint", st);
-        hipError_t e = launch_weight_adjoint(w, wt, m, s.Cin, s.Cout, st);
-        if (e != hipSuccess) return hip_fail(e);
-        rc = run_mix(gh, p.lg, wt, zh, p.lx, s.B, s.Cout, s.Cin, m, st);
+        rc = run_mix_adjoint(gh, p.lg, w, wt, zh, p.lx, s.B, s.Cout, s.Cin, m, st);
         if (rc) return rc;
         rc = p.small ? run_inverse2d_small(s, s.Cin, zh, gx, p.lx, tw, st)
                      : run_inverse2d_staged(s, s.Cin, zh, gx, r, tw, st);
@@ -568,10 +583,7 @@ int backward1d_common(const float* x, const void* w, const float* g, float* gx, 
             }
         }
         if (gx) {
-            rec_kernel("wadjoint", hs);
-            e = launch_weight_adjoint(wc, wt, modes, Cin, Cout, hs);
-            if (e != hipSuccess) return hip_fail(e);
-            const int mrc = run_mix(gh, lg, wt, zh, lx, B, Cout, Cin, modes, hs);
+            const int mrc = run_mix_adjoint(gh, lg, wc, wt, zh, lx, B, Cout, Cin, modes, hs);
             if (mrc) return mrc;
             rec_kernel("rows_inv", hs);
             e = launch_rows_inv(zh, gx, (int64_t)B * Cin, l2, modes, modes, scale, st->twiddle, hs);

@@ -75,9 +75,16 @@ hipError_t launch_inv2d_rowreg(const float2* yh, float* out, const SpecLayout& l
 // ---- channel mix on MFMA (fno_mix.hip) --------------------------------------
 // yh(b, o, m) = sum_i xh(b, i, m) * w[m][i][o], spectra addressed by layouts.
 // Needs an even Cout, a 16-byte aligned w (float4 weight pairs) and Cin <= 128.
+// adjoint: yh(b, o, m) = sum_i xh(b, i, m) * conj(w[m][o][i]) instead (the
+// weight of the forward layer, read transposed); needs an even Cin, Cin <=
+// 128, a 16-byte aligned w and spectra with whole, aligned 8-mode runs
+// (mix_mfma_adjoint_supported).
 bool mix_mfma_supported(int64_t Cin, int64_t Cout, const void* w);
+bool mix_mfma_adjoint_supported(const float2* xh, const SpecLayout& lx, const float2* w, const float2* yh,
+                                const SpecLayout& ly, int64_t Cin, int64_t M);
 hipError_t launch_mix_mfma(const float2* xh, const SpecLayout& lx, const float2* w, float2* yh,
-                           const SpecLayout& ly, int64_t B, int64_t Cin, int64_t Cout, int64_t M, hipStream_t s);
+                           const SpecLayout& ly, int64_t B, int64_t Cin, int64_t Cout, int64_t M, hipStream_t s,
+                           bool adjoint = false);
 
 // ---- pruned long-row transforms (fno_rows_pruned.hip) ------------------------
 // Rows of W = 2^log2W real points, W in [512, 4096], bins ky < my <= 64:

@@ -25,6 +25,14 @@
 // outstanding loads exactly), and a tile's results leave through LDS in
 // 32-byte runs while the next tile's first chunks are already in flight.
 // Rows, channels and modes past the ends are masked.
+//
+// TW (the adjoint mix of the backward pass): the B operand is the
+// conjugate transpose of the stored weight, conj(W_m[o][i]) with W stored
+// [m][Cout][Cin] (the forward weight of the layer whose input gradient is
+// computed).  Each lane then reads its column's weight row along the
+// contraction, as float4 pairs (k, k + 1): within a chunk, k-step s of lane
+// group lk contracts channel 2 lk + s (the staged X chunk is read with the
+// same order), and column block cb holds o = 16 cb + l16.
 #include "fno_device.hpp"
 #include "fno_internal.hpp"
 
@@ -70,7 +78,7 @@ __device__ __forceinline__ Tile tile_of(const TileGrid& tg, int t) {
 // layout), so X is read and Y written as float4; otherwise element-wise.
 // NCH: chunks of input channels per tile (even; chunks past Cin are zero).
 // NCB: 16-column MFMA blocks per tile (2 or 4); RB: 16-row blocks (1 or 2).
-template <int NCH, bool VEC, int NCB, int RB>
+template <int NCH, bool VEC, int NCB, int RB, bool TW>
 __global__ __launch_bounds__(kMixThreads) void k_mix_mfma(const float2* __restrict__ xh, Addr ax,
                                                           const float2* __restrict__ w, float2* __restrict__ yh,
                                                           Addr ay, int B, int Cin, int Cout, int M, TileGrid tg) {
@@ -137,6 +145,22 @@ __global__ __launch_bounds__(kMixThreads) void k_mix_mfma(const float2* __restri
     // columns past Cout are clamped and never stored).
     auto load_w = [&](const Tile& tl, int chunk, float2 (&wv)[2 * NCB]) __attribute__((always_inline)) {
         const int mw = tl.m0 + wave < M ? tl.m0 + wave : M - 1;
+        if constexpr (TW) {
+            // conj(W[o][k]), k = chunk * 8 + 2 lk + s: one float4 per column
+            // block (Cin is even on this path; pairs past it are clamped and
+            // meet zeroed X channels)
+            int k = chunk * kMixKC + 2 * lk;
+            k = k < Cin ? k : Cin - 2;
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb) {
+                int o = tl.o0 + 16 * cb + l16;
+                o = o < Cout ? o : Cout - 1;
+                const float4 v = *reinterpret_cast<const float4*>(w + ((int64_t)mw * Cout + o) * Cin + k);
+                wv[cb] = make_float2(v.x, -v.y);
+                wv[NCB + cb] = make_float2(v.z, -v.w);
+            }
+            return;
+        }
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
             const int i = chunk * kMixKC + 4 * s + lk;
@@ -159,7 +183,7 @@ __global__ __launch_bounds__(kMixThreads) void k_mix_mfma(const float2* __restri
             float2 a[RB];
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb) {
-                const int i = 4 * s + lk;
+                const int i = TW ? 2 * lk + s : 4 * s + lk;
                 a[rb] = buf[i * kAI + wave * kAM + ((16 * rb + l16) ^ (2 * (i >> 1)))];
             }
 #pragma unroll
@@ -196,10 +220,16 @@ __global__ __launch_bounds__(kMixThreads) void k_mix_mfma(const float2* __restri
                         yv[2 * cb] = pr - pi;
                         yv[2 * cb + 1] = p3[rb][cb][r] - pr - pi;
                     }
+                    if constexpr (TW) {
 #pragma unroll
-                    for (int h = 0; h < NCB / 2; ++h)
-                        *reinterpret_cast<float4*>(y_lds + (bl * 8 + wave) * kYS + 32 * h + 2 * l16) =
-                            make_float4(yv[4 * h], yv[4 * h + 1], yv[4 * h + 2], yv[4 * h + 3]);
+                        for (int cb = 0; cb < NCB; ++cb)
+                            y_lds[(bl * 8 + wave) * kYS + 16 * cb + l16] = make_float2(yv[2 * cb], yv[2 * cb + 1]);
+                    } else {
+#pragma unroll
+                        for (int h = 0; h < NCB / 2; ++h)
+                            *reinterpret_cast<float4*>(y_lds + (bl * 8 + wave) * kYS + 32 * h + 2 * l16) =
+                                make_float4(yv[4 * h], yv[4 * h + 1], yv[4 * h + 2], yv[4 * h + 3]);
+                    }
                 }
             }
             lds_barrier();
@@ -289,12 +319,12 @@ __global__ __launch_bounds__(kMixThreads) void k_mix_mfma(const float2* __restri
     }
 }
 
-template <bool VEC, int NCB, int RB>
+template <bool VEC, int NCB, int RB, bool TW = false>
 hipError_t launch_mix_variant(dim3 grid, hipStream_t s, const float2* xh, Addr ax, const float2* w, float2* yh, Addr ay,
                         int B, int Cin, int Cout, int M, TileGrid tg, int nch) {
 #define CASE(N)                                                                                                   \
     case N:                                                                                                       \
-        return launch_kernel((k_mix_mfma<N, VEC, NCB, RB>), grid, dim3(kMixThreads), 0, s, xh, ax, w, yh, ay, B, Cin, \
+        return launch_kernel((k_mix_mfma<N, VEC, NCB, RB, TW>), grid, dim3(kMixThreads), 0, s, xh, ax, w, yh, ay, B, Cin, \
                            Cout, M, tg);
     switch (nch) {
         CASE(2) CASE(4) CASE(6) CASE(8)
@@ -315,22 +345,33 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 // Chunks of 8 input channels, rounded up to an even count.
 int64_t mix_chunks(int64_t Cin) { return ((Cin + kMixKC - 1) / kMixKC + 1) / 2 * 2; }
 
+// float4 access needs every 8-mode run whole and 16-byte aligned: the tiled
+// layout has it, the canonical one when M is a multiple of 8 (all strides
+// even, 16-byte aligned bases).
+bool mix_vec(const float2* xh, const SpecLayout& lx, const float2* yh, const SpecLayout& ly, int64_t M) {
+    return lx.sc % 2 == 0 && ly.sc % 2 == 0 && lx.st % 2 == 0 && ly.st % 2 == 0 && lx.sb % 2 == 0 &&
+           ly.sb % 2 == 0 && M % 8 == 0 && aligned16(xh) && aligned16(yh);
+}
+
 }  // namespace
 
 bool mix_mfma_supported(int64_t Cin, int64_t Cout, const void* w) {
     return Cout % 2 == 0 && aligned16(w) && mix_chunks(Cin) <= 16;
 }
 
+bool mix_mfma_adjoint_supported(const float2* xh, const SpecLayout& lx, const float2* w, const float2* yh,
+                                const SpecLayout& ly, int64_t Cin, int64_t M) {
+    return Cin % 2 == 0 && aligned16(w) && mix_chunks(Cin) <= 16 && mix_vec(xh, lx, yh, ly, M);
+}
+
 hipError_t launch_mix_mfma(const float2* xh, const SpecLayout& lx, const float2* w, float2* yh, const SpecLayout& ly,
-                           int64_t B, int64_t Cin, int64_t Cout, int64_t M, hipStream_t s) {
-    if (!mix_mfma_supported(Cin, Cout, w)) return hipErrorInvalidValue;
+                           int64_t B, int64_t Cin, int64_t Cout, int64_t M, hipStream_t s, bool adjoint) {
+    if (adjoint ? !mix_mfma_adjoint_supported(xh, lx, w, yh, ly, Cin, M) : !mix_mfma_supported(Cin, Cout, w))
+        return hipErrorInvalidValue;
     int dev = 0, cus = 0;
     if (hipGetDevice(&dev) != hipSuccess) return hipErrorInvalidDevice;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
-    // float4 access needs every 8-mode run whole and 16-byte aligned: the
-    // tiled layout (runs of exactly 8 in a 256-byte aligned workspace) has it.
-    const bool vec = lx.sc == 8 && ly.sc == 8 && lx.st % 2 == 0 && ly.st % 2 == 0 && lx.sb % 2 == 0 &&
-                     ly.sb % 2 == 0 && M % 8 == 0 && aligned16(xh) && aligned16(yh);
+    const bool vec = mix_vec(xh, lx, yh, ly, M);
     const int nch = (int)mix_chunks(Cin);
     // Tile shape: 32 batch rows unless B fits 16 or 32-row tiles would leave
     // CUs without one; 64 output channels when Cout needs more than 32 and
@@ -356,6 +397,12 @@ hipError_t launch_mix_mfma(const float2* xh, const SpecLayout& lx, const float2*
     const Addr ay{ly.sb, ly.sc, ly.st};
     const dim3 grid((unsigned)g);
     const int iB = (int)B, iCin = (int)Cin, iCout = (int)Cout, iM = (int)M;
+    if (adjoint) {                       // float4 access (vec) on this path
+        if (wide && !short_b) return launch_mix_variant<true, 4, 2, true>(grid, s, xh, ax, w, yh, ay, iB, iCin, iCout, iM, tg, nch);
+        if (wide) return launch_mix_variant<true, 4, 1, true>(grid, s, xh, ax, w, yh, ay, iB, iCin, iCout, iM, tg, nch);
+        if (!short_b) return launch_mix_variant<true, 2, 2, true>(grid, s, xh, ax, w, yh, ay, iB, iCin, iCout, iM, tg, nch);
+        return launch_mix_variant<true, 2, 1, true>(grid, s, xh, ax, w, yh, ay, iB, iCin, iCout, iM, tg, nch);
+    }
     if (wide && !short_b) return launch_mix_variant<true, 4, 2>(grid, s, xh, ax, w, yh, ay, iB, iCin, iCout, iM, tg, nch);
     if (wide) return launch_mix_variant<true, 4, 1>(grid, s, xh, ax, w, yh, ay, iB, iCin, iCout, iM, tg, nch);
     if (vec && !short_b) return launch_mix_variant<true, 2, 2>(grid, s, xh, ax, w, yh, ay, iB, iCin, iCout, iM, tg, nch);

@@ -75,7 +75,8 @@ BACKWARD_2D = [
     (1, 2, 3, 256, 256, 9, 11),     # staged generic transforms
     (1, 2, 3, 16, 1024, 5, 50),     # pruned long rows
     (1, 2, 2, 1024, 16, 8, 9),      # pruned columns
-    (9, 16, 24, 64, 64, 8, 8),      # weight-gradient tiles of 16 x 32 channels
+    (9, 16, 24, 64, 64, 8, 8),      # weight-gradient tiles of 16 x 32 channels; adjoint mix, ragged channel chunk
+    (12, 18, 21, 32, 32, 8, 8),     # odd Cout: explicit weight adjoint, then the plain matrix-core mix
 ]
 
 
