@@ -74,6 +74,7 @@ def kernel_bytes(name: str, cfg, backward: bool = False) -> int:
         "cols_fwd": r_in + xh,
         "mix_valu": xh + wb + yh,
         "mix_mfma": xh + wb + yh,
+        "mix_mfma_adj": xh + wb + yh,
         "cols_inv": yh + r_out,
         "rows_inv": (r_out if cfg.kind == "2d" else yh) + n_out,
         "fwd2d": n_in + xh,

@@ -295,12 +295,25 @@ struct WgPlan {
 
 WgPlan weight_grad_plan(int64_t B, int64_t Cin, int64_t Cout, int64_t M, int cus) {
     WgPlan p;
-    p.ri = Cin > 16 ? 2 : 1;
-    p.ncb = Cout > 32 ? 4 : (Cout > 16 ? 2 : 1);
-    p.grid.n_it = (int)((Cin + 16 * p.ri - 1) / (16 * p.ri));
-    p.grid.n_ot = (int)((Cout + 16 * p.ncb - 1) / (16 * p.ncb));
+    // tile shape: the largest (fewest re-reads of X and G) that still gives
+    // every CU a tile, else the smallest, with the batch split below.  The
+    // 32 x 32 tiles run two workgroups per CU (66 KiB of LDS each), which
+    // overlaps one tile's result writes with another's loads; measured, that
+    // beats 32 x 64 tiles (one workgroup per CU) at 128x128 with 64 channels.
+    const int ri_max = Cin > 16 ? 2 : 1;
+    const int ncb_max = Cout > 16 ? 2 : 1;
+    static const int kShapes[3][2] = {{2, 2}, {1, 2}, {1, 1}};
+    int64_t tiles = 0;
+    for (const auto& sh : kShapes) {
+        if (sh[0] > ri_max || sh[1] > ncb_max) continue;
+        p.ri = sh[0];
+        p.ncb = sh[1];
+        p.grid.n_it = (int)((Cin + 16 * p.ri - 1) / (16 * p.ri));
+        p.grid.n_ot = (int)((Cout + 16 * p.ncb - 1) / (16 * p.ncb));
+        tiles = (M + 7) / 8 * p.grid.n_it * p.grid.n_ot;
+        if (tiles >= cus) break;
+    }
     p.grid.nch = (int)((B + kWgKB - 1) / kWgKB);
-    const int64_t tiles = (M + 7) / 8 * p.grid.n_it * p.grid.n_ot;
     // split the batch when the tiles leave CUs idle, keeping two chunks per split
     int64_t splits = tiles >= cus ? 1 : (cus + tiles - 1) / tiles;
     const int64_t max_splits = p.grid.nch / 2 > 1 ? p.grid.nch / 2 : 1;
@@ -361,13 +374,8 @@ hipError_t launch_weight_grad(const float2* xh, const SpecLayout& lx, const floa
     float2* out = p.grid.splits > 1 ? static_cast<float2*>(ws) : gw;
     const dim3 grid((unsigned)p.units);
     const int iB = (int)B, iCin = (int)Cin, iCout = (int)Cout, iM = (int)M;
-    if (p.ri == 2) {
-        return p.ncb == 4 ? launch_wg<2, 4>(vec, grid, s, xh, ax, gh, ag, out, iB, iCin, iCout, iM, my, nyq, p.grid)
-             : p.ncb == 2 ? launch_wg<2, 2>(vec, grid, s, xh, ax, gh, ag, out, iB, iCin, iCout, iM, my, nyq, p.grid)
-                          : launch_wg<2, 1>(vec, grid, s, xh, ax, gh, ag, out, iB, iCin, iCout, iM, my, nyq, p.grid);
-    }
-    return p.ncb == 4 ? launch_wg<1, 4>(vec, grid, s, xh, ax, gh, ag, out, iB, iCin, iCout, iM, my, nyq, p.grid)
-         : p.ncb == 2 ? launch_wg<1, 2>(vec, grid, s, xh, ax, gh, ag, out, iB, iCin, iCout, iM, my, nyq, p.grid)
+    if (p.ri == 2) return launch_wg<2, 2>(vec, grid, s, xh, ax, gh, ag, out, iB, iCin, iCout, iM, my, nyq, p.grid);
+    return p.ncb == 2 ? launch_wg<1, 2>(vec, grid, s, xh, ax, gh, ag, out, iB, iCin, iCout, iM, my, nyq, p.grid)
                       : launch_wg<1, 1>(vec, grid, s, xh, ax, gh, ag, out, iB, iCin, iCout, iM, my, nyq, p.grid);
 }
 
