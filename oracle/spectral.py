@@ -39,6 +39,13 @@ upcast exactly):
    Gh the truncated forward transform of g (derived below
    ``spectral_conv2d_backward_ref``; pinned by the adjoint identity and the
    exact change of the loss under weight perturbations).
+7. fused layer tail (P2 sections 5.1-5.2: the C2R output is activated with
+   GELU and added to a second, time-domain branch; section 6.2: fuse what
+   follows the C2R into the same kernel):
+     branch before the activation:  out = gelu(conv + bias[o] + branch)
+     branch after the activation:   out = gelu(conv + bias[o]) + branch
+   gelu(u) = u Phi(u) = u (1 + erf(u / sqrt 2)) / 2, the exact form (the page
+   names GELU without choosing between it and its tanh approximation).
 
 Two independent ways of computing the transforms are provided:
 
@@ -77,6 +84,9 @@ __all__ = [
     "spectral_conv1d_loops",
     "spectral_conv2d_backward_ref",
     "spectral_conv1d_backward_ref",
+    "gelu",
+    "spectral_conv2d_gelu_ref",
+    "spectral_conv1d_gelu_ref",
 ]
 
 
@@ -376,6 +386,44 @@ def spectral_conv1d_backward_ref(x, weight, grad_out, modes: int, transform: str
     grad_x = inverse_from_truncated_1d(zh, n, transform)
     grad_w = np.einsum("bik,bok->kio", np.conj(xh), gh) * c2r_weights(n, modes)[:, None, None]
     return grad_x, grad_w
+
+
+# --------------------------------------------------------------------------
+# Fused layer tail: GELU and a second branch after the inverse transform
+# --------------------------------------------------------------------------
+
+def gelu(u):
+    """u * Phi(u) with the standard normal CDF Phi(u) = (1 + erf(u / sqrt 2)) / 2."""
+    from scipy.special import erf
+    u = np.asarray(u, dtype=np.float64)
+    return 0.5 * u * (1.0 + erf(u / math.sqrt(2.0)))
+
+
+def _layer_tail(y, bias, branch, branch_after: bool, channel_axis_shape):
+    if bias is not None:
+        y = y + np.asarray(bias, dtype=np.float64).reshape(channel_axis_shape)
+    if branch is not None and not branch_after:
+        y = y + np.asarray(branch, dtype=np.float64)
+    y = gelu(y)
+    if branch is not None and branch_after:
+        y = y + np.asarray(branch, dtype=np.float64)
+    return y
+
+
+def spectral_conv2d_gelu_ref(x, weight, mx: int, my: int, bias=None, branch=None, branch_after: bool = False,
+                             transform: str = "dft"):
+    """gelu(conv + bias[o] + branch), or gelu(conv + bias[o]) + branch when
+    branch_after; conv = spectral_conv2d_ref(x, weight), bias [Cout] and
+    branch [B,Cout,H,W] optional."""
+    y = spectral_conv2d_ref(x, weight, mx, my, transform)
+    return _layer_tail(y, bias, branch, branch_after, (1, -1, 1, 1))
+
+
+def spectral_conv1d_gelu_ref(x, weight, modes: int, bias=None, branch=None, branch_after: bool = False,
+                             transform: str = "dft"):
+    """The 1D form of spectral_conv2d_gelu_ref (branch [B,Cout,N])."""
+    y = spectral_conv1d_ref(x, weight, modes, transform)
+    return _layer_tail(y, bias, branch, branch_after, (1, -1, 1))
 
 
 # --------------------------------------------------------------------------

@@ -612,3 +612,109 @@ def test_backward_planted_mistakes():
     assert not weight_ok(np.einsum("bisrk,bosrk->srkio", xh, np.conj(gh)) * c)
     # batch not summed (first item only)
     assert not weight_ok(np.einsum("isrk,osrk->srkio", np.conj(xh[0]), gh[0]) * c)
+
+
+# --------------------------------------------------------------------------
+# Fused layer tail: gelu(conv + bias + branch) or gelu(conv + bias) + branch
+# --------------------------------------------------------------------------
+
+# standard normal CDF Phi(u) from a printed table (to double precision)
+PHI_TABLE = {
+    -2.0: 0.022750131948179195,
+    -1.0: 0.15865525393145707,
+    -0.5: 0.3085375387259869,
+    0.0: 0.5,
+    0.5: 0.6914624612740131,
+    1.0: 0.8413447460685429,
+    2.0: 0.9772498680518208,
+    3.0: 0.9986501019683699,
+}
+
+
+def test_gelu_against_normal_cdf_table():
+    for u, phi in PHI_TABLE.items():
+        assert abs(float(S.gelu(u)) - u * phi) <= 1e-15 * max(1.0, abs(u))
+    # the tanh approximation of GELU would miss the table by ~1.5e-4 at u = 1
+    u = 1.0
+    tanh_form = 0.5 * u * (1.0 + math.tanh(math.sqrt(2.0 / math.pi) * (u + 0.044715 * u ** 3)))
+    assert abs(tanh_form - u * PHI_TABLE[1.0]) > 1e-4
+
+
+def test_gelu_odd_part_and_tails():
+    # Phi(u) + Phi(-u) = 1  =>  gelu(u) - gelu(-u) = u
+    u = np.random.default_rng(40).standard_normal(1000) * 3
+    assert np.max(np.abs(S.gelu(u) - S.gelu(-u) - u)) <= 1e-14
+    assert abs(float(S.gelu(12.0)) - 12.0) <= 1e-14 and abs(float(S.gelu(-12.0))) <= 1e-14
+
+
+def _dc_identity_weight(rng, shape, c):
+    # random weights, except the DC mode of block 0, which is the real identity
+    wt = rand_c(rng, shape)
+    wt[(0,) * (len(shape) - 2)] = np.eye(c)
+    return wt
+
+
+TABLE_POINTS = np.array(sorted(PHI_TABLE))
+
+
+@pytest.mark.parametrize("branch_after", [False, True])
+def test_layer_tail_closed_form_2d(branch_after):
+    # x constant per (b, i): only the DC mode is non-zero, so with the
+    # identity DC weight conv[b, o] = x[b, o] at every pixel, and the layer
+    # output is a table value of gelu wherever its argument is a table point
+    b, c, h, w, mx, my = 3, 3, 8, 16, 2, 3
+    rng = np.random.default_rng(41)
+    target = rng.choice(TABLE_POINTS, size=(b, c))
+    const = rng.standard_normal((b, c))
+    bias = rng.standard_normal(c)
+    if branch_after:
+        const = target - bias[None, :]               # gelu argument = target
+        d = rng.standard_normal((b, c))
+    else:
+        d = target - const - bias[None, :]
+    x = np.broadcast_to(const[:, :, None, None], (b, c, h, w)).copy()
+    branch = np.broadcast_to(d[:, :, None, None], (b, c, h, w)).copy()
+    wt = _dc_identity_weight(rng, (2, mx, my, c, c), c)
+    out = S.spectral_conv2d_gelu_ref(x, wt, mx, my, bias=bias, branch=branch, branch_after=branch_after)
+    phi = np.vectorize(PHI_TABLE.get)(target)
+    expect = target * phi + (d if branch_after else 0.0)
+    assert np.max(np.abs(out - expect[:, :, None, None])) <= 1e-12
+    # planted mistakes, each off the table
+    conv = S.spectral_conv2d_ref(x, wt, mx, my)
+    wrong = {
+        "bias along the batch axis": S.gelu(conv + bias[:, None, None, None] + (0 if branch_after else branch))
+        + (branch if branch_after else 0),
+        "branch on the other side of the activation": (S.gelu(conv + bias[None, :, None, None]) + branch)
+        if not branch_after else S.gelu(conv + bias[None, :, None, None] + branch),
+        "bias after the activation": S.gelu(conv + (0 if branch_after else branch)) + bias[None, :, None, None]
+        + (branch if branch_after else 0),
+    }
+    for name, val in wrong.items():
+        assert np.max(np.abs(val - expect[:, :, None, None])) > 1e-3, name
+
+
+@pytest.mark.parametrize("branch_after", [False, True])
+def test_layer_tail_closed_form_1d(branch_after):
+    b, c, n, modes = 2, 4, 16, 5
+    rng = np.random.default_rng(42)
+    target = rng.choice(TABLE_POINTS, size=(b, c))
+    bias = rng.standard_normal(c)
+    d = rng.standard_normal((b, c))
+    const = target - bias[None, :] - (0.0 if branch_after else d)
+    x = np.broadcast_to(const[:, :, None], (b, c, n)).copy()
+    branch = np.broadcast_to(d[:, :, None], (b, c, n)).copy()
+    wt = _dc_identity_weight(rng, (modes, c, c), c)
+    out = S.spectral_conv1d_gelu_ref(x, wt, modes, bias=bias, branch=branch, branch_after=branch_after)
+    expect = target * np.vectorize(PHI_TABLE.get)(target) + (d if branch_after else 0.0)
+    assert np.max(np.abs(out - expect[:, :, None])) <= 1e-12
+
+
+def test_layer_tail_optional_terms():
+    # no bias and no branch: gelu of the plain operator; the two orders agree
+    rng = np.random.default_rng(43)
+    x = rng.standard_normal((2, 3, 8, 8))
+    wt = rand_c(rng, (2, 2, 3, 3, 4))
+    conv = S.spectral_conv2d_ref(x, wt, 2, 3)
+    for after in (False, True):
+        out = S.spectral_conv2d_gelu_ref(x, wt, 2, 3, branch_after=after)
+        assert np.max(np.abs(out - S.gelu(conv))) == 0.0
