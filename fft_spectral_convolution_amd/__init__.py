@@ -30,6 +30,8 @@ __all__ = [
     "fno_spectral_conv1d_ws",
     "fno_spectral_conv2d_backward",
     "fno_spectral_conv1d_backward",
+    "fno_spectral_conv2d_gelu",
+    "fno_spectral_conv1d_gelu",
     "fno_workspace_size_2d",
     "fno_workspace_size_1d",
     "fno_forward2d",
@@ -72,6 +74,8 @@ _SIGNATURES = {
     "fno_inverse1d": (_I, [_P, _P, _I, _I, _I, _I, _P]),
     "fno_spectral_conv2d_backward": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P]),
     "fno_spectral_conv1d_backward": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P]),
+    "fno_spectral_conv2d_gelu": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _P]),
+    "fno_spectral_conv1d_gelu": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P]),
     "fno_set_timing_events": (_I, [ctypes.POINTER(ctypes.c_void_p), _I]),
     "fno_last_kernel_count": (_I, []),
     "fno_last_kernel_name": (ctypes.c_char_p, [_I]),
@@ -201,6 +205,44 @@ def fno_spectral_conv2d(x, w, mx: int, my: int, out=None):
     with _on_device(x):
         _check(lib().fno_spectral_conv2d(_ptr(x), _ptr(w), _ptr(out), b, cin, cout, h, wd, mx, my,
                                          _stream_ptr(x.device)), "fno_spectral_conv2d")
+    return out
+
+
+def _epilogue_args(x, bias, branch, out, cout):
+    torch = _torch()
+    if bias is not None:
+        _need(bias, torch.float32, 1, "bias")
+        if bias.shape[0] != cout or bias.device != x.device:
+            raise ValueError(f"bias must be [{cout}] on {x.device}")
+    if branch is not None:
+        _need(branch, torch.float32, out.dim(), "branch")
+        if branch.shape != out.shape or branch.device != x.device:
+            raise ValueError(f"branch must have the output's shape {tuple(out.shape)} on {x.device}")
+    nullp = ctypes.c_void_p(0)
+    return (_ptr(bias) if bias is not None else nullp), (_ptr(branch) if branch is not None else nullp)
+
+
+def fno_spectral_conv2d_gelu(x, w, mx: int, my: int, bias=None, branch=None, branch_after: bool = False, out=None):
+    """Spectral convolution with the fused layer tail: out = gelu(conv + bias[o] + branch),
+    or gelu(conv + bias[o]) + branch with branch_after; bias [Cout] and branch (the output's
+    shape) are optional; gelu is the exact erf form."""
+    out, (b, cin, cout, h, wd) = _conv2d_args(x, w, mx, my, out)
+    pb, pr = _epilogue_args(x, bias, branch, out, cout)
+    with _on_device(x):
+        _check(lib().fno_spectral_conv2d_gelu(_ptr(x), _ptr(w), pb, pr, _ptr(out), b, cin, cout, h, wd, mx, my,
+                                              int(bool(branch_after)), _stream_ptr(x.device)),
+               "fno_spectral_conv2d_gelu")
+    return out
+
+
+def fno_spectral_conv1d_gelu(x, w, modes: int, bias=None, branch=None, branch_after: bool = False, out=None):
+    """The 1D form of fno_spectral_conv2d_gelu (branch [B,Cout,N])."""
+    out, (b, cin, cout, n) = _conv1d_args(x, w, modes, out)
+    pb, pr = _epilogue_args(x, bias, branch, out, cout)
+    with _on_device(x):
+        _check(lib().fno_spectral_conv1d_gelu(_ptr(x), _ptr(w), pb, pr, _ptr(out), b, cin, cout, n, modes,
+                                              int(bool(branch_after)), _stream_ptr(x.device)),
+               "fno_spectral_conv1d_gelu")
     return out
 
 

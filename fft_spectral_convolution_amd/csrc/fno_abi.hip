@@ -243,14 +243,17 @@ int run_forward2d_staged(const Shape2d& s, int64_t C, const float* x, float2* xh
     return FNO_OK;
 }
 
+// epi: the fused output epilogue (its rows_per_chan is set here)
 int run_inverse2d_staged(const Shape2d& s, int64_t C, const float2* yh, float* out, float2* r, const float2* tw,
-                         hipStream_t st) {
+                         hipStream_t st, const Epilogue& epi = Epilogue{}) {
     const float scale = (float)(1.0 / std::sqrt((double)s.H * (double)s.W));
     rec_kernel("cols_inv", st);
     hipError_t e = launch_cols_inv(yh, r, s.B * C, s.log2H, s.mx, s.my, tw, st);
     if (e != hipSuccess) return hip_fail(e);
-    rec_kernel("rows_inv", st);
-    e = launch_rows_inv(r, out, s.B * C * s.H, s.log2W, s.my, s.my, scale, tw, st);
+    rec_kernel(epi.on ? "rows_inv_gelu" : "rows_inv", st);
+    Epilogue ep = epi;
+    ep.rows_per_chan = s.H;
+    e = launch_rows_inv(r, out, s.B * C * s.H, s.log2W, s.my, s.my, scale, tw, st, ep);
     if (e != hipSuccess) return hip_fail(e);
     return FNO_OK;
 }
@@ -267,12 +270,14 @@ int run_forward2d_small(const Shape2d& s, int64_t C, const float* x, float2* xh,
 }
 
 int run_inverse2d_small(const Shape2d& s, int64_t C, const float2* yh, float* out, const SpecLayout& lay,
-                        const float2* tw, hipStream_t st) {
+                        const float2* tw, hipStream_t st, const Epilogue& epi = Epilogue{}) {
     const float scale = (float)(1.0 / std::sqrt((double)s.H * (double)s.W));
-    rec_kernel("inv2d", st);
+    rec_kernel(epi.on ? "inv2d_gelu" : "inv2d", st);
+    Epilogue ep = epi;
+    ep.rows_per_chan = 1;                       // per-image kernels pass the image index
     hipError_t e = rowreg2d_supported(s.log2H, s.log2W, s.mx, s.my, lay)
-                       ? launch_inv2d_rowreg(yh, out, lay, s.B * C, s.log2H, s.log2W, s.mx, s.my, tw, st)
-                       : launch_inv2d_small(yh, out, lay, s.B * C, s.log2H, s.log2W, s.mx, s.my, scale, tw, st);
+                       ? launch_inv2d_rowreg(yh, out, lay, s.B * C, s.log2H, s.log2W, s.mx, s.my, tw, st, ep)
+                       : launch_inv2d_small(yh, out, lay, s.B * C, s.log2H, s.log2W, s.mx, s.my, scale, tw, st, ep);
     return e == hipSuccess ? FNO_OK : hip_fail(e);
 }
 
@@ -286,7 +291,7 @@ size_t unfused_ws_2d(const Shape2d& s) {
 }
 
 int run_unfused_2d(const Shape2d& s, const float* x, const float2* w, float* out, void* ws, const float2* tw,
-                   hipStream_t st) {
+                   hipStream_t st, const Epilogue& epi = Epilogue{}) {
     const int64_t m = (int64_t)2 * s.mx * s.my;
     const size_t rmax = (size_t)s.B * (size_t)(s.Cin > s.Cout ? s.Cin : s.Cout) * s.H * s.my * sizeof(float2);
     char* p = static_cast<char*>(ws);
@@ -299,7 +304,7 @@ int run_unfused_2d(const Shape2d& s, const float* x, const float2* w, float* out
     if (rc) return rc;
     rc = run_mix(xh, canonical_layout(s.Cin, m), w, yh, canonical_layout(s.Cout, m), s.B, s.Cin, s.Cout, m, st);
     if (rc) return rc;
-    return run_inverse2d_staged(s, s.Cout, yh, out, r, tw, st);
+    return run_inverse2d_staged(s, s.Cout, yh, out, r, tw, st, epi);
 }
 
 // Fused (grids up to 128 x 128): fwd2d -> mix -> inv2d, the truncated spectra
@@ -311,7 +316,7 @@ size_t fused_small_ws_2d(const Shape2d& s) {
 }
 
 int run_fused_small_2d(const Shape2d& s, const float* x, const float2* w, float* out, void* ws, const float2* tw,
-                       hipStream_t st) {
+                       hipStream_t st, const Epilogue& epi = Epilogue{}) {
     const int64_t m = (int64_t)2 * s.mx * s.my;
     const SpecLayout lx = tiled_layout(s.Cin, m);
     const SpecLayout ly = tiled_layout(s.Cout, m);
@@ -322,7 +327,7 @@ int run_fused_small_2d(const Shape2d& s, const float* x, const float2* w, float*
     if (rc) return rc;
     rc = run_mix(xh, lx, w, yh, ly, s.B, s.Cin, s.Cout, m, st);
     if (rc) return rc;
-    return run_inverse2d_small(s, s.Cout, yh, out, ly, tw, st);
+    return run_inverse2d_small(s, s.Cout, yh, out, ly, tw, st, epi);
 }
 
 size_t unfused_ws_1d(int64_t B, int64_t Cin, int64_t Cout, int modes) {
@@ -330,7 +335,7 @@ size_t unfused_ws_1d(int64_t B, int64_t Cin, int64_t Cout, int modes) {
 }
 
 int run_unfused_1d(int64_t B, int64_t Cin, int64_t Cout, int N, int modes, const float* x, const float2* w,
-                   float* out, void* ws, const float2* tw, hipStream_t st) {
+                   float* out, void* ws, const float2* tw, hipStream_t st, const Epilogue& epi = Epilogue{}) {
     const float scale = (float)(1.0 / std::sqrt((double)N));
     char* p = static_cast<char*>(ws);
     float2* xh = reinterpret_cast<float2*>(p);
@@ -342,8 +347,10 @@ int run_unfused_1d(int64_t B, int64_t Cin, int64_t Cout, int N, int modes, const
     if (e != hipSuccess) return hip_fail(e);
     int rc = run_mix(xh, canonical_layout(Cin, modes), w, yh, canonical_layout(Cout, modes), B, Cin, Cout, modes, st);
     if (rc) return rc;
-    rec_kernel("rows_inv", st);
-    e = launch_rows_inv(yh, out, B * Cout, l2, modes, modes, scale, tw, st);
+    rec_kernel(epi.on ? "rows_inv_gelu" : "rows_inv", st);
+    Epilogue ep = epi;
+    ep.rows_per_chan = 1;
+    e = launch_rows_inv(yh, out, B * Cout, l2, modes, modes, scale, tw, st, ep);
     if (e != hipSuccess) return hip_fail(e);
     return FNO_OK;
 }
@@ -352,13 +359,32 @@ int run_unfused_1d(int64_t B, int64_t Cin, int64_t Cout, int N, int modes, const
 size_t best_ws_2d(const Shape2d& s) { return small_path(s) ? fused_small_ws_2d(s) : unfused_ws_2d(s); }
 
 int run_best_2d(const Shape2d& s, const float* x, const float2* w, float* out, void* ws, const float2* tw,
-                hipStream_t st) {
-    if (small_path(s)) return run_fused_small_2d(s, x, w, out, ws, tw, st);
-    return run_unfused_2d(s, x, w, out, ws, tw, st);
+                hipStream_t st, const Epilogue& epi = Epilogue{}) {
+    if (small_path(s)) return run_fused_small_2d(s, x, w, out, ws, tw, st, epi);
+    return run_unfused_2d(s, x, w, out, ws, tw, st, epi);
+}
+
+// Inputs of the fused output epilogue: bias [Cout] (4-byte aligned) and
+// branch (the output's shape, 16-byte aligned) are optional; neither may
+// overlap the output.
+int check_epilogue(const float* bias, const float* branch, const float* out, int Cout, size_t obytes,
+                   int branch_after, Epilogue* epi) {
+    if (branch_after != 0 && branch_after != 1) return FNO_ERR_SHAPE;
+    if ((bias && (reinterpret_cast<uintptr_t>(bias) & 3u)) || (branch && misaligned(branch))) return FNO_ERR_ALIGN;
+    if ((bias && overlap(bias, (size_t)Cout * sizeof(float), out, obytes)) ||
+        (branch && overlap(branch, obytes, out, obytes)))
+        return FNO_ERR_ALIAS;
+    epi->on = true;
+    epi->bias = bias;
+    epi->branch = branch;
+    epi->cout = Cout;
+    epi->branch_after = branch_after;
+    return FNO_OK;
 }
 
 int conv2d_common(const float* x, const void* w, float* out, int B, int Cin, int Cout, int H, int W, int mx,
-                  int my, void* user_ws, size_t user_ws_bytes, bool use_user_ws, bool unfused, void* stream) {
+                  int my, void* user_ws, size_t user_ws_bytes, bool use_user_ws, bool unfused, void* stream,
+                  const Epilogue& epi = Epilogue{}) {
     int rc = check_dims_2d(B, Cin, H, W, mx, my);
     if (rc) return rc;
     if (Cout < 1) return FNO_ERR_SHAPE;
@@ -384,12 +410,13 @@ int conv2d_common(const float* x, const void* w, float* out, int B, int Cin, int
     hipStream_t hs = static_cast<hipStream_t>(stream);
     const float2* wc = static_cast<const float2*>(w);
     rec_begin();
-    if (unfused) return rec_end(hs, run_unfused_2d(s, x, wc, out, ws, st->twiddle, hs));
-    return rec_end(hs, run_best_2d(s, x, wc, out, ws, st->twiddle, hs));
+    if (unfused) return rec_end(hs, run_unfused_2d(s, x, wc, out, ws, st->twiddle, hs, epi));
+    return rec_end(hs, run_best_2d(s, x, wc, out, ws, st->twiddle, hs, epi));
 }
 
 int conv1d_common(const float* x, const void* w, float* out, int B, int Cin, int Cout, int N, int modes,
-                  void* user_ws, size_t user_ws_bytes, bool use_user_ws, bool unfused, void* stream) {
+                  void* user_ws, size_t user_ws_bytes, bool use_user_ws, bool unfused, void* stream,
+                  const Epilogue& epi = Epilogue{}) {
     (void)unfused;
     int rc = check_dims_1d(B, Cin, N, modes);
     if (rc) return rc;
@@ -415,7 +442,7 @@ int conv1d_common(const float* x, const void* w, float* out, int B, int Cin, int
     hipStream_t hs = static_cast<hipStream_t>(stream);
     rec_begin();
     return rec_end(hs, run_unfused_1d(B, Cin, Cout, N, modes, x, static_cast<const float2*>(w), out, ws,
-                                      st->twiddle, hs));
+                                      st->twiddle, hs, epi));
 }
 
 // ---------------------------------------------------------------------------
@@ -667,6 +694,31 @@ int fno_spectral_conv1d_unfused(const float* x, const void* w, float* out, int B
 int fno_spectral_conv1d_ws(const float* x, const void* w, float* out, int B, int Cin, int Cout, int N, int modes,
                            void* workspace, size_t ws_bytes, void* stream) {
     return conv1d_common(x, w, out, B, Cin, Cout, N, modes, workspace, ws_bytes, true, false, stream);
+}
+
+int fno_spectral_conv2d_gelu(const float* x, const void* w, const float* bias, const float* branch, float* out,
+                             int B, int Cin, int Cout, int H, int W, int mx, int my, int branch_after,
+                             void* stream) {
+    int rc = check_dims_2d(B, Cin, H, W, mx, my);
+    if (rc) return rc;
+    if (Cout < 1) return FNO_ERR_SHAPE;
+    if (!out) return FNO_ERR_NULL;
+    Epilogue epi;
+    rc = check_epilogue(bias, branch, out, Cout, (size_t)B * Cout * H * W * sizeof(float), branch_after, &epi);
+    if (rc) return rc;
+    return conv2d_common(x, w, out, B, Cin, Cout, H, W, mx, my, nullptr, 0, false, false, stream, epi);
+}
+
+int fno_spectral_conv1d_gelu(const float* x, const void* w, const float* bias, const float* branch, float* out,
+                             int B, int Cin, int Cout, int N, int modes, int branch_after, void* stream) {
+    int rc = check_dims_1d(B, Cin, N, modes);
+    if (rc) return rc;
+    if (Cout < 1) return FNO_ERR_SHAPE;
+    if (!out) return FNO_ERR_NULL;
+    Epilogue epi;
+    rc = check_epilogue(bias, branch, out, Cout, (size_t)B * Cout * N * sizeof(float), branch_after, &epi);
+    if (rc) return rc;
+    return conv1d_common(x, w, out, B, Cin, Cout, N, modes, nullptr, 0, false, false, stream, epi);
 }
 
 size_t fno_workspace_size_2d(int B, int Cin, int Cout, int H, int W, int mx, int my) {

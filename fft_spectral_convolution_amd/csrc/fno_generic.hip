@@ -120,10 +120,12 @@ __global__ __launch_bounds__(kThreads) void k_cols_inv(const float2* __restrict_
     }
 }
 
-template <int LOG2W>
+// EPI: the fused output epilogue (bias, GELU, second branch) on every
+// output, the branch read at the same index.
+template <int LOG2W, bool EPI>
 __global__ __launch_bounds__(kThreads) void k_rows_inv(const float2* __restrict__ y, float* __restrict__ out,
                                                       int64_t nrows, int my, int y_ld, float scale,
-                                                      const float2* __restrict__ tw) {
+                                                      const float2* __restrict__ tw, Epilogue epi) {
     constexpr int W = 1 << LOG2W;
     constexpr int P = W >= kLdsElems ? 1 : kLdsElems / W;
     __shared__ float2 buf[2][kLdsElems];
@@ -161,8 +163,17 @@ __global__ __launch_bounds__(kThreads) void k_rows_inv(const float2* __restrict_
         const int n = e & (W - 1);
         const int64_t ra = 2 * (pair0 + pr);
         const float2 z = res[pr * W + n];
-        out[ra * W + n] = z.x * scale;
-        if (ra + 1 < nrows) out[(ra + 1) * W + n] = z.y * scale;
+        if constexpr (EPI) {
+            const float br0 = epi.branch ? epi.branch[ra * W + n] : 0.0f;
+            out[ra * W + n] = epi_apply(epi, z.x * scale, epi_bias(epi, ra), br0);
+            if (ra + 1 < nrows) {
+                const float br1 = epi.branch ? epi.branch[(ra + 1) * W + n] : 0.0f;
+                out[(ra + 1) * W + n] = epi_apply(epi, z.y * scale, epi_bias(epi, ra + 1), br1);
+            }
+        } else {
+            out[ra * W + n] = z.x * scale;
+            if (ra + 1 < nrows) out[(ra + 1) * W + n] = z.y * scale;
+        }
     }
 }
 
@@ -247,14 +258,19 @@ hipError_t launch_rows_fwd(const float* x, float2* y, int64_t nrows, int log2W, 
 }
 
 hipError_t launch_rows_inv(const float2* y, float* out, int64_t nrows, int log2W, int my, int y_ld, float scale,
-                           const float2* tw, hipStream_t s) {
-    if (rows_pruned_supported(log2W, my)) return launch_rows_inv_pruned(y, out, nrows, log2W, my, y_ld, scale, tw, s);
+                           const float2* tw, hipStream_t s, const Epilogue& epi) {
+    if (rows_pruned_supported(log2W, my))
+        return launch_rows_inv_pruned(y, out, nrows, log2W, my, y_ld, scale, tw, s, epi);
     const int64_t npairs = (nrows + 1) / 2;
     const int p = rows_per_block(log2W);
     const dim3 grid((unsigned)((npairs + p - 1) / p));
     switch (log2W) {
-#define CASE(L) \
-    case L: return launch_kernel(k_rows_inv<L>, grid, dim3(kThreads), 0, s, y, out, nrows, my, y_ld, scale, tw);
+#define CASE(L)                                                                                                   \
+    case L:                                                                                                       \
+        return epi.on ? launch_kernel(k_rows_inv<L, true>, grid, dim3(kThreads), 0, s, y, out, nrows, my, y_ld,   \
+                                      scale, tw, epi)                                                             \
+                      : launch_kernel(k_rows_inv<L, false>, grid, dim3(kThreads), 0, s, y, out, nrows, my, y_ld,  \
+                                      scale, tw, epi);
         FNO_LOG2_CASES(CASE)
 #undef CASE
         default: return hipErrorInvalidValue;

@@ -55,12 +55,42 @@ inline SpecLayout tiled_layout(int64_t C, int64_t M) {
 // Complex elements a spectrum of B batch items spans in either layout.
 inline int64_t layout_elems(const SpecLayout& l, int64_t B) { return B * l.sb; }
 
+// ---- fused output epilogue of the inverse transforms ------------------------
+// The FFT blog's fused operator (sections 5.1-5.2) activates the C2R output
+// with GELU and adds a second, time-domain branch in the kernel that writes
+// the output (section 6.2: fuse what follows the C2R).  With `on` set, each
+// output value v of channel c becomes
+//   gelu(v + bias[c] + branch)     (branch_after == 0: the FNO-layer form), or
+//   gelu(v + bias[c]) + branch     (branch_after == 1: the blog's order),
+// branch read at the output's own index (same shape as the output), a null
+// bias or branch reads as zero, gelu(u) = u (1 + erf(u / sqrt 2)) / 2.  The
+// channel of output row r (rows of the kernel's row length) is
+// (r / rows_per_chan) % cout; the per-image kernels pass their image index
+// with rows_per_chan = 1.
+struct Epilogue {
+    bool on = false;
+    const float* branch = nullptr;
+    const float* bias = nullptr;
+    int64_t rows_per_chan = 1;
+    int cout = 1;
+    int branch_after = 0;
+};
+
+__device__ __forceinline__ float epi_gelu(float u) { return 0.5f * u * (1.0f + erff(u * 0.707106781186547524f)); }
+__device__ __forceinline__ float epi_bias(const Epilogue& e, int64_t row) {
+    return e.bias ? e.bias[(row / e.rows_per_chan) % e.cout] : 0.0f;
+}
+__device__ __forceinline__ float epi_apply(const Epilogue& e, float v, float bias, float br) {
+    return e.branch_after ? epi_gelu(v + bias) + br : epi_gelu(v + bias + br);
+}
+
 // ---- fused small-grid transforms (fno_small2d.hip), H, W in [8, 128] --------
 bool small2d_supported(int log2H, int log2W, int my);
 hipError_t launch_fwd2d_small(const float* x, float2* xh, const SpecLayout& lay, int64_t nimg, int log2H, int log2W,
                               int mx, int my, float scale, const float2* tw, hipStream_t s);
 hipError_t launch_inv2d_small(const float2* yh, float* out, const SpecLayout& lay, int64_t nimg, int log2H,
-                              int log2W, int mx, int my, float scale, const float2* tw, hipStream_t s);
+                              int log2W, int mx, int my, float scale, const float2* tw, hipStream_t s,
+                              const Epilogue& epi = Epilogue{});
 
 // ---- 2D transforms with one real row per thread (fno_rowreg2d.hip) ---------
 // H, W in {64, 128}, my <= 32; same output as launch_fwd2d_small (scaled by
@@ -70,7 +100,8 @@ hipError_t launch_fwd2d_rowreg(const float* x, float2* xh, const SpecLayout& lay
                                int log2W, int mx, int my, const float2* tw, hipStream_t s);
 // and its inverse: truncated spectrum -> real image, same shapes and scale
 hipError_t launch_inv2d_rowreg(const float2* yh, float* out, const SpecLayout& lay, int64_t nimg, int log2H,
-                               int log2W, int mx, int my, const float2* tw, hipStream_t s);
+                               int log2W, int mx, int my, const float2* tw, hipStream_t s,
+                               const Epilogue& epi = Epilogue{});
 
 // ---- channel mix on MFMA (fno_mix.hip) --------------------------------------
 // yh(b, o, m) = sum_i xh(b, i, m) * w[m][i][o], spectra addressed by layouts.
@@ -94,7 +125,7 @@ bool rows_pruned_supported(int log2W, int my);
 hipError_t launch_rows_fwd_pruned(const float* x, float2* y, int64_t nrows, int log2W, int my, int y_ld, float scale,
                                   const float2* tw, hipStream_t s);
 hipError_t launch_rows_inv_pruned(const float2* y, float* out, int64_t nrows, int log2W, int my, int y_ld,
-                                  float scale, const float2* tw, hipStream_t s);
+                                  float scale, const float2* tw, hipStream_t s, const Epilogue& epi = Epilogue{});
 
 // ---- pruned column transforms (fno_cols_pruned.hip) --------------------------
 // H in [512, 2048], 2 mx <= 128 and a multiple of H / 64, my <= 64: same
@@ -123,7 +154,7 @@ hipError_t launch_cols_inv(const float2* yh, float2* r, int64_t nimg, int log2H,
                            const float2* tw, hipStream_t s);
 // R'[nrows][y_ld] (bins ky < my) -> C2R rows of length W, times scale.
 hipError_t launch_rows_inv(const float2* y, float* out, int64_t nrows, int log2W, int my, int y_ld,
-                           float scale, const float2* tw, hipStream_t s);
+                           float scale, const float2* tw, hipStream_t s, const Epilogue& epi = Epilogue{});
 
 // ---- backward pass (fno_backward.hip) ---------------------------------------
 // wt[m][o][i] = conj(w[m][i][o]) for M modes.

@@ -281,11 +281,15 @@ __device__ __forceinline__ float2 packed_c2r_bin(const float2 (&X)[MYMAX]) {
 // from the spectrum, the hand-over, the twiddle conj W_H^{t k1}, R1-point
 // inverse DFTs over k1), its rows in the LDS plane; then one thread per row
 // builds the packed spectrum Z, runs the W/2-point inverse DFT in registers
-// and hands its row out through the stage to coalesced buffer stores.
-template <int LOG2H, int LOG2W, int MYMAX>
+// and hands its row out through the stage to coalesced buffer stores.  EPI:
+// the fused output epilogue (bias, GELU, second branch) runs as a second
+// pass over the image once its rows are stored and their registers free:
+// every lane reads back the float4s it wrote (still in L2) with the branch
+// at the same offsets, applies it and stores again.
+template <int LOG2H, int LOG2W, int MYMAX, bool EPI>
 __global__ __launch_bounds__(1 << LOG2H) __attribute__((amdgpu_waves_per_eu(2))) void k_inv2d_rows(
     const float2* __restrict__ yh, float* __restrict__ out, ImageBase ib, int st, int64_t nimg, int mx, int my,
-    const float2* __restrict__ tw) {
+    const float2* __restrict__ tw, Epilogue epi) {
     using S = RowPlan<LOG2H, LOG2W, MYMAX>;
     constexpr int H = S::H, W = S::W, NZ = S::NZ, F4 = S::F4, R1 = S::R1, R2 = S::R2, KB = S::KB, NB = S::NB,
                   NJ = S::NJ;
@@ -402,6 +406,29 @@ __global__ __launch_bounds__(1 << LOG2H) __attribute__((amdgpu_waves_per_eu(2)))
                 });
                 wave_lds_sync();
             });
+            if constexpr (EPI) {
+                // this lane's stores complete before it reads them back
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+                const float bias = epi_bias(epi, img);
+                // a null branch gets an empty range: its loads read zero
+                const __amdgpu_buffer_rsrc_t rb =
+                    make_rsrc(epi.branch ? epi.branch + img * (int64_t)(H * W) : out, epi.branch ? (uint32_t)(H * W * 4) : 0u);
+                static_for<0, S::NCK>([&](auto c) {
+                    float4 o[8], br[8];
+                    static_for<0, 8>([&](auto ii) {
+                        o[ii] = buffer_load_f4(ro, soffs[ii] + 128 * c, 0);
+                        br[ii] = buffer_load_f4(rb, soffs[ii] + 128 * c, 0);
+                    });
+                    static_for<0, 8>([&](auto ii) {
+                        const float4 v = make_float4(epi_apply(epi, o[ii].x, bias, br[ii].x),
+                                                     epi_apply(epi, o[ii].y, bias, br[ii].y),
+                                                     epi_apply(epi, o[ii].z, bias, br[ii].z),
+                                                     epi_apply(epi, o[ii].w, bias, br[ii].w));
+                        buffer_store_f4(v, ro, soffs[ii] + 128 * c, 0);
+                    });
+                    __builtin_amdgcn_sched_barrier(0);
+                });
+            }
         }
     }
 }
@@ -432,10 +459,13 @@ hipError_t launch_fwd_one(const float* x, float2* xh, const ImageBase& ib, int s
 
 template <int LH, int LW, int MYM>
 hipError_t launch_inv_one(const float2* yh, float* out, const ImageBase& ib, int st, int64_t nimg, int mx, int my,
-                          const float2* tw, hipStream_t s) {
+                          const float2* tw, hipStream_t s, const Epilogue& epi) {
     using P = RowPlan<LH, LW, MYM>;
-    return launch_persistent(k_inv2d_rows<LH, LW, MYM>, P::NT, P::lds_bytes(), nimg, s, yh, out, ib, st, nimg, mx,
-                             my, tw);
+    if (epi.on)
+        return launch_persistent(k_inv2d_rows<LH, LW, MYM, true>, P::NT, P::lds_bytes(), nimg, s, yh, out, ib, st,
+                                 nimg, mx, my, tw, epi);
+    return launch_persistent(k_inv2d_rows<LH, LW, MYM, false>, P::NT, P::lds_bytes(), nimg, s, yh, out, ib, st, nimg,
+                             mx, my, tw, epi);
 }
 
 ImageBase image_base(const SpecLayout& lay) {
@@ -471,11 +501,11 @@ hipError_t launch_fwd2d_rowreg(const float* x, float2* xh, const SpecLayout& lay
 }
 
 hipError_t launch_inv2d_rowreg(const float2* yh, float* out, const SpecLayout& lay, int64_t nimg, int log2H,
-                               int log2W, int mx, int my, const float2* tw, hipStream_t s) {
+                               int log2W, int mx, int my, const float2* tw, hipStream_t s, const Epilogue& epi) {
     if (!rowreg2d_supported(log2H, log2W, mx, my, lay) || nimg >= INT32_MAX) return hipErrorInvalidValue;
     const ImageBase ib = image_base(lay);
     const int st = (int)lay.st;
-    FNO_ROWREG_DISPATCH(launch_inv_one, yh, out, ib, st, nimg, mx, my, tw, s)
+    FNO_ROWREG_DISPATCH(launch_inv_one, yh, out, ib, st, nimg, mx, my, tw, s, epi)
 }
 #undef FNO_ROWREG_DISPATCH
 

@@ -227,11 +227,13 @@ __global__ __launch_bounds__(kPrunedThreads) __attribute__((amdgpu_waves_per_eu(
     }
 }
 
-template <int Q>
+// EPI: the fused output epilogue (bias, GELU, second branch) on every
+// output, the branch read at the same index.
+template <int Q, bool EPI>
 __global__ __launch_bounds__(kPrunedThreads) __attribute__((amdgpu_waves_per_eu(2))) void k_rows_inv_pruned(const float2* __restrict__ y,
                                                                     float* __restrict__ out, int64_t nrows, int my,
                                                                     int y_ld, float scale,
-                                                                    const float2* __restrict__ tw) {
+                                                                    const float2* __restrict__ tw, Epilogue epi) {
     constexpr int N = 64 * Q;
     constexpr int NZ = Q / 2;
     __shared__ float2 xrow_all[kPrunedWaves][64];
@@ -286,12 +288,31 @@ __global__ __launch_bounds__(kPrunedThreads) __attribute__((amdgpu_waves_per_eu(
             dst[64 * (2 * m)] = z[m].x;
             dst[64 * (2 * m + 1)] = z[m].y;
         }
+        if constexpr (EPI) {
+            // second pass once the row's registers are free: the lane reads
+            // back the Q values it stored (still in L2), applies the epilogue
+            // with the branch at the same index and stores again
+            __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
+            const float bias = epi_bias(epi, row);
+            const float* const brow = epi.branch ? epi.branch + row * N + lane : nullptr;
+#pragma unroll 1
+            for (int m = 0; m < Q; m += 8) {
+                float v[8], b[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    v[j] = dst[64 * (m + j)];
+                    b[j] = brow ? brow[64 * (m + j)] : 0.0f;
+                }
+#pragma unroll
+                for (int j = 0; j < 8; ++j) dst[64 * (m + j)] = epi_apply(epi, v[j], bias, b[j]);
+            }
+        }
     }
 }
 
-template <typename K, typename TI, typename TO>
+template <typename K, typename TI, typename TO, typename... Extra>
 hipError_t launch_rows(K kernel, int64_t nrows, hipStream_t s, const TI* in, TO* out, int my, int y_ld, float scale,
-                       const float2* tw) {
+                       const float2* tw, Extra... extra) {
     int dev = 0, cus = 0, per_cu = 0;
     if (hipGetDevice(&dev) != hipSuccess) return hipErrorInvalidDevice;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
@@ -300,7 +321,8 @@ hipError_t launch_rows(K kernel, int64_t nrows, hipStream_t s, const TI* in, TO*
     int64_t g = (int64_t)cus * (per_cu > 0 ? per_cu : 1);
     const int64_t need = (nrows + kPrunedWaves - 1) / kPrunedWaves;
     if (g > need) g = need;
-    return launch_kernel(kernel, dim3((unsigned)g), dim3(kPrunedThreads), 0, s, in, out, nrows, my, y_ld, scale, tw);
+    return launch_kernel(kernel, dim3((unsigned)g), dim3(kPrunedThreads), 0, s, in, out, nrows, my, y_ld, scale, tw,
+                         extra...);
 }
 
 }  // namespace
@@ -319,13 +341,21 @@ hipError_t launch_rows_fwd_pruned(const float* x, float2* y, int64_t nrows, int 
 }
 
 hipError_t launch_rows_inv_pruned(const float2* y, float* out, int64_t nrows, int log2W, int my, int y_ld,
-                                  float scale, const float2* tw, hipStream_t s) {
+                                  float scale, const float2* tw, hipStream_t s, const Epilogue& epi) {
     if (!rows_pruned_supported(log2W, my) || nrows <= 0) return hipErrorInvalidValue;
+    if (epi.on) {
+        switch (log2W) {
+            case 9: return launch_rows(k_rows_inv_pruned<8, true>, nrows, s, y, out, my, y_ld, scale, tw, epi);
+            case 10: return launch_rows(k_rows_inv_pruned<16, true>, nrows, s, y, out, my, y_ld, scale, tw, epi);
+            case 11: return launch_rows(k_rows_inv_pruned<32, true>, nrows, s, y, out, my, y_ld, scale, tw, epi);
+            default: return launch_rows(k_rows_inv_pruned<64, true>, nrows, s, y, out, my, y_ld, scale, tw, epi);
+        }
+    }
     switch (log2W) {
-        case 9: return launch_rows(k_rows_inv_pruned<8>, nrows, s, y, out, my, y_ld, scale, tw);
-        case 10: return launch_rows(k_rows_inv_pruned<16>, nrows, s, y, out, my, y_ld, scale, tw);
-        case 11: return launch_rows(k_rows_inv_pruned<32>, nrows, s, y, out, my, y_ld, scale, tw);
-        default: return launch_rows(k_rows_inv_pruned<64>, nrows, s, y, out, my, y_ld, scale, tw);
+        case 9: return launch_rows(k_rows_inv_pruned<8, false>, nrows, s, y, out, my, y_ld, scale, tw, epi);
+        case 10: return launch_rows(k_rows_inv_pruned<16, false>, nrows, s, y, out, my, y_ld, scale, tw, epi);
+        case 11: return launch_rows(k_rows_inv_pruned<32, false>, nrows, s, y, out, my, y_ld, scale, tw, epi);
+        default: return launch_rows(k_rows_inv_pruned<64, false>, nrows, s, y, out, my, y_ld, scale, tw, epi);
     }
 }
 

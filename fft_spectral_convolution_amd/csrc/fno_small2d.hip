@@ -278,10 +278,12 @@ __global__ __launch_bounds__(kSmallThreads, kSmallBlocksPerCU) void k_fwd2d_smal
     }
 }
 
-template <int LOG2H, int LOG2W>
+// EPI: the fused output epilogue (bias, GELU, second branch) on every
+// output pair, the branch read at the same index.
+template <int LOG2H, int LOG2W, bool EPI>
 __global__ __launch_bounds__(kSmallThreads, kSmallBlocksPerCU) void k_inv2d_small(
     const float2* __restrict__ yh, float* __restrict__ out, ModeAddr ma, int64_t nimg, int mx_arg, int my_arg,
-    float scale, const float2* __restrict__ tw) {
+    float scale, const float2* __restrict__ tw, Epilogue epi) {
     using S = SmallPlan<LOG2H, LOG2W>;
     constexpr int H = S::H, W = S::W, P = S::P;
     constexpr int MW = S::MW, TW = S::TW, R1H = S::R1H, R2H = S::R2H;
@@ -431,10 +433,25 @@ __global__ __launch_bounds__(kSmallThreads, kSmallBlocksPerCU) void k_inv2d_smal
                 dft<MW, +1>(v1);
                 float2* oa = reinterpret_cast<float2*>(oi + p * W) + t;
                 float2* ob = reinterpret_cast<float2*>(oi + (p + P) * W) + t;
+                if constexpr (EPI) {
+                    const float bias = epi_bias(epi, img);
+                    const float2* ba = epi.branch ? reinterpret_cast<const float2*>(epi.branch + img * (int64_t)(H * W) + p * W) + t : nullptr;
+                    const float2* bb = epi.branch ? reinterpret_cast<const float2*>(epi.branch + img * (int64_t)(H * W) + (p + P) * W) + t : nullptr;
 #pragma unroll
-                for (int m = 0; m < MW; ++m) {
-                    oa[TW * m] = make_float2(v0[m].x * scale, v1[m].x * scale);
-                    ob[TW * m] = make_float2(v0[m].y * scale, v1[m].y * scale);
+                    for (int m = 0; m < MW; ++m) {
+                        const float2 za = ba ? ba[TW * m] : make_float2(0.0f, 0.0f);
+                        const float2 zb = bb ? bb[TW * m] : make_float2(0.0f, 0.0f);
+                        oa[TW * m] = make_float2(epi_apply(epi, v0[m].x * scale, bias, za.x),
+                                                 epi_apply(epi, v1[m].x * scale, bias, za.y));
+                        ob[TW * m] = make_float2(epi_apply(epi, v0[m].y * scale, bias, zb.x),
+                                                 epi_apply(epi, v1[m].y * scale, bias, zb.y));
+                    }
+                } else {
+#pragma unroll
+                    for (int m = 0; m < MW; ++m) {
+                        oa[TW * m] = make_float2(v0[m].x * scale, v1[m].x * scale);
+                        ob[TW * m] = make_float2(v0[m].y * scale, v1[m].y * scale);
+                    }
                 }
             }
             lds_barrier();
@@ -505,15 +522,18 @@ hipError_t launch_fwd2d_small(const float* x, float2* xh, const SpecLayout& lay,
 }
 
 hipError_t launch_inv2d_small(const float2* yh, float* out, const SpecLayout& lay, int64_t nimg, int log2H, int log2W,
-                              int mx, int my, float scale, const float2* tw, hipStream_t s) {
+                              int mx, int my, float scale, const float2* tw, hipStream_t s, const Epilogue& epi) {
     const ModeAddr ma = make_addr(lay);
     const dim3 grid(persistent_grid(nimg));
     switch (log2H * 16 + log2W) {
-#define CASE(LH, LW)                                                                                            \
-    case LH * 16 + LW: {                                                                                        \
-        const size_t lds = SmallPlan<LH, LW>::lds_bytes(my);                                                    \
-        return launch_kernel((k_inv2d_small<LH, LW>), grid, dim3(kSmallThreads), lds, s, yh, out, ma, nimg, mx, my, \
-                           scale, tw);                                                                          \
+#define CASE(LH, LW)                                                                                              \
+    case LH * 16 + LW: {                                                                                          \
+        const size_t lds = SmallPlan<LH, LW>::lds_bytes(my);                                                      \
+        if (epi.on)                                                                                               \
+            return launch_kernel((k_inv2d_small<LH, LW, true>), grid, dim3(kSmallThreads), lds, s, yh, out, ma,   \
+                                 nimg, mx, my, scale, tw, epi);                                                   \
+        return launch_kernel((k_inv2d_small<LH, LW, false>), grid, dim3(kSmallThreads), lds, s, yh, out, ma, nimg, \
+                             mx, my, scale, tw, epi);                                                             \
     }
         FNO_SMALL_CASES(CASE)
 #undef CASE

@@ -2,8 +2,8 @@
  * libfno -- Fourier-neural-operator spectral convolution on MI355X (gfx950).
  *
  * C ABI.  Every pointer argument named x, w, out, xh, yh, grad_out, grad_x,
- * grad_w or workspace is DEVICE memory on the current HIP device, owned by
- * the caller; the library never frees caller memory.  `stream` is a hipStream_t passed as void*
+ * grad_w, bias, branch or workspace is DEVICE memory on the current HIP
+ * device, owned by the caller; the library never frees caller memory.  `stream` is a hipStream_t passed as void*
  * (NULL = the null stream).  All calls only enqueue work on `stream` and
  * return without synchronising; a kernel fault shows up at the caller's next
  * synchronisation.
@@ -164,6 +164,30 @@ int fno_spectral_conv2d_backward(const float* x, const void* w, const float* gra
 int fno_spectral_conv1d_backward(const float* x, const void* w, const float* grad_out,
                                  float* grad_x, void* grad_w,
                                  int B, int Cin, int Cout, int N, int modes, void* stream);
+
+/*
+ * Spectral convolution with the fused layer tail (the FFT blog's fused
+ * operator, sections 5.1-5.2: the C2R output is activated with GELU and
+ * added to a second, time-domain branch inside the kernel that writes the
+ * output, section 6.2).  With conv = fno_spectral_conv2d(x, w):
+ *
+ *   branch_after = 0:  out = gelu(conv + bias[o] + branch)   (FNO-layer form)
+ *   branch_after = 1:  out = gelu(conv + bias[o]) + branch   (the blog's order)
+ *
+ * gelu(u) = u (1 + erf(u / sqrt 2)) / 2.  bias float32 [Cout] (4-byte
+ * aligned) and branch float32 (the shape and layout of out, 16-byte aligned)
+ * are optional: NULL reads as zero.  Neither may overlap out (FNO_ERR_ALIAS);
+ * branch_after outside {0, 1} is FNO_ERR_SHAPE.  Everything else as
+ * fno_spectral_conv2d / fno_spectral_conv1d (internal workspace).
+ */
+int fno_spectral_conv2d_gelu(const float* x, const void* w, const float* bias,
+                             const float* branch, float* out,
+                             int B, int Cin, int Cout, int H, int W, int mx, int my,
+                             int branch_after, void* stream);
+int fno_spectral_conv1d_gelu(const float* x, const void* w, const float* bias,
+                             const float* branch, float* out,
+                             int B, int Cin, int Cout, int N, int modes,
+                             int branch_after, void* stream);
 
 /*
  * Per-kernel timing for benchmarks and profilers.  While `events` is non-NULL,

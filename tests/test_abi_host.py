@@ -154,3 +154,25 @@ def test_backward_checks(lib):
     assert f1(A, B, C, D, None, 1, 1, 1, 16, 10, None) == MODES
     assert f1(A, B, C, None, None, 1, 1, 1, 16, 4, None) == NULL
 
+
+
+def test_gelu_epilogue_checks(lib):
+    f2 = lib.fno_spectral_conv2d_gelu
+    dims = (2, 3, 4, 16, 16, 4, 4)
+    D = 0x40000000                               # a free 16-byte aligned address for bias / branch
+    obytes = 2 * 4 * 16 * 16 * 4
+    assert f2(A, B, None, None, None, *dims, 0, None) == NULL        # out is required
+    assert f2(None, B, None, None, C, *dims, 0, None) == NULL
+    assert f2(A, B, None, None, C, 2, 3, 4, 12, 16, 4, 4, 0, None) == SHAPE
+    assert f2(A, B, None, None, C, 2, 3, 4, 16, 16, 9, 4, 0, None) == MODES
+    assert f2(A, B, None, None, C, *dims, 2, None) == SHAPE         # branch_after must be 0 or 1
+    assert f2(A, B, D + 2, None, C, *dims, 0, None) == ALIGN        # bias needs 4-byte alignment
+    assert f2(A, B, None, D + 4, C, *dims, 0, None) == ALIGN        # branch needs 16-byte alignment
+    assert f2(A, B, C + 4, None, C, *dims, 0, None) == ALIAS        # bias inside out
+    assert f2(A, B, None, C + obytes - 16, C, *dims, 1, None) == ALIAS   # branch overlaps out
+    assert f2(A, B, None, C, C, *dims, 0, None) == ALIAS            # branch on top of out
+    f1 = lib.fno_spectral_conv1d_gelu
+    assert f1(A, B, None, None, C, 1, 1, 1, 12, 2, 0, None) == SHAPE
+    assert f1(A, B, None, None, C, 1, 1, 1, 16, 10, 0, None) == MODES
+    assert f1(A, B, None, None, None, 1, 1, 1, 16, 4, 0, None) == NULL
+    assert f1(A, B, None, None, C, 1, 1, 1, 16, 4, -1, None) == SHAPE

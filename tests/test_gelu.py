@@ -1,0 +1,103 @@
+"""GPU parity of the fused layer tail (fno_spectral_conv2d_gelu / _1d_gelu:
+GELU of the spectral convolution plus bias, with a second branch added
+before or after the activation) against the fp64 oracle, which the CPU suite
+pins by normal-CDF table values and a DC-identity closed form.  Same bar as
+the plain operator: relative L2 error <= 1e-5 and max-abs error <=
+1e-4 * max|ref|.
+"""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import oracle  # noqa: E402
+import fft_spectral_convolution_amd as fno  # noqa: E402
+from fft_spectral_convolution_amd.inputs import CONFIGS, Config, make_inputs  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+REL_L2 = 1e-5
+MAX_ABS = 1e-4
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu_present():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    fno.lib()
+
+
+def assert_close(gpu, ref, what):
+    g = gpu.detach().cpu().numpy().astype(np.float64)
+    rel = np.linalg.norm((g - ref).ravel()) / max(np.linalg.norm(ref.ravel()), 1e-300)
+    mx = np.max(np.abs(g - ref)) / max(np.max(np.abs(ref)), 1e-300)
+    print(f"  {what}: rel_l2={rel:.3e} max_abs/max|ref|={mx:.3e}", flush=True)
+    assert rel <= REL_L2, f"{what}: relative L2 error {rel:.3e} > {REL_L2}"
+    assert mx <= MAX_ABS, f"{what}: max-abs error {mx:.3e} > {MAX_ABS} * max|ref|"
+
+
+def check(cfg, seed=0, use_bias=True, use_branch=True, branch_after=False):
+    x, w = make_inputs(cfg, seed)
+    rng = np.random.default_rng(seed + 200)
+    out_shape = (cfg.B, cfg.Cout, cfg.W) if cfg.kind == "1d" else (cfg.B, cfg.Cout, cfg.H, cfg.W)
+    bias = rng.standard_normal(cfg.Cout).astype(np.float32) if use_bias else None
+    branch = rng.standard_normal(out_shape).astype(np.float32) if use_branch else None
+    dev = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(DEV)  # noqa: E731
+    xd, wd, bd, rd = dev(x), dev(w), dev(bias), dev(branch)
+    if cfg.kind == "1d":
+        out = fno.fno_spectral_conv1d_gelu(xd, wd, cfg.my, bias=bd, branch=rd, branch_after=branch_after)
+        ref = oracle.spectral_conv1d_gelu_ref(x, w, cfg.my, bias=bias, branch=branch, branch_after=branch_after)
+    else:
+        out = fno.fno_spectral_conv2d_gelu(xd, wd, cfg.mx, cfg.my, bias=bd, branch=rd, branch_after=branch_after)
+        ref = oracle.spectral_conv2d_gelu_ref(x, w, cfg.mx, cfg.my, bias=bias, branch=branch,
+                                              branch_after=branch_after)
+    torch.cuda.synchronize()
+    assert fno.fno_last_kernels()[-1].endswith("_gelu")
+    assert_close(out, ref, f"{cfg.name} gelu(branch_after={branch_after})")
+
+
+@pytest.mark.parametrize("branch_after", [False, True])
+@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4"])
+def test_gelu_workloads(name, branch_after):
+    cfg = CONFIGS[name]
+    print(f"\n[{name} gelu] {cfg.describe()}", flush=True)
+    check(cfg, branch_after=branch_after)
+
+
+GELU_2D = [
+    # B, Cin, Cout, H, W, mx, my      (inverse kernel that applies the tail)
+    (2, 3, 5, 8, 8, 4, 5),            # small-grid kernel, Nyquist column kept
+    (3, 4, 6, 32, 16, 3, 9),          # small-grid kernel
+    (2, 8, 16, 64, 64, 16, 16),       # one row per thread
+    (2, 4, 6, 64, 128, 8, 20),        # one row per thread, 64 x 128
+    (1, 2, 3, 256, 256, 9, 11),       # staged: generic rows
+    (1, 2, 3, 16, 1024, 5, 50),       # staged: pruned long rows
+    (1, 2, 2, 1024, 16, 8, 9),        # staged: pruned columns, generic rows
+]
+
+
+@pytest.mark.parametrize("shape", GELU_2D, ids=lambda s: "x".join(map(str, s)))
+def test_gelu_shapes_2d(shape):
+    b, cin, cout, h, w, mx, my = shape
+    check(Config("gelu", "2d", b, cin, cout, h, w, mx, my, "uniform"), 7, branch_after=bool(h % 3))
+
+
+GELU_1D = [
+    # B, Cin, Cout, N, modes
+    (3, 2, 5, 16, 9),                 # generic rows, every bin kept
+    (5, 3, 2, 512, 64),               # pruned rows
+    (2, 4, 3, 4096, 33),              # pruned rows, longest
+]
+
+
+@pytest.mark.parametrize("shape", GELU_1D, ids=lambda s: "x".join(map(str, s)))
+def test_gelu_shapes_1d(shape):
+    b, cin, cout, n, modes = shape
+    check(Config("gelu1d", "1d", b, cin, cout, 1, n, 1, modes, "normal"), 8, branch_after=bool(n % 3))
+
+
+@pytest.mark.parametrize("use_bias,use_branch", [(False, False), (True, False), (False, True)])
+def test_gelu_optional_terms(use_bias, use_branch):
+    check(Config("gelu", "2d", 2, 8, 16, 128, 128, 8, 8, "uniform"), 9, use_bias=use_bias, use_branch=use_branch)
+    check(Config("gelu1d", "1d", 4, 3, 4, 1, 2048, 1, 20, "normal"), 10, use_bias=use_bias, use_branch=use_branch)
