@@ -2,6 +2,7 @@
 """Benchmark of libfno's spectral convolution on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c3] [--variant fused|unfused]
+                    [--pass forward|backward|layer]
 
 One step = one full spectral-convolution call (forward pruned FFT, per-mode
 channel mix, inverse pruned FFT) over one batch of synthetic inputs already
@@ -23,6 +24,10 @@ launch over its average launch time), a `mix` entry for the matrix-core
 channel mix (its flops against the fp32 MFMA peak) when the workload uses
 it, and a `cpu_baseline` entry: the fp64 CPU oracle timed on this host on a
 bounded sample.
+
+--pass backward times both gradients of a real loss (compulsory bytes: x, W,
+dL/dout read, dL/dx, dL/dW written); --pass layer times the operator with
+the fused layer tail gelu(conv + bias + branch) (adds the branch read).
 """
 from __future__ import annotations
 
@@ -83,6 +88,9 @@ def kernel_bytes(name: str, cfg, backward: bool = False) -> int:
         "fused1d": n_in + wb + n_out,
         # backward pass: the weight gradient reads both truncated spectra and
         # writes a weight-sized gradient; the adjoint transposes the weight
+        # fused layer tail: the inverse also reads the branch (output-sized)
+        "inv2d_gelu": yh + 2 * n_out,
+        "rows_inv_gelu": (r_out if cfg.kind == "2d" else yh) + 2 * n_out,
         "wgrad": xh + yh + wb,
         "wadjoint": 2 * wb,
         # sum of the batch splits' partial weight gradients (when the batch
@@ -116,9 +124,10 @@ def load_traffic(kernel: str, workload: str):
         return None
 
 
-def cpu_baseline(cfg, x, w, budget_s: float = 12.0, g=None, compulsory=None):
+def cpu_baseline(cfg, x, w, budget_s: float = 12.0, g=None, compulsory=None, layer=None):
     """Time the fp64 oracle (as it stands) on this host on a bounded sample
-    (the backward pass when the output gradient g is given)."""
+    (the backward pass when the output gradient g is given, the operator with
+    the layer tail when layer = (bias, branch) is)."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -127,6 +136,11 @@ def cpu_baseline(cfg, x, w, budget_s: float = 12.0, g=None, compulsory=None):
         threads = 1
     # one batch item first, to size the sample
     def call(nb):
+        if layer is not None:
+            bias, branch = layer
+            if cfg.kind == "1d":
+                return oracle.spectral_conv1d_gelu_ref(x[:nb], w, cfg.my, bias=bias, branch=branch[:nb])
+            return oracle.spectral_conv2d_gelu_ref(x[:nb], w, cfg.mx, cfg.my, bias=bias, branch=branch[:nb])
         if g is not None:
             if cfg.kind == "1d":
                 return oracle.spectral_conv1d_backward_ref(x[:nb], w, g[:nb], cfg.my)
@@ -169,8 +183,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="c3", choices=sorted(CONFIGS))
     ap.add_argument("--variant", default="fused", choices=["fused", "unfused"])
-    ap.add_argument("--pass", dest="which", default="forward", choices=["forward", "backward"],
-                    help="time the operator (default) or its backward pass (both gradients)")
+    ap.add_argument("--pass", dest="which", default="forward", choices=["forward", "backward", "layer"],
+                    help="time the operator (default), its backward pass (both gradients), or the operator "
+                         "with the fused layer tail gelu(conv + bias + branch)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -213,6 +228,7 @@ def main():
 
     compulsory = cfg.compulsory_bytes
     g_np = None
+    layer_np = None
     if args.which == "backward":
         # step: both gradients of a real loss, given a synthetic dL/dout of the
         # output's shape; compulsory bytes: x, w, dL/dout read, dL/dx, dL/dw written
@@ -229,6 +245,24 @@ def main():
         else:
             step = lambda i: fno.fno_spectral_conv2d_backward(xs[i % nsets], w, gs[i % nsets], cfg.mx, cfg.my,
                                                               grad_x=gxs[i % nsets], grad_w=gw)
+    elif args.which == "layer":
+        # step: out = gelu(conv + bias[o] + branch), branch an output-sized
+        # tensor; compulsory bytes: x, w, bias, branch read, out written
+        rng = np.random.default_rng(2)
+        br_np = rng.standard_normal(cfg.out_shape).astype(np.float32)
+        bias_np = rng.standard_normal(cfg.Cout).astype(np.float32)
+        layer_np = (bias_np, br_np)
+        bias = torch.from_numpy(bias_np).to(dev)
+        brs = [torch.from_numpy(br_np).to(dev)]
+        for _ in range(nsets - 1):
+            brs.append(brs[0].clone())
+        compulsory = cfg.compulsory_bytes + int(br_np.nbytes) + 4 * cfg.Cout
+        if cfg.kind == "1d":
+            step = lambda i: fno.fno_spectral_conv1d_gelu(xs[i % nsets], w, cfg.my, bias=bias, branch=brs[i % nsets],
+                                                          out=outs[i % nsets])
+        else:
+            step = lambda i: fno.fno_spectral_conv2d_gelu(xs[i % nsets], w, cfg.mx, cfg.my, bias=bias,
+                                                          branch=brs[i % nsets], out=outs[i % nsets])
     elif cfg.kind == "1d":
         fn = fno.fno_spectral_conv1d if args.variant == "fused" else fno.fno_spectral_conv1d_unfused
         step = lambda i: fn(xs[i % nsets], w, cfg.my, out=outs[i % nsets])
@@ -283,7 +317,7 @@ def main():
     dom_name = kernels[dom]
     dom_bytes = kernel_bytes(dom_name, cfg, args.which == "backward")
     achieved = dom_bytes / (per_kernel_ms[dom] * 1e-3) / 1e9
-    traffic = load_traffic(dom_name, cfg.name if args.which == "forward" else cfg.name + "/backward")
+    traffic = load_traffic(dom_name, cfg.name if args.which == "forward" else f"{cfg.name}/{args.which}")
 
     gbs = compulsory / (ms_per_step * 1e-3) / 1e9
     # bytes of all buffers the timed steps touch (the backward adds dL/dx per
@@ -291,6 +325,8 @@ def main():
     touched = nsets * set_bytes + w_np.nbytes
     if args.which == "backward":
         touched += nsets * x_np.nbytes + w_np.nbytes
+    elif args.which == "layer":
+        touched += nsets * 4 * int(np.prod(cfg.out_shape))
     line = {
         "metric": "spectral-conv GB/s (HBM % of peak) and layer calls/s vs fp64 CPU oracle",
         "value": round(gbs, 3),
@@ -334,7 +370,7 @@ def main():
             "avg_launch_us": round(per_kernel_ms[dom] * 1e3, 3),
         },
     }
-    if "mix_mfma" in kernels and args.which == "forward":
+    if "mix_mfma" in kernels and args.which != "backward":
         # the matrix-core stage against the fp32 MFMA peak: executed flops of
         # the 3M form (three real GEMMs, 2 flops per multiply-add), and the
         # algorithmic count of 8 flops per complex multiply-add
@@ -354,7 +390,8 @@ def main():
             "avg_launch_us": round(per_kernel_ms[k] * 1e3, 3),
         }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(cfg, x_np, w_np, args.cpu_budget, g=g_np, compulsory=compulsory)
+        line["cpu_baseline"] = cpu_baseline(cfg, x_np, w_np, args.cpu_budget, g=g_np, compulsory=compulsory,
+                                            layer=layer_np)
     print(json.dumps(line), flush=True)
 
 

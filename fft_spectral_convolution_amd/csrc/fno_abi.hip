@@ -252,7 +252,7 @@ int run_inverse2d_staged(const Shape2d& s, int64_t C, const float2* yh, float* o
     if (e != hipSuccess) return hip_fail(e);
     rec_kernel(epi.on ? "rows_inv_gelu" : "rows_inv", st);
     Epilogue ep = epi;
-    ep.rows_per_chan = s.H;
+    ep.rows_per_chan = (uint32_t)s.H;
     e = launch_rows_inv(r, out, s.B * C * s.H, s.log2W, s.my, s.my, scale, tw, st, ep);
     if (e != hipSuccess) return hip_fail(e);
     return FNO_OK;
@@ -377,7 +377,7 @@ int check_epilogue(const float* bias, const float* branch, const float* out, int
     epi->on = true;
     epi->bias = bias;
     epi->branch = branch;
-    epi->cout = Cout;
+    epi->cout = (uint32_t)Cout;
     epi->branch_after = branch_after;
     return FNO_OK;
 }
@@ -702,6 +702,7 @@ int fno_spectral_conv2d_gelu(const float* x, const void* w, const float* bias, c
     int rc = check_dims_2d(B, Cin, H, W, mx, my);
     if (rc) return rc;
     if (Cout < 1) return FNO_ERR_SHAPE;
+    if ((uint64_t)B * Cout * H > UINT32_MAX) return FNO_ERR_SHAPE;     // output rows indexed in 32 bits
     if (!out) return FNO_ERR_NULL;
     Epilogue epi;
     rc = check_epilogue(bias, branch, out, Cout, (size_t)B * Cout * H * W * sizeof(float), branch_after, &epi);
@@ -714,6 +715,7 @@ int fno_spectral_conv1d_gelu(const float* x, const void* w, const float* bias, c
     int rc = check_dims_1d(B, Cin, N, modes);
     if (rc) return rc;
     if (Cout < 1) return FNO_ERR_SHAPE;
+    if ((uint64_t)B * Cout > UINT32_MAX) return FNO_ERR_SHAPE;         // output rows indexed in 32 bits
     if (!out) return FNO_ERR_NULL;
     Epilogue epi;
     rc = check_epilogue(bias, branch, out, Cout, (size_t)B * Cout * N * sizeof(float), branch_after, &epi);

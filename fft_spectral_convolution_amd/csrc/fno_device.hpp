@@ -244,6 +244,10 @@ __device__ __forceinline__ float4 buffer_load_f4(__amdgpu_buffer_rsrc_t r, uint3
     return make_float4(__uint_as_float(v[0]), __uint_as_float(v[1]), __uint_as_float(v[2]), __uint_as_float(v[3]));
 }
 
+__device__ __forceinline__ float buffer_load_f1(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, 0));
+}
+
 __device__ __forceinline__ float2 buffer_load_f2(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
     const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, (int)soff, 0);
     return make_float2(__uint_as_float(v[0]), __uint_as_float(v[1]));

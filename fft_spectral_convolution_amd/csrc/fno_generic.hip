@@ -164,12 +164,16 @@ __global__ __launch_bounds__(kThreads) void k_rows_inv(const float2* __restrict_
         const int64_t ra = 2 * (pair0 + pr);
         const float2 z = res[pr * W + n];
         if constexpr (EPI) {
-            const float br0 = epi.branch ? epi.branch[ra * W + n] : 0.0f;
-            out[ra * W + n] = epi_apply(epi, z.x * scale, epi_bias(epi, ra), br0);
-            if (ra + 1 < nrows) {
-                const float br1 = epi.branch ? epi.branch[(ra + 1) * W + n] : 0.0f;
-                out[(ra + 1) * W + n] = epi_apply(epi, z.y * scale, epi_bias(epi, ra + 1), br1);
-            }
+            // the branch through a buffer resource (an empty range for a null
+            // branch reads zero); rows 2 pair0 .. of this block
+            const __amdgpu_buffer_rsrc_t rb =
+                make_rsrc(epi.branch ? epi.branch + 2 * pair0 * W : nullptr,
+                          epi.branch ? (uint32_t)((nrows - 2 * pair0 < 2 * P ? nrows - 2 * pair0 : 2 * P) * W * 4) : 0u);
+            const uint32_t off = (uint32_t)((ra - 2 * pair0) * W + n) * 4u;
+            out[ra * W + n] = epi_apply(epi, z.x * scale, epi_bias(epi, (uint32_t)ra), buffer_load_f1(rb, off, 0));
+            if (ra + 1 < nrows)
+                out[(ra + 1) * W + n] = epi_apply(epi, z.y * scale, epi_bias(epi, (uint32_t)(ra + 1)),
+                                                  buffer_load_f1(rb, off + (uint32_t)W * 4u, 0));
         } else {
             out[ra * W + n] = z.x * scale;
             if (ra + 1 < nrows) out[(ra + 1) * W + n] = z.y * scale;

@@ -282,10 +282,10 @@ __device__ __forceinline__ float2 packed_c2r_bin(const float2 (&X)[MYMAX]) {
 // inverse DFTs over k1), its rows in the LDS plane; then one thread per row
 // builds the packed spectrum Z, runs the W/2-point inverse DFT in registers
 // and hands its row out through the stage to coalesced buffer stores.  EPI:
-// the fused output epilogue (bias, GELU, second branch) runs as a second
-// pass over the image once its rows are stored and their registers free:
-// every lane reads back the float4s it wrote (still in L2) with the branch
-// at the same offsets, applies it and stores again.
+// the fused output epilogue (bias, GELU, second branch) is applied to each
+// float4 between the stage and the store; a chunk's branch float4s are
+// loaded only once that chunk of the rows has left the registers for the
+// stage (the row registers are the kernel's peak).
 template <int LOG2H, int LOG2W, int MYMAX, bool EPI>
 __global__ __launch_bounds__(1 << LOG2H) __attribute__((amdgpu_waves_per_eu(2))) void k_inv2d_rows(
     const float2* __restrict__ yh, float* __restrict__ out, ImageBase ib, int st, int64_t nimg, int mx, int my,
@@ -392,43 +392,38 @@ __global__ __launch_bounds__(1 << LOG2H) __attribute__((amdgpu_waves_per_eu(2)))
         {
             const __amdgpu_buffer_rsrc_t ro = make_rsrc(out + img * (int64_t)(H * W), (uint32_t)(H * W * 4));
             float* stage = reinterpret_cast<float*>(xreg) + (tid >> 6) * 64 * S::SS;
+            // epilogue: the image's bias, its branch image (a null branch gets
+            // an empty range: its loads read zero)
+            float bias = 0.0f;
+            __amdgpu_buffer_rsrc_t rb = ro;
+            if constexpr (EPI) {
+                bias = epi_bias(epi, (uint32_t)img);
+                rb = make_rsrc(epi.branch ? epi.branch + img * (int64_t)(H * W) : nullptr,
+                               epi.branch ? (uint32_t)(H * W * 4) : 0u);
+            }
             static_for<0, S::NCK>([&](auto c) {
                 static_for<0, 8>([&](auto q) {
                     *reinterpret_cast<float4*>(stage + lane * S::SS + 4 * q) =
                         make_float4(z[2 * (8 * c + q)].x, z[2 * (8 * c + q)].y, z[2 * (8 * c + q) + 1].x,
                                     z[2 * (8 * c + q) + 1].y);
                 });
+                float4 br[EPI ? 8 : 1];
+                if constexpr (EPI) {
+                    __builtin_amdgcn_sched_barrier(0);      // the chunk's rows are in the stage first
+                    static_for<0, 8>([&](auto ii) { br[ii] = buffer_load_f4(rb, soffs[ii] + 128 * c, 0); });
+                }
                 wave_lds_sync();
                 static_for<0, 8>([&](auto ii) {
-                    const float4 o =
+                    float4 o =
                         *reinterpret_cast<const float4*>(stage + (8 * ii + (lane >> 3)) * S::SS + 4 * (lane & 7));
+                    if constexpr (EPI) {
+                        o = make_float4(epi_apply(epi, o.x, bias, br[ii].x), epi_apply(epi, o.y, bias, br[ii].y),
+                                        epi_apply(epi, o.z, bias, br[ii].z), epi_apply(epi, o.w, bias, br[ii].w));
+                    }
                     buffer_store_f4(o, ro, soffs[ii] + 128 * c, 0);
                 });
                 wave_lds_sync();
             });
-            if constexpr (EPI) {
-                // this lane's stores complete before it reads them back
-                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-                const float bias = epi_bias(epi, img);
-                // a null branch gets an empty range: its loads read zero
-                const __amdgpu_buffer_rsrc_t rb =
-                    make_rsrc(epi.branch ? epi.branch + img * (int64_t)(H * W) : out, epi.branch ? (uint32_t)(H * W * 4) : 0u);
-                static_for<0, S::NCK>([&](auto c) {
-                    float4 o[8], br[8];
-                    static_for<0, 8>([&](auto ii) {
-                        o[ii] = buffer_load_f4(ro, soffs[ii] + 128 * c, 0);
-                        br[ii] = buffer_load_f4(rb, soffs[ii] + 128 * c, 0);
-                    });
-                    static_for<0, 8>([&](auto ii) {
-                        const float4 v = make_float4(epi_apply(epi, o[ii].x, bias, br[ii].x),
-                                                     epi_apply(epi, o[ii].y, bias, br[ii].y),
-                                                     epi_apply(epi, o[ii].z, bias, br[ii].z),
-                                                     epi_apply(epi, o[ii].w, bias, br[ii].w));
-                        buffer_store_f4(v, ro, soffs[ii] + 128 * c, 0);
-                    });
-                    __builtin_amdgcn_sched_barrier(0);
-                });
-            }
         }
     }
 }

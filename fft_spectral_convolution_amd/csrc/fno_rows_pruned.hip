@@ -230,7 +230,7 @@ __global__ __launch_bounds__(kPrunedThreads) __attribute__((amdgpu_waves_per_eu(
 // EPI: the fused output epilogue (bias, GELU, second branch) on every
 // output, the branch read at the same index.
 template <int Q, bool EPI>
-__global__ __launch_bounds__(kPrunedThreads) __attribute__((amdgpu_waves_per_eu(2))) void k_rows_inv_pruned(const float2* __restrict__ y,
+__global__ __launch_bounds__(kPrunedThreads) __attribute__((amdgpu_waves_per_eu(EPI ? (Q == 64 ? 3 : 4) : 2))) void k_rows_inv_pruned(const float2* __restrict__ y,
                                                                     float* __restrict__ out, int64_t nrows, int my,
                                                                     int y_ld, float scale,
                                                                     const float2* __restrict__ tw, Epilogue epi) {
@@ -283,28 +283,30 @@ __global__ __launch_bounds__(kPrunedThreads) __attribute__((amdgpu_waves_per_eu(
         static_for<0, NZ>([&](auto k) { z[k] = packed_bin<Q, k>(H); });
         dft<NZ, 1>(z);
         float* const dst = out + row * N + lane;
-#pragma unroll
-        for (int m = 0; m < NZ; ++m) {
-            dst[64 * (2 * m)] = z[m].x;
-            dst[64 * (2 * m + 1)] = z[m].y;
-        }
         if constexpr (EPI) {
-            // second pass once the row's registers are free: the lane reads
-            // back the Q values it stored (still in L2), applies the epilogue
-            // with the branch at the same index and stores again
-            __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
-            const float bias = epi_bias(epi, row);
-            const float* const brow = epi.branch ? epi.branch + row * N + lane : nullptr;
-#pragma unroll 1
-            for (int m = 0; m < Q; m += 8) {
-                float v[8], b[8];
+            // the row's branch through a buffer resource (an empty range for
+            // a null branch: its loads read zero, no branch in the code)
+            // the row index is uniform across the wave: move it to scalar
+            // registers so that the resource and the bias stay scalar
+            const uint32_t urow = __builtin_amdgcn_readfirstlane((uint32_t)row);
+            const float bias = epi_bias(epi, urow);
+            const __amdgpu_buffer_rsrc_t rb =
+                make_rsrc(epi.branch ? epi.branch + (int64_t)urow * N : out, epi.branch ? (uint32_t)(N * 4) : 0u);
+            // every branch load of the row is issued before the first
+            // activation, so that the row waits for one round trip only
+            float br[2 * NZ];
 #pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    v[j] = dst[64 * (m + j)];
-                    b[j] = brow ? brow[64 * (m + j)] : 0.0f;
-                }
+            for (int k = 0; k < 2 * NZ; ++k) br[k] = buffer_load_f1(rb, (uint32_t)(lane + 64 * k) * 4u, 0);
 #pragma unroll
-                for (int j = 0; j < 8; ++j) dst[64 * (m + j)] = epi_apply(epi, v[j], bias, b[j]);
+            for (int m = 0; m < NZ; ++m) {
+                dst[64 * (2 * m)] = epi_apply(epi, z[m].x, bias, br[2 * m]);
+                dst[64 * (2 * m + 1)] = epi_apply(epi, z[m].y, bias, br[2 * m + 1]);
+            }
+        } else {
+#pragma unroll
+            for (int m = 0; m < NZ; ++m) {
+                dst[64 * (2 * m)] = z[m].x;
+                dst[64 * (2 * m + 1)] = z[m].y;
             }
         }
     }

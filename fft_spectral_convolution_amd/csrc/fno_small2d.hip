@@ -434,13 +434,16 @@ __global__ __launch_bounds__(kSmallThreads, kSmallBlocksPerCU) void k_inv2d_smal
                 float2* oa = reinterpret_cast<float2*>(oi + p * W) + t;
                 float2* ob = reinterpret_cast<float2*>(oi + (p + P) * W) + t;
                 if constexpr (EPI) {
-                    const float bias = epi_bias(epi, img);
-                    const float2* ba = epi.branch ? reinterpret_cast<const float2*>(epi.branch + img * (int64_t)(H * W) + p * W) + t : nullptr;
-                    const float2* bb = epi.branch ? reinterpret_cast<const float2*>(epi.branch + img * (int64_t)(H * W) + (p + P) * W) + t : nullptr;
+                    // the image's branch through a buffer resource (an empty
+                    // range for a null branch reads zero)
+                    const float bias = epi_bias(epi, (uint32_t)img);
+                    const __amdgpu_buffer_rsrc_t rb =
+                        make_rsrc(epi.branch ? epi.branch + img * (int64_t)(H * W) : nullptr,
+                                  epi.branch ? (uint32_t)(H * W * 4) : 0u);
 #pragma unroll
                     for (int m = 0; m < MW; ++m) {
-                        const float2 za = ba ? ba[TW * m] : make_float2(0.0f, 0.0f);
-                        const float2 zb = bb ? bb[TW * m] : make_float2(0.0f, 0.0f);
+                        const float2 za = buffer_load_f2(rb, (uint32_t)((p * W + 2 * (t + TW * m)) * 4), 0);
+                        const float2 zb = buffer_load_f2(rb, (uint32_t)(((p + P) * W + 2 * (t + TW * m)) * 4), 0);
                         oa[TW * m] = make_float2(epi_apply(epi, v0[m].x * scale, bias, za.x),
                                                  epi_apply(epi, v1[m].x * scale, bias, za.y));
                         ob[TW * m] = make_float2(epi_apply(epi, v0[m].y * scale, bias, zb.x),
