@@ -101,3 +101,32 @@ def test_gelu_shapes_1d(shape):
 def test_gelu_optional_terms(use_bias, use_branch):
     check(Config("gelu", "2d", 2, 8, 16, 128, 128, 8, 8, "uniform"), 9, use_bias=use_bias, use_branch=use_branch)
     check(Config("gelu1d", "1d", 4, 3, 4, 1, 2048, 1, 20, "normal"), 10, use_bias=use_bias, use_branch=use_branch)
+
+
+@pytest.mark.parametrize("kind,shape", [
+    ("2d", (1, 1, 2, 64, 64, 8, 8)),        # one row per thread
+    ("2d", (1, 1, 2, 32, 32, 4, 4)),        # small-grid kernel
+    ("2d", (1, 1, 2, 256, 256, 4, 4)),      # staged, generic rows
+    ("1d", (1, 1, 2, 1, 2048, 1, 16)),      # pruned long rows
+])
+def test_gelu_activation_accuracy(kind, shape):
+    # x = 0 makes the transform chain exactly zero, so out = gelu(branch):
+    # the device activation against the exact erf form over [-12, 12]
+    b, cin, cout, h, w, mx, my = shape
+    out_shape = (b, cout, w) if kind == "1d" else (b, cout, h, w)
+    n = int(np.prod(out_shape))
+    u = np.linspace(-12.0, 12.0, n).astype(np.float32).reshape(out_shape)
+    xd = torch.zeros((b, cin, w) if kind == "1d" else (b, cin, h, w), device=DEV)
+    if kind == "1d":
+        wd = torch.ones((my, cin, cout), dtype=torch.complex64, device=DEV)
+        out = fno.fno_spectral_conv1d_gelu(xd, wd, my, branch=torch.from_numpy(u).to(DEV))
+    else:
+        wd = torch.ones((2, mx, my, cin, cout), dtype=torch.complex64, device=DEV)
+        out = fno.fno_spectral_conv2d_gelu(xd, wd, mx, my, branch=torch.from_numpy(u).to(DEV))
+    torch.cuda.synchronize()
+    ref = oracle.gelu(u.astype(np.float64))
+    err = np.abs(out.cpu().numpy().astype(np.float64) - ref)
+    bound = 1e-6 * np.maximum(1.0, np.abs(u.astype(np.float64)))
+    worst = int(np.argmax(err / bound))
+    print(f"  max err {err.max():.3e}; worst ratio {float((err / bound).ravel()[worst]):.3f} at u={u.ravel()[worst]:.4f}")
+    assert np.all(err <= bound)
