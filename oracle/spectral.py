@@ -46,6 +46,13 @@ upcast exactly):
      branch after the activation:   out = gelu(conv + bias[o]) + branch
    gelu(u) = u Phi(u) = u (1 + erf(u / sqrt 2)) / 2, the exact form (the page
    names GELU without choosing between it and its tanh approximation).
+8. diagonal global filter / token mixer (P1 section 5.2: fft2 -> learnable
+   mask -> ifft2 on a 512 x 512 image; P2 section 3.2: R2C along the
+   sequence -> learnable complex mask -> C2R): one complex weight per kept
+   mode and channel, no channel mixing,
+     Yh[b,c,s,r,ky] = Xh[b,c,s,r,ky] * M[s,r,ky,c]   (1D: M[ky,c]),
+   then step 4.  Keeping every mode (mx = H/2, my = W/2 + 1) gives the
+   untruncated global filter.
 
 Two independent ways of computing the transforms are provided:
 
@@ -87,6 +94,8 @@ __all__ = [
     "gelu",
     "spectral_conv2d_gelu_ref",
     "spectral_conv1d_gelu_ref",
+    "spectral_filter2d_ref",
+    "spectral_filter1d_ref",
 ]
 
 
@@ -424,6 +433,33 @@ def spectral_conv1d_gelu_ref(x, weight, modes: int, bias=None, branch=None, bran
     """The 1D form of spectral_conv2d_gelu_ref (branch [B,Cout,N])."""
     y = spectral_conv1d_ref(x, weight, modes, transform)
     return _layer_tail(y, bias, branch, branch_after, (1, -1, 1))
+
+
+# --------------------------------------------------------------------------
+# Diagonal global filter: one complex weight per kept mode and channel
+# --------------------------------------------------------------------------
+
+def spectral_filter2d_ref(x, mask, mx: int, my: int, transform: str = "dft"):
+    """out = C2R(truncate(R2C(x)) * mask), mask[2,mx,my,C] complex, x[B,C,H,W]."""
+    x = np.asarray(x)
+    mask = np.asarray(mask, dtype=np.complex128)
+    _, c, h, w = x.shape
+    if mask.shape != (2, mx, my, c):
+        raise ValueError(f"mask shape {mask.shape} does not match (2, {mx}, {my}, {c})")
+    xh = forward_truncated_2d(x, mx, my, transform)              # [B,C,2,mx,my]
+    yh = xh * np.moveaxis(mask, -1, 0)[None]                     # [C,2,mx,my] per channel
+    return inverse_from_truncated_2d(yh, h, w, transform)
+
+
+def spectral_filter1d_ref(x, mask, modes: int, transform: str = "dft"):
+    """The 1D form: mask[modes,C], x[B,C,N]."""
+    x = np.asarray(x)
+    mask = np.asarray(mask, dtype=np.complex128)
+    _, c, n = x.shape
+    if mask.shape != (modes, c):
+        raise ValueError(f"mask shape {mask.shape} does not match ({modes}, {c})")
+    xh = forward_truncated_1d(x, modes, transform)               # [B,C,modes]
+    return inverse_from_truncated_1d(xh * mask.T[None], n, transform)
 
 
 # --------------------------------------------------------------------------

@@ -718,3 +718,84 @@ def test_layer_tail_optional_terms():
     for after in (False, True):
         out = S.spectral_conv2d_gelu_ref(x, wt, 2, 3, branch_after=after)
         assert np.max(np.abs(out - S.gelu(conv))) == 0.0
+
+
+# --------------------------------------------------------------------------
+# Diagonal global filter: one complex weight per kept mode and channel
+# --------------------------------------------------------------------------
+
+def _diag_weight(mask):
+    # mask [..., C] -> weight [..., C, C] with the mask on the diagonal
+    c = mask.shape[-1]
+    wt = np.zeros(mask.shape + (c,), dtype=np.complex128)
+    for i in range(c):
+        wt[..., i, i] = mask[..., i]
+    return wt
+
+
+@pytest.mark.parametrize("transform", TRANSFORMS)
+@pytest.mark.parametrize("shape", [(2, 3, 8, 8, 2, 3), (1, 4, 16, 8, 8, 5), (2, 2, 8, 16, 3, 9)])
+def test_filter_is_conv_with_diagonal_weight(transform, shape):
+    # the filter equals the (independently pinned) spectral convolution whose
+    # weight is diagonal in the channels
+    b, c, h, w, mx, my = shape
+    rng = np.random.default_rng(50)
+    x = rng.standard_normal((b, c, h, w))
+    mask = rand_c(rng, (2, mx, my, c))
+    out = S.spectral_filter2d_ref(x, mask, mx, my, transform)
+    assert rel(out, S.spectral_conv2d_ref(x, _diag_weight(mask), mx, my, transform)) < 1e-12
+    x1 = rng.standard_normal((b, c, w))
+    m1 = rand_c(rng, (my, c))
+    out1 = S.spectral_filter1d_ref(x1, m1, my, transform)
+    assert rel(out1, S.spectral_conv1d_ref(x1, _diag_weight(m1), my, transform)) < 1e-12
+
+
+def test_filter_full_modes_unit_mask_is_identity():
+    rng = np.random.default_rng(51)
+    h, w, c = 8, 16, 3
+    x = rng.standard_normal((2, c, h, w))
+    out = S.spectral_filter2d_ref(x, np.ones((2, h // 2, w // 2 + 1, c)), h // 2, w // 2 + 1)
+    assert rel(out, x) < 1e-12
+    x1 = rng.standard_normal((2, c, w))
+    assert rel(S.spectral_filter1d_ref(x1, np.ones((w // 2 + 1, c)), w // 2 + 1), x1) < 1e-12
+
+
+@pytest.mark.parametrize("block", [0, 1])
+def test_filter_single_cosine_closed_form(block):
+    # x = cos(theta), theta = 2 pi (kx h / H + ky w / W), 0 < ky < W/2, with kx
+    # in block 0 (kx = r) or block 1 (kx = H - mx + r): the kept half spectrum
+    # holds sqrt(HW)/2 at (kx, ky) only, so the output is Re(m e^{i theta})
+    # = a cos(theta) - b sin(theta) for the mask value m = a + ib there
+    h, w, mx, my, c = 16, 16, 4, 5, 2
+    r, ky = 2, 3
+    kx = r if block == 0 else h - mx + r
+    hh, ww = np.meshgrid(np.arange(h), np.arange(w), indexing="ij")
+    theta = 2 * np.pi * (kx * hh / h + ky * ww / w)
+    x = np.broadcast_to(np.cos(theta), (1, c, h, w)).copy()
+    mask = np.zeros((2, mx, my, c), dtype=np.complex128)
+    vals = [0.7 - 1.3j, -0.4 + 0.25j]
+    for ch in range(c):
+        mask[block, r, ky, ch] = vals[ch]
+    out = S.spectral_filter2d_ref(x, mask, mx, my)
+    for ch in range(c):
+        a, b = vals[ch].real, vals[ch].imag
+        assert np.max(np.abs(out[0, ch] - (a * np.cos(theta) - b * np.sin(theta)))) < 1e-12
+    # planted mistakes: a conjugated mask, the channels of the mask swapped
+    conj = S.spectral_filter2d_ref(x, np.conj(mask), mx, my)
+    swapped = S.spectral_filter2d_ref(x, mask[..., ::-1], mx, my)
+    expect0 = vals[0].real * np.cos(theta) - vals[0].imag * np.sin(theta)
+    assert np.max(np.abs(conj[0, 0] - expect0)) > 0.1
+    assert np.max(np.abs(swapped[0, 0] - expect0)) > 0.1
+
+
+def test_filter_1d_single_cosine_closed_form():
+    n, modes, c, k = 32, 6, 3, 4
+    t = np.arange(n)
+    theta = 2 * np.pi * k * t / n
+    x = np.broadcast_to(np.cos(theta), (2, c, n)).copy()
+    mask = np.zeros((modes, c), dtype=np.complex128)
+    mask[k] = [1.5 + 0.5j, -2.0j, 0.3]
+    out = S.spectral_filter1d_ref(x, mask, modes)
+    for ch in range(c):
+        m = mask[k, ch]
+        assert np.max(np.abs(out[:, ch] - (m.real * np.cos(theta) - m.imag * np.sin(theta)))) < 1e-12
