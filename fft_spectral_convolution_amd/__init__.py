@@ -32,6 +32,8 @@ __all__ = [
     "fno_spectral_conv1d_backward",
     "fno_spectral_conv2d_gelu",
     "fno_spectral_conv1d_gelu",
+    "fno_spectral_filter2d",
+    "fno_spectral_filter1d",
     "fno_workspace_size_2d",
     "fno_workspace_size_1d",
     "fno_forward2d",
@@ -76,6 +78,8 @@ _SIGNATURES = {
     "fno_spectral_conv1d_backward": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P]),
     "fno_spectral_conv2d_gelu": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _P]),
     "fno_spectral_conv1d_gelu": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P]),
+    "fno_spectral_filter2d": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _I, _P]),
+    "fno_spectral_filter1d": (_I, [_P, _P, _P, _I, _I, _I, _I, _P]),
     "fno_set_timing_events": (_I, [ctypes.POINTER(ctypes.c_void_p), _I]),
     "fno_last_kernel_count": (_I, []),
     "fno_last_kernel_name": (ctypes.c_char_p, [_I]),
@@ -243,6 +247,44 @@ def fno_spectral_conv1d_gelu(x, w, modes: int, bias=None, branch=None, branch_af
         _check(lib().fno_spectral_conv1d_gelu(_ptr(x), _ptr(w), pb, pr, _ptr(out), b, cin, cout, n, modes,
                                               int(bool(branch_after)), _stream_ptr(x.device)),
                "fno_spectral_conv1d_gelu")
+    return out
+
+
+def fno_spectral_filter2d(x, mask, mx: int, my: int, out=None):
+    """Diagonal global filter: out[B,C,H,W] = C2R(truncate(R2C(x)) * mask), mask [2,mx,my,C] c64."""
+    torch = _torch()
+    _need(x, torch.float32, 4, "x")
+    _need(mask, torch.complex64, 4, "mask")
+    b, c, h, wd = x.shape
+    if tuple(mask.shape) != (2, mx, my, c):
+        raise ValueError(f"mask has shape {tuple(mask.shape)}, expected (2, {mx}, {my}, {c})")
+    if out is None:
+        out = torch.empty_like(x)
+    _need(out, torch.float32, 4, "out")
+    if out.shape != x.shape or mask.device != x.device or out.device != x.device:
+        raise ValueError("mask and out must be on x's device, out of x's shape")
+    with _on_device(x):
+        _check(lib().fno_spectral_filter2d(_ptr(x), _ptr(mask), _ptr(out), b, c, h, wd, mx, my,
+                                           _stream_ptr(x.device)), "fno_spectral_filter2d")
+    return out
+
+
+def fno_spectral_filter1d(x, mask, modes: int, out=None):
+    """The 1D form: x [B,C,N], mask [modes,C] c64."""
+    torch = _torch()
+    _need(x, torch.float32, 3, "x")
+    _need(mask, torch.complex64, 2, "mask")
+    b, c, n = x.shape
+    if tuple(mask.shape) != (modes, c):
+        raise ValueError(f"mask has shape {tuple(mask.shape)}, expected ({modes}, {c})")
+    if out is None:
+        out = torch.empty_like(x)
+    _need(out, torch.float32, 3, "out")
+    if out.shape != x.shape or mask.device != x.device or out.device != x.device:
+        raise ValueError("mask and out must be on x's device, out of x's shape")
+    with _on_device(x):
+        _check(lib().fno_spectral_filter1d(_ptr(x), _ptr(mask), _ptr(out), b, c, n, modes, _stream_ptr(x.device)),
+               "fno_spectral_filter1d")
     return out
 
 

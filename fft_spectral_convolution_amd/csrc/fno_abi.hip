@@ -364,6 +364,94 @@ int run_best_2d(const Shape2d& s, const float* x, const float2* w, float* out, v
     return run_unfused_2d(s, x, w, out, ws, tw, st, epi);
 }
 
+// Diagonal global filter: forward -> per-(mode, channel) product -> inverse,
+// on the operator's fastest transforms and workspace (C channels in and out).
+int run_filter_2d(const Shape2d& s, const float* x, const float2* mask, float* out, void* ws, const float2* tw,
+                  hipStream_t st) {
+    const int64_t m = (int64_t)2 * s.mx * s.my;
+    if (small_path(s)) {
+        const SpecLayout lay = tiled_layout(s.Cin, m);
+        float2* xh = static_cast<float2*>(ws);
+        float2* yh = reinterpret_cast<float2*>(static_cast<char*>(ws) +
+                                               align_up((size_t)layout_elems(lay, s.B) * sizeof(float2)));
+        int rc = run_forward2d_small(s, s.Cin, x, xh, lay, tw, st);
+        if (rc) return rc;
+        rec_kernel("mix_diag", st);
+        hipError_t e = launch_mix_diag(xh, yh, lay, mask, s.B, s.Cin, m, st);
+        if (e != hipSuccess) return hip_fail(e);
+        return run_inverse2d_small(s, s.Cin, yh, out, lay, tw, st);
+    }
+    const size_t rmax = (size_t)s.B * s.Cin * s.H * s.my * sizeof(float2);
+    char* p = static_cast<char*>(ws);
+    float2* r = reinterpret_cast<float2*>(p);
+    p += align_up(rmax);
+    float2* xh = reinterpret_cast<float2*>(p);
+    p += align_up((size_t)s.B * s.Cin * m * sizeof(float2));
+    float2* yh = reinterpret_cast<float2*>(p);
+    const SpecLayout lay = canonical_layout(s.Cin, m);
+    int rc = run_forward2d_staged(s, s.Cin, x, xh, r, tw, st);
+    if (rc) return rc;
+    rec_kernel("mix_diag", st);
+    hipError_t e = launch_mix_diag(xh, yh, lay, mask, s.B, s.Cin, m, st);
+    if (e != hipSuccess) return hip_fail(e);
+    return run_inverse2d_staged(s, s.Cin, yh, out, r, tw, st);
+}
+
+int filter2d_common(const float* x, const void* mask, float* out, int B, int C, int H, int W, int mx, int my,
+                    void* stream) {
+    int rc = check_dims_2d(B, C, H, W, mx, my);
+    if (rc) return rc;
+    const size_t xbytes = (size_t)B * C * H * W * sizeof(float);
+    const size_t mbytes = (size_t)2 * mx * my * C * sizeof(float2);
+    rc = check_conv(x, mask, out, xbytes, mbytes, xbytes);
+    if (rc) return rc;
+    const Shape2d s = make2d(B, C, C, H, W, mx, my);
+    DeviceState* st = nullptr;
+    rc = device_state(&st);
+    if (rc) return rc;
+    void* ws = nullptr;
+    rc = internal_workspace(st, best_ws_2d(s), &ws);
+    if (rc) return rc;
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    rec_begin();
+    return rec_end(hs, run_filter_2d(s, x, static_cast<const float2*>(mask), out, ws, st->twiddle, hs));
+}
+
+int filter1d_common(const float* x, const void* mask, float* out, int B, int C, int N, int modes, void* stream) {
+    int rc = check_dims_1d(B, C, N, modes);
+    if (rc) return rc;
+    const size_t xbytes = (size_t)B * C * N * sizeof(float);
+    const size_t mbytes = (size_t)modes * C * sizeof(float2);
+    rc = check_conv(x, mask, out, xbytes, mbytes, xbytes);
+    if (rc) return rc;
+    DeviceState* st = nullptr;
+    rc = device_state(&st);
+    if (rc) return rc;
+    void* ws = nullptr;
+    const size_t hb = align_up((size_t)B * C * modes * sizeof(float2));
+    rc = internal_workspace(st, 2 * hb, &ws);
+    if (rc) return rc;
+    float2* xh = static_cast<float2*>(ws);
+    float2* yh = reinterpret_cast<float2*>(static_cast<char*>(ws) + hb);
+    const float scale = (float)(1.0 / std::sqrt((double)N));
+    const int l2 = ilog2(N);
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    auto run = [&]() -> int {
+        rec_kernel("rows_fwd", hs);
+        hipError_t e = launch_rows_fwd(x, xh, (int64_t)B * C, l2, modes, modes, scale, st->twiddle, hs);
+        if (e != hipSuccess) return hip_fail(e);
+        rec_kernel("mix_diag", hs);
+        e = launch_mix_diag(xh, yh, canonical_layout(C, modes), static_cast<const float2*>(mask), B, C, modes, hs);
+        if (e != hipSuccess) return hip_fail(e);
+        rec_kernel("rows_inv", hs);
+        e = launch_rows_inv(yh, out, (int64_t)B * C, l2, modes, modes, scale, st->twiddle, hs);
+        if (e != hipSuccess) return hip_fail(e);
+        return FNO_OK;
+    };
+    rec_begin();
+    return rec_end(hs, run());
+}
+
 // Inputs of the fused output epilogue: bias [Cout] (4-byte aligned) and
 // branch (the output's shape, 16-byte aligned) are optional; neither may
 // overlap the output.
@@ -721,6 +809,16 @@ int fno_spectral_conv1d_gelu(const float* x, const void* w, const float* bias, c
     rc = check_epilogue(bias, branch, out, Cout, (size_t)B * Cout * N * sizeof(float), branch_after, &epi);
     if (rc) return rc;
     return conv1d_common(x, w, out, B, Cin, Cout, N, modes, nullptr, 0, false, false, stream, epi);
+}
+
+int fno_spectral_filter2d(const float* x, const void* mask, float* out, int B, int C, int H, int W, int mx, int my,
+                          void* stream) {
+    return filter2d_common(x, mask, out, B, C, H, W, mx, my, stream);
+}
+
+int fno_spectral_filter1d(const float* x, const void* mask, float* out, int B, int C, int N, int modes,
+                          void* stream) {
+    return filter1d_common(x, mask, out, B, C, N, modes, stream);
 }
 
 size_t fno_workspace_size_2d(int B, int Cin, int Cout, int H, int W, int mx, int my) {

@@ -185,6 +185,13 @@ hipError_t launch_cols_inv(const float2* yh, float2* r, int64_t nimg, int log2H,
 hipError_t launch_rows_inv(const float2* y, float* out, int64_t nrows, int log2W, int my, int y_ld,
                            float scale, const float2* tw, hipStream_t s, const Epilogue& epi = Epilogue{});
 
+// ---- diagonal global filter (fno_filter.hip) --------------------------------
+// yh(b, c, m) = xh(b, c, m) * mask[m][c], both spectra in layout `lay`
+// (tiled or canonical).
+bool mix_diag_supported(const SpecLayout& lay, int64_t M);
+hipError_t launch_mix_diag(const float2* xh, float2* yh, const SpecLayout& lay, const float2* mask, int64_t B,
+                           int64_t C, int64_t M, hipStream_t s);
+
 // ---- backward pass (fno_backward.hip) ---------------------------------------
 // wt[m][o][i] = conj(w[m][i][o]) for M modes.
 hipError_t launch_weight_adjoint(const float2* w, float2* wt, int64_t M, int64_t Cin, int64_t Cout, hipStream_t s);

@@ -2,7 +2,7 @@
  * libfno -- Fourier-neural-operator spectral convolution on MI355X (gfx950).
  *
  * C ABI.  Every pointer argument named x, w, out, xh, yh, grad_out, grad_x,
- * grad_w, bias, branch or workspace is DEVICE memory on the current HIP
+ * grad_w, bias, branch, mask or workspace is DEVICE memory on the current HIP
  * device, owned by the caller; the library never frees caller memory.  `stream` is a hipStream_t passed as void*
  * (NULL = the null stream).  All calls only enqueue work on `stream` and
  * return without synchronising; a kernel fault shows up at the caller's next
@@ -188,6 +188,26 @@ int fno_spectral_conv1d_gelu(const float* x, const void* w, const float* bias,
                              const float* branch, float* out,
                              int B, int Cin, int Cout, int N, int modes,
                              int branch_after, void* stream);
+
+/*
+ * Diagonal global filter (the learnable frequency mask of the TurboFNO blog,
+ * section 5.2: fft2 -> mask -> ifft2; the frequency-domain token mixing of
+ * the FFT blog, section 3.2: R2C along the sequence -> learnable complex
+ * mask -> C2R): the spectral convolution with the channel mix replaced by
+ * one complex weight per kept mode and channel,
+ *
+ *   Y[b,c,s,r,ky] = X[b,c,s,r,ky] * mask[s,r,ky,c]      (1D: mask[ky,c])
+ *
+ * then zero-fill and the ortho C2R inverse, exactly as fno_spectral_conv2d.
+ * x float32 [B][C][H][W] (1D: [B][C][N]), mask complex64 [2][mx][my][C]
+ * (1D: [modes][C]), out float32 of x's shape.  Keeping every mode (mx = H/2,
+ * my = W/2 + 1) gives the untruncated global filter.  Checks and workspace
+ * as fno_spectral_conv2d (out must not overlap x or mask).
+ */
+int fno_spectral_filter2d(const float* x, const void* mask, float* out,
+                          int B, int C, int H, int W, int mx, int my, void* stream);
+int fno_spectral_filter1d(const float* x, const void* mask, float* out,
+                          int B, int C, int N, int modes, void* stream);
 
 /*
  * Per-kernel timing for benchmarks and profilers.  While `events` is non-NULL,

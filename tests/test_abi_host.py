@@ -176,3 +176,18 @@ def test_gelu_epilogue_checks(lib):
     assert f1(A, B, None, None, C, 1, 1, 1, 16, 10, 0, None) == MODES
     assert f1(A, B, None, None, None, 1, 1, 1, 16, 4, 0, None) == NULL
     assert f1(A, B, None, None, C, 1, 1, 1, 16, 4, -1, None) == SHAPE
+
+
+def test_filter_checks(lib):
+    f2 = lib.fno_spectral_filter2d
+    assert f2(None, B, C, 2, 3, 16, 16, 4, 4, None) == NULL
+    assert f2(A, None, C, 2, 3, 16, 16, 4, 4, None) == NULL
+    assert f2(A, B, C, 2, 3, 12, 16, 4, 4, None) == SHAPE
+    assert f2(A, B, C, 2, 3, 16, 16, 9, 4, None) == MODES
+    assert f2(A, B + 8, C, 2, 3, 16, 16, 4, 4, None) == ALIGN
+    assert f2(A, B, A, 2, 3, 16, 16, 4, 4, None) == ALIAS          # out on top of x
+    assert f2(A, B, B, 2, 3, 16, 16, 4, 4, None) == ALIAS          # out on top of the mask
+    f1 = lib.fno_spectral_filter1d
+    assert f1(A, B, C, 1, 1, 12, 2, None) == SHAPE
+    assert f1(A, B, C, 1, 1, 16, 10, None) == MODES
+    assert f1(None, B, C, 1, 1, 16, 4, None) == NULL
