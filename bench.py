@@ -2,7 +2,7 @@
 """Benchmark of libfno's spectral convolution on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c3] [--variant fused|unfused]
-                    [--pass forward|backward|layer]
+                    [--pass forward|backward|layer|filter]
 
 One step = one full spectral-convolution call (forward pruned FFT, per-mode
 channel mix, inverse pruned FFT) over one batch of synthetic inputs already
@@ -27,7 +27,9 @@ bounded sample.
 
 --pass backward times both gradients of a real loss (compulsory bytes: x, W,
 dL/dout read, dL/dx, dL/dW written); --pass layer times the operator with
-the fused layer tail gelu(conv + bias + branch) (adds the branch read).
+the fused layer tail gelu(conv + bias + branch) (adds the branch read);
+--pass filter times the diagonal global filter (x and the mask read, out
+written).
 """
 from __future__ import annotations
 
@@ -58,6 +60,7 @@ def kernel_bytes(name: str, cfg, backward: bool = False) -> int:
         import dataclasses
         cfg = dataclasses.replace(cfg, Cin=cfg.Cout, Cout=cfg.Cin)
     c8 = 8
+    m_modes = cfg.my if cfg.kind == "1d" else 2 * cfg.mx * cfg.my
     if cfg.kind == "1d":
         n_in = cfg.B * cfg.Cin * cfg.W * 4
         n_out = cfg.B * cfg.Cout * cfg.W * 4
@@ -91,6 +94,8 @@ def kernel_bytes(name: str, cfg, backward: bool = False) -> int:
         # fused layer tail: the inverse also reads the branch (output-sized)
         "inv2d_gelu": yh + 2 * n_out,
         "rows_inv_gelu": (r_out if cfg.kind == "2d" else yh) + 2 * n_out,
+        # diagonal filter: both truncated spectra and the (mode, channel) mask
+        "mix_diag": xh + yh + (m_modes * cfg.Cin * c8),
         "wgrad": xh + yh + wb,
         "wadjoint": 2 * wb,
         # sum of the batch splits' partial weight gradients (when the batch
@@ -124,7 +129,7 @@ def load_traffic(kernel: str, workload: str):
         return None
 
 
-def cpu_baseline(cfg, x, w, budget_s: float = 12.0, g=None, compulsory=None, layer=None):
+def cpu_baseline(cfg, x, w, budget_s: float = 12.0, g=None, compulsory=None, layer=None, mask=None):
     """Time the fp64 oracle (as it stands) on this host on a bounded sample
     (the backward pass when the output gradient g is given, the operator with
     the layer tail when layer = (bias, branch) is)."""
@@ -136,6 +141,10 @@ def cpu_baseline(cfg, x, w, budget_s: float = 12.0, g=None, compulsory=None, lay
         threads = 1
     # one batch item first, to size the sample
     def call(nb):
+        if mask is not None:
+            if cfg.kind == "1d":
+                return oracle.spectral_filter1d_ref(x[:nb], mask, cfg.my)
+            return oracle.spectral_filter2d_ref(x[:nb], mask, cfg.mx, cfg.my)
         if layer is not None:
             bias, branch = layer
             if cfg.kind == "1d":
@@ -183,9 +192,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="c3", choices=sorted(CONFIGS))
     ap.add_argument("--variant", default="fused", choices=["fused", "unfused"])
-    ap.add_argument("--pass", dest="which", default="forward", choices=["forward", "backward", "layer"],
-                    help="time the operator (default), its backward pass (both gradients), or the operator "
-                         "with the fused layer tail gelu(conv + bias + branch)")
+    ap.add_argument("--pass", dest="which", default="forward", choices=["forward", "backward", "layer", "filter"],
+                    help="time the operator (default), its backward pass (both gradients), the operator "
+                         "with the fused layer tail gelu(conv + bias + branch), or the diagonal global "
+                         "filter (one complex weight per kept mode and channel)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -229,6 +239,7 @@ def main():
     compulsory = cfg.compulsory_bytes
     g_np = None
     layer_np = None
+    filter_np = None
     if args.which == "backward":
         # step: both gradients of a real loss, given a synthetic dL/dout of the
         # output's shape; compulsory bytes: x, w, dL/dout read, dL/dx, dL/dw written
@@ -263,6 +274,19 @@ def main():
         else:
             step = lambda i: fno.fno_spectral_conv2d_gelu(xs[i % nsets], w, cfg.mx, cfg.my, bias=bias,
                                                           branch=brs[i % nsets], out=outs[i % nsets])
+    elif args.which == "filter":
+        # step: out = C2R(truncate(R2C(x)) * mask); compulsory bytes: x and
+        # the mask read, out written
+        rng = np.random.default_rng(3)
+        mshape = (cfg.my, cfg.Cin) if cfg.kind == "1d" else (2, cfg.mx, cfg.my, cfg.Cin)
+        mask_np = (rng.standard_normal(mshape) + 1j * rng.standard_normal(mshape)).astype(np.complex64)
+        mask = torch.from_numpy(mask_np).to(dev)
+        filter_np = mask_np
+        compulsory = 2 * int(x_np.nbytes) + int(mask_np.nbytes)
+        if cfg.kind == "1d":
+            step = lambda i: fno.fno_spectral_filter1d(xs[i % nsets], mask, cfg.my, out=outs[i % nsets])
+        else:
+            step = lambda i: fno.fno_spectral_filter2d(xs[i % nsets], mask, cfg.mx, cfg.my, out=outs[i % nsets])
     elif cfg.kind == "1d":
         fn = fno.fno_spectral_conv1d if args.variant == "fused" else fno.fno_spectral_conv1d_unfused
         step = lambda i: fn(xs[i % nsets], w, cfg.my, out=outs[i % nsets])
@@ -391,7 +415,7 @@ def main():
         }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(cfg, x_np, w_np, args.cpu_budget, g=g_np, compulsory=compulsory,
-                                            layer=layer_np)
+                                            layer=layer_np, mask=filter_np)
     print(json.dumps(line), flush=True)
 
 
