@@ -53,6 +53,13 @@ upcast exactly):
      Yh[b,c,s,r,ky] = Xh[b,c,s,r,ky] * M[s,r,ky,c]   (1D: M[ky,c]),
    then step 4.  Keeping every mode (mx = H/2, my = W/2 + 1) gives the
    untruncated global filter.
+9. zero-padded linear convolution (P2 sections 2.1 and 5.1-5.2: pad input
+   and kernel, R2C, pointwise product, C2R, crop): the plain definition
+     y[b,o,p,q] = sum_i sum_{dh<kh, dw<kw} x[b,i,p-dh,q-dw] k[o,i,dh,dw]
+   (x zero outside its grid; y of size (H+kh-1) x (W+kw-1)), cropped to
+   out = y[:, :, ch:ch+Ho, cw:cw+Wo].  The convolution theorem makes this
+   the circular convolution on any grid of at least that size, which the
+   GPU path computes with the spectral convolution at full modes.
 
 Two independent ways of computing the transforms are provided:
 
@@ -96,6 +103,8 @@ __all__ = [
     "spectral_conv1d_gelu_ref",
     "spectral_filter2d_ref",
     "spectral_filter1d_ref",
+    "linear_conv2d_ref",
+    "linear_conv1d_ref",
 ]
 
 
@@ -460,6 +469,40 @@ def spectral_filter1d_ref(x, mask, modes: int, transform: str = "dft"):
         raise ValueError(f"mask shape {mask.shape} does not match ({modes}, {c})")
     xh = forward_truncated_1d(x, modes, transform)               # [B,C,modes]
     return inverse_from_truncated_1d(xh * mask.T[None], n, transform)
+
+
+# --------------------------------------------------------------------------
+# Linear (non-circular) convolution, by its definition
+# --------------------------------------------------------------------------
+
+def linear_conv2d_ref(x, k, crop_h: int = 0, crop_w: int = 0, out_h=None, out_w=None):
+    """Full linear convolution of x[B,Cin,H,W] with k[Cout,Cin,kh,kw] (sum over
+    Cin, kernel not flipped back: y[p] = sum x[p - d] k[d]), cropped to
+    [crop_h : crop_h + out_h, crop_w : crop_w + out_w] (default: the rest)."""
+    x = np.asarray(x, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    b, cin, h, w = x.shape
+    cout, cin2, kh, kw = k.shape
+    if cin2 != cin:
+        raise ValueError(f"kernel {k.shape} does not match x {x.shape}")
+    fh, fw = h + kh - 1, w + kw - 1
+    y = np.zeros((b, cout, fh, fw))
+    for dh in range(kh):
+        for dw in range(kw):
+            # every input pixel (p - dh, q - dw) lands at (p, q)
+            y[:, :, dh:dh + h, dw:dw + w] += np.einsum("bihw,oi->bohw", x, k[:, :, dh, dw])
+    out_h = fh - crop_h if out_h is None else out_h
+    out_w = fw - crop_w if out_w is None else out_w
+    if crop_h < 0 or crop_w < 0 or crop_h + out_h > fh or crop_w + out_w > fw:
+        raise ValueError("crop window outside the full convolution")
+    return y[:, :, crop_h:crop_h + out_h, crop_w:crop_w + out_w]
+
+
+def linear_conv1d_ref(x, k, crop: int = 0, out_n=None):
+    """The 1D form: x[B,Cin,N], k[Cout,Cin,K], full length N + K - 1."""
+    x = np.asarray(x, dtype=np.float64)
+    y = linear_conv2d_ref(x[:, :, None, :], np.asarray(k, dtype=np.float64)[:, :, None, :], 0, crop, 1, out_n)
+    return y[:, :, 0, :]
 
 
 # --------------------------------------------------------------------------

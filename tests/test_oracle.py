@@ -799,3 +799,68 @@ def test_filter_1d_single_cosine_closed_form():
     for ch in range(c):
         m = mask[k, ch]
         assert np.max(np.abs(out[:, ch] - (m.real * np.cos(theta) - m.imag * np.sin(theta)))) < 1e-12
+
+
+# --------------------------------------------------------------------------
+# Linear (zero-padded) convolution
+# --------------------------------------------------------------------------
+
+def test_linear_conv_against_library_convolution():
+    from scipy.signal import convolve
+    rng = np.random.default_rng(60)
+    x = rng.standard_normal((2, 3, 7, 9))
+    k = rng.standard_normal((4, 3, 3, 5))
+    y = S.linear_conv2d_ref(x, k)
+    assert y.shape == (2, 4, 9, 13)
+    for b in range(2):
+        for o in range(4):
+            ref = sum(convolve(x[b, i], k[o, i], mode="full") for i in range(3))
+            assert np.max(np.abs(y[b, o] - ref)) < 1e-12
+    x1 = rng.standard_normal((2, 2, 11))
+    k1 = rng.standard_normal((3, 2, 4))
+    y1 = S.linear_conv1d_ref(x1, k1)
+    for b in range(2):
+        for o in range(3):
+            ref = sum(np.convolve(x1[b, i], k1[o, i]) for i in range(2))
+            assert np.max(np.abs(y1[b, o] - ref)) < 1e-12
+
+
+def test_linear_conv_delta_kernel_and_crop():
+    # a unit impulse at (dh, dw) shifts x by (dh, dw); the 'same' crop of a
+    # centred impulse returns x itself
+    rng = np.random.default_rng(61)
+    x = rng.standard_normal((1, 2, 6, 8))
+    k = np.zeros((2, 2, 5, 3))
+    k[0, 0, 2, 1] = 1.0
+    k[1, 1, 2, 1] = 1.0
+    same = S.linear_conv2d_ref(x, k, 2, 1, 6, 8)
+    assert np.max(np.abs(same - x)) == 0.0
+    k2 = np.zeros((1, 2, 5, 3))
+    k2[0, 1, 4, 0] = 1.0
+    full = S.linear_conv2d_ref(x, k2)
+    assert np.max(np.abs(full[0, 0, 4:10, 0:8] - x[0, 1])) == 0.0
+    assert np.count_nonzero(full) == np.count_nonzero(x[0, 1])      # nothing lands elsewhere
+
+
+def test_linear_conv_through_padded_spectral_conv():
+    # the method the GPU path uses: zero-pad both operands to a power-of-two
+    # grid P >= N + k - 1, spectral convolution at full modes with
+    # W = sqrt(PH PW) * ortho-R2C(kernel), crop; equal to the definition
+    rng = np.random.default_rng(62)
+    b, cin, cout, h, w, kh, kw = 2, 3, 2, 6, 5, 3, 4
+    x = rng.standard_normal((b, cin, h, w))
+    k = rng.standard_normal((cout, cin, kh, kw))
+    ph, pw = 8, 8
+    xp = np.zeros((b, cin, ph, pw))
+    xp[:, :, :h, :w] = x
+    kp = np.zeros((cout, cin, ph, pw))
+    kp[:, :, :kh, :kw] = k
+    mx, my = ph // 2, pw // 2 + 1
+    kh_spec = S.forward_truncated_2d(kp, mx, my)                     # [Cout,Cin,2,mx,my]
+    wt = math.sqrt(ph * pw) * np.transpose(kh_spec, (2, 3, 4, 1, 0))  # [2,mx,my,Cin,Cout]
+    y = S.spectral_conv2d_ref(xp, wt, mx, my)
+    ref = S.linear_conv2d_ref(x, k)
+    assert np.max(np.abs(y[:, :, :h + kh - 1, :w + kw - 1] - ref)) < 1e-12
+    # planted mistake: without the sqrt(PH PW) factor the result is off
+    y_bad = S.spectral_conv2d_ref(xp, wt / math.sqrt(ph * pw), mx, my)
+    assert np.max(np.abs(y_bad[:, :, :h + kh - 1, :w + kw - 1] - ref)) > 0.1
