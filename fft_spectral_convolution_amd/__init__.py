@@ -34,6 +34,11 @@ __all__ = [
     "fno_spectral_conv1d_gelu",
     "fno_spectral_filter2d",
     "fno_spectral_filter1d",
+    "fno_linear_conv_length",
+    "fno_linear_conv2d_prepare",
+    "fno_linear_conv2d",
+    "fno_linear_conv1d_prepare",
+    "fno_linear_conv1d",
     "fno_workspace_size_2d",
     "fno_workspace_size_1d",
     "fno_forward2d",
@@ -80,6 +85,11 @@ _SIGNATURES = {
     "fno_spectral_conv1d_gelu": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P]),
     "fno_spectral_filter2d": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _I, _P]),
     "fno_spectral_filter1d": (_I, [_P, _P, _P, _I, _I, _I, _I, _P]),
+    "fno_linear_conv_length": (_I, [_I, _I]),
+    "fno_linear_conv2d_prepare": (_I, [_P, _P, _I, _I, _I, _I, _I, _I, _P]),
+    "fno_linear_conv2d": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I, _I, _I, _P]),
+    "fno_linear_conv1d_prepare": (_I, [_P, _P, _I, _I, _I, _I, _P]),
+    "fno_linear_conv1d": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P]),
     "fno_set_timing_events": (_I, [ctypes.POINTER(ctypes.c_void_p), _I]),
     "fno_last_kernel_count": (_I, []),
     "fno_last_kernel_name": (ctypes.c_char_p, [_I]),
@@ -285,6 +295,92 @@ def fno_spectral_filter1d(x, mask, modes: int, out=None):
     with _on_device(x):
         _check(lib().fno_spectral_filter1d(_ptr(x), _ptr(mask), _ptr(out), b, c, n, modes, _stream_ptr(x.device)),
                "fno_spectral_filter1d")
+    return out
+
+
+def fno_linear_conv_length(n: int, k: int) -> int:
+    """Padded transform length of the linear convolution of n samples with a k-tap kernel."""
+    return int(lib().fno_linear_conv_length(int(n), int(k)))
+
+
+def fno_linear_conv2d_prepare(k, h: int, w: int):
+    """Weight spectrum [2,PH/2,PW/2+1,Cin,Cout] c64 of kernels k [Cout,Cin,kh,kw] f32 for H x W inputs."""
+    torch = _torch()
+    _need(k, torch.float32, 4, "k")
+    cout, cin, kh, kw = k.shape
+    ph, pw = fno_linear_conv_length(h, kh), fno_linear_conv_length(w, kw)
+    if not ph or not pw:
+        raise ValueError("padded grid out of range")
+    wspec = torch.empty((2, ph // 2, pw // 2 + 1, cin, cout), dtype=torch.complex64, device=k.device)
+    with _on_device(k):
+        _check(lib().fno_linear_conv2d_prepare(_ptr(k), _ptr(wspec), cin, cout, h, w, kh, kw,
+                                               _stream_ptr(k.device)), "fno_linear_conv2d_prepare")
+    return wspec
+
+
+def fno_linear_conv2d(x, k, crop=None, out_size=None, wspec=None, out=None):
+    """Linear convolution of x [B,Cin,H,W] with k [Cout,Cin,kh,kw] (sum over Cin), cropped:
+    out = y[:, :, ch:ch+Ho, cw:cw+Wo] with crop = (ch, cw), out_size = (Ho, Wo); the defaults
+    give the "same" output (crop ((kh-1)//2, (kw-1)//2), size H x W).  wspec (from
+    fno_linear_conv2d_prepare) skips the kernel transform."""
+    torch = _torch()
+    _need(x, torch.float32, 4, "x")
+    _need(k, torch.float32, 4, "k")
+    b, cin, h, w = x.shape
+    cout, cin2, kh, kw = k.shape
+    if cin2 != cin:
+        raise ValueError(f"k has shape {tuple(k.shape)}, expected (Cout, {cin}, kh, kw)")
+    ch, cw = crop if crop is not None else ((kh - 1) // 2, (kw - 1) // 2)
+    ho, wo = out_size if out_size is not None else (h, w)
+    if wspec is None:
+        wspec = fno_linear_conv2d_prepare(k, h, w)
+    if out is None:
+        out = torch.empty((b, cout, ho, wo), dtype=torch.float32, device=x.device)
+    _need(out, torch.float32, 4, "out")
+    if tuple(out.shape) != (b, cout, ho, wo):
+        raise ValueError(f"out has shape {tuple(out.shape)}, expected {(b, cout, ho, wo)}")
+    with _on_device(x):
+        _check(lib().fno_linear_conv2d(_ptr(x), _ptr(wspec), _ptr(out), b, cin, cout, h, w, kh, kw, ch, cw, ho, wo,
+                                       _stream_ptr(x.device)), "fno_linear_conv2d")
+    return out
+
+
+def fno_linear_conv1d_prepare(k, n: int):
+    """Weight spectrum [PN/2+1,Cin,Cout] c64 of kernels k [Cout,Cin,K] f32 for length-n inputs."""
+    torch = _torch()
+    _need(k, torch.float32, 3, "k")
+    cout, cin, kk = k.shape
+    pn = fno_linear_conv_length(n, kk)
+    if not pn:
+        raise ValueError("padded length out of range")
+    wspec = torch.empty((pn // 2 + 1, cin, cout), dtype=torch.complex64, device=k.device)
+    with _on_device(k):
+        _check(lib().fno_linear_conv1d_prepare(_ptr(k), _ptr(wspec), cin, cout, n, kk, _stream_ptr(k.device)),
+               "fno_linear_conv1d_prepare")
+    return wspec
+
+
+def fno_linear_conv1d(x, k, crop=None, out_len=None, wspec=None, out=None):
+    """The 1D form: x [B,Cin,N], k [Cout,Cin,K]; default "same" output (crop (K-1)//2, length N)."""
+    torch = _torch()
+    _need(x, torch.float32, 3, "x")
+    _need(k, torch.float32, 3, "k")
+    b, cin, n = x.shape
+    cout, cin2, kk = k.shape
+    if cin2 != cin:
+        raise ValueError(f"k has shape {tuple(k.shape)}, expected (Cout, {cin}, K)")
+    c0 = crop if crop is not None else (kk - 1) // 2
+    no = out_len if out_len is not None else n
+    if wspec is None:
+        wspec = fno_linear_conv1d_prepare(k, n)
+    if out is None:
+        out = torch.empty((b, cout, no), dtype=torch.float32, device=x.device)
+    _need(out, torch.float32, 3, "out")
+    if tuple(out.shape) != (b, cout, no):
+        raise ValueError(f"out has shape {tuple(out.shape)}, expected {(b, cout, no)}")
+    with _on_device(x):
+        _check(lib().fno_linear_conv1d(_ptr(x), _ptr(wspec), _ptr(out), b, cin, cout, n, kk, c0, no,
+                                       _stream_ptr(x.device)), "fno_linear_conv1d")
     return out
 
 

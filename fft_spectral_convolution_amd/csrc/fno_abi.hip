@@ -452,6 +452,172 @@ int filter1d_common(const float* x, const void* mask, float* out, int B, int C, 
     return rec_end(hs, run());
 }
 
+// ---------------------------------------------------------------------------
+// zero-padded linear convolution
+// ---------------------------------------------------------------------------
+
+// Transform length of the padded grid: the smallest power of two (>= 2) that
+// holds the full linear convolution of n samples with a k-tap kernel; 0 when
+// the sizes are out of range.
+int linconv_len(int n, int k) {
+    if (n < 1 || k < 1) return 0;
+    const int64_t need = (int64_t)n + k - 1;
+    int64_t p = 2;
+    while (p < need) p <<= 1;
+    return p <= kNMax ? (int)p : 0;
+}
+
+int linconv2d_prepare(const float* k, void* wspec, int Cin, int Cout, int H, int W, int kh, int kw, void* stream) {
+    const int PH = linconv_len(H, kh), PW = linconv_len(W, kw);
+    if (!PH || !PW || Cin < 1 || Cout < 1 || (int64_t)Cin * Cout > INT32_MAX) return FNO_ERR_SHAPE;
+    if (!k || !wspec) return FNO_ERR_NULL;
+    if (misaligned(k) || misaligned(wspec)) return FNO_ERR_ALIGN;
+    const int mx = PH / 2, my = PW / 2 + 1;
+    const int64_t io = (int64_t)Cin * Cout, M = (int64_t)PH * my;
+    const size_t kbytes = (size_t)io * kh * kw * sizeof(float);
+    const size_t wbytes = (size_t)M * io * sizeof(float2);
+    if (overlap(k, kbytes, wspec, wbytes)) return FNO_ERR_ALIAS;
+    // the kernels as Cout * Cin images of one batch item
+    const Shape2d s = make2d(1, (int)io, (int)io, PH, PW, mx, my);
+    const size_t kp_b = align_up((size_t)io * PH * PW * sizeof(float));
+    const size_t kh_b = align_up((size_t)io * M * sizeof(float2));
+    const size_t r_b = small_path(s) ? 0 : align_up((size_t)io * PH * my * sizeof(float2));
+    DeviceState* st = nullptr;
+    int rc = device_state(&st);
+    if (rc) return rc;
+    void* ws = nullptr;
+    rc = internal_workspace(st, kp_b + kh_b + r_b, &ws);
+    if (rc) return rc;
+    float* kp = static_cast<float*>(ws);
+    float2* khs = reinterpret_cast<float2*>(static_cast<char*>(ws) + kp_b);
+    float2* r = reinterpret_cast<float2*>(static_cast<char*>(ws) + kp_b + kh_b);
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    auto run = [&]() -> int {
+        rec_kernel("pad", hs);
+        hipError_t e = launch_pad2d(k, kp, io, kh, kw, PH, PW, hs);
+        if (e != hipSuccess) return hip_fail(e);
+        const int frc = small_path(s) ? run_forward2d_small(s, io, kp, khs, canonical_layout(io, M), st->twiddle, hs)
+                                      : run_forward2d_staged(s, io, kp, khs, r, st->twiddle, hs);
+        if (frc) return frc;
+        rec_kernel("spec_to_weight", hs);
+        e = launch_spec_to_weight(khs, static_cast<float2*>(wspec), M, Cin, Cout,
+                                  (float)std::sqrt((double)PH * (double)PW), hs);
+        return e == hipSuccess ? FNO_OK : hip_fail(e);
+    };
+    rec_begin();
+    return rec_end(hs, run());
+}
+
+int linconv2d_run(const float* x, const void* wspec, float* out, int B, int Cin, int Cout, int H, int W, int kh,
+                  int kw, int ch, int cw, int Ho, int Wo, void* stream) {
+    const int PH = linconv_len(H, kh), PW = linconv_len(W, kw);
+    if (!PH || !PW || B < 1 || Cin < 1 || Cout < 1) return FNO_ERR_SHAPE;
+    if (ch < 0 || cw < 0 || Ho < 1 || Wo < 1 || ch + Ho > H + kh - 1 || cw + Wo > W + kw - 1) return FNO_ERR_SHAPE;
+    const int mx = PH / 2, my = PW / 2 + 1;
+    const size_t xbytes = (size_t)B * Cin * H * W * sizeof(float);
+    const size_t wbytes = (size_t)PH * my * Cin * Cout * sizeof(float2);
+    const size_t obytes = (size_t)B * Cout * Ho * Wo * sizeof(float);
+    int rc = check_conv(x, wspec, out, xbytes, wbytes, obytes);
+    if (rc) return rc;
+    const Shape2d s = make2d(B, Cin, Cout, PH, PW, mx, my);
+    const size_t xp_b = align_up((size_t)B * Cin * PH * PW * sizeof(float));
+    const size_t yp_b = align_up((size_t)B * Cout * PH * PW * sizeof(float));
+    DeviceState* st = nullptr;
+    rc = device_state(&st);
+    if (rc) return rc;
+    void* ws = nullptr;
+    rc = internal_workspace(st, xp_b + yp_b + best_ws_2d(s), &ws);
+    if (rc) return rc;
+    float* xp = static_cast<float*>(ws);
+    float* yp = reinterpret_cast<float*>(static_cast<char*>(ws) + xp_b);
+    void* cws = static_cast<char*>(ws) + xp_b + yp_b;
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    auto run = [&]() -> int {
+        rec_kernel("pad", hs);
+        hipError_t e = launch_pad2d(x, xp, (int64_t)B * Cin, H, W, PH, PW, hs);
+        if (e != hipSuccess) return hip_fail(e);
+        const int crc = run_best_2d(s, xp, static_cast<const float2*>(wspec), yp, cws, st->twiddle, hs);
+        if (crc) return crc;
+        rec_kernel("crop", hs);
+        e = launch_crop2d(yp, out, (int64_t)B * Cout, PH, PW, ch, cw, Ho, Wo, hs);
+        return e == hipSuccess ? FNO_OK : hip_fail(e);
+    };
+    rec_begin();
+    return rec_end(hs, run());
+}
+
+int linconv1d_prepare(const float* k, void* wspec, int Cin, int Cout, int N, int K, void* stream) {
+    const int PN = linconv_len(N, K);
+    if (!PN || Cin < 1 || Cout < 1 || (int64_t)Cin * Cout > INT32_MAX) return FNO_ERR_SHAPE;
+    if (!k || !wspec) return FNO_ERR_NULL;
+    if (misaligned(k) || misaligned(wspec)) return FNO_ERR_ALIGN;
+    const int modes = PN / 2 + 1;
+    const int64_t io = (int64_t)Cin * Cout;
+    if (overlap(k, (size_t)io * K * sizeof(float), wspec, (size_t)modes * io * sizeof(float2))) return FNO_ERR_ALIAS;
+    const size_t kp_b = align_up((size_t)io * PN * sizeof(float));
+    const size_t kh_b = align_up((size_t)io * modes * sizeof(float2));
+    DeviceState* st = nullptr;
+    int rc = device_state(&st);
+    if (rc) return rc;
+    void* ws = nullptr;
+    rc = internal_workspace(st, kp_b + kh_b, &ws);
+    if (rc) return rc;
+    float* kp = static_cast<float*>(ws);
+    float2* khs = reinterpret_cast<float2*>(static_cast<char*>(ws) + kp_b);
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    auto run = [&]() -> int {
+        rec_kernel("pad", hs);
+        hipError_t e = launch_pad2d(k, kp, io, 1, K, 1, PN, hs);
+        if (e != hipSuccess) return hip_fail(e);
+        rec_kernel("rows_fwd", hs);
+        e = launch_rows_fwd(kp, khs, io, ilog2(PN), modes, modes, (float)(1.0 / std::sqrt((double)PN)), st->twiddle, hs);
+        if (e != hipSuccess) return hip_fail(e);
+        rec_kernel("spec_to_weight", hs);
+        e = launch_spec_to_weight(khs, static_cast<float2*>(wspec), modes, Cin, Cout, (float)std::sqrt((double)PN), hs);
+        return e == hipSuccess ? FNO_OK : hip_fail(e);
+    };
+    rec_begin();
+    return rec_end(hs, run());
+}
+
+int linconv1d_run(const float* x, const void* wspec, float* out, int B, int Cin, int Cout, int N, int K, int crop,
+                  int No, void* stream) {
+    const int PN = linconv_len(N, K);
+    if (!PN || B < 1 || Cin < 1 || Cout < 1) return FNO_ERR_SHAPE;
+    if (crop < 0 || No < 1 || crop + No > N + K - 1) return FNO_ERR_SHAPE;
+    const int modes = PN / 2 + 1;
+    const size_t xbytes = (size_t)B * Cin * N * sizeof(float);
+    const size_t wbytes = (size_t)modes * Cin * Cout * sizeof(float2);
+    const size_t obytes = (size_t)B * Cout * No * sizeof(float);
+    int rc = check_conv(x, wspec, out, xbytes, wbytes, obytes);
+    if (rc) return rc;
+    const size_t xp_b = align_up((size_t)B * Cin * PN * sizeof(float));
+    const size_t yp_b = align_up((size_t)B * Cout * PN * sizeof(float));
+    DeviceState* st = nullptr;
+    rc = device_state(&st);
+    if (rc) return rc;
+    void* ws = nullptr;
+    rc = internal_workspace(st, xp_b + yp_b + unfused_ws_1d(B, Cin, Cout, modes), &ws);
+    if (rc) return rc;
+    float* xp = static_cast<float*>(ws);
+    float* yp = reinterpret_cast<float*>(static_cast<char*>(ws) + xp_b);
+    void* cws = static_cast<char*>(ws) + xp_b + yp_b;
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    auto run = [&]() -> int {
+        rec_kernel("pad", hs);
+        hipError_t e = launch_pad2d(x, xp, (int64_t)B * Cin, 1, N, 1, PN, hs);
+        if (e != hipSuccess) return hip_fail(e);
+        const int crc = run_unfused_1d(B, Cin, Cout, PN, modes, xp, static_cast<const float2*>(wspec), yp, cws,
+                                       st->twiddle, hs);
+        if (crc) return crc;
+        rec_kernel("crop", hs);
+        e = launch_crop2d(yp, out, (int64_t)B * Cout, 1, PN, 0, crop, 1, No, hs);
+        return e == hipSuccess ? FNO_OK : hip_fail(e);
+    };
+    rec_begin();
+    return rec_end(hs, run());
+}
+
 // Inputs of the fused output epilogue: bias [Cout] (4-byte aligned) and
 // branch (the output's shape, 16-byte aligned) are optional; neither may
 // overlap the output.
@@ -819,6 +985,27 @@ int fno_spectral_filter2d(const float* x, const void* mask, float* out, int B, i
 int fno_spectral_filter1d(const float* x, const void* mask, float* out, int B, int C, int N, int modes,
                           void* stream) {
     return filter1d_common(x, mask, out, B, C, N, modes, stream);
+}
+
+int fno_linear_conv_length(int n, int k) { return linconv_len(n, k); }
+
+int fno_linear_conv2d_prepare(const float* k, void* wspec, int Cin, int Cout, int H, int W, int kh, int kw,
+                              void* stream) {
+    return linconv2d_prepare(k, wspec, Cin, Cout, H, W, kh, kw, stream);
+}
+
+int fno_linear_conv2d(const float* x, const void* wspec, float* out, int B, int Cin, int Cout, int H, int W, int kh,
+                      int kw, int crop_h, int crop_w, int Ho, int Wo, void* stream) {
+    return linconv2d_run(x, wspec, out, B, Cin, Cout, H, W, kh, kw, crop_h, crop_w, Ho, Wo, stream);
+}
+
+int fno_linear_conv1d_prepare(const float* k, void* wspec, int Cin, int Cout, int N, int K, void* stream) {
+    return linconv1d_prepare(k, wspec, Cin, Cout, N, K, stream);
+}
+
+int fno_linear_conv1d(const float* x, const void* wspec, float* out, int B, int Cin, int Cout, int N, int K,
+                      int crop, int No, void* stream) {
+    return linconv1d_run(x, wspec, out, B, Cin, Cout, N, K, crop, No, stream);
 }
 
 size_t fno_workspace_size_2d(int B, int Cin, int Cout, int H, int W, int mx, int my) {

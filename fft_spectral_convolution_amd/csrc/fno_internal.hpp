@@ -192,6 +192,16 @@ bool mix_diag_supported(const SpecLayout& lay, int64_t M);
 hipError_t launch_mix_diag(const float2* xh, float2* yh, const SpecLayout& lay, const float2* mask, int64_t B,
                            int64_t C, int64_t M, hipStream_t s);
 
+// ---- zero-padded linear convolution helpers (fno_linconv.hip) ---------------
+// dst[img][PH][PW] = src[img][H][W] zero-padded (bottom and right).
+hipError_t launch_pad2d(const float* src, float* dst, int64_t nimg, int H, int W, int PH, int PW, hipStream_t s);
+// dst[img][Ho][Wo] = src[img][PH][PW] from row ch, column cw.
+hipError_t launch_crop2d(const float* src, float* dst, int64_t nimg, int PH, int PW, int ch, int cw, int Ho, int Wo,
+                         hipStream_t s);
+// w[m][i][o] = scale * kh[o Cin + i][m] (kh canonical spectra of the kernels).
+hipError_t launch_spec_to_weight(const float2* kh, float2* w, int64_t M, int64_t Cin, int64_t Cout, float scale,
+                                 hipStream_t s);
+
 // ---- backward pass (fno_backward.hip) ---------------------------------------
 // wt[m][o][i] = conj(w[m][i][o]) for M modes.
 hipError_t launch_weight_adjoint(const float2* w, float2* wt, int64_t M, int64_t Cin, int64_t Cout, hipStream_t s);

@@ -2,7 +2,7 @@
  * libfno -- Fourier-neural-operator spectral convolution on MI355X (gfx950).
  *
  * C ABI.  Every pointer argument named x, w, out, xh, yh, grad_out, grad_x,
- * grad_w, bias, branch, mask or workspace is DEVICE memory on the current HIP
+ * grad_w, bias, branch, mask, k, wspec or workspace is DEVICE memory on the current HIP
  * device, owned by the caller; the library never frees caller memory.  `stream` is a hipStream_t passed as void*
  * (NULL = the null stream).  All calls only enqueue work on `stream` and
  * return without synchronising; a kernel fault shows up at the caller's next
@@ -208,6 +208,43 @@ int fno_spectral_filter2d(const float* x, const void* mask, float* out,
                           int B, int C, int H, int W, int mx, int my, void* stream);
 int fno_spectral_filter1d(const float* x, const void* mask, float* out,
                           int B, int C, int N, int modes, void* stream);
+
+/*
+ * Zero-padded linear convolution (the FFT blog, sections 2.1 and 5.1-5.2:
+ * pad input and kernel, R2C, pointwise product, C2R, crop):
+ *
+ *   y[b,o,p,q] = sum_i sum_{dh<kh, dw<kw} x[b,i,p-dh,q-dw] k[o,i,dh,dw]
+ *
+ * (x zero outside its H x W grid; y is (H+kh-1) x (W+kw-1)), and
+ * out[b,o,h,w] = y[b,o,h+crop_h,w+crop_w] for h < Ho, w < Wo ("same" output:
+ * crop (kh-1)/2, (kw-1)/2 and Ho = H, Wo = W).  H, W need not be powers of
+ * two.  Both operands are zero-padded to PH x PW with
+ * PH = fno_linear_conv_length(H, kh), PW = fno_linear_conv_length(W, kw) (the
+ * smallest power of two >= 2 holding the full convolution, at most 4096;
+ * 0 when out of range), where the circular convolution equals the linear
+ * one, and the spectral convolution runs at full modes (mx = PH/2,
+ * my = PW/2+1) with the weight spectrum
+ *
+ *   wspec[s][r][ky][i][o] = sqrt(PH PW) * (ortho R2C of the padded k[o][i])
+ *
+ * which fno_linear_conv2d_prepare computes from k float32 [Cout][Cin][kh][kw]
+ * into wspec complex64 [2][PH/2][PW/2+1][Cin][Cout] (compute it once per
+ * kernel and reuse it).  fno_linear_conv2d: x float32 [B][Cin][H][W], out
+ * float32 [B][Cout][Ho][Wo]; the crop window must lie inside y
+ * (FNO_ERR_SHAPE).  1D: k [Cout][Cin][K], wspec [PN/2+1][Cin][Cout] with
+ * PN = fno_linear_conv_length(N, K), x [B][Cin][N], out [B][Cout][No] from
+ * y[crop].  Internal workspace; out must not overlap x or wspec, wspec not k.
+ */
+int fno_linear_conv_length(int n, int k);
+int fno_linear_conv2d_prepare(const float* k, void* wspec, int Cin, int Cout, int H, int W,
+                              int kh, int kw, void* stream);
+int fno_linear_conv2d(const float* x, const void* wspec, float* out, int B, int Cin, int Cout,
+                      int H, int W, int kh, int kw, int crop_h, int crop_w, int Ho, int Wo,
+                      void* stream);
+int fno_linear_conv1d_prepare(const float* k, void* wspec, int Cin, int Cout, int N, int K,
+                              void* stream);
+int fno_linear_conv1d(const float* x, const void* wspec, float* out, int B, int Cin, int Cout,
+                      int N, int K, int crop, int No, void* stream);
 
 /*
  * Per-kernel timing for benchmarks and profilers.  While `events` is non-NULL,

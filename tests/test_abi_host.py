@@ -191,3 +191,24 @@ def test_filter_checks(lib):
     assert f1(A, B, C, 1, 1, 12, 2, None) == SHAPE
     assert f1(A, B, C, 1, 1, 16, 10, None) == MODES
     assert f1(None, B, C, 1, 1, 16, 4, None) == NULL
+
+
+def test_linear_conv_checks(lib):
+    assert lib.fno_linear_conv_length(100, 5) == 128
+    assert lib.fno_linear_conv_length(128, 1) == 128
+    assert lib.fno_linear_conv_length(1, 1) == 2
+    assert lib.fno_linear_conv_length(4096, 2) == 0           # beyond 4096
+    assert lib.fno_linear_conv_length(0, 3) == 0
+    p2 = lib.fno_linear_conv2d_prepare
+    assert p2(None, B, 3, 4, 100, 100, 5, 5, None) == NULL
+    assert p2(A, B, 3, 4, 100, 4095, 5, 5, None) == SHAPE
+    assert p2(A + 4, B, 3, 4, 100, 100, 5, 5, None) == ALIGN
+    assert p2(A, A, 3, 4, 100, 100, 5, 5, None) == ALIAS
+    f2 = lib.fno_linear_conv2d
+    assert f2(A, B, C, 2, 3, 4, 100, 100, 5, 5, 2, 2, 103, 100, None) == SHAPE     # crop window past y (104 rows)
+    assert f2(A, B, C, 2, 3, 4, 100, 100, 5, 5, -1, 2, 100, 100, None) == SHAPE
+    assert f2(None, B, C, 2, 3, 4, 100, 100, 5, 5, 2, 2, 100, 100, None) == NULL
+    assert f2(A, B, A, 2, 3, 4, 100, 100, 5, 5, 2, 2, 100, 100, None) == ALIAS
+    f1 = lib.fno_linear_conv1d
+    assert f1(A, B, C, 2, 3, 4, 100, 5, 0, 105, None) == SHAPE                     # full length is 104
+    assert f1(A, B, None, 2, 3, 4, 100, 5, 0, 104, None) == NULL
