@@ -2,7 +2,7 @@
 """Benchmark of libfno's spectral convolution on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c3] [--variant fused|unfused]
-                    [--pass forward|backward|layer|filter]
+                    [--pass forward|backward|layer|filter|linconv]
 
 One step = one full spectral-convolution call (forward pruned FFT, per-mode
 channel mix, inverse pruned FFT) over one batch of synthetic inputs already
@@ -29,7 +29,9 @@ bounded sample.
 dL/dout read, dL/dx, dL/dW written); --pass layer times the operator with
 the fused layer tail gelu(conv + bias + branch) (adds the branch read);
 --pass filter times the diagonal global filter (x and the mask read, out
-written).
+written); --pass linconv times the zero-padded linear convolution with a
+5x5 (1D: 7-tap) kernel and 'same' output (x and the kernel read, out
+written; the kernel's weight spectrum is prepared before the timed region).
 """
 from __future__ import annotations
 
@@ -51,6 +53,24 @@ from fft_spectral_convolution_amd.inputs import CONFIGS, make_inputs  # noqa: E4
 
 # Algorithmic bytes each kernel must move per launch (read once + write once),
 # by kernel name (per-unit figures: x, W, out and the truncated spectra).
+def _padded(cfg) -> int:
+    """Pixels of one padded image of the linear-convolution pass (5x5 / 7-tap kernel)."""
+    def p2(n):
+        # the library's padded length: the smallest even 7-smooth length >= n
+        m = max(2, n)
+        while True:
+            r = m
+            for f in (2, 3, 5, 7):
+                while r % f == 0:
+                    r //= f
+            if m % 2 == 0 and r == 1:
+                return m
+            m += 1
+    if cfg.kind == "1d":
+        return p2(cfg.W + 6)
+    return p2(cfg.H + 4) * p2(cfg.W + 4)
+
+
 def kernel_bytes(name: str, cfg, backward: bool = False) -> int:
     """Bytes of kernel `name` (a repeat launch carries ":n").  In the backward
     pass the first transform runs on dL/dout (Cout channels) and the inverse
@@ -96,6 +116,9 @@ def kernel_bytes(name: str, cfg, backward: bool = False) -> int:
         "rows_inv_gelu": (r_out if cfg.kind == "2d" else yh) + 2 * n_out,
         # diagonal filter: both truncated spectra and the (mode, channel) mask
         "mix_diag": xh + yh + (m_modes * cfg.Cin * c8),
+        # linear convolution: zero-padding copy and crop
+        "pad": n_in + cfg.B * cfg.Cin * _padded(cfg) * 4,
+        "crop": cfg.B * cfg.Cout * _padded(cfg) * 4 + n_out,
         "wgrad": xh + yh + wb,
         "wadjoint": 2 * wb,
         # sum of the batch splits' partial weight gradients (when the batch
@@ -129,7 +152,7 @@ def load_traffic(kernel: str, workload: str):
         return None
 
 
-def cpu_baseline(cfg, x, w, budget_s: float = 12.0, g=None, compulsory=None, layer=None, mask=None):
+def cpu_baseline(cfg, x, w, budget_s: float = 12.0, g=None, compulsory=None, layer=None, mask=None, kernel=None):
     """Time the fp64 oracle (as it stands) on this host on a bounded sample
     (the backward pass when the output gradient g is given, the operator with
     the layer tail when layer = (bias, branch) is)."""
@@ -141,6 +164,12 @@ def cpu_baseline(cfg, x, w, budget_s: float = 12.0, g=None, compulsory=None, lay
         threads = 1
     # one batch item first, to size the sample
     def call(nb):
+        if kernel is not None:
+            if cfg.kind == "1d":
+                kk = kernel.shape[-1]
+                return oracle.linear_conv1d_ref(x[:nb], kernel, (kk - 1) // 2, cfg.W)
+            kh, kw = kernel.shape[-2:]
+            return oracle.linear_conv2d_ref(x[:nb], kernel, (kh - 1) // 2, (kw - 1) // 2, cfg.H, cfg.W)
         if mask is not None:
             if cfg.kind == "1d":
                 return oracle.spectral_filter1d_ref(x[:nb], mask, cfg.my)
@@ -192,10 +221,13 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="c3", choices=sorted(CONFIGS))
     ap.add_argument("--variant", default="fused", choices=["fused", "unfused"])
-    ap.add_argument("--pass", dest="which", default="forward", choices=["forward", "backward", "layer", "filter"],
+    ap.add_argument("--pass", dest="which", default="forward",
+                    choices=["forward", "backward", "layer", "filter", "linconv"],
                     help="time the operator (default), its backward pass (both gradients), the operator "
                          "with the fused layer tail gelu(conv + bias + branch), or the diagonal global "
-                         "filter (one complex weight per kept mode and channel)")
+                         "filter (one complex weight per kept mode and channel), or the zero-padded linear "
+                         "convolution with a 5x5 (1D: 7-tap) kernel, 'same' output, weight spectrum prepared "
+                         "once outside the timed region")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -240,6 +272,7 @@ def main():
     g_np = None
     layer_np = None
     filter_np = None
+    linconv_np = None
     if args.which == "backward":
         # step: both gradients of a real loss, given a synthetic dL/dout of the
         # output's shape; compulsory bytes: x, w, dL/dout read, dL/dx, dL/dw written
@@ -287,6 +320,22 @@ def main():
             step = lambda i: fno.fno_spectral_filter1d(xs[i % nsets], mask, cfg.my, out=outs[i % nsets])
         else:
             step = lambda i: fno.fno_spectral_filter2d(xs[i % nsets], mask, cfg.mx, cfg.my, out=outs[i % nsets])
+    elif args.which == "linconv":
+        # step: out = crop(C2R(R2C(pad x) * wspec)), 'same' output; the weight
+        # spectrum of the kernel is prepared once (kernels are fixed across
+        # calls); compulsory bytes: x and the kernel read, out written
+        rng = np.random.default_rng(4)
+        kshape = (cfg.Cout, cfg.Cin, 7) if cfg.kind == "1d" else (cfg.Cout, cfg.Cin, 5, 5)
+        k_np = (rng.standard_normal(kshape) / np.sqrt(np.prod(kshape[1:]))).astype(np.float32)
+        kd = torch.from_numpy(k_np).to(dev)
+        compulsory = cfg.compulsory_bytes - int(w_np.nbytes) + int(k_np.nbytes)
+        linconv_np = k_np
+        if cfg.kind == "1d":
+            wspec = fno.fno_linear_conv1d_prepare(kd, cfg.W)
+            step = lambda i: fno.fno_linear_conv1d(xs[i % nsets], kd, wspec=wspec, out=outs[i % nsets])
+        else:
+            wspec = fno.fno_linear_conv2d_prepare(kd, cfg.H, cfg.W)
+            step = lambda i: fno.fno_linear_conv2d(xs[i % nsets], kd, wspec=wspec, out=outs[i % nsets])
     elif cfg.kind == "1d":
         fn = fno.fno_spectral_conv1d if args.variant == "fused" else fno.fno_spectral_conv1d_unfused
         step = lambda i: fn(xs[i % nsets], w, cfg.my, out=outs[i % nsets])
@@ -415,7 +464,7 @@ def main():
         }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(cfg, x_np, w_np, args.cpu_budget, g=g_np, compulsory=compulsory,
-                                            layer=layer_np, mask=filter_np)
+                                            layer=layer_np, mask=filter_np, kernel=linconv_np)
     print(json.dumps(line), flush=True)
 
 

@@ -88,6 +88,36 @@ int ilog2(int v) {
     return l;
 }
 
+// Transform lengths: powers of two up to 4096, or other 7-smooth lengths
+// (2^a 3^b 5^c 7^d) up to 4096 on the mixed-radix stage kernels.
+bool length_ok(int n) { return n >= 2 && n <= kNMax && (is_pow2(n) || mixed_supported(n)); }
+
+// Stage launchers by transform length: power-of-two lengths take the
+// specialised and generic kernels, the others the mixed-radix ones.
+hipError_t rows_fwd_n(const float* x, float2* y, int64_t nrows, int W, int my, int y_ld, float scale,
+                      const float2* tw, hipStream_t s) {
+    return is_pow2(W) ? launch_rows_fwd(x, y, nrows, ilog2(W), my, y_ld, scale, tw, s)
+                      : launch_rows_fwd_mr(x, y, nrows, W, my, y_ld, scale, s);
+}
+hipError_t rows_inv_n(const float2* y, float* out, int64_t nrows, int W, int my, int y_ld, float scale,
+                      const float2* tw, hipStream_t s, const Epilogue& epi = Epilogue{}) {
+    return is_pow2(W) ? launch_rows_inv(y, out, nrows, ilog2(W), my, y_ld, scale, tw, s, epi)
+                      : launch_rows_inv_mr(y, out, nrows, W, my, y_ld, scale, s, epi);
+}
+hipError_t cols_fwd_n(const float2* r, float2* xh, int64_t nimg, int H, int mx, int my, float scale,
+                      const float2* tw, hipStream_t s) {
+    return is_pow2(H) ? launch_cols_fwd(r, xh, nimg, ilog2(H), mx, my, scale, tw, s)
+                      : launch_cols_fwd_mr(r, xh, nimg, H, mx, my, scale, s);
+}
+hipError_t cols_inv_n(const float2* yh, float2* r, int64_t nimg, int H, int mx, int my, const float2* tw,
+                      hipStream_t s) {
+    return is_pow2(H) ? launch_cols_inv(yh, r, nimg, ilog2(H), mx, my, tw, s)
+                      : launch_cols_inv_mr(yh, r, nimg, H, mx, my, s);
+}
+
+// C2R Nyquist bin of a length-W transform (none when W is odd)
+int nyquist(int W) { return W % 2 == 0 ? W / 2 : -1; }
+
 bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
 
 bool overlap(const void* a, size_t abytes, const void* b, size_t bbytes) {
@@ -162,14 +192,14 @@ size_t align_up(size_t v) { return (v + 255) & ~size_t(255); }
 
 int check_dims_2d(int B, int C, int H, int W, int mx, int my) {
     if (B < 1 || C < 1) return FNO_ERR_SHAPE;
-    if (!is_pow2(H) || !is_pow2(W) || H < 2 || W < 2 || H > kNMax || W > kNMax) return FNO_ERR_SHAPE;
+    if (!length_ok(H) || !length_ok(W)) return FNO_ERR_SHAPE;
     if (mx < 1 || 2 * mx > H || my < 1 || my > W / 2 + 1) return FNO_ERR_MODES;
     return FNO_OK;
 }
 
 int check_dims_1d(int B, int C, int N, int modes) {
     if (B < 1 || C < 1) return FNO_ERR_SHAPE;
-    if (!is_pow2(N) || N < 2 || N > kNMax) return FNO_ERR_SHAPE;
+    if (!length_ok(N)) return FNO_ERR_SHAPE;
     if (modes < 1 || modes > N / 2 + 1) return FNO_ERR_MODES;
     return FNO_OK;
 }
@@ -227,7 +257,9 @@ int run_mix_adjoint(const float2* gh, const SpecLayout& lg, const float2* w, flo
     return run_mix(gh, lg, wt, zh, lz, B, Cg, Cz, M, st);
 }
 
-bool small_path(const Shape2d& s) { return small2d_supported(s.log2H, s.log2W, s.my); }
+bool small_path(const Shape2d& s) {
+    return is_pow2(s.H) && is_pow2(s.W) && small2d_supported(s.log2H, s.log2W, s.my);
+}
 
 // Staged (unfused) transforms: rows and columns as separate kernels, the row
 // spectrum R (or R') in workspace; spectra in the canonical layout.
@@ -235,10 +267,10 @@ int run_forward2d_staged(const Shape2d& s, int64_t C, const float* x, float2* xh
                          hipStream_t st) {
     const float scale = (float)(1.0 / std::sqrt((double)s.H * (double)s.W));
     rec_kernel("rows_fwd", st);
-    hipError_t e = launch_rows_fwd(x, r, s.B * C * s.H, s.log2W, s.my, s.my, 1.0f, tw, st);
+    hipError_t e = rows_fwd_n(x, r, s.B * C * s.H, s.W, s.my, s.my, 1.0f, tw, st);
     if (e != hipSuccess) return hip_fail(e);
     rec_kernel("cols_fwd", st);
-    e = launch_cols_fwd(r, xh, s.B * C, s.log2H, s.mx, s.my, scale, tw, st);
+    e = cols_fwd_n(r, xh, s.B * C, s.H, s.mx, s.my, scale, tw, st);
     if (e != hipSuccess) return hip_fail(e);
     return FNO_OK;
 }
@@ -248,12 +280,12 @@ int run_inverse2d_staged(const Shape2d& s, int64_t C, const float2* yh, float* o
                          hipStream_t st, const Epilogue& epi = Epilogue{}) {
     const float scale = (float)(1.0 / std::sqrt((double)s.H * (double)s.W));
     rec_kernel("cols_inv", st);
-    hipError_t e = launch_cols_inv(yh, r, s.B * C, s.log2H, s.mx, s.my, tw, st);
+    hipError_t e = cols_inv_n(yh, r, s.B * C, s.H, s.mx, s.my, tw, st);
     if (e != hipSuccess) return hip_fail(e);
     rec_kernel(epi.on ? "rows_inv_gelu" : "rows_inv", st);
     Epilogue ep = epi;
     ep.rows_per_chan = (uint32_t)s.H;
-    e = launch_rows_inv(r, out, s.B * C * s.H, s.log2W, s.my, s.my, scale, tw, st, ep);
+    e = rows_inv_n(r, out, s.B * C * s.H, s.W, s.my, s.my, scale, tw, st, ep);
     if (e != hipSuccess) return hip_fail(e);
     return FNO_OK;
 }
@@ -341,16 +373,15 @@ int run_unfused_1d(int64_t B, int64_t Cin, int64_t Cout, int N, int modes, const
     float2* xh = reinterpret_cast<float2*>(p);
     p += align_up((size_t)B * Cin * modes * sizeof(float2));
     float2* yh = reinterpret_cast<float2*>(p);
-    const int l2 = ilog2(N);
     rec_kernel("rows_fwd", st);
-    hipError_t e = launch_rows_fwd(x, xh, B * Cin, l2, modes, modes, scale, tw, st);
+    hipError_t e = rows_fwd_n(x, xh, B * Cin, N, modes, modes, scale, tw, st);
     if (e != hipSuccess) return hip_fail(e);
     int rc = run_mix(xh, canonical_layout(Cin, modes), w, yh, canonical_layout(Cout, modes), B, Cin, Cout, modes, st);
     if (rc) return rc;
     rec_kernel(epi.on ? "rows_inv_gelu" : "rows_inv", st);
     Epilogue ep = epi;
     ep.rows_per_chan = 1;
-    e = launch_rows_inv(yh, out, B * Cout, l2, modes, modes, scale, tw, st, ep);
+    e = rows_inv_n(yh, out, B * Cout, N, modes, modes, scale, tw, st, ep);
     if (e != hipSuccess) return hip_fail(e);
     return FNO_OK;
 }
@@ -434,17 +465,16 @@ int filter1d_common(const float* x, const void* mask, float* out, int B, int C, 
     float2* xh = static_cast<float2*>(ws);
     float2* yh = reinterpret_cast<float2*>(static_cast<char*>(ws) + hb);
     const float scale = (float)(1.0 / std::sqrt((double)N));
-    const int l2 = ilog2(N);
     hipStream_t hs = static_cast<hipStream_t>(stream);
     auto run = [&]() -> int {
         rec_kernel("rows_fwd", hs);
-        hipError_t e = launch_rows_fwd(x, xh, (int64_t)B * C, l2, modes, modes, scale, st->twiddle, hs);
+        hipError_t e = rows_fwd_n(x, xh, (int64_t)B * C, N, modes, modes, scale, st->twiddle, hs);
         if (e != hipSuccess) return hip_fail(e);
         rec_kernel("mix_diag", hs);
         e = launch_mix_diag(xh, yh, canonical_layout(C, modes), static_cast<const float2*>(mask), B, C, modes, hs);
         if (e != hipSuccess) return hip_fail(e);
         rec_kernel("rows_inv", hs);
-        e = launch_rows_inv(yh, out, (int64_t)B * C, l2, modes, modes, scale, st->twiddle, hs);
+        e = rows_inv_n(yh, out, (int64_t)B * C, N, modes, modes, scale, st->twiddle, hs);
         if (e != hipSuccess) return hip_fail(e);
         return FNO_OK;
     };
@@ -456,15 +486,16 @@ int filter1d_common(const float* x, const void* mask, float* out, int B, int C, 
 // zero-padded linear convolution
 // ---------------------------------------------------------------------------
 
-// Transform length of the padded grid: the smallest power of two (>= 2) that
-// holds the full linear convolution of n samples with a k-tap kernel; 0 when
-// the sizes are out of range.
+// Transform length of the padded grid: the smallest even 7-smooth length
+// (2^a 3^b 5^c 7^d, a >= 1) that holds the full linear convolution of n
+// samples with a k-tap kernel (even, so that full modes cover every kx);
+// 0 when the sizes are out of range.
 int linconv_len(int n, int k) {
     if (n < 1 || k < 1) return 0;
     const int64_t need = (int64_t)n + k - 1;
-    int64_t p = 2;
-    while (p < need) p <<= 1;
-    return p <= kNMax ? (int)p : 0;
+    for (int64_t p = need < 2 ? 2 : need; p <= kNMax; ++p)
+        if (p % 2 == 0 && length_ok((int)p)) return (int)p;
+    return 0;
 }
 
 int linconv2d_prepare(const float* k, void* wspec, int Cin, int Cout, int H, int W, int kh, int kw, void* stream) {
@@ -570,7 +601,7 @@ int linconv1d_prepare(const float* k, void* wspec, int Cin, int Cout, int N, int
         hipError_t e = launch_pad2d(k, kp, io, 1, K, 1, PN, hs);
         if (e != hipSuccess) return hip_fail(e);
         rec_kernel("rows_fwd", hs);
-        e = launch_rows_fwd(kp, khs, io, ilog2(PN), modes, modes, (float)(1.0 / std::sqrt((double)PN)), st->twiddle, hs);
+        e = rows_fwd_n(kp, khs, io, PN, modes, modes, (float)(1.0 / std::sqrt((double)PN)), st->twiddle, hs);
         if (e != hipSuccess) return hip_fail(e);
         rec_kernel("spec_to_weight", hs);
         e = launch_spec_to_weight(khs, static_cast<float2*>(wspec), modes, Cin, Cout, (float)std::sqrt((double)PN), hs);
@@ -770,12 +801,12 @@ int run_backward_2d(const Shape2d& s, const float* x, const float2* w, const flo
         if (rc) return rc;
         rec_kernel("wgrad", st);
         int splits = 1;
-        hipError_t e = launch_weight_grad(xh, p.lx, gh, p.lg, gw, s.B, s.Cin, s.Cout, m, s.my, s.W / 2, wg_ws,
+        hipError_t e = launch_weight_grad(xh, p.lx, gh, p.lg, gw, s.B, s.Cin, s.Cout, m, s.my, nyquist(s.W), wg_ws,
                                           p.wg_bytes, &splits, st);
         if (e != hipSuccess) return hip_fail(e);
         if (splits > 1) {
             rec_kernel("wgrad_reduce", st);
-            e = launch_weight_grad_reduce(wg_ws, gw, s.Cin, s.Cout, m, splits, s.my, s.W / 2, st);
+            e = launch_weight_grad_reduce(wg_ws, gw, s.Cin, s.Cout, m, splits, s.my, nyquist(s.W), st);
             if (e != hipSuccess) return hip_fail(e);
         }
     }
@@ -840,26 +871,25 @@ int backward1d_common(const float* x, const void* w, const float* g, float* gx, 
     void* wg_ws = q + 2 * xb + gb + wtb;
     const SpecLayout lx = canonical_layout(Cin, modes), lg = canonical_layout(Cout, modes);
     const float scale = (float)(1.0 / std::sqrt((double)N));
-    const int l2 = ilog2(N);
     hipStream_t hs = static_cast<hipStream_t>(stream);
     const float2* wc = static_cast<const float2*>(w);
     auto run = [&]() -> int {
         rec_kernel("rows_fwd", hs);
-        hipError_t e = launch_rows_fwd(g, gh, (int64_t)B * Cout, l2, modes, modes, scale, st->twiddle, hs);
+        hipError_t e = rows_fwd_n(g, gh, (int64_t)B * Cout, N, modes, modes, scale, st->twiddle, hs);
         if (e != hipSuccess) return hip_fail(e);
         if (gw) {
             rec_kernel("rows_fwd", hs);
-            e = launch_rows_fwd(x, xh, (int64_t)B * Cin, l2, modes, modes, scale, st->twiddle, hs);
+            e = rows_fwd_n(x, xh, (int64_t)B * Cin, N, modes, modes, scale, st->twiddle, hs);
             if (e != hipSuccess) return hip_fail(e);
             rec_kernel("wgrad", hs);
             int splits = 1;
-            e = launch_weight_grad(xh, lx, gh, lg, static_cast<float2*>(gw), B, Cin, Cout, modes, modes, N / 2, wg_ws,
+            e = launch_weight_grad(xh, lx, gh, lg, static_cast<float2*>(gw), B, Cin, Cout, modes, modes, nyquist(N), wg_ws,
                                    wgb, &splits, hs);
             if (e != hipSuccess) return hip_fail(e);
             if (splits > 1) {
                 rec_kernel("wgrad_reduce", hs);
                 e = launch_weight_grad_reduce(wg_ws, static_cast<float2*>(gw), Cin, Cout, modes, splits, modes,
-                                              N / 2, hs);
+                                              nyquist(N), hs);
                 if (e != hipSuccess) return hip_fail(e);
             }
         }
@@ -867,7 +897,7 @@ int backward1d_common(const float* x, const void* w, const float* g, float* gx, 
             const int mrc = run_mix_adjoint(gh, lg, wc, wt, zh, lx, B, Cout, Cin, modes, hs);
             if (mrc) return mrc;
             rec_kernel("rows_inv", hs);
-            e = launch_rows_inv(zh, gx, (int64_t)B * Cin, l2, modes, modes, scale, st->twiddle, hs);
+            e = rows_inv_n(zh, gx, (int64_t)B * Cin, N, modes, modes, scale, st->twiddle, hs);
             if (e != hipSuccess) return hip_fail(e);
         }
         return FNO_OK;
@@ -895,7 +925,7 @@ const char* fno_status_string(int status) {
     switch (status) {
         case FNO_OK: return "ok";
         case FNO_ERR_NULL: return "a required pointer is NULL";
-        case FNO_ERR_SHAPE: return "a size is out of range or not a power of two";
+        case FNO_ERR_SHAPE: return "a size is out of range or has a prime factor above 7";
         case FNO_ERR_MODES: return "mode counts out of range (need 1<=mx, 2*mx<=H, 1<=my<=W/2+1)";
         case FNO_ERR_ALIAS: return "output overlaps an input";
         case FNO_ERR_ALIGN: return "a pointer is not suitably aligned";
@@ -1096,7 +1126,7 @@ int fno_forward1d(const float* x, void* xh, int B, int C, int N, int modes, void
     hipStream_t hs = static_cast<hipStream_t>(stream);
     rec_begin();
     rec_kernel("rows_fwd", hs);
-    hipError_t e = launch_rows_fwd(x, static_cast<float2*>(xh), (int64_t)B * C, ilog2(N), modes, modes, scale,
+    hipError_t e = rows_fwd_n(x, static_cast<float2*>(xh), (int64_t)B * C, N, modes, modes, scale,
                                    st->twiddle, hs);
     return rec_end(hs, e == hipSuccess ? FNO_OK : hip_fail(e));
 }
@@ -1125,7 +1155,7 @@ int fno_inverse1d(const void* yh, float* out, int B, int C, int N, int modes, vo
     hipStream_t hs = static_cast<hipStream_t>(stream);
     rec_begin();
     rec_kernel("rows_inv", hs);
-    hipError_t e = launch_rows_inv(static_cast<const float2*>(yh), out, (int64_t)B * C, ilog2(N), modes, modes,
+    hipError_t e = rows_inv_n(static_cast<const float2*>(yh), out, (int64_t)B * C, N, modes, modes,
                                    scale, st->twiddle, hs);
     return rec_end(hs, e == hipSuccess ? FNO_OK : hip_fail(e));
 }

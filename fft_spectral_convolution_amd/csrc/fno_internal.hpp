@@ -192,6 +192,18 @@ bool mix_diag_supported(const SpecLayout& lay, int64_t M);
 hipError_t launch_mix_diag(const float2* xh, float2* yh, const SpecLayout& lay, const float2* mask, int64_t B,
                            int64_t C, int64_t M, hipStream_t s);
 
+// ---- mixed-radix stage kernels (fno_mixed.hip) -----------------------------
+// Same contracts as launch_rows_fwd / launch_cols_fwd / launch_cols_inv /
+// launch_rows_inv, for 7-smooth lengths 2..4096 given as lengths (W, H).
+bool mixed_supported(int n);
+hipError_t launch_rows_fwd_mr(const float* x, float2* y, int64_t nrows, int W, int my, int y_ld, float scale,
+                              hipStream_t s);
+hipError_t launch_cols_fwd_mr(const float2* r, float2* xh, int64_t nimg, int H, int mx, int my, float scale,
+                              hipStream_t s);
+hipError_t launch_cols_inv_mr(const float2* yh, float2* r, int64_t nimg, int H, int mx, int my, hipStream_t s);
+hipError_t launch_rows_inv_mr(const float2* y, float* out, int64_t nrows, int W, int my, int y_ld, float scale,
+                              hipStream_t s, const Epilogue& epi = Epilogue{});
+
 // ---- zero-padded linear convolution helpers (fno_linconv.hip) ---------------
 // dst[img][PH][PW] = src[img][H][W] zero-padded (bottom and right).
 hipError_t launch_pad2d(const float* src, float* dst, int64_t nimg, int H, int W, int PH, int PW, hipStream_t s);

@@ -1,0 +1,373 @@
+// Stage kernels for transform lengths that are not powers of two: any
+// 7-smooth N (2^a 3^b 5^c 7^d) from 2 to 4096 (the FFT blog, section 6.2:
+// sizes such as 96 or 100 take mixed-radix paths; section 2.1: the padded
+// length of a linear convolution).  Same contracts as the generic
+// power-of-two stage kernels (fno_generic.hip), with the transform run as
+// a mixed-radix Stockham FFT in LDS (radix-4/2 passes first, then 3, 5, 7)
+// on a per-length twiddle table W_N^m = exp(-2 pi i m / N), m < N, built on
+// the host in double precision and rounded once.
+#include <cmath>
+#include <map>
+#include <mutex>
+#include <utility>
+#include <vector>
+
+#include "fno_device.hpp"
+#include "fno_internal.hpp"
+
+namespace fno {
+namespace {
+
+constexpr int kMrThreads = 256;
+constexpr int kMrMaxPasses = 12;
+
+struct MRPlan {
+    int n, npass;
+    int r[kMrMaxPasses];
+};
+
+// Radix-R DFT by its definition (R = 3, 5, 7), compile-time twiddles:
+// v[k] <- sum_r v[r] exp(SIGN 2 pi i r k / R).
+template <int R, int SIGN>
+__device__ __forceinline__ void dft_odd(float2 (&v)[R]) {
+    float2 out[R];
+    static_for<0, R>([&](auto k) {
+        float2 acc = v[0];
+        static_for<1, R>([&](auto r) {
+            constexpr int e = (k * r) % R;
+            constexpr float c = (float)exact_cos(8 * e, 8 * R);
+            constexpr float s = (float)(SIGN * exact_sin(8 * e, 8 * R));
+            acc.x = fmaf(v[r].x, c, fmaf(-v[r].y, s, acc.x));
+            acc.y = fmaf(v[r].x, s, fmaf(v[r].y, c, acc.y));
+        });
+        out[k] = acc;
+    });
+#pragma unroll
+    for (int k = 0; k < R; ++k) v[k] = out[k];
+}
+
+// One radix-R Stockham pass of an n-point transform whose sub-transforms of
+// length ns are done: butterfly j reads src[j + r n/R], twiddles by
+// W_{ns R}^{r (j mod ns)}, runs the radix-R DFT and writes
+// dst[(j - j mod ns) R + j mod ns + r ns].
+template <int R, int SIGN>
+__device__ __forceinline__ void mr_pass(const float2* src, float2* dst, int n, int ns, int j,
+                                        const float2* __restrict__ twn) {
+    const int stride = n / R;
+    float2 v[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) v[r] = src[j + r * stride];
+    const int k = j % ns;
+    if (ns > 1) {
+        const int step = n / (ns * R);
+#pragma unroll
+        for (int r = 1; r < R; ++r) {
+            float2 t = twn[r * k * step];
+            if (SIGN > 0) t.y = -t.y;
+            v[r] = cmul(v[r], t);
+        }
+    }
+    if constexpr (R == 2 || R == 4) dft<R, SIGN>(v);
+    else dft_odd<R, SIGN>(v);
+    const int base = (j - k) * R + k;
+#pragma unroll
+    for (int r = 0; r < R; ++r) dst[base + r * ns] = v[r];
+}
+
+// Full transform of `nrows` rows of length p.n (row stride p.n) in LDS
+// buffer a, ping-ponging through b; returns the buffer with the result.
+template <int SIGN>
+__device__ float2* fft_rows_mr(float2* a, float2* b, int nrows, const MRPlan& p, const float2* __restrict__ twn,
+                               int tid, int nthr) {
+    const int n = p.n;
+    int ns = 1;
+    for (int pass = 0; pass < p.npass; ++pass) {
+        const int R = p.r[pass];
+        const int J = n / R;
+        const int total = nrows * J;
+        for (int idx = tid; idx < total; idx += nthr) {
+            const int row = idx / J;
+            const int j = idx - row * J;
+            float2* s = a + row * n;
+            float2* d = b + row * n;
+            switch (R) {
+                case 4: mr_pass<4, SIGN>(s, d, n, ns, j, twn); break;
+                case 2: mr_pass<2, SIGN>(s, d, n, ns, j, twn); break;
+                case 3: mr_pass<3, SIGN>(s, d, n, ns, j, twn); break;
+                case 5: mr_pass<5, SIGN>(s, d, n, ns, j, twn); break;
+                default: mr_pass<7, SIGN>(s, d, n, ns, j, twn); break;
+            }
+        }
+        __syncthreads();
+        float2* t = a;
+        a = b;
+        b = t;
+        ns *= R;
+    }
+    return a;
+}
+
+// rows of length W = p.n (real) -> bins ky < my, two rows per complex
+// transform (z = a + i b, A[k] = (Z[k] + conj Z[-k]) / 2, B[k] = (Z[k] - conj Z[-k]) / 2i)
+__global__ __launch_bounds__(kMrThreads) void k_rows_fwd_mr(const float* __restrict__ x, float2* __restrict__ y,
+                                                            int64_t nrows, int my, int y_ld, float scale, MRPlan p,
+                                                            const float2* __restrict__ twn) {
+    __shared__ float2 buf[2][kLdsElems];
+    const int W = p.n;
+    const int P = kLdsElems / W;
+    const int tid = threadIdx.x;
+    const int64_t npairs = (nrows + 1) / 2;
+    const int64_t pair0 = (int64_t)blockIdx.x * P;
+    const int prows = (int)(npairs - pair0 < P ? npairs - pair0 : P);
+    for (int e = tid; e < prows * W; e += kMrThreads) {
+        const int pr = e / W;
+        const int n = e - pr * W;
+        const int64_t ra = 2 * (pair0 + pr);
+        const float a = x[ra * W + n];
+        const float b = (ra + 1 < nrows) ? x[(ra + 1) * W + n] : 0.0f;
+        buf[0][e] = make_float2(a, b);
+    }
+    __syncthreads();
+    const float2* res = fft_rows_mr<-1>(buf[0], buf[1], prows, p, twn, tid, kMrThreads);
+    for (int e = tid; e < prows * my; e += kMrThreads) {
+        const int pr = e / my;
+        const int k = e - pr * my;
+        const float2 zk = res[pr * W + k];
+        const float2 zm = res[pr * W + (k == 0 ? 0 : W - k)];
+        const float2 a = make_float2(0.5f * (zk.x + zm.x), 0.5f * (zk.y - zm.y));
+        const float2 b = make_float2(0.5f * (zk.y + zm.y), -0.5f * (zk.x - zm.x));
+        const int64_t ra = 2 * (pair0 + pr);
+        y[ra * y_ld + k] = cscale(a, scale);
+        if (ra + 1 < nrows) y[(ra + 1) * y_ld + k] = cscale(b, scale);
+    }
+}
+
+// R[nimg][H][my] -> xh[nimg][2 mx][my] (kept kx only), H = p.n
+__global__ __launch_bounds__(kMrThreads) void k_cols_fwd_mr(const float2* __restrict__ r, float2* __restrict__ xh,
+                                                            int mx, int my, int kb, int nkb, float scale, MRPlan p,
+                                                            const float2* __restrict__ twn) {
+    __shared__ float2 buf[2][kLdsElems];
+    const int H = p.n;
+    const int tid = threadIdx.x;
+    const int64_t img = blockIdx.x / nkb;
+    const int ky0 = (int)(blockIdx.x % nkb) * kb;
+    const int ncol = min(kb, my - ky0);
+    const float2* src = r + img * H * my;
+    for (int e = tid; e < ncol * H; e += kMrThreads) {
+        const int h = e / ncol;
+        const int c = e - h * ncol;
+        buf[0][c * H + h] = src[(int64_t)h * my + ky0 + c];
+    }
+    __syncthreads();
+    const float2* res = fft_rows_mr<-1>(buf[0], buf[1], ncol, p, twn, tid, kMrThreads);
+    float2* dst = xh + img * (2 * mx) * my;
+    for (int e = tid; e < 2 * mx * ncol; e += kMrThreads) {
+        const int q = e / ncol;
+        const int c = e - q * ncol;
+        const int kx = q < mx ? q : H - 2 * mx + q;
+        dst[(int64_t)q * my + ky0 + c] = cscale(res[c * H + kx], scale);
+    }
+}
+
+// yh[nimg][2 mx][my] -> zero-filled inverse along H -> R'[nimg][H][my]
+__global__ __launch_bounds__(kMrThreads) void k_cols_inv_mr(const float2* __restrict__ yh, float2* __restrict__ r,
+                                                            int mx, int my, int kb, int nkb, MRPlan p,
+                                                            const float2* __restrict__ twn) {
+    __shared__ float2 buf[2][kLdsElems];
+    const int H = p.n;
+    const int tid = threadIdx.x;
+    const int64_t img = blockIdx.x / nkb;
+    const int ky0 = (int)(blockIdx.x % nkb) * kb;
+    const int ncol = min(kb, my - ky0);
+    const float2* src = yh + img * (2 * mx) * my;
+    for (int e = tid; e < ncol * H; e += kMrThreads) {
+        const int c = e / H;
+        const int kx = e - c * H;
+        if (kx >= mx && kx < H - mx) buf[0][e] = make_float2(0.0f, 0.0f);
+    }
+    for (int e = tid; e < 2 * mx * ncol; e += kMrThreads) {
+        const int q = e / ncol;
+        const int c = e - q * ncol;
+        const int kx = q < mx ? q : H - 2 * mx + q;
+        buf[0][c * H + kx] = src[(int64_t)q * my + ky0 + c];
+    }
+    __syncthreads();
+    const float2* res = fft_rows_mr<1>(buf[0], buf[1], ncol, p, twn, tid, kMrThreads);
+    float2* dst = r + img * H * my;
+    for (int e = tid; e < ncol * H; e += kMrThreads) {
+        const int h = e / ncol;
+        const int c = e - h * ncol;
+        dst[(int64_t)h * my + ky0 + c] = res[c * H + h];
+    }
+}
+
+// R'[nrows][y_ld] (bins ky < my) -> C2R rows of length W = p.n, times scale
+// (imaginary parts of the DC bin, and of the Nyquist bin when W is even,
+// dropped); EPI: the fused output epilogue on every output
+template <bool EPI>
+__global__ __launch_bounds__(kMrThreads) void k_rows_inv_mr(const float2* __restrict__ y, float* __restrict__ out,
+                                                            int64_t nrows, int my, int y_ld, float scale, MRPlan p,
+                                                            const float2* __restrict__ twn, Epilogue epi) {
+    __shared__ float2 buf[2][kLdsElems];
+    const int W = p.n;
+    const int P = kLdsElems / W;
+    const int tid = threadIdx.x;
+    const int64_t npairs = (nrows + 1) / 2;
+    const int64_t pair0 = (int64_t)blockIdx.x * P;
+    const int prows = (int)(npairs - pair0 < P ? npairs - pair0 : P);
+    for (int e = tid; e < prows * W; e += kMrThreads) {
+        const int pr = e / W;
+        const int k = e - pr * W;
+        const int kk = (2 * k <= W) ? k : W - k;
+        const int64_t ra = 2 * (pair0 + pr);
+        float2 z = make_float2(0.0f, 0.0f);
+        if (kk < my) {
+            const float2 ya = y[ra * y_ld + kk];
+            const float2 yb = (ra + 1 < nrows) ? y[(ra + 1) * y_ld + kk] : make_float2(0.0f, 0.0f);
+            if (kk == 0 || 2 * kk == W) z = make_float2(ya.x, yb.x);
+            else if (k == kk) z = make_float2(ya.x - yb.y, ya.y + yb.x);
+            else z = make_float2(ya.x + yb.y, yb.x - ya.y);
+        }
+        buf[0][e] = z;
+    }
+    __syncthreads();
+    const float2* res = fft_rows_mr<1>(buf[0], buf[1], prows, p, twn, tid, kMrThreads);
+    for (int e = tid; e < prows * W; e += kMrThreads) {
+        const int pr = e / W;
+        const int n = e - pr * W;
+        const int64_t ra = 2 * (pair0 + pr);
+        const float2 z = res[e];
+        if constexpr (EPI) {
+            const __amdgpu_buffer_rsrc_t rb =
+                make_rsrc(epi.branch ? epi.branch + 2 * pair0 * W : nullptr,
+                          epi.branch ? (uint32_t)((nrows - 2 * pair0 < 2 * P ? nrows - 2 * pair0 : 2 * P) * W * 4) : 0u);
+            const uint32_t off = (uint32_t)((ra - 2 * pair0) * W + n) * 4u;
+            out[ra * W + n] = epi_apply(epi, z.x * scale, epi_bias(epi, (uint32_t)ra), buffer_load_f1(rb, off, 0));
+            if (ra + 1 < nrows)
+                out[(ra + 1) * W + n] = epi_apply(epi, z.y * scale, epi_bias(epi, (uint32_t)(ra + 1)),
+                                                  buffer_load_f1(rb, off + (uint32_t)W * 4u, 0));
+        } else {
+            out[ra * W + n] = z.x * scale;
+            if (ra + 1 < nrows) out[(ra + 1) * W + n] = z.y * scale;
+        }
+    }
+}
+
+// radix-4 passes first, then 2, 3, 5, 7
+bool make_plan(int n, MRPlan* p) {
+    if (n < 2 || n > kLdsElems) return false;
+    p->n = n;
+    p->npass = 0;
+    int m = n;
+    for (int r : {4, 2, 3, 5, 7})
+        while (m % r == 0) {
+            if (p->npass == kMrMaxPasses) return false;
+            p->r[p->npass++] = r;
+            m /= r;
+        }
+    return m == 1;
+}
+
+// per (device, n) twiddle tables, built once and kept for the process
+std::mutex g_tw_mutex;
+std::map<std::pair<int, int>, float2*> g_tw;
+
+hipError_t twiddles(int n, const float2** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    std::lock_guard<std::mutex> lock(g_tw_mutex);
+    auto it = g_tw.find({dev, n});
+    if (it != g_tw.end()) {
+        *out = it->second;
+        return hipSuccess;
+    }
+    std::vector<float2> host(n);
+    for (int m = 0; m < n; ++m) {
+        const double a = -2.0 * M_PI * (double)m / (double)n;
+        host[m] = make_float2((float)std::cos(a), (float)std::sin(a));
+    }
+    float2* d = nullptr;
+    e = hipMalloc(&d, sizeof(float2) * n);
+    if (e != hipSuccess) return e;
+    e = hipMemcpy(d, host.data(), sizeof(float2) * n, hipMemcpyHostToDevice);
+    if (e != hipSuccess) {
+        (void)hipFree(d);
+        return e;
+    }
+    g_tw[{dev, n}] = d;
+    *out = d;
+    return hipSuccess;
+}
+
+int64_t blocks_for(int64_t n) { return n < 1 ? 1 : n; }
+
+}  // namespace
+
+bool mixed_supported(int n) {
+    MRPlan p;
+    return make_plan(n, &p);
+}
+
+hipError_t launch_rows_fwd_mr(const float* x, float2* y, int64_t nrows, int W, int my, int y_ld, float scale,
+                              hipStream_t s) {
+    MRPlan p;
+    if (!make_plan(W, &p) || my > W / 2 + 1) return hipErrorInvalidValue;
+    const float2* twn = nullptr;
+    hipError_t e = twiddles(W, &twn);
+    if (e != hipSuccess) return e;
+    const int P = kLdsElems / W;
+    const int64_t nb = ((nrows + 1) / 2 + P - 1) / P;
+    if (nb >= INT32_MAX) return hipErrorInvalidValue;
+    return launch_kernel(k_rows_fwd_mr, dim3((unsigned)blocks_for(nb)), dim3(kMrThreads), 0, s, x, y, nrows, my, y_ld,
+                         scale, p, twn);
+}
+
+hipError_t launch_cols_fwd_mr(const float2* r, float2* xh, int64_t nimg, int H, int mx, int my, float scale,
+                              hipStream_t s) {
+    MRPlan p;
+    if (!make_plan(H, &p) || 2 * mx > H) return hipErrorInvalidValue;
+    const float2* twn = nullptr;
+    hipError_t e = twiddles(H, &twn);
+    if (e != hipSuccess) return e;
+    const int cap = kLdsElems / H;
+    const int kb = cap < my ? cap : my;
+    const int nkb = (my + kb - 1) / kb;
+    const int64_t nb = nimg * nkb;
+    if (nb >= INT32_MAX) return hipErrorInvalidValue;
+    return launch_kernel(k_cols_fwd_mr, dim3((unsigned)nb), dim3(kMrThreads), 0, s, r, xh, mx, my, kb, nkb, scale, p,
+                         twn);
+}
+
+hipError_t launch_cols_inv_mr(const float2* yh, float2* r, int64_t nimg, int H, int mx, int my, hipStream_t s) {
+    MRPlan p;
+    if (!make_plan(H, &p) || 2 * mx > H) return hipErrorInvalidValue;
+    const float2* twn = nullptr;
+    hipError_t e = twiddles(H, &twn);
+    if (e != hipSuccess) return e;
+    const int cap = kLdsElems / H;
+    const int kb = cap < my ? cap : my;
+    const int nkb = (my + kb - 1) / kb;
+    const int64_t nb = nimg * nkb;
+    if (nb >= INT32_MAX) return hipErrorInvalidValue;
+    return launch_kernel(k_cols_inv_mr, dim3((unsigned)nb), dim3(kMrThreads), 0, s, yh, r, mx, my, kb, nkb, p, twn);
+}
+
+hipError_t launch_rows_inv_mr(const float2* y, float* out, int64_t nrows, int W, int my, int y_ld, float scale,
+                              hipStream_t s, const Epilogue& epi) {
+    MRPlan p;
+    if (!make_plan(W, &p) || my > W / 2 + 1) return hipErrorInvalidValue;
+    const float2* twn = nullptr;
+    hipError_t e = twiddles(W, &twn);
+    if (e != hipSuccess) return e;
+    const int P = kLdsElems / W;
+    const int64_t nb = ((nrows + 1) / 2 + P - 1) / P;
+    if (nb >= INT32_MAX) return hipErrorInvalidValue;
+    if (epi.on)
+        return launch_kernel(k_rows_inv_mr<true>, dim3((unsigned)blocks_for(nb)), dim3(kMrThreads), 0, s, y, out,
+                             nrows, my, y_ld, scale, p, twn, epi);
+    return launch_kernel(k_rows_inv_mr<false>, dim3((unsigned)blocks_for(nb)), dim3(kMrThreads), 0, s, y, out, nrows,
+                         my, y_ld, scale, p, twn, epi);
+}
+
+}  // namespace fno

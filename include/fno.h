@@ -32,8 +32,11 @@
  *   out  float32   [B][Cout][H][W]        (1D: [B][Cout][N])
  *   complex64 = interleaved (re, im) float32 pairs, as torch.complex64.
  *
- * Limits: 1 <= B, Cin, Cout; H and W powers of two with 2 <= H, W <= 4096
- * (1D: 2 <= N <= 4096); 1 <= mx, 2*mx <= H; 1 <= my <= W/2+1
+ * Limits: 1 <= B, Cin, Cout; H and W 7-smooth (2^a 3^b 5^c 7^d) with
+ * 2 <= H, W <= 4096 (1D: the same for N); 1 <= mx, 2*mx <= H;
+ * 1 <= my <= W/2+1 (floor).  Powers of two take the specialised kernels;
+ * other lengths take mixed-radix (4, 2, 3, 5, 7) stage kernels (the FFT
+ * blog, section 6.2, on non-power-of-two sizes).
  * (1D: 1 <= modes <= N/2+1).  x, w, out must be 16-byte aligned and x must
  * not overlap out.  `out` is fully overwritten.
  */
@@ -49,7 +52,7 @@ extern "C" {
 enum fno_status {
     FNO_OK = 0,
     FNO_ERR_NULL = -1,       /* a required pointer is NULL */
-    FNO_ERR_SHAPE = -2,      /* a size is out of range or not a power of two */
+    FNO_ERR_SHAPE = -2,      /* a size is out of range or has a prime factor above 7 */
     FNO_ERR_MODES = -3,      /* mx / my / modes out of range */
     FNO_ERR_ALIAS = -4,      /* x and out overlap */
     FNO_ERR_ALIGN = -5,      /* a pointer is not 16-byte aligned */
@@ -217,13 +220,13 @@ int fno_spectral_filter1d(const float* x, const void* mask, float* out,
  *
  * (x zero outside its H x W grid; y is (H+kh-1) x (W+kw-1)), and
  * out[b,o,h,w] = y[b,o,h+crop_h,w+crop_w] for h < Ho, w < Wo ("same" output:
- * crop (kh-1)/2, (kw-1)/2 and Ho = H, Wo = W).  H, W need not be powers of
- * two.  Both operands are zero-padded to PH x PW with
- * PH = fno_linear_conv_length(H, kh), PW = fno_linear_conv_length(W, kw) (the
- * smallest power of two >= 2 holding the full convolution, at most 4096;
- * 0 when out of range), where the circular convolution equals the linear
- * one, and the spectral convolution runs at full modes (mx = PH/2,
- * my = PW/2+1) with the weight spectrum
+ * crop (kh-1)/2, (kw-1)/2 and Ho = H, Wo = W).  H, W may be any size.  Both
+ * operands are zero-padded to PH x PW with PH = fno_linear_conv_length(H, kh),
+ * PW = fno_linear_conv_length(W, kw) (the smallest even 7-smooth length
+ * 2^a 3^b 5^c 7^d holding the full convolution, at most 4096; 0 when out of
+ * range), where the circular convolution equals the linear one, and the
+ * spectral convolution runs at full modes (mx = PH/2, my = PW/2+1) with the
+ * weight spectrum
  *
  *   wspec[s][r][ky][i][o] = sqrt(PH PW) * (ortho R2C of the padded k[o][i])
  *

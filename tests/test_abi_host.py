@@ -63,8 +63,8 @@ def conv2d(lib, x, w, out, *dims):
     ((0, 1, 1, 8, 8, 2, 2), SHAPE),
     ((1, 0, 1, 8, 8, 2, 2), SHAPE),
     ((1, 1, 0, 8, 8, 2, 2), SHAPE),
-    ((1, 1, 1, 12, 8, 2, 2), SHAPE),     # H not a power of two
-    ((1, 1, 1, 8, 6, 2, 2), SHAPE),      # W not a power of two
+    ((1, 1, 1, 22, 8, 2, 2), SHAPE),     # H has the prime factor 11
+    ((1, 1, 1, 8, 26, 2, 2), SHAPE),     # W has the prime factor 13
     ((1, 1, 1, 1, 8, 1, 2), SHAPE),      # H < 2
     ((1, 1, 1, 8192, 8, 2, 2), SHAPE),   # longer than the supported 4096
     ((1, 1, 1, 8, 8, 0, 2), MODES),
@@ -94,7 +94,7 @@ def test_conv2d_pointer_checks(lib):
 
 def test_conv1d_checks(lib):
     f = lib.fno_spectral_conv1d
-    assert f(A, B, C, 1, 1, 1, 12, 2, None) == SHAPE
+    assert f(A, B, C, 1, 1, 1, 22, 2, None) == SHAPE
     assert f(A, B, C, 1, 1, 1, 16, 0, None) == MODES
     assert f(A, B, C, 1, 1, 1, 16, 10, None) == MODES
     assert f(None, B, C, 1, 1, 1, 16, 9, None) == NULL
@@ -108,7 +108,7 @@ def test_ws_variant_checks(lib):
     assert lib.fno_spectral_conv2d_ws(A, B, C, *dims, None, need, None) == WORKSPACE
     assert lib.fno_spectral_conv2d_ws(A, B, C, *dims, 0x40000000, need - 1, None) == WORKSPACE
     assert lib.fno_spectral_conv2d_ws(A, B, C, *dims, 0x40000010, need, None) == ALIGN
-    assert fno.fno_workspace_size_2d(1, 1, 1, 12, 8, 2, 2) == 0
+    assert fno.fno_workspace_size_2d(1, 1, 1, 22, 8, 2, 2) == 0
     assert fno.fno_workspace_size_1d(1, 1, 1, 16, 10) == 0
 
 
@@ -118,7 +118,7 @@ def test_stage_call_checks(lib):
     assert lib.fno_inverse2d(A, B + 4, 1, 1, 8, 8, 2, 2, None) == ALIGN
     assert lib.fno_mix(A, B, C, 0, 1, 1, 1, None) == SHAPE
     assert lib.fno_mix(A, B, A, 1, 1, 1, 4, None) == ALIAS
-    assert lib.fno_forward1d(A, B, 1, 1, 6, 2, None) == SHAPE
+    assert lib.fno_forward1d(A, B, 1, 1, 22, 2, None) == SHAPE
     assert lib.fno_inverse1d(A, B, 1, 1, 8, 6, None) == MODES
 
 
@@ -143,14 +143,14 @@ def test_backward_checks(lib):
     D = 0x40000000
     assert f2(A, B, C, None, None, *dims, None) == NULL          # no gradient asked for
     assert f2(None, B, C, D, None, *dims, None) == NULL
-    assert f2(A, B, C, D, None, 2, 3, 4, 12, 16, 4, 4, None) == SHAPE
+    assert f2(A, B, C, D, None, 2, 3, 4, 22, 16, 4, 4, None) == SHAPE
     assert f2(A, B, C, D, None, 2, 3, 4, 16, 16, 9, 4, None) == MODES
     assert f2(A, B, C, D + 4, None, *dims, None) == ALIGN
     assert f2(A, B, C, A, None, *dims, None) == ALIAS              # grad_x on top of x
     assert f2(A, B, C, None, B, *dims, None) == ALIAS              # grad_w on top of w
     assert f2(A, B, C, D, D, *dims, None) == ALIAS                 # the two gradients overlap
     f1 = lib.fno_spectral_conv1d_backward
-    assert f1(A, B, C, D, None, 1, 1, 1, 12, 2, None) == SHAPE
+    assert f1(A, B, C, D, None, 1, 1, 1, 22, 2, None) == SHAPE
     assert f1(A, B, C, D, None, 1, 1, 1, 16, 10, None) == MODES
     assert f1(A, B, C, None, None, 1, 1, 1, 16, 4, None) == NULL
 
@@ -163,7 +163,7 @@ def test_gelu_epilogue_checks(lib):
     obytes = 2 * 4 * 16 * 16 * 4
     assert f2(A, B, None, None, None, *dims, 0, None) == NULL        # out is required
     assert f2(None, B, None, None, C, *dims, 0, None) == NULL
-    assert f2(A, B, None, None, C, 2, 3, 4, 12, 16, 4, 4, 0, None) == SHAPE
+    assert f2(A, B, None, None, C, 2, 3, 4, 22, 16, 4, 4, 0, None) == SHAPE
     assert f2(A, B, None, None, C, 2, 3, 4, 16, 16, 9, 4, 0, None) == MODES
     assert f2(A, B, None, None, C, *dims, 2, None) == SHAPE         # branch_after must be 0 or 1
     assert f2(A, B, D + 2, None, C, *dims, 0, None) == ALIGN        # bias needs 4-byte alignment
@@ -172,7 +172,7 @@ def test_gelu_epilogue_checks(lib):
     assert f2(A, B, None, C + obytes - 16, C, *dims, 1, None) == ALIAS   # branch overlaps out
     assert f2(A, B, None, C, C, *dims, 0, None) == ALIAS            # branch on top of out
     f1 = lib.fno_spectral_conv1d_gelu
-    assert f1(A, B, None, None, C, 1, 1, 1, 12, 2, 0, None) == SHAPE
+    assert f1(A, B, None, None, C, 1, 1, 1, 22, 2, 0, None) == SHAPE
     assert f1(A, B, None, None, C, 1, 1, 1, 16, 10, 0, None) == MODES
     assert f1(A, B, None, None, None, 1, 1, 1, 16, 4, 0, None) == NULL
     assert f1(A, B, None, None, C, 1, 1, 1, 16, 4, -1, None) == SHAPE
@@ -182,19 +182,20 @@ def test_filter_checks(lib):
     f2 = lib.fno_spectral_filter2d
     assert f2(None, B, C, 2, 3, 16, 16, 4, 4, None) == NULL
     assert f2(A, None, C, 2, 3, 16, 16, 4, 4, None) == NULL
-    assert f2(A, B, C, 2, 3, 12, 16, 4, 4, None) == SHAPE
+    assert f2(A, B, C, 2, 3, 22, 16, 4, 4, None) == SHAPE
     assert f2(A, B, C, 2, 3, 16, 16, 9, 4, None) == MODES
     assert f2(A, B + 8, C, 2, 3, 16, 16, 4, 4, None) == ALIGN
     assert f2(A, B, A, 2, 3, 16, 16, 4, 4, None) == ALIAS          # out on top of x
     assert f2(A, B, B, 2, 3, 16, 16, 4, 4, None) == ALIAS          # out on top of the mask
     f1 = lib.fno_spectral_filter1d
-    assert f1(A, B, C, 1, 1, 12, 2, None) == SHAPE
+    assert f1(A, B, C, 1, 1, 22, 2, None) == SHAPE
     assert f1(A, B, C, 1, 1, 16, 10, None) == MODES
     assert f1(None, B, C, 1, 1, 16, 4, None) == NULL
 
 
 def test_linear_conv_checks(lib):
-    assert lib.fno_linear_conv_length(100, 5) == 128
+    assert lib.fno_linear_conv_length(100, 5) == 108          # 2^2 3^3
+    assert lib.fno_linear_conv_length(128, 5) == 140          # 2^2 5 7
     assert lib.fno_linear_conv_length(128, 1) == 128
     assert lib.fno_linear_conv_length(1, 1) == 2
     assert lib.fno_linear_conv_length(4096, 2) == 0           # beyond 4096

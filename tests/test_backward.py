@@ -77,6 +77,8 @@ BACKWARD_2D = [
     (1, 2, 2, 1024, 16, 8, 9),      # pruned columns
     (9, 16, 24, 64, 64, 8, 8),      # weight-gradient tiles of 16 x 32 channels; adjoint mix, ragged channel chunk
     (12, 18, 21, 32, 32, 8, 8),     # odd Cout: explicit weight adjoint, then the plain matrix-core mix
+    (3, 4, 5, 45, 63, 10, 20),      # mixed-radix odd lengths (no Nyquist column in the weight gradient)
+    (2, 4, 4, 96, 100, 12, 16),     # mixed-radix even lengths
 ]
 
 
@@ -93,6 +95,7 @@ BACKWARD_1D = [
     (2, 16, 32, 4096, 64),          # longest rows, matrix-core mix both ways
     (37, 20, 40, 256, 13),          # weight gradient: batch split in two, odd chunk counts, modes not a multiple of 8
     (300, 8, 8, 128, 16),           # weight gradient: 19 uneven batch splits, ragged last chunk
+    (4, 3, 2, 1215, 40),            # mixed-radix odd length (3^5 5)
 ]
 
 

@@ -75,6 +75,7 @@ FILTER_2D = [
     (1, 3, 256, 256, 9, 11),        # staged generic transforms
     (1, 2, 16, 1024, 5, 50),        # pruned long rows
     (1, 2, 1024, 16, 8, 9),         # pruned columns
+    (2, 3, 60, 35, 12, 10),         # mixed-radix lengths
 ]
 
 

@@ -74,6 +74,7 @@ GELU_2D = [
     (1, 2, 3, 256, 256, 9, 11),       # staged: generic rows
     (1, 2, 3, 16, 1024, 5, 50),       # staged: pruned long rows
     (1, 2, 2, 1024, 16, 8, 9),        # staged: pruned columns, generic rows
+    (2, 3, 4, 45, 100, 10, 20),       # mixed-radix rows and columns
 ]
 
 

@@ -204,6 +204,47 @@ def test_edge_shapes_1d(shape, variant):
     assert_close(out, ref_out(cfg, x, w), f"edge1d {shape} {variant}")
 
 
+# lengths with prime factors 3, 5, 7 (mixed-radix stage kernels)
+MIXED_2D = [
+    # B, Cin, Cout, H, W, mx, my
+    (2, 3, 4, 96, 96, 12, 12),      # 2^5 3
+    (2, 4, 4, 100, 100, 16, 16),    # 2^2 5^2
+    (1, 2, 3, 45, 63, 10, 20),      # odd lengths: no Nyquist column
+    (2, 2, 2, 7, 5, 3, 3),          # prime lengths, every mode kept
+    (1, 1, 2, 2187, 10, 20, 6),     # 3^7-row columns
+    (1, 2, 2, 48, 1000, 24, 501),   # every mode of a 2^3 5^3 row kept
+    (16, 16, 32, 120, 120, 16, 16), # matrix-core mix between mixed-radix transforms
+]
+
+
+@pytest.mark.parametrize("shape", MIXED_2D, ids=lambda s: "x".join(map(str, s)))
+def test_mixed_radix_shapes_2d(shape):
+    b, cin, cout, h, wd, mx, my = shape
+    cfg = Config("mixed", "2d", b, cin, cout, h, wd, mx, my, "uniform")
+    x, w = make_inputs(cfg, 13)
+    out = run(cfg, x, w, "fused")
+    assert_close(out, ref_out(cfg, x, w), f"mixed {shape}")
+
+
+MIXED_1D = [
+    # B, Cin, Cout, N, modes
+    (3, 2, 3, 1000, 64),            # 2^3 5^3
+    (2, 2, 2, 3125, 100),           # 5^5
+    (2, 2, 2, 2401, 50),            # 7^4
+    (4, 3, 3, 15, 8),               # odd length, every bin kept
+    (8, 16, 16, 3072, 64),          # 2^10 3, matrix-core mix
+]
+
+
+@pytest.mark.parametrize("shape", MIXED_1D, ids=lambda s: "x".join(map(str, s)))
+def test_mixed_radix_shapes_1d(shape):
+    b, cin, cout, n, modes = shape
+    cfg = Config("mixed1d", "1d", b, cin, cout, 1, n, 1, modes, "normal")
+    x, w = make_inputs(cfg, 14)
+    out = run(cfg, x, w, "fused")
+    assert_close(out, ref_out(cfg, x, w), f"mixed1d {shape}")
+
+
 def test_identity_full_modes_reproduces_input():
     rng = np.random.default_rng(5)
     b, c, h, wd = 2, 3, 32, 16
@@ -254,7 +295,7 @@ def test_out_is_overwritten():
 
 
 def test_bad_arguments_raise():
-    x = torch.zeros((1, 2, 8, 12), device=DEV)          # W not a power of two
+    x = torch.zeros((1, 2, 8, 22), device=DEV)          # W has the prime factor 11
     w = torch.zeros((2, 2, 2, 2, 2), dtype=torch.complex64, device=DEV)
     with pytest.raises(fno.FnoError) as ei:
         fno.fno_spectral_conv2d(x, w, 2, 2)
