@@ -330,6 +330,10 @@ def main():
         kd = torch.from_numpy(k_np).to(dev)
         compulsory = cfg.compulsory_bytes - int(w_np.nbytes) + int(k_np.nbytes)
         linconv_np = k_np
+        lens = ([fno.fno_linear_conv_length(cfg.W, 7)] if cfg.kind == "1d"
+                else [fno.fno_linear_conv_length(cfg.H, 5), fno.fno_linear_conv_length(cfg.W, 5)])
+        if 0 in lens:
+            sys.exit(f"--pass linconv: the padded length of workload {cfg.name} exceeds the 4096-point transform")
         if cfg.kind == "1d":
             wspec = fno.fno_linear_conv1d_prepare(kd, cfg.W)
             step = lambda i: fno.fno_linear_conv1d(xs[i % nsets], kd, wspec=wspec, out=outs[i % nsets])

@@ -864,3 +864,38 @@ def test_linear_conv_through_padded_spectral_conv():
     # planted mistake: without the sqrt(PH PW) factor the result is off
     y_bad = S.spectral_conv2d_ref(xp, wt / math.sqrt(ph * pw), mx, my)
     assert np.max(np.abs(y_bad[:, :, :h + kh - 1, :w + kw - 1] - ref)) > 0.1
+
+
+# --------------------------------------------------------------------------
+# Lengths that are not powers of two (the definition holds for any length)
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("n", [3, 5, 6, 7, 12, 15, 45, 100])
+def test_dft_brute_vs_numpy_fft_any_length(n):
+    a = np.random.default_rng(80 + n).standard_normal((2, n)) + 1j * np.random.default_rng(90 + n).standard_normal((2, n))
+    assert rel(S.dft_brute(a, sign=-1), np.fft.fft(a, axis=-1)) < 1e-13
+    assert rel(S.dft_brute(a, sign=+1), np.fft.ifft(a, axis=-1) * n) < 1e-13
+
+
+@pytest.mark.parametrize("h,w", [(6, 10), (6, 9), (12, 15)])
+def test_convolution_theorem_full_modes_any_length(h, w):
+    # even H (every kx kept by 2 mx = H); W odd or even (the half spectrum
+    # W//2 + 1 has no Nyquist bin when W is odd)
+    rng = np.random.default_rng(81)
+    b_n, cin, cout = 2, 2, 3
+    x = rng.uniform(-1, 1, (b_n, cin, h, w))
+    k = rng.standard_normal((cin, cout, h, w))
+    mx, my = h // 2, w // 2 + 1
+    spec = np.fft.rfft2(k, axes=(-2, -1))
+    kx = np.concatenate([np.arange(mx), h - mx + np.arange(mx)])
+    wt = np.transpose(spec[:, :, kx, :my], (2, 3, 0, 1)).reshape(2, mx, my, cin, cout)
+    out = S.spectral_conv2d_ref(x, wt, mx, my)
+    np.testing.assert_allclose(out, circular_conv2d_direct(x, k), atol=1e-11)
+
+
+@pytest.mark.parametrize("n", [9, 15, 20])
+def test_identity_full_modes_1d_any_length(n):
+    rng = np.random.default_rng(82)
+    x = rng.standard_normal((2, 3, n))
+    wt = np.broadcast_to(np.eye(3, dtype=np.complex128), (n // 2 + 1, 3, 3)).copy()
+    assert rel(S.spectral_conv1d_ref(x, wt, n // 2 + 1), x) < 1e-12
