@@ -18,7 +18,7 @@
 namespace fno {
 namespace {
 
-constexpr int kMrThreads = 256;
+constexpr int kMrThreads = 1024;   // 16 waves; the 64 KiB of LDS allow two workgroups per CU
 constexpr int kMrMaxPasses = 12;
 
 struct MRPlan {
