@@ -53,24 +53,6 @@ from fft_spectral_convolution_amd.inputs import CONFIGS, make_inputs  # noqa: E4
 
 # Algorithmic bytes each kernel must move per launch (read once + write once),
 # by kernel name (per-unit figures: x, W, out and the truncated spectra).
-def _padded(cfg) -> int:
-    """Pixels of one padded image of the linear-convolution pass (5x5 / 7-tap kernel)."""
-    def p2(n):
-        # the library's padded length: the smallest even 7-smooth length >= n
-        m = max(2, n)
-        while True:
-            r = m
-            for f in (2, 3, 5, 7):
-                while r % f == 0:
-                    r //= f
-            if m % 2 == 0 and r == 1:
-                return m
-            m += 1
-    if cfg.kind == "1d":
-        return p2(cfg.W + 6)
-    return p2(cfg.H + 4) * p2(cfg.W + 4)
-
-
 def kernel_bytes(name: str, cfg, backward: bool = False) -> int:
     """Bytes of kernel `name` (a repeat launch carries ":n").  In the backward
     pass the first transform runs on dL/dout (Cout channels) and the inverse
@@ -116,9 +98,6 @@ def kernel_bytes(name: str, cfg, backward: bool = False) -> int:
         "rows_inv_gelu": (r_out if cfg.kind == "2d" else yh) + 2 * n_out,
         # diagonal filter: both truncated spectra and the (mode, channel) mask
         "mix_diag": xh + yh + (m_modes * cfg.Cin * c8),
-        # linear convolution: zero-padding copy and crop
-        "pad": n_in + cfg.B * cfg.Cin * _padded(cfg) * 4,
-        "crop": cfg.B * cfg.Cout * _padded(cfg) * 4 + n_out,
         "wgrad": xh + yh + wb,
         "wadjoint": 2 * wb,
         # sum of the batch splits' partial weight gradients (when the batch
@@ -392,7 +371,16 @@ def main():
     spans_us = [evs[i][0].elapsed_time(evs[i][2 * nk - 1]) * 1e3 for i in range(args.steps)]
     dom = int(np.argmax(per_kernel_ms))
     dom_name = kernels[dom]
-    dom_bytes = kernel_bytes(dom_name, cfg, args.which == "backward")
+    # the linear convolution runs on the padded grid at full modes: its kernels'
+    # bytes are those of that grid (rows counted at the padded length)
+    kcfg = cfg
+    if args.which == "linconv":
+        import dataclasses
+        if cfg.kind == "1d":
+            kcfg = dataclasses.replace(cfg, W=lens[0], my=lens[0] // 2 + 1)
+        else:
+            kcfg = dataclasses.replace(cfg, H=lens[0], W=lens[1], mx=lens[0] // 2, my=lens[1] // 2 + 1)
+    dom_bytes = kernel_bytes(dom_name, kcfg, args.which == "backward")
     achieved = dom_bytes / (per_kernel_ms[dom] * 1e-3) / 1e9
     traffic = load_traffic(dom_name, cfg.name if args.which == "forward" else f"{cfg.name}/{args.which}")
 
@@ -452,7 +440,7 @@ def main():
         # the 3M form (three real GEMMs, 2 flops per multiply-add), and the
         # algorithmic count of 8 flops per complex multiply-add
         k = kernels.index("mix_mfma")
-        macs = cfg.B * cfg.Cin * cfg.Cout * (cfg.my if cfg.kind == "1d" else 2 * cfg.mx * cfg.my)
+        macs = kcfg.B * kcfg.Cin * kcfg.Cout * (kcfg.my if kcfg.kind == "1d" else 2 * kcfg.mx * kcfg.my)
         t = per_kernel_ms[k] * 1e-3
         line["mix"] = {
             "kernel": "mix_mfma",
@@ -463,7 +451,7 @@ def main():
             "frac": round(6.0 * macs / t / 1e12 / MFMA_FP32_PEAK_TFLOPS, 5),
             "flops_executed_3m": 6 * macs,
             "flops_complex_8": 8 * macs,
-            "hbm_gbs": round(kernel_bytes("mix_mfma", cfg) / t / 1e9, 3),
+            "hbm_gbs": round(kernel_bytes("mix_mfma", kcfg) / t / 1e9, 3),
             "avg_launch_us": round(per_kernel_ms[k] * 1e3, 3),
         }
     if not args.no_cpu_baseline:

@@ -539,38 +539,54 @@ int linconv2d_prepare(const float* k, void* wspec, int Cin, int Cout, int H, int
     return rec_end(hs, run());
 }
 
+// The transforms run on the mixed-radix stage kernels for every padded
+// length: their row kernels read the unpadded input (the padding reads as
+// zero) and write only the crop window, so no padded copy of x or of the
+// output is made.
 int linconv2d_run(const float* x, const void* wspec, float* out, int B, int Cin, int Cout, int H, int W, int kh,
                   int kw, int ch, int cw, int Ho, int Wo, void* stream) {
     const int PH = linconv_len(H, kh), PW = linconv_len(W, kw);
     if (!PH || !PW || B < 1 || Cin < 1 || Cout < 1) return FNO_ERR_SHAPE;
     if (ch < 0 || cw < 0 || Ho < 1 || Wo < 1 || ch + Ho > H + kh - 1 || cw + Wo > W + kw - 1) return FNO_ERR_SHAPE;
     const int mx = PH / 2, my = PW / 2 + 1;
+    const int64_t m = (int64_t)PH * my;
     const size_t xbytes = (size_t)B * Cin * H * W * sizeof(float);
-    const size_t wbytes = (size_t)PH * my * Cin * Cout * sizeof(float2);
+    const size_t wbytes = (size_t)m * Cin * Cout * sizeof(float2);
     const size_t obytes = (size_t)B * Cout * Ho * Wo * sizeof(float);
     int rc = check_conv(x, wspec, out, xbytes, wbytes, obytes);
     if (rc) return rc;
-    const Shape2d s = make2d(B, Cin, Cout, PH, PW, mx, my);
-    const size_t xp_b = align_up((size_t)B * Cin * PH * PW * sizeof(float));
-    const size_t yp_b = align_up((size_t)B * Cout * PH * PW * sizeof(float));
+    const int64_t cmax = Cin > Cout ? Cin : Cout;
+    const size_t r_b = align_up((size_t)B * cmax * PH * my * sizeof(float2));
+    const size_t x_b = align_up((size_t)B * Cin * m * sizeof(float2));
+    const size_t y_b = align_up((size_t)B * Cout * m * sizeof(float2));
     DeviceState* st = nullptr;
     rc = device_state(&st);
     if (rc) return rc;
     void* ws = nullptr;
-    rc = internal_workspace(st, xp_b + yp_b + best_ws_2d(s), &ws);
+    rc = internal_workspace(st, r_b + x_b + y_b, &ws);
     if (rc) return rc;
-    float* xp = static_cast<float*>(ws);
-    float* yp = reinterpret_cast<float*>(static_cast<char*>(ws) + xp_b);
-    void* cws = static_cast<char*>(ws) + xp_b + yp_b;
+    float2* r = static_cast<float2*>(ws);
+    float2* xh = reinterpret_cast<float2*>(static_cast<char*>(ws) + r_b);
+    float2* yh = reinterpret_cast<float2*>(static_cast<char*>(ws) + r_b + x_b);
+    const float scale = (float)(1.0 / std::sqrt((double)PH * (double)PW));
     hipStream_t hs = static_cast<hipStream_t>(stream);
     auto run = [&]() -> int {
-        rec_kernel("pad", hs);
-        hipError_t e = launch_pad2d(x, xp, (int64_t)B * Cin, H, W, PH, PW, hs);
+        const RowWindow in_win{PH, H, W, 0, 0};
+        rec_kernel("rows_fwd", hs);
+        hipError_t e = launch_rows_fwd_mr(x, r, (int64_t)B * Cin * PH, PW, my, my, 1.0f, hs, &in_win);
         if (e != hipSuccess) return hip_fail(e);
-        const int crc = run_best_2d(s, xp, static_cast<const float2*>(wspec), yp, cws, st->twiddle, hs);
-        if (crc) return crc;
-        rec_kernel("crop", hs);
-        e = launch_crop2d(yp, out, (int64_t)B * Cout, PH, PW, ch, cw, Ho, Wo, hs);
+        rec_kernel("cols_fwd", hs);
+        e = launch_cols_fwd_mr(r, xh, (int64_t)B * Cin, PH, mx, my, scale, hs);
+        if (e != hipSuccess) return hip_fail(e);
+        const int mrc = run_mix(xh, canonical_layout(Cin, m), static_cast<const float2*>(wspec), yh,
+                                canonical_layout(Cout, m), B, Cin, Cout, m, hs);
+        if (mrc) return mrc;
+        rec_kernel("cols_inv", hs);
+        e = launch_cols_inv_mr(yh, r, (int64_t)B * Cout, PH, mx, my, hs);
+        if (e != hipSuccess) return hip_fail(e);
+        const RowWindow out_win{PH, Ho, Wo, ch, cw};
+        rec_kernel("rows_inv", hs);
+        e = launch_rows_inv_mr(r, out, (int64_t)B * Cout * PH, PW, my, my, scale, hs, Epilogue{}, &out_win);
         return e == hipSuccess ? FNO_OK : hip_fail(e);
     };
     rec_begin();
@@ -622,27 +638,29 @@ int linconv1d_run(const float* x, const void* wspec, float* out, int B, int Cin,
     const size_t obytes = (size_t)B * Cout * No * sizeof(float);
     int rc = check_conv(x, wspec, out, xbytes, wbytes, obytes);
     if (rc) return rc;
-    const size_t xp_b = align_up((size_t)B * Cin * PN * sizeof(float));
-    const size_t yp_b = align_up((size_t)B * Cout * PN * sizeof(float));
+    const size_t x_b = align_up((size_t)B * Cin * modes * sizeof(float2));
+    const size_t y_b = align_up((size_t)B * Cout * modes * sizeof(float2));
     DeviceState* st = nullptr;
     rc = device_state(&st);
     if (rc) return rc;
     void* ws = nullptr;
-    rc = internal_workspace(st, xp_b + yp_b + unfused_ws_1d(B, Cin, Cout, modes), &ws);
+    rc = internal_workspace(st, x_b + y_b, &ws);
     if (rc) return rc;
-    float* xp = static_cast<float*>(ws);
-    float* yp = reinterpret_cast<float*>(static_cast<char*>(ws) + xp_b);
-    void* cws = static_cast<char*>(ws) + xp_b + yp_b;
+    float2* xh = static_cast<float2*>(ws);
+    float2* yh = reinterpret_cast<float2*>(static_cast<char*>(ws) + x_b);
+    const float scale = (float)(1.0 / std::sqrt((double)PN));
     hipStream_t hs = static_cast<hipStream_t>(stream);
     auto run = [&]() -> int {
-        rec_kernel("pad", hs);
-        hipError_t e = launch_pad2d(x, xp, (int64_t)B * Cin, 1, N, 1, PN, hs);
+        const RowWindow in_win{1, 1, N, 0, 0};
+        rec_kernel("rows_fwd", hs);
+        hipError_t e = launch_rows_fwd_mr(x, xh, (int64_t)B * Cin, PN, modes, modes, scale, hs, &in_win);
         if (e != hipSuccess) return hip_fail(e);
-        const int crc = run_unfused_1d(B, Cin, Cout, PN, modes, xp, static_cast<const float2*>(wspec), yp, cws,
-                                       st->twiddle, hs);
-        if (crc) return crc;
-        rec_kernel("crop", hs);
-        e = launch_crop2d(yp, out, (int64_t)B * Cout, 1, PN, 0, crop, 1, No, hs);
+        const int mrc = run_mix(xh, canonical_layout(Cin, modes), static_cast<const float2*>(wspec), yh,
+                                canonical_layout(Cout, modes), B, Cin, Cout, modes, hs);
+        if (mrc) return mrc;
+        const RowWindow out_win{1, 1, No, 0, crop};
+        rec_kernel("rows_inv", hs);
+        e = launch_rows_inv_mr(yh, out, (int64_t)B * Cout, PN, modes, modes, scale, hs, Epilogue{}, &out_win);
         return e == hipSuccess ? FNO_OK : hip_fail(e);
     };
     rec_begin();

@@ -195,21 +195,25 @@ hipError_t launch_mix_diag(const float2* xh, float2* yh, const SpecLayout& lay, 
 // ---- mixed-radix stage kernels (fno_mixed.hip) -----------------------------
 // Same contracts as launch_rows_fwd / launch_cols_fwd / launch_cols_inv /
 // launch_rows_inv, for 7-smooth lengths 2..4096 given as lengths (W, H).
+// A RowWindow makes the rows those of images of ph rows of which only a
+// window is stored: forward, x holds each image's top-left h x w corner
+// (the rest reads as zero); inverse, only rows [h0, h0+h) x columns
+// [w0, w0+w) are written, packed (no epilogue with a window).
+struct RowWindow {
+    int ph, h, w, h0, w0;
+};
 bool mixed_supported(int n);
 hipError_t launch_rows_fwd_mr(const float* x, float2* y, int64_t nrows, int W, int my, int y_ld, float scale,
-                              hipStream_t s);
+                              hipStream_t s, const RowWindow* window = nullptr);
 hipError_t launch_cols_fwd_mr(const float2* r, float2* xh, int64_t nimg, int H, int mx, int my, float scale,
                               hipStream_t s);
 hipError_t launch_cols_inv_mr(const float2* yh, float2* r, int64_t nimg, int H, int mx, int my, hipStream_t s);
 hipError_t launch_rows_inv_mr(const float2* y, float* out, int64_t nrows, int W, int my, int y_ld, float scale,
-                              hipStream_t s, const Epilogue& epi = Epilogue{});
+                              hipStream_t s, const Epilogue& epi = Epilogue{}, const RowWindow* window = nullptr);
 
 // ---- zero-padded linear convolution helpers (fno_linconv.hip) ---------------
 // dst[img][PH][PW] = src[img][H][W] zero-padded (bottom and right).
 hipError_t launch_pad2d(const float* src, float* dst, int64_t nimg, int H, int W, int PH, int PW, hipStream_t s);
-// dst[img][Ho][Wo] = src[img][PH][PW] from row ch, column cw.
-hipError_t launch_crop2d(const float* src, float* dst, int64_t nimg, int PH, int PW, int ch, int cw, int Ho, int Wo,
-                         hipStream_t s);
 // w[m][i][o] = scale * kh[o Cin + i][m] (kh canonical spectra of the kernels).
 hipError_t launch_spec_to_weight(const float2* kh, float2* w, int64_t M, int64_t Cin, int64_t Cout, float scale,
                                  hipStream_t s);

@@ -1,8 +1,9 @@
 // Helpers of the zero-padded linear convolution (the FFT blog, sections
 // 2.1 and 5.1-5.2: pad input and kernel, R2C, pointwise product, C2R,
 // crop).  The transforms and the per-frequency channel product are the
-// spectral convolution's own kernels at full modes; this file adds the
-// zero-padding copy, the crop and the weight spectrum's layout change.
+// spectral convolution's own kernels at full modes (the row kernels pad the
+// input and crop the output themselves); this file adds the zero-padding
+// copy of the kernels and the weight spectrum's layout change.
 #include "fno_device.hpp"
 #include "fno_internal.hpp"
 
@@ -27,19 +28,6 @@ __global__ __launch_bounds__(kLcThreads) void k_pad2d(const float* __restrict__ 
         const int p = (int)(r % PH);
         const int64_t img = r / PH;
         dst[e] = (p < H && q < W) ? src[(img * H + p) * W + q] : 0.0f;
-    }
-}
-
-// dst[img][h][w] = src[img][h + ch][w + cw] (src PH x PW, dst Ho x Wo)
-__global__ __launch_bounds__(kLcThreads) void k_crop2d(const float* __restrict__ src, float* __restrict__ dst,
-                                                       int64_t n, int PH, int PW, int ch, int cw, int Ho, int Wo) {
-    const int64_t stride = (int64_t)gridDim.x * kLcThreads;
-    for (int64_t e = (int64_t)blockIdx.x * kLcThreads + threadIdx.x; e < n; e += stride) {
-        const int w = (int)(e % Wo);
-        const int64_t r = e / Wo;
-        const int h = (int)(r % Ho);
-        const int64_t img = r / Ho;
-        dst[e] = src[(img * PH + h + ch) * PW + w + cw];
     }
 }
 
@@ -75,13 +63,6 @@ __global__ __launch_bounds__(kLcThreads) void k_spec_to_weight(const float2* __r
 hipError_t launch_pad2d(const float* src, float* dst, int64_t nimg, int H, int W, int PH, int PW, hipStream_t s) {
     const int64_t n = nimg * PH * PW;
     return launch_kernel(k_pad2d, dim3((unsigned)grid_for(n)), dim3(kLcThreads), 0, s, src, dst, n, H, W, PH, PW);
-}
-
-hipError_t launch_crop2d(const float* src, float* dst, int64_t nimg, int PH, int PW, int ch, int cw, int Ho, int Wo,
-                         hipStream_t s) {
-    const int64_t n = nimg * Ho * Wo;
-    return launch_kernel(k_crop2d, dim3((unsigned)grid_for(n)), dim3(kLcThreads), 0, s, src, dst, n, PH, PW, ch, cw,
-                         Ho, Wo);
 }
 
 hipError_t launch_spec_to_weight(const float2* kh, float2* w, int64_t M, int64_t Cin, int64_t Cout, float scale,

@@ -108,10 +108,13 @@ __device__ float2* fft_rows_mr(float2* a, float2* b, int nrows, const MRPlan& p,
 }
 
 // rows of length W = p.n (real) -> bins ky < my, two rows per complex
-// transform (z = a + i b, A[k] = (Z[k] + conj Z[-k]) / 2, B[k] = (Z[k] - conj Z[-k]) / 2i)
+// transform (z = a + i b, A[k] = (Z[k] + conj Z[-k]) / 2, B[k] = (Z[k] - conj Z[-k]) / 2i).
+// win: the rows are those of images of win.ph rows, and x holds only each
+// image's top-left win.h x win.w corner (the rest reads as zero: the
+// zero padding of a linear convolution).
 __global__ __launch_bounds__(kMrThreads) void k_rows_fwd_mr(const float* __restrict__ x, float2* __restrict__ y,
                                                             int64_t nrows, int my, int y_ld, float scale, MRPlan p,
-                                                            const float2* __restrict__ twn) {
+                                                            const float2* __restrict__ twn, RowWindow win) {
     __shared__ float2 buf[2][kLdsElems];
     const int W = p.n;
     const int P = kLdsElems / W;
@@ -119,13 +122,20 @@ __global__ __launch_bounds__(kMrThreads) void k_rows_fwd_mr(const float* __restr
     const int64_t npairs = (nrows + 1) / 2;
     const int64_t pair0 = (int64_t)blockIdx.x * P;
     const int prows = (int)(npairs - pair0 < P ? npairs - pair0 : P);
+    // sample n of row r: x's element when inside the window, else zero
+    // (row indices fit 32 bits when a window is used: checked on the host)
+    auto sample = [&](int64_t r, int n) -> float {
+        if (r >= nrows) return 0.0f;
+        if (win.w == W && win.h == win.ph) return x[r * W + n];
+        const uint32_t img = (uint32_t)r / (uint32_t)win.ph;
+        const int q = (int)((uint32_t)r - img * (uint32_t)win.ph);
+        return (q < win.h && n < win.w) ? x[((int64_t)img * win.h + q) * win.w + n] : 0.0f;
+    };
     for (int e = tid; e < prows * W; e += kMrThreads) {
         const int pr = e / W;
         const int n = e - pr * W;
         const int64_t ra = 2 * (pair0 + pr);
-        const float a = x[ra * W + n];
-        const float b = (ra + 1 < nrows) ? x[(ra + 1) * W + n] : 0.0f;
-        buf[0][e] = make_float2(a, b);
+        buf[0][e] = make_float2(sample(ra, n), sample(ra + 1, n));
     }
     __syncthreads();
     const float2* res = fft_rows_mr<-1>(buf[0], buf[1], prows, p, twn, tid, kMrThreads);
@@ -203,11 +213,14 @@ __global__ __launch_bounds__(kMrThreads) void k_cols_inv_mr(const float2* __rest
 
 // R'[nrows][y_ld] (bins ky < my) -> C2R rows of length W = p.n, times scale
 // (imaginary parts of the DC bin, and of the Nyquist bin when W is even,
-// dropped); EPI: the fused output epilogue on every output
+// dropped); EPI: the fused output epilogue on every output.  win: only the
+// window of rows [h0, h0 + h) x columns [w0, w0 + w) of each image of
+// win.ph rows is written, packed (the crop of a linear convolution).
 template <bool EPI>
 __global__ __launch_bounds__(kMrThreads) void k_rows_inv_mr(const float2* __restrict__ y, float* __restrict__ out,
                                                             int64_t nrows, int my, int y_ld, float scale, MRPlan p,
-                                                            const float2* __restrict__ twn, Epilogue epi) {
+                                                            const float2* __restrict__ twn, Epilogue epi,
+                                                            RowWindow win) {
     __shared__ float2 buf[2][kLdsElems];
     const int W = p.n;
     const int P = kLdsElems / W;
@@ -237,6 +250,19 @@ __global__ __launch_bounds__(kMrThreads) void k_rows_inv_mr(const float2* __rest
         const int n = e - pr * W;
         const int64_t ra = 2 * (pair0 + pr);
         const float2 z = res[e];
+        if (!(win.w == W && win.h == win.ph)) {
+            // crop: rows ra and ra + 1 may fall in different images
+            if (n < win.w0 || n >= win.w0 + win.w) continue;
+            for (int s2 = 0; s2 < 2; ++s2) {
+                const int64_t r = ra + s2;
+                if (r >= nrows) break;
+                const uint32_t img = (uint32_t)r / (uint32_t)win.ph;
+                const int q = (int)((uint32_t)r - img * (uint32_t)win.ph) - win.h0;
+                if (q >= 0 && q < win.h)
+                    out[((int64_t)img * win.h + q) * win.w + n - win.w0] = (s2 ? z.y : z.x) * scale;
+            }
+            continue;
+        }
         if constexpr (EPI) {
             const __amdgpu_buffer_rsrc_t rb =
                 make_rsrc(epi.branch ? epi.branch + 2 * pair0 * W : nullptr,
@@ -310,7 +336,7 @@ bool mixed_supported(int n) {
 }
 
 hipError_t launch_rows_fwd_mr(const float* x, float2* y, int64_t nrows, int W, int my, int y_ld, float scale,
-                              hipStream_t s) {
+                              hipStream_t s, const RowWindow* window) {
     MRPlan p;
     if (!make_plan(W, &p) || my > W / 2 + 1) return hipErrorInvalidValue;
     const float2* twn = nullptr;
@@ -319,8 +345,12 @@ hipError_t launch_rows_fwd_mr(const float* x, float2* y, int64_t nrows, int W, i
     const int P = kLdsElems / W;
     const int64_t nb = ((nrows + 1) / 2 + P - 1) / P;
     if (nb >= INT32_MAX) return hipErrorInvalidValue;
+    const RowWindow win = window ? *window : RowWindow{1, 1, W, 0, 0};
+    if (win.ph < 1 || win.h < 1 || win.h > win.ph || win.w < 1 || win.w > W || nrows % win.ph ||
+        (window && nrows >= INT32_MAX))
+        return hipErrorInvalidValue;
     return launch_kernel(k_rows_fwd_mr, dim3((unsigned)blocks_for(nb)), dim3(kMrThreads), 0, s, x, y, nrows, my, y_ld,
-                         scale, p, twn);
+                         scale, p, twn, win);
 }
 
 hipError_t launch_cols_fwd_mr(const float2* r, float2* xh, int64_t nimg, int H, int mx, int my, float scale,
@@ -354,7 +384,7 @@ hipError_t launch_cols_inv_mr(const float2* yh, float2* r, int64_t nimg, int H, 
 }
 
 hipError_t launch_rows_inv_mr(const float2* y, float* out, int64_t nrows, int W, int my, int y_ld, float scale,
-                              hipStream_t s, const Epilogue& epi) {
+                              hipStream_t s, const Epilogue& epi, const RowWindow* window) {
     MRPlan p;
     if (!make_plan(W, &p) || my > W / 2 + 1) return hipErrorInvalidValue;
     const float2* twn = nullptr;
@@ -363,11 +393,15 @@ hipError_t launch_rows_inv_mr(const float2* y, float* out, int64_t nrows, int W,
     const int P = kLdsElems / W;
     const int64_t nb = ((nrows + 1) / 2 + P - 1) / P;
     if (nb >= INT32_MAX) return hipErrorInvalidValue;
+    const RowWindow win = window ? *window : RowWindow{1, 1, W, 0, 0};
+    if (win.ph < 1 || win.h < 1 || win.h0 < 0 || win.h0 + win.h > win.ph || win.w < 1 || win.w0 < 0 ||
+        win.w0 + win.w > W || nrows % win.ph || (window && (epi.on || nrows >= INT32_MAX)))
+        return hipErrorInvalidValue;
     if (epi.on)
         return launch_kernel(k_rows_inv_mr<true>, dim3((unsigned)blocks_for(nb)), dim3(kMrThreads), 0, s, y, out,
-                             nrows, my, y_ld, scale, p, twn, epi);
+                             nrows, my, y_ld, scale, p, twn, epi, win);
     return launch_kernel(k_rows_inv_mr<false>, dim3((unsigned)blocks_for(nb)), dim3(kMrThreads), 0, s, y, out, nrows,
-                         my, y_ld, scale, p, twn, epi);
+                         my, y_ld, scale, p, twn, epi, win);
 }
 
 }  // namespace fno

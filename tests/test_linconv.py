@@ -64,7 +64,7 @@ def test_linear_conv2d(case):
     out = fno.fno_linear_conv2d(dev(x), dev(k), crop=(ch, cw), out_size=(ho, wo))
     torch.cuda.synchronize()
     kernels = fno.fno_last_kernels()
-    assert kernels[0] == "pad" and kernels[-1] == "crop"
+    assert kernels[0] == "rows_fwd" and kernels[-1] == "rows_inv"      # padding and crop inside the row kernels
     ref = oracle.linear_conv2d_ref(x, k, ch, cw, ho, wo)
     assert_close(out, ref, f"linear conv {h}x{w} * {kh}x{kw}")
 
