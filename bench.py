@@ -98,6 +98,8 @@ def kernel_bytes(name: str, cfg, backward: bool = False) -> int:
         "rows_inv_gelu": (r_out if cfg.kind == "2d" else yh) + 2 * n_out,
         # diagonal filter: both truncated spectra and the (mode, channel) mask
         "mix_diag": xh + yh + (m_modes * cfg.Cin * c8),
+        "fwd2d_diag": n_in + xh + (m_modes * cfg.Cin * c8),
+        "mask_transpose": 2 * m_modes * cfg.Cin * c8,
         "wgrad": xh + yh + wb,
         "wadjoint": 2 * wb,
         # sum of the batch splits' partial weight gradients (when the batch

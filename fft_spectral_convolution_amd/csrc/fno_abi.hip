@@ -405,6 +405,18 @@ int run_filter_2d(const Shape2d& s, const float* x, const float2* mask, float* o
         float2* xh = static_cast<float2*>(ws);
         float2* yh = reinterpret_cast<float2*>(static_cast<char*>(ws) +
                                                align_up((size_t)layout_elems(lay, s.B) * sizeof(float2)));
+        if (rowreg2d_supported(s.log2H, s.log2W, s.mx, s.my, lay) &&
+            (int64_t)m * s.Cin * 8 < (int64_t)kBufferSkip) {
+            // the product folded into the forward transform's stores, on the
+            // mask transposed channel-major (in the unused xh region)
+            rec_kernel("mask_transpose", st);
+            hipError_t e = launch_mask_transpose(mask, xh, m, s.Cin, st);
+            if (e != hipSuccess) return hip_fail(e);
+            rec_kernel("fwd2d_diag", st);
+            e = launch_fwd2d_rowreg(x, yh, lay, s.B * s.Cin, s.log2H, s.log2W, s.mx, s.my, tw, st, xh);
+            if (e != hipSuccess) return hip_fail(e);
+            return run_inverse2d_small(s, s.Cin, yh, out, lay, tw, st);
+        }
         int rc = run_forward2d_small(s, s.Cin, x, xh, lay, tw, st);
         if (rc) return rc;
         rec_kernel("mix_diag", st);

@@ -56,7 +56,31 @@ __global__ __launch_bounds__(kDiagThreads) void k_mix_diag_single(const float2* 
     }
 }
 
+// mt[c][m] = mask[m][c]: 32 x 32 tiles through LDS
+constexpr int kTrTile = 32;
+__global__ __launch_bounds__(kDiagThreads) void k_mask_transpose(const float2* __restrict__ mask,
+                                                                 float2* __restrict__ mt, int M, int C, int n_mt) {
+    __shared__ float2 tile[kTrTile][kTrTile + 1];
+    const int m0 = (int)(blockIdx.x % n_mt) * kTrTile;
+    const int c0 = (int)(blockIdx.x / n_mt) * kTrTile;
+    const int tx = threadIdx.x & (kTrTile - 1);
+    const int ty = threadIdx.x / kTrTile;
+    for (int r = ty; r < kTrTile; r += kDiagThreads / kTrTile)
+        if (m0 + r < M && c0 + tx < C) tile[r][tx] = mask[(int64_t)(m0 + r) * C + c0 + tx];
+    __syncthreads();
+    for (int r = ty; r < kTrTile; r += kDiagThreads / kTrTile)
+        if (c0 + r < C && m0 + tx < M) mt[(int64_t)(c0 + r) * M + m0 + tx] = tile[tx][r];
+}
+
 }  // namespace
+
+hipError_t launch_mask_transpose(const float2* mask, float2* mt, int64_t M, int64_t C, hipStream_t s) {
+    const int64_t n_mt = (M + kTrTile - 1) / kTrTile;
+    const int64_t n = n_mt * ((C + kTrTile - 1) / kTrTile);
+    if (n >= INT32_MAX || M > INT32_MAX || C > INT32_MAX) return hipErrorInvalidValue;
+    return launch_kernel(k_mask_transpose, dim3((unsigned)n), dim3(kDiagThreads), 0, s, mask, mt, (int)M, (int)C,
+                         (int)n_mt);
+}
 
 bool mix_diag_supported(const SpecLayout& lay, int64_t M) {
     return lay.sc == 8 ? lay.st == 8 * (int64_t)lay.C : (lay.sc == M && lay.st == 8);

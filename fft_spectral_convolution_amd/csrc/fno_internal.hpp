@@ -125,8 +125,11 @@ hipError_t launch_inv2d_small(const float2* yh, float* out, const SpecLayout& la
 // H, W in {64, 128}, my <= 32; same output as launch_fwd2d_small (scaled by
 // (HW)^-1/2).  Persistent grid sized from the kernel's occupancy.
 bool rowreg2d_supported(int log2H, int log2W, int mx, int my, const SpecLayout& lay);
+// mask_t (optional): the diagonal filter applied on the way out,
+// xh(b, c, m) *= mask_t[c][m] (the mask transposed channel-major)
 hipError_t launch_fwd2d_rowreg(const float* x, float2* xh, const SpecLayout& lay, int64_t nimg, int log2H,
-                               int log2W, int mx, int my, const float2* tw, hipStream_t s);
+                               int log2W, int mx, int my, const float2* tw, hipStream_t s,
+                               const float2* mask = nullptr);
 // and its inverse: truncated spectrum -> real image, same shapes and scale
 hipError_t launch_inv2d_rowreg(const float2* yh, float* out, const SpecLayout& lay, int64_t nimg, int log2H,
                                int log2W, int mx, int my, const float2* tw, hipStream_t s,
@@ -189,6 +192,8 @@ hipError_t launch_rows_inv(const float2* y, float* out, int64_t nrows, int log2W
 // yh(b, c, m) = xh(b, c, m) * mask[m][c], both spectra in layout `lay`
 // (tiled or canonical).
 bool mix_diag_supported(const SpecLayout& lay, int64_t M);
+// mt[c][m] = mask[m][c] (M modes, C channels)
+hipError_t launch_mask_transpose(const float2* mask, float2* mt, int64_t M, int64_t C, hipStream_t s);
 hipError_t launch_mix_diag(const float2* xh, float2* yh, const SpecLayout& lay, const float2* mask, int64_t B,
                            int64_t C, int64_t M, hipStream_t s);
 

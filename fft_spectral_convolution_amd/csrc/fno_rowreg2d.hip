@@ -112,10 +112,15 @@ __device__ __forceinline__ float2 half_bin_scaled(const float2 (&z)[NZ]) {
     return make_float2(fmaf(h, ax, tx), fmaf(h, ay, ty));
 }
 
-template <int LOG2H, int LOG2W, int MYMAX>
+// DIAG: the diagonal global filter folded into the store: every kept mode m
+// of image b C + c is multiplied by mask[c][m] (the mask transposed
+// channel-major, so that a wave's lanes, over consecutive ky, read
+// consecutive entries) on its way out.
+template <int LOG2H, int LOG2W, int MYMAX, bool DIAG>
 __global__ __launch_bounds__(1 << LOG2H) __attribute__((amdgpu_waves_per_eu(2))) void k_fwd2d_rows(const float* __restrict__ x, float2* __restrict__ xh,
                                                            ImageBase ib, int st, int64_t nimg, int mx, int my,
-                                                           const float2* __restrict__ tw) {
+                                                           const float2* __restrict__ tw,
+                                                           const float2* __restrict__ mask) {
     using S = RowPlan<LOG2H, LOG2W, MYMAX>;
     constexpr int H = S::H, W = S::W, NZ = S::NZ, F4 = S::F4, R1 = S::R1, R2 = S::R2, KB = S::KB, NB = S::NB,
                   NJ = S::NJ;
@@ -213,6 +218,13 @@ __global__ __launch_bounds__(1 << LOG2H) __attribute__((amdgpu_waves_per_eu(2)))
         });
         lds_barrier();
         const __amdgpu_buffer_rsrc_t ro = make_rsrc(xh + ib(img), out_bytes);
+        // filter: image b C + c reads row c of the transposed mask; dropped
+        // modes read zero through the range check
+        __amdgpu_buffer_rsrc_t rmask = ro;
+        if constexpr (DIAG) {
+            const uint32_t c = (uint32_t)img % (uint32_t)ib.C;
+            rmask = make_rsrc(mask + (int64_t)c * (2 * mx * my), (uint32_t)(2 * mx * my) * 8u);
+        }
         static_for<0, NB>([&](auto bt) {
             const float2* const xb = xreg + bt * S::XBUF + cl * S::GS;
             const int ky = bt * KB + cl;
@@ -221,6 +233,14 @@ __global__ __launch_bounds__(1 << LOG2H) __attribute__((amdgpu_waves_per_eu(2)))
             for (int jj = 0; jj < NJ; ++jj) {
                 const int k1 = t + R2 * jj;
                 float2 u[R2];
+                float2 mv[DIAG ? R2 : 1];
+                if constexpr (DIAG) {
+#pragma unroll
+                    for (int k2 = 0; k2 < R2; ++k2) {
+                        const int q = qm[jj][k2];
+                        mv[k2] = buffer_load_f2(rmask, (q < 0 || !kyok) ? kBufferSkip : (uint32_t)(q + ky) * 8u, 0);
+                    }
+                }
 #pragma unroll
                 for (int tt = 0; tt < R2; ++tt) u[tt] = xb[tt * S::XS + k1];
                 dft<R2, -1>(u);
@@ -230,7 +250,9 @@ __global__ __launch_bounds__(1 << LOG2H) __attribute__((amdgpu_waves_per_eu(2)))
                     const int q = qm[jj][k2];
                     const uint32_t m = (uint32_t)(q + ky);
                     const uint32_t off = (q < 0 || !kyok) ? kBufferSkip : (m + (m >> 3) * st8) * 8u;
-                    buffer_store_f2(u[k2], ro, off, 0);
+                    float2 val = u[k2];
+                    if constexpr (DIAG) val = cmul(val, mv[k2]);
+                    buffer_store_f2(val, ro, off, 0);
                 }
             }
         });
@@ -446,10 +468,13 @@ hipError_t launch_persistent(K k, int nt, size_t lds, int64_t nimg, hipStream_t 
 
 template <int LH, int LW, int MYM>
 hipError_t launch_fwd_one(const float* x, float2* xh, const ImageBase& ib, int st, int64_t nimg, int mx, int my,
-                          const float2* tw, hipStream_t s) {
+                          const float2* tw, hipStream_t s, const float2* mask) {
     using P = RowPlan<LH, LW, MYM>;
-    return launch_persistent(k_fwd2d_rows<LH, LW, MYM>, P::NT, P::lds_bytes(), nimg, s, x, xh, ib, st, nimg, mx, my,
-                             tw);
+    if (mask)
+        return launch_persistent(k_fwd2d_rows<LH, LW, MYM, true>, P::NT, P::lds_bytes(), nimg, s, x, xh, ib, st, nimg,
+                                 mx, my, tw, mask);
+    return launch_persistent(k_fwd2d_rows<LH, LW, MYM, false>, P::NT, P::lds_bytes(), nimg, s, x, xh, ib, st, nimg,
+                             mx, my, tw, mask);
 }
 
 template <int LH, int LW, int MYM>
@@ -488,11 +513,13 @@ bool rowreg2d_supported(int log2H, int log2W, int mx, int my, const SpecLayout& 
     return hipErrorInvalidValue;
 
 hipError_t launch_fwd2d_rowreg(const float* x, float2* xh, const SpecLayout& lay, int64_t nimg, int log2H,
-                               int log2W, int mx, int my, const float2* tw, hipStream_t s) {
+                               int log2W, int mx, int my, const float2* tw, hipStream_t s, const float2* mask) {
     if (!rowreg2d_supported(log2H, log2W, mx, my, lay) || nimg >= INT32_MAX) return hipErrorInvalidValue;
+    // the mask's byte range (2 mx my C complex) stays below the buffer range limit
+    if (mask && (int64_t)2 * mx * my * lay.C * 8 >= (int64_t)kBufferSkip) return hipErrorInvalidValue;
     const ImageBase ib = image_base(lay);
     const int st = (int)lay.st;
-    FNO_ROWREG_DISPATCH(launch_fwd_one, x, xh, ib, st, nimg, mx, my, tw, s)
+    FNO_ROWREG_DISPATCH(launch_fwd_one, x, xh, ib, st, nimg, mx, my, tw, s, mask)
 }
 
 hipError_t launch_inv2d_rowreg(const float2* yh, float* out, const SpecLayout& lay, int64_t nimg, int log2H,

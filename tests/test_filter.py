@@ -56,7 +56,8 @@ def check(cfg, seed=0):
         out = fno.fno_spectral_filter2d(xd, md, cfg.mx, cfg.my)
         ref = oracle.spectral_filter2d_ref(x, mask, cfg.mx, cfg.my)
     torch.cuda.synchronize()
-    assert "mix_diag" in fno.fno_last_kernels()
+    kernels = fno.fno_last_kernels()
+    assert "mix_diag" in kernels or "fwd2d_diag" in kernels
     assert_close(out, ref, f"{cfg.name} filter")
 
 
