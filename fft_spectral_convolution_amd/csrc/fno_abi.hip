@@ -25,11 +25,16 @@ constexpr int kVersion = 100;   // 0.1.0
 
 thread_local int g_last_hip_error = 0;
 
+struct Workspace {
+    void* stream = nullptr;
+    void* ptr = nullptr;
+    size_t bytes = 0;
+};
+
 struct DeviceState {
     bool init = false;
     float2* twiddle = nullptr;     // kNMax entries exp(-2 pi i m / kNMax)
-    void* ws = nullptr;            // internal grow-only workspace
-    size_t ws_bytes = 0;
+    std::vector<Workspace> ws;     // internal grow-only workspace, one per stream
 };
 
 std::mutex g_mutex;
@@ -156,20 +161,29 @@ int device_state(DeviceState** out) {
 }
 
 // Grow the internal workspace of the current device to at least `bytes`.
-int internal_workspace(DeviceState* st, size_t bytes, void** ws) {
+// The internal workspace of calls on `stream`: one grow-only buffer per
+// (device, stream), so that calls on different streams never share scratch.
+int internal_workspace(DeviceState* st, size_t bytes, void** ws, void* stream) {
     std::lock_guard<std::mutex> lock(g_mutex);
     if (bytes == 0) {
         *ws = nullptr;
         return FNO_OK;
     }
-    if (st->ws_bytes < bytes) {
-        if (st->ws) {
+    Workspace* slot = nullptr;
+    for (auto& w : st->ws)
+        if (w.stream == stream) slot = &w;
+    if (!slot) {
+        st->ws.push_back(Workspace{stream, nullptr, 0});
+        slot = &st->ws.back();
+    }
+    if (slot->bytes < bytes) {
+        if (slot->ptr) {
             // in-flight work may still read the old buffer
             hipError_t e = hipDeviceSynchronize();
             if (e != hipSuccess) return hip_fail(e);
-            (void)hipFree(st->ws);
-            st->ws = nullptr;
-            st->ws_bytes = 0;
+            (void)hipFree(slot->ptr);
+            slot->ptr = nullptr;
+            slot->bytes = 0;
         }
         void* d = nullptr;
         hipError_t e = hipMalloc(&d, bytes);
@@ -177,10 +191,10 @@ int internal_workspace(DeviceState* st, size_t bytes, void** ws) {
             (void)hipGetLastError();
             return e == hipErrorOutOfMemory ? FNO_ERR_NOMEM : hip_fail(e);
         }
-        st->ws = d;
-        st->ws_bytes = bytes;
+        slot->ptr = d;
+        slot->bytes = bytes;
     }
-    *ws = st->ws;
+    *ws = slot->ptr;
     return FNO_OK;
 }
 
@@ -453,7 +467,7 @@ int filter2d_common(const float* x, const void* mask, float* out, int B, int C, 
     rc = device_state(&st);
     if (rc) return rc;
     void* ws = nullptr;
-    rc = internal_workspace(st, best_ws_2d(s), &ws);
+    rc = internal_workspace(st, best_ws_2d(s), &ws, stream);
     if (rc) return rc;
     hipStream_t hs = static_cast<hipStream_t>(stream);
     rec_begin();
@@ -472,7 +486,7 @@ int filter1d_common(const float* x, const void* mask, float* out, int B, int C, 
     if (rc) return rc;
     void* ws = nullptr;
     const size_t hb = align_up((size_t)B * C * modes * sizeof(float2));
-    rc = internal_workspace(st, 2 * hb, &ws);
+    rc = internal_workspace(st, 2 * hb, &ws, stream);
     if (rc) return rc;
     float2* xh = static_cast<float2*>(ws);
     float2* yh = reinterpret_cast<float2*>(static_cast<char*>(ws) + hb);
@@ -529,7 +543,7 @@ int linconv2d_prepare(const float* k, void* wspec, int Cin, int Cout, int H, int
     int rc = device_state(&st);
     if (rc) return rc;
     void* ws = nullptr;
-    rc = internal_workspace(st, kp_b + kh_b + r_b, &ws);
+    rc = internal_workspace(st, kp_b + kh_b + r_b, &ws, stream);
     if (rc) return rc;
     float* kp = static_cast<float*>(ws);
     float2* khs = reinterpret_cast<float2*>(static_cast<char*>(ws) + kp_b);
@@ -575,7 +589,7 @@ int linconv2d_run(const float* x, const void* wspec, float* out, int B, int Cin,
     rc = device_state(&st);
     if (rc) return rc;
     void* ws = nullptr;
-    rc = internal_workspace(st, r_b + x_b + y_b, &ws);
+    rc = internal_workspace(st, r_b + x_b + y_b, &ws, stream);
     if (rc) return rc;
     float2* r = static_cast<float2*>(ws);
     float2* xh = reinterpret_cast<float2*>(static_cast<char*>(ws) + r_b);
@@ -619,7 +633,7 @@ int linconv1d_prepare(const float* k, void* wspec, int Cin, int Cout, int N, int
     int rc = device_state(&st);
     if (rc) return rc;
     void* ws = nullptr;
-    rc = internal_workspace(st, kp_b + kh_b, &ws);
+    rc = internal_workspace(st, kp_b + kh_b, &ws, stream);
     if (rc) return rc;
     float* kp = static_cast<float*>(ws);
     float2* khs = reinterpret_cast<float2*>(static_cast<char*>(ws) + kp_b);
@@ -656,7 +670,7 @@ int linconv1d_run(const float* x, const void* wspec, float* out, int B, int Cin,
     rc = device_state(&st);
     if (rc) return rc;
     void* ws = nullptr;
-    rc = internal_workspace(st, x_b + y_b, &ws);
+    rc = internal_workspace(st, x_b + y_b, &ws, stream);
     if (rc) return rc;
     float2* xh = static_cast<float2*>(ws);
     float2* yh = reinterpret_cast<float2*>(static_cast<char*>(ws) + x_b);
@@ -719,7 +733,7 @@ int conv2d_common(const float* x, const void* w, float* out, int B, int Cin, int
     rc = device_state(&st);
     if (rc) return rc;
     if (!use_user_ws) {
-        rc = internal_workspace(st, need, &ws);
+        rc = internal_workspace(st, need, &ws, stream);
         if (rc) return rc;
     }
     hipStream_t hs = static_cast<hipStream_t>(stream);
@@ -751,7 +765,7 @@ int conv1d_common(const float* x, const void* w, float* out, int B, int Cin, int
     rc = device_state(&st);
     if (rc) return rc;
     if (!use_user_ws) {
-        rc = internal_workspace(st, need, &ws);
+        rc = internal_workspace(st, need, &ws, stream);
         if (rc) return rc;
     }
     hipStream_t hs = static_cast<hipStream_t>(stream);
@@ -865,7 +879,7 @@ int backward2d_common(const float* x, const void* w, const float* g, float* gx, 
     rc = device_state(&st);
     if (rc) return rc;
     void* ws = nullptr;
-    rc = internal_workspace(st, backward_plan_2d(s).total(), &ws);
+    rc = internal_workspace(st, backward_plan_2d(s).total(), &ws, stream);
     if (rc) return rc;
     hipStream_t hs = static_cast<hipStream_t>(stream);
     rec_begin();
@@ -891,7 +905,7 @@ int backward1d_common(const float* x, const void* w, const float* g, float* gx, 
     rc = device_state(&st);
     if (rc) return rc;
     void* ws = nullptr;
-    rc = internal_workspace(st, 2 * xb + gb + wtb + wgb, &ws);
+    rc = internal_workspace(st, 2 * xb + gb + wtb + wgb, &ws, stream);
     if (rc) return rc;
     char* q = static_cast<char*>(ws);
     float2* xh = reinterpret_cast<float2*>(q);
@@ -1097,7 +1111,7 @@ int fno_forward2d(const float* x, void* xh, int B, int C, int H, int W, int mx, 
         return rec_end(hs, run_forward2d_small(s, C, x, out, canonical_layout(C, 2 * mx * my), st->twiddle, hs));
     }
     void* ws = nullptr;
-    rc = internal_workspace(st, (size_t)B * C * H * my * sizeof(float2), &ws);
+    rc = internal_workspace(st, (size_t)B * C * H * my * sizeof(float2), &ws, stream);
     if (rc) return rc;
     rec_begin();
     return rec_end(hs, run_forward2d_staged(s, C, x, out, static_cast<float2*>(ws), st->twiddle, hs));
@@ -1122,7 +1136,7 @@ int fno_inverse2d(const void* yh, float* out, int B, int C, int H, int W, int mx
         return rec_end(hs, run_inverse2d_small(s, C, in, out, canonical_layout(C, 2 * mx * my), st->twiddle, hs));
     }
     void* ws = nullptr;
-    rc = internal_workspace(st, (size_t)B * C * H * my * sizeof(float2), &ws);
+    rc = internal_workspace(st, (size_t)B * C * H * my * sizeof(float2), &ws, stream);
     if (rc) return rc;
     rec_begin();
     return rec_end(hs, run_inverse2d_staged(s, C, in, out, static_cast<float2*>(ws), st->twiddle, hs));

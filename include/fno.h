@@ -73,9 +73,10 @@ int fno_last_hip_error(void);
 /*
  * 2D spectral convolution (TurboFNO blog, sections 1 and 2.2; FFT blog
  * sections 2.1-2.2).  Picks the fastest implemented schedule for the shape.
- * Uses an internal per-device workspace (grow-only, allocated on first use and
- * kept until process exit); calls that share a device and overlap in time on
- * different streams must use fno_spectral_conv2d_ws instead.
+ * Uses an internal workspace per (device, stream): grow-only, allocated on
+ * first use and kept until process exit, so calls on different streams may
+ * overlap in time (growing it synchronises the device once).  The _ws
+ * variants take caller-owned scratch instead.
  */
 int fno_spectral_conv2d(const float* x, const void* w, float* out,
                         int B, int Cin, int Cout, int H, int W, int mx, int my,

@@ -286,6 +286,28 @@ def test_workspace_variant_and_stream():
         assert ei.value.status == -8
 
 
+def test_concurrent_streams_internal_workspace():
+    # calls on two streams overlap in time; each stream has its own internal
+    # workspace, so the results equal those of calls made one after another
+    cfg = CONFIGS["c3"]
+    x, w = make_inputs(cfg, 0)
+    xd, wd = to_dev(x), to_dev(w)
+    x2 = torch.flip(xd, dims=[0]).contiguous()
+    ref1 = fno.fno_spectral_conv2d(xd, wd, cfg.mx, cfg.my)
+    ref2 = fno.fno_spectral_conv2d(x2, wd, cfg.mx, cfg.my)
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    outs1, outs2 = [], []
+    for _ in range(3):
+        with torch.cuda.stream(s1):
+            outs1.append(fno.fno_spectral_conv2d(xd, wd, cfg.mx, cfg.my))
+        with torch.cuda.stream(s2):
+            outs2.append(fno.fno_spectral_conv2d(x2, wd, cfg.mx, cfg.my))
+    torch.cuda.synchronize()
+    for a, b in zip(outs1, outs2):
+        assert torch.equal(a, ref1) and torch.equal(b, ref2)
+
+
 def test_out_is_overwritten():
     cfg, x, w, ref = config_case("c1")
     out = torch.full(cfg.out_shape, float("nan"), dtype=torch.float32, device=DEV)
