@@ -11,6 +11,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <memory>
 #include <mutex>
 #include <vector>
 
@@ -38,7 +39,8 @@ struct DeviceState {
 };
 
 std::mutex g_mutex;
-std::vector<DeviceState> g_devices;
+// one state per device, never moved (calls on other devices keep pointers)
+std::vector<std::unique_ptr<DeviceState>> g_devices;
 
 // Optional per-kernel timing (fno_set_timing_events): kernel k of a call
 // launches with events[2k], events[2k + 1] as its start and stop events.
@@ -138,7 +140,8 @@ int device_state(DeviceState** out) {
     if (e != hipSuccess) return hip_fail(e);
     std::lock_guard<std::mutex> lock(g_mutex);
     if ((int)g_devices.size() <= dev) g_devices.resize(dev + 1);
-    DeviceState& st = g_devices[dev];
+    if (!g_devices[dev]) g_devices[dev] = std::make_unique<DeviceState>();
+    DeviceState& st = *g_devices[dev];
     if (!st.init) {
         std::vector<float2> host(kNMax);
         for (int m = 0; m < kNMax; ++m) {
@@ -160,7 +163,6 @@ int device_state(DeviceState** out) {
     return FNO_OK;
 }
 
-// Grow the internal workspace of the current device to at least `bytes`.
 // The internal workspace of calls on `stream`: one grow-only buffer per
 // (device, stream), so that calls on different streams never share scratch.
 int internal_workspace(DeviceState* st, size_t bytes, void** ws, void* stream) {

@@ -36,7 +36,9 @@
  * 2 <= H, W <= 4096 (1D: the same for N); 1 <= mx, 2*mx <= H;
  * 1 <= my <= W/2+1 (floor).  Powers of two take the specialised kernels;
  * other lengths take mixed-radix (4, 2, 3, 5, 7) stage kernels (the FFT
- * blog, section 6.2, on non-power-of-two sizes).
+ * blog, section 6.2, on non-power-of-two sizes); the first call with a new
+ * such length on a device builds that length's twiddle table (a device
+ * allocation and a synchronous copy, like the first use of a workspace).
  * (1D: 1 <= modes <= N/2+1).  x, w, out must be 16-byte aligned and x must
  * not overlap out.  `out` is fully overwritten.
  */
