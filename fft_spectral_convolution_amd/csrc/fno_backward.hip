@@ -266,7 +266,10 @@ __global__ __launch_bounds__(kWgThreads) void k_weight_grad_mfma(const float2* _
                 const int i = i0 + 16 * ri + 4 * lk + j;
                 if (i < Cin && o < Cout) {
                     const float pr = p1[ri][cb][j], pi = p2[ri][cb][j];
-                    dst[(int64_t)i * Cout + o] = make_float2(c * (pr + pi), c * (p3[ri][cb][j] - pr + pi));
+                    const float2 v = make_float2(c * (pr + pi), c * (p3[ri][cb][j] - pr + pi));
+                    // the gradient itself streams out; split partials stay cached for the reduction
+                    if (wg.splits == 1) nt_store2(&dst[(int64_t)i * Cout + o], v);
+                    else dst[(int64_t)i * Cout + o] = v;
                 }
             }
         }
@@ -282,7 +285,7 @@ __global__ __launch_bounds__(kWgReduceThreads) void k_weight_grad_reduce(const f
         float2 acc = part[e];
         for (int sp = 1; sp < splits; ++sp) acc = cadd(acc, part[(int64_t)sp * n + e]);
         const int ky = (int)((e / per_mode) % my);
-        gw[e] = cscale(acc, (ky == 0 || ky == nyq) ? 1.0f : 2.0f);
+        nt_store2(&gw[e], cscale(acc, (ky == 0 || ky == nyq) ? 1.0f : 2.0f));
     }
 }
 

@@ -262,6 +262,26 @@ __device__ __forceinline__ void buffer_store_f4(float4 a, __amdgpu_buffer_rsrc_t
     __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)voff, (int)soff, 0);
 }
 
+// Non-temporal stores for a call's final outputs (never read back within
+// the call): they stream to memory instead of staying dirty in the
+// last-level cache, where their write-back would compete with the next
+// reads.  Buffer form: cache-policy bit 1 (nt).
+__device__ __forceinline__ void buffer_store_f4_nt(float4 a, __amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    u32x4_t v;
+    v[0] = __float_as_uint(a.x);
+    v[1] = __float_as_uint(a.y);
+    v[2] = __float_as_uint(a.z);
+    v[3] = __float_as_uint(a.w);
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)voff, (int)soff, 2);
+}
+
+__device__ __forceinline__ void nt_store(float* p, float v) { __builtin_nontemporal_store(v, p); }
+__device__ __forceinline__ void nt_store2(float2* p, float2 v) {
+    typedef float f2v __attribute__((ext_vector_type(2)));
+    const f2v t = {v.x, v.y};
+    __builtin_nontemporal_store(t, reinterpret_cast<f2v*>(p));
+}
+
 __device__ __forceinline__ void buffer_store_f2(float2 a, __amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
     u32x2_t v;
     v[0] = __float_as_uint(a.x);

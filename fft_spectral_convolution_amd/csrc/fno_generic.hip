@@ -170,13 +170,13 @@ __global__ __launch_bounds__(kThreads) void k_rows_inv(const float2* __restrict_
                 make_rsrc(epi.branch ? epi.branch + 2 * pair0 * W : nullptr,
                           epi.branch ? (uint32_t)((nrows - 2 * pair0 < 2 * P ? nrows - 2 * pair0 : 2 * P) * W * 4) : 0u);
             const uint32_t off = (uint32_t)((ra - 2 * pair0) * W + n) * 4u;
-            out[ra * W + n] = epi_apply(epi, z.x * scale, epi_bias(epi, (uint32_t)ra), buffer_load_f1(rb, off, 0));
+            nt_store(&out[ra * W + n], epi_apply(epi, z.x * scale, epi_bias(epi, (uint32_t)ra), buffer_load_f1(rb, off, 0)));
             if (ra + 1 < nrows)
-                out[(ra + 1) * W + n] = epi_apply(epi, z.y * scale, epi_bias(epi, (uint32_t)(ra + 1)),
-                                                  buffer_load_f1(rb, off + (uint32_t)W * 4u, 0));
+                nt_store(&out[(ra + 1) * W + n], epi_apply(epi, z.y * scale, epi_bias(epi, (uint32_t)(ra + 1)),
+                                                           buffer_load_f1(rb, off + (uint32_t)W * 4u, 0)));
         } else {
-            out[ra * W + n] = z.x * scale;
-            if (ra + 1 < nrows) out[(ra + 1) * W + n] = z.y * scale;
+            nt_store(&out[ra * W + n], z.x * scale);
+            if (ra + 1 < nrows) nt_store(&out[(ra + 1) * W + n], z.y * scale);
         }
     }
 }

@@ -259,7 +259,7 @@ __global__ __launch_bounds__(kMrThreads) void k_rows_inv_mr(const float2* __rest
                 const uint32_t img = (uint32_t)r / (uint32_t)win.ph;
                 const int q = (int)((uint32_t)r - img * (uint32_t)win.ph) - win.h0;
                 if (q >= 0 && q < win.h)
-                    out[((int64_t)img * win.h + q) * win.w + n - win.w0] = (s2 ? z.y : z.x) * scale;
+                    nt_store(&out[((int64_t)img * win.h + q) * win.w + n - win.w0], (s2 ? z.y : z.x) * scale);
             }
             continue;
         }
@@ -268,13 +268,13 @@ __global__ __launch_bounds__(kMrThreads) void k_rows_inv_mr(const float2* __rest
                 make_rsrc(epi.branch ? epi.branch + 2 * pair0 * W : nullptr,
                           epi.branch ? (uint32_t)((nrows - 2 * pair0 < 2 * P ? nrows - 2 * pair0 : 2 * P) * W * 4) : 0u);
             const uint32_t off = (uint32_t)((ra - 2 * pair0) * W + n) * 4u;
-            out[ra * W + n] = epi_apply(epi, z.x * scale, epi_bias(epi, (uint32_t)ra), buffer_load_f1(rb, off, 0));
+            nt_store(&out[ra * W + n], epi_apply(epi, z.x * scale, epi_bias(epi, (uint32_t)ra), buffer_load_f1(rb, off, 0)));
             if (ra + 1 < nrows)
-                out[(ra + 1) * W + n] = epi_apply(epi, z.y * scale, epi_bias(epi, (uint32_t)(ra + 1)),
-                                                  buffer_load_f1(rb, off + (uint32_t)W * 4u, 0));
+                nt_store(&out[(ra + 1) * W + n], epi_apply(epi, z.y * scale, epi_bias(epi, (uint32_t)(ra + 1)),
+                                                           buffer_load_f1(rb, off + (uint32_t)W * 4u, 0)));
         } else {
-            out[ra * W + n] = z.x * scale;
-            if (ra + 1 < nrows) out[(ra + 1) * W + n] = z.y * scale;
+            nt_store(&out[ra * W + n], z.x * scale);
+            if (ra + 1 < nrows) nt_store(&out[(ra + 1) * W + n], z.y * scale);
         }
     }
 }

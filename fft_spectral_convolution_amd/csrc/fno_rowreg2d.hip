@@ -442,7 +442,7 @@ __global__ __launch_bounds__(1 << LOG2H) __attribute__((amdgpu_waves_per_eu(2)))
                         o = make_float4(epi_apply(epi, o.x, bias, br[ii].x), epi_apply(epi, o.y, bias, br[ii].y),
                                         epi_apply(epi, o.z, bias, br[ii].z), epi_apply(epi, o.w, bias, br[ii].w));
                     }
-                    buffer_store_f4(o, ro, soffs[ii] + 128 * c, 0);
+                    buffer_store_f4_nt(o, ro, soffs[ii] + 128 * c, 0);
                 });
                 wave_lds_sync();
             });

@@ -299,14 +299,14 @@ __global__ __launch_bounds__(kPrunedThreads) __attribute__((amdgpu_waves_per_eu(
             for (int k = 0; k < 2 * NZ; ++k) br[k] = buffer_load_f1(rb, (uint32_t)(lane + 64 * k) * 4u, 0);
 #pragma unroll
             for (int m = 0; m < NZ; ++m) {
-                dst[64 * (2 * m)] = epi_apply(epi, z[m].x, bias, br[2 * m]);
-                dst[64 * (2 * m + 1)] = epi_apply(epi, z[m].y, bias, br[2 * m + 1]);
+                nt_store(&dst[64 * (2 * m)], epi_apply(epi, z[m].x, bias, br[2 * m]));
+                nt_store(&dst[64 * (2 * m + 1)], epi_apply(epi, z[m].y, bias, br[2 * m + 1]));
             }
         } else {
 #pragma unroll
             for (int m = 0; m < NZ; ++m) {
-                dst[64 * (2 * m)] = z[m].x;
-                dst[64 * (2 * m + 1)] = z[m].y;
+                nt_store(&dst[64 * (2 * m)], z[m].x);
+                nt_store(&dst[64 * (2 * m + 1)], z[m].y);
             }
         }
     }

@@ -444,16 +444,16 @@ __global__ __launch_bounds__(kSmallThreads, kSmallBlocksPerCU) void k_inv2d_smal
                     for (int m = 0; m < MW; ++m) {
                         const float2 za = buffer_load_f2(rb, (uint32_t)((p * W + 2 * (t + TW * m)) * 4), 0);
                         const float2 zb = buffer_load_f2(rb, (uint32_t)(((p + P) * W + 2 * (t + TW * m)) * 4), 0);
-                        oa[TW * m] = make_float2(epi_apply(epi, v0[m].x * scale, bias, za.x),
-                                                 epi_apply(epi, v1[m].x * scale, bias, za.y));
-                        ob[TW * m] = make_float2(epi_apply(epi, v0[m].y * scale, bias, zb.x),
-                                                 epi_apply(epi, v1[m].y * scale, bias, zb.y));
+                        nt_store2(&oa[TW * m], make_float2(epi_apply(epi, v0[m].x * scale, bias, za.x),
+                                                           epi_apply(epi, v1[m].x * scale, bias, za.y)));
+                        nt_store2(&ob[TW * m], make_float2(epi_apply(epi, v0[m].y * scale, bias, zb.x),
+                                                           epi_apply(epi, v1[m].y * scale, bias, zb.y)));
                     }
                 } else {
 #pragma unroll
                     for (int m = 0; m < MW; ++m) {
-                        oa[TW * m] = make_float2(v0[m].x * scale, v1[m].x * scale);
-                        ob[TW * m] = make_float2(v0[m].y * scale, v1[m].y * scale);
+                        nt_store2(&oa[TW * m], make_float2(v0[m].x * scale, v1[m].x * scale));
+                        nt_store2(&ob[TW * m], make_float2(v0[m].y * scale, v1[m].y * scale));
                     }
                 }
             }
