@@ -9,10 +9,14 @@
 // With n = n1 + 64 n2 and W = exp(-2 pi i / N):
 //   X[k] = sum_n1 W^{n1 k} Y_n1[k mod Q],   Y_n1 = DFT_Q of lane n1's samples.
 // Forward: each lane runs its Q-point real DFT in registers (packed as a
-// Q/2-point complex one), twiddles the kept bins by W^{n1 k} = A[k mod 8]
-// B[k div 8] (A[j] = W^{n1 j}, B[j] = W^{8 n1 j}: one product of two
-// correctly rounded table values) and the 64 lanes' contributions are summed
-// through a per-wave LDS stage, 16 bins at a time.
+// Q/2-point complex one) and writes its untwiddled residues Y_n1[r] to a
+// per-wave LDS stage; the twiddles are applied on the reading side, where
+// lane (bin k, quarter q) sums its 16 lanes n1 = 16 q + t as
+// W^{16 q k} sum_t (W^k)^t Y_n1 with a binary tree (factors W^k, W^{2k},
+// W^{4k}, W^{8k}), and the quarters are added across neighbouring lanes.
+// The reading lane needs two twiddles per 16 bins instead of the writing
+// lane needing one per bin, which leaves the registers for four waves per
+// SIMD at N = 2048.
 // Inverse: lane n1 forms V[r] = sum_{k = r mod Q} c_k X[k] W^{-n1 k}
 // (c_0 = 1 with the DC imaginary part dropped, c_k = 2 otherwise: the
 // Hermitian extension of the half spectrum); the real part of its inverse
@@ -97,33 +101,6 @@ struct LaneTwiddles {
     }
 };
 
-// W^{n1 K} = A[K mod 8] * B[K div 8], A[j] = W^{n1 j}, B[j] = W^{8 n1 j}
-template <int Q>
-struct ABTwiddles {
-    float2 A[8], B[8];
-    __device__ __forceinline__ void init(const float2* __restrict__ tw, int lane) {
-        constexpr int N = 64 * Q;
-        static_assert(Q <= 64, "A.B covers bins below 64");
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            A[j] = tw[(lane * j * (kNMax / N)) & (kNMax - 1)];
-            B[j] = tw[(lane * 8 * j * (kNMax / N)) & (kNMax - 1)];
-        }
-    }
-    // Hides the factors from loop-invariant code motion: called once per row,
-    // it keeps their 64 products per row instead of hoisted into live registers.
-    __device__ __forceinline__ void opaque() {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) asm volatile("" : "+v"(A[j].x), "+v"(A[j].y), "+v"(B[j].x), "+v"(B[j].y));
-    }
-    template <int K>
-    __device__ __forceinline__ float2 full() const {
-        if constexpr (K < 8) return A[K];
-        else if constexpr (K % 8 == 0) return B[K / 8];
-        else return cmul(A[K % 8], B[K / 8]);
-    }
-};
-
 // Twice bin K (K <= Q/2) of the DFT of a real length-Q sequence s, from its
 // packed transform Z = DFT_{Q/2}(s[2m] + i s[2m+1]):
 //   2 Y[K] = (Z[K] + conj Z[-K]) - i W_Q^K (Z[K] - conj Z[-K]).
@@ -152,34 +129,43 @@ __device__ __forceinline__ float2 packed_bin(const float2 (&H)[Q / 2 + 1]) {
 }
 
 template <int Q>
-__global__ __launch_bounds__(kPrunedThreads) __attribute__((amdgpu_waves_per_eu(2))) void k_rows_fwd_pruned(
+__global__ __launch_bounds__(kPrunedThreads) __attribute__((amdgpu_waves_per_eu(Q == 64 ? 2 : 4))) void k_rows_fwd_pruned(
     const float* __restrict__ x, float2* __restrict__ y, int64_t nrows, int my, int y_ld, float scale,
     const float2* __restrict__ tw) {
     constexpr int N = 64 * Q;
     constexpr int NZ = Q / 2;
-    __shared__ float2 stage_all[kPrunedWaves][16 * kStageStride];
+    // The kept bins k < 64 fall on Q residues k mod Q, NJ = 64 / Q bins each.
+    // A chunk stages RPC residues: stage row rr of chunk ch holds lane n1's
+    // Y[RPC ch + rr], untwiddled.
+    constexpr int NJ = 64 / Q;
+    constexpr int RPC = 16 / NJ;
+    __shared__ float2 stage_all[kPrunedWaves][RPC * kStageStride];
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     float2* const stage = stage_all[wave];
-    // Q <= 32: residue factors W^{n1 r} and W_64^{n1 j} (bin k = r + Q j);
-    // Q = 64: every bin its own residue, twiddles as A.B products
-    using TW = std::conditional_t<(Q <= 32), LaneTwiddles<Q>, ABTwiddles<Q>>;
-    TW tws;
-    if constexpr (Q <= 32) tws.init(tw, lane, nullptr);
-    else tws.init(tw, lane);
-    const int kk_r = lane >> 2;              // reduction role: stage row kk_r of a chunk,
-    const int q_r = lane & 3;                // summing lanes 16 q_r .. 16 q_r + 15
-    const float half_scale = 0.5f * scale;   // the bins below are doubled
-    // Q <= 32: a chunk holds RPC residues r and, for each, its NJ bins
-    // r + Q j, so that t_r = W^{n1 r} Y[r] is formed once and reused NJ times;
-    // stage row jj RPC + rr holds bin RPC ch + rr + Q jj.
-    constexpr int NJ = Q <= 32 ? 64 / Q : 1;
-    constexpr int RPC = 16 / NJ;
-    const int k_r = Q <= 32 ? (kk_r % RPC) + Q * (kk_r / RPC) : kk_r;   // bin of stage row kk_r, chunk 0
+    // Reduction role: lane (kk_r, q_r) forms bin k = RPC ch + rr_r + Q jj_r
+    // from lanes n1 = 16 q_r + t, t < 16:
+    //   sum_t W^{n1 k} Y_n1[k mod Q] = W^{16 q_r k} sum_t (W^k)^t Y_{16 q_r + t}
+    // (the inner sum as a binary tree with factors W^k, W^2k, W^4k, W^8k),
+    // and the four quarters q_r are added across neighbouring lanes.
+    const int kk_r = lane >> 2;
+    const int q_r = lane & 3;
+    const int rr_r = kk_r % RPC;
+    const int jj_r = kk_r / RPC;
+    float2 wk[4], vk[4];                       // W^k and W^{16 q_r k} of the lane's bin in each chunk
+#pragma unroll
+    for (int ch = 0; ch < 4; ++ch) {
+        const int k = RPC * ch + rr_r + Q * jj_r;
+        wk[ch] = tw[(k * (kNMax / N)) & (kNMax - 1)];
+        vk[ch] = tw[(16 * q_r * k * (kNMax / N)) & (kNMax - 1)];
+    }
+    const float half_scale = 0.5f * scale;     // the bins below are doubled
+    const float2* const srow = stage + rr_r * kStageStride + 16 * q_r + q_r;   // = stage_at(rr_r, 16 q_r)
 
     const int64_t nwaves = (int64_t)gridDim.x * kPrunedWaves;
     for (int64_t row = (int64_t)blockIdx.x * kPrunedWaves + wave; row < nrows; row += nwaves) {
-        if constexpr (Q == 64) tws.opaque();
+#pragma unroll
+        for (int ch = 0; ch < 4; ++ch) asm volatile("" : "+v"(wk[ch].x), "+v"(wk[ch].y), "+v"(vk[ch].x), "+v"(vk[ch].y));
         const float* src = x + row * N + lane;
         float2 z[NZ];
 #pragma unroll
@@ -194,32 +180,30 @@ __global__ __launch_bounds__(kPrunedThreads) __attribute__((amdgpu_waves_per_eu(
 
         float2* const dst = y + row * (int64_t)y_ld;
         static_for<0, 4>([&](auto ch) {
-            constexpr int k0 = Q <= 32 ? RPC * ch : 16 * ch;      // lowest bin of the chunk
-            if (k0 < my) {                      // uniform: chunks with a kept bin
-                if constexpr (Q <= 32) {
-                    static_for<0, RPC>([&](auto rr) {
-                        constexpr int r = RPC * ch + rr;
-                        const float2 t = cmul(tws.tr[r], ybin(std::integral_constant<int, r>{}));
-                        stage[stage_at(rr, lane)] = t;
-                        static_for<1, NJ>([&](auto jj) {
-                            if (r + Q * jj < my) stage[stage_at(jj * RPC + rr, lane)] = cmul(tws.pj[jj], t);
-                        });
-                    });
-                } else {
-                    static_for<0, 16>([&](auto kk) {
-                        constexpr int k = 16 * ch + kk;
-                        stage[stage_at(kk, lane)] = cmul(tws.template full<k>(), ybin(std::integral_constant<int, k>{}));
-                    });
-                }
+            if (RPC * ch < my) {                // uniform: chunks with a kept bin
+                static_for<0, RPC>([&](auto rr) {
+                    stage[stage_at(rr, lane)] = ybin(std::integral_constant<int, RPC * ch + rr>{});
+                });
                 wave_lds_sync();
-                float2 acc = make_float2(0.0f, 0.0f);
+                float2 v[16];
 #pragma unroll
-                for (int t = 0; t < 16; ++t) acc = cadd(acc, stage[stage_at(kk_r, 16 * q_r + t)]);
+                for (int t = 0; t < 16; ++t) v[t] = srow[t];
+                const float2 w1 = wk[ch];
+                const float2 w2 = cmul(w1, w1);
+                const float2 w4 = cmul(w2, w2);
+                const float2 w8 = cmul(w4, w4);
+#pragma unroll
+                for (int t = 0; t < 8; ++t) v[t] = cadd(v[2 * t], cmul(w1, v[2 * t + 1]));
+#pragma unroll
+                for (int t = 0; t < 4; ++t) v[t] = cadd(v[2 * t], cmul(w2, v[2 * t + 1]));
+#pragma unroll
+                for (int t = 0; t < 2; ++t) v[t] = cadd(v[2 * t], cmul(w4, v[2 * t + 1]));
+                float2 acc = cmul(vk[ch], cadd(v[0], cmul(w8, v[1])));
                 acc.x += xchg1(acc.x);
                 acc.y += xchg1(acc.y);
                 acc.x += xchg2(acc.x);
                 acc.y += xchg2(acc.y);
-                const int k = k0 + k_r;
+                const int k = RPC * ch + rr_r + Q * jj_r;
                 if (q_r == 0 && k < my) dst[k] = cscale(acc, half_scale);
                 wave_lds_sync();
             }
