@@ -195,6 +195,30 @@ def cpu_baseline(cfg, x, w, budget_s: float = 12.0, g=None, compulsory=None, lay
     }
 
 
+def device_memory_report(dev: int) -> dict:
+    """HBM figures as the HIP runtime reports them for device `dev`: memory
+    bus width (bits) and peak memory clock (kHz), from hipDeviceGetAttribute
+    (hipDeviceAttributeMemoryBusWidth = 59 and hipDeviceAttributeMemoryClockRate
+    = 60 in ROCm 7's hip_runtime_api.h), and the peak they imply.  HBM3E
+    moves four transfers per reported memory clock (MI355X: 2.0 GHz, 8 Gbps
+    per pin), so the peak is 4 x clock x width / 8 (8192 bits: 8.19 TB/s,
+    the published ~8 TB/s).  The runtime library is the one already loaded
+    in this process (same soname)."""
+    import ctypes
+    try:
+        hip = ctypes.CDLL("libamdhip64.so.7")
+        v = ctypes.c_int(0)
+        vals = {}
+        for name, attr in (("bus_width_bits", 59), ("memory_clock_khz", 60)):
+            vals[name] = v.value if hip.hipDeviceGetAttribute(ctypes.byref(v), attr, dev) == 0 else None
+    except OSError as e:
+        return {"error": str(e)}
+    if vals["bus_width_bits"] and vals["memory_clock_khz"]:
+        vals["derived_peak_gbs"] = round(4.0 * vals["memory_clock_khz"] * 1e3 * vals["bus_width_bits"] / 8 / 1e9, 1)
+    vals["nominal_peak_gbs"] = HBM_PEAK_GBS
+    return vals
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -420,6 +444,7 @@ def main():
         },
         "calls_per_s": round(1e3 / ms_per_step, 3),
         "hbm_pct": round(100.0 * gbs / HBM_PEAK_GBS, 3),
+        "hbm_device": device_memory_report(torch.cuda.current_device()),
         "wall_s_timed": round(wall, 4),
         "kernels": {k: round(t * 1e3, 3) for k, t in zip(kernels, per_kernel_ms)},
         "kernels_unit": "us per launch (start/stop events carried by each launch)",
