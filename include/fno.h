@@ -79,6 +79,14 @@ int fno_last_hip_error(void);
  * first use and kept until process exit, so calls on different streams may
  * overlap in time (growing it synchronises the device once).  The _ws
  * variants take caller-owned scratch instead.
+ *
+ * HIP graph capture: every call enqueues kernels only (no memset or copy
+ * nodes) and may be captured once the same call has run eagerly on the
+ * capturing stream (that allocates the stream's workspace and the twiddle
+ * tables; nothing is allocated while capturing), or through the _ws variants.
+ * A captured graph holds the workspace's address: a later call on the same
+ * stream that needs a larger workspace reallocates it, after which graphs
+ * captured on that stream must not be replayed.
  */
 int fno_spectral_conv2d(const float* x, const void* w, float* out,
                         int B, int Cin, int Cout, int H, int W, int mx, int my,
