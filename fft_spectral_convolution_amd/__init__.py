@@ -12,6 +12,7 @@ cannot be loaded, every call raises; there is no fallback.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 import threading
@@ -209,8 +210,17 @@ def _conv1d_args(x, w, modes, out):
     return out, (b, cin, cout, n)
 
 
+_SAME_DEVICE = contextlib.nullcontext()
+
+
 def _on_device(t):
-    return _torch().cuda.device(t.device)
+    """Make t's device current for the call (a no-op when it already is,
+    which keeps the per-call host cost of small problems down)."""
+    torch = _torch()
+    idx = t.device.index
+    if idx is None or idx == torch.cuda.current_device():
+        return _SAME_DEVICE
+    return torch.cuda.device(t.device)
 
 
 def fno_spectral_conv2d(x, w, mx: int, my: int, out=None):
