@@ -235,6 +235,9 @@ def main():
                          "once outside the timed region")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
+    ap.add_argument("--stream-ceilings", action="store_true",
+                    help="time torch's own write (fill_), read (sum) and copy (copy_) kernels over rotated "
+                         "256 MiB buffers: the box's practical streaming rates, a calibration only")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run 5 plain device copies of MIB MiB (scale for HBM byte counters) and exit")
     args = ap.parse_args()
@@ -252,6 +255,30 @@ def main():
         sys.exit(1)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.stream_ceilings:
+        # four 256 MiB buffers rotated, so that the 256 MiB last-level cache
+        # never holds the buffer an operation touches
+        n = 256 * 2**20 // 4
+        bufs = [torch.ones(n, dtype=torch.float32, device=dev) for _ in range(4)]
+        res = {}
+        for name, moved, op in (("write", 1, lambda i: bufs[i % 4].fill_(1.0)),
+                                ("read", 1, lambda i: bufs[i % 4].sum()),
+                                ("copy", 2, lambda i: bufs[(i + 1) % 4].copy_(bufs[i % 4]))):
+            ts = []
+            for i in range(24):
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record()
+                op(i)
+                e1.record()
+                e1.synchronize()
+                if i >= 4:
+                    ts.append(e0.elapsed_time(e1) * 1e-3)
+            med = float(np.median(ts))
+            res[name] = {"gbs": round(moved * n * 4 / med / 1e9, 1), "us": round(med * 1e6, 1)}
+        print(json.dumps({"stream_ceilings": res, "bytes_per_buffer": n * 4,
+                          "note": "torch fill_ / sum / copy_ on rotated 256 MiB buffers, median of 20"}))
+        return
     if args.calibrate_copy:
         n = args.calibrate_copy * 2**20 // 4
         src = torch.ones(n, dtype=torch.float32, device=dev)
