@@ -213,6 +213,12 @@ def device_memory_report(dev: int) -> dict:
             vals[name] = v.value if hip.hipDeviceGetAttribute(ctypes.byref(v), attr, dev) == 0 else None
     except OSError as e:
         return {"error": str(e)}
+    # the enum values are those of ROCm 7; a runtime that numbers them
+    # differently would answer another attribute: keep only plausible values
+    if not (vals["bus_width_bits"] and 256 <= vals["bus_width_bits"] <= 65536):
+        vals["bus_width_bits"] = None
+    if not (vals["memory_clock_khz"] and 100_000 <= vals["memory_clock_khz"] <= 20_000_000):
+        vals["memory_clock_khz"] = None
     if vals["bus_width_bits"] and vals["memory_clock_khz"]:
         vals["derived_peak_gbs"] = round(4.0 * vals["memory_clock_khz"] * 1e3 * vals["bus_width_bits"] / 8 / 1e9, 1)
     vals["nominal_peak_gbs"] = HBM_PEAK_GBS
