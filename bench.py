@@ -19,11 +19,17 @@ launch-carried events lengthen the gaps between kernels.
 
 Prints ONE JSON line.  `value` is compulsory bytes (x + W + out) per second
 in GB/s; the line also carries calls/s, the fraction of the 8 TB/s HBM peak,
-a `roofline` entry for the longest-running kernel (its algorithmic bytes per
-launch over its average launch time), a `mix` entry for the matrix-core
-channel mix (its flops against the fp32 MFMA peak) when the workload uses
-it, and a `cpu_baseline` entry: the fp64 CPU oracle timed on this host on a
-bounded sample.
+a `roofline` entry for the longest-running kernel (its share of x + W + out
+per launch over its average launch time: the first transform reads x, the
+mix reads W, the last transform writes out; the truncated spectra it also
+moves appear as `spectra_ratio`), a `whole_call` entry (x + W + out over the
+call time), a `mix` entry for the matrix-core channel mix (8 flops per
+complex multiply-add against the fp32 MFMA peak, and the 6 the 3M form
+executes) when the workload uses it, a `cpu_baseline` entry (the fp64 CPU
+oracle timed on this host on a bounded sample), `parity` (the benched
+output against that oracle output), and `workloads`: the other four
+workloads timed in the same run (ms per call, GB/s, calls/s, per-kernel
+times) with their parity against the oracle on a sample of batch items.
 
 --pass backward times both gradients of a real loss (compulsory bytes: x, W,
 dL/dout read, dL/dx, dL/dW written); --pass layer times the operator with
@@ -109,6 +115,27 @@ def kernel_bytes(name: str, cfg, backward: bool = False) -> int:
     return table[name.split(":")[0]]
 
 
+def compulsory_share(name: str, cfg, backward: bool = False) -> int:
+    """The kernel's share of the compulsory bytes x + W + out: the first
+    transform reads x, the mix reads W, the last transform writes out (the
+    truncated spectra between kernels are not compulsory).  Kernels that
+    only move spectra (the column passes of the staged schedule) have none."""
+    if backward and not name.endswith(":2"):
+        import dataclasses
+        cfg = dataclasses.replace(cfg, Cin=cfg.Cout, Cout=cfg.Cin)
+    n_in = 4 * int(np.prod(cfg.x_shape))
+    n_out = 4 * int(np.prod(cfg.out_shape))
+    wb = 8 * int(np.prod(cfg.w_shape))
+    base = name.split(":")[0]
+    share = {
+        "fwd2d": n_in, "rows_fwd": n_in, "fwd2d_diag": n_in,
+        "mix_mfma": wb, "mix_valu": wb, "mix_mfma_adj": wb, "mix_fused": wb,
+        "inv2d": n_out, "rows_inv": n_out, "inv2d_gelu": 2 * n_out, "rows_inv_gelu": 2 * n_out,
+        "wgrad": wb, "wgrad_reduce": 0,
+    }
+    return share.get(base, 0)
+
+
 def load_traffic(kernel: str, workload: str):
     """Measured HBM bytes per launch from committed rocprofv3 counter runs, if
     they were taken on the current kernel sources; else None."""
@@ -136,7 +163,8 @@ def load_traffic(kernel: str, workload: str):
 def cpu_baseline(cfg, x, w, budget_s: float = 12.0, g=None, compulsory=None, layer=None, mask=None, kernel=None):
     """Time the fp64 oracle (as it stands) on this host on a bounded sample
     (the backward pass when the output gradient g is given, the operator with
-    the layer tail when layer = (bias, branch) is)."""
+    the layer tail when layer = (bias, branch) is).  Returns the baseline
+    entry, the oracle's output on the first nb batch items and nb."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -175,7 +203,7 @@ def cpu_baseline(cfg, x, w, budget_s: float = 12.0, g=None, compulsory=None, lay
     reps = 0
     t0 = time.perf_counter()
     while True:
-        call(nb)
+        ref = call(nb)
         reps += 1
         el = time.perf_counter() - t0
         if el >= budget_s * 0.5 or reps >= 3:
@@ -192,7 +220,7 @@ def cpu_baseline(cfg, x, w, budget_s: float = 12.0, g=None, compulsory=None, lay
         "calls_per_s": round(1.0 / call_time, 6),
         "os_cpu_count": os.cpu_count(),
         "affinity_cpus": len(os.sched_getaffinity(0)),
-    }
+    }, ref, nb
 
 
 def device_memory_report(dev: int) -> dict:
@@ -225,6 +253,201 @@ def device_memory_report(dev: int) -> dict:
     return vals
 
 
+def build_step(fno, torch, dev, cfg, which, variant, x_np, w_np, nsets):
+    """Device buffers and the step function of one workload and pass.  Returns
+    (step, outs, compulsory, extras) with extras holding the host arrays the
+    oracle needs for that pass."""
+    xs = [torch.from_numpy(x_np).to(dev)]
+    for _ in range(nsets - 1):
+        xs.append(xs[0].clone())
+    outs = [torch.empty(cfg.out_shape, dtype=torch.float32, device=dev) for _ in range(nsets)]
+    w = torch.from_numpy(w_np).to(dev)
+    compulsory = cfg.compulsory_bytes
+    extras = {"g": None, "layer": None, "mask": None, "kernel": None, "lens": None, "touched_extra": 0}
+    if which == "backward":
+        # step: both gradients of a real loss, given a synthetic dL/dout of the
+        # output's shape; compulsory bytes: x, w, dL/dout read, dL/dx, dL/dw written
+        g_np = np.random.default_rng(1).uniform(-1.0, 1.0, size=cfg.out_shape).astype(np.float32)
+        gs = [torch.from_numpy(g_np).to(dev)]
+        for _ in range(nsets - 1):
+            gs.append(gs[0].clone())
+        compulsory = 2 * int(x_np.nbytes) + 2 * int(w_np.nbytes) + int(g_np.nbytes)
+        gxs = [torch.empty_like(xs[0]) for _ in range(nsets)]
+        gw = torch.empty_like(w)
+        extras["g"] = g_np
+        extras["touched_extra"] = nsets * x_np.nbytes + w_np.nbytes
+        if cfg.kind == "1d":
+            step = lambda i: fno.fno_spectral_conv1d_backward(xs[i % nsets], w, gs[i % nsets], cfg.my,
+                                                              grad_x=gxs[i % nsets], grad_w=gw)
+        else:
+            step = lambda i: fno.fno_spectral_conv2d_backward(xs[i % nsets], w, gs[i % nsets], cfg.mx, cfg.my,
+                                                              grad_x=gxs[i % nsets], grad_w=gw)
+        outs = gxs
+    elif which == "layer":
+        # step: out = gelu(conv + bias[o] + branch), branch an output-sized
+        # tensor; compulsory bytes: x, w, bias, branch read, out written
+        rng = np.random.default_rng(2)
+        br_np = rng.standard_normal(cfg.out_shape).astype(np.float32)
+        bias_np = rng.standard_normal(cfg.Cout).astype(np.float32)
+        extras["layer"] = (bias_np, br_np)
+        bias = torch.from_numpy(bias_np).to(dev)
+        brs = [torch.from_numpy(br_np).to(dev)]
+        for _ in range(nsets - 1):
+            brs.append(brs[0].clone())
+        compulsory = cfg.compulsory_bytes + int(br_np.nbytes) + 4 * cfg.Cout
+        extras["touched_extra"] = nsets * 4 * int(np.prod(cfg.out_shape))
+        if cfg.kind == "1d":
+            step = lambda i: fno.fno_spectral_conv1d_gelu(xs[i % nsets], w, cfg.my, bias=bias, branch=brs[i % nsets],
+                                                          out=outs[i % nsets])
+        else:
+            step = lambda i: fno.fno_spectral_conv2d_gelu(xs[i % nsets], w, cfg.mx, cfg.my, bias=bias,
+                                                          branch=brs[i % nsets], out=outs[i % nsets])
+    elif which == "filter":
+        # step: out = C2R(truncate(R2C(x)) * mask); compulsory bytes: x and
+        # the mask read, out written
+        rng = np.random.default_rng(3)
+        mshape = (cfg.my, cfg.Cin) if cfg.kind == "1d" else (2, cfg.mx, cfg.my, cfg.Cin)
+        mask_np = (rng.standard_normal(mshape) + 1j * rng.standard_normal(mshape)).astype(np.complex64)
+        mask = torch.from_numpy(mask_np).to(dev)
+        extras["mask"] = mask_np
+        compulsory = 2 * int(x_np.nbytes) + int(mask_np.nbytes)
+        if cfg.kind == "1d":
+            step = lambda i: fno.fno_spectral_filter1d(xs[i % nsets], mask, cfg.my, out=outs[i % nsets])
+        else:
+            step = lambda i: fno.fno_spectral_filter2d(xs[i % nsets], mask, cfg.mx, cfg.my, out=outs[i % nsets])
+    elif which == "linconv":
+        # step: out = crop(C2R(R2C(pad x) * wspec)), 'same' output; the weight
+        # spectrum of the kernel is prepared once (kernels are fixed across
+        # calls); compulsory bytes: x and the kernel read, out written
+        rng = np.random.default_rng(4)
+        kshape = (cfg.Cout, cfg.Cin, 7) if cfg.kind == "1d" else (cfg.Cout, cfg.Cin, 5, 5)
+        k_np = (rng.standard_normal(kshape) / np.sqrt(np.prod(kshape[1:]))).astype(np.float32)
+        kd = torch.from_numpy(k_np).to(dev)
+        compulsory = cfg.compulsory_bytes - int(w_np.nbytes) + int(k_np.nbytes)
+        extras["kernel"] = k_np
+        lens = ([fno.fno_linear_conv_length(cfg.W, 7)] if cfg.kind == "1d"
+                else [fno.fno_linear_conv_length(cfg.H, 5), fno.fno_linear_conv_length(cfg.W, 5)])
+        if 0 in lens:
+            sys.exit(f"--pass linconv: the padded length of workload {cfg.name} exceeds the 4096-point transform")
+        extras["lens"] = lens
+        if cfg.kind == "1d":
+            wspec = fno.fno_linear_conv1d_prepare(kd, cfg.W)
+            step = lambda i: fno.fno_linear_conv1d(xs[i % nsets], kd, wspec=wspec, out=outs[i % nsets])
+        else:
+            wspec = fno.fno_linear_conv2d_prepare(kd, cfg.H, cfg.W)
+            step = lambda i: fno.fno_linear_conv2d(xs[i % nsets], kd, wspec=wspec, out=outs[i % nsets])
+    elif cfg.kind == "1d":
+        fn = fno.fno_spectral_conv1d if variant == "fused" else fno.fno_spectral_conv1d_unfused
+        step = lambda i: fn(xs[i % nsets], w, cfg.my, out=outs[i % nsets])
+    else:
+        fn = fno.fno_spectral_conv2d if variant == "fused" else fno.fno_spectral_conv2d_unfused
+        step = lambda i: fn(xs[i % nsets], w, cfg.mx, cfg.my, out=outs[i % nsets])
+    return step, outs, compulsory, extras
+
+
+def buffer_sets(cfg) -> int:
+    """Enough (x, out) sets that the rotation exceeds the 256 MiB last-level cache."""
+    set_bytes = 4 * (np.prod(cfg.x_shape) + np.prod(cfg.out_shape))
+    return int(max(1, min(4, -(-3 * 256 * 2**20 // set_bytes))))
+
+
+def time_steps(fno, torch, stream, step, steps, warmup):
+    """Warm up, then time `steps` plain steps between two HIP events on the
+    call's stream (ms per step), then the same steps again with every kernel
+    launched with its own start / stop events (per-kernel times)."""
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    kernels = fno.fno_last_kernels()
+    # a kernel that runs more than once per step gets its launch number
+    seen = {}
+    for j, k in enumerate(kernels):
+        seen[k] = seen.get(k, 0) + 1
+        if seen[k] > 1:
+            kernels[j] = f"{k}:{seen[k]}"
+    nk = len(kernels)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * nk)] for _ in range(steps)]
+    for row in evs:                      # torch creates the HIP event on first record
+        for e in row:
+            e.record(stream)
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record(stream)
+    for i in range(steps):
+        step(i)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    # launch-carried events change the gaps between kernels, so this pass
+    # does not set ms_per_step
+    for i in range(steps):
+        fno.fno_set_timing_events(evs[i])
+        step(i)
+    torch.cuda.synchronize()
+    fno.fno_set_timing_events(None)
+    ms = start.elapsed_time(stop) / steps
+    per_kernel_ms = [float(np.mean([evs[i][2 * k].elapsed_time(evs[i][2 * k + 1]) for i in range(steps)]))
+                     for k in range(nk)]
+    spans_us = [evs[i][0].elapsed_time(evs[i][2 * nk - 1]) * 1e3 for i in range(steps)]
+    return ms, kernels, per_kernel_ms, spans_us, wall
+
+
+def oracle_out(cfg, x, w, nb):
+    import oracle
+    if cfg.kind == "1d":
+        return oracle.spectral_conv1d_ref(x[:nb], w, cfg.my)
+    return oracle.spectral_conv2d_ref(x[:nb], w, cfg.mx, cfg.my)
+
+
+def parity(got, ref) -> dict:
+    """Relative L2 and max-abs error (relative to max|ref|) of the GPU output
+    against the oracle on the same batch items."""
+    g = got.astype(np.float64)
+    rel = float(np.linalg.norm((g - ref).ravel()) / max(np.linalg.norm(ref.ravel()), 1e-300))
+    mx = float(np.max(np.abs(g - ref)) / max(np.max(np.abs(ref)), 1e-300))
+    return {"rel_l2": float(f"{rel:.3e}"), "max_abs_rel": float(f"{mx:.3e}"),
+            "pass": bool(rel <= 1e-5 and mx <= 1e-4)}
+
+
+def workload_summary(fno, torch, dev, stream, name, steps, warmup, oracle_budget_s=2.0) -> dict:
+    """ms per call, GB/s, HBM %, calls/s and per-kernel times of the plain
+    operator on workload `name`, plus its parity against the oracle on as many
+    batch items as ~oracle_budget_s of oracle time allows."""
+    cfg = CONFIGS[name]
+    x_np, w_np = make_inputs(cfg, 0)
+    nsets = buffer_sets(cfg)
+    step, outs, compulsory, _ = build_step(fno, torch, dev, cfg, "forward", "fused", x_np, w_np, nsets)
+    ms, kernels, pk, _, _ = time_steps(fno, torch, stream, step, steps, warmup)
+    gbs = compulsory / (ms * 1e-3) / 1e9
+    set_bytes = 4 * (np.prod(cfg.x_shape) + np.prod(cfg.out_shape))
+    resident = bool(nsets * set_bytes + w_np.nbytes <= 256 * 2**20)
+    got = outs[(steps - 1) % nsets][:1].cpu().numpy()
+    t0 = time.perf_counter()
+    ref = oracle_out(cfg, x_np, w_np, 1)
+    t1 = time.perf_counter() - t0
+    nb = int(max(1, min(cfg.B, oracle_budget_s / max(t1, 1e-3))))
+    if nb > 1:
+        got = outs[(steps - 1) % nsets][:nb].cpu().numpy()
+        ref = oracle_out(cfg, x_np, w_np, nb)
+    res = {
+        "workload": f"{cfg.name}: {cfg.describe()}",
+        "ms_per_step": round(ms, 6),
+        "calls_per_s": round(1e3 / ms, 3),
+        "gbs": round(gbs, 3),
+        "hbm_pct": round(100.0 * gbs / HBM_PEAK_GBS, 3),
+        "cache_resident": resident,
+        "kernels_us": {k: round(t * 1e3, 3) for k, t in zip(kernels, pk)},
+        "parity": dict(parity(got, ref), batch_items=nb),
+    }
+    if resident:
+        res["note"] = "every buffer fits the 256 MiB last-level cache: GB/s is not an HBM rate; calls/s is the figure"
+    del outs
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -240,6 +463,8 @@ def main():
                          "convolution with a 5x5 (1D: 7-tap) kernel, 'same' output, weight spectrum prepared "
                          "once outside the timed region")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="skip the other four workloads (timed and parity-checked in the same run by default)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--stream-ceilings", action="store_true",
                     help="time torch's own write (fill_), read (sum) and copy (copy_) kernels over rotated "
@@ -296,138 +521,13 @@ def main():
         return
     cfg = CONFIGS[args.workload]
     x_np, w_np = make_inputs(cfg, 0)
-
-    # enough (x, out) sets that the rotation exceeds the 256 MiB last-level cache
+    nsets = buffer_sets(cfg)
     set_bytes = 4 * (np.prod(cfg.x_shape) + np.prod(cfg.out_shape))
-    nsets = int(max(1, min(4, -(-3 * 256 * 2**20 // set_bytes))))
-    xs = [torch.from_numpy(x_np).to(dev)]
-    for _ in range(nsets - 1):
-        xs.append(xs[0].clone())
-    outs = [torch.empty(cfg.out_shape, dtype=torch.float32, device=dev) for _ in range(nsets)]
-    w = torch.from_numpy(w_np).to(dev)
-
-    compulsory = cfg.compulsory_bytes
-    g_np = None
-    layer_np = None
-    filter_np = None
-    linconv_np = None
-    if args.which == "backward":
-        # step: both gradients of a real loss, given a synthetic dL/dout of the
-        # output's shape; compulsory bytes: x, w, dL/dout read, dL/dx, dL/dw written
-        g_np = np.random.default_rng(1).uniform(-1.0, 1.0, size=cfg.out_shape).astype(np.float32)
-        gs = [torch.from_numpy(g_np).to(dev)]
-        for _ in range(nsets - 1):
-            gs.append(gs[0].clone())
-        compulsory = 2 * int(x_np.nbytes) + 2 * int(w_np.nbytes) + int(g_np.nbytes)
-        gxs = [torch.empty_like(xs[0]) for _ in range(nsets)]
-        gw = torch.empty_like(w)
-        if cfg.kind == "1d":
-            step = lambda i: fno.fno_spectral_conv1d_backward(xs[i % nsets], w, gs[i % nsets], cfg.my,
-                                                              grad_x=gxs[i % nsets], grad_w=gw)
-        else:
-            step = lambda i: fno.fno_spectral_conv2d_backward(xs[i % nsets], w, gs[i % nsets], cfg.mx, cfg.my,
-                                                              grad_x=gxs[i % nsets], grad_w=gw)
-    elif args.which == "layer":
-        # step: out = gelu(conv + bias[o] + branch), branch an output-sized
-        # tensor; compulsory bytes: x, w, bias, branch read, out written
-        rng = np.random.default_rng(2)
-        br_np = rng.standard_normal(cfg.out_shape).astype(np.float32)
-        bias_np = rng.standard_normal(cfg.Cout).astype(np.float32)
-        layer_np = (bias_np, br_np)
-        bias = torch.from_numpy(bias_np).to(dev)
-        brs = [torch.from_numpy(br_np).to(dev)]
-        for _ in range(nsets - 1):
-            brs.append(brs[0].clone())
-        compulsory = cfg.compulsory_bytes + int(br_np.nbytes) + 4 * cfg.Cout
-        if cfg.kind == "1d":
-            step = lambda i: fno.fno_spectral_conv1d_gelu(xs[i % nsets], w, cfg.my, bias=bias, branch=brs[i % nsets],
-                                                          out=outs[i % nsets])
-        else:
-            step = lambda i: fno.fno_spectral_conv2d_gelu(xs[i % nsets], w, cfg.mx, cfg.my, bias=bias,
-                                                          branch=brs[i % nsets], out=outs[i % nsets])
-    elif args.which == "filter":
-        # step: out = C2R(truncate(R2C(x)) * mask); compulsory bytes: x and
-        # the mask read, out written
-        rng = np.random.default_rng(3)
-        mshape = (cfg.my, cfg.Cin) if cfg.kind == "1d" else (2, cfg.mx, cfg.my, cfg.Cin)
-        mask_np = (rng.standard_normal(mshape) + 1j * rng.standard_normal(mshape)).astype(np.complex64)
-        mask = torch.from_numpy(mask_np).to(dev)
-        filter_np = mask_np
-        compulsory = 2 * int(x_np.nbytes) + int(mask_np.nbytes)
-        if cfg.kind == "1d":
-            step = lambda i: fno.fno_spectral_filter1d(xs[i % nsets], mask, cfg.my, out=outs[i % nsets])
-        else:
-            step = lambda i: fno.fno_spectral_filter2d(xs[i % nsets], mask, cfg.mx, cfg.my, out=outs[i % nsets])
-    elif args.which == "linconv":
-        # step: out = crop(C2R(R2C(pad x) * wspec)), 'same' output; the weight
-        # spectrum of the kernel is prepared once (kernels are fixed across
-        # calls); compulsory bytes: x and the kernel read, out written
-        rng = np.random.default_rng(4)
-        kshape = (cfg.Cout, cfg.Cin, 7) if cfg.kind == "1d" else (cfg.Cout, cfg.Cin, 5, 5)
-        k_np = (rng.standard_normal(kshape) / np.sqrt(np.prod(kshape[1:]))).astype(np.float32)
-        kd = torch.from_numpy(k_np).to(dev)
-        compulsory = cfg.compulsory_bytes - int(w_np.nbytes) + int(k_np.nbytes)
-        linconv_np = k_np
-        lens = ([fno.fno_linear_conv_length(cfg.W, 7)] if cfg.kind == "1d"
-                else [fno.fno_linear_conv_length(cfg.H, 5), fno.fno_linear_conv_length(cfg.W, 5)])
-        if 0 in lens:
-            sys.exit(f"--pass linconv: the padded length of workload {cfg.name} exceeds the 4096-point transform")
-        if cfg.kind == "1d":
-            wspec = fno.fno_linear_conv1d_prepare(kd, cfg.W)
-            step = lambda i: fno.fno_linear_conv1d(xs[i % nsets], kd, wspec=wspec, out=outs[i % nsets])
-        else:
-            wspec = fno.fno_linear_conv2d_prepare(kd, cfg.H, cfg.W)
-            step = lambda i: fno.fno_linear_conv2d(xs[i % nsets], kd, wspec=wspec, out=outs[i % nsets])
-    elif cfg.kind == "1d":
-        fn = fno.fno_spectral_conv1d if args.variant == "fused" else fno.fno_spectral_conv1d_unfused
-        step = lambda i: fn(xs[i % nsets], w, cfg.my, out=outs[i % nsets])
-    else:
-        fn = fno.fno_spectral_conv2d if args.variant == "fused" else fno.fno_spectral_conv2d_unfused
-        step = lambda i: fn(xs[i % nsets], w, cfg.mx, cfg.my, out=outs[i % nsets])
-
+    step, outs, compulsory, extras = build_step(fno, torch, dev, cfg, args.which, args.variant, x_np, w_np, nsets)
     stream = torch.cuda.current_stream(dev)
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    kernels = fno.fno_last_kernels()
-    # a kernel that runs more than once per step gets its launch number
-    seen = {}
-    for j, k in enumerate(kernels):
-        seen[k] = seen.get(k, 0) + 1
-        if seen[k] > 1:
-            kernels[j] = f"{k}:{seen[k]}"
+    ms_per_step, kernels, per_kernel_ms, spans_us, wall = time_steps(fno, torch, stream, step, args.steps,
+                                                                     args.warmup)
     nk = len(kernels)
-    # start / stop events that every kernel of every timed step launches with
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * nk)] for _ in range(args.steps)]
-    for row in evs:                      # torch creates the HIP event on first record
-        for e in row:
-            e.record(stream)
-    start = torch.cuda.Event(enable_timing=True)
-    stop = torch.cuda.Event(enable_timing=True)
-
-    # Pass 1 (the figure of merit): K plain steps between two events.
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    start.record(stream)
-    for i in range(args.steps):
-        step(i)
-    stop.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    # Pass 2: the same K steps with every kernel launched with its own start /
-    # stop events, for the per-kernel times.  Launch-carried events change
-    # the gaps between kernels, so this pass does not set ms_per_step.
-    for i in range(args.steps):
-        fno.fno_set_timing_events(evs[i])
-        step(i)
-    torch.cuda.synchronize()
-    fno.fno_set_timing_events(None)
-
-    ms_per_step = start.elapsed_time(stop) / args.steps
-    per_kernel_ms = [float(np.mean([evs[i][2 * k].elapsed_time(evs[i][2 * k + 1]) for i in range(args.steps)]))
-                     for k in range(nk)]
-    # per-step span in pass 2 (first kernel's start to last kernel's stop)
-    spans_us = [evs[i][0].elapsed_time(evs[i][2 * nk - 1]) * 1e3 for i in range(args.steps)]
     dom = int(np.argmax(per_kernel_ms))
     dom_name = kernels[dom]
     # the linear convolution runs on the padded grid at full modes: its kernels'
@@ -435,22 +535,35 @@ def main():
     kcfg = cfg
     if args.which == "linconv":
         import dataclasses
+        lens = extras["lens"]
         if cfg.kind == "1d":
             kcfg = dataclasses.replace(cfg, W=lens[0], my=lens[0] // 2 + 1)
         else:
             kcfg = dataclasses.replace(cfg, H=lens[0], W=lens[1], mx=lens[0] // 2, my=lens[1] // 2 + 1)
-    dom_bytes = kernel_bytes(dom_name, kcfg, args.which == "backward")
-    achieved = dom_bytes / (per_kernel_ms[dom] * 1e-3) / 1e9
+    bwd = args.which == "backward"
+    # Roofline of the longest kernel on its share of the compulsory bytes
+    # (x + W + out: the first transform's x, the mix's W, the last
+    # transform's out); the truncated spectra it also moves are reported as
+    # the ratio of all its bytes to that share.
+    dom_share = compulsory_share(dom_name, cfg, bwd) if args.which in ("forward", "backward", "layer") else 0
+    dom_all = kernel_bytes(dom_name, kcfg, bwd)
+    dom_alg = dom_share if dom_share > 0 else dom_all
+    achieved = dom_alg / (per_kernel_ms[dom] * 1e-3) / 1e9
     traffic = load_traffic(dom_name, cfg.name if args.which == "forward" else f"{cfg.name}/{args.which}")
-
     gbs = compulsory / (ms_per_step * 1e-3) / 1e9
-    # bytes of all buffers the timed steps touch (the backward adds dL/dx per
-    # set and dL/dw)
-    touched = nsets * set_bytes + w_np.nbytes
-    if args.which == "backward":
-        touched += nsets * x_np.nbytes + w_np.nbytes
-    elif args.which == "layer":
-        touched += nsets * 4 * int(np.prod(cfg.out_shape))
+    # bytes of all buffers the timed steps touch
+    touched = nsets * set_bytes + w_np.nbytes + extras["touched_extra"]
+    per_kernel = {}
+    for k, t in zip(kernels, per_kernel_ms):
+        share = compulsory_share(k, cfg, bwd) if args.which in ("forward", "backward", "layer") else 0
+        allb = kernel_bytes(k, kcfg, bwd)
+        per_kernel[k] = {
+            "us": round(t * 1e3, 3),
+            "compulsory_bytes": share,
+            "frac_compulsory": round(share / (t * 1e-3) / 1e9 / HBM_PEAK_GBS, 5) if share else None,
+            "all_bytes": allb,
+            "gbs_all_bytes": round(allb / (t * 1e-3) / 1e9, 3),
+        }
     line = {
         "metric": "spectral-conv GB/s (HBM % of peak) and layer calls/s vs fp64 CPU oracle",
         "value": round(gbs, 3),
@@ -481,6 +594,7 @@ def main():
         "wall_s_timed": round(wall, 4),
         "kernels": {k: round(t * 1e3, 3) for k, t in zip(kernels, per_kernel_ms)},
         "kernels_unit": "us per launch (start/stop events carried by each launch)",
+        "kernel_bytes": per_kernel,
         "step_span_us": {"median": round(float(np.median(spans_us)), 3), "min": round(float(np.min(spans_us)), 3),
                          "note": "first kernel start to last kernel stop of each step, event-carrying pass"},
         "roofline": {
@@ -491,32 +605,60 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 5),
             "traffic": traffic,
-            "algorithmic_bytes": dom_bytes,
+            "algorithmic_bytes": dom_alg,
+            "algorithmic_bytes_note": ("the kernel's share of x + W + out" if dom_share > 0 else
+                                       "all bytes the kernel must move (it has no share of x + W + out)"),
+            "bytes_incl_spectra": dom_all,
+            "spectra_ratio": round(dom_all / dom_alg, 4),
             "avg_launch_us": round(per_kernel_ms[dom] * 1e3, 3),
+        },
+        "whole_call": {
+            "achieved": round(gbs, 3),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(gbs / HBM_PEAK_GBS, 5),
+            "bytes_incl_spectra": int(sum(kernel_bytes(k, kcfg, bwd) for k in kernels)),
+            "spectra_ratio": round(sum(kernel_bytes(k, kcfg, bwd) for k in kernels) / compulsory, 4),
         },
     }
     if "mix_mfma" in kernels and args.which != "backward":
-        # the matrix-core stage against the fp32 MFMA peak: executed flops of
-        # the 3M form (three real GEMMs, 2 flops per multiply-add), and the
-        # algorithmic count of 8 flops per complex multiply-add
+        # the matrix-core stage against the fp32 MFMA peak: the method's count
+        # of 8 flops per complex multiply-add (frac), and what the 3M form
+        # executes (three real products, 6 flops per complex multiply-add)
         k = kernels.index("mix_mfma")
         macs = kcfg.B * kcfg.Cin * kcfg.Cout * (kcfg.my if kcfg.kind == "1d" else 2 * kcfg.mx * kcfg.my)
         t = per_kernel_ms[k] * 1e-3
         line["mix"] = {
             "kernel": "mix_mfma",
             "bound": "mfma",
-            "achieved": round(6.0 * macs / t / 1e12, 3),
+            "achieved": round(8.0 * macs / t / 1e12, 3),
             "peak": MFMA_FP32_PEAK_TFLOPS,
             "unit": "TFLOP/s",
-            "frac": round(6.0 * macs / t / 1e12 / MFMA_FP32_PEAK_TFLOPS, 5),
-            "flops_executed_3m": 6 * macs,
+            "frac": round(8.0 * macs / t / 1e12 / MFMA_FP32_PEAK_TFLOPS, 5),
+            "flops_note": "achieved/frac count 8 flops per complex multiply-add; *_executed_3m count the 6 the 3M form runs",
             "flops_complex_8": 8 * macs,
-            "hbm_gbs": round(kernel_bytes("mix_mfma", kcfg) / t / 1e9, 3),
+            "flops_executed_3m": 6 * macs,
+            "achieved_executed_3m": round(6.0 * macs / t / 1e12, 3),
+            "frac_executed_3m": round(6.0 * macs / t / 1e12 / MFMA_FP32_PEAK_TFLOPS, 5),
+            "w_gbs": round(compulsory_share("mix_mfma", kcfg) / t / 1e9, 3),
+            "all_bytes_gbs": round(kernel_bytes("mix_mfma", kcfg) / t / 1e9, 3),
             "avg_launch_us": round(per_kernel_ms[k] * 1e3, 3),
         }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(cfg, x_np, w_np, args.cpu_budget, g=g_np, compulsory=compulsory,
-                                            layer=layer_np, mask=filter_np, kernel=linconv_np)
+        cb, ref, nb = cpu_baseline(cfg, x_np, w_np, args.cpu_budget, g=extras["g"], compulsory=compulsory,
+                                   layer=extras["layer"], mask=extras["mask"], kernel=extras["kernel"])
+        line["cpu_baseline"] = cb
+        if args.which in ("forward", "layer", "filter", "linconv"):
+            # parity of the benched output (the last timed step's) on the
+            # batch items the oracle leg computed
+            got = outs[(args.steps - 1) % nsets][:nb].cpu().numpy()
+            line["parity"] = dict(parity(got, ref), batch_items=nb,
+                                  note="last timed step's output against the cpu_baseline leg's oracle output")
+    if not args.no_workloads and args.which == "forward" and args.variant == "fused":
+        del outs, step
+        torch.cuda.empty_cache()
+        line["workloads"] = {n: workload_summary(fno, torch, dev, stream, n, args.steps, args.warmup)
+                             for n in sorted(CONFIGS) if n != cfg.name}
     print(json.dumps(line), flush=True)
 
 
