@@ -113,7 +113,16 @@ __global__ __launch_bounds__(kMixThreads) void k_mix_mfma(const float2* __restri
     // X[b0 + sbl][chunk * 8 + sil][m0 + 4 * shalf + q], q < 4.  Clamped
     // indices only feed results that are never stored, except channels past
     // Cin, which are zeroed when the chunk is written to LDS.
+    // Chunk order: every workgroup walks its channel chunks rotated by an
+    // even offset of its own.  In lock-step, all workgroups would read the
+    // weight rows of the same chunk (the same offset modulo a mode's 32 KiB
+    // at c3) at once; on some devices' memory placements those reads pile
+    // onto a subset of the HBM channels (the kernel took 41 us instead of 30
+    // on such a device, 30 with the rotation).  The rotation changes only
+    // the order of the sum over input channels.
+    const int rot = (int)(blockIdx.x % (NCH / 2)) * 2;
     auto load_a = [&](const Tile& tl, int chunk, float2 (&av)[4]) __attribute__((always_inline)) {
+        chunk = (chunk + rot) % NCH;
         const int i = chunk * kMixKC + sil;
         const int ic = i < Cin ? i : Cin - 1;
         const int bl = RB == 2 ? sbl : sbl % kB;   // non-stagers repeat a stager's row (same lines)
@@ -134,6 +143,7 @@ __global__ __launch_bounds__(kMixThreads) void k_mix_mfma(const float2* __restri
         }
     };
     auto store_a = [&](int chunk, const float2 (&av)[4], float2* buf) __attribute__((always_inline)) {
+        chunk = (chunk + rot) % NCH;
         if (!stager) return;
         const bool iok = chunk * kMixKC + sil < Cin;
 #pragma unroll
@@ -144,6 +154,7 @@ __global__ __launch_bounds__(kMixThreads) void k_mix_mfma(const float2* __restri
     // = W[i][o_h + p], o_h = o0 + 32 h + 2 l16 (Cout is even on this path;
     // columns past Cout are clamped and never stored).
     auto load_w = [&](const Tile& tl, int chunk, float2 (&wv)[2 * NCB]) __attribute__((always_inline)) {
+        chunk = (chunk + rot) % NCH;
         const int mw = tl.m0 + wave < M ? tl.m0 + wave : M - 1;
         if constexpr (TW) {
             // conj(W[o][k]), k = chunk * 8 + 2 lk + s: one float4 per column
