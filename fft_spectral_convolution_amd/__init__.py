@@ -23,6 +23,7 @@ __all__ = [
     "library_path",
     "fno_version",
     "fno_status_string",
+    "fno_init",
     "fno_spectral_conv2d",
     "fno_spectral_conv1d",
     "fno_spectral_conv2d_unfused",
@@ -67,6 +68,7 @@ _SIGNATURES = {
     "fno_version": (_I, []),
     "fno_status_string": (ctypes.c_char_p, [_I]),
     "fno_last_hip_error": (_I, []),
+    "fno_init": (_I, []),
     "fno_spectral_conv2d": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P]),
     "fno_spectral_conv1d": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _P]),
     "fno_spectral_conv2d_unfused": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P]),
@@ -136,6 +138,12 @@ def fno_version() -> int:
 
 def fno_status_string(status: int) -> str:
     return lib().fno_status_string(status).decode()
+
+
+def fno_init() -> None:
+    """Build the current device's twiddle table now (a later call may then be
+    captured into a graph without an eager call first)."""
+    _check(lib().fno_init(), "fno_init")
 
 
 def _check(status: int, where: str) -> None:

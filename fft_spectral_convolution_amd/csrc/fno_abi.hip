@@ -26,16 +26,27 @@ constexpr int kVersion = 100;   // 0.1.0
 
 thread_local int g_last_hip_error = 0;
 
+// One internal workspace per (device, stream).  `use` is held by a call from
+// the moment it takes the buffer until its kernels are enqueued, so that a
+// second host thread calling on the same stream cannot free or replace the
+// buffer in between (a replacement then waits for that stream's work).
 struct Workspace {
     void* stream = nullptr;
     void* ptr = nullptr;
     size_t bytes = 0;
+    std::mutex use;
 };
 
 struct DeviceState {
     bool init = false;
     float2* twiddle = nullptr;     // kNMax entries exp(-2 pi i m / kNMax)
-    std::vector<Workspace> ws;     // internal grow-only workspace, one per stream
+    std::vector<std::unique_ptr<Workspace>> ws;   // internal grow-only workspaces, one per stream
+};
+
+// A call's hold on its stream's workspace (released when the call returns,
+// after its kernels are enqueued).
+struct WsLease {
+    std::unique_lock<std::mutex> lock;
 };
 
 std::mutex g_mutex;
@@ -84,7 +95,9 @@ int rec_end(hipStream_t, int rc) {
 
 int hip_fail(hipError_t e) {
     g_last_hip_error = (int)e;
-    return FNO_ERR_HIP;
+    // a launcher that would have had to build a table while the stream is
+    // being captured reports this code
+    return e == hipErrorStreamCaptureUnsupported ? FNO_ERR_CAPTURE : FNO_ERR_HIP;
 }
 
 bool is_pow2(int v) { return v > 0 && (v & (v - 1)) == 0; }
@@ -133,8 +146,10 @@ bool overlap(const void* a, size_t abytes, const void* b, size_t bbytes) {
 }
 
 // Per-device twiddle table, built in double precision with the exact integer
-// angle index m and rounded once to float.
-int device_state(DeviceState** out) {
+// angle index m and rounded once to float.  Building it allocates and copies,
+// which a stream under graph capture does not allow: the call then fails with
+// FNO_ERR_CAPTURE (fno_init or any eager call builds it beforehand).
+int device_state(DeviceState** out, void* stream) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return hip_fail(e);
@@ -143,6 +158,7 @@ int device_state(DeviceState** out) {
     if (!g_devices[dev]) g_devices[dev] = std::make_unique<DeviceState>();
     DeviceState& st = *g_devices[dev];
     if (!st.init) {
+        if (stream_capturing(static_cast<hipStream_t>(stream))) return FNO_ERR_CAPTURE;
         std::vector<float2> host(kNMax);
         for (int m = 0; m < kNMax; ++m) {
             const double ang = 2.0 * M_PI * (double)m / (double)kNMax;
@@ -164,24 +180,34 @@ int device_state(DeviceState** out) {
 }
 
 // The internal workspace of calls on `stream`: one grow-only buffer per
-// (device, stream), so that calls on different streams never share scratch.
-int internal_workspace(DeviceState* st, size_t bytes, void** ws, void* stream) {
-    std::lock_guard<std::mutex> lock(g_mutex);
-    if (bytes == 0) {
-        *ws = nullptr;
-        return FNO_OK;
-    }
+// (device, stream), so that calls on different streams never share scratch
+// (the FFT blog, sections 2.2 and 5.3: plans and their work areas are made
+// once and reused across calls).  On return the caller holds `lease` until it
+// has enqueued its kernels.  Growing a buffer first waits for the work already
+// enqueued on that stream (which may still read the old buffer), then frees
+// it; while the stream is being captured nothing is allocated or freed
+// (FNO_ERR_CAPTURE).
+int internal_workspace(WsLease& lease, DeviceState* st, size_t bytes, void** ws, void* stream) {
+    *ws = nullptr;
+    if (bytes == 0) return FNO_OK;
     Workspace* slot = nullptr;
-    for (auto& w : st->ws)
-        if (w.stream == stream) slot = &w;
-    if (!slot) {
-        st->ws.push_back(Workspace{stream, nullptr, 0});
-        slot = &st->ws.back();
+    {
+        std::lock_guard<std::mutex> lock(g_mutex);
+        for (auto& w : st->ws)
+            if (w->stream == stream) slot = w.get();
+        if (!slot) {
+            st->ws.push_back(std::make_unique<Workspace>());
+            slot = st->ws.back().get();
+            slot->stream = stream;
+        }
     }
+    lease.lock = std::unique_lock<std::mutex>(slot->use);
     if (slot->bytes < bytes) {
+        hipStream_t hs = static_cast<hipStream_t>(stream);
+        if (stream_capturing(hs)) return FNO_ERR_CAPTURE;
         if (slot->ptr) {
-            // in-flight work may still read the old buffer
-            hipError_t e = hipDeviceSynchronize();
+            // in-flight work on this stream may still read the old buffer
+            hipError_t e = hipStreamSynchronize(hs);
             if (e != hipSuccess) return hip_fail(e);
             (void)hipFree(slot->ptr);
             slot->ptr = nullptr;
@@ -466,10 +492,11 @@ int filter2d_common(const float* x, const void* mask, float* out, int B, int C, 
     if (rc) return rc;
     const Shape2d s = make2d(B, C, C, H, W, mx, my);
     DeviceState* st = nullptr;
-    rc = device_state(&st);
+    WsLease lease;
+    rc = device_state(&st, stream);
     if (rc) return rc;
     void* ws = nullptr;
-    rc = internal_workspace(st, best_ws_2d(s), &ws, stream);
+    rc = internal_workspace(lease, st, best_ws_2d(s), &ws, stream);
     if (rc) return rc;
     hipStream_t hs = static_cast<hipStream_t>(stream);
     rec_begin();
@@ -484,11 +511,12 @@ int filter1d_common(const float* x, const void* mask, float* out, int B, int C, 
     rc = check_conv(x, mask, out, xbytes, mbytes, xbytes);
     if (rc) return rc;
     DeviceState* st = nullptr;
-    rc = device_state(&st);
+    WsLease lease;
+    rc = device_state(&st, stream);
     if (rc) return rc;
     void* ws = nullptr;
     const size_t hb = align_up((size_t)B * C * modes * sizeof(float2));
-    rc = internal_workspace(st, 2 * hb, &ws, stream);
+    rc = internal_workspace(lease, st, 2 * hb, &ws, stream);
     if (rc) return rc;
     float2* xh = static_cast<float2*>(ws);
     float2* yh = reinterpret_cast<float2*>(static_cast<char*>(ws) + hb);
@@ -542,10 +570,11 @@ int linconv2d_prepare(const float* k, void* wspec, int Cin, int Cout, int H, int
     const size_t kh_b = align_up((size_t)io * M * sizeof(float2));
     const size_t r_b = small_path(s) ? 0 : align_up((size_t)io * PH * my * sizeof(float2));
     DeviceState* st = nullptr;
-    int rc = device_state(&st);
+    WsLease lease;
+    int rc = device_state(&st, stream);
     if (rc) return rc;
     void* ws = nullptr;
-    rc = internal_workspace(st, kp_b + kh_b + r_b, &ws, stream);
+    rc = internal_workspace(lease, st, kp_b + kh_b + r_b, &ws, stream);
     if (rc) return rc;
     float* kp = static_cast<float*>(ws);
     float2* khs = reinterpret_cast<float2*>(static_cast<char*>(ws) + kp_b);
@@ -588,10 +617,11 @@ int linconv2d_run(const float* x, const void* wspec, float* out, int B, int Cin,
     const size_t x_b = align_up((size_t)B * Cin * m * sizeof(float2));
     const size_t y_b = align_up((size_t)B * Cout * m * sizeof(float2));
     DeviceState* st = nullptr;
-    rc = device_state(&st);
+    WsLease lease;
+    rc = device_state(&st, stream);
     if (rc) return rc;
     void* ws = nullptr;
-    rc = internal_workspace(st, r_b + x_b + y_b, &ws, stream);
+    rc = internal_workspace(lease, st, r_b + x_b + y_b, &ws, stream);
     if (rc) return rc;
     float2* r = static_cast<float2*>(ws);
     float2* xh = reinterpret_cast<float2*>(static_cast<char*>(ws) + r_b);
@@ -632,10 +662,11 @@ int linconv1d_prepare(const float* k, void* wspec, int Cin, int Cout, int N, int
     const size_t kp_b = align_up((size_t)io * PN * sizeof(float));
     const size_t kh_b = align_up((size_t)io * modes * sizeof(float2));
     DeviceState* st = nullptr;
-    int rc = device_state(&st);
+    WsLease lease;
+    int rc = device_state(&st, stream);
     if (rc) return rc;
     void* ws = nullptr;
-    rc = internal_workspace(st, kp_b + kh_b, &ws, stream);
+    rc = internal_workspace(lease, st, kp_b + kh_b, &ws, stream);
     if (rc) return rc;
     float* kp = static_cast<float*>(ws);
     float2* khs = reinterpret_cast<float2*>(static_cast<char*>(ws) + kp_b);
@@ -669,10 +700,11 @@ int linconv1d_run(const float* x, const void* wspec, float* out, int B, int Cin,
     const size_t x_b = align_up((size_t)B * Cin * modes * sizeof(float2));
     const size_t y_b = align_up((size_t)B * Cout * modes * sizeof(float2));
     DeviceState* st = nullptr;
-    rc = device_state(&st);
+    WsLease lease;
+    rc = device_state(&st, stream);
     if (rc) return rc;
     void* ws = nullptr;
-    rc = internal_workspace(st, x_b + y_b, &ws, stream);
+    rc = internal_workspace(lease, st, x_b + y_b, &ws, stream);
     if (rc) return rc;
     float2* xh = static_cast<float2*>(ws);
     float2* yh = reinterpret_cast<float2*>(static_cast<char*>(ws) + x_b);
@@ -732,10 +764,11 @@ int conv2d_common(const float* x, const void* w, float* out, int B, int Cin, int
         if (need > 0 && (reinterpret_cast<uintptr_t>(user_ws) & 255u)) return FNO_ERR_ALIGN;
     }
     DeviceState* st = nullptr;
-    rc = device_state(&st);
+    WsLease lease;
+    rc = device_state(&st, stream);
     if (rc) return rc;
     if (!use_user_ws) {
-        rc = internal_workspace(st, need, &ws, stream);
+        rc = internal_workspace(lease, st, need, &ws, stream);
         if (rc) return rc;
     }
     hipStream_t hs = static_cast<hipStream_t>(stream);
@@ -764,10 +797,11 @@ int conv1d_common(const float* x, const void* w, float* out, int B, int Cin, int
         if (reinterpret_cast<uintptr_t>(user_ws) & 255u) return FNO_ERR_ALIGN;
     }
     DeviceState* st = nullptr;
-    rc = device_state(&st);
+    WsLease lease;
+    rc = device_state(&st, stream);
     if (rc) return rc;
     if (!use_user_ws) {
-        rc = internal_workspace(st, need, &ws, stream);
+        rc = internal_workspace(lease, st, need, &ws, stream);
         if (rc) return rc;
     }
     hipStream_t hs = static_cast<hipStream_t>(stream);
@@ -878,10 +912,11 @@ int backward2d_common(const float* x, const void* w, const float* g, float* gx, 
     if (rc) return rc;
     const Shape2d s = make2d(B, Cin, Cout, H, W, mx, my);
     DeviceState* st = nullptr;
-    rc = device_state(&st);
+    WsLease lease;
+    rc = device_state(&st, stream);
     if (rc) return rc;
     void* ws = nullptr;
-    rc = internal_workspace(st, backward_plan_2d(s).total(), &ws, stream);
+    rc = internal_workspace(lease, st, backward_plan_2d(s).total(), &ws, stream);
     if (rc) return rc;
     hipStream_t hs = static_cast<hipStream_t>(stream);
     rec_begin();
@@ -904,10 +939,11 @@ int backward1d_common(const float* x, const void* w, const float* g, float* gx, 
     const size_t wtb = align_up((size_t)modes * Cin * Cout * sizeof(float2));
     const size_t wgb = align_up(weight_grad_workspace(B, Cin, Cout, modes));
     DeviceState* st = nullptr;
-    rc = device_state(&st);
+    WsLease lease;
+    rc = device_state(&st, stream);
     if (rc) return rc;
     void* ws = nullptr;
-    rc = internal_workspace(st, 2 * xb + gb + wtb + wgb, &ws, stream);
+    rc = internal_workspace(lease, st, 2 * xb + gb + wtb + wgb, &ws, stream);
     if (rc) return rc;
     char* q = static_cast<char*>(ws);
     float2* xh = reinterpret_cast<float2*>(q);
@@ -978,11 +1014,17 @@ const char* fno_status_string(int status) {
         case FNO_ERR_NOMEM: return "device workspace allocation failed";
         case FNO_ERR_HIP: return "a HIP runtime call or kernel launch failed";
         case FNO_ERR_WORKSPACE: return "caller workspace missing or too small";
+        case FNO_ERR_CAPTURE: return "a table or workspace would have to be allocated while the stream is captured";
         default: return "unknown status";
     }
 }
 
 int fno_last_hip_error(void) { return g_last_hip_error; }
+
+int fno_init(void) {
+    DeviceState* st = nullptr;
+    return device_state(&st, nullptr);
+}
 
 int fno_set_timing_events(void** events, int n_events) {
     g_rec.events = (events && n_events > 0) ? events : nullptr;
@@ -1104,7 +1146,8 @@ int fno_forward2d(const float* x, void* xh, int B, int C, int H, int W, int mx, 
     if (overlap(x, xbytes, xh, hbytes)) return FNO_ERR_ALIAS;
     const Shape2d s = make2d(B, C, C, H, W, mx, my);
     DeviceState* st = nullptr;
-    rc = device_state(&st);
+    WsLease lease;
+    rc = device_state(&st, stream);
     if (rc) return rc;
     hipStream_t hs = static_cast<hipStream_t>(stream);
     float2* out = static_cast<float2*>(xh);
@@ -1113,7 +1156,7 @@ int fno_forward2d(const float* x, void* xh, int B, int C, int H, int W, int mx, 
         return rec_end(hs, run_forward2d_small(s, C, x, out, canonical_layout(C, 2 * mx * my), st->twiddle, hs));
     }
     void* ws = nullptr;
-    rc = internal_workspace(st, (size_t)B * C * H * my * sizeof(float2), &ws, stream);
+    rc = internal_workspace(lease, st, (size_t)B * C * H * my * sizeof(float2), &ws, stream);
     if (rc) return rc;
     rec_begin();
     return rec_end(hs, run_forward2d_staged(s, C, x, out, static_cast<float2*>(ws), st->twiddle, hs));
@@ -1129,7 +1172,8 @@ int fno_inverse2d(const void* yh, float* out, int B, int C, int H, int W, int mx
     if (overlap(out, obytes, yh, hbytes)) return FNO_ERR_ALIAS;
     const Shape2d s = make2d(B, C, C, H, W, mx, my);
     DeviceState* st = nullptr;
-    rc = device_state(&st);
+    WsLease lease;
+    rc = device_state(&st, stream);
     if (rc) return rc;
     hipStream_t hs = static_cast<hipStream_t>(stream);
     const float2* in = static_cast<const float2*>(yh);
@@ -1138,7 +1182,7 @@ int fno_inverse2d(const void* yh, float* out, int B, int C, int H, int W, int mx
         return rec_end(hs, run_inverse2d_small(s, C, in, out, canonical_layout(C, 2 * mx * my), st->twiddle, hs));
     }
     void* ws = nullptr;
-    rc = internal_workspace(st, (size_t)B * C * H * my * sizeof(float2), &ws, stream);
+    rc = internal_workspace(lease, st, (size_t)B * C * H * my * sizeof(float2), &ws, stream);
     if (rc) return rc;
     rec_begin();
     return rec_end(hs, run_inverse2d_staged(s, C, in, out, static_cast<float2*>(ws), st->twiddle, hs));
@@ -1166,7 +1210,8 @@ int fno_forward1d(const float* x, void* xh, int B, int C, int N, int modes, void
     if (overlap(x, (size_t)B * C * N * sizeof(float), xh, (size_t)B * C * modes * sizeof(float2)))
         return FNO_ERR_ALIAS;
     DeviceState* st = nullptr;
-    rc = device_state(&st);
+    WsLease lease;
+    rc = device_state(&st, stream);
     if (rc) return rc;
     const float scale = (float)(1.0 / std::sqrt((double)N));
     hipStream_t hs = static_cast<hipStream_t>(stream);
@@ -1195,7 +1240,8 @@ int fno_inverse1d(const void* yh, float* out, int B, int C, int N, int modes, vo
     if (overlap(out, (size_t)B * C * N * sizeof(float), yh, (size_t)B * C * modes * sizeof(float2)))
         return FNO_ERR_ALIAS;
     DeviceState* st = nullptr;
-    rc = device_state(&st);
+    WsLease lease;
+    rc = device_state(&st, stream);
     if (rc) return rc;
     const float scale = (float)(1.0 / std::sqrt((double)N));
     hipStream_t hs = static_cast<hipStream_t>(stream);

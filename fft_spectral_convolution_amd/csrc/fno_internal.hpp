@@ -47,6 +47,17 @@ hipError_t launch_kernel(K kernel, dim3 grid, dim3 block, size_t lds, hipStream_
     return hipGetLastError();
 }
 
+// True while `s` is being captured into a HIP graph (nothing may be
+// allocated, freed or copied synchronously then).
+inline bool stream_capturing(hipStream_t s) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(s, &cs) != hipSuccess) {
+        (void)hipGetLastError();
+        return false;
+    }
+    return cs != hipStreamCaptureStatusNone;
+}
+
 inline SpecLayout canonical_layout(int64_t C, int64_t M) { return SpecLayout{C * M, M, 8, (int)C}; }
 inline SpecLayout tiled_layout(int64_t C, int64_t M) {
     const int64_t nt = (M + 7) / 8;

@@ -298,7 +298,9 @@ bool make_plan(int n, MRPlan* p) {
 std::mutex g_tw_mutex;
 std::map<std::pair<int, int>, float2*> g_tw;
 
-hipError_t twiddles(int n, const float2** out) {
+// (a new table cannot be built while `s` is being captured: the allocation
+// and the synchronous copy are refused with hipErrorStreamCaptureUnsupported)
+hipError_t twiddles(int n, hipStream_t s, const float2** out) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
@@ -308,6 +310,7 @@ hipError_t twiddles(int n, const float2** out) {
         *out = it->second;
         return hipSuccess;
     }
+    if (stream_capturing(s)) return hipErrorStreamCaptureUnsupported;
     std::vector<float2> host(n);
     for (int m = 0; m < n; ++m) {
         const double a = -2.0 * M_PI * (double)m / (double)n;
@@ -340,7 +343,7 @@ hipError_t launch_rows_fwd_mr(const float* x, float2* y, int64_t nrows, int W, i
     MRPlan p;
     if (!make_plan(W, &p) || my > W / 2 + 1) return hipErrorInvalidValue;
     const float2* twn = nullptr;
-    hipError_t e = twiddles(W, &twn);
+    hipError_t e = twiddles(W, s, &twn);
     if (e != hipSuccess) return e;
     const int P = kLdsElems / W;
     const int64_t nb = ((nrows + 1) / 2 + P - 1) / P;
@@ -358,7 +361,7 @@ hipError_t launch_cols_fwd_mr(const float2* r, float2* xh, int64_t nimg, int H, 
     MRPlan p;
     if (!make_plan(H, &p) || 2 * mx > H) return hipErrorInvalidValue;
     const float2* twn = nullptr;
-    hipError_t e = twiddles(H, &twn);
+    hipError_t e = twiddles(H, s, &twn);
     if (e != hipSuccess) return e;
     const int cap = kLdsElems / H;
     const int kb = cap < my ? cap : my;
@@ -373,7 +376,7 @@ hipError_t launch_cols_inv_mr(const float2* yh, float2* r, int64_t nimg, int H, 
     MRPlan p;
     if (!make_plan(H, &p) || 2 * mx > H) return hipErrorInvalidValue;
     const float2* twn = nullptr;
-    hipError_t e = twiddles(H, &twn);
+    hipError_t e = twiddles(H, s, &twn);
     if (e != hipSuccess) return e;
     const int cap = kLdsElems / H;
     const int kb = cap < my ? cap : my;
@@ -388,7 +391,7 @@ hipError_t launch_rows_inv_mr(const float2* y, float* out, int64_t nrows, int W,
     MRPlan p;
     if (!make_plan(W, &p) || my > W / 2 + 1) return hipErrorInvalidValue;
     const float2* twn = nullptr;
-    hipError_t e = twiddles(W, &twn);
+    hipError_t e = twiddles(W, s, &twn);
     if (e != hipSuccess) return e;
     const int P = kLdsElems / W;
     const int64_t nb = ((nrows + 1) / 2 + P - 1) / P;

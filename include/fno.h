@@ -60,7 +60,9 @@ enum fno_status {
     FNO_ERR_ALIGN = -5,      /* a pointer is not 16-byte aligned */
     FNO_ERR_NOMEM = -6,      /* the internal workspace could not be allocated */
     FNO_ERR_HIP = -7,        /* a HIP runtime call or kernel launch failed */
-    FNO_ERR_WORKSPACE = -8   /* caller workspace missing or smaller than required */
+    FNO_ERR_WORKSPACE = -8,  /* caller workspace missing or smaller than required */
+    FNO_ERR_CAPTURE = -9     /* a table or workspace would have to be allocated while
+                                the stream is being captured into a graph */
 };
 
 /* Library version as major*10000 + minor*100 + patch. */
@@ -73,20 +75,34 @@ const char* fno_status_string(int status);
 int fno_last_hip_error(void);
 
 /*
+ * Builds the calling thread's current device's state: the twiddle table of
+ * the power-of-two transforms (a device allocation and a synchronous copy).
+ * Any other call does this on its first use of a device; calling it first
+ * lets a caller capture a later call into a graph without an eager call
+ * before (the stream's internal workspace still needs one eager call, or use
+ * the _ws variants).  Idempotent; FNO_OK or FNO_ERR_NOMEM / FNO_ERR_HIP.
+ */
+int fno_init(void);
+
+/*
  * 2D spectral convolution (TurboFNO blog, sections 1 and 2.2; FFT blog
  * sections 2.1-2.2).  Picks the fastest implemented schedule for the shape.
- * Uses an internal workspace per (device, stream): grow-only, allocated on
+ * Uses an internal workspace per (device, stream), following the FFT blog's
+ * plan and work-area reuse (sections 2.2 and 5.3): grow-only, allocated on
  * first use and kept until process exit, so calls on different streams may
- * overlap in time (growing it synchronises the device once).  The _ws
- * variants take caller-owned scratch instead.
+ * overlap in time.  Growing it waits for the work already enqueued on that
+ * stream, then frees the old buffer; host threads calling on the same stream
+ * are serialised from workspace lookup until their kernels are enqueued.
+ * The _ws variants take caller-owned scratch instead.
  *
  * HIP graph capture: every call enqueues kernels only (no memset or copy
- * nodes) and may be captured once the same call has run eagerly on the
- * capturing stream (that allocates the stream's workspace and the twiddle
- * tables; nothing is allocated while capturing), or through the _ws variants.
- * A captured graph holds the workspace's address: a later call on the same
- * stream that needs a larger workspace reallocates it, after which graphs
- * captured on that stream must not be replayed.
+ * nodes).  A call that would have to allocate while its stream is being
+ * captured (the device's twiddle table before fno_init or any eager call; a
+ * new or larger internal workspace; the table of a new non-power-of-two
+ * length) returns FNO_ERR_CAPTURE and enqueues nothing.  A captured graph
+ * holds the workspace's address: a later call on the same stream that needs
+ * a larger workspace reallocates it, after which graphs captured on that
+ * stream must not be replayed.
  */
 int fno_spectral_conv2d(const float* x, const void* w, float* out,
                         int B, int Cin, int Cout, int H, int W, int mx, int my,
@@ -103,8 +119,11 @@ int fno_spectral_conv1d(const float* x, const void* w, float* out,
 /*
  * Unfused schedules of the same hand-written stages, kept for ablation
  * (TurboFNO blog, sections 1 and 2.1: FFT, GEMM and iFFT as separate passes
- * with the spectra round-tripping through device memory).  Same arguments and
- * results as the calls above.
+ * with the spectra round-tripping through device memory): row transforms,
+ * column transforms, mix, column inverse, row inverse as five kernels, the
+ * row spectra in device memory.  Same arguments and results as the calls
+ * above.  The 1D call has no separate fused schedule: fno_spectral_conv1d_unfused
+ * runs the same three kernels as fno_spectral_conv1d.
  */
 int fno_spectral_conv2d_unfused(const float* x, const void* w, float* out,
                                 int B, int Cin, int Cout, int H, int W, int mx, int my,
@@ -114,7 +133,9 @@ int fno_spectral_conv1d_unfused(const float* x, const void* w, float* out,
 
 /*
  * Bytes of caller workspace the _ws calls need for this shape (0 when the
- * fastest schedule needs none).  Never fails; returns 0 for invalid shapes.
+ * fastest schedule needs none): the query half of the FFT blog's plan /
+ * work-area pattern (sections 2.2 and 5.3).  Never fails; returns 0 for
+ * invalid shapes.
  */
 size_t fno_workspace_size_2d(int B, int Cin, int Cout, int H, int W, int mx, int my);
 size_t fno_workspace_size_1d(int B, int Cin, int Cout, int N, int modes);
@@ -122,8 +143,13 @@ size_t fno_workspace_size_1d(int B, int Cin, int Cout, int N, int modes);
 /*
  * As fno_spectral_conv2d / _1d, but all scratch lives in `workspace`
  * (device memory, at least fno_workspace_size_* bytes, 256-byte aligned,
- * caller-owned).  Returns FNO_ERR_WORKSPACE if it is too small or NULL while
- * a non-zero size is needed.  No allocation happens inside these calls.
+ * caller-owned; the FFT blog's caller-provided work area, sections 2.2 and
+ * 5.3).  Returns FNO_ERR_WORKSPACE if it is too small or NULL while a
+ * non-zero size is needed.  These calls allocate nothing once the device's
+ * twiddle table exists (fno_init or any earlier call on the device) and, for
+ * a length that is not a power of two, once that length's table exists (any
+ * earlier call with that length); otherwise they build those tables first,
+ * or return FNO_ERR_CAPTURE while the stream is being captured.
  */
 int fno_spectral_conv2d_ws(const float* x, const void* w, float* out,
                            int B, int Cin, int Cout, int H, int W, int mx, int my,

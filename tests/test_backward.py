@@ -11,6 +11,7 @@ torch = pytest.importorskip("torch")
 
 import oracle  # noqa: E402
 import fft_spectral_convolution_amd as fno  # noqa: E402
+import parity_log  # noqa: E402
 from fft_spectral_convolution_amd.inputs import CONFIGS, Config, make_inputs  # noqa: E402
 
 pytestmark = pytest.mark.gpu
@@ -34,6 +35,7 @@ def assert_close(gpu, ref, what):
     rel = np.linalg.norm((g - ref).ravel()) / max(np.linalg.norm(ref.ravel()), 1e-300)
     mx = np.max(np.abs(g - ref)) / max(np.max(np.abs(ref)), 1e-300)
     print(f"  {what}: rel_l2={rel:.3e} max_abs/max|ref|={mx:.3e}", flush=True)
+    parity_log.record(what, rel, mx)
     assert rel <= REL_L2, f"{what}: relative L2 error {rel:.3e} > {REL_L2}"
     assert mx <= MAX_ABS, f"{what}: max-abs error {mx:.3e} > {MAX_ABS} * max|ref|"
 
@@ -59,7 +61,7 @@ def check(cfg, seed=0):
     assert_close(gw, rw, f"{cfg.name} grad_w")
 
 
-@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4"])
+@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4", "c5"])
 def test_backward_workloads(name):
     cfg = CONFIGS[name]
     print(f"\n[{name} backward] {cfg.describe()}", flush=True)

@@ -126,3 +126,104 @@ def test_graph_backward(cfg):
         cap = lambda x, w, e: fno.fno_spectral_conv2d_backward(x, w, e, cfg.mx, cfg.my, grad_x=gx, grad_w=gw)  # noqa: E731
         eag = lambda x, w, e: fno.fno_spectral_conv2d_backward(x, w, e, cfg.mx, cfg.my)  # noqa: E731
     _replay_matches_eager(cfg, cap, eag, extra=_grad_out)
+
+
+# ---------------------------------------------------------------------------
+# allocation is refused during capture; host threads sharing a stream
+# ---------------------------------------------------------------------------
+
+def _captured_status(s, call, also):
+    """Run call() inside a capture on stream s (with one ordinary kernel,
+    also(), captured beside it); return the FnoError status it raised, or 0."""
+    g = torch.cuda.CUDAGraph()
+    status = 0
+    with torch.cuda.graph(g, stream=s):
+        also()
+        try:
+            call()
+        except fno.FnoError as err:
+            status = err.status
+    torch.cuda.synchronize()
+    return status
+
+
+def test_capture_refuses_workspace_growth():
+    # a fresh stream has no workspace yet: the call would allocate one
+    cfg = Config("cap", "2d", 2, 8, 8, 64, 64, 8, 8, "uniform")
+    x, w = _inputs(cfg, 0)
+    out = torch.empty((cfg.B, cfg.Cout, cfg.H, cfg.W), device=DEV)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    st = _captured_status(s, lambda: fno.fno_spectral_conv2d(x, w, cfg.mx, cfg.my, out=out), lambda: out.add_(1.0))
+    assert st == -9, f"expected FNO_ERR_CAPTURE, got {st}"
+    # the same call eagerly on that stream, then captured: allowed
+    with torch.cuda.stream(s):
+        ref = fno.fno_spectral_conv2d(x, w, cfg.mx, cfg.my)
+    s.synchronize()
+    st = _captured_status(s, lambda: fno.fno_spectral_conv2d(x, w, cfg.mx, cfg.my, out=out), lambda: out.add_(1.0))
+    assert st == 0
+    assert torch.isfinite(ref).all()
+
+
+def test_capture_refuses_new_mixed_radix_table():
+    # the workspace of the stream is large enough, but a 7-smooth length used
+    # for the first time in this process needs its twiddle table built
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    big = Config("cap1d", "1d", 2, 4, 4, 1, 4096, 1, 64, "normal")
+    xb, wb = _inputs(big, 0)
+    with torch.cuda.stream(s):
+        fno.fno_spectral_conv1d(xb, wb, big.my)
+    s.synchronize()
+    n = 2 * 3 * 5 * 7 * 3          # 630: not used by any other test
+    odd = Config("cap630", "1d", 2, 4, 4, 1, n, 1, 32, "normal")
+    x, w = _inputs(odd, 0)
+    out = torch.empty((odd.B, odd.Cout, n), device=DEV)
+    st = _captured_status(s, lambda: fno.fno_spectral_conv1d(x, w, odd.my, out=out), lambda: out.add_(1.0))
+    assert st == -9, f"expected FNO_ERR_CAPTURE, got {st}"
+    with torch.cuda.stream(s):
+        fno.fno_spectral_conv1d(x, w, odd.my, out=out)     # builds the table eagerly
+    s.synchronize()
+    st = _captured_status(s, lambda: fno.fno_spectral_conv1d(x, w, odd.my, out=out), lambda: out.add_(1.0))
+    assert st == 0
+
+
+def test_threads_sharing_a_stream_grow_its_workspace():
+    # Two host threads call on the same (new) stream at once, one with a
+    # shape that needs a larger internal workspace than the other's: the
+    # growth must wait until the other call's kernels are enqueued and done
+    # before it frees the old buffer.  Every result must equal the eager one.
+    import threading
+    small = Config("thr_s", "2d", 2, 8, 8, 64, 64, 8, 8, "uniform")
+    large = Config("thr_l", "2d", 4, 32, 32, 128, 128, 32, 32, "uniform")
+    xs, ws = _inputs(small, 1)
+    xl, wl = _inputs(large, 2)
+    ref_s = fno.fno_spectral_conv2d(xs, ws, small.mx, small.my)
+    ref_l = fno.fno_spectral_conv2d(xl, wl, large.mx, large.my)
+    torch.cuda.synchronize()
+    for it in range(8):
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        outs_s = [torch.empty_like(ref_s) for _ in range(4)]
+        outs_l = [torch.empty_like(ref_l) for _ in range(4)]
+        errs = []
+
+        def worker(outs, x, w, cfg):
+            try:
+                with torch.cuda.stream(s):
+                    for o in outs:
+                        fno.fno_spectral_conv2d(x, w, cfg.mx, cfg.my, out=o)
+            except Exception as e:  # noqa: BLE001
+                errs.append(e)
+        ta = threading.Thread(target=worker, args=(outs_s, xs, ws, small))
+        tb = threading.Thread(target=worker, args=(outs_l, xl, wl, large))
+        ta.start()
+        tb.start()
+        ta.join()
+        tb.join()
+        s.synchronize()
+        assert not errs, errs
+        for o in outs_s:
+            assert torch.equal(o, ref_s), f"iteration {it}: small call differs"
+        for o in outs_l:
+            assert torch.equal(o, ref_l), f"iteration {it}: large call differs"

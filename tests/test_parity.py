@@ -13,6 +13,7 @@ torch = pytest.importorskip("torch")
 
 import oracle  # noqa: E402
 import fft_spectral_convolution_amd as fno  # noqa: E402
+import parity_log  # noqa: E402
 from fft_spectral_convolution_amd.inputs import CONFIGS, Config, make_inputs, make_weight, make_x  # noqa: E402
 
 pytestmark = pytest.mark.gpu
@@ -35,6 +36,7 @@ def errors(gpu, ref):
 def assert_close(gpu, ref, what):
     rel, mx = errors(gpu, ref)
     print(f"  {what}: rel_l2={rel:.3e} max_abs/max|ref|={mx:.3e}", flush=True)
+    parity_log.record(what, rel, mx)
     assert rel <= REL_L2, f"{what}: relative L2 error {rel:.3e} > {REL_L2}"
     assert mx <= MAX_ABS, f"{what}: max-abs error {mx:.3e} > {MAX_ABS} * max|ref|"
 
@@ -97,7 +99,7 @@ def test_workload_parity(name, variant):
 # stage by stage
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("name", ["c1", "c2", "c3"])
+@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c5"])
 def test_stages_2d(name):
     cfg = CONFIGS[name]
     x, w = make_inputs(cfg, 0)
@@ -118,22 +120,29 @@ def test_stages_2d(name):
     assert_close(out, out_ref, f"{name} inverse")
 
 
-def test_stages_1d():
-    cfg = Config("s1d", "1d", 8, 16, 12, 1, 1024, 1, 40, "normal")
-    x, w = make_inputs(cfg, 3)
+@pytest.mark.parametrize("name", ["s1d", "c4"])
+def test_stages_1d(name):
+    # s1d: a 1024-point sequence with a ragged mode count; c4: the full
+    # token-mixing workload (4096 points, 64 modes, 256 x 64 rows)
+    if name == "c4":
+        cfg = CONFIGS["c4"]
+        x, w = make_inputs(cfg, 0)
+    else:
+        cfg = Config("s1d", "1d", 8, 16, 12, 1, 1024, 1, 40, "normal")
+        x, w = make_inputs(cfg, 3)
     xh_ref = oracle.forward_truncated_1d(x, cfg.my)
     xh = fno.fno_forward1d(to_dev(x), cfg.my)
     torch.cuda.synchronize()
-    assert_close(xh, xh_ref, "1d forward spectrum")
+    assert_close(xh, xh_ref, f"{name} forward spectrum")
     xh32 = xh_ref.astype(np.complex64)
     yh_ref = oracle.mix_1d(xh32, w)
     yh = fno.fno_mix(to_dev(xh32), to_dev(w))
     torch.cuda.synchronize()
-    assert_close(yh, yh_ref, "1d mixed spectrum")
+    assert_close(yh, yh_ref, f"{name} mixed spectrum")
     yh32 = yh_ref.astype(np.complex64)
     out = fno.fno_inverse1d(to_dev(yh32), cfg.W)
     torch.cuda.synchronize()
-    assert_close(out, oracle.inverse_from_truncated_1d(yh32, cfg.W), "1d inverse")
+    assert_close(out, oracle.inverse_from_truncated_1d(yh32, cfg.W), f"{name} inverse")
 
 
 # ---------------------------------------------------------------------------

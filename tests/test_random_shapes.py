@@ -10,6 +10,7 @@ torch = pytest.importorskip("torch")
 
 import oracle  # noqa: E402
 import fft_spectral_convolution_amd as fno  # noqa: E402
+import parity_log  # noqa: E402
 from fft_spectral_convolution_amd.inputs import Config, make_inputs  # noqa: E402
 
 pytestmark = pytest.mark.gpu
@@ -33,6 +34,7 @@ def close(gpu, ref, what):
     rel = np.linalg.norm((g - ref).ravel()) / max(np.linalg.norm(ref.ravel()), 1e-300)
     mx = np.max(np.abs(g - ref)) / max(np.max(np.abs(ref)), 1e-300)
     print(f"  {what}: rel_l2={rel:.3e} max_abs/max|ref|={mx:.3e}", flush=True)
+    parity_log.record(what, rel, mx)
     assert rel <= REL_L2 and mx <= MAX_ABS, what
 
 
