@@ -29,6 +29,8 @@ __all__ = [
     "fno_spectral_conv2d_unfused",
     "fno_spectral_conv1d_unfused",
     "fno_spectral_conv2d_ws",
+    "fno_spectral_conv2d_noalloc",
+    "fno_noalloc_scratch_bytes",
     "fno_spectral_conv1d_ws",
     "fno_spectral_conv2d_backward",
     "fno_spectral_conv1d_backward",
@@ -76,6 +78,8 @@ _SIGNATURES = {
     "fno_workspace_size_2d": (_S, [_I, _I, _I, _I, _I, _I, _I]),
     "fno_workspace_size_1d": (_S, [_I, _I, _I, _I, _I]),
     "fno_spectral_conv2d_ws": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _S, _P]),
+    "fno_spectral_conv2d_noalloc": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P]),
+    "fno_noalloc_scratch_bytes": (_S, []),
     "fno_spectral_conv1d_ws": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _P, _S, _P]),
     "fno_forward2d": (_I, [_P, _P, _I, _I, _I, _I, _I, _I, _P]),
     "fno_mix": (_I, [_P, _P, _P, _I, _I, _I, _I, _P]),
@@ -428,6 +432,22 @@ def fno_spectral_conv2d_ws(x, w, mx: int, my: int, workspace, out=None):
         _check(lib().fno_spectral_conv2d_ws(_ptr(x), _ptr(w), _ptr(out), b, cin, cout, h, wd, mx, my,
                                             ws_ptr, ws_bytes, _stream_ptr(x.device)), "fno_spectral_conv2d_ws")
     return out
+
+
+def fno_spectral_conv2d_noalloc(x, w, mx: int, my: int, out=None):
+    """2D spectral convolution whose scratch is the library's fixed device
+    array (no allocation inside the call; fno_init must have run on the
+    device).  `out` must be given by callers that cannot allocate."""
+    out, (b, cin, cout, h, wd) = _conv2d_args(x, w, mx, my, out)
+    with _on_device(x):
+        _check(lib().fno_spectral_conv2d_noalloc(_ptr(x), _ptr(w), _ptr(out), b, cin, cout, h, wd, mx, my,
+                                                 _stream_ptr(x.device)), "fno_spectral_conv2d_noalloc")
+    return out
+
+
+def fno_noalloc_scratch_bytes() -> int:
+    """Bytes of the fixed device array fno_spectral_conv2d_noalloc uses."""
+    return int(lib().fno_noalloc_scratch_bytes())
 
 
 def fno_spectral_conv1d(x, w, modes: int, out=None):

@@ -41,7 +41,17 @@ struct DeviceState {
     bool init = false;
     float2* twiddle = nullptr;     // kNMax entries exp(-2 pi i m / kNMax)
     std::vector<std::unique_ptr<Workspace>> ws;   // internal grow-only workspaces, one per stream
+    void* scratch = nullptr;       // this device's address of `scratch` (set by fno_init)
 };
+
+// Scratch of fno_spectral_conv2d_noalloc: the truncated spectra of one call
+// live in this fixed device array, so that the call allocates nothing.  Each
+// device that loads the library holds its own copy until the process ends.
+// Host code never passes the array's name to a kernel (on the host it is only
+// a stand-in): fno_init looks up its device address per device with
+// hipGetSymbolAddress and every use goes through that address.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 
 // A call's hold on its stream's workspace (released when the call returns,
 // after its kernels are enqueued).
@@ -745,6 +755,17 @@ int check_epilogue(const float* bias, const float* branch, const float* out, int
     return FNO_OK;
 }
 
+// The state of the current device as fno_init left it, without building
+// anything (nullptr when fno_init has not run on this device).
+DeviceState* initialised_state() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return nullptr;
+    std::lock_guard<std::mutex> lock(g_mutex);
+    if (dev < 0 || dev >= (int)g_devices.size() || !g_devices[dev]) return nullptr;
+    DeviceState* st = g_devices[dev].get();
+    return st->init && st->scratch ? st : nullptr;
+}
+
 int conv2d_common(const float* x, const void* w, float* out, int B, int Cin, int Cout, int H, int W, int mx,
                   int my, void* user_ws, size_t user_ws_bytes, bool use_user_ws, bool unfused, void* stream,
                   const Epilogue& epi = Epilogue{}) {
@@ -1015,6 +1036,8 @@ const char* fno_status_string(int status) {
         case FNO_ERR_HIP: return "a HIP runtime call or kernel launch failed";
         case FNO_ERR_WORKSPACE: return "caller workspace missing or too small";
         case FNO_ERR_CAPTURE: return "a table or workspace would have to be allocated while the stream is captured";
+        case FNO_ERR_TOO_LARGE: return "the shape needs more scratch than the fixed device array of the no-allocation call holds";
+        case FNO_ERR_NOT_INIT: return "fno_init has not been called on this device";
         default: return "unknown status";
     }
 }
@@ -1023,7 +1046,16 @@ int fno_last_hip_error(void) { return g_last_hip_error; }
 
 int fno_init(void) {
     DeviceState* st = nullptr;
-    return device_state(&st, nullptr);
+    int rc = device_state(&st, nullptr);
+    if (rc) return rc;
+    std::lock_guard<std::mutex> lock(g_mutex);
+    if (!st->scratch) {
+        void* p = nullptr;
+        hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p) return hip_fail(e != hipSuccess ? e : hipErrorInvalidSymbol);
+        st->scratch = p;
+    }
+    return FNO_OK;
 }
 
 int fno_set_timing_events(void** events, int n_events) {
@@ -1052,6 +1084,23 @@ int fno_spectral_conv2d_ws(const float* x, const void* w, float* out, int B, int
                            int mx, int my, void* workspace, size_t ws_bytes, void* stream) {
     return conv2d_common(x, w, out, B, Cin, Cout, H, W, mx, my, workspace, ws_bytes, true, false, stream);
 }
+
+int fno_spectral_conv2d_noalloc(const float* x, const void* w, float* out, int B, int Cin, int Cout, int H, int W,
+                                int mx, int my, void* stream) {
+    int rc = check_dims_2d(B, Cin, H, W, mx, my);
+    if (rc) return rc;
+    if (Cout < 1) return FNO_ERR_SHAPE;
+    // lengths other than powers of two would need their twiddle tables built
+    if (!is_pow2(H) || !is_pow2(W)) return FNO_ERR_SHAPE;
+    DeviceState* st = initialised_state();
+    if (!st) return FNO_ERR_NOT_INIT;
+    const size_t need = best_ws_2d(make2d(B, Cin, Cout, H, W, mx, my));
+    if (need > kScratchBytes) return FNO_ERR_TOO_LARGE;
+    // the device state exists, so conv2d_common's lookup allocates nothing
+    return conv2d_common(x, w, out, B, Cin, Cout, H, W, mx, my, st->scratch, kScratchBytes, true, false, stream);
+}
+
+size_t fno_noalloc_scratch_bytes(void) { return kScratchBytes; }
 
 int fno_spectral_conv1d(const float* x, const void* w, float* out, int B, int Cin, int Cout, int N, int modes,
                         void* stream) {

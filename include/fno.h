@@ -61,8 +61,10 @@ enum fno_status {
     FNO_ERR_NOMEM = -6,      /* the internal workspace could not be allocated */
     FNO_ERR_HIP = -7,        /* a HIP runtime call or kernel launch failed */
     FNO_ERR_WORKSPACE = -8,  /* caller workspace missing or smaller than required */
-    FNO_ERR_CAPTURE = -9     /* a table or workspace would have to be allocated while
+    FNO_ERR_CAPTURE = -9,    /* a table or workspace would have to be allocated while
                                 the stream is being captured into a graph */
+    FNO_ERR_TOO_LARGE = -10, /* shape needs more than fno_spectral_conv2d_noalloc's fixed scratch */
+    FNO_ERR_NOT_INIT = -11   /* fno_init has not been called on the current device */
 };
 
 /* Library version as major*10000 + minor*100 + patch. */
@@ -157,6 +159,29 @@ int fno_spectral_conv2d_ws(const float* x, const void* w, float* out,
 int fno_spectral_conv1d_ws(const float* x, const void* w, float* out,
                            int B, int Cin, int Cout, int N, int modes,
                            void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * For callers that cannot allocate device memory (code under graph capture,
+ * tight serving loops, harnesses that forbid allocation): fno_spectral_conv2d
+ * with its scratch (the truncated spectra) in a fixed device array of
+ * fno_noalloc_scratch_bytes() bytes (64 MiB), which every device that loads
+ * the library holds until the process ends.  The call allocates and frees
+ * nothing.  Before the first call on a device, call fno_init on it (it looks
+ * up that device's address of the array and builds the twiddle table);
+ * otherwise FNO_ERR_NOT_INIT.  H and W must be powers of two (other lengths
+ * would need a table built; FNO_ERR_SHAPE); a shape whose spectra need more
+ * than the array holds returns FNO_ERR_TOO_LARGE (the 128x128 workload with
+ * B=32, Cin=Cout=64 and 32x32 modes needs exactly 64 MiB).  Nothing in the
+ * array needs to start at zero: every call writes the spectra it reads.  All
+ * calls on one device share the one array, which keeps the last call's
+ * contents: calls that overlap in time on one device (other streams or host
+ * threads) race on it and must be serialised by the caller.  Same arguments,
+ * results and other errors as fno_spectral_conv2d.
+ */
+int fno_spectral_conv2d_noalloc(const float* x, const void* w, float* out,
+                                int B, int Cin, int Cout, int H, int W, int mx, int my,
+                                void* stream);
+size_t fno_noalloc_scratch_bytes(void);
 
 /*
  * Stage calls, for stage-by-stage comparison of the intermediate spectra
