@@ -507,8 +507,42 @@ def main():
                     ts.append(e0.elapsed_time(e1) * 1e-3)
             med = float(np.median(ts))
             res[name] = {"gbs": round(moved * n * 4 / med / 1e9, 1), "us": round(med * 1e6, 1)}
+        # Reuse through the last-level (memory-side) cache: time a copy out of
+        # S (32, 64, 128 MiB) into D after a 1 GiB flush, right after S was
+        # written (fill_) and right after S was read (sum).  If the cache kept
+        # S, the copy's read half would be faster than after the flush.
+        del bufs
+        flush = torch.empty(2**28, dtype=torch.float32, device=dev)        # 1 GiB
+        reuse = {}
+        for mib in (32, 64, 128):
+            m = mib * 2**20 // 4
+            S = torch.ones(m, dtype=torch.float32, device=dev)
+            D = torch.empty_like(S)
+
+            def t_copy(pre):
+                ts = []
+                for i in range(9):
+                    flush.fill_(0.0)
+                    flush.sum()
+                    pre()
+                    e0 = torch.cuda.Event(enable_timing=True)
+                    e1 = torch.cuda.Event(enable_timing=True)
+                    e0.record()
+                    D.copy_(S)
+                    e1.record()
+                    e1.synchronize()
+                    if i >= 2:
+                        ts.append(e0.elapsed_time(e1) * 1e3)
+                return round(float(np.median(ts)), 2)
+            reuse[f"{mib}MiB"] = {"copy_after_flush_us": t_copy(lambda: None),
+                                  "copy_after_write_us": t_copy(lambda: S.fill_(2.0)),
+                                  "copy_after_read_us": t_copy(lambda: S.sum())}
+            del S, D
         print(json.dumps({"stream_ceilings": res, "bytes_per_buffer": n * 4,
-                          "note": "torch fill_ / sum / copy_ on rotated 256 MiB buffers, median of 20"}))
+                          "note": "torch fill_ / sum / copy_ on rotated 256 MiB buffers, median of 20",
+                          "cache_reuse": reuse,
+                          "cache_reuse_note": "copy of S into D (us, median of 7) after a 1 GiB flush, "
+                                              "after S was written, after S was read"}))
         return
     if args.calibrate_copy:
         n = args.calibrate_copy * 2**20 // 4

@@ -423,7 +423,9 @@ __global__ __launch_bounds__(1 << LOG2H) __attribute__((amdgpu_waves_per_eu(2)))
                 rb = make_rsrc(epi.branch ? epi.branch + img * (int64_t)(H * W) : nullptr,
                                epi.branch ? (uint32_t)(H * W * 4) : 0u);
             }
-            static_for<0, S::NCK>([&](auto c) {
+            // chunk c: float4 8c .. 8c+7 of every row of the wave (128-byte
+            // column slabs of the image)
+            auto emit = [&](auto c) __attribute__((always_inline)) {
                 static_for<0, 8>([&](auto q) {
                     *reinterpret_cast<float4*>(stage + lane * S::SS + 4 * q) =
                         make_float4(z[2 * (8 * c + q)].x, z[2 * (8 * c + q)].y, z[2 * (8 * c + q) + 1].x,
@@ -445,6 +447,14 @@ __global__ __launch_bounds__(1 << LOG2H) __attribute__((amdgpu_waves_per_eu(2)))
                     buffer_store_f4_nt(o, ro, soffs[ii] + 128 * c, 0);
                 });
                 wave_lds_sync();
+            };
+            // Each workgroup starts at its own slab, so that the workgroups
+            // (which run nearly in step) do not all write the same slab of
+            // their images at once (measured at 128x128: 33.9-34.2 -> 33.0 us).
+            const int rot = (int)(blockIdx.x % S::NCK);
+            static_for<0, S::NCK>([&](auto r) {
+                if (rot == r)
+                    static_for<0, S::NCK>([&](auto i) { emit(std::integral_constant<int, (i + r) % S::NCK>{}); });
             });
         }
     }
