@@ -83,6 +83,16 @@ struct RowPlan {
     static size_t lds_bytes() { return sizeof(float2) * (size_t)REGION; }
 };
 
+// MXK > 0: the kept kx count per side is MXK, a multiple of R1, known when the
+// kernel is compiled.  Column-stage index k2 then covers kx in
+// [R1 k2, R1 k2 + R1), a block that is either wholly kept or wholly dropped,
+// so the forward need not form (and the inverse need not read) the dropped
+// blocks.  MXK = 0: mx is read at run time and every block is formed.
+template <int H, int R1, int MXK>
+__device__ constexpr bool block_kept(int k2) {
+    return MXK == 0 || R1 * k2 + R1 <= MXK || R1 * k2 >= H - MXK;
+}
+
 // Bin K of the scaled half spectrum of a real row of length W from its packed
 // transform Z (NZ = W/2 points), s = 2^(-LOG2HW/2):
 //   s X[K] = (s/2) a + c b,   c = (s/2) (-i) W_W^K = (s/2) (-sin, -cos)(2 pi K / W).
@@ -116,7 +126,7 @@ __device__ __forceinline__ float2 half_bin_scaled(const float2 (&z)[NZ]) {
 // of image b C + c is multiplied by mask[c][m] (the mask transposed
 // channel-major, so that a wave's lanes, over consecutive ky, read
 // consecutive entries) on its way out.
-template <int LOG2H, int LOG2W, int MYMAX, bool DIAG>
+template <int LOG2H, int LOG2W, int MYMAX, bool DIAG, int MXK>
 __global__ __launch_bounds__(1 << LOG2H) __attribute__((amdgpu_waves_per_eu(2))) void k_fwd2d_rows(const float* __restrict__ x, float2* __restrict__ xh,
                                                            ImageBase ib, int st, int64_t nimg, int mx, int my,
                                                            const float2* __restrict__ tw,
@@ -235,25 +245,27 @@ __global__ __launch_bounds__(1 << LOG2H) __attribute__((amdgpu_waves_per_eu(2)))
                 float2 u[R2];
                 float2 mv[DIAG ? R2 : 1];
                 if constexpr (DIAG) {
-#pragma unroll
-                    for (int k2 = 0; k2 < R2; ++k2) {
-                        const int q = qm[jj][k2];
-                        mv[k2] = buffer_load_f2(rmask, (q < 0 || !kyok) ? kBufferSkip : (uint32_t)(q + ky) * 8u, 0);
-                    }
+                    static_for<0, R2>([&](auto k2) {
+                        if constexpr (block_kept<H, R1, MXK>(k2)) {
+                            const int q = qm[jj][k2];
+                            mv[k2] = buffer_load_f2(rmask, (q < 0 || !kyok) ? kBufferSkip : (uint32_t)(q + ky) * 8u, 0);
+                        }
+                    });
                 }
 #pragma unroll
                 for (int tt = 0; tt < R2; ++tt) u[tt] = xb[tt * S::XS + k1];
                 dft<R2, -1>(u);
-#pragma unroll
-                for (int k2 = 0; k2 < R2; ++k2) {
-                    // mode m = q my + ky at (m >> 3) st + (m & 7) = m + (m >> 3)(st - 8)
-                    const int q = qm[jj][k2];
-                    const uint32_t m = (uint32_t)(q + ky);
-                    const uint32_t off = (q < 0 || !kyok) ? kBufferSkip : (m + (m >> 3) * st8) * 8u;
-                    float2 val = u[k2];
-                    if constexpr (DIAG) val = cmul(val, mv[k2]);
-                    buffer_store_f2(val, ro, off, 0);
-                }
+                static_for<0, R2>([&](auto k2) {
+                    if constexpr (block_kept<H, R1, MXK>(k2)) {
+                        // mode m = q my + ky at (m >> 3) st + (m & 7) = m + (m >> 3)(st - 8)
+                        const int q = qm[jj][k2];
+                        const uint32_t m = (uint32_t)(q + ky);
+                        const uint32_t off = (q < 0 || !kyok) ? kBufferSkip : (m + (m >> 3) * st8) * 8u;
+                        float2 val = u[k2];
+                        if constexpr (DIAG) val = cmul(val, mv[k2]);
+                        buffer_store_f2(val, ro, off, 0);
+                    }
+                });
             }
         });
     }
@@ -308,7 +320,7 @@ __device__ __forceinline__ float2 packed_c2r_bin(const float2 (&X)[MYMAX]) {
 // float4 between the stage and the store; a chunk's branch float4s are
 // loaded only once that chunk of the rows has left the registers for the
 // stage (the row registers are the kernel's peak).
-template <int LOG2H, int LOG2W, int MYMAX, bool EPI>
+template <int LOG2H, int LOG2W, int MYMAX, bool EPI, int MXK>
 __global__ __launch_bounds__(1 << LOG2H) __attribute__((amdgpu_waves_per_eu(2))) void k_inv2d_rows(
     const float2* __restrict__ yh, float* __restrict__ out, ImageBase ib, int st, int64_t nimg, int mx, int my,
     const float2* __restrict__ tw, Epilogue epi) {
@@ -360,13 +372,16 @@ __global__ __launch_bounds__(1 << LOG2H) __attribute__((amdgpu_waves_per_eu(2)))
             const bool kyok = ky < my;
 #pragma unroll
             for (int jj = 0; jj < NJ; ++jj)
-#pragma unroll
-                for (int k2 = 0; k2 < R2; ++k2) {
-                    const int q = qm[jj][k2];
-                    const uint32_t m = (uint32_t)(q + ky);
-                    const uint32_t off = (q < 0 || !kyok) ? kBufferSkip : (m + (m >> 3) * st8) * 8u;
-                    g[bt][jj][k2] = buffer_load_f2(ri, off, 0);
-                }
+                static_for<0, R2>([&](auto k2) {
+                    if constexpr (block_kept<H, R1, MXK>(k2)) {
+                        const int q = qm[jj][k2];
+                        const uint32_t m = (uint32_t)(q + ky);
+                        const uint32_t off = (q < 0 || !kyok) ? kBufferSkip : (m + (m >> 3) * st8) * 8u;
+                        g[bt][jj][k2] = buffer_load_f2(ri, off, 0);
+                    } else {
+                        g[bt][jj][k2] = make_float2(0.0f, 0.0f);
+                    }
+                });
         });
         static_for<0, NB>([&](auto bt) {
             float2* const xb = xreg + bt * S::XBUF + cl * S::GS;
@@ -476,14 +491,25 @@ hipError_t launch_persistent(K k, int nt, size_t lds, int64_t nimg, hipStream_t 
     return launch_kernel(k, dim3((unsigned)g), dim3(nt), lds, s, args...);
 }
 
+// The 128 x 128 grid with 32 kept kx per side (the 128x128 PDE workload's
+// shape) gets kernels compiled for that mx; every other shape reads mx at run
+// time.
+template <int LH, int LW>
+constexpr bool has_mx32() { return LH == 7; }
+
 template <int LH, int LW, int MYM>
 hipError_t launch_fwd_one(const float* x, float2* xh, const ImageBase& ib, int st, int64_t nimg, int mx, int my,
                           const float2* tw, hipStream_t s, const float2* mask) {
     using P = RowPlan<LH, LW, MYM>;
+    if constexpr (has_mx32<LH, LW>() && MYM == 32) {
+        if (mx == 32 && !mask)
+            return launch_persistent(k_fwd2d_rows<LH, LW, MYM, false, 32>, P::NT, P::lds_bytes(), nimg, s, x, xh, ib,
+                                     st, nimg, mx, my, tw, mask);
+    }
     if (mask)
-        return launch_persistent(k_fwd2d_rows<LH, LW, MYM, true>, P::NT, P::lds_bytes(), nimg, s, x, xh, ib, st, nimg,
-                                 mx, my, tw, mask);
-    return launch_persistent(k_fwd2d_rows<LH, LW, MYM, false>, P::NT, P::lds_bytes(), nimg, s, x, xh, ib, st, nimg,
+        return launch_persistent(k_fwd2d_rows<LH, LW, MYM, true, 0>, P::NT, P::lds_bytes(), nimg, s, x, xh, ib, st,
+                                 nimg, mx, my, tw, mask);
+    return launch_persistent(k_fwd2d_rows<LH, LW, MYM, false, 0>, P::NT, P::lds_bytes(), nimg, s, x, xh, ib, st, nimg,
                              mx, my, tw, mask);
 }
 
@@ -491,11 +517,16 @@ template <int LH, int LW, int MYM>
 hipError_t launch_inv_one(const float2* yh, float* out, const ImageBase& ib, int st, int64_t nimg, int mx, int my,
                           const float2* tw, hipStream_t s, const Epilogue& epi) {
     using P = RowPlan<LH, LW, MYM>;
+    if constexpr (has_mx32<LH, LW>() && MYM == 32) {
+        if (mx == 32 && !epi.on)
+            return launch_persistent(k_inv2d_rows<LH, LW, MYM, false, 32>, P::NT, P::lds_bytes(), nimg, s, yh, out,
+                                     ib, st, nimg, mx, my, tw, epi);
+    }
     if (epi.on)
-        return launch_persistent(k_inv2d_rows<LH, LW, MYM, true>, P::NT, P::lds_bytes(), nimg, s, yh, out, ib, st,
+        return launch_persistent(k_inv2d_rows<LH, LW, MYM, true, 0>, P::NT, P::lds_bytes(), nimg, s, yh, out, ib, st,
                                  nimg, mx, my, tw, epi);
-    return launch_persistent(k_inv2d_rows<LH, LW, MYM, false>, P::NT, P::lds_bytes(), nimg, s, yh, out, ib, st, nimg,
-                             mx, my, tw, epi);
+    return launch_persistent(k_inv2d_rows<LH, LW, MYM, false, 0>, P::NT, P::lds_bytes(), nimg, s, yh, out, ib, st,
+                             nimg, mx, my, tw, epi);
 }
 
 ImageBase image_base(const SpecLayout& lay) {
