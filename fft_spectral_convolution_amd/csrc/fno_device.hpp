@@ -25,32 +25,6 @@ constexpr int kNMax = 1 << kLog2NMax;    // twiddle table length
 constexpr int kLdsElems = 4096;          // complex elements per LDS ping-pong buffer
 
 constexpr float kSqrtHalf = 0.70710678118654752440f;  // cos(pi/4)
-constexpr float kCosPi8 = 0.92387953251128675613f;    // cos(pi/8)
-constexpr float kSinPi8 = 0.38268343236508977173f;    // sin(pi/8)
-
-__host__ __device__ constexpr float cos16(int e) {
-    // cos(2 pi e / 16)
-    switch (e & 15) {
-        case 0: return 1.0f;
-        case 1: return kCosPi8;
-        case 2: return kSqrtHalf;
-        case 3: return kSinPi8;
-        case 4: return 0.0f;
-        case 5: return -kSinPi8;
-        case 6: return -kSqrtHalf;
-        case 7: return -kCosPi8;
-        case 8: return -1.0f;
-        case 9: return -kCosPi8;
-        case 10: return -kSqrtHalf;
-        case 11: return -kSinPi8;
-        case 12: return 0.0f;
-        case 13: return kSinPi8;
-        case 14: return kSqrtHalf;
-        default: return kCosPi8;
-    }
-}
-
-__host__ __device__ constexpr float sin16(int e) { return cos16(e - 4); }  // sin x = cos(x - pi/2)
 
 // Compile-time cos / sin of 2 pi e / N for the register-resident transforms:
 // argument reduction to [0, pi/4] by octant symmetries, then Taylor series in
@@ -116,19 +90,6 @@ __device__ __forceinline__ float2 mul_i(float2 v) {
     return SIGN < 0 ? make_float2(v.y, -v.x) : make_float2(-v.y, v.x);
 }
 
-// v * exp(SIGN * 2 pi i * e / 16), e a compile-time constant after unrolling.
-template <int SIGN>
-__device__ __forceinline__ float2 w16mul(float2 v, int e) {
-    e &= 15;
-    if (e == 0) return v;
-    if (e == 4) return mul_i<SIGN>(v);
-    if (e == 8) return make_float2(-v.x, -v.y);
-    if (e == 12) return mul_i<-SIGN>(v);
-    const float c = cos16(e);
-    const float s = SIGN * sin16(e);
-    return make_float2(v.x * c - v.y * s, v.x * s + v.y * c);
-}
-
 // v * exp(SIGN * 2 pi i * E / N), N a power of two >= 8.  E is a template
 // argument so the constants are folded at compile time.
 template <int SIGN, int N, int E>
@@ -163,32 +124,65 @@ __device__ __forceinline__ void static_for(F&& f) {
     }
 }
 
+// acc + v * exp(SIGN * 2 pi i * E / N) on fused multiply-adds (E and N
+// compile-time): four instructions for a general factor instead of the six
+// of a separate product and sum.
+template <int SIGN, int N, int E>
+__device__ __forceinline__ float2 wfma(float2 acc, float2 v) {
+    constexpr int e = E & (N - 1);
+    if constexpr (e == 0) {
+        return cadd(acc, v);
+    } else if constexpr (4 * e == N) {
+        return cadd(acc, mul_i<SIGN>(v));
+    } else if constexpr (2 * e == N) {
+        return csub(acc, v);
+    } else if constexpr (4 * e == 3 * N) {
+        return cadd(acc, mul_i<-SIGN>(v));
+    } else {
+        constexpr float c = (float)exact_cos(e, N);
+        constexpr float s = (float)(SIGN * exact_sin(e, N));
+        return make_float2(fmaf(v.x, c, fmaf(-v.y, s, acc.x)), fmaf(v.x, s, fmaf(v.y, c, acc.y)));
+    }
+}
+
+// Radix-2 butterfly lo = a + T b, hi = a - T b, T = exp(SIGN * 2 pi i * E / N)
+// (E and N compile-time).  A general factor T = c + i s is applied as
+// c (1 + i s/c) when |s| <= |c|, else as s (c/s + i): the product with the
+// bracket takes two fused multiply-adds and each output two more, six in
+// all instead of the eight of a product followed by a sum and a difference.
+template <int SIGN, int N, int E>
+__device__ __forceinline__ void bfly(float2 a, float2 b, float2& lo, float2& hi) {
+    constexpr int e = E & (N - 1);
+    if constexpr (e == 0) {
+        lo = cadd(a, b);
+        hi = csub(a, b);
+    } else if constexpr (4 * e == N || 4 * e == 3 * N) {
+        const float2 t = mul_i<4 * e == N ? SIGN : -SIGN>(b);
+        lo = cadd(a, t);
+        hi = csub(a, t);
+    } else if constexpr (2 * e == N) {
+        lo = csub(a, b);
+        hi = cadd(a, b);
+    } else {
+        constexpr double c = exact_cos(e, N);
+        constexpr double s = SIGN * exact_sin(e, N);
+        constexpr bool by_c = (c < 0 ? -c : c) >= (s < 0 ? -s : s);
+        constexpr float f = (float)(by_c ? c : s);
+        constexpr float t = (float)(by_c ? s / c : c / s);
+        float2 u;
+        if constexpr (by_c) u = make_float2(fmaf(-t, b.y, b.x), fmaf(t, b.x, b.y));   // (1 + i t) b
+        else u = make_float2(fmaf(t, b.x, -b.y), fmaf(t, b.y, b.x));                   // (t + i) b
+        lo = make_float2(fmaf(f, u.x, a.x), fmaf(f, u.y, a.y));
+        hi = make_float2(fmaf(-f, u.x, a.x), fmaf(-f, u.y, a.y));
+    }
+}
+
 // In-register DFT of size R <= 64, natural order in and out:
 // v[k] <- sum_r v[r] exp(SIGN 2 pi i r k / R).  Radix-2 decimation in time.
 template <int R, int SIGN>
 __device__ __forceinline__ void dft(float2 (&v)[R]) {
     static_assert(R >= 1 && R <= 64 && (R & (R - 1)) == 0, "radix must be a power of two <= 64");
-    if constexpr (R == 2) {
-        const float2 a = v[0], b = v[1];
-        v[0] = cadd(a, b);
-        v[1] = csub(a, b);
-    } else if constexpr (R > 2 && R <= 16) {
-        constexpr int HALF = R / 2;
-        float2 e[HALF], o[HALF];
-#pragma unroll
-        for (int i = 0; i < HALF; ++i) {
-            e[i] = v[2 * i];
-            o[i] = v[2 * i + 1];
-        }
-        dft<HALF, SIGN>(e);
-        dft<HALF, SIGN>(o);
-#pragma unroll
-        for (int k = 0; k < HALF; ++k) {
-            const float2 t = w16mul<SIGN>(o[k], k * (16 / R));
-            v[k] = cadd(e[k], t);
-            v[k + HALF] = csub(e[k], t);
-        }
-    } else if constexpr (R > 16) {
+    if constexpr (R >= 2) {
         constexpr int HALF = R / 2;
         float2 e[HALF], o[HALF];
         static_for<0, HALF>([&](auto i) {
@@ -197,11 +191,7 @@ __device__ __forceinline__ void dft(float2 (&v)[R]) {
         });
         dft<HALF, SIGN>(e);
         dft<HALF, SIGN>(o);
-        static_for<0, HALF>([&](auto k) {
-            const float2 t = wmul<SIGN, R, k>(o[k]);
-            v[k] = cadd(e[k], t);
-            v[k + HALF] = csub(e[k], t);
-        });
+        static_for<0, HALF>([&](auto k) { bfly<SIGN, R, k>(e[k], o[k], v[k], v[k + HALF]); });
     }
 }
 

@@ -115,9 +115,13 @@ __device__ __forceinline__ float2 half_bin_scaled(const float2 (&z)[NZ]) {
         tx = bx * cr;
         ty = by * cr;
     } else {
-        constexpr float cr = (float)(-hs * sn), ci = (float)(-hs * cs);
-        tx = fmaf(bx, cr, -by * ci);
-        ty = fmaf(bx, ci, by * cr);
+        // expanded over zk and zm, the constants h +- cr formed in double:
+        // four fused multiply-adds per part instead of the pre-sums
+        constexpr double crd = -hs * sn;
+        constexpr float p = (float)(hs + crd), m = (float)(hs - crd), ci = (float)(-hs * cs);
+        (void)ax, (void)ay, (void)bx, (void)by;
+        return make_float2(fmaf(p, zk.x, fmaf(m, zm.x, fmaf(-ci, zk.y, -ci * zm.y))),
+                           fmaf(p, zk.y, fmaf(-m, zm.y, fmaf(ci, zk.x, -ci * zm.x))));
     }
     return make_float2(fmaf(h, ax, tx), fmaf(h, ay, ty));
 }

@@ -64,17 +64,19 @@ struct LaneTwiddles {
     float2 pj[NJ];                                  // W_64^{n1 j}, j < 64 / Q
     const float2* tl;                               // Q = 64: LDS table [r][64 lanes]
 
-    __device__ __forceinline__ void init(const float2* __restrict__ tw, int lane, float2* lds_table) {
+    // The residue factors are stored times rs (a real scale folded into
+    // them); the W_64 factors are not.
+    __device__ __forceinline__ void init(const float2* __restrict__ tw, int lane, float2* lds_table, float rs) {
         constexpr int N = 64 * Q;
         if constexpr (Q <= 32) {
             (void)lds_table;
 #pragma unroll
-            for (int r = 0; r < NR; ++r) tr[r] = tw[(lane * r * (kNMax / N)) & (kNMax - 1)];
+            for (int r = 0; r < NR; ++r) tr[r] = cscale(tw[(lane * r * (kNMax / N)) & (kNMax - 1)], rs);
         } else {
             // 64 x 64 residue factors, filled by the whole workgroup
             for (int e = threadIdx.x; e < 64 * 64; e += blockDim.x) {
                 const int r = e >> 6, l = e & 63;
-                lds_table[e] = tw[(l * r * (kNMax / N)) & (kNMax - 1)];
+                lds_table[e] = cscale(tw[(l * r * (kNMax / N)) & (kNMax - 1)], rs);
             }
             tl = lds_table;
         }
@@ -112,7 +114,7 @@ __device__ __forceinline__ float2 real_bin2(const float2 (&z)[Q / 2]) {
     const float2 zm = z[(NZ - K % NZ) % NZ];
     const float2 e = make_float2(zk.x + zm.x, zk.y - zm.y);
     const float2 o = make_float2(zk.y + zm.y, zm.x - zk.x);
-    return cadd(e, wmul<-1, Q, K>(o));
+    return wfma<-1, Q, K>(e, o);
 }
 
 // Packed C2R bin K (K < Q/2) from a Hermitian half spectrum H[0..Q/2]:
@@ -125,7 +127,7 @@ __device__ __forceinline__ float2 packed_bin(const float2 (&H)[Q / 2 + 1]) {
     const float2 a = make_float2(hk.x + hm.x, hk.y - hm.y);
     const float2 b = make_float2(hk.x - hm.x, hk.y + hm.y);
     // i W_Q^{-K} b = W_Q^{-K} (i b)
-    return cadd(a, wmul<1, Q, K>(make_float2(-b.y, b.x)));
+    return wfma<1, Q, K>(a, make_float2(-b.y, b.x));
 }
 
 template <int Q>
@@ -152,14 +154,16 @@ __global__ __launch_bounds__(kPrunedThreads) __attribute__((amdgpu_waves_per_eu(
     const int q_r = lane & 3;
     const int rr_r = kk_r % RPC;
     const int jj_r = kk_r / RPC;
-    float2 wk[4], vk[4];                       // W^k and W^{16 q_r k} of the lane's bin in each chunk
+    // W^k and W^{16 q_r k} of the lane's bin in each chunk, the latter times
+    // the output scale (halved: the bins below are doubled)
+    float2 wk[4], vk[4];
+    const float half_scale = 0.5f * scale;
 #pragma unroll
     for (int ch = 0; ch < 4; ++ch) {
         const int k = RPC * ch + rr_r + Q * jj_r;
         wk[ch] = tw[(k * (kNMax / N)) & (kNMax - 1)];
-        vk[ch] = tw[(16 * q_r * k * (kNMax / N)) & (kNMax - 1)];
+        vk[ch] = cscale(tw[(16 * q_r * k * (kNMax / N)) & (kNMax - 1)], half_scale);
     }
-    const float half_scale = 0.5f * scale;     // the bins below are doubled
     const float2* const srow = stage + rr_r * kStageStride + 16 * q_r + q_r;   // = stage_at(rr_r, 16 q_r)
 
     const int64_t nwaves = (int64_t)gridDim.x * kPrunedWaves;
@@ -193,18 +197,18 @@ __global__ __launch_bounds__(kPrunedThreads) __attribute__((amdgpu_waves_per_eu(
                 const float2 w4 = cmul(w2, w2);
                 const float2 w8 = cmul(w4, w4);
 #pragma unroll
-                for (int t = 0; t < 8; ++t) v[t] = cadd(v[2 * t], cmul(w1, v[2 * t + 1]));
+                for (int t = 0; t < 8; ++t) v[t] = cfma(v[2 * t], w1, v[2 * t + 1]);
 #pragma unroll
-                for (int t = 0; t < 4; ++t) v[t] = cadd(v[2 * t], cmul(w2, v[2 * t + 1]));
+                for (int t = 0; t < 4; ++t) v[t] = cfma(v[2 * t], w2, v[2 * t + 1]);
 #pragma unroll
-                for (int t = 0; t < 2; ++t) v[t] = cadd(v[2 * t], cmul(w4, v[2 * t + 1]));
-                float2 acc = cmul(vk[ch], cadd(v[0], cmul(w8, v[1])));
+                for (int t = 0; t < 2; ++t) v[t] = cfma(v[2 * t], w4, v[2 * t + 1]);
+                float2 acc = cmul(vk[ch], cfma(v[0], w8, v[1]));
                 acc.x += xchg1(acc.x);
                 acc.y += xchg1(acc.y);
                 acc.x += xchg2(acc.x);
                 acc.y += xchg2(acc.y);
                 const int k = RPC * ch + rr_r + Q * jj_r;
-                if (q_r == 0 && k < my) dst[k] = cscale(acc, half_scale);
+                if (q_r == 0 && k < my) dst[k] = acc;
                 wave_lds_sync();
             }
         });
@@ -225,8 +229,12 @@ __global__ __launch_bounds__(kPrunedThreads) __attribute__((amdgpu_waves_per_eu(
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     float2* const xrow = xrow_all[wave];
+    // The Hermitian part below is H[r] = (scale / 2) (V[r] + conj V[-r]) with
+    // V[r] = sum c_k X[k] ..., c_0 = 1, c_k = 2 otherwise.  With X[0] halved
+    // on load every c_k is 2, and the factor 2 (scale / 2) = scale rides on
+    // the residue factors.
     LaneTwiddles<Q, true> tws;
-    tws.init(tw, lane, table);
+    tws.init(tw, lane, table, scale);
     if constexpr (Q == 64) __syncthreads();
 
     const int64_t nwaves = (int64_t)gridDim.x * kPrunedWaves;
@@ -235,32 +243,25 @@ __global__ __launch_bounds__(kPrunedThreads) __attribute__((amdgpu_waves_per_eu(
         // the row's kept bins, zero past my, DC imaginary part dropped
         {
             float2 v = lane < my ? y[row * (int64_t)y_ld + lane] : make_float2(0.0f, 0.0f);
-            if (lane == 0) v.y = 0.0f;
+            if (lane == 0) v = make_float2(0.5f * v.x, 0.0f);
             xrow[lane] = v;
         }
         wave_lds_sync();
-        // V[r] = conj(W^{n1 r}) sum_j c_k X[k] conj(W_64^{n1 j}), k = r + Q j,
-        // c_0 = 1, c_k = 2
+        // V[r] / 2 = conj(W^{n1 r}) sum_j X'[k] conj(W_64^{n1 j}), k = r + Q j
+        // (X' = X with X[0] halved), times scale through the residue factor
         auto vres = [&](auto r) __attribute__((always_inline)) {
-            float2 acc = make_float2(0.0f, 0.0f);
-            static_for<0, 64 / Q>([&](auto j) {
-                constexpr int k = r + Q * j;
-                constexpr float c = k == 0 ? 1.0f : 2.0f;
-                float2 u = xrow[k];
-                if constexpr (j > 0) u = cmul(u, conj2(tws.pj[j]));
-                acc = make_float2(fmaf(c, u.x, acc.x), fmaf(c, u.y, acc.y));
-            });
+            float2 acc = xrow[r];
+            static_for<1, 64 / Q>([&](auto j) { acc = cfma(acc, xrow[r + Q * j], conj2(tws.pj[j])); });
             return cmul(acc, conj2(tws.template res<r>(lane)));
         };
-        // Hermitian part H[r] = (V[r] + conj V[-r]) / 2, r <= Q/2, scaled,
+        // Hermitian part H[r] = (scale / 2) (V[r] + conj V[-r]), r <= Q/2,
         // each pair V[r], V[Q - r] formed where it is used
         float2 H[NZ + 1];
         static_for<0, NZ + 1>([&](auto r) {
             constexpr int rm = (Q - r) % Q;
             const float2 a = vres(r);
             const float2 b = (rm == r) ? a : vres(std::integral_constant<int, rm>{});
-            const float h = 0.5f * scale;
-            H[r] = make_float2(h * (a.x + b.x), h * (a.y - b.y));
+            H[r] = make_float2(a.x + b.x, a.y - b.y);
         });
         wave_lds_sync();                        // the row buffer is read before the next row overwrites it
         float2 z[NZ];
