@@ -238,11 +238,19 @@ __global__ __launch_bounds__(kPrunedThreads) __attribute__((amdgpu_waves_per_eu(
     if constexpr (Q == 64) __syncthreads();
 
     const int64_t nwaves = (int64_t)gridDim.x * kPrunedWaves;
-    for (int64_t row = (int64_t)blockIdx.x * kPrunedWaves + wave; row < nrows; row += nwaves) {
+    const int64_t row0 = (int64_t)blockIdx.x * kPrunedWaves + wave;
+    // the next row's kept bins are loaded while this row is transformed
+    // (the last row of a wave reloads itself)
+    auto load_bins = [&](int64_t r) __attribute__((always_inline)) {
+        return lane < my ? y[r * (int64_t)y_ld + lane] : make_float2(0.0f, 0.0f);
+    };
+    float2 vn = row0 < nrows ? load_bins(row0) : make_float2(0.0f, 0.0f);
+    for (int64_t row = row0; row < nrows; row += nwaves) {
         if constexpr (Q <= 32) tws.opaque();
         // the row's kept bins, zero past my, DC imaginary part dropped
         {
-            float2 v = lane < my ? y[row * (int64_t)y_ld + lane] : make_float2(0.0f, 0.0f);
+            float2 v = vn;
+            vn = load_bins(row + nwaves < nrows ? row + nwaves : row);
             if (lane == 0) v = make_float2(0.5f * v.x, 0.0f);
             xrow[lane] = v;
         }
