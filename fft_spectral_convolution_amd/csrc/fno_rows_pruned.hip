@@ -138,15 +138,20 @@ __global__ __launch_bounds__(kPrunedThreads) __attribute__((amdgpu_waves_per_eu(
     constexpr int NZ = Q / 2;
     // The kept bins k < 64 fall on Q residues k mod Q, NJ = 64 / Q bins each.
     // A chunk stages RPC residues: stage row rr of chunk ch holds lane n1's
-    // Y[RPC ch + rr], untwiddled.
+    // Y[RPC ch + rr], untwiddled.  For Q >= 16 a chunk holds 16 residues and
+    // each reading lane forms all NJ bins of its residue from one read of its
+    // 16 staged values (BPL = NJ bins per lane); for Q = 8 the chunk holds
+    // two residues and the bins of a residue fall on NJ lane groups.
     constexpr int NJ = 64 / Q;
-    constexpr int RPC = 16 / NJ;
+    constexpr int BPL = Q >= 16 ? NJ : 1;
+    constexpr int RPC = 16 * BPL / NJ;
+    constexpr int NCHK = Q / RPC;
     __shared__ float2 stage_all[kPrunedWaves][RPC * kStageStride];
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     float2* const stage = stage_all[wave];
-    // Reduction role: lane (kk_r, q_r) forms bin k = RPC ch + rr_r + Q jj_r
-    // from lanes n1 = 16 q_r + t, t < 16:
+    // Reduction role: lane (kk_r, q_r) forms the bins k = RPC ch + rr_r +
+    // Q (BPL jj_r + b), b < BPL, from lanes n1 = 16 q_r + t, t < 16:
     //   sum_t W^{n1 k} Y_n1[k mod Q] = W^{16 q_r k} sum_t (W^k)^t Y_{16 q_r + t}
     // (the inner sum as a binary tree with factors W^k, W^2k, W^4k, W^8k),
     // and the four quarters q_r are added across neighbouring lanes.
@@ -154,22 +159,27 @@ __global__ __launch_bounds__(kPrunedThreads) __attribute__((amdgpu_waves_per_eu(
     const int q_r = lane & 3;
     const int rr_r = kk_r % RPC;
     const int jj_r = kk_r / RPC;
-    // W^k and W^{16 q_r k} of the lane's bin in each chunk, the latter times
+    // W^k and W^{16 q_r k} of the lane's bins in each chunk, the latter times
     // the output scale (halved: the bins below are doubled)
-    float2 wk[4], vk[4];
+    float2 wk[NCHK][BPL], vk[NCHK][BPL];
     const float half_scale = 0.5f * scale;
 #pragma unroll
-    for (int ch = 0; ch < 4; ++ch) {
-        const int k = RPC * ch + rr_r + Q * jj_r;
-        wk[ch] = tw[(k * (kNMax / N)) & (kNMax - 1)];
-        vk[ch] = cscale(tw[(16 * q_r * k * (kNMax / N)) & (kNMax - 1)], half_scale);
-    }
+    for (int ch = 0; ch < NCHK; ++ch)
+#pragma unroll
+        for (int b = 0; b < BPL; ++b) {
+            const int k = RPC * ch + rr_r + Q * (BPL * jj_r + b);
+            wk[ch][b] = tw[(k * (kNMax / N)) & (kNMax - 1)];
+            vk[ch][b] = cscale(tw[(16 * q_r * k * (kNMax / N)) & (kNMax - 1)], half_scale);
+        }
     const float2* const srow = stage + rr_r * kStageStride + 16 * q_r + q_r;   // = stage_at(rr_r, 16 q_r)
 
     const int64_t nwaves = (int64_t)gridDim.x * kPrunedWaves;
     for (int64_t row = (int64_t)blockIdx.x * kPrunedWaves + wave; row < nrows; row += nwaves) {
 #pragma unroll
-        for (int ch = 0; ch < 4; ++ch) asm volatile("" : "+v"(wk[ch].x), "+v"(wk[ch].y), "+v"(vk[ch].x), "+v"(vk[ch].y));
+        for (int ch = 0; ch < NCHK; ++ch)
+#pragma unroll
+            for (int b = 0; b < BPL; ++b)
+                asm volatile("" : "+v"(wk[ch][b].x), "+v"(wk[ch][b].y), "+v"(vk[ch][b].x), "+v"(vk[ch][b].y));
         const float* src = x + row * N + lane;
         float2 z[NZ];
 #pragma unroll
@@ -183,7 +193,7 @@ __global__ __launch_bounds__(kPrunedThreads) __attribute__((amdgpu_waves_per_eu(
         };
 
         float2* const dst = y + row * (int64_t)y_ld;
-        static_for<0, 4>([&](auto ch) {
+        static_for<0, NCHK>([&](auto ch) {
             if (RPC * ch < my) {                // uniform: chunks with a kept bin
                 static_for<0, RPC>([&](auto rr) {
                     stage[stage_at(rr, lane)] = ybin(std::integral_constant<int, RPC * ch + rr>{});
@@ -192,23 +202,31 @@ __global__ __launch_bounds__(kPrunedThreads) __attribute__((amdgpu_waves_per_eu(
                 float2 v[16];
 #pragma unroll
                 for (int t = 0; t < 16; ++t) v[t] = srow[t];
-                const float2 w1 = wk[ch];
-                const float2 w2 = cmul(w1, w1);
-                const float2 w4 = cmul(w2, w2);
-                const float2 w8 = cmul(w4, w4);
+                // first level of every bin's tree (v is dead after it), then
+                // the rest of each tree
+                float2 u[BPL][8];
+                static_for<0, BPL>([&](auto b) {
 #pragma unroll
-                for (int t = 0; t < 8; ++t) v[t] = cfma(v[2 * t], w1, v[2 * t + 1]);
+                    for (int t = 0; t < 8; ++t) u[b][t] = cfma(v[2 * t], wk[ch][b], v[2 * t + 1]);
+                });
+                static_for<0, BPL>([&](auto b) {
+                    if (b == 0 || RPC * ch + Q * b < my) {      // uniform: a kept bin in this group
+                        const float2 w2 = cmul(wk[ch][b], wk[ch][b]);
+                        const float2 w4 = cmul(w2, w2);
+                        const float2 w8 = cmul(w4, w4);
 #pragma unroll
-                for (int t = 0; t < 4; ++t) v[t] = cfma(v[2 * t], w2, v[2 * t + 1]);
+                        for (int t = 0; t < 4; ++t) u[b][t] = cfma(u[b][2 * t], w2, u[b][2 * t + 1]);
 #pragma unroll
-                for (int t = 0; t < 2; ++t) v[t] = cfma(v[2 * t], w4, v[2 * t + 1]);
-                float2 acc = cmul(vk[ch], cfma(v[0], w8, v[1]));
-                acc.x += xchg1(acc.x);
-                acc.y += xchg1(acc.y);
-                acc.x += xchg2(acc.x);
-                acc.y += xchg2(acc.y);
-                const int k = RPC * ch + rr_r + Q * jj_r;
-                if (q_r == 0 && k < my) dst[k] = acc;
+                        for (int t = 0; t < 2; ++t) u[b][t] = cfma(u[b][2 * t], w4, u[b][2 * t + 1]);
+                        float2 acc = cmul(vk[ch][b], cfma(u[b][0], w8, u[b][1]));
+                        acc.x += xchg1(acc.x);
+                        acc.y += xchg1(acc.y);
+                        acc.x += xchg2(acc.x);
+                        acc.y += xchg2(acc.y);
+                        const int k = RPC * ch + rr_r + Q * (BPL * jj_r + b);
+                        if (q_r == 0 && k < my) dst[k] = acc;
+                    }
+                });
                 wave_lds_sync();
             }
         });

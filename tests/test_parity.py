@@ -199,6 +199,8 @@ EDGE_1D = [
     (5, 3, 2, 512, 64),             # pruned rows, 8 samples per lane, bins wrap mod 8
     (3, 2, 3, 1024, 1),             # pruned rows, DC only
     (4, 3, 5, 2048, 37),            # pruned rows, partial last chunk of 16 bins
+    (2, 2, 3, 2048, 16),            # pruned rows: only the first 16 residues staged
+    (3, 1, 2, 1024, 17),            # pruned rows: one bin in the second group of each residue
     (9, 2, 2, 4096, 17),            # pruned rows, odd row count
 ]
 
