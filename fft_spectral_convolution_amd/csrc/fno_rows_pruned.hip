@@ -146,7 +146,10 @@ __global__ __launch_bounds__(kPrunedThreads) __attribute__((amdgpu_waves_per_eu(
     constexpr int BPL = Q >= 16 ? NJ : 1;
     constexpr int RPC = 16 * BPL / NJ;
     constexpr int NCHK = Q / RPC;
-    __shared__ float2 stage_all[kPrunedWaves][RPC * kStageStride];
+    // The lane's residues above Q/2 are the conjugates of those below
+    // (its samples are real): only rows r <= Q/2 are staged, once per row.
+    constexpr int SROWS = NZ + 1;
+    __shared__ float2 stage_all[kPrunedWaves][SROWS * kStageStride];
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     float2* const stage = stage_all[wave];
@@ -160,7 +163,10 @@ __global__ __launch_bounds__(kPrunedThreads) __attribute__((amdgpu_waves_per_eu(
     const int rr_r = kk_r % RPC;
     const int jj_r = kk_r / RPC;
     // W^k and W^{16 q_r k} of the lane's bins in each chunk, the latter times
-    // the output scale (halved: the bins below are doubled)
+    // the output scale (halved: the bins below are doubled).  A residue
+    // r > Q/2 reads the staged row Q - r, i.e. conj(Y[r]); its factors are
+    // conjugated too, so that the tree yields the conjugate of the bin, and
+    // the sign of the imaginary part is restored on the store.
     float2 wk[NCHK][BPL], vk[NCHK][BPL];
     const float half_scale = 0.5f * scale;
 #pragma unroll
@@ -168,10 +174,18 @@ __global__ __launch_bounds__(kPrunedThreads) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
         for (int b = 0; b < BPL; ++b) {
             const int k = RPC * ch + rr_r + Q * (BPL * jj_r + b);
-            wk[ch][b] = tw[(k * (kNMax / N)) & (kNMax - 1)];
-            vk[ch][b] = cscale(tw[(16 * q_r * k * (kNMax / N)) & (kNMax - 1)], half_scale);
+            const bool cj = RPC * ch + rr_r > NZ;
+            const float2 w = tw[(k * (kNMax / N)) & (kNMax - 1)];
+            const float2 u = cscale(tw[(16 * q_r * k * (kNMax / N)) & (kNMax - 1)], half_scale);
+            wk[ch][b] = cj ? conj2(w) : w;
+            vk[ch][b] = cj ? conj2(u) : u;
         }
-    const float2* const srow = stage + rr_r * kStageStride + 16 * q_r + q_r;   // = stage_at(rr_r, 16 q_r)
+    // staged row of the lane's residue in chunk ch, and the sign of the
+    // stored imaginary part
+    auto srow_of = [&](int ch) __attribute__((always_inline)) {
+        const int r = RPC * ch + rr_r;
+        return stage + (r > NZ ? Q - r : r) * kStageStride + 16 * q_r + q_r;   // = stage_at(row, 16 q_r)
+    };
 
     const int64_t nwaves = (int64_t)gridDim.x * kPrunedWaves;
     for (int64_t row = (int64_t)blockIdx.x * kPrunedWaves + wave; row < nrows; row += nwaves) {
@@ -185,20 +199,15 @@ __global__ __launch_bounds__(kPrunedThreads) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
         for (int m = 0; m < NZ; ++m) z[m] = make_float2(src[64 * (2 * m)], src[64 * (2 * m + 1)]);
         dft<NZ, -1>(z);
-        float2 Y2[NZ + 1];
-        static_for<0, NZ + 1>([&](auto k) { Y2[k] = real_bin2<Q, k>(z); });
-        auto ybin = [&](auto r) __attribute__((always_inline)) {    // 2 Y[r], r < Q
-            if constexpr (r <= NZ) return Y2[r <= NZ ? r : 0];
-            else return conj2(Y2[r <= NZ ? 0 : Q - r]);
-        };
+        // 2 Y[r], r <= Q/2, staged
+        static_for<0, SROWS>([&](auto r) { stage[stage_at(r, lane)] = real_bin2<Q, r>(z); });
+        wave_lds_sync();
 
         float2* const dst = y + row * (int64_t)y_ld;
         static_for<0, NCHK>([&](auto ch) {
             if (RPC * ch < my) {                // uniform: chunks with a kept bin
-                static_for<0, RPC>([&](auto rr) {
-                    stage[stage_at(rr, lane)] = ybin(std::integral_constant<int, RPC * ch + rr>{});
-                });
-                wave_lds_sync();
+                const float2* const srow = srow_of(ch);
+                const bool cj = RPC * ch + rr_r > NZ;
                 float2 v[16];
 #pragma unroll
                 for (int t = 0; t < 16; ++t) v[t] = srow[t];
@@ -224,12 +233,12 @@ __global__ __launch_bounds__(kPrunedThreads) __attribute__((amdgpu_waves_per_eu(
                         acc.x += xchg2(acc.x);
                         acc.y += xchg2(acc.y);
                         const int k = RPC * ch + rr_r + Q * (BPL * jj_r + b);
-                        if (q_r == 0 && k < my) dst[k] = acc;
+                        if (q_r == 0 && k < my) dst[k] = cj ? conj2(acc) : acc;
                     }
                 });
-                wave_lds_sync();
             }
         });
+        wave_lds_sync();                        // the stage is read before the next row overwrites it
     }
 }
 
