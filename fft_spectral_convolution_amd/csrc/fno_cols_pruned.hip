@@ -10,11 +10,18 @@
 //   R'[n1 + 64 n2] = sum_r W_Q^{-n2 r} V_n1[r],   V_n1[r] = sum_{kept k = r mod Q} W^{-n1 k} X[k].
 // A workgroup of 512 threads takes one image and 8 neighbouring columns;
 // thread (n1, c) holds column c's samples n1 + 64 n2 (so a wave's loads and
-// stores touch eight 64-byte runs), runs its Q-point DFT in registers and
-// the 64-way sums over n1 go through LDS, 8 kept modes at a time.  The
-// twiddles W^{n1 k} of the kept modes are tabulated once per workgroup in LDS
-// from the host-built table.  2 mx must be a multiple of Q: then a kept
-// mode's residue mod Q is its index's, and every register index is static.
+// stores touch eight 64-byte runs) and runs its Q-point DFT in registers.
+// 2 mx must be a multiple of Q: then a kept mode's residue mod Q is its
+// index's, and every register index is static.
+// Forward: every Y_n1[r] is staged in LDS once; a reading lane (residue r,
+// column, quarter p of the phases) sums its 16 phases n1 = 16 p + t for four
+// kept modes k of that residue at once, as
+//   W^{16 p k} sum_t (W^k)^t Y_{16 p + t}[r]
+// (a binary tree with the factors W^k, W^2k, W^4k, W^8k), and the quarters
+// are added across the lane quad.
+// Inverse: the twiddles W^{-n1 k} of the kept modes are tabulated once per
+// workgroup in LDS from the host-built table; each thread accumulates its
+// V_n1[r] from the kept modes in LDS.
 #include "fno_device.hpp"
 #include "fno_internal.hpp"
 
@@ -24,7 +31,6 @@ namespace {
 constexpr int kColThreads = 512;
 constexpr int kColC = 8;                 // columns per workgroup
 constexpr int kMaxKept = 128;            // 2 mx
-constexpr int kRedStride = 64 * 9;       // reduction buffer: [kk][n1] rows of 9 (8 columns + pad)
 
 // Twiddle table T[q][n1] = W^{n1 k_q} for the kept modes k_q (q < 2 mx).
 // Every thread issues all of its (at most 16) table reads before it writes
@@ -48,13 +54,18 @@ __device__ __forceinline__ void fill_twiddles(float2* T, int mx, const float2* _
     }
 }
 
+constexpr int kColStage = 68;            // forward stage row stride (complex): 64 phases + pad
+
+// index of (stage row, phase n1) in the forward stage
+__device__ __forceinline__ int col_stage_at(int row, int n1) { return row * kColStage + n1 + (n1 >> 4); }
+
 template <int Q>
 __global__ __launch_bounds__(kColThreads) void k_cols_fwd_pruned(const float2* __restrict__ r,
                                                                  float2* __restrict__ xh, int nkb, int mx, int my,
                                                                  float scale, const float2* __restrict__ tw) {
     constexpr int H = 64 * Q;
-    __shared__ float2 T[kMaxKept * 64];              // 64 KiB
-    __shared__ float2 red[kColC * kRedStride];       // 36 KiB
+    constexpr int NRH = 2;                           // reading roles per thread
+    __shared__ float2 stage[Q * kColC * kColStage];  // row (residue r, column c): Y_n1[r] of the 64 phases
     const int tid = threadIdx.x;
     const int c = tid & 7;                           // column within the block
     const int n1 = tid >> 3;                         // row phase
@@ -63,48 +74,72 @@ __global__ __launch_bounds__(kColThreads) void k_cols_fwd_pruned(const float2* _
     // so that L2 fetches each line once
     const int64_t blk = paired_image(blockIdx.x, (int64_t)gridDim.x);
     const int64_t img = blk / nkb;
-    const int ky = (int)(blk % nkb) * kColC + c;
-    const bool cok = ky < my;
-    const int kyc = cok ? ky : my - 1;
+    const int ky0 = (int)(blk % nkb) * kColC;
+    const int ky = ky0 + c;
+    const int kyc = ky < my ? ky : my - 1;
+    const int nk = 2 * mx;
 
-    // column samples n1 + 64 n2 (issued first, so that the twiddle table is
-    // built while they are in flight) -> Q-point DFT in registers
+    // column samples n1 + 64 n2 (issued first, so that the twiddles below
+    // are fetched while they are in flight)
     const float2* src = r + img * (int64_t)H * my + kyc;
     float2 v[Q];
 #pragma unroll
     for (int n2 = 0; n2 < Q; ++n2) v[n2] = src[(int64_t)(n1 + 64 * n2) * my];
-    fill_twiddles<H>(T, mx, tw, -1);
-    dft<Q, -1>(v);
-    __syncthreads();                                 // twiddle table complete
 
-    float2* const dst = xh + img * (int64_t)(2 * mx) * my;
-    const int nk = 2 * mx;
-    // reduction role: (kk = wave, column c, eighth p of the 64 phases)
-    const int kk_r = tid >> 6;
-    const int p_r = (tid >> 3) & 7;
-    // kept mode q is k_q = q or H - 2 mx + q; 2 mx is a multiple of Q, so
-    // k_q mod Q = q mod Q and every register index below is static
-    static_for<0, kMaxKept / 8>([&](auto ch) {
-        if (8 * ch < nk) {                           // uniform: chunks of 8 kept modes
-            static_for<0, 8>([&](auto kk) {
-                constexpr int q = 8 * ch + kk;
-                red[kk * kRedStride + n1 * 9 + c] = cmul(T[(q < nk ? q : 0) * 64 + n1], v[q % Q]);
-            });
-            __syncthreads();
-            float2 acc = make_float2(0.0f, 0.0f);
+    // Reading role rho = tid + 512 h: quad lane p = rho & 3, column
+    // cr = (rho >> 2) & 7, residue group g = rho >> 5 (residue g mod Q, kept
+    // modes q = g mod Q + Q (4 (g div Q) + b), b < 4; 2 mx <= 128 gives at
+    // most 32 groups).  Kept mode q is k_q = q or H - 2 mx + q; modes past
+    // 2 mx take k = 0 and are not stored.
+    float2 wk[NRH][4], vk[NRH][4];
 #pragma unroll
-            for (int t = 0; t < 8; ++t) acc = cadd(acc, red[kk_r * kRedStride + (8 * p_r + t) * 9 + c]);
-            // sum over the 8 lanes c + 8 p of the wave
+    for (int h = 0; h < NRH; ++h) {
+        const int rho = tid + kColThreads * h;
+        const int p = rho & 3, g = rho >> 5;
 #pragma unroll
-            for (int m = 8; m < 64; m <<= 1) {
-                acc.x += __shfl_xor(acc.x, m);
-                acc.y += __shfl_xor(acc.y, m);
-            }
-            const int q = 8 * ch + kk_r;
-            if (p_r == 0 && cok && q < nk) dst[(int64_t)q * my + ky] = cscale(acc, scale);
-            __syncthreads();
+        for (int b = 0; b < 4; ++b) {
+            const int q = g % Q + Q * (4 * (g / Q) + b);
+            const int k = q < nk ? (q < mx ? q : H - nk + q) : 0;
+            wk[h][b] = tw[((int64_t)k * (kNMax / H)) & (kNMax - 1)];
+            vk[h][b] = cscale(tw[((int64_t)16 * p * k * (kNMax / H)) & (kNMax - 1)], scale);
         }
-    });
+    }
+    dft<Q, -1>(v);
+#pragma unroll
+    for (int rr = 0; rr < Q; ++rr) stage[col_stage_at(rr * kColC + c, n1)] = v[rr];
+    __syncthreads();
+
+    float2* const dst = xh + img * (int64_t)nk * my;
+#pragma unroll
+    for (int h = 0; h < NRH; ++h) {
+        const int rho = tid + kColThreads * h;
+        const int p = rho & 3, cr = (rho >> 2) & 7, g = rho >> 5;
+        const int rr = g % Q;
+        const float2* const srow = stage + col_stage_at(rr * kColC + cr, 16 * p);
+        float2 s16[16];
+#pragma unroll
+        for (int t = 0; t < 16; ++t) s16[t] = srow[t];
+        // first level of every mode's tree (s16 is dead after it), then the
+        // rest of each tree
+        float2 u[4][8];
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+#pragma unroll
+            for (int t = 0; t < 8; ++t) u[b][t] = cfma(s16[2 * t], wk[h][b], s16[2 * t + 1]);
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const float2 w2 = cmul(wk[h][b], wk[h][b]);
+            const float2 w4 = cmul(w2, w2);
+            const float2 w8 = cmul(w4, w4);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) u[b][t] = cfma(u[b][2 * t], w2, u[b][2 * t + 1]);
+#pragma unroll
+            for (int t = 0; t < 2; ++t) u[b][t] = cfma(u[b][2 * t], w4, u[b][2 * t + 1]);
+            const float2 acc = quad_sum(cmul(vk[h][b], cfma(u[b][0], w8, u[b][1])));
+            const int q = rr + Q * (4 * (g / Q) + b);
+            if (p == 0 && q < nk && ky0 + cr < my) dst[(int64_t)q * my + ky0 + cr] = acc;
+        }
+    }
 }
 
 template <int Q>

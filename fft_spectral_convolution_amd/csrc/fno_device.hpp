@@ -72,6 +72,7 @@ constexpr double exact_sin(int e, int n) { return exact_cos(e - n / 4, n); }
 __device__ __forceinline__ float2 cadd(float2 a, float2 b) { return make_float2(a.x + b.x, a.y + b.y); }
 __device__ __forceinline__ float2 csub(float2 a, float2 b) { return make_float2(a.x - b.x, a.y - b.y); }
 __device__ __forceinline__ float2 cscale(float2 a, float s) { return make_float2(a.x * s, a.y * s); }
+__device__ __forceinline__ float2 conj2(float2 a) { return make_float2(a.x, -a.y); }
 __device__ __forceinline__ float2 cmul(float2 a, float2 b) {
     // (a+bi)(c+di) = (ac-bd) + (ad+bc)i   (TurboFNO blog, section 2.2)
     return make_float2(a.x * b.x - a.y * b.y, a.x * b.y + a.y * b.x);
@@ -194,6 +195,15 @@ __device__ __forceinline__ void dft(float2 (&v)[R]) {
         static_for<0, HALF>([&](auto k) { bfly<SIGN, R, k>(e[k], o[k], v[k], v[k + HALF]); });
     }
 }
+
+// Sum of a value over the four lanes of its quad (DPP quad_perm [1,0,3,2]
+// then [2,3,0,1]); every lane of the quad gets the sum.  All four lanes must
+// be active.
+__device__ __forceinline__ float quad_sum1(float v) {
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+    return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float2 quad_sum(float2 v) { return make_float2(quad_sum1(v.x), quad_sum1(v.y)); }
 
 // Workgroup barrier that orders LDS accesses only: global loads issued before
 // it stay in flight (a plain __syncthreads would wait for them too), which

@@ -41,15 +41,6 @@ constexpr int kStageStride = 68;        // forward reduction stage row stride (c
 // index of (bin kk, lane n1) in a wave's forward reduction stage
 __device__ __forceinline__ int stage_at(int kk, int n1) { return kk * kStageStride + n1 + (n1 >> 4); }
 
-// Lane exchanges of the forward reduction's last two steps.
-__device__ __forceinline__ float xchg2(float v) {           // DPP quad_perm [2,3,0,1]
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
-}
-__device__ __forceinline__ float xchg1(float v) {           // DPP quad_perm [1,0,3,2]
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
-}
-
-__device__ __forceinline__ float2 conj2(float2 a) { return make_float2(a.x, -a.y); }
 
 // Residue-factored twiddles of a row of N = 64 Q points, lane n1:
 // W^{n1 k} = res(k mod Q) * W_64^{n1 (k div Q)} (W = exp(-2 pi i / N)).
@@ -228,10 +219,7 @@ __global__ __launch_bounds__(kPrunedThreads) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
                         for (int t = 0; t < 2; ++t) u[b][t] = cfma(u[b][2 * t], w4, u[b][2 * t + 1]);
                         float2 acc = cmul(vk[ch][b], cfma(u[b][0], w8, u[b][1]));
-                        acc.x += xchg1(acc.x);
-                        acc.y += xchg1(acc.y);
-                        acc.x += xchg2(acc.x);
-                        acc.y += xchg2(acc.y);
+                        acc = quad_sum(acc);
                         const int k = RPC * ch + rr_r + Q * (BPL * jj_r + b);
                         if (q_r == 0 && k < my) dst[k] = cj ? conj2(acc) : acc;
                     }
