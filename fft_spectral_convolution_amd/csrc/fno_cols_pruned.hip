@@ -152,8 +152,12 @@ __global__ __launch_bounds__(kColThreads) void k_cols_inv_pruned(const float2* _
     const int tid = threadIdx.x;
     const int c = tid & 7;
     const int n1 = tid >> 3;
-    const int64_t img = blockIdx.x / nkb;
-    const int ky0 = (blockIdx.x % nkb) * kColC;
+    // column blocks 2j and 2j + 1 (the two halves of every 128-byte line of
+    // the row spectrum) go to workgroups on the same XCD at the same time,
+    // so that L2 writes each line back whole
+    const int64_t blk = paired_image(blockIdx.x, (int64_t)gridDim.x);
+    const int64_t img = blk / nkb;
+    const int ky0 = (int)(blk % nkb) * kColC;
     const int ky = ky0 + c;
     const int nk = 2 * mx;
 
