@@ -78,7 +78,11 @@ __device__ __forceinline__ Tile tile_of(const TileGrid& tg, int t) {
 // layout), so X is read and Y written as float4; otherwise element-wise.
 // NCH: chunks of input channels per tile (even; chunks past Cin are zero).
 // NCB: 16-column MFMA blocks per tile (2 or 4); RB: 16-row blocks (1 or 2).
-template <int NCH, bool VEC, int NCB, int RB, bool TW>
+// ONE: the grid has exactly one workgroup per tile; every chunk's X and W
+// are fetched at once, staged together, and multiplied after one barrier
+// (nothing to pipeline across tiles; one memory round trip instead of one per
+// chunk pair).
+template <int NCH, bool VEC, int NCB, int RB, bool TW, bool ONE = false>
 __global__ __launch_bounds__(kMixThreads) void k_mix_mfma(const float2* __restrict__ xh, Addr ax,
                                                           const float2* __restrict__ w, float2* __restrict__ yh,
                                                           Addr ay, int B, int Cin, int Cout, int M, TileGrid tg) {
@@ -95,7 +99,8 @@ __global__ __launch_bounds__(kMixThreads) void k_mix_mfma(const float2* __restri
     constexpr int kAI = 8 * kAM;                           // channel stride: 16 mod 32
     constexpr int kAChunk = kMixKC * kAI;
     constexpr int kYS = kO + 4;                            // [b8][m][o] row stride (16-byte rows, 4 mod 8)
-    __shared__ float2 a_lds[2 * kAChunk];                  // 2 x 17 KiB
+    static_assert(!ONE || (!TW && NCB == 2 && NCH <= 8), "one-shot tiles: forward, 32 columns, <= 64 channels");
+    __shared__ float2 a_lds[(ONE ? NCH : 2) * kAChunk];    // 2 (or NCH) x 17 KiB
     __shared__ __attribute__((aligned(16))) float2 y_lds[8 * 8 * kYS];   // 18 or 34 KiB
 
     const int tid = threadIdx.x;
@@ -287,6 +292,28 @@ __global__ __launch_bounds__(kMixThreads) void k_mix_mfma(const float2* __restri
     const int j = G % 8 == 0 ? (int)(blockIdx.x % 8) * (G / 8) + (int)(blockIdx.x / 8) : (int)blockIdx.x;
     const int t_begin = (int)((int64_t)tg.n_tiles * j / G);
     const int t_end = (int)((int64_t)tg.n_tiles * (j + 1) / G);
+    if constexpr (ONE) {
+        const Tile one = tile_of<kB, kO>(tg, t_begin);       // t_end == t_begin + 1
+        float2 av[NCH][4];
+        float2 wv[NCH][2 * NCB];
+        static_for<0, NCH>([&](auto c) {
+            load_a(one, c, av[c]);
+            load_w(one, c, wv[c]);
+        });
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb) {
+                p1[rb][cb] = floatx4{0.f, 0.f, 0.f, 0.f};
+                p2[rb][cb] = floatx4{0.f, 0.f, 0.f, 0.f};
+                p3[rb][cb] = floatx4{0.f, 0.f, 0.f, 0.f};
+            }
+        static_for<0, NCH>([&](auto c) { store_a(c, av[c], a_lds + c * kAChunk); });
+        lds_barrier();
+        static_for<0, NCH>([&](auto c) { mfma_chunk(a_lds + c * kAChunk, wv[c]); });
+        epilogue(one);
+        return;
+    }
     int t = t_begin;
     Tile cur = tile_of<kB, kO>(tg, t);
     Tile nxt = tile_of<kB, kO>(tg, t + 1 < t_end ? t + 1 : t);
@@ -330,18 +357,25 @@ __global__ __launch_bounds__(kMixThreads) void k_mix_mfma(const float2* __restri
     }
 }
 
-template <bool VEC, int NCB, int RB, bool TW = false>
+template <bool VEC, int NCB, int RB, bool TW = false, bool ONE = false>
 hipError_t launch_mix_variant(dim3 grid, hipStream_t s, const float2* xh, Addr ax, const float2* w, float2* yh, Addr ay,
                         int B, int Cin, int Cout, int M, TileGrid tg, int nch) {
 #define CASE(N)                                                                                                   \
     case N:                                                                                                       \
-        return launch_kernel((k_mix_mfma<N, VEC, NCB, RB, TW>), grid, dim3(kMixThreads), 0, s, xh, ax, w, yh, ay, B, Cin, \
-                           Cout, M, tg);
+        return launch_kernel((k_mix_mfma<N, VEC, NCB, RB, TW, ONE>), grid, dim3(kMixThreads), 0, s, xh, ax, w, yh, ay, B, \
+                           Cin, Cout, M, tg);
+    if constexpr (ONE) {
+        switch (nch) {
+            CASE(2) CASE(4) CASE(6) CASE(8)
+            default: break;
+        }
+        return hipErrorInvalidValue;
+    }
     switch (nch) {
         CASE(2) CASE(4) CASE(6) CASE(8)
         default: break;
     }
-    if constexpr (NCB == 2) {               // the 64-column tiles take at most 8 chunks
+    if constexpr (NCB == 2 && !ONE) {       // the 64-column tiles take at most 8 chunks
         switch (nch) {
             CASE(10) CASE(12) CASE(14) CASE(16)
             default: break;
@@ -416,6 +450,12 @@ hipError_t launch_mix_mfma(const float2* xh, const SpecLayout& lx, const float2*
     }
     if (wide && !short_b) return launch_mix_variant<true, 4, 2>(grid, s, xh, ax, w, yh, ay, iB, iCin, iCout, iM, tg, nch);
     if (wide) return launch_mix_variant<true, 4, 1>(grid, s, xh, ax, w, yh, ay, iB, iCin, iCout, iM, tg, nch);
+    // one workgroup per tile with 32-column tiles and <= 64 channels: one-shot tiles
+    const bool one = n_tiles <= cus && nch <= 8;
+    if (vec && !short_b && one)
+        return launch_mix_variant<true, 2, 2, false, true>(grid, s, xh, ax, w, yh, ay, iB, iCin, iCout, iM, tg, nch);
+    if (vec && short_b && one)
+        return launch_mix_variant<true, 2, 1, false, true>(grid, s, xh, ax, w, yh, ay, iB, iCin, iCout, iM, tg, nch);
     if (vec && !short_b) return launch_mix_variant<true, 2, 2>(grid, s, xh, ax, w, yh, ay, iB, iCin, iCout, iM, tg, nch);
     if (vec) return launch_mix_variant<true, 2, 1>(grid, s, xh, ax, w, yh, ay, iB, iCin, iCout, iM, tg, nch);
     if (!short_b) return launch_mix_variant<false, 2, 2>(grid, s, xh, ax, w, yh, ay, iB, iCin, iCout, iM, tg, nch);
