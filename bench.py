@@ -132,6 +132,7 @@ def compulsory_share(name: str, cfg, backward: bool = False) -> int:
         "mix_mfma": wb, "mix_valu": wb, "mix_mfma_adj": wb, "mix_fused": wb,
         "inv2d": n_out, "rows_inv": n_out, "inv2d_gelu": 2 * n_out, "rows_inv_gelu": 2 * n_out,
         "wgrad": wb, "wgrad_reduce": 0,
+        "conv_fused": n_in + wb + n_out,
     }
     return share.get(base, 0)
 

@@ -441,8 +441,22 @@ int run_unfused_1d(int64_t B, int64_t Cin, int64_t Cout, int N, int modes, const
 // Fastest schedule for the shape; the workspace size follows the schedule.
 size_t best_ws_2d(const Shape2d& s) { return small_path(s) ? fused_small_ws_2d(s) : unfused_ws_2d(s); }
 
+// Small problems (grids of at most 1024 points, at most 8 channels in and out): the
+// whole call as one kernel, one workgroup per batch item with its truncated
+// spectra in LDS (no workspace is used).
+bool one_kernel_path(const Shape2d& s) {
+    return small_path(s) && conv2d_small_fused_supported(s.B, s.Cin, s.Cout, s.log2H, s.log2W, s.mx, s.my);
+}
+
 int run_best_2d(const Shape2d& s, const float* x, const float2* w, float* out, void* ws, const float2* tw,
                 hipStream_t st, const Epilogue& epi = Epilogue{}) {
+    if (!epi.on && one_kernel_path(s)) {
+        rec_kernel("conv_fused", st);
+        const float scale = (float)(1.0 / std::sqrt((double)s.H * (double)s.W));
+        const hipError_t e =
+            launch_conv2d_small_fused(x, w, out, s.B, s.Cin, s.Cout, s.log2H, s.log2W, s.mx, s.my, scale, tw, st);
+        return e == hipSuccess ? FNO_OK : hip_fail(e);
+    }
     if (small_path(s)) return run_fused_small_2d(s, x, w, out, ws, tw, st, epi);
     return run_unfused_2d(s, x, w, out, ws, tw, st, epi);
 }

@@ -126,6 +126,14 @@ __device__ __forceinline__ float epi_apply(const Epilogue& e, float v, float bia
 
 // ---- fused small-grid transforms (fno_small2d.hip), H, W in [8, 128] --------
 bool small2d_supported(int log2H, int log2W, int my);
+// The whole 2D call in one kernel for small problems (grids of at most 1024
+// points, 8..128 per side, at most 8 channels in and out): one workgroup per
+// batch item, the truncated spectra in LDS; scale = (H W)^-1/2, applied on
+// both transforms.
+bool conv2d_small_fused_supported(int64_t B, int64_t Cin, int64_t Cout, int log2H, int log2W, int mx, int my);
+hipError_t launch_conv2d_small_fused(const float* x, const float2* w, float* out, int64_t B, int64_t Cin, int64_t Cout,
+                                     int log2H, int log2W, int mx, int my, float scale, const float2* tw,
+                                     hipStream_t s);
 hipError_t launch_fwd2d_small(const float* x, float2* xh, const SpecLayout& lay, int64_t nimg, int log2H, int log2W,
                               int mx, int my, float scale, const float2* tw, hipStream_t s);
 hipError_t launch_inv2d_small(const float2* yh, float* out, const SpecLayout& lay, int64_t nimg, int log2H,

@@ -70,6 +70,7 @@ def _replay_matches_eager(cfg, capture, eager, extra=None):
 
 
 FORWARD_2D = [
+    Config("g32f", "2d", 3, 4, 4, 32, 32, 8, 8, "uniform"),           # the whole call in one kernel
     Config("g64", "2d", 4, 16, 16, 64, 64, 16, 16, "uniform"),         # one-thread-per-row kernels
     Config("g128", "2d", 2, 64, 64, 128, 128, 32, 32, "uniform"),      # matrix-core mix
     Config("g512", "2d", 1, 4, 4, 512, 512, 32, 32, "uniform"),        # pruned rows and columns

@@ -151,6 +151,11 @@ def test_stages_1d(name):
 
 EDGE_2D = [
     # B, Cin, Cout, H, W, mx, my
+    (300, 2, 3, 32, 32, 8, 8),      # one-kernel small path: more batch items than CUs
+    (5, 8, 8, 32, 32, 16, 16),      # one-kernel small path: most channels (two rounds), every kx kept
+    (4, 7, 1, 16, 64, 8, 17),       # one-kernel small path: one output channel (idle groups in the inverse)
+    (2, 3, 3, 8, 128, 2, 40),       # one-kernel small path: 8 x 128 grid
+    (3, 1, 8, 8, 32, 4, 17),        # one-kernel small path: one input channel, Nyquist column kept
     (1, 1, 1, 2, 2, 1, 1),
     (1, 1, 1, 2, 2, 1, 2),          # full modes of a 2x2 grid (Nyquist column kept)
     (3, 5, 7, 8, 8, 4, 5),          # full modes, odd channel counts
