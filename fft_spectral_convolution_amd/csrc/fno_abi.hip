@@ -438,14 +438,20 @@ int run_unfused_1d(int64_t B, int64_t Cin, int64_t Cout, int N, int modes, const
     return FNO_OK;
 }
 
-// Fastest schedule for the shape; the workspace size follows the schedule.
-size_t best_ws_2d(const Shape2d& s) { return small_path(s) ? fused_small_ws_2d(s) : unfused_ws_2d(s); }
-
 // Small problems (grids of at most 1024 points, at most 8 channels in and out): the
 // whole call as one kernel, one workgroup per batch item with its truncated
 // spectra in LDS (no workspace is used).
 bool one_kernel_path(const Shape2d& s) {
     return small_path(s) && conv2d_small_fused_supported(s.B, s.Cin, s.Cout, s.log2H, s.log2W, s.mx, s.my);
+}
+
+// Workspace of the three-kernel small schedule or of the staged one.
+size_t staged_ws_2d(const Shape2d& s) { return small_path(s) ? fused_small_ws_2d(s) : unfused_ws_2d(s); }
+
+// Fastest schedule for the shape (epi: with the fused layer tail, which the
+// one-kernel schedule does not take); the workspace size follows the schedule.
+size_t best_ws_2d(const Shape2d& s, bool epi = false) {
+    return !epi && one_kernel_path(s) ? 0 : staged_ws_2d(s);
 }
 
 int run_best_2d(const Shape2d& s, const float* x, const float2* w, float* out, void* ws, const float2* tw,
@@ -520,7 +526,7 @@ int filter2d_common(const float* x, const void* mask, float* out, int B, int C, 
     rc = device_state(&st, stream);
     if (rc) return rc;
     void* ws = nullptr;
-    rc = internal_workspace(lease, st, best_ws_2d(s), &ws, stream);
+    rc = internal_workspace(lease, st, staged_ws_2d(s), &ws, stream);
     if (rc) return rc;
     hipStream_t hs = static_cast<hipStream_t>(stream);
     rec_begin();
@@ -792,7 +798,7 @@ int conv2d_common(const float* x, const void* w, float* out, int B, int Cin, int
     rc = check_conv(x, w, out, xbytes, wbytes, obytes);
     if (rc) return rc;
     const Shape2d s = make2d(B, Cin, Cout, H, W, mx, my);
-    const size_t need = unfused ? unfused_ws_2d(s) : best_ws_2d(s);
+    const size_t need = unfused ? unfused_ws_2d(s) : best_ws_2d(s, epi.on);
     void* ws = user_ws;
     if (use_user_ws) {
         if (user_ws_bytes < need || (need > 0 && !user_ws)) return FNO_ERR_WORKSPACE;

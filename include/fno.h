@@ -88,7 +88,12 @@ int fno_init(void);
 
 /*
  * 2D spectral convolution (TurboFNO blog, sections 1 and 2.2; FFT blog
- * sections 2.1-2.2).  Picks the fastest implemented schedule for the shape.
+ * sections 2.1-2.2).  Picks the fastest implemented schedule for the shape:
+ * grids of at most 1024 points with at most 8 channels in and out run as one
+ * kernel, one workgroup per batch item with its truncated spectra on chip
+ * (no workspace); other grids up to 128 per side as three kernels (forward,
+ * channel mix, inverse, the spectra in workspace); longer rows and taller
+ * grids as five (rows, columns, mix, columns, rows).
  * Uses an internal workspace per (device, stream), following the FFT blog's
  * plan and work-area reuse (sections 2.2 and 5.3): grow-only, allocated on
  * first use and kept until process exit, so calls on different streams may

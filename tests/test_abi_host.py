@@ -102,9 +102,12 @@ def test_conv1d_checks(lib):
 
 
 def test_ws_variant_checks(lib):
-    dims = (2, 3, 4, 16, 16, 4, 4)
+    dims = (2, 3, 4, 64, 64, 4, 4)          # three-kernel small schedule: spectra in workspace
     need = fno.fno_workspace_size_2d(*dims)
     assert need > 0
+    # grids of at most 1024 points with at most 8 channels run as one kernel, no workspace
+    assert fno.fno_workspace_size_2d(2, 3, 4, 16, 16, 4, 4) == 0
+    assert fno.fno_workspace_size_2d(2, 9, 4, 16, 16, 4, 4) > 0
     assert lib.fno_spectral_conv2d_ws(A, B, C, *dims, None, need, None) == WORKSPACE
     assert lib.fno_spectral_conv2d_ws(A, B, C, *dims, 0x40000000, need - 1, None) == WORKSPACE
     assert lib.fno_spectral_conv2d_ws(A, B, C, *dims, 0x40000010, need, None) == ALIGN
