@@ -95,8 +95,8 @@ def kernel_bytes(name: str, cfg, backward: bool = False) -> int:
         "rows_inv": (r_out if cfg.kind == "2d" else yh) + n_out,
         "fwd2d": n_in + xh,
         "inv2d": yh + n_out,
-        "fused2d": n_in + wb + n_out,
-        "fused1d": n_in + wb + n_out,
+        # the whole call in one kernel: the spectra never leave the chip
+        "conv_fused": n_in + wb + n_out,
         # backward pass: the weight gradient reads both truncated spectra and
         # writes a weight-sized gradient; the adjoint transposes the weight
         # fused layer tail: the inverse also reads the branch (output-sized)

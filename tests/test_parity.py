@@ -343,3 +343,34 @@ def test_bad_arguments_raise():
     with pytest.raises(fno.FnoError) as ei:
         fno.fno_spectral_conv2d(x, w, 5, 2)               # 2*mx > H
     assert ei.value.status == -3
+
+
+SCHEDULES = {
+    "c1": ["conv_fused"],                                   # the whole call in one kernel
+    "c2": ["fwd2d", "mix_mfma", "inv2d"],
+    "c3": ["fwd2d", "mix_mfma", "inv2d"],
+    "c4": ["rows_fwd", "mix_mfma", "rows_inv"],
+    "c5": ["rows_fwd", "cols_fwd", "mix_valu", "cols_inv", "rows_inv"],
+}
+
+
+@pytest.mark.parametrize("name", sorted(SCHEDULES))
+def test_schedule_selection(name):
+    # which kernels the plain call launches for each workload shape (the
+    # parity of each schedule is checked above; this pins the dispatch)
+    cfg = CONFIGS[name]
+    g = torch.Generator(device=DEV).manual_seed(0)
+    x = torch.rand(cfg.x_shape, device=DEV, generator=g)
+    w = torch.randn(cfg.w_shape, dtype=torch.complex64, device=DEV, generator=g)
+    if cfg.kind == "1d":
+        fno.fno_spectral_conv1d(x, w, cfg.my)
+    else:
+        fno.fno_spectral_conv2d(x, w, cfg.mx, cfg.my)
+    torch.cuda.synchronize()
+    assert fno.fno_last_kernels() == SCHEDULES[name]
+    if name == "c1":
+        # the ablation and the fused layer tail keep their own schedules
+        fno.fno_spectral_conv2d_unfused(x, w, cfg.mx, cfg.my)
+        assert fno.fno_last_kernels() == ["rows_fwd", "cols_fwd", "mix_valu", "cols_inv", "rows_inv"]
+        fno.fno_spectral_conv2d_gelu(x, w, cfg.mx, cfg.my)
+        assert fno.fno_last_kernels() == ["fwd2d", "mix_valu", "inv2d_gelu"]
