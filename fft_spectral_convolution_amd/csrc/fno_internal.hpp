@@ -59,6 +59,13 @@ inline bool stream_capturing(hipStream_t s) {
 }
 
 inline SpecLayout canonical_layout(int64_t C, int64_t M) { return SpecLayout{C * M, M, 8, (int)C}; }
+// The canonical layout with each channel's M modes padded to a whole number
+// of 8-mode runs (channel stride M rounded up to 8); the padding slots hold
+// no modes (the mix may write there).
+inline SpecLayout padded_layout(int64_t C, int64_t M) {
+    const int64_t mp = (M + 7) / 8 * 8;
+    return SpecLayout{C * mp, mp, 8, (int)C};
+}
 inline SpecLayout tiled_layout(int64_t C, int64_t M) {
     const int64_t nt = (M + 7) / 8;
     return SpecLayout{nt * C * 8, 8, C * 8, (int)C};
@@ -229,9 +236,11 @@ struct RowWindow {
 bool mixed_supported(int n);
 hipError_t launch_rows_fwd_mr(const float* x, float2* y, int64_t nrows, int W, int my, int y_ld, float scale,
                               hipStream_t s, const RowWindow* window = nullptr);
+// img_ld: the spectrum's image stride in complex elements (default 2 mx my)
 hipError_t launch_cols_fwd_mr(const float2* r, float2* xh, int64_t nimg, int H, int mx, int my, float scale,
-                              hipStream_t s);
-hipError_t launch_cols_inv_mr(const float2* yh, float2* r, int64_t nimg, int H, int mx, int my, hipStream_t s);
+                              hipStream_t s, int64_t img_ld = -1);
+hipError_t launch_cols_inv_mr(const float2* yh, float2* r, int64_t nimg, int H, int mx, int my, hipStream_t s,
+                              int64_t img_ld = -1);
 hipError_t launch_rows_inv_mr(const float2* y, float* out, int64_t nrows, int W, int my, int y_ld, float scale,
                               hipStream_t s, const Epilogue& epi = Epilogue{}, const RowWindow* window = nullptr);
 

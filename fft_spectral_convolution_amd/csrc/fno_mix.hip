@@ -390,12 +390,22 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 // Chunks of 8 input channels, rounded up to an even count.
 int64_t mix_chunks(int64_t Cin) { return ((Cin + kMixKC - 1) / kMixKC + 1) / 2 * 2; }
 
+// A canonical layout (8-mode runs contiguous) whose channels hold whole
+// runs past M: the last run's missing modes have slots of their own.  The
+// kernel reads those slots and writes their results back there (each mode
+// is a separate product, so nothing else depends on them).
+bool padded_runs(const SpecLayout& l, int64_t M) {
+    const int64_t mp = (M + 7) / 8 * 8;
+    return l.st == 8 && l.sc % 8 == 0 && l.sc >= mp && l.sb >= (int64_t)l.C * l.sc;
+}
+
 // float4 access needs every 8-mode run whole and 16-byte aligned: the tiled
-// layout has it, the canonical one when M is a multiple of 8 (all strides
-// even, 16-byte aligned bases).
+// layout has it, the canonical one when M is a multiple of 8 or its channels
+// are padded to whole runs (all strides even, 16-byte aligned bases).
 bool mix_vec(const float2* xh, const SpecLayout& lx, const float2* yh, const SpecLayout& ly, int64_t M) {
+    const bool whole = M % 8 == 0 || (padded_runs(lx, M) && padded_runs(ly, M));
     return lx.sc % 2 == 0 && ly.sc % 2 == 0 && lx.st % 2 == 0 && ly.st % 2 == 0 && lx.sb % 2 == 0 &&
-           ly.sb % 2 == 0 && M % 8 == 0 && aligned16(xh) && aligned16(yh);
+           ly.sb % 2 == 0 && whole && aligned16(xh) && aligned16(yh);
 }
 
 }  // namespace

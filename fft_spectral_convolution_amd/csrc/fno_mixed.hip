@@ -18,13 +18,24 @@
 namespace fno {
 namespace {
 
-constexpr int kMrThreads = 1024;   // 16 waves; the 64 KiB of LDS allow two workgroups per CU
+constexpr int kMrThreads = 1024;   // 16 waves; the 72 KiB of LDS allow two workgroups per CU
 constexpr int kMrMaxPasses = 12;
+constexpr int kMrTwLds = 1024;     // lengths up to this take their twiddle table from LDS
 
+// Passes of an n-point transform: radix r[p], J = n / r[p] butterflies per
+// row, ns[p] = product of the earlier radices, twiddle step n / (ns r); the
+// reciprocals of J and ns for qdiv.
 struct MRPlan {
     int n, npass;
-    int r[kMrMaxPasses];
+    int r[kMrMaxPasses], j[kMrMaxPasses], ns[kMrMaxPasses], step[kMrMaxPasses];
+    float inv_j[kMrMaxPasses], inv_ns[kMrMaxPasses];
 };
+
+// floor(x / d) for 0 <= x < 2^21, from inv = 1/d rounded to float (or within
+// one ulp of it): (x + 1/2) / d lies at least 1/(2d) from every integer,
+// and the product's relative error (below 2^-22) moves it by less than that.
+// All the index arithmetic here is below 2^13.
+__device__ __forceinline__ int qdiv(int x, float inv) { return (int)(((float)x + 0.5f) * inv); }
 
 // Radix-R DFT by its definition (R = 3, 5, 7), compile-time twiddles:
 // v[k] <- sum_r v[r] exp(SIGN 2 pi i r k / R).
@@ -48,21 +59,19 @@ __device__ __forceinline__ void dft_odd(float2 (&v)[R]) {
 
 // One radix-R Stockham pass of an n-point transform whose sub-transforms of
 // length ns are done: butterfly j reads src[j + r n/R], twiddles by
-// W_{ns R}^{r (j mod ns)}, runs the radix-R DFT and writes
-// dst[(j - j mod ns) R + j mod ns + r ns].
+// W_{ns R}^{r (j mod ns)} (= W_n^{r (j mod ns) step}, step = n / (ns R)),
+// runs the radix-R DFT and writes dst[(j - j mod ns) R + j mod ns + r ns].
 template <int R, int SIGN>
-__device__ __forceinline__ void mr_pass(const float2* src, float2* dst, int n, int ns, int j,
-                                        const float2* __restrict__ twn) {
-    const int stride = n / R;
+__device__ __forceinline__ void mr_pass(const float2* src, float2* dst, int stride, int ns, float inv_ns, int step,
+                                        int j, const float2* tws) {
     float2 v[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) v[r] = src[j + r * stride];
-    const int k = j % ns;
+    const int k = j - qdiv(j, inv_ns) * ns;
     if (ns > 1) {
-        const int step = n / (ns * R);
 #pragma unroll
         for (int r = 1; r < R; ++r) {
-            float2 t = twn[r * k * step];
+            float2 t = tws[r * k * step];
             if (SIGN > 0) t.y = -t.y;
             v[r] = cmul(v[r], t);
         }
@@ -76,35 +85,48 @@ __device__ __forceinline__ void mr_pass(const float2* src, float2* dst, int n, i
 
 // Full transform of `nrows` rows of length p.n (row stride p.n) in LDS
 // buffer a, ping-ponging through b; returns the buffer with the result.
+// tws: the twiddle table, in LDS or global memory.
 template <int SIGN>
-__device__ float2* fft_rows_mr(float2* a, float2* b, int nrows, const MRPlan& p, const float2* __restrict__ twn,
-                               int tid, int nthr) {
+__device__ __forceinline__ float2* fft_rows_mr(float2* a, float2* b, int nrows, const MRPlan& p, const float2* tws,
+                                               int tid, int nthr) {
     const int n = p.n;
-    int ns = 1;
     for (int pass = 0; pass < p.npass; ++pass) {
-        const int R = p.r[pass];
-        const int J = n / R;
+        const int R = p.r[pass], J = p.j[pass], ns = p.ns[pass], step = p.step[pass];
+        const float inv_j = p.inv_j[pass], inv_ns = p.inv_ns[pass];
         const int total = nrows * J;
         for (int idx = tid; idx < total; idx += nthr) {
-            const int row = idx / J;
+            const int row = qdiv(idx, inv_j);
             const int j = idx - row * J;
             float2* s = a + row * n;
             float2* d = b + row * n;
             switch (R) {
-                case 4: mr_pass<4, SIGN>(s, d, n, ns, j, twn); break;
-                case 2: mr_pass<2, SIGN>(s, d, n, ns, j, twn); break;
-                case 3: mr_pass<3, SIGN>(s, d, n, ns, j, twn); break;
-                case 5: mr_pass<5, SIGN>(s, d, n, ns, j, twn); break;
-                default: mr_pass<7, SIGN>(s, d, n, ns, j, twn); break;
+                case 4: mr_pass<4, SIGN>(s, d, J, ns, inv_ns, step, j, tws); break;
+                case 2: mr_pass<2, SIGN>(s, d, J, ns, inv_ns, step, j, tws); break;
+                case 3: mr_pass<3, SIGN>(s, d, J, ns, inv_ns, step, j, tws); break;
+                case 5: mr_pass<5, SIGN>(s, d, J, ns, inv_ns, step, j, tws); break;
+                default: mr_pass<7, SIGN>(s, d, J, ns, inv_ns, step, j, tws); break;
             }
         }
         __syncthreads();
         float2* t = a;
         a = b;
         b = t;
-        ns *= R;
     }
     return a;
+}
+
+// The twiddle table, copied into LDS when TWL (every thread's copy is
+// ordered before the first pass by the barrier that follows the loads).
+template <bool TWL>
+__device__ __forceinline__ const float2* twiddle_table(float2* lds, const float2* __restrict__ twn, int n, int tid,
+                                                       int nthr) {
+    if constexpr (TWL) {
+        for (int e = tid; e < n; e += nthr) lds[e] = twn[e];
+        return lds;
+    } else {
+        (void)lds;
+        return twn;
+    }
 }
 
 // rows of length W = p.n (real) -> bins ky < my, two rows per complex
@@ -112,35 +134,42 @@ __device__ float2* fft_rows_mr(float2* a, float2* b, int nrows, const MRPlan& p,
 // win: the rows are those of images of win.ph rows, and x holds only each
 // image's top-left win.h x win.w corner (the rest reads as zero: the
 // zero padding of a linear convolution).
+template <bool TWL>
 __global__ __launch_bounds__(kMrThreads) void k_rows_fwd_mr(const float* __restrict__ x, float2* __restrict__ y,
                                                             int64_t nrows, int my, int y_ld, float scale, MRPlan p,
                                                             const float2* __restrict__ twn, RowWindow win) {
     __shared__ float2 buf[2][kLdsElems];
+    __shared__ float2 twl[TWL ? kMrTwLds : 1];
     const int W = p.n;
     const int P = kLdsElems / W;
     const int tid = threadIdx.x;
+    const float inv_w = 1.0f / (float)W;
+    const float inv_my = 1.0f / (float)my;
+    const double inv_ph = 1.0 / (double)win.ph;
+    const float2* tws = twiddle_table<TWL>(twl, twn, W, tid, kMrThreads);
     const int64_t npairs = (nrows + 1) / 2;
     const int64_t pair0 = (int64_t)blockIdx.x * P;
     const int prows = (int)(npairs - pair0 < P ? npairs - pair0 : P);
     // sample n of row r: x's element when inside the window, else zero
-    // (row indices fit 32 bits when a window is used: checked on the host)
+    // (row indices fit 32 bits when a window is used: checked on the host;
+    // the image index is the quotient of r by win.ph, formed in double)
     auto sample = [&](int64_t r, int n) -> float {
         if (r >= nrows) return 0.0f;
         if (win.w == W && win.h == win.ph) return x[r * W + n];
-        const uint32_t img = (uint32_t)r / (uint32_t)win.ph;
+        const uint32_t img = (uint32_t)(((double)(uint32_t)r + 0.5) * inv_ph);
         const int q = (int)((uint32_t)r - img * (uint32_t)win.ph);
         return (q < win.h && n < win.w) ? x[((int64_t)img * win.h + q) * win.w + n] : 0.0f;
     };
     for (int e = tid; e < prows * W; e += kMrThreads) {
-        const int pr = e / W;
+        const int pr = qdiv(e, inv_w);
         const int n = e - pr * W;
         const int64_t ra = 2 * (pair0 + pr);
         buf[0][e] = make_float2(sample(ra, n), sample(ra + 1, n));
     }
     __syncthreads();
-    const float2* res = fft_rows_mr<-1>(buf[0], buf[1], prows, p, twn, tid, kMrThreads);
+    const float2* res = fft_rows_mr<-1>(buf[0], buf[1], prows, p, tws, tid, kMrThreads);
     for (int e = tid; e < prows * my; e += kMrThreads) {
-        const int pr = e / my;
+        const int pr = qdiv(e, inv_my);
         const int k = e - pr * my;
         const float2 zk = res[pr * W + k];
         const float2 zm = res[pr * W + (k == 0 ? 0 : W - k)];
@@ -152,60 +181,71 @@ __global__ __launch_bounds__(kMrThreads) void k_rows_fwd_mr(const float* __restr
     }
 }
 
-// R[nimg][H][my] -> xh[nimg][2 mx][my] (kept kx only), H = p.n
+// R[nimg][H][my] -> xh (kept kx only, image img at img * img_ld, mode
+// q my + ky), H = p.n
+template <bool TWL>
 __global__ __launch_bounds__(kMrThreads) void k_cols_fwd_mr(const float2* __restrict__ r, float2* __restrict__ xh,
-                                                            int mx, int my, int kb, int nkb, float scale, MRPlan p,
-                                                            const float2* __restrict__ twn) {
+                                                            int64_t img_ld, int mx, int my, int kb, int nkb,
+                                                            float scale, MRPlan p, const float2* __restrict__ twn) {
     __shared__ float2 buf[2][kLdsElems];
+    __shared__ float2 twl[TWL ? kMrTwLds : 1];
     const int H = p.n;
     const int tid = threadIdx.x;
+    const float2* tws = twiddle_table<TWL>(twl, twn, H, tid, kMrThreads);
     const int64_t img = blockIdx.x / nkb;
     const int ky0 = (int)(blockIdx.x % nkb) * kb;
     const int ncol = min(kb, my - ky0);
+    const float inv_ncol = 1.0f / (float)ncol;
     const float2* src = r + img * H * my;
     for (int e = tid; e < ncol * H; e += kMrThreads) {
-        const int h = e / ncol;
+        const int h = qdiv(e, inv_ncol);
         const int c = e - h * ncol;
         buf[0][c * H + h] = src[(int64_t)h * my + ky0 + c];
     }
     __syncthreads();
-    const float2* res = fft_rows_mr<-1>(buf[0], buf[1], ncol, p, twn, tid, kMrThreads);
-    float2* dst = xh + img * (2 * mx) * my;
+    const float2* res = fft_rows_mr<-1>(buf[0], buf[1], ncol, p, tws, tid, kMrThreads);
+    float2* dst = xh + img * img_ld;
     for (int e = tid; e < 2 * mx * ncol; e += kMrThreads) {
-        const int q = e / ncol;
+        const int q = qdiv(e, inv_ncol);
         const int c = e - q * ncol;
         const int kx = q < mx ? q : H - 2 * mx + q;
         dst[(int64_t)q * my + ky0 + c] = cscale(res[c * H + kx], scale);
     }
 }
 
-// yh[nimg][2 mx][my] -> zero-filled inverse along H -> R'[nimg][H][my]
+// yh (image img at img * img_ld, mode q my + ky) -> zero-filled inverse
+// along H -> R'[nimg][H][my]
+template <bool TWL>
 __global__ __launch_bounds__(kMrThreads) void k_cols_inv_mr(const float2* __restrict__ yh, float2* __restrict__ r,
-                                                            int mx, int my, int kb, int nkb, MRPlan p,
+                                                            int64_t img_ld, int mx, int my, int kb, int nkb, MRPlan p,
                                                             const float2* __restrict__ twn) {
     __shared__ float2 buf[2][kLdsElems];
+    __shared__ float2 twl[TWL ? kMrTwLds : 1];
     const int H = p.n;
     const int tid = threadIdx.x;
+    const float2* tws = twiddle_table<TWL>(twl, twn, H, tid, kMrThreads);
     const int64_t img = blockIdx.x / nkb;
     const int ky0 = (int)(blockIdx.x % nkb) * kb;
     const int ncol = min(kb, my - ky0);
-    const float2* src = yh + img * (2 * mx) * my;
+    const float inv_ncol = 1.0f / (float)ncol;
+    const float inv_h = 1.0f / (float)H;
+    const float2* src = yh + img * img_ld;
     for (int e = tid; e < ncol * H; e += kMrThreads) {
-        const int c = e / H;
+        const int c = qdiv(e, inv_h);
         const int kx = e - c * H;
         if (kx >= mx && kx < H - mx) buf[0][e] = make_float2(0.0f, 0.0f);
     }
     for (int e = tid; e < 2 * mx * ncol; e += kMrThreads) {
-        const int q = e / ncol;
+        const int q = qdiv(e, inv_ncol);
         const int c = e - q * ncol;
         const int kx = q < mx ? q : H - 2 * mx + q;
         buf[0][c * H + kx] = src[(int64_t)q * my + ky0 + c];
     }
     __syncthreads();
-    const float2* res = fft_rows_mr<1>(buf[0], buf[1], ncol, p, twn, tid, kMrThreads);
+    const float2* res = fft_rows_mr<1>(buf[0], buf[1], ncol, p, tws, tid, kMrThreads);
     float2* dst = r + img * H * my;
     for (int e = tid; e < ncol * H; e += kMrThreads) {
-        const int h = e / ncol;
+        const int h = qdiv(e, inv_ncol);
         const int c = e - h * ncol;
         dst[(int64_t)h * my + ky0 + c] = res[c * H + h];
     }
@@ -216,20 +256,24 @@ __global__ __launch_bounds__(kMrThreads) void k_cols_inv_mr(const float2* __rest
 // dropped); EPI: the fused output epilogue on every output.  win: only the
 // window of rows [h0, h0 + h) x columns [w0, w0 + w) of each image of
 // win.ph rows is written, packed (the crop of a linear convolution).
-template <bool EPI>
+template <bool EPI, bool TWL>
 __global__ __launch_bounds__(kMrThreads) void k_rows_inv_mr(const float2* __restrict__ y, float* __restrict__ out,
                                                             int64_t nrows, int my, int y_ld, float scale, MRPlan p,
                                                             const float2* __restrict__ twn, Epilogue epi,
                                                             RowWindow win) {
     __shared__ float2 buf[2][kLdsElems];
+    __shared__ float2 twl[TWL ? kMrTwLds : 1];
     const int W = p.n;
     const int P = kLdsElems / W;
     const int tid = threadIdx.x;
+    const float inv_w = 1.0f / (float)W;
+    const double inv_ph = 1.0 / (double)win.ph;
+    const float2* tws = twiddle_table<TWL>(twl, twn, W, tid, kMrThreads);
     const int64_t npairs = (nrows + 1) / 2;
     const int64_t pair0 = (int64_t)blockIdx.x * P;
     const int prows = (int)(npairs - pair0 < P ? npairs - pair0 : P);
     for (int e = tid; e < prows * W; e += kMrThreads) {
-        const int pr = e / W;
+        const int pr = qdiv(e, inv_w);
         const int k = e - pr * W;
         const int kk = (2 * k <= W) ? k : W - k;
         const int64_t ra = 2 * (pair0 + pr);
@@ -244,19 +288,20 @@ __global__ __launch_bounds__(kMrThreads) void k_rows_inv_mr(const float2* __rest
         buf[0][e] = z;
     }
     __syncthreads();
-    const float2* res = fft_rows_mr<1>(buf[0], buf[1], prows, p, twn, tid, kMrThreads);
+    const float2* res = fft_rows_mr<1>(buf[0], buf[1], prows, p, tws, tid, kMrThreads);
     for (int e = tid; e < prows * W; e += kMrThreads) {
-        const int pr = e / W;
+        const int pr = qdiv(e, inv_w);
         const int n = e - pr * W;
         const int64_t ra = 2 * (pair0 + pr);
         const float2 z = res[e];
         if (!(win.w == W && win.h == win.ph)) {
-            // crop: rows ra and ra + 1 may fall in different images
+            // crop: rows ra and ra + 1 may fall in different images (the
+            // image index is the quotient by win.ph, formed in double)
             if (n < win.w0 || n >= win.w0 + win.w) continue;
             for (int s2 = 0; s2 < 2; ++s2) {
                 const int64_t r = ra + s2;
                 if (r >= nrows) break;
-                const uint32_t img = (uint32_t)r / (uint32_t)win.ph;
+                const uint32_t img = (uint32_t)(((double)(uint32_t)r + 0.5) * inv_ph);
                 const int q = (int)((uint32_t)r - img * (uint32_t)win.ph) - win.h0;
                 if (q >= 0 && q < win.h)
                     nt_store(&out[((int64_t)img * win.h + q) * win.w + n - win.w0], (s2 ? z.y : z.x) * scale);
@@ -282,13 +327,21 @@ __global__ __launch_bounds__(kMrThreads) void k_rows_inv_mr(const float2* __rest
 // radix-4 passes first, then 2, 3, 5, 7
 bool make_plan(int n, MRPlan* p) {
     if (n < 2 || n > kLdsElems) return false;
+    *p = MRPlan{};
     p->n = n;
     p->npass = 0;
-    int m = n;
+    int m = n, ns = 1;
     for (int r : {4, 2, 3, 5, 7})
         while (m % r == 0) {
             if (p->npass == kMrMaxPasses) return false;
-            p->r[p->npass++] = r;
+            const int k = p->npass++;
+            p->r[k] = r;
+            p->j[k] = n / r;
+            p->ns[k] = ns;
+            p->step[k] = n / (ns * r);
+            p->inv_j[k] = (float)(1.0 / (double)(n / r));
+            p->inv_ns[k] = (float)(1.0 / (double)ns);
+            ns *= r;
             m /= r;
         }
     return m == 1;
@@ -352,12 +405,15 @@ hipError_t launch_rows_fwd_mr(const float* x, float2* y, int64_t nrows, int W, i
     if (win.ph < 1 || win.h < 1 || win.h > win.ph || win.w < 1 || win.w > W || nrows % win.ph ||
         (window && nrows >= INT32_MAX))
         return hipErrorInvalidValue;
-    return launch_kernel(k_rows_fwd_mr, dim3((unsigned)blocks_for(nb)), dim3(kMrThreads), 0, s, x, y, nrows, my, y_ld,
-                         scale, p, twn, win);
+    if (W <= kMrTwLds)
+        return launch_kernel(k_rows_fwd_mr<true>, dim3((unsigned)blocks_for(nb)), dim3(kMrThreads), 0, s, x, y, nrows,
+                             my, y_ld, scale, p, twn, win);
+    return launch_kernel(k_rows_fwd_mr<false>, dim3((unsigned)blocks_for(nb)), dim3(kMrThreads), 0, s, x, y, nrows, my,
+                         y_ld, scale, p, twn, win);
 }
 
 hipError_t launch_cols_fwd_mr(const float2* r, float2* xh, int64_t nimg, int H, int mx, int my, float scale,
-                              hipStream_t s) {
+                              hipStream_t s, int64_t img_ld) {
     MRPlan p;
     if (!make_plan(H, &p) || 2 * mx > H) return hipErrorInvalidValue;
     const float2* twn = nullptr;
@@ -368,11 +424,17 @@ hipError_t launch_cols_fwd_mr(const float2* r, float2* xh, int64_t nimg, int H, 
     const int nkb = (my + kb - 1) / kb;
     const int64_t nb = nimg * nkb;
     if (nb >= INT32_MAX) return hipErrorInvalidValue;
-    return launch_kernel(k_cols_fwd_mr, dim3((unsigned)nb), dim3(kMrThreads), 0, s, r, xh, mx, my, kb, nkb, scale, p,
-                         twn);
+    if (img_ld < 0) img_ld = (int64_t)2 * mx * my;
+    if (img_ld < (int64_t)2 * mx * my) return hipErrorInvalidValue;
+    if (H <= kMrTwLds)
+        return launch_kernel(k_cols_fwd_mr<true>, dim3((unsigned)nb), dim3(kMrThreads), 0, s, r, xh, img_ld, mx, my,
+                             kb, nkb, scale, p, twn);
+    return launch_kernel(k_cols_fwd_mr<false>, dim3((unsigned)nb), dim3(kMrThreads), 0, s, r, xh, img_ld, mx, my, kb,
+                         nkb, scale, p, twn);
 }
 
-hipError_t launch_cols_inv_mr(const float2* yh, float2* r, int64_t nimg, int H, int mx, int my, hipStream_t s) {
+hipError_t launch_cols_inv_mr(const float2* yh, float2* r, int64_t nimg, int H, int mx, int my, hipStream_t s,
+                              int64_t img_ld) {
     MRPlan p;
     if (!make_plan(H, &p) || 2 * mx > H) return hipErrorInvalidValue;
     const float2* twn = nullptr;
@@ -383,7 +445,13 @@ hipError_t launch_cols_inv_mr(const float2* yh, float2* r, int64_t nimg, int H, 
     const int nkb = (my + kb - 1) / kb;
     const int64_t nb = nimg * nkb;
     if (nb >= INT32_MAX) return hipErrorInvalidValue;
-    return launch_kernel(k_cols_inv_mr, dim3((unsigned)nb), dim3(kMrThreads), 0, s, yh, r, mx, my, kb, nkb, p, twn);
+    if (img_ld < 0) img_ld = (int64_t)2 * mx * my;
+    if (img_ld < (int64_t)2 * mx * my) return hipErrorInvalidValue;
+    if (H <= kMrTwLds)
+        return launch_kernel(k_cols_inv_mr<true>, dim3((unsigned)nb), dim3(kMrThreads), 0, s, yh, r, img_ld, mx, my,
+                             kb, nkb, p, twn);
+    return launch_kernel(k_cols_inv_mr<false>, dim3((unsigned)nb), dim3(kMrThreads), 0, s, yh, r, img_ld, mx, my, kb,
+                         nkb, p, twn);
 }
 
 hipError_t launch_rows_inv_mr(const float2* y, float* out, int64_t nrows, int W, int my, int y_ld, float scale,
@@ -400,11 +468,19 @@ hipError_t launch_rows_inv_mr(const float2* y, float* out, int64_t nrows, int W,
     if (win.ph < 1 || win.h < 1 || win.h0 < 0 || win.h0 + win.h > win.ph || win.w < 1 || win.w0 < 0 ||
         win.w0 + win.w > W || nrows % win.ph || (window && (epi.on || nrows >= INT32_MAX)))
         return hipErrorInvalidValue;
+    const dim3 grid((unsigned)blocks_for(nb)), block(kMrThreads);
+    if (W <= kMrTwLds) {
+        if (epi.on)
+            return launch_kernel(k_rows_inv_mr<true, true>, grid, block, 0, s, y, out, nrows, my, y_ld, scale, p, twn,
+                                 epi, win);
+        return launch_kernel(k_rows_inv_mr<false, true>, grid, block, 0, s, y, out, nrows, my, y_ld, scale, p, twn, epi,
+                             win);
+    }
     if (epi.on)
-        return launch_kernel(k_rows_inv_mr<true>, dim3((unsigned)blocks_for(nb)), dim3(kMrThreads), 0, s, y, out,
-                             nrows, my, y_ld, scale, p, twn, epi, win);
-    return launch_kernel(k_rows_inv_mr<false>, dim3((unsigned)blocks_for(nb)), dim3(kMrThreads), 0, s, y, out, nrows,
-                         my, y_ld, scale, p, twn, epi, win);
+        return launch_kernel(k_rows_inv_mr<true, false>, grid, block, 0, s, y, out, nrows, my, y_ld, scale, p, twn, epi,
+                             win);
+    return launch_kernel(k_rows_inv_mr<false, false>, grid, block, 0, s, y, out, nrows, my, y_ld, scale, p, twn, epi,
+                         win);
 }
 
 }  // namespace fno
