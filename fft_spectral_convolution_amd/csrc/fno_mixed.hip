@@ -37,21 +37,37 @@ struct MRPlan {
 // All the index arithmetic here is below 2^13.
 __device__ __forceinline__ int qdiv(int x, float inv) { return (int)(((float)x + 0.5f) * inv); }
 
-// Radix-R DFT by its definition (R = 3, 5, 7), compile-time twiddles:
-// v[k] <- sum_r v[r] exp(SIGN 2 pi i r k / R).
+// Radix-R DFT (R = 3, 5, 7), compile-time twiddles:
+// v[k] <- sum_r v[r] exp(SIGN 2 pi i r k / R).  The terms r and R - r are
+// taken together: with p_r = v[r] + v[R-r], m_r = v[r] - v[R-r] and
+// theta = 2 pi r k / R,
+//   X[k] = v[0] + sum_{r <= (R-1)/2} (p_r cos theta + i SIGN m_r sin theta),
+// and X[R - k] is the same with the sine terms negated: 4 ((R-1)/2)^2 fused
+// multiply-adds for the non-zero bins instead of 4 (R-1)^2.
 template <int R, int SIGN>
 __device__ __forceinline__ void dft_odd(float2 (&v)[R]) {
+    constexpr int NH = (R - 1) / 2;
+    float2 sp[NH], sm[NH];
+    static_for<0, NH>([&](auto t) {
+        sp[t] = cadd(v[t + 1], v[R - 1 - t]);
+        sm[t] = csub(v[t + 1], v[R - 1 - t]);
+    });
     float2 out[R];
-    static_for<0, R>([&](auto k) {
-        float2 acc = v[0];
-        static_for<1, R>([&](auto r) {
-            constexpr int e = (k * r) % R;
+    out[0] = v[0];
+    static_for<0, NH>([&](auto t) { out[0] = cadd(out[0], sp[t]); });
+    static_for<1, NH + 1>([&](auto k) {
+        float2 a = v[0], b = make_float2(0.0f, 0.0f);
+        static_for<0, NH>([&](auto t) {
+            constexpr int e = (k * (t + 1)) % R;
             constexpr float c = (float)exact_cos(8 * e, 8 * R);
             constexpr float s = (float)(SIGN * exact_sin(8 * e, 8 * R));
-            acc.x = fmaf(v[r].x, c, fmaf(-v[r].y, s, acc.x));
-            acc.y = fmaf(v[r].x, s, fmaf(v[r].y, c, acc.y));
+            a.x = fmaf(sp[t].x, c, a.x);
+            a.y = fmaf(sp[t].y, c, a.y);
+            b.x = fmaf(sm[t].x, s, b.x);
+            b.y = fmaf(sm[t].y, s, b.y);
         });
-        out[k] = acc;
+        out[k] = make_float2(a.x - b.y, a.y + b.x);          // a + i b
+        out[R - k] = make_float2(a.x + b.y, a.y - b.x);      // a - i b
     });
 #pragma unroll
     for (int k = 0; k < R; ++k) v[k] = out[k];
