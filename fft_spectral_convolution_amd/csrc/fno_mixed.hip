@@ -166,21 +166,34 @@ __global__ __launch_bounds__(kMrThreads) void k_rows_fwd_mr(const float* __restr
     const int64_t npairs = (nrows + 1) / 2;
     const int64_t pair0 = (int64_t)blockIdx.x * P;
     const int prows = (int)(npairs - pair0 < P ? npairs - pair0 : P);
-    // sample n of row r: x's element when inside the window, else zero
-    // (row indices fit 32 bits when a window is used: checked on the host;
-    // the image index is the quotient of r by win.ph, formed in double)
-    auto sample = [&](int64_t r, int n) -> float {
-        if (r >= nrows) return 0.0f;
-        if (win.w == W && win.h == win.ph) return x[r * W + n];
-        const uint32_t img = (uint32_t)(((double)(uint32_t)r + 0.5) * inv_ph);
-        const int q = (int)((uint32_t)r - img * (uint32_t)win.ph);
-        return (q < win.h && n < win.w) ? x[((int64_t)img * win.h + q) * win.w + n] : 0.0f;
-    };
+    // Offset in x of each of the block's 2 prows rows, or -1 for a row of
+    // zeros (padding rows, rows past the end), in the second buffer, which
+    // the passes overwrite only later.  Row r is row q = r mod win.ph of
+    // image r div win.ph (without a window, ph = h = 1: row r itself; row
+    // indices fit 32 bits when a window is used: checked on the host); the
+    // quotient is formed in double.
+    int64_t* const srow = reinterpret_cast<int64_t*>(buf[1]);
+    for (int t = tid; t < 2 * prows; t += kMrThreads) {
+        const int64_t r = 2 * pair0 + t;
+        int64_t off = -1;
+        if (r < nrows) {
+            if (win.ph == 1) {
+                off = r * win.w;
+            } else {
+                const uint32_t img = (uint32_t)(((double)(uint32_t)r + 0.5) * inv_ph);
+                const int q = (int)((uint32_t)r - img * (uint32_t)win.ph);
+                if (q < win.h) off = ((int64_t)img * win.h + q) * win.w;
+            }
+        }
+        srow[t] = off;
+    }
+    __syncthreads();
     for (int e = tid; e < prows * W; e += kMrThreads) {
         const int pr = qdiv(e, inv_w);
         const int n = e - pr * W;
-        const int64_t ra = 2 * (pair0 + pr);
-        buf[0][e] = make_float2(sample(ra, n), sample(ra + 1, n));
+        const int64_t oa = srow[2 * pr], ob = srow[2 * pr + 1];
+        const bool in = n < win.w;
+        buf[0][e] = make_float2(in && oa >= 0 ? x[oa + n] : 0.0f, in && ob >= 0 ? x[ob + n] : 0.0f);
     }
     __syncthreads();
     const float2* res = fft_rows_mr<-1>(buf[0], buf[1], prows, p, tws, tid, kMrThreads);
@@ -305,23 +318,35 @@ __global__ __launch_bounds__(kMrThreads) void k_rows_inv_mr(const float2* __rest
     }
     __syncthreads();
     const float2* res = fft_rows_mr<1>(buf[0], buf[1], prows, p, tws, tid, kMrThreads);
+    const bool crop = !(win.w == W && win.h == win.ph);
+    // crop: offset in out of each of the block's 2 prows rows, or -1 for a
+    // row outside the window; rows ra and ra + 1 may fall
+    // in different images (the image index is the quotient by win.ph,
+    // formed in double).  The table sits in the buffer the passes left free.
+    int64_t* const drow = reinterpret_cast<int64_t*>(res == buf[0] ? buf[1] : buf[0]);
+    if (crop) {
+        for (int t = tid; t < 2 * prows; t += kMrThreads) {
+            const int64_t r = 2 * pair0 + t;
+            int64_t off = -1;
+            if (r < nrows) {
+                const uint32_t img = (uint32_t)(((double)(uint32_t)r + 0.5) * inv_ph);
+                const int q = (int)((uint32_t)r - img * (uint32_t)win.ph) - win.h0;
+                if (q >= 0 && q < win.h) off = ((int64_t)img * win.h + q) * win.w;
+            }
+            drow[t] = off;
+        }
+        __syncthreads();
+    }
     for (int e = tid; e < prows * W; e += kMrThreads) {
         const int pr = qdiv(e, inv_w);
         const int n = e - pr * W;
         const int64_t ra = 2 * (pair0 + pr);
         const float2 z = res[e];
-        if (!(win.w == W && win.h == win.ph)) {
-            // crop: rows ra and ra + 1 may fall in different images (the
-            // image index is the quotient by win.ph, formed in double)
+        if (crop) {
             if (n < win.w0 || n >= win.w0 + win.w) continue;
-            for (int s2 = 0; s2 < 2; ++s2) {
-                const int64_t r = ra + s2;
-                if (r >= nrows) break;
-                const uint32_t img = (uint32_t)(((double)(uint32_t)r + 0.5) * inv_ph);
-                const int q = (int)((uint32_t)r - img * (uint32_t)win.ph) - win.h0;
-                if (q >= 0 && q < win.h)
-                    nt_store(&out[((int64_t)img * win.h + q) * win.w + n - win.w0], (s2 ? z.y : z.x) * scale);
-            }
+            const int64_t oa = drow[2 * pr], ob = drow[2 * pr + 1];
+            if (oa >= 0) nt_store(&out[oa + n - win.w0], z.x * scale);
+            if (ob >= 0) nt_store(&out[ob + n - win.w0], z.y * scale);
             continue;
         }
         if constexpr (EPI) {
