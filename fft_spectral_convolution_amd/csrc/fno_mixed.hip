@@ -99,29 +99,31 @@ __device__ __forceinline__ void mr_pass(const float2* src, float2* dst, int stri
     for (int r = 0; r < R; ++r) dst[base + r * ns] = v[r];
 }
 
-// Full transform of `nrows` rows of length p.n (row stride p.n) in LDS
+// Full transform of `nrows` rows of length p.n (row pitch ld >= p.n) in LDS
 // buffer a, ping-ponging through b; returns the buffer with the result.
 // tws: the twiddle table, in LDS or global memory.
 template <int SIGN>
-__device__ __forceinline__ float2* fft_rows_mr(float2* a, float2* b, int nrows, const MRPlan& p, const float2* tws,
-                                               int tid, int nthr) {
-    const int n = p.n;
+__device__ __forceinline__ float2* fft_rows_mr(float2* a, float2* b, int nrows, int ld, const MRPlan& p,
+                                               const float2* tws, int tid) {
     for (int pass = 0; pass < p.npass; ++pass) {
         const int R = p.r[pass], J = p.j[pass], ns = p.ns[pass], step = p.step[pass];
         const float inv_j = p.inv_j[pass], inv_ns = p.inv_ns[pass];
         const int total = nrows * J;
-        for (int idx = tid; idx < total; idx += nthr) {
-            const int row = qdiv(idx, inv_j);
-            const int j = idx - row * J;
-            float2* s = a + row * n;
-            float2* d = b + row * n;
-            switch (R) {
-                case 4: mr_pass<4, SIGN>(s, d, J, ns, inv_ns, step, j, tws); break;
-                case 2: mr_pass<2, SIGN>(s, d, J, ns, inv_ns, step, j, tws); break;
-                case 3: mr_pass<3, SIGN>(s, d, J, ns, inv_ns, step, j, tws); break;
-                case 5: mr_pass<5, SIGN>(s, d, J, ns, inv_ns, step, j, tws); break;
-                default: mr_pass<7, SIGN>(s, d, J, ns, inv_ns, step, j, tws); break;
+        // one loop per radix (the radix is uniform over the pass)
+        auto run = [&](auto rc) __attribute__((always_inline)) {
+            constexpr int RC = decltype(rc)::value;
+            for (int idx = tid; idx < total; idx += kMrThreads) {
+                const int row = qdiv(idx, inv_j);
+                const int j = idx - row * J;
+                mr_pass<RC, SIGN>(a + row * ld, b + row * ld, J, ns, inv_ns, step, j, tws);
             }
+        };
+        switch (R) {
+            case 4: run(std::integral_constant<int, 4>{}); break;
+            case 2: run(std::integral_constant<int, 2>{}); break;
+            case 3: run(std::integral_constant<int, 3>{}); break;
+            case 5: run(std::integral_constant<int, 5>{}); break;
+            default: run(std::integral_constant<int, 7>{}); break;
         }
         __syncthreads();
         float2* t = a;
@@ -143,6 +145,23 @@ __device__ __forceinline__ const float2* twiddle_table(float2* lds, const float2
         (void)lds;
         return twn;
     }
+}
+
+// Column block (image, block kb of nkb) of hardware block L: in every group
+// of 8 nkb consecutive blocks, the nkb column blocks of one image get
+// indices equal mod 8 (the same XCD under round-robin dispatch) and
+// consecutive dispatch slots, so that the XCD's L2 fetches the rows they
+// share once; a tail group keeps the plain order.
+__device__ __forceinline__ void col_block(int64_t L, int nkb, int64_t nblocks, int64_t* img, int* kb) {
+    const int64_t gsz = 8 * (int64_t)nkb;
+    const int64_t g0 = L - L % gsz;
+    int64_t logical = L;
+    if (g0 + gsz <= nblocks) {
+        const int u = (int)(L - g0);
+        logical = g0 + (int64_t)(u % 8) * nkb + u / 8;
+    }
+    *img = logical / nkb;
+    *kb = (int)(logical % nkb);
 }
 
 // rows of length W = p.n (real) -> bins ky < my, two rows per complex
@@ -196,7 +215,7 @@ __global__ __launch_bounds__(kMrThreads) void k_rows_fwd_mr(const float* __restr
         buf[0][e] = make_float2(in && oa >= 0 ? x[oa + n] : 0.0f, in && ob >= 0 ? x[ob + n] : 0.0f);
     }
     __syncthreads();
-    const float2* res = fft_rows_mr<-1>(buf[0], buf[1], prows, p, tws, tid, kMrThreads);
+    const float2* res = fft_rows_mr<-1>(buf[0], buf[1], prows, W, p, tws, tid);
     for (int e = tid; e < prows * my; e += kMrThreads) {
         const int pr = qdiv(e, inv_my);
         const int k = e - pr * my;
@@ -221,24 +240,27 @@ __global__ __launch_bounds__(kMrThreads) void k_cols_fwd_mr(const float2* __rest
     const int H = p.n;
     const int tid = threadIdx.x;
     const float2* tws = twiddle_table<TWL>(twl, twn, H, tid, kMrThreads);
-    const int64_t img = blockIdx.x / nkb;
-    const int ky0 = (int)(blockIdx.x % nkb) * kb;
+    int64_t img;
+    int kbi;
+    col_block(blockIdx.x, nkb, gridDim.x, &img, &kbi);
+    const int ky0 = kbi * kb;
     const int ncol = min(kb, my - ky0);
     const float inv_ncol = 1.0f / (float)ncol;
+    const int ld = H | 1;           // odd pitch: the column-wise accesses below hit distinct banks
     const float2* src = r + img * H * my;
     for (int e = tid; e < ncol * H; e += kMrThreads) {
         const int h = qdiv(e, inv_ncol);
         const int c = e - h * ncol;
-        buf[0][c * H + h] = src[(int64_t)h * my + ky0 + c];
+        buf[0][c * ld + h] = src[(int64_t)h * my + ky0 + c];
     }
     __syncthreads();
-    const float2* res = fft_rows_mr<-1>(buf[0], buf[1], ncol, p, tws, tid, kMrThreads);
+    const float2* res = fft_rows_mr<-1>(buf[0], buf[1], ncol, ld, p, tws, tid);
     float2* dst = xh + img * img_ld;
     for (int e = tid; e < 2 * mx * ncol; e += kMrThreads) {
         const int q = qdiv(e, inv_ncol);
         const int c = e - q * ncol;
         const int kx = q < mx ? q : H - 2 * mx + q;
-        dst[(int64_t)q * my + ky0 + c] = cscale(res[c * H + kx], scale);
+        dst[(int64_t)q * my + ky0 + c] = cscale(res[c * ld + kx], scale);
     }
 }
 
@@ -253,30 +275,33 @@ __global__ __launch_bounds__(kMrThreads) void k_cols_inv_mr(const float2* __rest
     const int H = p.n;
     const int tid = threadIdx.x;
     const float2* tws = twiddle_table<TWL>(twl, twn, H, tid, kMrThreads);
-    const int64_t img = blockIdx.x / nkb;
-    const int ky0 = (int)(blockIdx.x % nkb) * kb;
+    int64_t img;
+    int kbi;
+    col_block(blockIdx.x, nkb, gridDim.x, &img, &kbi);
+    const int ky0 = kbi * kb;
     const int ncol = min(kb, my - ky0);
     const float inv_ncol = 1.0f / (float)ncol;
     const float inv_h = 1.0f / (float)H;
+    const int ld = H | 1;           // odd pitch: the column-wise accesses below hit distinct banks
     const float2* src = yh + img * img_ld;
     for (int e = tid; e < ncol * H; e += kMrThreads) {
         const int c = qdiv(e, inv_h);
         const int kx = e - c * H;
-        if (kx >= mx && kx < H - mx) buf[0][e] = make_float2(0.0f, 0.0f);
+        if (kx >= mx && kx < H - mx) buf[0][c * ld + kx] = make_float2(0.0f, 0.0f);
     }
     for (int e = tid; e < 2 * mx * ncol; e += kMrThreads) {
         const int q = qdiv(e, inv_ncol);
         const int c = e - q * ncol;
         const int kx = q < mx ? q : H - 2 * mx + q;
-        buf[0][c * H + kx] = src[(int64_t)q * my + ky0 + c];
+        buf[0][c * ld + kx] = src[(int64_t)q * my + ky0 + c];
     }
     __syncthreads();
-    const float2* res = fft_rows_mr<1>(buf[0], buf[1], ncol, p, tws, tid, kMrThreads);
+    const float2* res = fft_rows_mr<1>(buf[0], buf[1], ncol, ld, p, tws, tid);
     float2* dst = r + img * H * my;
     for (int e = tid; e < ncol * H; e += kMrThreads) {
         const int h = qdiv(e, inv_ncol);
         const int c = e - h * ncol;
-        dst[(int64_t)h * my + ky0 + c] = res[c * H + h];
+        dst[(int64_t)h * my + ky0 + c] = res[c * ld + h];
     }
 }
 
@@ -317,7 +342,7 @@ __global__ __launch_bounds__(kMrThreads) void k_rows_inv_mr(const float2* __rest
         buf[0][e] = z;
     }
     __syncthreads();
-    const float2* res = fft_rows_mr<1>(buf[0], buf[1], prows, p, tws, tid, kMrThreads);
+    const float2* res = fft_rows_mr<1>(buf[0], buf[1], prows, W, p, tws, tid);
     const bool crop = !(win.w == W && win.h == win.ph);
     // crop: offset in out of each of the block's 2 prows rows, or -1 for a
     // row outside the window; rows ra and ra + 1 may fall
@@ -460,7 +485,8 @@ hipError_t launch_cols_fwd_mr(const float2* r, float2* xh, int64_t nimg, int H, 
     const float2* twn = nullptr;
     hipError_t e = twiddles(H, s, &twn);
     if (e != hipSuccess) return e;
-    const int cap = kLdsElems / H;
+    const int cap = kLdsElems / (H | 1);       // columns at the kernel's odd pitch
+    if (cap < 1) return hipErrorInvalidValue;
     const int kb = cap < my ? cap : my;
     const int nkb = (my + kb - 1) / kb;
     const int64_t nb = nimg * nkb;
@@ -481,7 +507,8 @@ hipError_t launch_cols_inv_mr(const float2* yh, float2* r, int64_t nimg, int H, 
     const float2* twn = nullptr;
     hipError_t e = twiddles(H, s, &twn);
     if (e != hipSuccess) return e;
-    const int cap = kLdsElems / H;
+    const int cap = kLdsElems / (H | 1);       // columns at the kernel's odd pitch
+    if (cap < 1) return hipErrorInvalidValue;
     const int kb = cap < my ? cap : my;
     const int nkb = (my + kb - 1) / kb;
     const int64_t nb = nimg * nkb;
