@@ -637,9 +637,10 @@ int linconv2d_run(const float* x, const void* wspec, float* out, int B, int Cin,
     if (ch < 0 || cw < 0 || Ho < 1 || Wo < 1 || ch + Ho > H + kh - 1 || cw + Wo > W + kw - 1) return FNO_ERR_SHAPE;
     const int mx = PH / 2, my = PW / 2 + 1;
     const int64_t m = (int64_t)PH * my;
-    // each channel's spectrum padded to whole 8-mode runs (mp modes), so
-    // that the matrix-core mix reads and writes them as aligned float4 runs
-    const int64_t mp = (m + 7) / 8 * 8;
+    // the spectra in the tiled layout (batch item, 8-mode tile, channel, 8
+    // modes): the matrix-core mix reads and writes whole aligned runs, each
+    // tile's runs of all channels contiguous
+    const SpecLayout lx = tiled_layout(Cin, m), ly = tiled_layout(Cout, m);
     const size_t xbytes = (size_t)B * Cin * H * W * sizeof(float);
     const size_t wbytes = (size_t)m * Cin * Cout * sizeof(float2);
     const size_t obytes = (size_t)B * Cout * Ho * Wo * sizeof(float);
@@ -647,8 +648,8 @@ int linconv2d_run(const float* x, const void* wspec, float* out, int B, int Cin,
     if (rc) return rc;
     const int64_t cmax = Cin > Cout ? Cin : Cout;
     const size_t r_b = align_up((size_t)B * cmax * PH * my * sizeof(float2));
-    const size_t x_b = align_up((size_t)B * Cin * mp * sizeof(float2));
-    const size_t y_b = align_up((size_t)B * Cout * mp * sizeof(float2));
+    const size_t x_b = align_up((size_t)layout_elems(lx, B) * sizeof(float2));
+    const size_t y_b = align_up((size_t)layout_elems(ly, B) * sizeof(float2));
     DeviceState* st = nullptr;
     WsLease lease;
     rc = device_state(&st, stream);
@@ -667,13 +668,12 @@ int linconv2d_run(const float* x, const void* wspec, float* out, int B, int Cin,
         hipError_t e = launch_rows_fwd_mr(x, r, (int64_t)B * Cin * PH, PW, my, my, 1.0f, hs, &in_win);
         if (e != hipSuccess) return hip_fail(e);
         rec_kernel("cols_fwd", hs);
-        e = launch_cols_fwd_mr(r, xh, (int64_t)B * Cin, PH, mx, my, scale, hs, mp);
+        e = launch_cols_fwd_mr(r, xh, (int64_t)B * Cin, PH, mx, my, scale, hs, &lx);
         if (e != hipSuccess) return hip_fail(e);
-        const int mrc = run_mix(xh, padded_layout(Cin, m), static_cast<const float2*>(wspec), yh,
-                                padded_layout(Cout, m), B, Cin, Cout, m, hs);
+        const int mrc = run_mix(xh, lx, static_cast<const float2*>(wspec), yh, ly, B, Cin, Cout, m, hs);
         if (mrc) return mrc;
         rec_kernel("cols_inv", hs);
-        e = launch_cols_inv_mr(yh, r, (int64_t)B * Cout, PH, mx, my, hs, mp);
+        e = launch_cols_inv_mr(yh, r, (int64_t)B * Cout, PH, mx, my, hs, &ly);
         if (e != hipSuccess) return hip_fail(e);
         const RowWindow out_win{PH, Ho, Wo, ch, cw};
         rec_kernel("rows_inv", hs);

@@ -236,11 +236,12 @@ struct RowWindow {
 bool mixed_supported(int n);
 hipError_t launch_rows_fwd_mr(const float* x, float2* y, int64_t nrows, int W, int my, int y_ld, float scale,
                               hipStream_t s, const RowWindow* window = nullptr);
-// img_ld: the spectrum's image stride in complex elements (default 2 mx my)
+// layout: where mode m = q my + ky of image img = b C + c sits in the
+// spectrum (default: image after image, 2 mx my modes each)
 hipError_t launch_cols_fwd_mr(const float2* r, float2* xh, int64_t nimg, int H, int mx, int my, float scale,
-                              hipStream_t s, int64_t img_ld = -1);
+                              hipStream_t s, const SpecLayout* layout = nullptr);
 hipError_t launch_cols_inv_mr(const float2* yh, float2* r, int64_t nimg, int H, int mx, int my, hipStream_t s,
-                              int64_t img_ld = -1);
+                              const SpecLayout* layout = nullptr);
 hipError_t launch_rows_inv_mr(const float2* y, float* out, int64_t nrows, int W, int my, int y_ld, float scale,
                               hipStream_t s, const Epilogue& epi = Epilogue{}, const RowWindow* window = nullptr);
 

@@ -390,18 +390,20 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 // Chunks of 8 input channels, rounded up to an even count.
 int64_t mix_chunks(int64_t Cin) { return ((Cin + kMixKC - 1) / kMixKC + 1) / 2 * 2; }
 
-// A canonical layout (8-mode runs contiguous) whose channels hold whole
-// runs past M: the last run's missing modes have slots of their own.  The
-// kernel reads those slots and writes their results back there (each mode
-// is a separate product, so nothing else depends on them).
+// A layout in which the last 8-mode run is whole even when M is not a
+// multiple of 8: the tiled one (its tiles always hold 8 modes per channel),
+// or a canonical one whose channels are padded to whole runs.  The missing
+// modes have slots of their own; the kernel reads those slots and writes
+// their results back there (each mode is a separate product, so nothing
+// else depends on them).
 bool padded_runs(const SpecLayout& l, int64_t M) {
-    const int64_t mp = (M + 7) / 8 * 8;
-    return l.st == 8 && l.sc % 8 == 0 && l.sc >= mp && l.sb >= (int64_t)l.C * l.sc;
+    const int64_t nt = (M + 7) / 8;
+    if (l.sc == 8) return l.st >= (int64_t)l.C * 8 && l.sb >= nt * l.st;                    // tiled
+    return l.st == 8 && l.sc % 8 == 0 && l.sc >= 8 * nt && l.sb >= (int64_t)l.C * l.sc;   // canonical, padded
 }
 
-// float4 access needs every 8-mode run whole and 16-byte aligned: the tiled
-// layout has it, the canonical one when M is a multiple of 8 or its channels
-// are padded to whole runs (all strides even, 16-byte aligned bases).
+// float4 access needs every 8-mode run whole and 16-byte aligned: M a
+// multiple of 8 or padded_runs (all strides even, 16-byte aligned bases).
 bool mix_vec(const float2* xh, const SpecLayout& lx, const float2* yh, const SpecLayout& ly, int64_t M) {
     const bool whole = M % 8 == 0 || (padded_runs(lx, M) && padded_runs(ly, M));
     return lx.sc % 2 == 0 && ly.sc % 2 == 0 && lx.st % 2 == 0 && ly.st % 2 == 0 && lx.sb % 2 == 0 &&

@@ -148,20 +148,24 @@ __device__ __forceinline__ const float2* twiddle_table(float2* lds, const float2
 }
 
 // Column block (image, block kb of nkb) of hardware block L: in every group
-// of 8 nkb consecutive blocks, the nkb column blocks of one image get
+// of 16 nkb consecutive blocks, the column blocks of two neighbouring images
+// (channels c and c + 1 of the tiled spectrum share its 128-byte lines; in
+// any layout they share the row spectrum's lines across column blocks) get
 // indices equal mod 8 (the same XCD under round-robin dispatch) and
-// consecutive dispatch slots, so that the XCD's L2 fetches the rows they
-// share once; a tail group keeps the plain order.
+// consecutive dispatch slots, interleaved, so that the XCD's L2 fetches
+// and writes back those lines once; a tail group keeps the plain order.
 __device__ __forceinline__ void col_block(int64_t L, int nkb, int64_t nblocks, int64_t* img, int* kb) {
-    const int64_t gsz = 8 * (int64_t)nkb;
+    const int64_t gsz = 16 * (int64_t)nkb;
     const int64_t g0 = L - L % gsz;
-    int64_t logical = L;
     if (g0 + gsz <= nblocks) {
         const int u = (int)(L - g0);
-        logical = g0 + (int64_t)(u % 8) * nkb + u / 8;
+        const int sl = u / 8;                           // slot on the XCD: 0 .. 2 nkb - 1
+        *img = g0 / nkb + 2 * (u % 8) + (sl & 1);
+        *kb = sl >> 1;
+        return;
     }
-    *img = logical / nkb;
-    *kb = (int)(logical % nkb);
+    *img = L / nkb;
+    *kb = (int)(L % nkb);
 }
 
 // rows of length W = p.n (real) -> bins ky < my, two rows per complex
@@ -229,11 +233,17 @@ __global__ __launch_bounds__(kMrThreads) void k_rows_fwd_mr(const float* __restr
     }
 }
 
-// R[nimg][H][my] -> xh (kept kx only, image img at img * img_ld, mode
-// q my + ky), H = p.n
+// Element (image img = b C + c, mode m) of a spectrum in layout `lay`.
+__device__ __forceinline__ int64_t spec_at(const SpecLayout& lay, int64_t img, int m) {
+    const int64_t b = img / lay.C;
+    return b * lay.sb + (img - b * lay.C) * lay.sc + (int64_t)(m >> 3) * lay.st + (m & 7);
+}
+
+// R[nimg][H][my] -> xh (kept kx only, mode q my + ky, in layout `lay`),
+// H = p.n
 template <bool TWL>
 __global__ __launch_bounds__(kMrThreads) void k_cols_fwd_mr(const float2* __restrict__ r, float2* __restrict__ xh,
-                                                            int64_t img_ld, int mx, int my, int kb, int nkb,
+                                                            SpecLayout lay, int mx, int my, int kb, int nkb,
                                                             float scale, MRPlan p, const float2* __restrict__ twn) {
     __shared__ float2 buf[2][kLdsElems];
     __shared__ float2 twl[TWL ? kMrTwLds : 1];
@@ -255,20 +265,21 @@ __global__ __launch_bounds__(kMrThreads) void k_cols_fwd_mr(const float2* __rest
     }
     __syncthreads();
     const float2* res = fft_rows_mr<-1>(buf[0], buf[1], ncol, ld, p, tws, tid);
-    float2* dst = xh + img * img_ld;
+    float2* dst = xh + spec_at(lay, img, 0);
     for (int e = tid; e < 2 * mx * ncol; e += kMrThreads) {
         const int q = qdiv(e, inv_ncol);
         const int c = e - q * ncol;
         const int kx = q < mx ? q : H - 2 * mx + q;
-        dst[(int64_t)q * my + ky0 + c] = cscale(res[c * ld + kx], scale);
+        const int m = q * my + ky0 + c;
+        dst[(int64_t)(m >> 3) * lay.st + (m & 7)] = cscale(res[c * ld + kx], scale);
     }
 }
 
-// yh (image img at img * img_ld, mode q my + ky) -> zero-filled inverse
-// along H -> R'[nimg][H][my]
+// yh (mode q my + ky, in layout `lay`) -> zero-filled inverse along H ->
+// R'[nimg][H][my]
 template <bool TWL>
 __global__ __launch_bounds__(kMrThreads) void k_cols_inv_mr(const float2* __restrict__ yh, float2* __restrict__ r,
-                                                            int64_t img_ld, int mx, int my, int kb, int nkb, MRPlan p,
+                                                            SpecLayout lay, int mx, int my, int kb, int nkb, MRPlan p,
                                                             const float2* __restrict__ twn) {
     __shared__ float2 buf[2][kLdsElems];
     __shared__ float2 twl[TWL ? kMrTwLds : 1];
@@ -283,7 +294,7 @@ __global__ __launch_bounds__(kMrThreads) void k_cols_inv_mr(const float2* __rest
     const float inv_ncol = 1.0f / (float)ncol;
     const float inv_h = 1.0f / (float)H;
     const int ld = H | 1;           // odd pitch: the column-wise accesses below hit distinct banks
-    const float2* src = yh + img * img_ld;
+    const float2* src = yh + spec_at(lay, img, 0);
     for (int e = tid; e < ncol * H; e += kMrThreads) {
         const int c = qdiv(e, inv_h);
         const int kx = e - c * H;
@@ -293,7 +304,8 @@ __global__ __launch_bounds__(kMrThreads) void k_cols_inv_mr(const float2* __rest
         const int q = qdiv(e, inv_ncol);
         const int c = e - q * ncol;
         const int kx = q < mx ? q : H - 2 * mx + q;
-        buf[0][c * ld + kx] = src[(int64_t)q * my + ky0 + c];
+        const int m = q * my + ky0 + c;
+        buf[0][c * ld + kx] = src[(int64_t)(m >> 3) * lay.st + (m & 7)];
     }
     __syncthreads();
     const float2* res = fft_rows_mr<1>(buf[0], buf[1], ncol, ld, p, tws, tid);
@@ -479,7 +491,7 @@ hipError_t launch_rows_fwd_mr(const float* x, float2* y, int64_t nrows, int W, i
 }
 
 hipError_t launch_cols_fwd_mr(const float2* r, float2* xh, int64_t nimg, int H, int mx, int my, float scale,
-                              hipStream_t s, int64_t img_ld) {
+                              hipStream_t s, const SpecLayout* layout) {
     MRPlan p;
     if (!make_plan(H, &p) || 2 * mx > H) return hipErrorInvalidValue;
     const float2* twn = nullptr;
@@ -491,17 +503,18 @@ hipError_t launch_cols_fwd_mr(const float2* r, float2* xh, int64_t nimg, int H, 
     const int nkb = (my + kb - 1) / kb;
     const int64_t nb = nimg * nkb;
     if (nb >= INT32_MAX) return hipErrorInvalidValue;
-    if (img_ld < 0) img_ld = (int64_t)2 * mx * my;
-    if (img_ld < (int64_t)2 * mx * my) return hipErrorInvalidValue;
+    // default: image after image, 2 mx my modes each
+    const SpecLayout lay = layout ? *layout : SpecLayout{(int64_t)2 * mx * my, 0, 8, 1};
+    if (lay.C < 1 || lay.st < 8) return hipErrorInvalidValue;
     if (H <= kMrTwLds)
-        return launch_kernel(k_cols_fwd_mr<true>, dim3((unsigned)nb), dim3(kMrThreads), 0, s, r, xh, img_ld, mx, my,
+        return launch_kernel(k_cols_fwd_mr<true>, dim3((unsigned)nb), dim3(kMrThreads), 0, s, r, xh, lay, mx, my,
                              kb, nkb, scale, p, twn);
-    return launch_kernel(k_cols_fwd_mr<false>, dim3((unsigned)nb), dim3(kMrThreads), 0, s, r, xh, img_ld, mx, my, kb,
+    return launch_kernel(k_cols_fwd_mr<false>, dim3((unsigned)nb), dim3(kMrThreads), 0, s, r, xh, lay, mx, my, kb,
                          nkb, scale, p, twn);
 }
 
 hipError_t launch_cols_inv_mr(const float2* yh, float2* r, int64_t nimg, int H, int mx, int my, hipStream_t s,
-                              int64_t img_ld) {
+                              const SpecLayout* layout) {
     MRPlan p;
     if (!make_plan(H, &p) || 2 * mx > H) return hipErrorInvalidValue;
     const float2* twn = nullptr;
@@ -513,12 +526,13 @@ hipError_t launch_cols_inv_mr(const float2* yh, float2* r, int64_t nimg, int H, 
     const int nkb = (my + kb - 1) / kb;
     const int64_t nb = nimg * nkb;
     if (nb >= INT32_MAX) return hipErrorInvalidValue;
-    if (img_ld < 0) img_ld = (int64_t)2 * mx * my;
-    if (img_ld < (int64_t)2 * mx * my) return hipErrorInvalidValue;
+    // default: image after image, 2 mx my modes each
+    const SpecLayout lay = layout ? *layout : SpecLayout{(int64_t)2 * mx * my, 0, 8, 1};
+    if (lay.C < 1 || lay.st < 8) return hipErrorInvalidValue;
     if (H <= kMrTwLds)
-        return launch_kernel(k_cols_inv_mr<true>, dim3((unsigned)nb), dim3(kMrThreads), 0, s, yh, r, img_ld, mx, my,
+        return launch_kernel(k_cols_inv_mr<true>, dim3((unsigned)nb), dim3(kMrThreads), 0, s, yh, r, lay, mx, my,
                              kb, nkb, p, twn);
-    return launch_kernel(k_cols_inv_mr<false>, dim3((unsigned)nb), dim3(kMrThreads), 0, s, yh, r, img_ld, mx, my, kb,
+    return launch_kernel(k_cols_inv_mr<false>, dim3((unsigned)nb), dim3(kMrThreads), 0, s, yh, r, lay, mx, my, kb,
                          nkb, p, twn);
 }
 
