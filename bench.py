@@ -329,7 +329,7 @@ def build_step(fno, torch, dev, cfg, which, variant, x_np, w_np, nsets):
         lens = ([fno.fno_linear_conv_length(cfg.W, 7)] if cfg.kind == "1d"
                 else [fno.fno_linear_conv_length(cfg.H, 5), fno.fno_linear_conv_length(cfg.W, 5)])
         if 0 in lens:
-            sys.exit(f"--pass linconv: the padded length of workload {cfg.name} exceeds the 4096-point transform")
+            sys.exit(f"--pass linconv: the padded lengths of workload {cfg.name} exceed the transforms' range")
         extras["lens"] = lens
         if cfg.kind == "1d":
             wspec = fno.fno_linear_conv1d_prepare(kd, cfg.W)

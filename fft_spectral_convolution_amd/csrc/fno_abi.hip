@@ -576,17 +576,23 @@ int filter1d_common(const float* x, const void* mask, float* out, int B, int C, 
 // (2^a 3^b 5^c 7^d, a >= 1) that holds the full linear convolution of n
 // samples with a k-tap kernel (even, so that full modes cover every kx);
 // 0 when the sizes are out of range.
+// Padded length of a linear convolution along a row (1D, or the W axis of
+// 2D): the smallest even length >= n + k - 1 that a transform takes (up to
+// 4096 any supported one, beyond that up to 8192 a 7-smooth one that is not
+// a power of two: the long mixed-radix rows).  The 2D column axis takes
+// only lengths up to 4096 (checked by the 2D calls).
 int linconv_len(int n, int k) {
     if (n < 1 || k < 1) return 0;
     const int64_t need = (int64_t)n + k - 1;
-    for (int64_t p = need < 2 ? 2 : need; p <= kNMax; ++p)
-        if (p % 2 == 0 && length_ok((int)p)) return (int)p;
+    for (int64_t p = need < 2 ? 2 : need; p <= 2 * kNMax; ++p)
+        if (p % 2 == 0 && (p <= kNMax ? length_ok((int)p) : (!is_pow2((int)p) && mixed_row_supported((int)p))))
+            return (int)p;
     return 0;
 }
 
 int linconv2d_prepare(const float* k, void* wspec, int Cin, int Cout, int H, int W, int kh, int kw, void* stream) {
     const int PH = linconv_len(H, kh), PW = linconv_len(W, kw);
-    if (!PH || !PW || Cin < 1 || Cout < 1 || (int64_t)Cin * Cout > INT32_MAX) return FNO_ERR_SHAPE;
+    if (!PH || !PW || PH > kNMax || Cin < 1 || Cout < 1 || (int64_t)Cin * Cout > INT32_MAX) return FNO_ERR_SHAPE;
     if (!k || !wspec) return FNO_ERR_NULL;
     if (misaligned(k) || misaligned(wspec)) return FNO_ERR_ALIGN;
     const int mx = PH / 2, my = PW / 2 + 1;
@@ -633,7 +639,7 @@ int linconv2d_prepare(const float* k, void* wspec, int Cin, int Cout, int H, int
 int linconv2d_run(const float* x, const void* wspec, float* out, int B, int Cin, int Cout, int H, int W, int kh,
                   int kw, int ch, int cw, int Ho, int Wo, void* stream) {
     const int PH = linconv_len(H, kh), PW = linconv_len(W, kw);
-    if (!PH || !PW || B < 1 || Cin < 1 || Cout < 1) return FNO_ERR_SHAPE;
+    if (!PH || !PW || PH > kNMax || B < 1 || Cin < 1 || Cout < 1) return FNO_ERR_SHAPE;
     if (ch < 0 || cw < 0 || Ho < 1 || Wo < 1 || ch + Ho > H + kh - 1 || cw + Wo > W + kw - 1) return FNO_ERR_SHAPE;
     const int mx = PH / 2, my = PW / 2 + 1;
     const int64_t m = (int64_t)PH * my;

@@ -234,6 +234,9 @@ struct RowWindow {
     int ph, h, w, h0, w0;
 };
 bool mixed_supported(int n);
+// 7-smooth lengths up to 8192 for the row kernels alone (no epilogue beyond
+// 4096 points): the rows of a zero-padded linear convolution.
+bool mixed_row_supported(int n);
 hipError_t launch_rows_fwd_mr(const float* x, float2* y, int64_t nrows, int W, int my, int y_ld, float scale,
                               hipStream_t s, const RowWindow* window = nullptr);
 // layout: where mode m = q my + ky of image img = b C + c sits in the

@@ -21,6 +21,10 @@ namespace {
 constexpr int kMrThreads = 1024;   // 16 waves; the 72 KiB of LDS allow two workgroups per CU
 constexpr int kMrMaxPasses = 12;
 constexpr int kMrTwLds = 1024;     // lengths up to this take their twiddle table from LDS
+// Rows longer than kLdsElems (up to kMrLongRow points: the padded rows of a
+// linear convolution) take workgroups with two 8192-point buffers (128 KiB
+// of LDS, one pair of rows per workgroup, one workgroup per CU).
+constexpr int kMrLongRow = 8192;
 
 // Passes of an n-point transform: radix r[p], J = n / r[p] butterflies per
 // row, ns[p] = product of the earlier radices, twiddle step n / (ns r); the
@@ -173,14 +177,14 @@ __device__ __forceinline__ void col_block(int64_t L, int nkb, int64_t nblocks, i
 // win: the rows are those of images of win.ph rows, and x holds only each
 // image's top-left win.h x win.w corner (the rest reads as zero: the
 // zero padding of a linear convolution).
-template <bool TWL>
+template <int NE, bool TWL>
 __global__ __launch_bounds__(kMrThreads) void k_rows_fwd_mr(const float* __restrict__ x, float2* __restrict__ y,
                                                             int64_t nrows, int my, int y_ld, float scale, MRPlan p,
                                                             const float2* __restrict__ twn, RowWindow win) {
-    __shared__ float2 buf[2][kLdsElems];
+    __shared__ float2 buf[2][NE];
     __shared__ float2 twl[TWL ? kMrTwLds : 1];
     const int W = p.n;
-    const int P = kLdsElems / W;
+    const int P = NE / W;
     const int tid = threadIdx.x;
     const float inv_w = 1.0f / (float)W;
     const float inv_my = 1.0f / (float)my;
@@ -322,15 +326,15 @@ __global__ __launch_bounds__(kMrThreads) void k_cols_inv_mr(const float2* __rest
 // dropped); EPI: the fused output epilogue on every output.  win: only the
 // window of rows [h0, h0 + h) x columns [w0, w0 + w) of each image of
 // win.ph rows is written, packed (the crop of a linear convolution).
-template <bool EPI, bool TWL>
+template <bool EPI, int NE, bool TWL>
 __global__ __launch_bounds__(kMrThreads) void k_rows_inv_mr(const float2* __restrict__ y, float* __restrict__ out,
                                                             int64_t nrows, int my, int y_ld, float scale, MRPlan p,
                                                             const float2* __restrict__ twn, Epilogue epi,
                                                             RowWindow win) {
-    __shared__ float2 buf[2][kLdsElems];
+    __shared__ float2 buf[2][NE];
     __shared__ float2 twl[TWL ? kMrTwLds : 1];
     const int W = p.n;
-    const int P = kLdsElems / W;
+    const int P = NE / W;
     const int tid = threadIdx.x;
     const float inv_w = 1.0f / (float)W;
     const double inv_ph = 1.0 / (double)win.ph;
@@ -403,8 +407,8 @@ __global__ __launch_bounds__(kMrThreads) void k_rows_inv_mr(const float2* __rest
 }
 
 // radix-4 passes first, then 2, 3, 5, 7
-bool make_plan(int n, MRPlan* p) {
-    if (n < 2 || n > kLdsElems) return false;
+bool make_plan(int n, MRPlan* p, int nmax = kLdsElems) {
+    if (n < 2 || n > nmax) return false;
     *p = MRPlan{};
     p->n = n;
     p->npass = 0;
@@ -469,25 +473,34 @@ bool mixed_supported(int n) {
     return make_plan(n, &p);
 }
 
+bool mixed_row_supported(int n) {
+    MRPlan p;
+    return make_plan(n, &p, kMrLongRow);
+}
+
 hipError_t launch_rows_fwd_mr(const float* x, float2* y, int64_t nrows, int W, int my, int y_ld, float scale,
                               hipStream_t s, const RowWindow* window) {
     MRPlan p;
-    if (!make_plan(W, &p) || my > W / 2 + 1) return hipErrorInvalidValue;
+    if (!make_plan(W, &p, kMrLongRow) || my > W / 2 + 1) return hipErrorInvalidValue;
     const float2* twn = nullptr;
     hipError_t e = twiddles(W, s, &twn);
     if (e != hipSuccess) return e;
-    const int P = kLdsElems / W;
+    const bool lng = W > kLdsElems;
+    const int P = (lng ? kMrLongRow : kLdsElems) / W;
     const int64_t nb = ((nrows + 1) / 2 + P - 1) / P;
     if (nb >= INT32_MAX) return hipErrorInvalidValue;
     const RowWindow win = window ? *window : RowWindow{1, 1, W, 0, 0};
     if (win.ph < 1 || win.h < 1 || win.h > win.ph || win.w < 1 || win.w > W || nrows % win.ph ||
         (window && nrows >= INT32_MAX))
         return hipErrorInvalidValue;
+    const dim3 grid((unsigned)blocks_for(nb)), block(kMrThreads);
+    if (lng)
+        return launch_kernel(k_rows_fwd_mr<kMrLongRow, false>, grid, block, 0, s, x, y, nrows, my, y_ld, scale, p, twn,
+                             win);
     if (W <= kMrTwLds)
-        return launch_kernel(k_rows_fwd_mr<true>, dim3((unsigned)blocks_for(nb)), dim3(kMrThreads), 0, s, x, y, nrows,
-                             my, y_ld, scale, p, twn, win);
-    return launch_kernel(k_rows_fwd_mr<false>, dim3((unsigned)blocks_for(nb)), dim3(kMrThreads), 0, s, x, y, nrows, my,
-                         y_ld, scale, p, twn, win);
+        return launch_kernel(k_rows_fwd_mr<kLdsElems, true>, grid, block, 0, s, x, y, nrows, my, y_ld, scale, p, twn,
+                             win);
+    return launch_kernel(k_rows_fwd_mr<kLdsElems, false>, grid, block, 0, s, x, y, nrows, my, y_ld, scale, p, twn, win);
 }
 
 hipError_t launch_cols_fwd_mr(const float2* r, float2* xh, int64_t nimg, int H, int mx, int my, float scale,
@@ -539,11 +552,13 @@ hipError_t launch_cols_inv_mr(const float2* yh, float2* r, int64_t nimg, int H, 
 hipError_t launch_rows_inv_mr(const float2* y, float* out, int64_t nrows, int W, int my, int y_ld, float scale,
                               hipStream_t s, const Epilogue& epi, const RowWindow* window) {
     MRPlan p;
-    if (!make_plan(W, &p) || my > W / 2 + 1) return hipErrorInvalidValue;
+    if (!make_plan(W, &p, kMrLongRow) || my > W / 2 + 1) return hipErrorInvalidValue;
+    const bool lng = W > kLdsElems;
+    if (lng && epi.on) return hipErrorInvalidValue;      // the long rows serve the linear convolution only
     const float2* twn = nullptr;
     hipError_t e = twiddles(W, s, &twn);
     if (e != hipSuccess) return e;
-    const int P = kLdsElems / W;
+    const int P = (lng ? kMrLongRow : kLdsElems) / W;
     const int64_t nb = ((nrows + 1) / 2 + P - 1) / P;
     if (nb >= INT32_MAX) return hipErrorInvalidValue;
     const RowWindow win = window ? *window : RowWindow{1, 1, W, 0, 0};
@@ -551,18 +566,21 @@ hipError_t launch_rows_inv_mr(const float2* y, float* out, int64_t nrows, int W,
         win.w0 + win.w > W || nrows % win.ph || (window && (epi.on || nrows >= INT32_MAX)))
         return hipErrorInvalidValue;
     const dim3 grid((unsigned)blocks_for(nb)), block(kMrThreads);
+    if (lng)
+        return launch_kernel(k_rows_inv_mr<false, kMrLongRow, false>, grid, block, 0, s, y, out, nrows, my, y_ld, scale,
+                             p, twn, epi, win);
     if (W <= kMrTwLds) {
         if (epi.on)
-            return launch_kernel(k_rows_inv_mr<true, true>, grid, block, 0, s, y, out, nrows, my, y_ld, scale, p, twn,
-                                 epi, win);
-        return launch_kernel(k_rows_inv_mr<false, true>, grid, block, 0, s, y, out, nrows, my, y_ld, scale, p, twn, epi,
-                             win);
+            return launch_kernel(k_rows_inv_mr<true, kLdsElems, true>, grid, block, 0, s, y, out, nrows, my, y_ld, scale,
+                                 p, twn, epi, win);
+        return launch_kernel(k_rows_inv_mr<false, kLdsElems, true>, grid, block, 0, s, y, out, nrows, my, y_ld, scale, p,
+                             twn, epi, win);
     }
     if (epi.on)
-        return launch_kernel(k_rows_inv_mr<true, false>, grid, block, 0, s, y, out, nrows, my, y_ld, scale, p, twn, epi,
-                             win);
-    return launch_kernel(k_rows_inv_mr<false, false>, grid, block, 0, s, y, out, nrows, my, y_ld, scale, p, twn, epi,
-                         win);
+        return launch_kernel(k_rows_inv_mr<true, kLdsElems, false>, grid, block, 0, s, y, out, nrows, my, y_ld, scale, p,
+                             twn, epi, win);
+    return launch_kernel(k_rows_inv_mr<false, kLdsElems, false>, grid, block, 0, s, y, out, nrows, my, y_ld, scale, p,
+                         twn, epi, win);
 }
 
 }  // namespace fno

@@ -290,8 +290,10 @@ int fno_spectral_filter1d(const float* x, const void* mask, float* out,
  * crop (kh-1)/2, (kw-1)/2 and Ho = H, Wo = W).  H, W may be any size.  Both
  * operands are zero-padded to PH x PW with PH = fno_linear_conv_length(H, kh),
  * PW = fno_linear_conv_length(W, kw) (the smallest even 7-smooth length
- * 2^a 3^b 5^c 7^d holding the full convolution, at most 4096; 0 when out of
- * range), where the circular convolution equals the linear one, and the
+ * 2^a 3^b 5^c 7^d holding the full convolution: at most 8192, and not a
+ * power of two above 4096; 0 when out of range; the 2D column length PH at
+ * most 4096, else FNO_ERR_SHAPE), where the circular convolution equals the
+ * linear one, and the
  * spectral convolution runs at full modes (mx = PH/2, my = PW/2+1) with the
  * weight spectrum
  *

@@ -201,11 +201,14 @@ def test_linear_conv_checks(lib):
     assert lib.fno_linear_conv_length(128, 5) == 140          # 2^2 5 7
     assert lib.fno_linear_conv_length(128, 1) == 128
     assert lib.fno_linear_conv_length(1, 1) == 2
-    assert lib.fno_linear_conv_length(4096, 2) == 0           # beyond 4096
+    assert lib.fno_linear_conv_length(4096, 2) == 4116        # 2^2 3 7^3: a long mixed-radix row
+    assert lib.fno_linear_conv_length(4090, 7) == 4096
+    assert lib.fno_linear_conv_length(8190, 1) == 0           # the next one, 8232, is beyond 8192
     assert lib.fno_linear_conv_length(0, 3) == 0
     p2 = lib.fno_linear_conv2d_prepare
     assert p2(None, B, 3, 4, 100, 100, 5, 5, None) == NULL
-    assert p2(A, B, 3, 4, 100, 4095, 5, 5, None) == SHAPE
+    assert p2(A, B, 3, 4, 4095, 100, 5, 5, None) == SHAPE    # columns: padded length 4116 > 4096
+    assert p2(A, B, 3, 4, 100, 8190, 5, 5, None) == SHAPE    # rows: no padded length up to 8192
     assert p2(A + 4, B, 3, 4, 100, 100, 5, 5, None) == ALIGN
     assert p2(A, A, 3, 4, 100, 100, 5, 5, None) == ALIAS
     f2 = lib.fno_linear_conv2d

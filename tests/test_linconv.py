@@ -52,6 +52,7 @@ CASES_2D = [
     (1, 2, 3, 50, 30, 7, 4, (4, 1), (40, 20)),        # an arbitrary crop window
     (1, 2, 2, 300, 200, 9, 9, None, None),            # staged transforms (512 x 256)
     (2, 1, 1, 1, 33, 1, 4, None, None),               # single-row images
+    (1, 2, 2, 6, 5000, 3, 3, None, None),             # rows padded beyond 4096 (5040 = 2^4 3^2 5 7)
 ]
 
 
@@ -91,6 +92,7 @@ CASES_1D = [
     (4, 8, 8, 1000, 7, None, None),                   # non-power-of-two length (padded to 1024)
     (2, 3, 5, 2000, 64, 0, 2063),                     # the full convolution (padded to 4096)
     (3, 2, 2, 37, 5, 3, 30),                          # a crop window
+    (2, 4, 4, 4096, 7, None, None),                   # the 4096-point sequences, 7 taps (padded to 4116)
 ]
 
 
