@@ -137,6 +137,71 @@ __device__ __forceinline__ float2* fft_rows_mr(float2* a, float2* b, int nrows, 
     return a;
 }
 
+// In-place form for rows longer than kLdsElems (one LDS buffer, so that two
+// workgroups fit a CU): in each pass every thread first loads the inputs of
+// all its butterflies (at most MB) into registers, the workgroup waits, and
+// then every thread writes its outputs (the Stockham output order).  The
+// rows hold at most NE elements (nrows * n <= NE), so a radix-R pass has at
+// most NE / R butterflies: MB = ceil(NE / (R kMrThreads)) per thread.
+template <int SIGN, int NE>
+__device__ __forceinline__ void fft_rows_mr_inplace(float2* a, int nrows, int ld, const MRPlan& p, const float2* tws,
+                                                    int tid) {
+    for (int pass = 0; pass < p.npass; ++pass) {
+        const int R = p.r[pass], J = p.j[pass], ns = p.ns[pass], step = p.step[pass];
+        const float inv_j = p.inv_j[pass], inv_ns = p.inv_ns[pass];
+        const int total = nrows * J;
+        auto run = [&](auto rc) __attribute__((always_inline)) {
+            constexpr int RC = decltype(rc)::value;
+            constexpr int MB = (NE + RC * kMrThreads - 1) / (RC * kMrThreads);
+            float2 v[MB][RC];
+            int jb[MB], rb[MB];
+#pragma unroll
+            for (int bi = 0; bi < MB; ++bi) {
+                const int idx = tid + bi * kMrThreads;
+                jb[bi] = -1;
+                rb[bi] = 0;
+                if (idx < total) {
+                    const int row = qdiv(idx, inv_j);
+                    const int j = idx - row * J;
+                    rb[bi] = row;
+                    jb[bi] = j;
+#pragma unroll
+                    for (int r = 0; r < RC; ++r) v[bi][r] = a[row * ld + j + r * J];
+                }
+            }
+            __syncthreads();
+#pragma unroll
+            for (int bi = 0; bi < MB; ++bi) {
+                const int j = jb[bi];
+                if (j >= 0) {
+                    const int k = j - qdiv(j, inv_ns) * ns;
+                    if (ns > 1) {
+#pragma unroll
+                        for (int r = 1; r < RC; ++r) {
+                            float2 t = tws[r * k * step];
+                            if (SIGN > 0) t.y = -t.y;
+                            v[bi][r] = cmul(v[bi][r], t);
+                        }
+                    }
+                    if constexpr (RC == 2 || RC == 4) dft<RC, SIGN>(v[bi]);
+                    else dft_odd<RC, SIGN>(v[bi]);
+                    const int base = (j - k) * RC + k;
+#pragma unroll
+                    for (int r = 0; r < RC; ++r) a[rb[bi] * ld + base + r * ns] = v[bi][r];
+                }
+            }
+        };
+        switch (R) {
+            case 4: run(std::integral_constant<int, 4>{}); break;
+            case 2: run(std::integral_constant<int, 2>{}); break;
+            case 3: run(std::integral_constant<int, 3>{}); break;
+            case 5: run(std::integral_constant<int, 5>{}); break;
+            default: run(std::integral_constant<int, 7>{}); break;
+        }
+        __syncthreads();
+    }
+}
+
 // The twiddle table, copied into LDS when TWL (every thread's copy is
 // ordered before the first pass by the barrier that follows the loads).
 template <bool TWL>
@@ -181,8 +246,12 @@ template <int NE, bool TWL>
 __global__ __launch_bounds__(kMrThreads) void k_rows_fwd_mr(const float* __restrict__ x, float2* __restrict__ y,
                                                             int64_t nrows, int my, int y_ld, float scale, MRPlan p,
                                                             const float2* __restrict__ twn, RowWindow win) {
-    __shared__ float2 buf[2][NE];
+    // rows longer than kLdsElems: one buffer (in-place passes) and the
+    // block's two row offsets in a table of their own
+    constexpr bool INP = NE > kLdsElems;
+    __shared__ float2 buf[INP ? 1 : 2][NE];
     __shared__ float2 twl[TWL ? kMrTwLds : 1];
+    __shared__ int64_t rtab[2];
     const int W = p.n;
     const int P = NE / W;
     const int tid = threadIdx.x;
@@ -199,7 +268,7 @@ __global__ __launch_bounds__(kMrThreads) void k_rows_fwd_mr(const float* __restr
     // image r div win.ph (without a window, ph = h = 1: row r itself; row
     // indices fit 32 bits when a window is used: checked on the host); the
     // quotient is formed in double.
-    int64_t* const srow = reinterpret_cast<int64_t*>(buf[1]);
+    int64_t* const srow = INP ? rtab : reinterpret_cast<int64_t*>(buf[INP ? 0 : 1]);
     for (int t = tid; t < 2 * prows; t += kMrThreads) {
         const int64_t r = 2 * pair0 + t;
         int64_t off = -1;
@@ -223,7 +292,9 @@ __global__ __launch_bounds__(kMrThreads) void k_rows_fwd_mr(const float* __restr
         buf[0][e] = make_float2(in && oa >= 0 ? x[oa + n] : 0.0f, in && ob >= 0 ? x[ob + n] : 0.0f);
     }
     __syncthreads();
-    const float2* res = fft_rows_mr<-1>(buf[0], buf[1], prows, W, p, tws, tid);
+    const float2* res = buf[0];
+    if constexpr (INP) fft_rows_mr_inplace<-1, NE>(buf[0], prows, W, p, tws, tid);
+    else res = fft_rows_mr<-1>(buf[0], buf[INP ? 0 : 1], prows, W, p, tws, tid);
     for (int e = tid; e < prows * my; e += kMrThreads) {
         const int pr = qdiv(e, inv_my);
         const int k = e - pr * my;
@@ -331,8 +402,10 @@ __global__ __launch_bounds__(kMrThreads) void k_rows_inv_mr(const float2* __rest
                                                             int64_t nrows, int my, int y_ld, float scale, MRPlan p,
                                                             const float2* __restrict__ twn, Epilogue epi,
                                                             RowWindow win) {
-    __shared__ float2 buf[2][NE];
+    constexpr bool INP = NE > kLdsElems;      // as in the forward: one buffer, in-place passes
+    __shared__ float2 buf[INP ? 1 : 2][NE];
     __shared__ float2 twl[TWL ? kMrTwLds : 1];
+    __shared__ int64_t rtab[2];
     const int W = p.n;
     const int P = NE / W;
     const int tid = threadIdx.x;
@@ -358,13 +431,15 @@ __global__ __launch_bounds__(kMrThreads) void k_rows_inv_mr(const float2* __rest
         buf[0][e] = z;
     }
     __syncthreads();
-    const float2* res = fft_rows_mr<1>(buf[0], buf[1], prows, W, p, tws, tid);
+    const float2* res = buf[0];
+    if constexpr (INP) fft_rows_mr_inplace<1, NE>(buf[0], prows, W, p, tws, tid);
+    else res = fft_rows_mr<1>(buf[0], buf[INP ? 0 : 1], prows, W, p, tws, tid);
     const bool crop = !(win.w == W && win.h == win.ph);
     // crop: offset in out of each of the block's 2 prows rows, or -1 for a
     // row outside the window; rows ra and ra + 1 may fall
     // in different images (the image index is the quotient by win.ph,
     // formed in double).  The table sits in the buffer the passes left free.
-    int64_t* const drow = reinterpret_cast<int64_t*>(res == buf[0] ? buf[1] : buf[0]);
+    int64_t* const drow = INP ? rtab : reinterpret_cast<int64_t*>(res == buf[0] ? buf[INP ? 0 : 1] : buf[0]);
     if (crop) {
         for (int t = tid; t < 2 * prows; t += kMrThreads) {
             const int64_t r = 2 * pair0 + t;
