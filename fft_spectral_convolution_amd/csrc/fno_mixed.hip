@@ -1,5 +1,6 @@
 // Stage kernels for transform lengths that are not powers of two: any
-// 7-smooth N (2^a 3^b 5^c 7^d) from 2 to 4096 (the FFT blog, section 6.2:
+// 7-smooth N (2^a 3^b 5^c 7^d) from 2 to 4096, and for the rows alone up to
+// 8192 (the padded rows of a linear convolution) (the FFT blog, section 6.2:
 // sizes such as 96 or 100 take mixed-radix paths; section 2.1: the padded
 // length of a linear convolution).  Same contracts as the generic
 // power-of-two stage kernels (fno_generic.hip), with the transform run as
@@ -22,8 +23,9 @@ constexpr int kMrThreads = 1024;   // 16 waves; the 72 KiB of LDS allow two work
 constexpr int kMrMaxPasses = 12;
 constexpr int kMrTwLds = 1024;     // lengths up to this take their twiddle table from LDS
 // Rows longer than kLdsElems (up to kMrLongRow points: the padded rows of a
-// linear convolution) take workgroups with two 8192-point buffers (128 KiB
-// of LDS, one pair of rows per workgroup, one workgroup per CU).
+// linear convolution) take workgroups with one 8192-point buffer and
+// in-place passes (64 KiB of LDS, one pair of rows per workgroup, two
+// workgroups per CU).
 constexpr int kMrLongRow = 8192;
 
 // Passes of an n-point transform: radix r[p], J = n / r[p] butterflies per
