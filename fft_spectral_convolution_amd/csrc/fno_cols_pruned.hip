@@ -1,4 +1,4 @@
-// Pruned column transforms for tall grids (H = 64 Q rows, Q in {8, 16, 32})
+// Pruned column transforms for tall grids (H = 64 Q rows, Q in {4, 8, 16, 32})
 // when at most 64 kx are kept on each side and my <= 64 columns exist:
 // the forward one computes only kx in [0,mx) u [H-mx,H), the inverse one
 // starts from those alone (TurboFNO blog, sections 2.1-2.2: the second 1D
@@ -32,13 +32,15 @@ constexpr int kColThreads = 512;
 constexpr int kColC = 8;                 // columns per workgroup
 constexpr int kMaxKept = 128;            // 2 mx
 
-// Twiddle table T[q][n1] = W^{n1 k_q} for the kept modes k_q (q < 2 mx).
-// Every thread issues all of its (at most 16) table reads before it writes
-// any entry, so the gathers overlap instead of queueing one by one.
+// Twiddle table T[q][n1] = W^{n1 k_q} for the kept modes k_q (q < 2 mx),
+// and up to the end of the last 8-mode chunk (the accumulation below runs
+// whole chunks; those entries meet zeroed modes).  Every thread issues all
+// of its (at most 16) table reads before it writes any entry, so the
+// gathers overlap instead of queueing one by one.
 template <int H>
 __device__ __forceinline__ void fill_twiddles(float2* T, int mx, const float2* __restrict__ tw, int sign) {
     constexpr int kPer = kMaxKept * 64 / kColThreads;
-    const int ne = 2 * mx * 64;
+    const int ne = (2 * mx + 7) / 8 * 8 * 64;
     float2 w[kPer];
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
@@ -163,9 +165,12 @@ __global__ __launch_bounds__(kColThreads) void k_cols_inv_pruned(const float2* _
 
     fill_twiddles<H>(T, mx, tw, 1);
     const float2* src = yh + img * (int64_t)nk * my;
-    for (int e = tid; e < nk * kColC; e += kColThreads) {
+    // the kept modes, zero up to the end of the last 8-mode chunk (2 mx is a
+    // multiple of Q, which is 4 at H = 256: not always of 8)
+    const int nk8 = (nk + 7) / 8 * 8;
+    for (int e = tid; e < nk8 * kColC; e += kColThreads) {
         const int q = e >> 3, cc = e & 7;
-        xs[e] = ky0 + cc < my ? src[(int64_t)q * my + ky0 + cc] : make_float2(0.0f, 0.0f);
+        xs[e] = q < nk && ky0 + cc < my ? src[(int64_t)q * my + ky0 + cc] : make_float2(0.0f, 0.0f);
     }
     __syncthreads();
     // V[r] = sum_{kept k = r mod Q} W^{-n1 k} X[k]; k_q mod Q = q mod Q
@@ -193,7 +198,7 @@ __global__ __launch_bounds__(kColThreads) void k_cols_inv_pruned(const float2* _
 }  // namespace
 
 bool cols_pruned_supported(int log2H, int mx, int my) {
-    if (log2H < 9 || log2H > 11) return false;
+    if (log2H < 8 || log2H > 11) return false;
     const int Q = 1 << (log2H - 6);
     return mx >= 1 && 2 * mx <= kMaxKept && (2 * mx) % Q == 0 && my >= 1 && my <= 64;
 }
@@ -206,6 +211,7 @@ hipError_t launch_cols_fwd_pruned(const float2* r, float2* xh, int64_t nimg, int
     if (nb >= INT32_MAX) return hipErrorInvalidValue;
     const dim3 grid((unsigned)nb), block(kColThreads);
     switch (log2H) {
+        case 8: return launch_kernel(k_cols_fwd_pruned<4>, grid, block, 0, s, r, xh, nkb, mx, my, scale, tw);
         case 9: return launch_kernel(k_cols_fwd_pruned<8>, grid, block, 0, s, r, xh, nkb, mx, my, scale, tw);
         case 10: return launch_kernel(k_cols_fwd_pruned<16>, grid, block, 0, s, r, xh, nkb, mx, my, scale, tw);
         default: return launch_kernel(k_cols_fwd_pruned<32>, grid, block, 0, s, r, xh, nkb, mx, my, scale, tw);
@@ -220,6 +226,7 @@ hipError_t launch_cols_inv_pruned(const float2* yh, float2* r, int64_t nimg, int
     if (nb >= INT32_MAX) return hipErrorInvalidValue;
     const dim3 grid((unsigned)nb), block(kColThreads);
     switch (log2H) {
+        case 8: return launch_kernel(k_cols_inv_pruned<4>, grid, block, 0, s, yh, r, nkb, mx, my, tw);
         case 9: return launch_kernel(k_cols_inv_pruned<8>, grid, block, 0, s, yh, r, nkb, mx, my, tw);
         case 10: return launch_kernel(k_cols_inv_pruned<16>, grid, block, 0, s, yh, r, nkb, mx, my, tw);
         default: return launch_kernel(k_cols_inv_pruned<32>, grid, block, 0, s, yh, r, nkb, mx, my, tw);

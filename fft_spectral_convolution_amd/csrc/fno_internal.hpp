@@ -176,7 +176,7 @@ hipError_t launch_mix_mfma(const float2* xh, const SpecLayout& lx, const float2*
                            bool adjoint = false);
 
 // ---- pruned long-row transforms (fno_rows_pruned.hip) ------------------------
-// Rows of W = 2^log2W real points, W in [512, 4096], bins ky < my <= 64:
+// Rows of W = 2^log2W real points, W in [256, 4096], bins ky < my <= 64:
 // same contract as launch_rows_fwd / launch_rows_inv below, which use them
 // whenever rows_pruned_supported holds.
 bool rows_pruned_supported(int log2W, int my);
@@ -186,7 +186,7 @@ hipError_t launch_rows_inv_pruned(const float2* y, float* out, int64_t nrows, in
                                   float scale, const float2* tw, hipStream_t s, const Epilogue& epi = Epilogue{});
 
 // ---- pruned column transforms (fno_cols_pruned.hip) --------------------------
-// H in [512, 2048], 2 mx <= 128 and a multiple of H / 64, my <= 64: same
+// H in [256, 2048], 2 mx <= 128 and a multiple of H / 64, my <= 64: same
 // contract as launch_cols_fwd / launch_cols_inv below, which use them
 // whenever cols_pruned_supported holds.
 bool cols_pruned_supported(int log2H, int mx, int my);

@@ -1,4 +1,4 @@
-// Pruned transforms of long real rows (N = 64 Q points, Q in {8, 16, 32, 64})
+// Pruned transforms of long real rows (N = 64 Q points, Q in {4, 8, 16, 32, 64})
 // when only the bins k < my <= 64 are kept: the forward R2C that computes
 // just those bins, and the C2R that rebuilds a row from them (FFT blog,
 // section 2.2: R2C / C2R on the N/2+1 half spectrum; TurboFNO blog, section
@@ -337,12 +337,13 @@ hipError_t launch_rows(K kernel, int64_t nrows, hipStream_t s, const TI* in, TO*
 
 }  // namespace
 
-bool rows_pruned_supported(int log2W, int my) { return log2W >= 9 && log2W <= 12 && my >= 1 && my <= 64; }
+bool rows_pruned_supported(int log2W, int my) { return log2W >= 8 && log2W <= 12 && my >= 1 && my <= 64; }
 
 hipError_t launch_rows_fwd_pruned(const float* x, float2* y, int64_t nrows, int log2W, int my, int y_ld, float scale,
                                   const float2* tw, hipStream_t s) {
     if (!rows_pruned_supported(log2W, my) || nrows <= 0) return hipErrorInvalidValue;
     switch (log2W) {
+        case 8: return launch_rows(k_rows_fwd_pruned<4>, nrows, s, x, y, my, y_ld, scale, tw);
         case 9: return launch_rows(k_rows_fwd_pruned<8>, nrows, s, x, y, my, y_ld, scale, tw);
         case 10: return launch_rows(k_rows_fwd_pruned<16>, nrows, s, x, y, my, y_ld, scale, tw);
         case 11: return launch_rows(k_rows_fwd_pruned<32>, nrows, s, x, y, my, y_ld, scale, tw);
@@ -355,6 +356,7 @@ hipError_t launch_rows_inv_pruned(const float2* y, float* out, int64_t nrows, in
     if (!rows_pruned_supported(log2W, my) || nrows <= 0) return hipErrorInvalidValue;
     if (epi.on) {
         switch (log2W) {
+            case 8: return launch_rows(k_rows_inv_pruned<4, true>, nrows, s, y, out, my, y_ld, scale, tw, epi);
             case 9: return launch_rows(k_rows_inv_pruned<8, true>, nrows, s, y, out, my, y_ld, scale, tw, epi);
             case 10: return launch_rows(k_rows_inv_pruned<16, true>, nrows, s, y, out, my, y_ld, scale, tw, epi);
             case 11: return launch_rows(k_rows_inv_pruned<32, true>, nrows, s, y, out, my, y_ld, scale, tw, epi);
@@ -362,6 +364,7 @@ hipError_t launch_rows_inv_pruned(const float2* y, float* out, int64_t nrows, in
         }
     }
     switch (log2W) {
+        case 8: return launch_rows(k_rows_inv_pruned<4, false>, nrows, s, y, out, my, y_ld, scale, tw, epi);
         case 9: return launch_rows(k_rows_inv_pruned<8, false>, nrows, s, y, out, my, y_ld, scale, tw, epi);
         case 10: return launch_rows(k_rows_inv_pruned<16, false>, nrows, s, y, out, my, y_ld, scale, tw, epi);
         case 11: return launch_rows(k_rows_inv_pruned<32, false>, nrows, s, y, out, my, y_ld, scale, tw, epi);

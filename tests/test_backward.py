@@ -74,7 +74,8 @@ BACKWARD_2D = [
     (3, 4, 6, 32, 16, 3, 9),        # small-grid kernels, Nyquist column kept
     (2, 8, 16, 64, 64, 16, 16),     # one-row-per-thread kernels, matrix-core mix both ways
     (17, 12, 18, 128, 128, 7, 13),  # ragged batch and channels
-    (1, 2, 3, 256, 256, 9, 11),     # staged generic transforms
+    (1, 2, 3, 256, 256, 9, 11),     # staged: 256-point pruned rows, generic columns (odd mx)
+    (1, 2, 3, 256, 256, 8, 16),     # staged: 256-point pruned rows and columns
     (1, 2, 3, 16, 1024, 5, 50),     # pruned long rows
     (1, 2, 2, 1024, 16, 8, 9),      # pruned columns
     (9, 16, 24, 64, 64, 8, 8),      # weight-gradient tiles of 16 x 32 channels; adjoint mix, ragged channel chunk

@@ -73,7 +73,8 @@ GELU_2D = [
     (3, 4, 6, 32, 16, 3, 9),          # small-grid kernel
     (2, 8, 16, 64, 64, 16, 16),       # one row per thread
     (2, 4, 6, 64, 128, 8, 20),        # one row per thread, 64 x 128
-    (1, 2, 3, 256, 256, 9, 11),       # staged: generic rows
+    (1, 2, 3, 256, 256, 9, 11),       # staged: 256-point pruned rows, generic columns (odd mx)
+    (1, 2, 3, 128, 256, 9, 100),      # staged: generic rows (more than 64 bins)
     (1, 2, 3, 16, 1024, 5, 50),       # staged: pruned long rows
     (1, 2, 2, 1024, 16, 8, 9),        # staged: pruned columns, generic rows
     (2, 3, 4, 45, 100, 10, 20),       # mixed-radix rows and columns
@@ -109,7 +110,7 @@ def test_gelu_optional_terms(use_bias, use_branch):
 @pytest.mark.parametrize("kind,shape", [
     ("2d", (1, 1, 2, 64, 64, 8, 8)),        # one row per thread
     ("2d", (1, 1, 2, 32, 32, 4, 4)),        # small-grid kernel
-    ("2d", (1, 1, 2, 256, 256, 4, 4)),      # staged, generic rows
+    ("2d", (1, 1, 2, 256, 256, 4, 4)),      # staged, 256-point pruned rows and columns
     ("1d", (1, 1, 2, 1, 2048, 1, 16)),      # pruned long rows
 ])
 def test_gelu_activation_accuracy(kind, shape):
