@@ -1,4 +1,4 @@
-// Pruned transforms of long real rows (N = 64 Q points, Q in {4, 8, 16, 32, 64})
+// Pruned transforms of real rows of 256 to 4096 points
 // when only the bins k < my <= 64 are kept: the forward R2C that computes
 // just those bins, and the C2R that rebuilds a row from them (FFT blog,
 // section 2.2: R2C / C2R on the N/2+1 half spectrum; TurboFNO blog, section
@@ -27,7 +27,9 @@
 // in registers for Q <= 32 and in a per-workgroup LDS table for Q = 64, so
 // the factor W^{-n1 r} is applied once per residue after the sum over j.
 // The waves of a workgroup share no data; the grid is persistent, each wave
-// walking rows.
+// walking rows.  Rows of 1024 to 4096 points (Q in {16, 32, 64}) take the
+// one-row-per-wave kernels; rows of 256 and 512 points take the short-row
+// kernels further down, several rows per wave.
 #include "fno_device.hpp"
 #include "fno_internal.hpp"
 
@@ -125,17 +127,17 @@ template <int Q>
 __global__ __launch_bounds__(kPrunedThreads) __attribute__((amdgpu_waves_per_eu(Q == 64 ? 2 : 4))) void k_rows_fwd_pruned(
     const float* __restrict__ x, float2* __restrict__ y, int64_t nrows, int my, int y_ld, float scale,
     const float2* __restrict__ tw) {
+    static_assert(Q == 16 || Q == 32 || Q == 64, "rows of 1024 to 4096 points");
     constexpr int N = 64 * Q;
     constexpr int NZ = Q / 2;
     // The kept bins k < 64 fall on Q residues k mod Q, NJ = 64 / Q bins each.
-    // A chunk stages RPC residues: stage row rr of chunk ch holds lane n1's
-    // Y[RPC ch + rr], untwiddled.  For Q >= 16 a chunk holds 16 residues and
-    // each reading lane forms all NJ bins of its residue from one read of its
-    // 16 staged values (BPL = NJ bins per lane); for Q = 8 the chunk holds
-    // two residues and the bins of a residue fall on NJ lane groups.
+    // A chunk stages RPC = 16 residues: stage row rr of chunk ch holds lane
+    // n1's Y[RPC ch + rr], untwiddled, and each reading lane forms all NJ
+    // bins of its residue from one read of its 16 staged values (BPL = NJ
+    // bins per lane).
     constexpr int NJ = 64 / Q;
-    constexpr int BPL = Q >= 16 ? NJ : 1;
-    constexpr int RPC = 16 * BPL / NJ;
+    constexpr int BPL = NJ;
+    constexpr int RPC = 16;
     constexpr int NCHK = Q / RPC;
     // The lane's residues above Q/2 are the conjugates of those below
     // (its samples are real): only rows r <= Q/2 are staged, once per row.
@@ -237,6 +239,7 @@ __global__ __launch_bounds__(kPrunedThreads) __attribute__((amdgpu_waves_per_eu(
                                                                     float* __restrict__ out, int64_t nrows, int my,
                                                                     int y_ld, float scale,
                                                                     const float2* __restrict__ tw, Epilogue epi) {
+    static_assert(Q == 16 || Q == 32 || Q == 64, "rows of 1024 to 4096 points");
     constexpr int N = 64 * Q;
     constexpr int NZ = Q / 2;
     __shared__ float2 xrow_all[kPrunedWaves][64];
@@ -320,6 +323,216 @@ __global__ __launch_bounds__(kPrunedThreads) __attribute__((amdgpu_waves_per_eu(
     }
 }
 
+// ---- short rows: N = 16 L points, L in {16, 32} ------------------------------
+// One row per wave would leave a lane of a 256-point row four samples, and
+// the 64-phase reduction above would cost several times the instructions
+// per byte of the long rows.  A row of 256 or 512 points takes L = N / 16
+// lanes instead: lane n1 < L holds the samples n1 + L n2 (n2 < 16) and runs
+// a 16-point real DFT, and a wave carries 64 / L rows at once.  With
+// W = exp(-2 pi i / N):
+//   X[k] = sum_{n1 < L} W^{n1 k} Y_n1[k mod 16],
+// formed by one reading lane per (row, bin, block of 16 phases) with the
+// binary tree of the long rows (factors W^k, W^2k, W^4k, W^8k), the L / 16
+// blocks added across neighbouring lanes.  The inverse mirrors the long-row
+// one with 16 residues, V[r] = conj(W^{n1 r}) sum_j X'[r + 16 j] conj(W_L^{n1 j}),
+// and carries the same fused epilogue.
+template <int L>
+__global__ __launch_bounds__(kPrunedThreads) __attribute__((amdgpu_waves_per_eu(4))) void k_rows_fwd_short(
+    const float* __restrict__ x, float2* __restrict__ y, int64_t nrows, int my, int y_ld, float scale,
+    const float2* __restrict__ tw) {
+    static_assert(L == 16 || L == 32, "short rows: 256 or 512 points");
+    constexpr int Q = 16, N = Q * L, NZ = Q / 2, SROWS = NZ + 1;
+    constexpr int RPW = 64 / L;              // rows per wave
+    constexpr int PB = L / 16;               // 16-phase blocks per row
+    constexpr int SS = L + PB;               // stage row stride (complex): a pad after every 16 phases
+    __shared__ float2 stage_all[kPrunedWaves][RPW * SROWS * SS];
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    float2* const stage = stage_all[wave];
+    const int rw = lane / L, n1 = lane % L;   // loading role: row rw of the wave's rows, phase n1
+    // Reading role: phase block pb and item group g; slot s (bins 16 s ..
+    // 16 s + 15 of every row) holds item s 64/PB + g = (row it mod RPW,
+    // bin it div RPW).  A bin whose residue r exceeds Q/2 reads the staged
+    // row Q - r (its conjugate) with conjugated factors and conjugates the sum.
+    const int pb = lane % PB;
+    const int g = lane / PB;
+    auto item = [&](int sl, int& rr, int& k) __attribute__((always_inline)) {
+        const int it = sl * (64 / PB) + g;
+        rr = it % RPW;
+        k = it / RPW;
+    };
+    float2 wk[4], vk[4];
+    const float half_scale = 0.5f * scale;
+#pragma unroll
+    for (int sl = 0; sl < 4; ++sl) {
+        int rr, k;
+        item(sl, rr, k);
+        const bool cj = k % Q > NZ;
+        const float2 w = tw[(k * (kNMax / N)) & (kNMax - 1)];
+        const float2 u = cscale(tw[(16 * pb * k * (kNMax / N)) & (kNMax - 1)], half_scale);
+        wk[sl] = cj ? conj2(w) : w;
+        vk[sl] = cj ? conj2(u) : u;
+    }
+    const int64_t nwaves = (int64_t)gridDim.x * kPrunedWaves;
+    for (int64_t row0 = ((int64_t)blockIdx.x * kPrunedWaves + wave) * RPW; row0 < nrows; row0 += nwaves * RPW) {
+#pragma unroll
+        for (int sl = 0; sl < 4; ++sl)
+            asm volatile("" : "+v"(wk[sl].x), "+v"(wk[sl].y), "+v"(vk[sl].x), "+v"(vk[sl].y));
+        // a row past the end repeats the last one (never stored)
+        const int64_t row = row0 + rw < nrows ? row0 + rw : nrows - 1;
+        const float* src = x + row * N + n1;
+        float2 z[NZ];
+#pragma unroll
+        for (int m = 0; m < NZ; ++m) z[m] = make_float2(src[L * (2 * m)], src[L * (2 * m + 1)]);
+        dft<NZ, -1>(z);
+        // 2 Y[r], r <= Q/2, staged at (row, r, phase n1 + its pad)
+        static_for<0, SROWS>([&](auto r) { stage[(rw * SROWS + r) * SS + n1 + n1 / 16] = real_bin2<Q, r>(z); });
+        wave_lds_sync();
+        static_for<0, 4>([&](auto sl) {
+            if (16 * sl < my) {                  // uniform: a slot with a kept bin
+                int rr, k;
+                item(sl, rr, k);
+                const int r = k % Q;
+                const bool cj = r > NZ;
+                const float2* const sp = stage + (rr * SROWS + (cj ? Q - r : r)) * SS + 17 * pb;
+                float2 v[16];
+#pragma unroll
+                for (int t = 0; t < 16; ++t) v[t] = sp[t];
+                float2 u[8];
+#pragma unroll
+                for (int t = 0; t < 8; ++t) u[t] = cfma(v[2 * t], wk[sl], v[2 * t + 1]);
+                const float2 w2 = cmul(wk[sl], wk[sl]);
+                const float2 w4 = cmul(w2, w2);
+                const float2 w8 = cmul(w4, w4);
+#pragma unroll
+                for (int t = 0; t < 4; ++t) u[t] = cfma(u[2 * t], w2, u[2 * t + 1]);
+#pragma unroll
+                for (int t = 0; t < 2; ++t) u[t] = cfma(u[2 * t], w4, u[2 * t + 1]);
+                float2 acc = cmul(vk[sl], cfma(u[0], w8, u[1]));
+                if constexpr (PB == 2) {
+                    acc.x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(acc.x), 0xB1, 0xF, 0xF, false));
+                    acc.y += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(acc.y), 0xB1, 0xF, 0xF, false));
+                }
+                if (pb == 0 && k < my && row0 + rr < nrows) y[(row0 + rr) * (int64_t)y_ld + k] = cj ? conj2(acc) : acc;
+            }
+        });
+        wave_lds_sync();                        // the stage is read before the next rows overwrite it
+    }
+}
+
+template <int L, bool EPI>
+__global__ __launch_bounds__(kPrunedThreads) __attribute__((amdgpu_waves_per_eu(4))) void k_rows_inv_short(
+    const float2* __restrict__ y, float* __restrict__ out, int64_t nrows, int my, int y_ld, float scale,
+    const float2* __restrict__ tw, Epilogue epi) {
+    static_assert(L == 16 || L == 32, "short rows: 256 or 512 points");
+    constexpr int Q = 16, N = Q * L, NZ = Q / 2;
+    constexpr int RPW = 64 / L;
+    __shared__ float2 xrow_all[kPrunedWaves][RPW * 64];
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    float2* const xrow = xrow_all[wave];
+    const int rw = lane / L, n1 = lane % L;
+    // residue factors W^{n1 r} (r <= Q/2) times scale (X[0] is halved on load,
+    // so every bin counts twice and 2 (scale / 2) = scale), and W^{16 n1 j} =
+    // W_L^{n1 j}; W^{n1 r} for r > Q/2 is W_L^{n1} conj(W^{n1 (Q - r)})
+    float2 tr[NZ + 1], pj[4];
+#pragma unroll
+    for (int r = 0; r <= NZ; ++r) tr[r] = cscale(tw[(n1 * r * (kNMax / N)) & (kNMax - 1)], scale);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) pj[j] = tw[(16 * n1 * j * (kNMax / N)) & (kNMax - 1)];
+    auto res = [&](auto r) __attribute__((always_inline)) {
+        if constexpr (r <= NZ) return tr[r];
+        else return cmul(pj[1], conj2(tr[r <= NZ ? 0 : Q - r]));
+    };
+    const int64_t nwaves = (int64_t)gridDim.x * kPrunedWaves;
+    // the kept bins of the wave's rows starting at r0, zero past my and past
+    // the last row (in-range loads only: row and bin clamped, the zeros
+    // selected), DC imaginary part dropped and the DC bin halved
+    auto load_bins = [&](int64_t r0, float2 (&v)[RPW]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int rr = 0; rr < RPW; ++rr) {
+            const bool keep = lane < my && r0 + rr < nrows;
+            v[rr] = y[(r0 + rr < nrows ? r0 + rr : nrows - 1) * (int64_t)y_ld + (lane < my ? lane : my - 1)];
+            if (!keep) v[rr] = make_float2(0.0f, 0.0f);
+        }
+    };
+    const int64_t first = ((int64_t)blockIdx.x * kPrunedWaves + wave) * RPW;
+    float2 vn[RPW];
+    load_bins(first < nrows ? first : 0, vn);
+    for (int64_t row0 = first; row0 < nrows; row0 += nwaves * RPW) {
+#pragma unroll
+        for (int r = 0; r <= NZ; ++r) asm volatile("" : "+v"(tr[r].x), "+v"(tr[r].y));
+#pragma unroll
+        for (int j = 0; j < 4; ++j) asm volatile("" : "+v"(pj[j].x), "+v"(pj[j].y));
+        // this group's bins to LDS; the next group's loaded meanwhile
+#pragma unroll
+        for (int rr = 0; rr < RPW; ++rr)
+            xrow[rr * 64 + lane] = lane == 0 ? make_float2(0.5f * vn[rr].x, 0.0f) : vn[rr];
+        load_bins(row0 + nwaves * RPW < nrows ? row0 + nwaves * RPW : row0, vn);
+        wave_lds_sync();
+        const float2* const xr = xrow + rw * 64;
+        // V[r] = conj(W^{n1 r}) sum_j X'[r + Q j] conj(W_L^{n1 j}) for every
+        // residue, one at a time with the next residue's four bins read
+        // ahead: left alone the compiler issues all 64 reads at once and
+        // holds them in registers
+        float2 V[Q], cur[4], nxt[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) cur[j] = xr[Q * j];
+        static_for<0, Q>([&](auto r) {
+            if constexpr (r + 1 < Q) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) nxt[j] = xr[r + 1 + Q * j];
+            }
+            float2 acc = cur[0];
+            static_for<1, 4>([&](auto j) { acc = cfma(acc, cur[j], conj2(pj[j])); });
+            V[r] = cmul(acc, conj2(res(r)));
+            asm volatile("" : "+v"(V[r].x), "+v"(V[r].y) : : "memory");
+#pragma unroll
+            for (int j = 0; j < 4; ++j) cur[j] = nxt[j];
+        });
+        // the Hermitian part H[r] = V[r] + conj V[-r]
+        float2 H[NZ + 1];
+#pragma unroll
+        for (int r = 0; r <= NZ; ++r) {
+            const float2 a = V[r], b = V[(Q - r) % Q];
+            H[r] = make_float2(a.x + b.x, a.y - b.y);
+        }
+        wave_lds_sync();                        // the bins are read before the next rows overwrite them
+        float2 z[NZ];
+        static_for<0, NZ>([&](auto k) { z[k] = packed_bin<Q, k>(H); });
+        dft<NZ, 1>(z);
+        float* const dst = out + (row0 + rw) * N + n1;
+        if constexpr (EPI) {
+            // the wave's rows of the branch through one buffer resource whose
+            // range ends at the last row (an empty range for a null branch:
+            // its loads read zero); the row group's first row is uniform
+            // across the wave, so the resource stays scalar
+            const uint32_t urow0 = __builtin_amdgcn_readfirstlane((uint32_t)row0);
+            const int64_t left = nrows - row0;
+            const uint32_t bytes = (uint32_t)((left < RPW ? left : RPW) * N * 4);
+            const __amdgpu_buffer_rsrc_t rb = make_rsrc(epi.branch ? epi.branch + (int64_t)urow0 * N : out,
+                                                        epi.branch ? bytes : 0u);
+            const float bias = epi_bias(epi, urow0 + rw);
+            float br[2 * NZ];
+#pragma unroll
+            for (int k = 0; k < 2 * NZ; ++k) br[k] = buffer_load_f1(rb, (uint32_t)(rw * N + n1 + L * k) * 4u, 0);
+            if (row0 + rw < nrows) {
+#pragma unroll
+                for (int m = 0; m < NZ; ++m) {
+                    nt_store(&dst[L * (2 * m)], epi_apply(epi, z[m].x, bias, br[2 * m]));
+                    nt_store(&dst[L * (2 * m + 1)], epi_apply(epi, z[m].y, bias, br[2 * m + 1]));
+                }
+            }
+        } else if (row0 + rw < nrows) {
+#pragma unroll
+            for (int m = 0; m < NZ; ++m) {
+                nt_store(&dst[L * (2 * m)], z[m].x);
+                nt_store(&dst[L * (2 * m + 1)], z[m].y);
+            }
+        }
+    }
+}
+
 template <typename K, typename TI, typename TO, typename... Extra>
 hipError_t launch_rows(K kernel, int64_t nrows, hipStream_t s, const TI* in, TO* out, int my, int y_ld, float scale,
                        const float2* tw, Extra... extra) {
@@ -343,8 +556,8 @@ hipError_t launch_rows_fwd_pruned(const float* x, float2* y, int64_t nrows, int 
                                   const float2* tw, hipStream_t s) {
     if (!rows_pruned_supported(log2W, my) || nrows <= 0) return hipErrorInvalidValue;
     switch (log2W) {
-        case 8: return launch_rows(k_rows_fwd_pruned<4>, nrows, s, x, y, my, y_ld, scale, tw);
-        case 9: return launch_rows(k_rows_fwd_pruned<8>, nrows, s, x, y, my, y_ld, scale, tw);
+        case 8: return launch_rows(k_rows_fwd_short<16>, nrows, s, x, y, my, y_ld, scale, tw);
+        case 9: return launch_rows(k_rows_fwd_short<32>, nrows, s, x, y, my, y_ld, scale, tw);
         case 10: return launch_rows(k_rows_fwd_pruned<16>, nrows, s, x, y, my, y_ld, scale, tw);
         case 11: return launch_rows(k_rows_fwd_pruned<32>, nrows, s, x, y, my, y_ld, scale, tw);
         default: return launch_rows(k_rows_fwd_pruned<64>, nrows, s, x, y, my, y_ld, scale, tw);
@@ -356,16 +569,16 @@ hipError_t launch_rows_inv_pruned(const float2* y, float* out, int64_t nrows, in
     if (!rows_pruned_supported(log2W, my) || nrows <= 0) return hipErrorInvalidValue;
     if (epi.on) {
         switch (log2W) {
-            case 8: return launch_rows(k_rows_inv_pruned<4, true>, nrows, s, y, out, my, y_ld, scale, tw, epi);
-            case 9: return launch_rows(k_rows_inv_pruned<8, true>, nrows, s, y, out, my, y_ld, scale, tw, epi);
+            case 8: return launch_rows(k_rows_inv_short<16, true>, nrows, s, y, out, my, y_ld, scale, tw, epi);
+            case 9: return launch_rows(k_rows_inv_short<32, true>, nrows, s, y, out, my, y_ld, scale, tw, epi);
             case 10: return launch_rows(k_rows_inv_pruned<16, true>, nrows, s, y, out, my, y_ld, scale, tw, epi);
             case 11: return launch_rows(k_rows_inv_pruned<32, true>, nrows, s, y, out, my, y_ld, scale, tw, epi);
             default: return launch_rows(k_rows_inv_pruned<64, true>, nrows, s, y, out, my, y_ld, scale, tw, epi);
         }
     }
     switch (log2W) {
-        case 8: return launch_rows(k_rows_inv_pruned<4, false>, nrows, s, y, out, my, y_ld, scale, tw, epi);
-        case 9: return launch_rows(k_rows_inv_pruned<8, false>, nrows, s, y, out, my, y_ld, scale, tw, epi);
+        case 8: return launch_rows(k_rows_inv_short<16, false>, nrows, s, y, out, my, y_ld, scale, tw, epi);
+        case 9: return launch_rows(k_rows_inv_short<32, false>, nrows, s, y, out, my, y_ld, scale, tw, epi);
         case 10: return launch_rows(k_rows_inv_pruned<16, false>, nrows, s, y, out, my, y_ld, scale, tw, epi);
         case 11: return launch_rows(k_rows_inv_pruned<32, false>, nrows, s, y, out, my, y_ld, scale, tw, epi);
         default: return launch_rows(k_rows_inv_pruned<64, false>, nrows, s, y, out, my, y_ld, scale, tw, epi);
