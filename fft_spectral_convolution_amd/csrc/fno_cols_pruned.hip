@@ -1,4 +1,6 @@
-// Pruned column transforms for tall grids (H = 64 Q rows, Q in {4, 8, 16, 32})
+// Pruned column transforms for tall grids (H = 64 Q rows, Q in {4, 8, 16, 32};
+// 256 and 512 rows with 2 mx a multiple of 16 take the short-column kernels
+// further down)
 // when at most 64 kx are kept on each side and my <= 64 columns exist:
 // the forward one computes only kx in [0,mx) u [H-mx,H), the inverse one
 // starts from those alone (TurboFNO blog, sections 2.1-2.2: the second 1D
@@ -195,6 +197,171 @@ __global__ __launch_bounds__(kColThreads) void k_cols_inv_pruned(const float2* _
     }
 }
 
+// ---- short columns: H = 16 L rows, L in {16, 32} ---------------------------
+// At 256 and 512 rows the kernels above hold four or eight samples per
+// thread and gather their twiddles per workgroup for 16 KiB of data.  Here
+// thread (n1, c) of 16 L holds column c's samples n1 + L n2 (n2 < 16) of a
+// block of 16 columns (each load and store instruction covers whole
+// 128-byte runs of the row spectrum) and runs a 16-point DFT; the grid is
+// persistent, so the twiddles are formed once per thread (forward) or per
+// workgroup (inverse) for all the column blocks it walks.  2 mx must be a
+// multiple of 16: kept mode q then has the residue q mod 16.
+// Forward: every Y_n1[r] is staged in LDS; reading lane (residue r, column,
+// block of 16 phases) forms every kept mode q = r + 16 i of its residue as
+// W^{16 pb k} sum_t (W^k)^t Y_{16 pb + t}[r] by the binary tree above, the
+// L / 16 blocks added across neighbouring lanes.
+// Inverse: thread (n1, c) accumulates V_n1[r] = sum_{q = r mod 16}
+// W^{-n1 k_q} X[k_q] from a per-workgroup LDS table of the kept modes'
+// twiddles and the block's kept modes, then runs its 16-point inverse DFT.
+constexpr int kShortC = 16;              // columns per work item
+constexpr int kShortKS = kMaxKept + 2;   // LDS row stride of the inverse tables (complex, 16-byte multiple): rows on distinct banks
+
+template <int L>
+__global__ __launch_bounds__(16 * L) __attribute__((amdgpu_waves_per_eu(4))) void k_cols_fwd_short(const float2* __restrict__ r, float2* __restrict__ xh,
+                                                          int64_t nitems, int nkb, int mx, int my, float scale,
+                                                          const float2* __restrict__ tw) {
+    static_assert(L == 16 || L == 32, "short columns: 256 or 512 rows");
+    constexpr int H = 16 * L, C = kShortC, PB = L / 16, SS = L + PB;
+    constexpr int MPR = kMaxKept / 16;               // kept modes per residue, at most
+    __shared__ float2 stage[16 * C * SS];            // row (residue, column): the L phases, a pad after every 16
+    const int tid = threadIdx.x;
+    const int c = tid % C, n1 = tid / C;             // loading role
+    const int pb = tid % PB, cr = (tid / PB) % C, rr = tid / (PB * C);   // reading role
+    const int nk = 2 * mx;
+    const int nm = nk / 16;                          // kept modes per residue
+    // W^k and W^{16 pb k} (times the output scale) of the lane's modes
+    float2 wk[MPR], vk[MPR];
+#pragma unroll
+    for (int i = 0; i < MPR; ++i) {
+        const int q = rr + 16 * i;
+        const int k = q < nk ? (q < mx ? q : H - nk + q) : 0;
+        wk[i] = tw[((int64_t)k * (kNMax / H)) & (kNMax - 1)];
+        vk[i] = cscale(tw[((int64_t)16 * pb * k * (kNMax / H)) & (kNMax - 1)], scale);
+    }
+    for (int64_t item = blockIdx.x; item < nitems; item += gridDim.x) {
+#pragma unroll
+        for (int i = 0; i < MPR; ++i) asm volatile("" : "+v"(wk[i].x), "+v"(wk[i].y), "+v"(vk[i].x), "+v"(vk[i].y));
+        const int64_t img = item / nkb;
+        const int ky0 = (int)(item % nkb) * C;
+        const int kyc = ky0 + c < my ? ky0 + c : my - 1;
+        // a uniform image base and 32-bit element offsets (an image holds
+        // at most 512 x 64 of them): one address register per load
+        const float2* const src = r + img * (int64_t)H * my;
+        const uint32_t o0 = (uint32_t)(n1 * my + kyc), os = (uint32_t)(L * my);
+        float2 v[16];
+#pragma unroll
+        for (int n2 = 0; n2 < 16; ++n2) v[n2] = src[o0 + os * (uint32_t)n2];
+        dft<16, -1>(v);
+#pragma unroll
+        for (int q = 0; q < 16; ++q) stage[(q * C + c) * SS + n1 + n1 / 16] = v[q];
+        __syncthreads();
+        const float2* const sp = stage + (rr * C + cr) * SS + 17 * pb;
+        float2 s16[16];
+#pragma unroll
+        for (int t = 0; t < 16; ++t) s16[t] = sp[t];
+        float2* const dst = xh + img * (int64_t)nk * my + ky0 + cr;
+        const bool store = pb == 0 && ky0 + cr < my;
+#pragma unroll
+        for (int i = 0; i < MPR; ++i) {
+            if (i < nm) {                                // uniform
+                float2 u[8];
+#pragma unroll
+                for (int t = 0; t < 8; ++t) u[t] = cfma(s16[2 * t], wk[i], s16[2 * t + 1]);
+                const float2 w2 = cmul(wk[i], wk[i]);
+                const float2 w4 = cmul(w2, w2);
+                const float2 w8 = cmul(w4, w4);
+#pragma unroll
+                for (int t = 0; t < 4; ++t) u[t] = cfma(u[2 * t], w2, u[2 * t + 1]);
+#pragma unroll
+                for (int t = 0; t < 2; ++t) u[t] = cfma(u[2 * t], w4, u[2 * t + 1]);
+                float2 acc = cmul(vk[i], cfma(u[0], w8, u[1]));
+                if constexpr (PB == 2) {
+                    acc.x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(acc.x), 0xB1, 0xF, 0xF, false));
+                    acc.y += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(acc.y), 0xB1, 0xF, 0xF, false));
+                }
+                if (store) dst[(int64_t)(rr + 16 * i) * my] = acc;
+                // one mode at a time: the next mode's tree starts from a
+                // factor defined after this mode's result, so that the trees
+                // do not all run side by side in registers
+                if (i + 1 < MPR) asm volatile("" : "+v"(wk[i + 1].x), "+v"(wk[i + 1].y) : "v"(acc.x), "v"(acc.y));
+            }
+        }
+        __syncthreads();                                 // the stage is read before the next block overwrites it
+    }
+}
+
+template <int L>
+__global__ __launch_bounds__(16 * L) void k_cols_inv_short(const float2* __restrict__ yh, float2* __restrict__ r,
+                                                          int64_t nitems, int nkb, int mx, int my,
+                                                          const float2* __restrict__ tw) {
+    static_assert(L == 16 || L == 32, "short columns: 256 or 512 rows");
+    constexpr int H = 16 * L, C = kShortC, NT = 16 * L;
+    // 16-byte aligned: the mode pairs below are read as one 16-byte word
+    __shared__ __align__(16) float2 T[L * kShortKS];   // [n1][q]: W^{-n1 k_q}
+    __shared__ __align__(16) float2 xs[C * kShortKS];  // [c][q]: the block's kept modes
+    const int tid = threadIdx.x;
+    const int c = tid % C, n1 = tid / C;
+    const int nk = 2 * mx;
+    for (int e = tid; e < L * nk; e += NT) {
+        const int n = e / nk, q = e % nk;
+        const int k = q < mx ? q : H - nk + q;
+        T[n * kShortKS + q] = conj2(tw[((int64_t)n * k * (kNMax / H)) & (kNMax - 1)]);
+    }
+    const float2* const tp = T + n1 * kShortKS;
+    const float2* const xp = xs + c * kShortKS;
+    for (int64_t item = blockIdx.x; item < nitems; item += gridDim.x) {
+        const int64_t img = item / nkb;
+        const int ky0 = (int)(item % nkb) * C;
+        const float2* const src = yh + img * (int64_t)nk * my + ky0;
+        // the block's kept modes (column fastest: whole runs of each mode row)
+        for (int e = tid; e < nk * C; e += NT) {
+            const int q = e / C, cc = e % C;
+            xs[cc * kShortKS + q] = ky0 + cc < my ? src[(int64_t)q * my + cc] : make_float2(0.0f, 0.0f);
+        }
+        __syncthreads();
+        float2 v[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) v[j] = make_float2(0.0f, 0.0f);
+        // modes in chunks of 16 (q mod 16 static), two per LDS read
+        static_for<0, kMaxKept / 16>([&](auto ch) {
+            if (16 * ch < nk) {                          // uniform
+                static_for<0, 8>([&](auto p) {
+                    constexpr int q = 16 * ch + 2 * p;
+                    const float4 t2 = *reinterpret_cast<const float4*>(tp + q);
+                    const float4 x2 = *reinterpret_cast<const float4*>(xp + q);
+                    v[2 * p] = cfma(v[2 * p], make_float2(t2.x, t2.y), make_float2(x2.x, x2.y));
+                    v[2 * p + 1] = cfma(v[2 * p + 1], make_float2(t2.z, t2.w), make_float2(x2.z, x2.w));
+                });
+            }
+        });
+        __syncthreads();                                 // the modes are read before the next block overwrites them
+        dft<16, 1>(v);
+        if (ky0 + c < my) {
+            float2* const dst = r + img * (int64_t)H * my;
+            const uint32_t o0 = (uint32_t)(n1 * my + ky0 + c), os = (uint32_t)(L * my);
+#pragma unroll
+            for (int n2 = 0; n2 < 16; ++n2) dst[o0 + os * (uint32_t)n2] = v[n2];
+        }
+    }
+}
+
+// persistent grid: as many workgroups as fit on the device at once, at
+// most one per work item
+template <typename K>
+hipError_t short_grid(K kernel, int threads, int64_t nitems, unsigned* g) {
+    int dev = 0, cus = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return hipErrorInvalidDevice;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+    const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0);
+    if (e != hipSuccess) return e;
+    int64_t n = (int64_t)cus * (per_cu > 0 ? per_cu : 1);
+    if (n > nitems) n = nitems;
+    *g = (unsigned)n;
+    return hipSuccess;
+}
+
+bool cols_short_supported(int log2H, int mx) { return (log2H == 8 || log2H == 9) && (2 * mx) % 16 == 0; }
+
 }  // namespace
 
 bool cols_pruned_supported(int log2H, int mx, int my) {
@@ -206,6 +373,19 @@ bool cols_pruned_supported(int log2H, int mx, int my) {
 hipError_t launch_cols_fwd_pruned(const float2* r, float2* xh, int64_t nimg, int log2H, int mx, int my, float scale,
                                   const float2* tw, hipStream_t s) {
     if (!cols_pruned_supported(log2H, mx, my)) return hipErrorInvalidValue;
+    if (cols_short_supported(log2H, mx)) {
+        const int nkb = (my + kShortC - 1) / kShortC;
+        const int64_t ni = nimg * nkb;
+        unsigned g = 0;
+        if (log2H == 8) {
+            const hipError_t e = short_grid(k_cols_fwd_short<16>, 256, ni, &g);
+            if (e != hipSuccess) return e;
+            return launch_kernel(k_cols_fwd_short<16>, dim3(g), dim3(256), 0, s, r, xh, ni, nkb, mx, my, scale, tw);
+        }
+        const hipError_t e = short_grid(k_cols_fwd_short<32>, 512, ni, &g);
+        if (e != hipSuccess) return e;
+        return launch_kernel(k_cols_fwd_short<32>, dim3(g), dim3(512), 0, s, r, xh, ni, nkb, mx, my, scale, tw);
+    }
     const int nkb = (my + kColC - 1) / kColC;
     const int64_t nb = nimg * nkb;
     if (nb >= INT32_MAX) return hipErrorInvalidValue;
@@ -221,6 +401,19 @@ hipError_t launch_cols_fwd_pruned(const float2* r, float2* xh, int64_t nimg, int
 hipError_t launch_cols_inv_pruned(const float2* yh, float2* r, int64_t nimg, int log2H, int mx, int my,
                                   const float2* tw, hipStream_t s) {
     if (!cols_pruned_supported(log2H, mx, my)) return hipErrorInvalidValue;
+    if (cols_short_supported(log2H, mx)) {
+        const int nkb = (my + kShortC - 1) / kShortC;
+        const int64_t ni = nimg * nkb;
+        unsigned g = 0;
+        if (log2H == 8) {
+            const hipError_t e = short_grid(k_cols_inv_short<16>, 256, ni, &g);
+            if (e != hipSuccess) return e;
+            return launch_kernel(k_cols_inv_short<16>, dim3(g), dim3(256), 0, s, yh, r, ni, nkb, mx, my, tw);
+        }
+        const hipError_t e = short_grid(k_cols_inv_short<32>, 512, ni, &g);
+        if (e != hipSuccess) return e;
+        return launch_kernel(k_cols_inv_short<32>, dim3(g), dim3(512), 0, s, yh, r, ni, nkb, mx, my, tw);
+    }
     const int nkb = (my + kColC - 1) / kColC;
     const int64_t nb = nimg * nkb;
     if (nb >= INT32_MAX) return hipErrorInvalidValue;

@@ -75,7 +75,7 @@ FILTER_2D = [
     (2, 3, 8, 8, 4, 5),             # every mode kept (the untruncated global filter)
     (3, 5, 32, 16, 3, 9),           # small-grid kernels, odd channels, tiled padding modes
     (2, 7, 64, 64, 5, 7),           # one row per thread, ragged mode tile
-    (1, 3, 256, 256, 9, 11),        # staged: 256-point pruned rows, generic columns (odd mx)
+    (1, 3, 256, 256, 9, 11),        # staged: 256-point short rows, generic columns (odd mx)
     (1, 2, 16, 1024, 5, 50),        # pruned long rows
     (1, 2, 1024, 16, 8, 9),         # pruned columns
     (2, 3, 60, 35, 12, 10),         # mixed-radix lengths
@@ -91,7 +91,7 @@ def test_filter_shapes_2d(shape):
 FILTER_1D = [
     # B, C, N, modes
     (3, 2, 16, 9),                  # every bin kept, odd mode count
-    (5, 3, 512, 64),                # pruned rows
+    (5, 3, 512, 64),                # 512-point short rows
     (2, 4, 4096, 33),               # pruned rows, odd mode count
 ]
 

@@ -73,7 +73,7 @@ GELU_2D = [
     (3, 4, 6, 32, 16, 3, 9),          # small-grid kernel
     (2, 8, 16, 64, 64, 16, 16),       # one row per thread
     (2, 4, 6, 64, 128, 8, 20),        # one row per thread, 64 x 128
-    (1, 2, 3, 256, 256, 9, 11),       # staged: 256-point pruned rows, generic columns (odd mx)
+    (1, 2, 3, 256, 256, 9, 11),       # staged: 256-point short rows, generic columns (odd mx)
     (1, 2, 3, 128, 256, 9, 100),      # staged: generic rows (more than 64 bins)
     (1, 2, 3, 16, 1024, 5, 50),       # staged: pruned long rows
     (1, 2, 2, 1024, 16, 8, 9),        # staged: pruned columns, generic rows
@@ -90,7 +90,9 @@ def test_gelu_shapes_2d(shape):
 GELU_1D = [
     # B, Cin, Cout, N, modes
     (3, 2, 5, 16, 9),                 # generic rows, every bin kept
-    (5, 3, 2, 512, 64),               # pruned rows
+    (5, 3, 2, 512, 64),               # 512-point short rows
+    (3, 2, 3, 256, 64),               # 256-point short rows, ragged last group of four rows
+    (3, 2, 3, 512, 40),               # 512-point short rows, ragged last pair of rows
     (2, 4, 3, 4096, 33),              # pruned rows, longest
 ]
 
@@ -110,7 +112,7 @@ def test_gelu_optional_terms(use_bias, use_branch):
 @pytest.mark.parametrize("kind,shape", [
     ("2d", (1, 1, 2, 64, 64, 8, 8)),        # one row per thread
     ("2d", (1, 1, 2, 32, 32, 4, 4)),        # small-grid kernel
-    ("2d", (1, 1, 2, 256, 256, 4, 4)),      # staged, 256-point pruned rows and columns
+    ("2d", (1, 1, 2, 256, 256, 4, 4)),      # staged, 256-point short rows and pruned columns
     ("1d", (1, 1, 2, 1, 2048, 1, 16)),      # pruned long rows
 ])
 def test_gelu_activation_accuracy(kind, shape):

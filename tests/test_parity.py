@@ -152,10 +152,13 @@ def test_stages_1d(name):
 EDGE_2D = [
     # B, Cin, Cout, H, W, mx, my
     (300, 2, 3, 32, 32, 8, 8),      # one-kernel small path: more batch items than CUs
-    (2, 4, 4, 256, 256, 32, 32),    # 256-point pruned rows and columns (Q = 4)
-    (2, 3, 5, 256, 512, 16, 17),    # 512-point pruned rows, 256-row pruned columns
-    (2, 3, 2, 512, 256, 64, 64),    # 256-point rows, every bin up to 64; 128 kept kx of 512 rows
+    (2, 4, 4, 256, 256, 32, 32),    # 256-point short rows, 256-row short columns
+    (2, 3, 5, 256, 512, 16, 17),    # 512-point short rows, 256-row short columns, one column in the last block
+    (2, 3, 2, 512, 256, 64, 64),    # 256-point short rows, every bin up to 64; 512-row short columns, 128 kept kx
     (1, 2, 3, 128, 256, 9, 100),    # 256-point rows with more than 64 bins: generic rows and columns
+    (1, 2, 3, 512, 128, 24, 5),     # 512-row short columns, one partial block of 16 columns
+    (4, 160, 160, 256, 128, 8, 40), # 256-row short columns: more column blocks than workgroups, ragged last block
+    (3, 100, 100, 512, 128, 8, 40), # 512-row short columns: more column blocks than workgroups
     (5, 8, 8, 32, 32, 16, 16),      # one-kernel small path: most channels (two rounds), every kx kept
     (4, 7, 1, 16, 64, 8, 17),       # one-kernel small path: one output channel (idle groups in the inverse)
     (2, 3, 3, 8, 128, 2, 40),       # one-kernel small path: 8 x 128 grid
@@ -204,13 +207,14 @@ EDGE_1D = [
     (3, 1, 2, 16, 9),               # odd number of rows, full modes
     (7, 3, 5, 64, 17),              # odd rows B*Cin = 21
     (2, 4, 70, 4096, 2049),         # longest sequence, every bin kept
-    (33, 2, 3, 256, 1),             # DC only
-    (5, 3, 2, 512, 64),             # pruned rows, 8 samples per lane, bins wrap mod 8
+    (33, 2, 3, 256, 1),             # DC only, short rows with a ragged last group of four
+    (5, 3, 2, 512, 64),             # 512-point short rows, every bin up to 64, odd forward row count
     (3, 2, 3, 1024, 1),             # pruned rows, DC only
     (4, 3, 5, 2048, 37),            # pruned rows, partial last chunk of 16 bins
     (2, 2, 3, 2048, 16),            # pruned rows: only the first 16 residues staged
-    (3, 2, 3, 256, 64),             # 256-point pruned rows, every bin up to 64
-    (2, 3, 2, 256, 33),             # 256-point pruned rows, odd mode count
+    (3, 2, 3, 256, 64),             # 256-point short rows, every bin up to 64
+    (2, 3, 2, 256, 33),             # 256-point short rows, odd mode count
+    (3, 2, 3, 512, 17),             # 512-point short rows, one bin past the first 16, odd row counts
     (3, 1, 2, 1024, 17),            # pruned rows: one bin in the second group of each residue
     (9, 2, 2, 4096, 17),            # pruned rows, odd row count
 ]
