@@ -420,11 +420,14 @@ __global__ __launch_bounds__(kPrunedThreads) __attribute__((amdgpu_waves_per_eu(
     }
 }
 
-template <int L, bool EPI>
+// NJ: the 16-bin groups that can hold a kept bin (1, 2 or 4: my <= 16 NJ);
+// the others are zero and skipped.
+template <int L, bool EPI, int NJ>
 __global__ __launch_bounds__(kPrunedThreads) __attribute__((amdgpu_waves_per_eu(4))) void k_rows_inv_short(
     const float2* __restrict__ y, float* __restrict__ out, int64_t nrows, int my, int y_ld, float scale,
     const float2* __restrict__ tw, Epilogue epi) {
     static_assert(L == 16 || L == 32, "short rows: 256 or 512 points");
+    static_assert(NJ == 1 || NJ == 2 || NJ == 4, "16-bin groups");
     constexpr int Q = 16, N = Q * L, NZ = Q / 2;
     constexpr int RPW = 64 / L;
     __shared__ float2 xrow_all[kPrunedWaves][RPW * 64];
@@ -439,7 +442,7 @@ __global__ __launch_bounds__(kPrunedThreads) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
     for (int r = 0; r <= NZ; ++r) tr[r] = cscale(tw[(n1 * r * (kNMax / N)) & (kNMax - 1)], scale);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) pj[j] = tw[(16 * n1 * j * (kNMax / N)) & (kNMax - 1)];
+    for (int j = 0; j < 4; ++j) pj[j] = tw[(16 * n1 * j * (kNMax / N)) & (kNMax - 1)];   // pj[1] is needed for any NJ
     auto res = [&](auto r) __attribute__((always_inline)) {
         if constexpr (r <= NZ) return tr[r];
         else return cmul(pj[1], conj2(tr[r <= NZ ? 0 : Q - r]));
@@ -475,20 +478,20 @@ __global__ __launch_bounds__(kPrunedThreads) __attribute__((amdgpu_waves_per_eu(
         // residue, one at a time with the next residue's four bins read
         // ahead: left alone the compiler issues all 64 reads at once and
         // holds them in registers
-        float2 V[Q], cur[4], nxt[4];
+        float2 V[Q], cur[NJ], nxt[NJ];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) cur[j] = xr[Q * j];
+        for (int j = 0; j < NJ; ++j) cur[j] = xr[Q * j];
         static_for<0, Q>([&](auto r) {
             if constexpr (r + 1 < Q) {
 #pragma unroll
-                for (int j = 0; j < 4; ++j) nxt[j] = xr[r + 1 + Q * j];
+                for (int j = 0; j < NJ; ++j) nxt[j] = xr[r + 1 + Q * j];
             }
             float2 acc = cur[0];
-            static_for<1, 4>([&](auto j) { acc = cfma(acc, cur[j], conj2(pj[j])); });
+            static_for<1, NJ>([&](auto j) { acc = cfma(acc, cur[j], conj2(pj[j])); });
             V[r] = cmul(acc, conj2(res(r)));
             asm volatile("" : "+v"(V[r].x), "+v"(V[r].y) : : "memory");
 #pragma unroll
-            for (int j = 0; j < 4; ++j) cur[j] = nxt[j];
+            for (int j = 0; j < NJ; ++j) cur[j] = nxt[j];
         });
         // the Hermitian part H[r] = V[r] + conj V[-r]
         float2 H[NZ + 1];
@@ -548,6 +551,15 @@ hipError_t launch_rows(K kernel, int64_t nrows, hipStream_t s, const TI* in, TO*
                          extra...);
 }
 
+// the short inverse for the 16-bin groups that my reaches
+template <int L, bool EPI>
+hipError_t launch_rows_inv_short(int64_t nrows, hipStream_t s, const float2* y, float* out, int my, int y_ld,
+                                 float scale, const float2* tw, const Epilogue& epi) {
+    if (my <= 16) return launch_rows(k_rows_inv_short<L, EPI, 1>, nrows, s, y, out, my, y_ld, scale, tw, epi);
+    if (my <= 32) return launch_rows(k_rows_inv_short<L, EPI, 2>, nrows, s, y, out, my, y_ld, scale, tw, epi);
+    return launch_rows(k_rows_inv_short<L, EPI, 4>, nrows, s, y, out, my, y_ld, scale, tw, epi);
+}
+
 }  // namespace
 
 bool rows_pruned_supported(int log2W, int my) { return log2W >= 8 && log2W <= 12 && my >= 1 && my <= 64; }
@@ -569,16 +581,16 @@ hipError_t launch_rows_inv_pruned(const float2* y, float* out, int64_t nrows, in
     if (!rows_pruned_supported(log2W, my) || nrows <= 0) return hipErrorInvalidValue;
     if (epi.on) {
         switch (log2W) {
-            case 8: return launch_rows(k_rows_inv_short<16, true>, nrows, s, y, out, my, y_ld, scale, tw, epi);
-            case 9: return launch_rows(k_rows_inv_short<32, true>, nrows, s, y, out, my, y_ld, scale, tw, epi);
+            case 8: return launch_rows_inv_short<16, true>(nrows, s, y, out, my, y_ld, scale, tw, epi);
+            case 9: return launch_rows_inv_short<32, true>(nrows, s, y, out, my, y_ld, scale, tw, epi);
             case 10: return launch_rows(k_rows_inv_pruned<16, true>, nrows, s, y, out, my, y_ld, scale, tw, epi);
             case 11: return launch_rows(k_rows_inv_pruned<32, true>, nrows, s, y, out, my, y_ld, scale, tw, epi);
             default: return launch_rows(k_rows_inv_pruned<64, true>, nrows, s, y, out, my, y_ld, scale, tw, epi);
         }
     }
     switch (log2W) {
-        case 8: return launch_rows(k_rows_inv_short<16, false>, nrows, s, y, out, my, y_ld, scale, tw, epi);
-        case 9: return launch_rows(k_rows_inv_short<32, false>, nrows, s, y, out, my, y_ld, scale, tw, epi);
+        case 8: return launch_rows_inv_short<16, false>(nrows, s, y, out, my, y_ld, scale, tw, epi);
+        case 9: return launch_rows_inv_short<32, false>(nrows, s, y, out, my, y_ld, scale, tw, epi);
         case 10: return launch_rows(k_rows_inv_pruned<16, false>, nrows, s, y, out, my, y_ld, scale, tw, epi);
         case 11: return launch_rows(k_rows_inv_pruned<32, false>, nrows, s, y, out, my, y_ld, scale, tw, epi);
         default: return launch_rows(k_rows_inv_pruned<64, false>, nrows, s, y, out, my, y_ld, scale, tw, epi);

@@ -93,6 +93,9 @@ GELU_1D = [
     (5, 3, 2, 512, 64),               # 512-point short rows
     (3, 2, 3, 256, 64),               # 256-point short rows, ragged last group of four rows
     (3, 2, 3, 512, 40),               # 512-point short rows, ragged last pair of rows
+    (2, 3, 2, 256, 32),               # 256-point short rows, bins in the first two groups of 16
+    (2, 2, 3, 512, 16),               # 512-point short rows, bins in the first group of 16 only
+    (2, 2, 2, 512, 20),               # 512-point short rows, bins in the first two groups of 16
     (2, 4, 3, 4096, 33),              # pruned rows, longest
 ]
 

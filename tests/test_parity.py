@@ -215,6 +215,7 @@ EDGE_1D = [
     (3, 2, 3, 256, 64),             # 256-point short rows, every bin up to 64
     (2, 3, 2, 256, 33),             # 256-point short rows, odd mode count
     (3, 2, 3, 512, 17),             # 512-point short rows, one bin past the first 16, odd row counts
+    (2, 2, 3, 512, 16),             # 512-point short rows, bins in the first group of 16 only
     (3, 1, 2, 1024, 17),            # pruned rows: one bin in the second group of each residue
     (9, 2, 2, 4096, 17),            # pruned rows, odd row count
 ]
