@@ -175,8 +175,9 @@ hipError_t launch_mix_mfma(const float2* xh, const SpecLayout& lx, const float2*
                            const SpecLayout& ly, int64_t B, int64_t Cin, int64_t Cout, int64_t M, hipStream_t s,
                            bool adjoint = false);
 
-// ---- pruned long-row transforms (fno_rows_pruned.hip) ------------------------
-// Rows of W = 2^log2W real points, W in [256, 4096], bins ky < my <= 64:
+// ---- pruned row transforms (fno_rows_pruned.hip) ----------------------------
+// Rows of W = 2^log2W real points, W in [64, 4096], bins ky < my <= 64
+// (my <= 32 at W = 64):
 // same contract as launch_rows_fwd / launch_rows_inv below, which use them
 // whenever rows_pruned_supported holds.
 bool rows_pruned_supported(int log2W, int my);

@@ -1,4 +1,4 @@
-// Pruned transforms of real rows of 256 to 4096 points
+// Pruned transforms of real rows of 64 to 4096 points
 // when only the bins k < my <= 64 are kept: the forward R2C that computes
 // just those bins, and the C2R that rebuilds a row from them (FFT blog,
 // section 2.2: R2C / C2R on the N/2+1 half spectrum; TurboFNO blog, section
@@ -28,7 +28,7 @@
 // the factor W^{-n1 r} is applied once per residue after the sum over j.
 // The waves of a workgroup share no data; the grid is persistent, each wave
 // walking rows.  Rows of 1024 to 4096 points (Q in {16, 32, 64}) take the
-// one-row-per-wave kernels; rows of 256 and 512 points take the short-row
+// one-row-per-wave kernels; rows of 64 to 512 points take the short-row
 // kernels further down, several rows per wave.
 #include "fno_device.hpp"
 #include "fno_internal.hpp"
@@ -323,35 +323,38 @@ __global__ __launch_bounds__(kPrunedThreads) __attribute__((amdgpu_waves_per_eu(
     }
 }
 
-// ---- short rows: N = 16 L points, L in {16, 32} ------------------------------
+// ---- short rows: N = 16 L points, L in {4, 8, 16, 32} ------------------------
 // One row per wave would leave a lane of a 256-point row four samples, and
 // the 64-phase reduction above would cost several times the instructions
-// per byte of the long rows.  A row of 256 or 512 points takes L = N / 16
+// per byte of the long rows.  A row of 64 to 512 points takes L = N / 16
 // lanes instead: lane n1 < L holds the samples n1 + L n2 (n2 < 16) and runs
 // a 16-point real DFT, and a wave carries 64 / L rows at once.  With
 // W = exp(-2 pi i / N):
 //   X[k] = sum_{n1 < L} W^{n1 k} Y_n1[k mod 16],
-// formed by one reading lane per (row, bin, block of 16 phases) with the
-// binary tree of the long rows (factors W^k, W^2k, W^4k, W^8k), the L / 16
-// blocks added across neighbouring lanes.  The inverse mirrors the long-row
+// formed by one reading lane per (row, bin, block of up to 16 phases) with
+// the binary tree of the long rows (factors W^k, W^2k, W^4k, ...), the two
+// blocks of a 512-point row added across neighbouring lanes.  The inverse mirrors the long-row
 // one with 16 residues, V[r] = conj(W^{n1 r}) sum_j X'[r + 16 j] conj(W_L^{n1 j}),
 // and carries the same fused epilogue.
 template <int L>
 __global__ __launch_bounds__(kPrunedThreads) __attribute__((amdgpu_waves_per_eu(4))) void k_rows_fwd_short(
     const float* __restrict__ x, float2* __restrict__ y, int64_t nrows, int my, int y_ld, float scale,
     const float2* __restrict__ tw) {
-    static_assert(L == 16 || L == 32, "short rows: 256 or 512 points");
+    static_assert(L == 4 || L == 8 || L == 16 || L == 32, "short rows: 64 to 512 points");
     constexpr int Q = 16, N = Q * L, NZ = Q / 2, SROWS = NZ + 1;
     constexpr int RPW = 64 / L;              // rows per wave
-    constexpr int PB = L / 16;               // 16-phase blocks per row
-    constexpr int SS = L + PB;               // stage row stride (complex): a pad after every 16 phases
+    constexpr int PBS = L < 16 ? L : 16;     // phases per block
+    constexpr int PB = L / PBS;              // phase blocks per row
+    constexpr int SS = L + PB;               // stage row stride (complex): a pad after every block
+    constexpr int NSL = RPW * PB;            // slots: every lane holds one item of each
+    constexpr int BPS = 64 / NSL;            // bins per slot
     __shared__ float2 stage_all[kPrunedWaves][RPW * SROWS * SS];
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     float2* const stage = stage_all[wave];
     const int rw = lane / L, n1 = lane % L;   // loading role: row rw of the wave's rows, phase n1
-    // Reading role: phase block pb and item group g; slot s (bins 16 s ..
-    // 16 s + 15 of every row) holds item s 64/PB + g = (row it mod RPW,
+    // Reading role: phase block pb and item group g; slot s (bins BPS s ..
+    // BPS s + BPS - 1 of every row) holds item s 64/PB + g = (row it mod RPW,
     // bin it div RPW).  A bin whose residue r exceeds Q/2 reads the staged
     // row Q - r (its conjugate) with conjugated factors and conjugates the sum.
     const int pb = lane % PB;
@@ -361,23 +364,29 @@ __global__ __launch_bounds__(kPrunedThreads) __attribute__((amdgpu_waves_per_eu(
         rr = it % RPW;
         k = it / RPW;
     };
-    float2 wk[4], vk[4];
+    // W^k of each slot's bin, and W^{PBS pb k} with two blocks per row
+    float2 wk[NSL], vk[PB == 2 ? NSL : 1];
     const float half_scale = 0.5f * scale;
 #pragma unroll
-    for (int sl = 0; sl < 4; ++sl) {
+    for (int sl = 0; sl < NSL; ++sl) {
         int rr, k;
         item(sl, rr, k);
         const bool cj = k % Q > NZ;
         const float2 w = tw[(k * (kNMax / N)) & (kNMax - 1)];
-        const float2 u = cscale(tw[(16 * pb * k * (kNMax / N)) & (kNMax - 1)], half_scale);
         wk[sl] = cj ? conj2(w) : w;
-        vk[sl] = cj ? conj2(u) : u;
+        if constexpr (PB == 2) {
+            const float2 u = cscale(tw[(PBS * pb * k * (kNMax / N)) & (kNMax - 1)], half_scale);
+            vk[sl] = cj ? conj2(u) : u;
+        }
     }
     const int64_t nwaves = (int64_t)gridDim.x * kPrunedWaves;
     for (int64_t row0 = ((int64_t)blockIdx.x * kPrunedWaves + wave) * RPW; row0 < nrows; row0 += nwaves * RPW) {
 #pragma unroll
-        for (int sl = 0; sl < 4; ++sl)
-            asm volatile("" : "+v"(wk[sl].x), "+v"(wk[sl].y), "+v"(vk[sl].x), "+v"(vk[sl].y));
+        for (int sl = 0; sl < NSL; ++sl) asm volatile("" : "+v"(wk[sl].x), "+v"(wk[sl].y));
+        if constexpr (PB == 2) {
+#pragma unroll
+            for (int sl = 0; sl < NSL; ++sl) asm volatile("" : "+v"(vk[sl].x), "+v"(vk[sl].y));
+        }
         // a row past the end repeats the last one (never stored)
         const int64_t row = row0 + rw < nrows ? row0 + rw : nrows - 1;
         const float* src = x + row * N + n1;
@@ -385,33 +394,35 @@ __global__ __launch_bounds__(kPrunedThreads) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
         for (int m = 0; m < NZ; ++m) z[m] = make_float2(src[L * (2 * m)], src[L * (2 * m + 1)]);
         dft<NZ, -1>(z);
-        // 2 Y[r], r <= Q/2, staged at (row, r, phase n1 + its pad)
-        static_for<0, SROWS>([&](auto r) { stage[(rw * SROWS + r) * SS + n1 + n1 / 16] = real_bin2<Q, r>(z); });
+        // 2 Y[r], r <= Q/2, staged at (row, r, phase n1 + its block's pad)
+        static_for<0, SROWS>([&](auto r) { stage[(rw * SROWS + r) * SS + n1 + n1 / PBS] = real_bin2<Q, r>(z); });
         wave_lds_sync();
-        static_for<0, 4>([&](auto sl) {
-            if (16 * sl < my) {                  // uniform: a slot with a kept bin
+        static_for<0, NSL>([&](auto sl) {
+            if (BPS * sl < my) {                 // uniform: a slot with a kept bin
                 int rr, k;
                 item(sl, rr, k);
                 const int r = k % Q;
                 const bool cj = r > NZ;
-                const float2* const sp = stage + (rr * SROWS + (cj ? Q - r : r)) * SS + 17 * pb;
-                float2 v[16];
+                const float2* const sp = stage + (rr * SROWS + (cj ? Q - r : r)) * SS + (PBS + 1) * pb;
+                // the block's sum over its PBS phases t as a binary tree
+                // with the factors W^k, W^2k, W^4k, ...
+                float2 v[PBS];
 #pragma unroll
-                for (int t = 0; t < 16; ++t) v[t] = sp[t];
-                float2 u[8];
+                for (int t = 0; t < PBS; ++t) v[t] = sp[t];
+                float2 w = wk[sl];
 #pragma unroll
-                for (int t = 0; t < 8; ++t) u[t] = cfma(v[2 * t], wk[sl], v[2 * t + 1]);
-                const float2 w2 = cmul(wk[sl], wk[sl]);
-                const float2 w4 = cmul(w2, w2);
-                const float2 w8 = cmul(w4, w4);
+                for (int len = PBS; len > 1; len /= 2) {
 #pragma unroll
-                for (int t = 0; t < 4; ++t) u[t] = cfma(u[2 * t], w2, u[2 * t + 1]);
-#pragma unroll
-                for (int t = 0; t < 2; ++t) u[t] = cfma(u[2 * t], w4, u[2 * t + 1]);
-                float2 acc = cmul(vk[sl], cfma(u[0], w8, u[1]));
+                    for (int t = 0; t < len / 2; ++t) v[t] = cfma(v[2 * t], w, v[2 * t + 1]);
+                    if (len > 2) w = cmul(w, w);
+                }
+                float2 acc;
                 if constexpr (PB == 2) {
+                    acc = cmul(vk[sl], v[0]);
                     acc.x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(acc.x), 0xB1, 0xF, 0xF, false));
                     acc.y += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(acc.y), 0xB1, 0xF, 0xF, false));
+                } else {
+                    acc = cscale(v[0], half_scale);
                 }
                 if (pb == 0 && k < my && row0 + rr < nrows) y[(row0 + rr) * (int64_t)y_ld + k] = cj ? conj2(acc) : acc;
             }
@@ -423,10 +434,10 @@ __global__ __launch_bounds__(kPrunedThreads) __attribute__((amdgpu_waves_per_eu(
 // NJ: the 16-bin groups that can hold a kept bin (1, 2 or 4: my <= 16 NJ);
 // the others are zero and skipped.
 template <int L, bool EPI, int NJ>
-__global__ __launch_bounds__(kPrunedThreads) __attribute__((amdgpu_waves_per_eu(4))) void k_rows_inv_short(
+__global__ __launch_bounds__(kPrunedThreads) __attribute__((amdgpu_waves_per_eu(EPI && L <= 8 ? 3 : 4))) void k_rows_inv_short(
     const float2* __restrict__ y, float* __restrict__ out, int64_t nrows, int my, int y_ld, float scale,
     const float2* __restrict__ tw, Epilogue epi) {
-    static_assert(L == 16 || L == 32, "short rows: 256 or 512 points");
+    static_assert(L == 4 || L == 8 || L == 16 || L == 32, "short rows: 64 to 512 points");
     static_assert(NJ == 1 || NJ == 2 || NJ == 4, "16-bin groups");
     constexpr int Q = 16, N = Q * L, NZ = Q / 2;
     constexpr int RPW = 64 / L;
@@ -448,29 +459,38 @@ __global__ __launch_bounds__(kPrunedThreads) __attribute__((amdgpu_waves_per_eu(
         else return cmul(pj[1], conj2(tr[r <= NZ ? 0 : Q - r]));
     };
     const int64_t nwaves = (int64_t)gridDim.x * kPrunedWaves;
-    // the kept bins of the wave's rows starting at r0, zero past my and past
-    // the last row (in-range loads only: row and bin clamped, the zeros
-    // selected), DC imaginary part dropped and the DC bin halved
-    auto load_bins = [&](int64_t r0, float2 (&v)[RPW]) __attribute__((always_inline)) {
+    // The bins 0 .. BW - 1 (BW = 16 NJ) of the wave's rows starting at r0,
+    // RPL rows per load instruction (lane: row lane / BW, bin lane mod BW),
+    // NL loads per lane; zero past my and past the last row (in-range loads
+    // only: row and bin clamped, the zeros selected).  The bins past BW are
+    // never read.
+    constexpr int BW = 16 * NJ;
+    constexpr int RPL = 64 / BW;
+    constexpr int NL = RPW > RPL ? RPW / RPL : 1;
+    const int lrow = lane / BW, lbin = lane % BW;
+    auto load_bins = [&](int64_t r0, float2 (&v)[NL]) __attribute__((always_inline)) {
 #pragma unroll
-        for (int rr = 0; rr < RPW; ++rr) {
-            const bool keep = lane < my && r0 + rr < nrows;
-            v[rr] = y[(r0 + rr < nrows ? r0 + rr : nrows - 1) * (int64_t)y_ld + (lane < my ? lane : my - 1)];
-            if (!keep) v[rr] = make_float2(0.0f, 0.0f);
+        for (int i = 0; i < NL; ++i) {
+            const int64_t r = r0 + i * RPL + lrow;
+            const bool keep = lbin < my && r < nrows && i * RPL + lrow < RPW;
+            v[i] = y[(r < nrows ? r : nrows - 1) * (int64_t)y_ld + (lbin < my ? lbin : my - 1)];
+            if (!keep) v[i] = make_float2(0.0f, 0.0f);
         }
     };
     const int64_t first = ((int64_t)blockIdx.x * kPrunedWaves + wave) * RPW;
-    float2 vn[RPW];
+    float2 vn[NL];
     load_bins(first < nrows ? first : 0, vn);
     for (int64_t row0 = first; row0 < nrows; row0 += nwaves * RPW) {
 #pragma unroll
         for (int r = 0; r <= NZ; ++r) asm volatile("" : "+v"(tr[r].x), "+v"(tr[r].y));
 #pragma unroll
         for (int j = 0; j < 4; ++j) asm volatile("" : "+v"(pj[j].x), "+v"(pj[j].y));
-        // this group's bins to LDS; the next group's loaded meanwhile
+        // this group's bins to LDS (the DC bin halved, its imaginary part
+        // dropped); the next group's loaded meanwhile
 #pragma unroll
-        for (int rr = 0; rr < RPW; ++rr)
-            xrow[rr * 64 + lane] = lane == 0 ? make_float2(0.5f * vn[rr].x, 0.0f) : vn[rr];
+        for (int i = 0; i < NL; ++i)
+            if (i * RPL + lrow < RPW)
+                xrow[(i * RPL + lrow) * 64 + lbin] = lbin == 0 ? make_float2(0.5f * vn[i].x, 0.0f) : vn[i];
         load_bins(row0 + nwaves * RPW < nrows ? row0 + nwaves * RPW : row0, vn);
         wave_lds_sync();
         const float2* const xr = xrow + rw * 64;
@@ -556,18 +576,26 @@ template <int L, bool EPI>
 hipError_t launch_rows_inv_short(int64_t nrows, hipStream_t s, const float2* y, float* out, int my, int y_ld,
                                  float scale, const float2* tw, const Epilogue& epi) {
     if (my <= 16) return launch_rows(k_rows_inv_short<L, EPI, 1>, nrows, s, y, out, my, y_ld, scale, tw, epi);
-    if (my <= 32) return launch_rows(k_rows_inv_short<L, EPI, 2>, nrows, s, y, out, my, y_ld, scale, tw, epi);
-    return launch_rows(k_rows_inv_short<L, EPI, 4>, nrows, s, y, out, my, y_ld, scale, tw, epi);
+    if (my <= 32 || L == 4)             // 64-point rows keep at most 32 bins
+        return launch_rows(k_rows_inv_short<L, EPI, 2>, nrows, s, y, out, my, y_ld, scale, tw, epi);
+    if constexpr (L > 4) return launch_rows(k_rows_inv_short<L, EPI, 4>, nrows, s, y, out, my, y_ld, scale, tw, epi);
+    return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-bool rows_pruned_supported(int log2W, int my) { return log2W >= 8 && log2W <= 12 && my >= 1 && my <= 64; }
+// at 64 points the kept bins stay below the Nyquist bin 32 (every kept bin
+// but the DC one counts twice in the inverse)
+bool rows_pruned_supported(int log2W, int my) {
+    return log2W >= 6 && log2W <= 12 && my >= 1 && my <= (log2W == 6 ? 32 : 64);
+}
 
 hipError_t launch_rows_fwd_pruned(const float* x, float2* y, int64_t nrows, int log2W, int my, int y_ld, float scale,
                                   const float2* tw, hipStream_t s) {
     if (!rows_pruned_supported(log2W, my) || nrows <= 0) return hipErrorInvalidValue;
     switch (log2W) {
+        case 6: return launch_rows(k_rows_fwd_short<4>, nrows, s, x, y, my, y_ld, scale, tw);
+        case 7: return launch_rows(k_rows_fwd_short<8>, nrows, s, x, y, my, y_ld, scale, tw);
         case 8: return launch_rows(k_rows_fwd_short<16>, nrows, s, x, y, my, y_ld, scale, tw);
         case 9: return launch_rows(k_rows_fwd_short<32>, nrows, s, x, y, my, y_ld, scale, tw);
         case 10: return launch_rows(k_rows_fwd_pruned<16>, nrows, s, x, y, my, y_ld, scale, tw);
@@ -581,6 +609,8 @@ hipError_t launch_rows_inv_pruned(const float2* y, float* out, int64_t nrows, in
     if (!rows_pruned_supported(log2W, my) || nrows <= 0) return hipErrorInvalidValue;
     if (epi.on) {
         switch (log2W) {
+            case 6: return launch_rows_inv_short<4, true>(nrows, s, y, out, my, y_ld, scale, tw, epi);
+            case 7: return launch_rows_inv_short<8, true>(nrows, s, y, out, my, y_ld, scale, tw, epi);
             case 8: return launch_rows_inv_short<16, true>(nrows, s, y, out, my, y_ld, scale, tw, epi);
             case 9: return launch_rows_inv_short<32, true>(nrows, s, y, out, my, y_ld, scale, tw, epi);
             case 10: return launch_rows(k_rows_inv_pruned<16, true>, nrows, s, y, out, my, y_ld, scale, tw, epi);
@@ -589,6 +619,8 @@ hipError_t launch_rows_inv_pruned(const float2* y, float* out, int64_t nrows, in
         }
     }
     switch (log2W) {
+        case 6: return launch_rows_inv_short<4, false>(nrows, s, y, out, my, y_ld, scale, tw, epi);
+        case 7: return launch_rows_inv_short<8, false>(nrows, s, y, out, my, y_ld, scale, tw, epi);
         case 8: return launch_rows_inv_short<16, false>(nrows, s, y, out, my, y_ld, scale, tw, epi);
         case 9: return launch_rows_inv_short<32, false>(nrows, s, y, out, my, y_ld, scale, tw, epi);
         case 10: return launch_rows(k_rows_inv_pruned<16, false>, nrows, s, y, out, my, y_ld, scale, tw, epi);

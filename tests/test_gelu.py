@@ -75,6 +75,7 @@ GELU_2D = [
     (2, 4, 6, 64, 128, 8, 20),        # one row per thread, 64 x 128
     (1, 2, 3, 256, 256, 9, 11),       # staged: 256-point short rows, generic columns (odd mx)
     (1, 2, 3, 128, 256, 9, 100),      # staged: generic rows (more than 64 bins)
+    (1, 2, 3, 256, 64, 8, 12),        # staged: 64-point short rows, 256-row pruned columns
     (1, 2, 3, 16, 1024, 5, 50),       # staged: pruned long rows
     (1, 2, 2, 1024, 16, 8, 9),        # staged: pruned columns, generic rows
     (2, 3, 4, 45, 100, 10, 20),       # mixed-radix rows and columns
@@ -96,6 +97,8 @@ GELU_1D = [
     (2, 3, 2, 256, 32),               # 256-point short rows, bins in the first two groups of 16
     (2, 2, 3, 512, 16),               # 512-point short rows, bins in the first group of 16 only
     (2, 2, 2, 512, 20),               # 512-point short rows, bins in the first two groups of 16
+    (3, 2, 3, 64, 20),                # 64-point short rows, ragged last group of 16 rows
+    (3, 2, 3, 128, 40),               # 128-point short rows, ragged last group of 8 rows
     (2, 4, 3, 4096, 33),              # pruned rows, longest
 ]
 

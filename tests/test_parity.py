@@ -157,6 +157,10 @@ EDGE_2D = [
     (2, 3, 2, 512, 256, 64, 64),    # 256-point short rows, every bin up to 64; 512-row short columns, 128 kept kx
     (1, 2, 3, 128, 256, 9, 100),    # 256-point rows with more than 64 bins: generic rows and columns
     (1, 2, 3, 512, 128, 24, 5),     # 512-row short columns, one partial block of 16 columns
+    (2, 3, 4, 256, 64, 8, 20),      # 64-point short rows (16 rows per wave), bins in two groups of 16
+    (2, 3, 4, 512, 64, 16, 32),     # 64-point short rows, every bin below the Nyquist bin
+    (1, 2, 3, 256, 64, 8, 33),      # 64-point rows keeping the Nyquist bin: generic rows
+    (2, 2, 3, 256, 128, 16, 64),    # 128-point short rows, every bin up to 64
     (4, 160, 160, 256, 128, 8, 40), # 256-row short columns: more column blocks than workgroups, ragged last block
     (3, 100, 100, 512, 128, 8, 40), # 512-row short columns: more column blocks than workgroups
     (5, 8, 8, 32, 32, 16, 16),      # one-kernel small path: most channels (two rounds), every kx kept
@@ -216,6 +220,11 @@ EDGE_1D = [
     (2, 3, 2, 256, 33),             # 256-point short rows, odd mode count
     (3, 2, 3, 512, 17),             # 512-point short rows, one bin past the first 16, odd row counts
     (2, 2, 3, 512, 16),             # 512-point short rows, bins in the first group of 16 only
+    (7, 3, 5, 64, 32),              # 64-point short rows, ragged last group of 16 rows
+    (4, 2, 3, 64, 33),              # 64-point rows keeping the Nyquist bin: generic rows
+    (5, 3, 2, 128, 64),             # 128-point short rows, every bin up to 64
+    (3, 2, 3, 128, 65),             # 128-point rows keeping the Nyquist bin: generic rows
+    (9, 3, 1, 128, 7),              # 128-point short rows, one output channel, ragged groups of 8 rows
     (3, 1, 2, 1024, 17),            # pruned rows: one bin in the second group of each residue
     (9, 2, 2, 4096, 17),            # pruned rows, odd row count
 ]
