@@ -197,7 +197,7 @@ __global__ __launch_bounds__(kColThreads) void k_cols_inv_pruned(const float2* _
     }
 }
 
-// ---- short columns: H = 16 L rows, L in {16, 32} ---------------------------
+// ---- short columns: H = 16 L rows, L in {4, 8, 16, 32} ---------------------
 // At 256 and 512 rows the kernels above hold four or eight samples per
 // thread and gather their twiddles per workgroup for 16 KiB of data.  Here
 // thread (n1, c) of 16 L holds column c's samples n1 + L n2 (n2 < 16) of a
@@ -206,41 +206,68 @@ __global__ __launch_bounds__(kColThreads) void k_cols_inv_pruned(const float2* _
 // persistent, so the twiddles are formed once per thread (forward) or per
 // workgroup (inverse) for all the column blocks it walks.  2 mx must be a
 // multiple of 16: kept mode q then has the residue q mod 16.
-// Forward: every Y_n1[r] is staged in LDS; reading lane (residue r, column,
-// block of 16 phases) forms every kept mode q = r + 16 i of its residue as
-// W^{16 pb k} sum_t (W^k)^t Y_{16 pb + t}[r] by the binary tree above, the
-// L / 16 blocks added across neighbouring lanes.
+// Forward: every Y_n1[r] is staged in LDS; reading role (residue r, column,
+// block of up to 16 phases) forms every kept mode q = r + 16 i of its
+// residue as W^{PBS pb k} sum_t (W^k)^t Y_{PBS pb + t}[r] by the binary
+// tree above, the two blocks of a 512-row column added across neighbouring
+// lanes; with fewer threads than roles (64 and 128 rows) each thread takes
+// several.
 // Inverse: thread (n1, c) accumulates V_n1[r] = sum_{q = r mod 16}
 // W^{-n1 k_q} X[k_q] from a per-workgroup LDS table of the kept modes'
 // twiddles and the block's kept modes, then runs its 16-point inverse DFT.
 constexpr int kShortC = 16;              // columns per work item
-constexpr int kShortKS = kMaxKept + 2;   // LDS row stride of the inverse tables (complex, 16-byte multiple): rows on distinct banks
+
+// kept modes at most, for H rows, and the LDS row stride of the inverse
+// tables (complex, a 16-byte multiple, rows on distinct bank pairs)
+constexpr int short_kept(int H) { return H < kMaxKept ? H : kMaxKept; }
+constexpr int short_ks(int H) { return short_kept(H) + 2; }
 
 template <int L>
 __global__ __launch_bounds__(16 * L) __attribute__((amdgpu_waves_per_eu(4))) void k_cols_fwd_short(const float2* __restrict__ r, float2* __restrict__ xh,
                                                           int64_t nitems, int nkb, int mx, int my, float scale,
                                                           const float2* __restrict__ tw) {
-    static_assert(L == 16 || L == 32, "short columns: 256 or 512 rows");
-    constexpr int H = 16 * L, C = kShortC, PB = L / 16, SS = L + PB;
-    constexpr int MPR = kMaxKept / 16;               // kept modes per residue, at most
-    __shared__ float2 stage[16 * C * SS];            // row (residue, column): the L phases, a pad after every 16
+    static_assert(L == 4 || L == 8 || L == 16 || L == 32, "short columns: 64 to 512 rows");
+    constexpr int H = 16 * L, C = kShortC, NT = 16 * L;
+    constexpr int PBS = L < 16 ? L : 16;             // phases per block
+    constexpr int PB = L / PBS;                      // blocks per column
+    constexpr int SS = L + PB;                       // stage row stride: a pad after every block
+    constexpr int NRD = 16 * C * PB / NT;            // reading roles per thread
+    constexpr int MPR = short_kept(H) / 16;          // kept modes per residue, at most
+    __shared__ float2 stage[16 * C * SS];            // row (residue, column): the L phases
     const int tid = threadIdx.x;
     const int c = tid % C, n1 = tid / C;             // loading role
-    const int pb = tid % PB, cr = (tid / PB) % C, rr = tid / (PB * C);   // reading role
     const int nk = 2 * mx;
     const int nm = nk / 16;                          // kept modes per residue
-    // W^k and W^{16 pb k} (times the output scale) of the lane's modes
-    float2 wk[MPR], vk[MPR];
+    // reading role rho = tid + NT h: block pb, column cr, residue rr
+    auto role = [&](int h, int& pb, int& cr, int& rr) __attribute__((always_inline)) {
+        const int rho = tid + NT * h;
+        pb = rho % PB;
+        cr = (rho / PB) % C;
+        rr = rho / (PB * C);
+    };
+    // W^k of the role's modes, and W^{PBS pb k} (times the output scale)
+    // with two blocks per column
+    float2 wk[NRD][MPR], vk[PB == 2 ? NRD : 1][MPR];
 #pragma unroll
-    for (int i = 0; i < MPR; ++i) {
-        const int q = rr + 16 * i;
-        const int k = q < nk ? (q < mx ? q : H - nk + q) : 0;
-        wk[i] = tw[((int64_t)k * (kNMax / H)) & (kNMax - 1)];
-        vk[i] = cscale(tw[((int64_t)16 * pb * k * (kNMax / H)) & (kNMax - 1)], scale);
+    for (int h = 0; h < NRD; ++h) {
+        int pb, cr, rr;
+        role(h, pb, cr, rr);
+#pragma unroll
+        for (int i = 0; i < MPR; ++i) {
+            const int q = rr + 16 * i;
+            const int k = q < nk ? (q < mx ? q : H - nk + q) : 0;
+            wk[h][i] = tw[((int64_t)k * (kNMax / H)) & (kNMax - 1)];
+            if constexpr (PB == 2) vk[h][i] = cscale(tw[((int64_t)PBS * pb * k * (kNMax / H)) & (kNMax - 1)], scale);
+        }
     }
     for (int64_t item = blockIdx.x; item < nitems; item += gridDim.x) {
 #pragma unroll
-        for (int i = 0; i < MPR; ++i) asm volatile("" : "+v"(wk[i].x), "+v"(wk[i].y), "+v"(vk[i].x), "+v"(vk[i].y));
+        for (int h = 0; h < NRD; ++h)
+#pragma unroll
+            for (int i = 0; i < MPR; ++i) {
+                asm volatile("" : "+v"(wk[h][i].x), "+v"(wk[h][i].y));
+                if constexpr (PB == 2) asm volatile("" : "+v"(vk[h][i].x), "+v"(vk[h][i].y));
+            }
         const int64_t img = item / nkb;
         const int ky0 = (int)(item % nkb) * C;
         const int kyc = ky0 + c < my ? ky0 + c : my - 1;
@@ -253,37 +280,46 @@ __global__ __launch_bounds__(16 * L) __attribute__((amdgpu_waves_per_eu(4))) voi
         for (int n2 = 0; n2 < 16; ++n2) v[n2] = src[o0 + os * (uint32_t)n2];
         dft<16, -1>(v);
 #pragma unroll
-        for (int q = 0; q < 16; ++q) stage[(q * C + c) * SS + n1 + n1 / 16] = v[q];
+        for (int q = 0; q < 16; ++q) stage[(q * C + c) * SS + n1 + n1 / PBS] = v[q];
         __syncthreads();
-        const float2* const sp = stage + (rr * C + cr) * SS + 17 * pb;
-        float2 s16[16];
+        float2* const dst0 = xh + img * (int64_t)nk * my + ky0;
 #pragma unroll
-        for (int t = 0; t < 16; ++t) s16[t] = sp[t];
-        float2* const dst = xh + img * (int64_t)nk * my + ky0 + cr;
-        const bool store = pb == 0 && ky0 + cr < my;
+        for (int h = 0; h < NRD; ++h) {
+            int pb, cr, rr;
+            role(h, pb, cr, rr);
+            const float2* const sp = stage + (rr * C + cr) * SS + (PBS + 1) * pb;
+            float2 sv[PBS];
 #pragma unroll
-        for (int i = 0; i < MPR; ++i) {
-            if (i < nm) {                                // uniform
-                float2 u[8];
+            for (int t = 0; t < PBS; ++t) sv[t] = sp[t];
+            const bool store = pb == 0 && ky0 + cr < my;
 #pragma unroll
-                for (int t = 0; t < 8; ++t) u[t] = cfma(s16[2 * t], wk[i], s16[2 * t + 1]);
-                const float2 w2 = cmul(wk[i], wk[i]);
-                const float2 w4 = cmul(w2, w2);
-                const float2 w8 = cmul(w4, w4);
+            for (int i = 0; i < MPR; ++i) {
+                if (i < nm) {                            // uniform
+                    float2 u[PBS / 2];
+                    float2 w = wk[h][i];
 #pragma unroll
-                for (int t = 0; t < 4; ++t) u[t] = cfma(u[2 * t], w2, u[2 * t + 1]);
+                    for (int t = 0; t < PBS / 2; ++t) u[t] = cfma(sv[2 * t], w, sv[2 * t + 1]);
 #pragma unroll
-                for (int t = 0; t < 2; ++t) u[t] = cfma(u[2 * t], w4, u[2 * t + 1]);
-                float2 acc = cmul(vk[i], cfma(u[0], w8, u[1]));
-                if constexpr (PB == 2) {
-                    acc.x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(acc.x), 0xB1, 0xF, 0xF, false));
-                    acc.y += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(acc.y), 0xB1, 0xF, 0xF, false));
+                    for (int len = PBS / 2; len > 1; len /= 2) {
+                        w = cmul(w, w);
+#pragma unroll
+                        for (int t = 0; t < len / 2; ++t) u[t] = cfma(u[2 * t], w, u[2 * t + 1]);
+                    }
+                    float2 acc;
+                    if constexpr (PB == 2) {
+                        acc = cmul(vk[h][i], u[0]);
+                        acc.x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(acc.x), 0xB1, 0xF, 0xF, false));
+                        acc.y += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(acc.y), 0xB1, 0xF, 0xF, false));
+                    } else {
+                        acc = cscale(u[0], scale);
+                    }
+                    if (store) dst0[(int64_t)(rr + 16 * i) * my + cr] = acc;
+                    // one mode at a time: the next mode's tree starts from a
+                    // factor defined after this mode's result, so that the
+                    // trees do not all run side by side in registers
+                    if (i + 1 < MPR)
+                        asm volatile("" : "+v"(wk[h][i + 1].x), "+v"(wk[h][i + 1].y) : "v"(acc.x), "v"(acc.y));
                 }
-                if (store) dst[(int64_t)(rr + 16 * i) * my] = acc;
-                // one mode at a time: the next mode's tree starts from a
-                // factor defined after this mode's result, so that the trees
-                // do not all run side by side in registers
-                if (i + 1 < MPR) asm volatile("" : "+v"(wk[i + 1].x), "+v"(wk[i + 1].y) : "v"(acc.x), "v"(acc.y));
             }
         }
         __syncthreads();                                 // the stage is read before the next block overwrites it
@@ -294,21 +330,22 @@ template <int L>
 __global__ __launch_bounds__(16 * L) void k_cols_inv_short(const float2* __restrict__ yh, float2* __restrict__ r,
                                                           int64_t nitems, int nkb, int mx, int my,
                                                           const float2* __restrict__ tw) {
-    static_assert(L == 16 || L == 32, "short columns: 256 or 512 rows");
+    static_assert(L == 4 || L == 8 || L == 16 || L == 32, "short columns: 64 to 512 rows");
     constexpr int H = 16 * L, C = kShortC, NT = 16 * L;
+    constexpr int KS = short_ks(H);
     // 16-byte aligned: the mode pairs below are read as one 16-byte word
-    __shared__ __align__(16) float2 T[L * kShortKS];   // [n1][q]: W^{-n1 k_q}
-    __shared__ __align__(16) float2 xs[C * kShortKS];  // [c][q]: the block's kept modes
+    __shared__ __align__(16) float2 T[L * KS];   // [n1][q]: W^{-n1 k_q}
+    __shared__ __align__(16) float2 xs[C * KS];  // [c][q]: the block's kept modes
     const int tid = threadIdx.x;
     const int c = tid % C, n1 = tid / C;
     const int nk = 2 * mx;
     for (int e = tid; e < L * nk; e += NT) {
         const int n = e / nk, q = e % nk;
         const int k = q < mx ? q : H - nk + q;
-        T[n * kShortKS + q] = conj2(tw[((int64_t)n * k * (kNMax / H)) & (kNMax - 1)]);
+        T[n * KS + q] = conj2(tw[((int64_t)n * k * (kNMax / H)) & (kNMax - 1)]);
     }
-    const float2* const tp = T + n1 * kShortKS;
-    const float2* const xp = xs + c * kShortKS;
+    const float2* const tp = T + n1 * KS;
+    const float2* const xp = xs + c * KS;
     for (int64_t item = blockIdx.x; item < nitems; item += gridDim.x) {
         const int64_t img = item / nkb;
         const int ky0 = (int)(item % nkb) * C;
@@ -316,14 +353,14 @@ __global__ __launch_bounds__(16 * L) void k_cols_inv_short(const float2* __restr
         // the block's kept modes (column fastest: whole runs of each mode row)
         for (int e = tid; e < nk * C; e += NT) {
             const int q = e / C, cc = e % C;
-            xs[cc * kShortKS + q] = ky0 + cc < my ? src[(int64_t)q * my + cc] : make_float2(0.0f, 0.0f);
+            xs[cc * KS + q] = ky0 + cc < my ? src[(int64_t)q * my + cc] : make_float2(0.0f, 0.0f);
         }
         __syncthreads();
         float2 v[16];
 #pragma unroll
         for (int j = 0; j < 16; ++j) v[j] = make_float2(0.0f, 0.0f);
         // modes in chunks of 16 (q mod 16 static), two per LDS read
-        static_for<0, kMaxKept / 16>([&](auto ch) {
+        static_for<0, short_kept(H) / 16>([&](auto ch) {
             if (16 * ch < nk) {                          // uniform
                 static_for<0, 8>([&](auto p) {
                     constexpr int q = 16 * ch + 2 * p;
@@ -347,8 +384,8 @@ __global__ __launch_bounds__(16 * L) void k_cols_inv_short(const float2* __restr
 
 // persistent grid: as many workgroups as fit on the device at once, at
 // most one per work item
-template <typename K>
-hipError_t short_grid(K kernel, int threads, int64_t nitems, unsigned* g) {
+template <typename K, typename... A>
+hipError_t launch_cols_short(K kernel, int threads, int64_t nitems, hipStream_t s, A... args) {
     int dev = 0, cus = 0, per_cu = 0;
     if (hipGetDevice(&dev) != hipSuccess) return hipErrorInvalidDevice;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
@@ -356,18 +393,21 @@ hipError_t short_grid(K kernel, int threads, int64_t nitems, unsigned* g) {
     if (e != hipSuccess) return e;
     int64_t n = (int64_t)cus * (per_cu > 0 ? per_cu : 1);
     if (n > nitems) n = nitems;
-    *g = (unsigned)n;
-    return hipSuccess;
+    return launch_kernel(kernel, dim3((unsigned)n), dim3(threads), 0, s, args...);
 }
 
-bool cols_short_supported(int log2H, int mx) { return (log2H == 8 || log2H == 9) && (2 * mx) % 16 == 0; }
+bool cols_short_supported(int log2H, int mx) {
+    return log2H >= 6 && log2H <= 9 && (2 * mx) % 16 == 0 && 2 * mx <= short_kept(1 << log2H);
+}
 
 }  // namespace
 
 bool cols_pruned_supported(int log2H, int mx, int my) {
+    if (mx < 1 || my < 1 || my > 64) return false;
+    if (cols_short_supported(log2H, mx)) return true;
     if (log2H < 8 || log2H > 11) return false;
     const int Q = 1 << (log2H - 6);
-    return mx >= 1 && 2 * mx <= kMaxKept && (2 * mx) % Q == 0 && my >= 1 && my <= 64;
+    return 2 * mx <= kMaxKept && (2 * mx) % Q == 0;
 }
 
 hipError_t launch_cols_fwd_pruned(const float2* r, float2* xh, int64_t nimg, int log2H, int mx, int my, float scale,
@@ -376,15 +416,12 @@ hipError_t launch_cols_fwd_pruned(const float2* r, float2* xh, int64_t nimg, int
     if (cols_short_supported(log2H, mx)) {
         const int nkb = (my + kShortC - 1) / kShortC;
         const int64_t ni = nimg * nkb;
-        unsigned g = 0;
-        if (log2H == 8) {
-            const hipError_t e = short_grid(k_cols_fwd_short<16>, 256, ni, &g);
-            if (e != hipSuccess) return e;
-            return launch_kernel(k_cols_fwd_short<16>, dim3(g), dim3(256), 0, s, r, xh, ni, nkb, mx, my, scale, tw);
+        switch (log2H) {
+            case 6: return launch_cols_short(k_cols_fwd_short<4>, 64, ni, s, r, xh, ni, nkb, mx, my, scale, tw);
+            case 7: return launch_cols_short(k_cols_fwd_short<8>, 128, ni, s, r, xh, ni, nkb, mx, my, scale, tw);
+            case 8: return launch_cols_short(k_cols_fwd_short<16>, 256, ni, s, r, xh, ni, nkb, mx, my, scale, tw);
+            default: return launch_cols_short(k_cols_fwd_short<32>, 512, ni, s, r, xh, ni, nkb, mx, my, scale, tw);
         }
-        const hipError_t e = short_grid(k_cols_fwd_short<32>, 512, ni, &g);
-        if (e != hipSuccess) return e;
-        return launch_kernel(k_cols_fwd_short<32>, dim3(g), dim3(512), 0, s, r, xh, ni, nkb, mx, my, scale, tw);
     }
     const int nkb = (my + kColC - 1) / kColC;
     const int64_t nb = nimg * nkb;
@@ -404,15 +441,12 @@ hipError_t launch_cols_inv_pruned(const float2* yh, float2* r, int64_t nimg, int
     if (cols_short_supported(log2H, mx)) {
         const int nkb = (my + kShortC - 1) / kShortC;
         const int64_t ni = nimg * nkb;
-        unsigned g = 0;
-        if (log2H == 8) {
-            const hipError_t e = short_grid(k_cols_inv_short<16>, 256, ni, &g);
-            if (e != hipSuccess) return e;
-            return launch_kernel(k_cols_inv_short<16>, dim3(g), dim3(256), 0, s, yh, r, ni, nkb, mx, my, tw);
+        switch (log2H) {
+            case 6: return launch_cols_short(k_cols_inv_short<4>, 64, ni, s, yh, r, ni, nkb, mx, my, tw);
+            case 7: return launch_cols_short(k_cols_inv_short<8>, 128, ni, s, yh, r, ni, nkb, mx, my, tw);
+            case 8: return launch_cols_short(k_cols_inv_short<16>, 256, ni, s, yh, r, ni, nkb, mx, my, tw);
+            default: return launch_cols_short(k_cols_inv_short<32>, 512, ni, s, yh, r, ni, nkb, mx, my, tw);
         }
-        const hipError_t e = short_grid(k_cols_inv_short<32>, 512, ni, &g);
-        if (e != hipSuccess) return e;
-        return launch_kernel(k_cols_inv_short<32>, dim3(g), dim3(512), 0, s, yh, r, ni, nkb, mx, my, tw);
     }
     const int nkb = (my + kColC - 1) / kColC;
     const int64_t nb = nimg * nkb;

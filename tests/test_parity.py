@@ -161,6 +161,10 @@ EDGE_2D = [
     (2, 3, 4, 512, 64, 16, 32),     # 64-point short rows, every bin below the Nyquist bin
     (1, 2, 3, 256, 64, 8, 33),      # 64-point rows keeping the Nyquist bin: generic rows
     (2, 2, 3, 256, 128, 16, 64),    # 128-point short rows, every bin up to 64
+    (2, 3, 4, 128, 256, 16, 20),    # 128-row short columns (8 phases per thread), ragged column block
+    (2, 3, 4, 64, 512, 8, 12),      # 64-row short columns (4 phases per thread)
+    (1, 2, 3, 128, 512, 32, 64),    # 128-row short columns, four modes per residue
+    (1, 2, 2, 128, 256, 64, 8),     # 128-row short columns, every kx kept
     (4, 160, 160, 256, 128, 8, 40), # 256-row short columns: more column blocks than workgroups, ragged last block
     (3, 100, 100, 512, 128, 8, 40), # 512-row short columns: more column blocks than workgroups
     (5, 8, 8, 32, 32, 16, 16),      # one-kernel small path: most channels (two rounds), every kx kept
