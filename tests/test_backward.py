@@ -75,7 +75,9 @@ BACKWARD_2D = [
     (2, 8, 16, 64, 64, 16, 16),     # one-row-per-thread kernels, matrix-core mix both ways
     (17, 12, 18, 128, 128, 7, 13),  # ragged batch and channels
     (1, 2, 3, 256, 256, 9, 11),     # staged: 256-point short rows, generic columns (odd mx)
-    (1, 2, 3, 256, 256, 8, 16),     # staged: 256-point short rows, pruned columns
+    (1, 2, 3, 256, 256, 8, 16),     # staged: 256-point short rows, 256-row short columns
+    (1, 2, 3, 256, 128, 16, 24),    # staged: 128-point short rows, 256-row short columns
+    (1, 2, 2, 64, 512, 8, 12),      # staged: 512-point short rows, 64-row short columns
     (1, 2, 3, 16, 1024, 5, 50),     # pruned long rows
     (1, 2, 2, 1024, 16, 8, 9),      # pruned columns
     (9, 16, 24, 64, 64, 8, 8),      # weight-gradient tiles of 16 x 32 channels; adjoint mix, ragged channel chunk
@@ -97,7 +99,8 @@ BACKWARD_1D = [
     (5, 3, 2, 512, 64),             # 512-point short rows
     (2, 16, 32, 4096, 64),          # longest rows, matrix-core mix both ways
     (37, 20, 40, 256, 13),          # weight gradient: batch split in two, odd chunk counts, modes not a multiple of 8
-    (300, 8, 8, 128, 16),           # weight gradient: 19 uneven batch splits, ragged last chunk
+    (300, 8, 8, 128, 16),           # weight gradient: 19 uneven batch splits, ragged last chunk; 128-point short rows
+    (7, 3, 4, 64, 20),              # 64-point short rows, ragged last group of 16 rows
     (4, 3, 2, 1215, 40),            # mixed-radix odd length (3^5 5)
 ]
 

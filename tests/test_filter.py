@@ -76,6 +76,7 @@ FILTER_2D = [
     (3, 5, 32, 16, 3, 9),           # small-grid kernels, odd channels, tiled padding modes
     (2, 7, 64, 64, 5, 7),           # one row per thread, ragged mode tile
     (1, 3, 256, 256, 9, 11),        # staged: 256-point short rows, generic columns (odd mx)
+    (1, 3, 256, 64, 8, 12),         # staged: 64-point short rows, 256-row short columns
     (1, 2, 16, 1024, 5, 50),        # pruned long rows
     (1, 2, 1024, 16, 8, 9),         # pruned columns
     (2, 3, 60, 35, 12, 10),         # mixed-radix lengths
@@ -92,6 +93,7 @@ FILTER_1D = [
     # B, C, N, modes
     (3, 2, 16, 9),                  # every bin kept, odd mode count
     (5, 3, 512, 64),                # 512-point short rows
+    (3, 2, 128, 40),                # 128-point short rows
     (2, 4, 4096, 33),               # pruned rows, odd mode count
 ]
 
