@@ -448,15 +448,39 @@ __global__ __launch_bounds__(kPrunedThreads) __attribute__((amdgpu_waves_per_eu(
     const int rw = lane / L, n1 = lane % L;
     // residue factors W^{n1 r} (r <= Q/2) times scale (X[0] is halved on load,
     // so every bin counts twice and 2 (scale / 2) = scale), and W^{16 n1 j} =
-    // W_L^{n1 j}; W^{n1 r} for r > Q/2 is W_L^{n1} conj(W^{n1 (Q - r)})
-    float2 tr[NZ + 1], pj[4];
+    // W_L^{n1 j}; W^{n1 r} for r > Q/2 is W_L^{n1} conj(W^{n1 (Q - r)}).
+    // Without the epilogue they sit in a per-workgroup LDS table (a row of
+    // TF factors per phase n1), which frees their registers for more waves;
+    // with it they stay in registers (the table measured slower there).
+    constexpr int TF = NZ + 5;                // odd: the phases' rows fall on distinct bank pairs
+    __shared__ float2 ftab[EPI ? 1 : L * TF];
+    float2 tr[EPI ? NZ + 1 : 1], pj[EPI ? 4 : 1];
+    if constexpr (EPI) {
 #pragma unroll
-    for (int r = 0; r <= NZ; ++r) tr[r] = cscale(tw[(n1 * r * (kNMax / N)) & (kNMax - 1)], scale);
+        for (int r = 0; r <= NZ; ++r) tr[r] = cscale(tw[(n1 * r * (kNMax / N)) & (kNMax - 1)], scale);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) pj[j] = tw[(16 * n1 * j * (kNMax / N)) & (kNMax - 1)];   // pj[1] is needed for any NJ
+        for (int j = 0; j < 4; ++j) pj[j] = tw[(16 * n1 * j * (kNMax / N)) & (kNMax - 1)];   // pj[1] is needed for any NJ
+    } else {
+        // entry t of phase n: W^{n t} scale for t <= Q/2, W_L^{n (t - Q/2)} above
+        for (int e = threadIdx.x; e < L * TF; e += kPrunedThreads) {
+            const int nn = e / TF, t = e % TF;
+            ftab[e] = t <= NZ ? cscale(tw[(nn * t * (kNMax / N)) & (kNMax - 1)], scale)
+                              : tw[(16 * nn * (t - NZ) * (kNMax / N)) & (kNMax - 1)];
+        }
+        __syncthreads();
+    }
+    const float2* const ft = ftab + (EPI ? 0 : n1 * TF);
+    auto trf = [&](int r) __attribute__((always_inline)) {
+        if constexpr (EPI) return tr[r];
+        else return ft[r];
+    };
+    auto pjf = [&](int j) __attribute__((always_inline)) {
+        if constexpr (EPI) return pj[j];
+        else return ft[NZ + j];
+    };
     auto res = [&](auto r) __attribute__((always_inline)) {
-        if constexpr (r <= NZ) return tr[r];
-        else return cmul(pj[1], conj2(tr[r <= NZ ? 0 : Q - r]));
+        if constexpr (r <= NZ) return trf(r);
+        else return cmul(pjf(1), conj2(trf(r <= NZ ? 0 : Q - r)));
     };
     const int64_t nwaves = (int64_t)gridDim.x * kPrunedWaves;
     // The bins 0 .. BW - 1 (BW = 16 NJ) of the wave's rows starting at r0,
@@ -481,10 +505,12 @@ __global__ __launch_bounds__(kPrunedThreads) __attribute__((amdgpu_waves_per_eu(
     float2 vn[NL];
     load_bins(first < nrows ? first : 0, vn);
     for (int64_t row0 = first; row0 < nrows; row0 += nwaves * RPW) {
+        if constexpr (EPI) {
 #pragma unroll
-        for (int r = 0; r <= NZ; ++r) asm volatile("" : "+v"(tr[r].x), "+v"(tr[r].y));
+            for (int r = 0; r <= NZ; ++r) asm volatile("" : "+v"(tr[r].x), "+v"(tr[r].y));
 #pragma unroll
-        for (int j = 0; j < 4; ++j) asm volatile("" : "+v"(pj[j].x), "+v"(pj[j].y));
+            for (int j = 0; j < 4; ++j) asm volatile("" : "+v"(pj[j].x), "+v"(pj[j].y));
+        }
         // this group's bins to LDS (the DC bin halved, its imaginary part
         // dropped); the next group's loaded meanwhile
 #pragma unroll
@@ -507,7 +533,7 @@ __global__ __launch_bounds__(kPrunedThreads) __attribute__((amdgpu_waves_per_eu(
                 for (int j = 0; j < NJ; ++j) nxt[j] = xr[r + 1 + Q * j];
             }
             float2 acc = cur[0];
-            static_for<1, NJ>([&](auto j) { acc = cfma(acc, cur[j], conj2(pj[j])); });
+            static_for<1, NJ>([&](auto j) { acc = cfma(acc, cur[j], conj2(pjf(j))); });
             V[r] = cmul(acc, conj2(res(r)));
             asm volatile("" : "+v"(V[r].x), "+v"(V[r].y) : : "memory");
 #pragma unroll
