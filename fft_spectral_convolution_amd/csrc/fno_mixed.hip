@@ -297,16 +297,19 @@ __global__ __launch_bounds__(kMrThreads) void k_rows_fwd_mr(const float* __restr
     const float2* res = buf[0];
     if constexpr (INP) fft_rows_mr_inplace<-1, NE>(buf[0], prows, W, p, tws, tid);
     else res = fft_rows_mr<-1>(buf[0], buf[INP ? 0 : 1], prows, W, p, tws, tid);
+    // the block's 2 P rows of bins from a uniform base, 32-bit offsets
+    // (2 P y_ld < 2^31: checked on the host)
+    float2* const yb = y + 2 * pair0 * (int64_t)y_ld;
+    const int64_t rows_left = nrows - 2 * pair0;
+    const float hs = 0.5f * scale;
     for (int e = tid; e < prows * my; e += kMrThreads) {
         const int pr = qdiv(e, inv_my);
         const int k = e - pr * my;
         const float2 zk = res[pr * W + k];
         const float2 zm = res[pr * W + (k == 0 ? 0 : W - k)];
-        const float2 a = make_float2(0.5f * (zk.x + zm.x), 0.5f * (zk.y - zm.y));
-        const float2 b = make_float2(0.5f * (zk.y + zm.y), -0.5f * (zk.x - zm.x));
-        const int64_t ra = 2 * (pair0 + pr);
-        y[ra * y_ld + k] = cscale(a, scale);
-        if (ra + 1 < nrows) y[(ra + 1) * y_ld + k] = cscale(b, scale);
+        const uint32_t o = (uint32_t)(2 * pr) * (uint32_t)y_ld + (uint32_t)k;
+        yb[o] = make_float2(hs * (zk.x + zm.x), hs * (zk.y - zm.y));
+        if (2 * pr + 1 < rows_left) yb[o + (uint32_t)y_ld] = make_float2(hs * (zk.y + zm.y), hs * (zm.x - zk.x));
     }
 }
 
@@ -334,11 +337,12 @@ __global__ __launch_bounds__(kMrThreads) void k_cols_fwd_mr(const float2* __rest
     const int ncol = min(kb, my - ky0);
     const float inv_ncol = 1.0f / (float)ncol;
     const int ld = H | 1;           // odd pitch: the column-wise accesses below hit distinct banks
-    const float2* src = r + img * H * my;
+    // the image's rows from a uniform base, 32-bit offsets (H my < 2^24)
+    const float2* src = r + img * H * my + ky0;
     for (int e = tid; e < ncol * H; e += kMrThreads) {
         const int h = qdiv(e, inv_ncol);
         const int c = e - h * ncol;
-        buf[0][c * ld + h] = src[(int64_t)h * my + ky0 + c];
+        buf[0][c * ld + h] = src[(uint32_t)(h * my + c)];
     }
     __syncthreads();
     const float2* res = fft_rows_mr<-1>(buf[0], buf[1], ncol, ld, p, tws, tid);
@@ -386,11 +390,11 @@ __global__ __launch_bounds__(kMrThreads) void k_cols_inv_mr(const float2* __rest
     }
     __syncthreads();
     const float2* res = fft_rows_mr<1>(buf[0], buf[1], ncol, ld, p, tws, tid);
-    float2* dst = r + img * H * my;
+    float2* dst = r + img * H * my + ky0;
     for (int e = tid; e < ncol * H; e += kMrThreads) {
         const int h = qdiv(e, inv_ncol);
         const int c = e - h * ncol;
-        dst[(int64_t)h * my + ky0 + c] = res[c * ld + h];
+        dst[(uint32_t)(h * my + c)] = res[c * ld + h];
     }
 }
 
@@ -417,15 +421,19 @@ __global__ __launch_bounds__(kMrThreads) void k_rows_inv_mr(const float2* __rest
     const int64_t npairs = (nrows + 1) / 2;
     const int64_t pair0 = (int64_t)blockIdx.x * P;
     const int prows = (int)(npairs - pair0 < P ? npairs - pair0 : P);
+    // the block's 2 P rows of bins from a uniform base, 32-bit offsets
+    // (2 P y_ld < 2^31: checked on the host)
+    const float2* const ybase = y + 2 * pair0 * (int64_t)y_ld;
+    const int64_t rows_left = nrows - 2 * pair0;
     for (int e = tid; e < prows * W; e += kMrThreads) {
         const int pr = qdiv(e, inv_w);
         const int k = e - pr * W;
         const int kk = (2 * k <= W) ? k : W - k;
-        const int64_t ra = 2 * (pair0 + pr);
         float2 z = make_float2(0.0f, 0.0f);
         if (kk < my) {
-            const float2 ya = y[ra * y_ld + kk];
-            const float2 yb = (ra + 1 < nrows) ? y[(ra + 1) * y_ld + kk] : make_float2(0.0f, 0.0f);
+            const uint32_t o = (uint32_t)(2 * pr) * (uint32_t)y_ld + (uint32_t)kk;
+            const float2 ya = ybase[o];
+            const float2 yb = (2 * pr + 1 < rows_left) ? ybase[o + (uint32_t)y_ld] : make_float2(0.0f, 0.0f);
             if (kk == 0 || 2 * kk == W) z = make_float2(ya.x, yb.x);
             else if (k == kk) z = make_float2(ya.x - yb.y, ya.y + yb.x);
             else z = make_float2(ya.x + yb.y, yb.x - ya.y);
@@ -455,10 +463,14 @@ __global__ __launch_bounds__(kMrThreads) void k_rows_inv_mr(const float2* __rest
         }
         __syncthreads();
     }
+    // uncropped output: the block's 2 P rows from a uniform base, 32-bit
+    // offsets (2 P W <= 2 NE)
+    float* const obase = out + 2 * pair0 * (int64_t)W;
     for (int e = tid; e < prows * W; e += kMrThreads) {
         const int pr = qdiv(e, inv_w);
         const int n = e - pr * W;
         const int64_t ra = 2 * (pair0 + pr);
+        const uint32_t o = (uint32_t)(2 * pr * W + n);
         const float2 z = res[e];
         if (crop) {
             if (n < win.w0 || n >= win.w0 + win.w) continue;
@@ -471,14 +483,14 @@ __global__ __launch_bounds__(kMrThreads) void k_rows_inv_mr(const float2* __rest
             const __amdgpu_buffer_rsrc_t rb =
                 make_rsrc(epi.branch ? epi.branch + 2 * pair0 * W : nullptr,
                           epi.branch ? (uint32_t)((nrows - 2 * pair0 < 2 * P ? nrows - 2 * pair0 : 2 * P) * W * 4) : 0u);
-            const uint32_t off = (uint32_t)((ra - 2 * pair0) * W + n) * 4u;
-            nt_store(&out[ra * W + n], epi_apply(epi, z.x * scale, epi_bias(epi, (uint32_t)ra), buffer_load_f1(rb, off, 0)));
+            const uint32_t off = o * 4u;
+            nt_store(&obase[o], epi_apply(epi, z.x * scale, epi_bias(epi, (uint32_t)ra), buffer_load_f1(rb, off, 0)));
             if (ra + 1 < nrows)
-                nt_store(&out[(ra + 1) * W + n], epi_apply(epi, z.y * scale, epi_bias(epi, (uint32_t)(ra + 1)),
-                                                           buffer_load_f1(rb, off + (uint32_t)W * 4u, 0)));
+                nt_store(&obase[o + (uint32_t)W], epi_apply(epi, z.y * scale, epi_bias(epi, (uint32_t)(ra + 1)),
+                                                            buffer_load_f1(rb, off + (uint32_t)W * 4u, 0)));
         } else {
-            nt_store(&out[ra * W + n], z.x * scale);
-            if (ra + 1 < nrows) nt_store(&out[(ra + 1) * W + n], z.y * scale);
+            nt_store(&obase[o], z.x * scale);
+            if (ra + 1 < nrows) nt_store(&obase[o + (uint32_t)W], z.y * scale);
         }
     }
 }
@@ -565,7 +577,7 @@ hipError_t launch_rows_fwd_mr(const float* x, float2* y, int64_t nrows, int W, i
     const bool lng = W > kLdsElems;
     const int P = (lng ? kMrLongRow : kLdsElems) / W;
     const int64_t nb = ((nrows + 1) / 2 + P - 1) / P;
-    if (nb >= INT32_MAX) return hipErrorInvalidValue;
+    if (nb >= INT32_MAX || (int64_t)2 * P * y_ld >= INT32_MAX) return hipErrorInvalidValue;
     const RowWindow win = window ? *window : RowWindow{1, 1, W, 0, 0};
     if (win.ph < 1 || win.h < 1 || win.h > win.ph || win.w < 1 || win.w > W || nrows % win.ph ||
         (window && nrows >= INT32_MAX))
@@ -637,7 +649,7 @@ hipError_t launch_rows_inv_mr(const float2* y, float* out, int64_t nrows, int W,
     if (e != hipSuccess) return e;
     const int P = (lng ? kMrLongRow : kLdsElems) / W;
     const int64_t nb = ((nrows + 1) / 2 + P - 1) / P;
-    if (nb >= INT32_MAX) return hipErrorInvalidValue;
+    if (nb >= INT32_MAX || (int64_t)2 * P * y_ld >= INT32_MAX) return hipErrorInvalidValue;
     const RowWindow win = window ? *window : RowWindow{1, 1, W, 0, 0};
     if (win.ph < 1 || win.h < 1 || win.h0 < 0 || win.h0 + win.h > win.ph || win.w < 1 || win.w0 < 0 ||
         win.w0 + win.w > W || nrows % win.ph || (window && (epi.on || nrows >= INT32_MAX)))
