@@ -333,8 +333,9 @@ __global__ __launch_bounds__(kPrunedThreads) __attribute__((amdgpu_waves_per_eu(
 //   X[k] = sum_{n1 < L} W^{n1 k} Y_n1[k mod 16],
 // formed by one reading lane per (row, bin, block of up to 16 phases) with
 // the binary tree of the long rows (factors W^k, W^2k, W^4k, ...), the two
-// blocks of a 512-point row added across neighbouring lanes.  The inverse mirrors the long-row
-// one with 16 residues, V[r] = conj(W^{n1 r}) sum_j X'[r + 16 j] conj(W_L^{n1 j}),
+// blocks of a 512-point row added across neighbouring lanes.  The inverse
+// mirrors the long-row one with 16 residues,
+//   V[r] = conj(W^{n1 r}) sum_j X'[r + 16 j] conj(W_L^{n1 j}),
 // and carries the same fused epilogue.
 template <int L>
 __global__ __launch_bounds__(kPrunedThreads) __attribute__((amdgpu_waves_per_eu(4))) void k_rows_fwd_short(
@@ -521,8 +522,8 @@ __global__ __launch_bounds__(kPrunedThreads) __attribute__((amdgpu_waves_per_eu(
         wave_lds_sync();
         const float2* const xr = xrow + rw * 64;
         // V[r] = conj(W^{n1 r}) sum_j X'[r + Q j] conj(W_L^{n1 j}) for every
-        // residue, one at a time with the next residue's four bins read
-        // ahead: left alone the compiler issues all 64 reads at once and
+        // residue, one at a time with the next residue's NJ bins read
+        // ahead: left alone the compiler issues all 16 NJ reads at once and
         // holds them in registers
         float2 V[Q], cur[NJ], nxt[NJ];
 #pragma unroll
