@@ -32,6 +32,7 @@
 // kernels further down, several rows per wave.
 #include "fno_device.hpp"
 #include "fno_internal.hpp"
+#include "fno_realbins.hpp"
 
 namespace fno {
 namespace {
@@ -96,32 +97,6 @@ struct LaneTwiddles {
     }
 };
 
-// Twice bin K (K <= Q/2) of the DFT of a real length-Q sequence s, from its
-// packed transform Z = DFT_{Q/2}(s[2m] + i s[2m+1]):
-//   2 Y[K] = (Z[K] + conj Z[-K]) - i W_Q^K (Z[K] - conj Z[-K]).
-// The factor 2 is taken out with the output scale.
-template <int Q, int K>
-__device__ __forceinline__ float2 real_bin2(const float2 (&z)[Q / 2]) {
-    constexpr int NZ = Q / 2;
-    const float2 zk = z[K % NZ];
-    const float2 zm = z[(NZ - K % NZ) % NZ];
-    const float2 e = make_float2(zk.x + zm.x, zk.y - zm.y);
-    const float2 o = make_float2(zk.y + zm.y, zm.x - zk.x);
-    return wfma<-1, Q, K>(e, o);
-}
-
-// Packed C2R bin K (K < Q/2) from a Hermitian half spectrum H[0..Q/2]:
-//   s[2m] + i s[2m+1] = IDFT_{Q/2}(Zp)[m],
-//   Zp[K] = (H[K] + conj H[Q/2-K]) + i W_Q^{-K} (H[K] - conj H[Q/2-K]).
-template <int Q, int K>
-__device__ __forceinline__ float2 packed_bin(const float2 (&H)[Q / 2 + 1]) {
-    constexpr int NZ = Q / 2;
-    const float2 hk = H[K], hm = H[NZ - K];
-    const float2 a = make_float2(hk.x + hm.x, hk.y - hm.y);
-    const float2 b = make_float2(hk.x - hm.x, hk.y + hm.y);
-    // i W_Q^{-K} b = W_Q^{-K} (i b)
-    return wfma<1, Q, K>(a, make_float2(-b.y, b.x));
-}
 
 template <int Q>
 __global__ __launch_bounds__(kPrunedThreads) __attribute__((amdgpu_waves_per_eu(Q == 64 ? 2 : 4))) void k_rows_fwd_pruned(

@@ -152,9 +152,13 @@ def test_stages_1d(name):
 EDGE_2D = [
     # B, Cin, Cout, H, W, mx, my
     (300, 2, 3, 32, 32, 8, 8),      # one-kernel small path: more batch items than CUs
-    (2, 4, 4, 256, 256, 32, 32),    # 256-point short rows, 256-row short columns
-    (2, 3, 5, 256, 512, 16, 17),    # 512-point short rows, 256-row short columns, one column in the last block
+    (2, 4, 4, 256, 256, 32, 32),    # one-kernel 256 x 256 forward and inverse, two column blocks
+    (2, 3, 5, 256, 512, 16, 17),    # one-kernel 256 x 512 transforms, one column in the last block
     (2, 3, 2, 512, 256, 64, 64),    # 256-point short rows, every bin up to 64; 512-row short columns, 128 kept kx
+    (3, 2, 3, 256, 256, 64, 16),    # one-kernel 256 x 256 transforms: every kept kx of 128, one column block
+    (2, 3, 2, 256, 512, 8, 32),     # one-kernel 256 x 512 transforms: two column blocks
+    (8, 64, 4, 256, 256, 8, 8),     # one-kernel 256 x 256 forward: more images than workgroups
+    (4, 4, 96, 256, 256, 8, 20),    # one-kernel 256 x 256 inverse: more images than workgroups, ragged last block
     (1, 2, 3, 128, 256, 9, 100),    # 256-point rows with more than 64 bins: generic rows and columns
     (1, 2, 3, 512, 128, 24, 5),     # 512-row short columns, one partial block of 16 columns
     (2, 3, 4, 256, 64, 8, 20),      # 64-point short rows (16 rows per wave), bins in two groups of 16
