@@ -313,11 +313,25 @@ bool small_path(const Shape2d& s) {
     return is_pow2(s.H) && is_pow2(s.W) && small2d_supported(s.log2H, s.log2W, s.my);
 }
 
-// Staged (unfused) transforms: rows and columns as separate kernels, the row
-// spectrum R (or R') in workspace; spectra in the canonical layout.
+// 256-row grids of 256 or 512 columns (my <= 32, 2 mx a multiple of 16):
+// the forward or inverse transform of each image in one kernel, the row
+// spectrum in LDS (same canonical spectra as the staged kernels).
+bool short2d_path(const Shape2d& s) {
+    return is_pow2(s.H) && is_pow2(s.W) && short2d_supported(s.log2H, s.log2W, s.mx, s.my);
+}
+
+// Staged transforms: rows and columns as separate kernels, the row spectrum R
+// (or R') in workspace; spectra in the canonical layout.  fuse: the
+// one-kernel 256-row transforms where they apply (not in the unfused
+// ablation).
 int run_forward2d_staged(const Shape2d& s, int64_t C, const float* x, float2* xh, float2* r, const float2* tw,
-                         hipStream_t st) {
+                         hipStream_t st, bool fuse = true) {
     const float scale = (float)(1.0 / std::sqrt((double)s.H * (double)s.W));
+    if (fuse && short2d_path(s)) {
+        rec_kernel("fwd2d", st);
+        const hipError_t e = launch_fwd2d_short(x, xh, s.B * C, s.log2H, s.log2W, s.mx, s.my, scale, tw, st);
+        return e == hipSuccess ? FNO_OK : hip_fail(e);
+    }
     rec_kernel("rows_fwd", st);
     hipError_t e = rows_fwd_n(x, r, s.B * C * s.H, s.W, s.my, s.my, 1.0f, tw, st);
     if (e != hipSuccess) return hip_fail(e);
@@ -329,8 +343,16 @@ int run_forward2d_staged(const Shape2d& s, int64_t C, const float* x, float2* xh
 
 // epi: the fused output epilogue (its rows_per_chan is set here)
 int run_inverse2d_staged(const Shape2d& s, int64_t C, const float2* yh, float* out, float2* r, const float2* tw,
-                         hipStream_t st, const Epilogue& epi = Epilogue{}) {
+                         hipStream_t st, const Epilogue& epi = Epilogue{}, bool fuse = true) {
     const float scale = (float)(1.0 / std::sqrt((double)s.H * (double)s.W));
+    if (fuse && short2d_path(s)) {
+        rec_kernel(epi.on ? "inv2d_gelu" : "inv2d", st);
+        Epilogue ep = epi;
+        ep.rows_per_chan = (uint32_t)s.H;
+        const hipError_t e =
+            launch_inv2d_short(yh, out, s.B * C, s.log2H, s.log2W, s.mx, s.my, scale, tw, st, ep);
+        return e == hipSuccess ? FNO_OK : hip_fail(e);
+    }
     rec_kernel("cols_inv", st);
     hipError_t e = cols_inv_n(yh, r, s.B * C, s.H, s.mx, s.my, tw, st);
     if (e != hipSuccess) return hip_fail(e);
@@ -374,8 +396,10 @@ size_t unfused_ws_2d(const Shape2d& s) {
            align_up((size_t)s.B * s.Cout * m * sizeof(float2));
 }
 
+// fuse: the one-kernel 256-row transforms where they apply (the default
+// schedule); the unfused ablation runs every pass as its own kernel.
 int run_unfused_2d(const Shape2d& s, const float* x, const float2* w, float* out, void* ws, const float2* tw,
-                   hipStream_t st, const Epilogue& epi = Epilogue{}) {
+                   hipStream_t st, const Epilogue& epi = Epilogue{}, bool fuse = false) {
     const int64_t m = (int64_t)2 * s.mx * s.my;
     const size_t rmax = (size_t)s.B * (size_t)(s.Cin > s.Cout ? s.Cin : s.Cout) * s.H * s.my * sizeof(float2);
     char* p = static_cast<char*>(ws);
@@ -384,11 +408,11 @@ int run_unfused_2d(const Shape2d& s, const float* x, const float2* w, float* out
     float2* xh = reinterpret_cast<float2*>(p);
     p += align_up((size_t)s.B * s.Cin * m * sizeof(float2));
     float2* yh = reinterpret_cast<float2*>(p);
-    int rc = run_forward2d_staged(s, s.Cin, x, xh, r, tw, st);
+    int rc = run_forward2d_staged(s, s.Cin, x, xh, r, tw, st, fuse);
     if (rc) return rc;
     rc = run_mix(xh, canonical_layout(s.Cin, m), w, yh, canonical_layout(s.Cout, m), s.B, s.Cin, s.Cout, m, st);
     if (rc) return rc;
-    return run_inverse2d_staged(s, s.Cout, yh, out, r, tw, st, epi);
+    return run_inverse2d_staged(s, s.Cout, yh, out, r, tw, st, epi, fuse);
 }
 
 // Fused (grids up to 128 x 128): fwd2d -> mix -> inv2d, the truncated spectra
@@ -454,38 +478,6 @@ size_t best_ws_2d(const Shape2d& s, bool epi = false) {
     return !epi && one_kernel_path(s) ? 0 : staged_ws_2d(s);
 }
 
-// 256-row grids of 256 or 512 columns: the forward and the inverse transform
-// of each image in one kernel each (the row spectrum in LDS), the mix between
-// them; the workspace of the staged schedule (its row-spectrum region
-// unused).
-bool short2d_path(const Shape2d& s) {
-    return is_pow2(s.H) && is_pow2(s.W) && short2d_supported(s.log2H, s.log2W, s.mx, s.my);
-}
-
-int run_short2d(const Shape2d& s, const float* x, const float2* w, float* out, void* ws, const float2* tw,
-                hipStream_t st, const Epilogue& epi) {
-    const int64_t m = (int64_t)2 * s.mx * s.my;
-    const size_t rmax = (size_t)s.B * (size_t)(s.Cin > s.Cout ? s.Cin : s.Cout) * s.H * s.my * sizeof(float2);
-    char* p = static_cast<char*>(ws);
-    float2* r = reinterpret_cast<float2*>(p);
-    p += align_up(rmax);
-    float2* xh = reinterpret_cast<float2*>(p);
-    p += align_up((size_t)s.B * s.Cin * m * sizeof(float2));
-    float2* yh = reinterpret_cast<float2*>(p);
-    const float scale = (float)(1.0 / std::sqrt((double)s.H * (double)s.W));
-    rec_kernel("fwd2d", st);
-    const hipError_t e = launch_fwd2d_short(x, xh, s.B * s.Cin, s.log2H, s.log2W, s.mx, s.my, scale, tw, st);
-    if (e != hipSuccess) return hip_fail(e);
-    int rc = run_mix(xh, canonical_layout(s.Cin, m), w, yh, canonical_layout(s.Cout, m), s.B, s.Cin, s.Cout, m, st);
-    if (rc) return rc;
-    (void)r;
-    rec_kernel(epi.on ? "inv2d_gelu" : "inv2d", st);
-    Epilogue ep = epi;
-    ep.rows_per_chan = (uint32_t)s.H;
-    const hipError_t ei = launch_inv2d_short(yh, out, s.B * s.Cout, s.log2H, s.log2W, s.mx, s.my, scale, tw, st, ep);
-    return ei == hipSuccess ? FNO_OK : hip_fail(ei);
-}
-
 int run_best_2d(const Shape2d& s, const float* x, const float2* w, float* out, void* ws, const float2* tw,
                 hipStream_t st, const Epilogue& epi = Epilogue{}) {
     if (!epi.on && one_kernel_path(s)) {
@@ -496,8 +488,7 @@ int run_best_2d(const Shape2d& s, const float* x, const float2* w, float* out, v
         return e == hipSuccess ? FNO_OK : hip_fail(e);
     }
     if (small_path(s)) return run_fused_small_2d(s, x, w, out, ws, tw, st, epi);
-    if (short2d_path(s)) return run_short2d(s, x, w, out, ws, tw, st, epi);
-    return run_unfused_2d(s, x, w, out, ws, tw, st, epi);
+    return run_unfused_2d(s, x, w, out, ws, tw, st, epi, true);
 }
 
 // Diagonal global filter: forward -> per-(mode, channel) product -> inverse,

@@ -120,6 +120,23 @@ def test_stages_2d(name):
     assert_close(out, out_ref, f"{name} inverse")
 
 
+@pytest.mark.parametrize("shape", [
+    (2, 3, 4, 256, 256, 16, 32),    # the one-kernel 256 x 256 forward and inverse, two column blocks
+    (2, 3, 4, 256, 512, 8, 12),     # the one-kernel 256 x 512 forward and inverse, one column block
+], ids=lambda s: "x".join(map(str, s)))
+def test_stages_2d_shapes(shape):
+    b, cin, cout, h, wd, mx, my = shape
+    cfg = Config("stage", "2d", b, cin, cout, h, wd, mx, my, "uniform")
+    x, w = make_inputs(cfg, 3)
+    xh = fno.fno_forward2d(to_dev(x), mx, my)
+    torch.cuda.synchronize()
+    assert_close(xh, oracle.forward_truncated_2d(x, mx, my), f"{shape} forward spectrum")
+    yh32 = oracle.mix_2d(oracle.forward_truncated_2d(x, mx, my).astype(np.complex64), w).astype(np.complex64)
+    out = fno.fno_inverse2d(to_dev(yh32), h, wd)
+    torch.cuda.synchronize()
+    assert_close(out, oracle.inverse_from_truncated_2d(yh32, h, wd), f"{shape} inverse")
+
+
 @pytest.mark.parametrize("name", ["s1d", "c4"])
 def test_stages_1d(name):
     # s1d: a 1024-point sequence with a ragged mode count; c4: the full
