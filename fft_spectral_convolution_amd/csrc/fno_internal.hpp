@@ -175,12 +175,15 @@ hipError_t launch_mix_mfma(const float2* xh, const SpecLayout& lx, const float2*
                            const SpecLayout& ly, int64_t B, int64_t Cin, int64_t Cout, int64_t M, hipStream_t s,
                            bool adjoint = false);
 
-// ---- per-image transforms of 256-row grids (fno_short2d.hip) ----------------
-// H = 256, W in {256, 512}, my <= 32, 2 mx a multiple of 16 (at most 128):
+// ---- per-image transforms of 256- and 512-row grids (fno_short2d.hip) --------
+// H in {256, 512}, W in {256, 512}, my <= 32 (16 at H = 512), 2 mx a
+// multiple of 16 (at most 128):
 // the row and column passes of one image in one workgroup, the row spectrum
 // in LDS.  Forward: x [nimg][H][W] -> the canonical spectrum
 // xh [nimg][2 mx][my] (kept kx rows, mode q my + ky), scaled by scale.
 bool short2d_supported(int log2H, int log2W, int mx, int my);
+// whether nimg images keep enough CUs busy for the one-kernel form
+bool short2d_pays(int64_t nimg);
 hipError_t launch_fwd2d_short(const float* x, float2* xh, int64_t nimg, int log2H, int log2W, int mx, int my,
                               float scale, const float2* tw, hipStream_t s);
 // Inverse: the canonical spectrum yh [nimg][2 mx][my] -> out [nimg][H][W]

@@ -1,5 +1,5 @@
-// Per-image 2D transforms for grids of 256 rows and 256 or 512 columns with
-// at most 32 kept columns: the row pass and the column pass of
+// Per-image 2D transforms for grids of 256 or 512 rows and 256 or 512
+// columns with at most 32 (16 at 512 rows) kept columns: the row pass and the column pass of
 // one image in one workgroup, the row spectrum kept in LDS between them
 // (TurboFNO blog, section 2.1: the truncated spectrum stays on chip between
 // the passes of the 2D transform; section 2.2: only the kept modes are ever
@@ -9,7 +9,8 @@
 // transforms 64 / LW rows at a time as the short-row kernels do (lane n1 < LW
 // of a row holds its samples n1 + LW n2, n2 < 16, and runs a 16-point real
 // DFT; the kept bins are formed by binary trees over the phases) and writes
-// the bins ky < my of its rows into an LDS plane [H][33].  Column pass: the
+// the bins ky < my of its rows into an LDS plane [H][33] ([H][17] at 512
+// rows).  Column pass: the
 // kept columns in blocks of 16, thread (n1, c) of 16 LH per block holding
 // column c's samples n1 + LH n2 (n2 < 16) of the plane, a 16-point DFT, the
 // residues staged in LDS, and every kept mode kx formed by a binary tree
@@ -29,8 +30,6 @@ namespace {
 
 constexpr int kS2Threads = 1024;
 constexpr int kS2Waves = kS2Threads / 64;
-constexpr int kS2PS = 33;            // plane row stride (complex): odd, rows on distinct bank pairs
-constexpr int kS2CB = 2;             // column blocks of 16: my <= 32
 constexpr int kS2MaxKept = 128;      // 2 mx
 
 constexpr int s2_kept(int H) { return H < kS2MaxKept ? H : kS2MaxKept; }
@@ -57,9 +56,13 @@ struct S2Plan {
     static constexpr int CSTAGE = 16 * C * SSc;         // column stage per block
     static constexpr int MPR = s2_kept(H) / 16;         // kept modes per residue, at most
     static constexpr int KS = s2_kept(H) + 2;           // inverse table row stride (16-byte multiple)
-    static constexpr int STAGE = kS2Waves * RSTAGE > kS2CB * CSTAGE ? kS2Waves * RSTAGE : kS2CB * CSTAGE;
+    // kept columns: two blocks of 16 (my <= 32), one at 512 rows (my <= 16,
+    // so that the plane fits the LDS beside the stages)
+    static constexpr int CB = H >= 512 ? 1 : 2;
+    static constexpr int PS = 16 * CB + 1;              // plane row stride (complex): odd, rows on distinct bank pairs
+    static constexpr int STAGE = kS2Waves * RSTAGE > CB * CSTAGE ? kS2Waves * RSTAGE : CB * CSTAGE;
     static_assert(H % RPI == 0, "whole row iterations");
-    static_assert(kS2CB * NTc <= kS2Threads, "column blocks");
+    static_assert(CB * NTc <= kS2Threads, "column blocks");
 };
 
 // ---- forward ------------------------------------------------------------------
@@ -71,8 +74,8 @@ __global__ __launch_bounds__(kS2Threads) void k_fwd2d_short(const float* __restr
     constexpr int W = P::W, H = P::H, Q = P::Q, NZ = P::NZ, SROWS = P::SROWS;
     constexpr int RPW = P::RPW, PBS = P::PBS, PB = P::PB, SS = P::SS, NSL = P::NSL, BPS = P::BPS;
     constexpr int C = P::C, PBSc = P::PBSc, PBc = P::PBc, SSc = P::SSc, NTc = P::NTc, NRDc = P::NRDc;
-    constexpr int MPR = P::MPR;
-    __shared__ float2 plane[H * kS2PS];
+    constexpr int MPR = P::MPR, CB = P::CB, PS = P::PS;
+    __shared__ float2 plane[H * PS];
     __shared__ float2 stage[P::STAGE];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -109,7 +112,7 @@ __global__ __launch_bounds__(kS2Threads) void k_fwd2d_short(const float* __restr
     // phase m1); reading role rho = tl + NTc h (block pbc, column cr, residue
     // rr)
     const int cb = tid / NTc, tl = tid % NTc;
-    const bool col_thread = cb < kS2CB;
+    const bool col_thread = cb < CB;
     const int c = tl % C, m1 = tl / C;
     auto role = [&](int h, int& pbc, int& cr, int& rr) __attribute__((always_inline)) {
         const int rho = tl + NTc * h;
@@ -117,7 +120,9 @@ __global__ __launch_bounds__(kS2Threads) void k_fwd2d_short(const float* __restr
         cr = (rho / PBc) % C;
         rr = rho / (PBc * C);
     };
-    float2 wc[NRDc][MPR], vc[PBc == 2 ? NRDc : 1][MPR];
+    // W^k of the role's modes (with two phase blocks, the second block's
+    // factor W^{16 k} is the tree's last square squared once more)
+    float2 wc[NRDc][MPR];
 #pragma unroll
     for (int h = 0; h < NRDc; ++h) {
         int pbc, cr, rr;
@@ -127,7 +132,6 @@ __global__ __launch_bounds__(kS2Threads) void k_fwd2d_short(const float* __restr
             const int q = rr + 16 * i;
             const int k = q < nk ? (q < mx ? q : H - nk + q) : 0;
             wc[h][i] = tw[((int64_t)k * (kNMax / H)) & (kNMax - 1)];
-            if constexpr (PBc == 2) vc[h][i] = cscale(tw[((int64_t)PBSc * pbc * k * (kNMax / H)) & (kNMax - 1)], scale);
         }
     }
     float2* const cstage = stage + (col_thread ? cb : 0) * P::CSTAGE;
@@ -170,7 +174,7 @@ __global__ __launch_bounds__(kS2Threads) void k_fwd2d_short(const float* __restr
                     } else {
                         acc = cscale(v[0], 0.5f);
                     }
-                    if (pb == 0 && k < my) plane[(row0 + rr) * kS2PS + k] = cj ? conj2(acc) : acc;
+                    if (pb == 0 && k < my) plane[(row0 + rr) * PS + k] = cj ? conj2(acc) : acc;
                 }
             });
             wave_lds_sync();                    // the stage is read before the next rows overwrite it
@@ -182,7 +186,7 @@ __global__ __launch_bounds__(kS2Threads) void k_fwd2d_short(const float* __restr
             const int kyc = C * cb + c < my ? C * cb + c : my - 1;
             float2 v[16];
 #pragma unroll
-            for (int n2 = 0; n2 < 16; ++n2) v[n2] = plane[(m1 + LH * n2) * kS2PS + kyc];
+            for (int n2 = 0; n2 < 16; ++n2) v[n2] = plane[(m1 + LH * n2) * PS + kyc];
             dft<16, -1>(v);
 #pragma unroll
             for (int q = 0; q < 16; ++q) cstage[(q * C + c) * SSc + m1 + m1 / PBSc] = v[q];
@@ -214,7 +218,9 @@ __global__ __launch_bounds__(kS2Threads) void k_fwd2d_short(const float* __restr
                         }
                         float2 acc;
                         if constexpr (PBc == 2) {
-                            acc = cmul(vc[h][i], u[0]);
+                            // w is W^{8k} here
+                            const float2 f = pbc ? cscale(cmul(w, w), scale) : make_float2(scale, 0.0f);
+                            acc = cmul(f, u[0]);
                             acc.x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(acc.x), 0xB1, 0xF, 0xF, false));
                             acc.y += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(acc.y), 0xB1, 0xF, 0xF, false));
                         } else {
@@ -242,11 +248,12 @@ __global__ __launch_bounds__(kS2Threads) void k_inv2d_short(const float2* __rest
     using P = S2Plan<LW, LH>;
     constexpr int W = P::W, H = P::H, Q = P::Q, NZ = P::NZ;
     constexpr int RPW = P::RPW, C = P::C, NTc = P::NTc, KS = P::KS;
+    constexpr int CB = P::CB, PS = P::PS;
     constexpr int TF = NZ + 5;                 // residue-factor table row (odd: phases on distinct bank pairs)
-    static_assert(NJ == 1 || NJ == 2, "at most 32 kept columns");
-    __shared__ float2 plane[H * kS2PS];
+    static_assert(NJ <= CB, "at most 16 CB kept columns");
+    __shared__ float2 plane[H * PS];
     __shared__ __align__(16) float2 T[LH * KS];           // [m1][q]: W_H^{-m1 k_q}
-    __shared__ __align__(16) float2 xs[kS2CB * C * KS];   // [block][c][q]: the image's kept modes
+    __shared__ __align__(16) float2 xs[CB * C * KS];   // [block][c][q]: the image's kept modes
     __shared__ float2 ftab[LW * TF];                      // [n1][t]: row residue factors
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -271,7 +278,7 @@ __global__ __launch_bounds__(kS2Threads) void k_inv2d_short(const float2* __rest
 
     // column roles: block cb, phase m1, column c
     const int cb = tid / NTc, tl = tid % NTc;
-    const bool col_thread = cb < kS2CB;
+    const bool col_thread = cb < CB;
     const int c = tl % C, m1 = tl / C;
     const float2* const tp = T + m1 * KS;
     const float2* const xp = xs + ((col_thread ? cb : 0) * C + c) * KS;
@@ -286,8 +293,8 @@ __global__ __launch_bounds__(kS2Threads) void k_inv2d_short(const float2* __rest
     for (int64_t img = blockIdx.x; img < nimg; img += gridDim.x) {
         // ---- the image's kept modes (zero past my), column fastest --------
         const float2* const src = yh + img * (int64_t)nk * my;
-        for (int e = tid; e < nk * kS2CB * C; e += kS2Threads) {
-            const int q = e / (kS2CB * C), col = e % (kS2CB * C);
+        for (int e = tid; e < nk * CB * C; e += kS2Threads) {
+            const int q = e / (CB * C), col = e % (CB * C);
             xs[col * KS + q] = col < my ? src[(int64_t)q * my + col] : make_float2(0.0f, 0.0f);
         }
         __syncthreads();
@@ -315,13 +322,13 @@ __global__ __launch_bounds__(kS2Threads) void k_inv2d_short(const float2* __rest
                 // with its imaginary part dropped
                 float2 o = ky < my ? v[n2] : make_float2(0.0f, 0.0f);
                 if (ky == 0) o = make_float2(0.5f * o.x, 0.0f);
-                plane[(m1 + LH * n2) * kS2PS + ky] = o;
+                plane[(m1 + LH * n2) * PS + ky] = o;
             }
         }
         __syncthreads();                        // the plane is whole (and the modes are read)
         // ---- row pass: each plane row to its image row ----------------------
         for (int row0 = wave * RPW; row0 < H; row0 += P::RPI) {
-            const float2* const xr = plane + (row0 + rw) * kS2PS;
+            const float2* const xr = plane + (row0 + rw) * PS;
             float2 V[Q], cur[NJ], nxt[NJ];
 #pragma unroll
             for (int j = 0; j < NJ; ++j) cur[j] = xr[Q * j];
@@ -389,11 +396,23 @@ hipError_t launch_s2(K kernel, int64_t nimg, hipStream_t s, int& g) {
 
 }  // namespace
 
-// 256 rows of 256 or 512 points (the forms that fit the registers of 16
-// waves without spills)
+// 256 or 512 rows of 256 or 512 points (the forms that fit the registers of
+// 16 waves without spills); at 512 rows at most 16 kept columns (the plane
+// beside the stages in the LDS)
 bool short2d_supported(int log2H, int log2W, int mx, int my) {
-    return log2H == 8 && (log2W == 8 || log2W == 9) && my >= 1 && my <= 32 && mx >= 1 && (2 * mx) % 16 == 0 &&
-           2 * mx <= s2_kept(1 << log2H);
+    return (log2H == 8 || log2H == 9) && (log2W == 8 || log2W == 9) && my >= 1 && my <= (log2H == 9 ? 16 : 32) &&
+           mx >= 1 && (2 * mx) % 16 == 0 && 2 * mx <= s2_kept(1 << log2H);
+}
+
+// One image per workgroup and one workgroup per CU: with fewer images than
+// half the CUs the staged kernels, which spread an image over several
+// workgroups, were faster (256 x 256, 32 and 64 images: 37 against 28 and
+// 32 us; even at 128 images, faster from 256 on).
+bool short2d_pays(int64_t nimg) {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return false;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+    return 2 * nimg >= cus;
 }
 
 hipError_t launch_fwd2d_short(const float* x, float2* xh, int64_t nimg, int log2H, int log2W, int mx, int my,
@@ -405,6 +424,7 @@ hipError_t launch_fwd2d_short(const float* x, float2* xh, int64_t nimg, int log2
         if (e != hipSuccess) return e;
         return launch_kernel(kernel, dim3((unsigned)g), dim3(kS2Threads), 0, s, x, xh, nimg, mx, my, scale, tw);
     };
+    if (log2H == 9) return log2W == 8 ? go(k_fwd2d_short<16, 32>) : go(k_fwd2d_short<32, 32>);
     if (log2W == 8) return go(k_fwd2d_short<16, 16>);
     return go(k_fwd2d_short<32, 16>);
 }
@@ -420,6 +440,10 @@ hipError_t launch_inv2d_short(const float2* yh, float* out, int64_t nimg, int lo
                              epi);
     };
     const bool two = my > 16;
+    if (log2H == 9) {                       // my <= 16
+        if (log2W == 8) return epi.on ? go(k_inv2d_short<16, 32, true, 1>) : go(k_inv2d_short<16, 32, false, 1>);
+        return epi.on ? go(k_inv2d_short<32, 32, true, 1>) : go(k_inv2d_short<32, 32, false, 1>);
+    }
     if (log2W == 8) {
         if (epi.on) return two ? go(k_inv2d_short<16, 16, true, 2>) : go(k_inv2d_short<16, 16, true, 1>);
         return two ? go(k_inv2d_short<16, 16, false, 2>) : go(k_inv2d_short<16, 16, false, 1>);

@@ -77,7 +77,7 @@ FILTER_2D = [
     (2, 7, 64, 64, 5, 7),           # one row per thread, ragged mode tile
     (1, 3, 256, 256, 9, 11),        # staged: 256-point short rows, generic columns (odd mx)
     (1, 3, 256, 64, 8, 12),         # staged: 64-point short rows, 256-row short columns
-    (1, 3, 256, 256, 8, 12),        # one-kernel 256 x 256 transforms
+    (16, 8, 256, 256, 8, 12),       # one-kernel 256 x 256 transforms (128 images)
     (1, 2, 16, 1024, 5, 50),        # pruned long rows
     (1, 2, 1024, 16, 8, 9),         # pruned columns
     (2, 3, 60, 35, 12, 10),         # mixed-radix lengths

@@ -76,8 +76,12 @@ GELU_2D = [
     (1, 2, 3, 256, 256, 9, 11),       # staged: 256-point short rows, generic columns (odd mx)
     (1, 2, 3, 128, 256, 9, 100),      # staged: generic rows (more than 64 bins)
     (1, 2, 3, 256, 64, 8, 12),        # staged: 64-point short rows, 256-row pruned columns
-    (1, 2, 3, 256, 256, 8, 12),       # one-kernel 256 x 256 transforms, the tail in the inverse
-    (2, 2, 3, 256, 512, 16, 24),      # one-kernel 256 x 512 transforms, two column blocks, the tail
+    (16, 8, 8, 256, 256, 8, 12),      # one-kernel 256 x 256 transforms (128 images), the tail in the inverse
+    (16, 8, 8, 256, 256, 8, 24),      # one-kernel 256 x 256 transforms, two column blocks, the tail
+    (16, 8, 8, 256, 512, 16, 24),     # one-kernel 256 x 512 transforms, two column blocks, the tail
+    (16, 8, 8, 256, 512, 8, 12),      # one-kernel 256 x 512 transforms, one column block, the tail
+    (16, 8, 8, 512, 512, 8, 16),      # one-kernel 512 x 512 transforms, the tail
+    (16, 8, 8, 512, 256, 8, 12),      # one-kernel 512 x 256 transforms, the tail
     (1, 2, 3, 16, 1024, 5, 50),       # staged: pruned long rows
     (1, 2, 2, 1024, 16, 8, 9),        # staged: pruned columns, generic rows
     (2, 3, 4, 45, 100, 10, 20),       # mixed-radix rows and columns

@@ -121,8 +121,10 @@ def test_stages_2d(name):
 
 
 @pytest.mark.parametrize("shape", [
-    (2, 3, 4, 256, 256, 16, 32),    # the one-kernel 256 x 256 forward and inverse, two column blocks
-    (2, 3, 4, 256, 512, 8, 12),     # the one-kernel 256 x 512 forward and inverse, one column block
+    (16, 8, 8, 256, 256, 16, 32),   # the one-kernel 256 x 256 forward and inverse (128 images), two column blocks
+    (16, 8, 8, 256, 512, 8, 12),    # the one-kernel 256 x 512 forward and inverse, one column block
+    (16, 8, 8, 512, 512, 8, 16),    # the one-kernel 512 x 512 forward and inverse
+    (2, 3, 4, 256, 256, 16, 32),    # few images: the staged transforms
 ], ids=lambda s: "x".join(map(str, s)))
 def test_stages_2d_shapes(shape):
     b, cin, cout, h, wd, mx, my = shape
@@ -169,13 +171,19 @@ def test_stages_1d(name):
 EDGE_2D = [
     # B, Cin, Cout, H, W, mx, my
     (300, 2, 3, 32, 32, 8, 8),      # one-kernel small path: more batch items than CUs
-    (2, 4, 4, 256, 256, 32, 32),    # one-kernel 256 x 256 forward and inverse, two column blocks
-    (2, 3, 5, 256, 512, 16, 17),    # one-kernel 256 x 512 transforms, one column in the last block
+    (2, 4, 4, 256, 256, 32, 32),    # few images: staged 256-point short rows and 256-row short columns
+    (16, 8, 8, 256, 256, 32, 32),   # one-kernel 256 x 256 transforms (128 images), two column blocks
+    (16, 8, 8, 256, 256, 16, 12),   # one-kernel 256 x 256 transforms, one column block
+    (2, 3, 5, 256, 512, 16, 17),    # few images: staged 512-point short rows, one column in the last block
+    (16, 8, 8, 256, 512, 16, 17),   # one-kernel 256 x 512 transforms, one column in the last block
+    (16, 8, 8, 256, 512, 16, 16),   # one-kernel 256 x 512 transforms, one column block
     (2, 3, 2, 512, 256, 64, 64),    # 256-point short rows, every bin up to 64; 512-row short columns, 128 kept kx
-    (3, 2, 3, 256, 256, 64, 16),    # one-kernel 256 x 256 transforms: every kept kx of 128, one column block
-    (2, 3, 2, 256, 512, 8, 32),     # one-kernel 256 x 512 transforms: two column blocks
+    (16, 8, 8, 256, 256, 64, 16),   # one-kernel 256 x 256 transforms: every kept kx of 128, one column block
+    (16, 8, 8, 256, 512, 8, 32),    # one-kernel 256 x 512 transforms: two column blocks
     (8, 64, 4, 256, 256, 8, 8),     # one-kernel 256 x 256 forward: more images than workgroups
     (4, 4, 96, 256, 256, 8, 20),    # one-kernel 256 x 256 inverse: more images than workgroups, ragged last block
+    (16, 8, 8, 512, 512, 16, 16),   # one-kernel 512 x 512 transforms (16 kept columns, two phase blocks per column)
+    (16, 8, 8, 512, 256, 8, 12),    # one-kernel 512 x 256 transforms, ragged column block
     (1, 2, 3, 128, 256, 9, 100),    # 256-point rows with more than 64 bins: generic rows and columns
     (1, 2, 3, 512, 128, 24, 5),     # 512-row short columns, one partial block of 16 columns
     (2, 3, 4, 256, 64, 8, 20),      # 64-point short rows (16 rows per wave), bins in two groups of 16
