@@ -175,9 +175,9 @@ hipError_t launch_mix_mfma(const float2* xh, const SpecLayout& lx, const float2*
                            const SpecLayout& ly, int64_t B, int64_t Cin, int64_t Cout, int64_t M, hipStream_t s,
                            bool adjoint = false);
 
-// ---- per-image transforms of 256- and 512-row grids (fno_short2d.hip) --------
-// H in {256, 512}, W in {256, 512}, my <= 32 (16 at H = 512), 2 mx a
-// multiple of 16 (at most 128):
+// ---- per-image transforms of 128- to 512-row grids (fno_short2d.hip) ---------
+// 128 x 256, or H in {256, 512} and W in {256, 512}; my <= 32 (16 at
+// H = 512), 2 mx a multiple of 16 (at most 128, 64 at H = 128):
 // the row and column passes of one image in one workgroup, the row spectrum
 // in LDS.  Forward: x [nimg][H][W] -> the canonical spectrum
 // xh [nimg][2 mx][my] (kept kx rows, mode q my + ky), scaled by scale.

@@ -1,5 +1,5 @@
-// Per-image 2D transforms for grids of 256 or 512 rows and 256 or 512
-// columns with at most 32 (16 at 512 rows) kept columns: the row pass and the column pass of
+// Per-image 2D transforms for grids of 128 x 256 and of 256 or 512 rows by
+// 256 or 512 columns with at most 32 (16 at 512 rows) kept columns: the row pass and the column pass of
 // one image in one workgroup, the row spectrum kept in LDS between them
 // (TurboFNO blog, section 2.1: the truncated spectrum stays on chip between
 // the passes of the 2D transform; section 2.2: only the kept modes are ever
@@ -20,7 +20,7 @@
 // the short-column inverse, and the short-row inverse turns each plane row
 // into the image row, with the fused layer epilogue when asked.
 // 2 mx must be a multiple of 16 (kept mode q has residue q mod 16) and at
-// most min(H, 128); the grid is persistent, one image per workgroup at a time.
+// most 128 (64 at 128 rows); the grid is persistent, one image per workgroup at a time.
 #include "fno_device.hpp"
 #include "fno_internal.hpp"
 #include "fno_realbins.hpp"
@@ -32,7 +32,9 @@ constexpr int kS2Threads = 1024;
 constexpr int kS2Waves = kS2Threads / 64;
 constexpr int kS2MaxKept = 128;      // 2 mx
 
-constexpr int s2_kept(int H) { return H < kS2MaxKept ? H : kS2MaxKept; }
+// kept kx at most: 128, or half the rows at 128 rows (the column twiddles of
+// two reading roles per thread then fit the registers)
+constexpr int s2_kept(int H) { return H >= 256 ? kS2MaxKept : H / 2; }
 
 template <int LW, int LH>
 struct S2Plan {
@@ -396,11 +398,12 @@ hipError_t launch_s2(K kernel, int64_t nimg, hipStream_t s, int& g) {
 
 }  // namespace
 
-// 256 or 512 rows of 256 or 512 points (the forms that fit the registers of
-// 16 waves without spills); at 512 rows at most 16 kept columns (the plane
-// beside the stages in the LDS)
+// 128 rows of 256 points, 256 or 512 rows of 256 or 512 points (the forms
+// that fit the registers of 16 waves without spills); at 512 rows at most 16
+// kept columns (the plane beside the stages in the LDS)
 bool short2d_supported(int log2H, int log2W, int mx, int my) {
-    return (log2H == 8 || log2H == 9) && (log2W == 8 || log2W == 9) && my >= 1 && my <= (log2H == 9 ? 16 : 32) &&
+    return log2H >= 7 && log2H <= 9 && (log2W == 8 || (log2W == 9 && log2H > 7)) && my >= 1 &&
+           my <= (log2H == 9 ? 16 : 32) &&
            mx >= 1 && (2 * mx) % 16 == 0 && 2 * mx <= s2_kept(1 << log2H);
 }
 
@@ -425,6 +428,7 @@ hipError_t launch_fwd2d_short(const float* x, float2* xh, int64_t nimg, int log2
         return launch_kernel(kernel, dim3((unsigned)g), dim3(kS2Threads), 0, s, x, xh, nimg, mx, my, scale, tw);
     };
     if (log2H == 9) return log2W == 8 ? go(k_fwd2d_short<16, 32>) : go(k_fwd2d_short<32, 32>);
+    if (log2H == 7) return go(k_fwd2d_short<16, 8>);
     if (log2W == 8) return go(k_fwd2d_short<16, 16>);
     return go(k_fwd2d_short<32, 16>);
 }
@@ -440,6 +444,10 @@ hipError_t launch_inv2d_short(const float2* yh, float* out, int64_t nimg, int lo
                              epi);
     };
     const bool two = my > 16;
+    if (log2H == 7) {                       // W = 256
+        if (epi.on) return two ? go(k_inv2d_short<16, 8, true, 2>) : go(k_inv2d_short<16, 8, true, 1>);
+        return two ? go(k_inv2d_short<16, 8, false, 2>) : go(k_inv2d_short<16, 8, false, 1>);
+    }
     if (log2H == 9) {                       // my <= 16
         if (log2W == 8) return epi.on ? go(k_inv2d_short<16, 32, true, 1>) : go(k_inv2d_short<16, 32, false, 1>);
         return epi.on ? go(k_inv2d_short<32, 32, true, 1>) : go(k_inv2d_short<32, 32, false, 1>);

@@ -184,6 +184,9 @@ EDGE_2D = [
     (4, 4, 96, 256, 256, 8, 20),    # one-kernel 256 x 256 inverse: more images than workgroups, ragged last block
     (16, 8, 8, 512, 512, 16, 16),   # one-kernel 512 x 512 transforms (16 kept columns, two phase blocks per column)
     (16, 8, 8, 512, 256, 8, 12),    # one-kernel 512 x 256 transforms, ragged column block
+    (16, 8, 8, 128, 256, 16, 20),   # one-kernel 128 x 256 transforms, ragged second column block
+    (16, 8, 8, 128, 256, 32, 12),   # one-kernel 128 x 256 transforms, every kx kept (64 of 128 rows)
+    (16, 8, 8, 128, 256, 40, 12),   # 128 x 256 with more than 64 kept kx: staged transforms
     (1, 2, 3, 128, 256, 9, 100),    # 256-point rows with more than 64 bins: generic rows and columns
     (1, 2, 3, 512, 128, 24, 5),     # 512-row short columns, one partial block of 16 columns
     (2, 3, 4, 256, 64, 8, 20),      # 64-point short rows (16 rows per wave), bins in two groups of 16
