@@ -1,5 +1,5 @@
-// Per-image 2D transforms for grids of 128 x 256 and of 256 or 512 rows by
-// 256 or 512 columns with at most 32 (16 at 512 rows) kept columns: the row pass and the column pass of
+// Per-image 2D transforms for grids of 128 x 256, 256 x 128 and of 256 or 512
+// rows by 256 or 512 columns with at most 32 (16 at 512 rows) kept columns: the row pass and the column pass of
 // one image in one workgroup, the row spectrum kept in LDS between them
 // (TurboFNO blog, section 2.1: the truncated spectrum stays on chip between
 // the passes of the 2D transform; section 2.2: only the kept modes are ever
@@ -95,14 +95,21 @@ __global__ __launch_bounds__(kS2Threads) void k_fwd2d_short(const float* __restr
         rr = it % RPW;
         k = it / RPW;
     };
-    float2 wk[NSL], vk[PB == 2 ? NSL : 1];
+    // W^k of each slot's bin; with 128-point rows (eight slots, which would
+    // not fit the registers beside the column factors) only the lane's part
+    // W^{g / RPW} is kept and the slot's part W^{PBS sl}, the same in every
+    // lane, is read where it is used (bin k = PBS sl + g / RPW)
+    constexpr bool WKL = LW == 8;
+    constexpr int NWK = WKL ? 1 : NSL;
+    float2 wk[NWK], vk[PB == 2 ? NSL : 1];
+    if constexpr (WKL) wk[0] = tw[((g / RPW) * (kNMax / W)) & (kNMax - 1)];
 #pragma unroll
     for (int sl = 0; sl < NSL; ++sl) {
         int rr, k;
         item(sl, rr, k);
         const bool cj = k % Q > NZ;
         const float2 w = tw[(k * (kNMax / W)) & (kNMax - 1)];
-        wk[sl] = cj ? conj2(w) : w;
+        if constexpr (!WKL) wk[sl] = cj ? conj2(w) : w;
         if constexpr (PB == 2) {
             const float2 u = cscale(tw[(PBS * pb * k * (kNMax / W)) & (kNMax - 1)], 0.5f);
             vk[sl] = cj ? conj2(u) : u;
@@ -140,7 +147,7 @@ __global__ __launch_bounds__(kS2Threads) void k_fwd2d_short(const float* __restr
 
     for (int64_t img = blockIdx.x; img < nimg; img += gridDim.x) {
 #pragma unroll
-        for (int sl = 0; sl < NSL; ++sl) asm volatile("" : "+v"(wk[sl].x), "+v"(wk[sl].y));
+        for (int sl = 0; sl < NWK; ++sl) asm volatile("" : "+v"(wk[sl].x), "+v"(wk[sl].y));
         const float* const ximg = x + img * (int64_t)(H * W);
         // ---- row pass: bins ky < my of every row into the plane --------------
         for (int row0 = wave * RPW; row0 < H; row0 += P::RPI) {
@@ -161,7 +168,13 @@ __global__ __launch_bounds__(kS2Threads) void k_fwd2d_short(const float* __restr
                     float2 v[PBS];
 #pragma unroll
                     for (int t = 0; t < PBS; ++t) v[t] = sp[t];
-                    float2 w = wk[sl];
+                    float2 w;
+                    if constexpr (WKL) {
+                        w = cmul(wk[0], tw[(PBS * sl * (kNMax / W)) & (kNMax - 1)]);
+                        if (cj) w = conj2(w);
+                    } else {
+                        w = wk[sl];
+                    }
 #pragma unroll
                     for (int len = PBS; len > 1; len /= 2) {
 #pragma unroll
@@ -398,11 +411,12 @@ hipError_t launch_s2(K kernel, int64_t nimg, hipStream_t s, int& g) {
 
 }  // namespace
 
-// 128 rows of 256 points, 256 or 512 rows of 256 or 512 points (the forms
-// that fit the registers of 16 waves without spills); at 512 rows at most 16
-// kept columns (the plane beside the stages in the LDS)
+// 128 rows of 256 points, 256 rows of 128 points, 256 or 512 rows of 256 or
+// 512 points (the forms that fit the registers of 16 waves without spills);
+// at 512 rows at most 16 kept columns (the plane beside the stages in the LDS)
 bool short2d_supported(int log2H, int log2W, int mx, int my) {
-    return log2H >= 7 && log2H <= 9 && (log2W == 8 || (log2W == 9 && log2H > 7)) && my >= 1 &&
+    return log2H >= 7 && log2H <= 9 && (log2W == 8 || (log2W == 9 && log2H > 7) || (log2W == 7 && log2H == 8)) &&
+           my >= 1 &&
            my <= (log2H == 9 ? 16 : 32) &&
            mx >= 1 && (2 * mx) % 16 == 0 && 2 * mx <= s2_kept(1 << log2H);
 }
@@ -410,12 +424,15 @@ bool short2d_supported(int log2H, int log2W, int mx, int my) {
 // One image per workgroup and one workgroup per CU: with fewer images than
 // half the CUs the staged kernels, which spread an image over several
 // workgroups, were faster (256 x 256, 32 and 64 images: 37 against 28 and
-// 32 us; even at 128 images, faster from 256 on).
-bool short2d_pays(int64_t nimg) {
+// 32 us; even at 128 images, faster from 256 on).  With 128-point rows
+// (256 x 128) the one-kernel form pays only up to one image per CU: 128 and
+// 256 images 25 and 31 us against 30 and 35 staged, 512 images 50 against 50
+// (16 kept columns) and 46.5 against 43 (8).
+bool short2d_pays(int64_t nimg, int log2W) {
     int dev = 0, cus = 0;
     if (hipGetDevice(&dev) != hipSuccess) return false;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
-    return 2 * nimg >= cus;
+    return 2 * nimg >= cus && (log2W != 7 || nimg <= cus);
 }
 
 hipError_t launch_fwd2d_short(const float* x, float2* xh, int64_t nimg, int log2H, int log2W, int mx, int my,
@@ -429,6 +446,7 @@ hipError_t launch_fwd2d_short(const float* x, float2* xh, int64_t nimg, int log2
     };
     if (log2H == 9) return log2W == 8 ? go(k_fwd2d_short<16, 32>) : go(k_fwd2d_short<32, 32>);
     if (log2H == 7) return go(k_fwd2d_short<16, 8>);
+    if (log2W == 7) return go(k_fwd2d_short<8, 16>);
     if (log2W == 8) return go(k_fwd2d_short<16, 16>);
     return go(k_fwd2d_short<32, 16>);
 }
@@ -451,6 +469,10 @@ hipError_t launch_inv2d_short(const float2* yh, float* out, int64_t nimg, int lo
     if (log2H == 9) {                       // my <= 16
         if (log2W == 8) return epi.on ? go(k_inv2d_short<16, 32, true, 1>) : go(k_inv2d_short<16, 32, false, 1>);
         return epi.on ? go(k_inv2d_short<32, 32, true, 1>) : go(k_inv2d_short<32, 32, false, 1>);
+    }
+    if (log2W == 7) {                       // H = 256
+        if (epi.on) return two ? go(k_inv2d_short<8, 16, true, 2>) : go(k_inv2d_short<8, 16, true, 1>);
+        return two ? go(k_inv2d_short<8, 16, false, 2>) : go(k_inv2d_short<8, 16, false, 1>);
     }
     if (log2W == 8) {
         if (epi.on) return two ? go(k_inv2d_short<16, 16, true, 2>) : go(k_inv2d_short<16, 16, true, 1>);

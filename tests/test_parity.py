@@ -124,6 +124,7 @@ def test_stages_2d(name):
     (16, 8, 8, 256, 256, 16, 32),   # the one-kernel 256 x 256 forward and inverse (128 images), two column blocks
     (16, 8, 8, 256, 512, 8, 12),    # the one-kernel 256 x 512 forward and inverse, one column block
     (16, 8, 8, 512, 512, 8, 16),    # the one-kernel 512 x 512 forward and inverse
+    (16, 8, 8, 256, 128, 24, 16),   # the one-kernel 256 x 128 forward and inverse, one column block
     (2, 3, 4, 256, 256, 16, 32),    # few images: the staged transforms
 ], ids=lambda s: "x".join(map(str, s)))
 def test_stages_2d_shapes(shape):
@@ -187,6 +188,10 @@ EDGE_2D = [
     (16, 8, 8, 128, 256, 16, 20),   # one-kernel 128 x 256 transforms, ragged second column block
     (16, 8, 8, 128, 256, 32, 12),   # one-kernel 128 x 256 transforms, every kx kept (64 of 128 rows)
     (16, 8, 8, 128, 256, 40, 12),   # 128 x 256 with more than 64 kept kx: staged transforms
+    (16, 8, 8, 256, 128, 16, 20),   # one-kernel 256 x 128 transforms, ragged second column block
+    (16, 8, 8, 256, 128, 64, 8),    # one-kernel 256 x 128 transforms, every kept kx of 128, one column block
+    (16, 8, 8, 256, 128, 8, 32),    # one-kernel 256 x 128 transforms, two whole column blocks
+    (40, 8, 8, 256, 128, 16, 20),   # 256 x 128 with more images than CUs: staged transforms
     (1, 2, 3, 128, 256, 9, 100),    # 256-point rows with more than 64 bins: generic rows and columns
     (1, 2, 3, 512, 128, 24, 5),     # 512-row short columns, one partial block of 16 columns
     (2, 3, 4, 256, 64, 8, 20),      # 64-point short rows (16 rows per wave), bins in two groups of 16
