@@ -323,12 +323,12 @@ bool short2d_path(const Shape2d& s) {
 
 // Staged transforms: rows and columns as separate kernels, the row spectrum R
 // (or R') in workspace; spectra in the canonical layout.  fuse: the
-// one-kernel 256-row transforms where they apply (not in the unfused
+// one-kernel transforms where they apply and pay (not in the unfused
 // ablation).
 int run_forward2d_staged(const Shape2d& s, int64_t C, const float* x, float2* xh, float2* r, const float2* tw,
                          hipStream_t st, bool fuse = true) {
     const float scale = (float)(1.0 / std::sqrt((double)s.H * (double)s.W));
-    if (fuse && short2d_path(s) && short2d_pays(s.B * C, s.log2W)) {
+    if (fuse && short2d_path(s) && short2d_pays(s.B * C, s.log2H, s.log2W)) {
         rec_kernel("fwd2d", st);
         const hipError_t e = launch_fwd2d_short(x, xh, s.B * C, s.log2H, s.log2W, s.mx, s.my, scale, tw, st);
         return e == hipSuccess ? FNO_OK : hip_fail(e);
@@ -346,7 +346,7 @@ int run_forward2d_staged(const Shape2d& s, int64_t C, const float* x, float2* xh
 int run_inverse2d_staged(const Shape2d& s, int64_t C, const float2* yh, float* out, float2* r, const float2* tw,
                          hipStream_t st, const Epilogue& epi = Epilogue{}, bool fuse = true) {
     const float scale = (float)(1.0 / std::sqrt((double)s.H * (double)s.W));
-    if (fuse && short2d_path(s) && short2d_pays(s.B * C, s.log2W)) {
+    if (fuse && short2d_path(s) && short2d_pays(s.B * C, s.log2H, s.log2W)) {
         rec_kernel(epi.on ? "inv2d_gelu" : "inv2d", st);
         Epilogue ep = epi;
         ep.rows_per_chan = (uint32_t)s.H;

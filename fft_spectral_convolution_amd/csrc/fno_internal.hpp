@@ -176,15 +176,16 @@ hipError_t launch_mix_mfma(const float2* xh, const SpecLayout& lx, const float2*
                            bool adjoint = false);
 
 // ---- per-image transforms of 128- to 512-row grids (fno_short2d.hip) ---------
-// 128 x 256, 256 x 128, or H in {256, 512} and W in {256, 512}; my <= 32 (16 at
+// 128 x 256, or H in {256, 512} and W in {128, 256, 512}; my <= 32 (16 at
 // H = 512), 2 mx a multiple of 16 (at most 128, 64 at H = 128):
 // the row and column passes of one image in one workgroup, the row spectrum
 // in LDS.  Forward: x [nimg][H][W] -> the canonical spectrum
 // xh [nimg][2 mx][my] (kept kx rows, mode q my + ky), scaled by scale.
 bool short2d_supported(int log2H, int log2W, int mx, int my);
-// whether the one-kernel form pays for nimg images of 2^log2W-point rows
-// (enough images for the CUs; with 128-point rows, at most one per CU)
-bool short2d_pays(int64_t nimg, int log2W);
+// whether the one-kernel form pays for nimg images of 2^log2H rows of
+// 2^log2W points (enough images for the CUs; with 128-point rows, at most
+// one per CU, one per two CUs at 512 rows)
+bool short2d_pays(int64_t nimg, int log2H, int log2W);
 hipError_t launch_fwd2d_short(const float* x, float2* xh, int64_t nimg, int log2H, int log2W, int mx, int my,
                               float scale, const float2* tw, hipStream_t s);
 // Inverse: the canonical spectrum yh [nimg][2 mx][my] -> out [nimg][H][W]

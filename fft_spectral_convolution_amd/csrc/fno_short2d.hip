@@ -1,5 +1,5 @@
-// Per-image 2D transforms for grids of 128 x 256, 256 x 128 and of 256 or 512
-// rows by 256 or 512 columns with at most 32 (16 at 512 rows) kept columns: the row pass and the column pass of
+// Per-image 2D transforms for grids of 128 x 256 and of 256 or 512 rows by
+// 128, 256 or 512 columns with at most 32 (16 at 512 rows) kept columns: the row pass and the column pass of
 // one image in one workgroup, the row spectrum kept in LDS between them
 // (TurboFNO blog, section 2.1: the truncated spectrum stays on chip between
 // the passes of the 2D transform; section 2.2: only the kept modes are ever
@@ -411,11 +411,10 @@ hipError_t launch_s2(K kernel, int64_t nimg, hipStream_t s, int& g) {
 
 }  // namespace
 
-// 128 rows of 256 points, 256 rows of 128 points, 256 or 512 rows of 256 or
-// 512 points (the forms that fit the registers of 16 waves without spills);
+// 128 rows of 256 points, 256 or 512 rows of 128, 256 or 512 points (the forms that fit the registers of 16 waves without spills);
 // at 512 rows at most 16 kept columns (the plane beside the stages in the LDS)
 bool short2d_supported(int log2H, int log2W, int mx, int my) {
-    return log2H >= 7 && log2H <= 9 && (log2W == 8 || (log2W == 9 && log2H > 7) || (log2W == 7 && log2H == 8)) &&
+    return log2H >= 7 && log2H <= 9 && (log2W == 8 || (log2W == 9 && log2H > 7) || (log2W == 7 && log2H > 7)) &&
            my >= 1 &&
            my <= (log2H == 9 ? 16 : 32) &&
            mx >= 1 && (2 * mx) % 16 == 0 && 2 * mx <= s2_kept(1 << log2H);
@@ -424,15 +423,17 @@ bool short2d_supported(int log2H, int log2W, int mx, int my) {
 // One image per workgroup and one workgroup per CU: with fewer images than
 // half the CUs the staged kernels, which spread an image over several
 // workgroups, were faster (256 x 256, 32 and 64 images: 37 against 28 and
-// 32 us; even at 128 images, faster from 256 on).  With 128-point rows
-// (256 x 128) the one-kernel form pays only up to one image per CU: 128 and
-// 256 images 25 and 31 us against 30 and 35 staged, 512 images 50 against 50
-// (16 kept columns) and 46.5 against 43 (8).
-bool short2d_pays(int64_t nimg, int log2W) {
+// 32 us; even at 128 images, faster from 256 on).  With 128-point rows the
+// one-kernel form pays only up to one image per CU at 256 rows (128 and 256
+// images 25 and 31 us against 30 and 35 staged; 512 images 50 against 50
+// with 16 kept columns, 46.5 against 43 with 8) and up to one image per two
+// CUs at 512 rows (128 images 34 against 39 us; 192 and 256 images the same
+// as staged).
+bool short2d_pays(int64_t nimg, int log2H, int log2W) {
     int dev = 0, cus = 0;
     if (hipGetDevice(&dev) != hipSuccess) return false;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
-    return 2 * nimg >= cus && (log2W != 7 || nimg <= cus);
+    return 2 * nimg >= cus && (log2W != 7 || nimg <= (log2H == 9 ? cus / 2 : cus));
 }
 
 hipError_t launch_fwd2d_short(const float* x, float2* xh, int64_t nimg, int log2H, int log2W, int mx, int my,
@@ -444,7 +445,10 @@ hipError_t launch_fwd2d_short(const float* x, float2* xh, int64_t nimg, int log2
         if (e != hipSuccess) return e;
         return launch_kernel(kernel, dim3((unsigned)g), dim3(kS2Threads), 0, s, x, xh, nimg, mx, my, scale, tw);
     };
-    if (log2H == 9) return log2W == 8 ? go(k_fwd2d_short<16, 32>) : go(k_fwd2d_short<32, 32>);
+    if (log2H == 9) {
+        if (log2W == 7) return go(k_fwd2d_short<8, 32>);
+        return log2W == 8 ? go(k_fwd2d_short<16, 32>) : go(k_fwd2d_short<32, 32>);
+    }
     if (log2H == 7) return go(k_fwd2d_short<16, 8>);
     if (log2W == 7) return go(k_fwd2d_short<8, 16>);
     if (log2W == 8) return go(k_fwd2d_short<16, 16>);
@@ -467,6 +471,7 @@ hipError_t launch_inv2d_short(const float2* yh, float* out, int64_t nimg, int lo
         return two ? go(k_inv2d_short<16, 8, false, 2>) : go(k_inv2d_short<16, 8, false, 1>);
     }
     if (log2H == 9) {                       // my <= 16
+        if (log2W == 7) return epi.on ? go(k_inv2d_short<8, 32, true, 1>) : go(k_inv2d_short<8, 32, false, 1>);
         if (log2W == 8) return epi.on ? go(k_inv2d_short<16, 32, true, 1>) : go(k_inv2d_short<16, 32, false, 1>);
         return epi.on ? go(k_inv2d_short<32, 32, true, 1>) : go(k_inv2d_short<32, 32, false, 1>);
     }

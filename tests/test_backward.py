@@ -81,6 +81,7 @@ BACKWARD_2D = [
     (16, 8, 8, 512, 256, 16, 8),    # one-kernel 512 x 256 transforms
     (16, 8, 8, 128, 256, 8, 16),    # one-kernel 128 x 256 transforms
     (16, 8, 8, 256, 128, 16, 24),   # one-kernel 256 x 128 transforms
+    (16, 8, 8, 512, 128, 24, 16),   # one-kernel 512 x 128 transforms
     (1, 2, 3, 256, 128, 16, 24),    # staged: 128-point short rows, 256-row short columns
     (1, 2, 2, 64, 512, 8, 12),      # staged: 512-point short rows, 64-row short columns
     (1, 2, 3, 16, 1024, 5, 50),     # pruned long rows

@@ -84,6 +84,7 @@ GELU_2D = [
     (16, 8, 8, 512, 256, 8, 12),      # one-kernel 512 x 256 transforms, the tail
     (16, 8, 8, 128, 256, 8, 24),      # one-kernel 128 x 256 transforms, the tail
     (16, 8, 8, 256, 128, 16, 20),     # one-kernel 256 x 128 transforms, the tail
+    (16, 8, 8, 512, 128, 8, 12),      # one-kernel 512 x 128 transforms, the tail
     (1, 2, 3, 16, 1024, 5, 50),       # staged: pruned long rows
     (1, 2, 2, 1024, 16, 8, 9),        # staged: pruned columns, generic rows
     (2, 3, 4, 45, 100, 10, 20),       # mixed-radix rows and columns

@@ -125,6 +125,7 @@ def test_stages_2d(name):
     (16, 8, 8, 256, 512, 8, 12),    # the one-kernel 256 x 512 forward and inverse, one column block
     (16, 8, 8, 512, 512, 8, 16),    # the one-kernel 512 x 512 forward and inverse
     (16, 8, 8, 256, 128, 24, 16),   # the one-kernel 256 x 128 forward and inverse, one column block
+    (16, 8, 8, 512, 128, 8, 16),    # the one-kernel 512 x 128 forward and inverse
     (2, 3, 4, 256, 256, 16, 32),    # few images: the staged transforms
 ], ids=lambda s: "x".join(map(str, s)))
 def test_stages_2d_shapes(shape):
@@ -192,6 +193,9 @@ EDGE_2D = [
     (16, 8, 8, 256, 128, 64, 8),    # one-kernel 256 x 128 transforms, every kept kx of 128, one column block
     (16, 8, 8, 256, 128, 8, 32),    # one-kernel 256 x 128 transforms, two whole column blocks
     (40, 8, 8, 256, 128, 16, 20),   # 256 x 128 with more images than CUs: staged transforms
+    (16, 8, 8, 512, 128, 16, 12),   # one-kernel 512 x 128 transforms, ragged column block
+    (16, 8, 8, 512, 128, 64, 16),   # one-kernel 512 x 128 transforms, 128 kept kx, a whole column block
+    (8, 24, 16, 512, 128, 16, 12),  # 512 x 128: 192 images in (staged forward), 128 out (one-kernel inverse)
     (1, 2, 3, 128, 256, 9, 100),    # 256-point rows with more than 64 bins: generic rows and columns
     (1, 2, 3, 512, 128, 24, 5),     # 512-row short columns, one partial block of 16 columns
     (2, 3, 4, 256, 64, 8, 20),      # 64-point short rows (16 rows per wave), bins in two groups of 16
