@@ -196,6 +196,8 @@ EDGE_2D = [
     (16, 8, 8, 512, 128, 16, 12),   # one-kernel 512 x 128 transforms, ragged column block
     (16, 8, 8, 512, 128, 64, 16),   # one-kernel 512 x 128 transforms, 128 kept kx, a whole column block
     (8, 24, 16, 512, 128, 16, 12),  # 512 x 128: 192 images in (staged forward), 128 out (one-kernel inverse)
+    (16, 8, 8, 256, 128, 8, 1),     # one-kernel 256 x 128 transforms, one kept column
+    (16, 8, 8, 512, 128, 8, 1),     # one-kernel 512 x 128 transforms, one kept column
     (1, 2, 3, 128, 256, 9, 100),    # 256-point rows with more than 64 bins: generic rows and columns
     (1, 2, 3, 512, 128, 24, 5),     # 512-row short columns, one partial block of 16 columns
     (2, 3, 4, 256, 64, 8, 20),      # 64-point short rows (16 rows per wave), bins in two groups of 16
