@@ -1,6 +1,7 @@
 // Per-image 2D transforms for grids of 128 x 256 and of 256 or 512 rows by
-// 128, 256 or 512 columns with at most 32 (16 at 512 rows) kept columns: the row pass and the column pass of
-// one image in one workgroup, the row spectrum kept in LDS between them
+// 128, 256 or 512 columns with at most 32 (16 at 512 rows) kept columns: the
+// row pass and the column pass of one image in one workgroup, the row
+// spectrum kept in LDS between them
 // (TurboFNO blog, section 2.1: the truncated spectrum stays on chip between
 // the passes of the 2D transform; section 2.2: only the kept modes are ever
 // formed).
@@ -411,8 +412,9 @@ hipError_t launch_s2(K kernel, int64_t nimg, hipStream_t s, int& g) {
 
 }  // namespace
 
-// 128 rows of 256 points, 256 or 512 rows of 128, 256 or 512 points (the forms that fit the registers of 16 waves without spills);
-// at 512 rows at most 16 kept columns (the plane beside the stages in the LDS)
+// 128 rows of 256 points, 256 or 512 rows of 128, 256 or 512 points (the
+// forms that fit the registers of 16 waves without spills); at 512 rows at
+// most 16 kept columns (the plane beside the stages in the LDS)
 bool short2d_supported(int log2H, int log2W, int mx, int my) {
     return log2H >= 7 && log2H <= 9 && (log2W == 8 || (log2W == 9 && log2H > 7) || (log2W == 7 && log2H > 7)) &&
            my >= 1 &&
